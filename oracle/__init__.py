@@ -1,0 +1,227 @@
+"""CPU oracle for block-wise microscaling FP4 (MXFP4 / NVFP4) -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
+may import this package.  The product path (the HIP library and its Python
+binding) never loads it, and the two share no code.
+
+The arithmetic lives in ``fp4_oracle.c`` (plain C, IEEE binary32/binary64, no
+FMA contraction); this module only marshals numpy arrays into it through ctypes.
+Every function of the C file cites the passage it follows.
+
+Pinning status: every function here is pinned by ``tests/test_oracle_pins.py``
+(worked examples and printed emulation results of "NVFP4 vs MXFP4: 4-Bit
+Floating Point for LLM Training and Inference (2026)", format definitions,
+closed forms, brute force on tiny inputs, invariants).  No function is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp4_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+MXFP4 = 0
+NVFP4 = 1
+BLOCK = {MXFP4: 32, NVFP4: 16}
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (plain C, no vectorisation tricks)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load(path: str):
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    l = ctypes.c_long
+    L.ora_e2m1_decode.restype = ctypes.c_double
+    L.ora_e2m1_decode.argtypes = [ctypes.c_int]
+    L.ora_e2m1_encode.restype = ctypes.c_int
+    L.ora_e2m1_encode.argtypes = [ctypes.c_float]
+    L.ora_e4m3_decode.restype = ctypes.c_double
+    L.ora_e4m3_decode.argtypes = [ctypes.c_int]
+    L.ora_e4m3_encode.restype = ctypes.c_int
+    L.ora_e4m3_encode.argtypes = [ctypes.c_float]
+    L.ora_e8m0_decode.restype = ctypes.c_double
+    L.ora_e8m0_decode.argtypes = [ctypes.c_int]
+    L.ora_rotate.restype = ctypes.c_int
+    L.ora_rotate.argtypes = [P, P, l, l, ctypes.c_int]
+    L.ora_quantize.restype = ctypes.c_int
+    L.ora_quantize.argtypes = [ctypes.c_int, ctypes.c_int, P, l, l, P, P, P, ctypes.c_int]
+    L.ora_dequantize.restype = ctypes.c_int
+    L.ora_dequantize.argtypes = [ctypes.c_int, P, P, ctypes.c_float, l, l, ctypes.c_int, P]
+    L.ora_error_sums.restype = None
+    L.ora_error_sums.argtypes = [P, P, l, P]
+    L.ora_gemm_entries.restype = ctypes.c_int
+    L.ora_gemm_entries.argtypes = [ctypes.c_int, l, P, P, ctypes.c_float, P, P,
+                                   ctypes.c_float, l, P, P, P, P]
+    L.ora_e2m1_encode_array.restype = None
+    L.ora_e2m1_encode_array.argtypes = [P, l, P]
+    L.ora_e4m3_encode_array.restype = None
+    L.ora_e4m3_encode_array.argtypes = [P, l, P]
+    return L
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        _lib = _load(_LIB)
+    return _lib
+
+
+def use_library(path: str | None):
+    """Point the wrapper at another build of the oracle source (the mutation
+    test loads deliberately broken copies); None restores the default."""
+    global _lib
+    _lib = None if path is None else _load(path)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def e2m1_decode(code: int) -> float:
+    return lib().ora_e2m1_decode(int(code))
+
+
+def e2m1_encode(q: float) -> int:
+    return lib().ora_e2m1_encode(float(q))
+
+
+def e2m1_encode_array(q) -> np.ndarray:
+    q = _f32(q).reshape(-1)
+    out = np.empty(q.size, dtype=np.uint8)
+    lib().ora_e2m1_encode_array(_p(q), q.size, _p(out))
+    return out
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().ora_e4m3_decode(int(code))
+
+
+def e4m3_encode(t: float) -> int:
+    return lib().ora_e4m3_encode(float(t))
+
+
+def e4m3_encode_array(t) -> np.ndarray:
+    t = _f32(t).reshape(-1)
+    out = np.empty(t.size, dtype=np.uint8)
+    lib().ora_e4m3_encode_array(_p(t), t.size, _p(out))
+    return out
+
+
+def e8m0_decode(code: int) -> float:
+    return lib().ora_e8m0_decode(int(code))
+
+
+def rotate(x, n: int) -> np.ndarray:
+    """Block Hadamard (Sylvester, / sqrt(n)) along the last axis."""
+    x = _f32(x)
+    rows, cols = (1, x.size) if x.ndim == 1 else x.shape
+    y = np.empty_like(x)
+    rc = lib().ora_rotate(_p(x), _p(y), rows, cols, n)
+    if rc != 0:
+        raise ValueError("ora_rotate: bad arguments")
+    return y
+
+
+def quantize(x, fmt: int, rotate: bool = False, ts: float | None = None):
+    """Returns (codes [rows, cols/2] u8, scales [rows, cols/G] u8, ts float32)."""
+    x = _f32(x)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    rows, cols = x.shape
+    G = BLOCK[fmt]
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // G), dtype=np.uint8)
+    tsa = np.zeros(1, dtype=np.float32)
+    if ts is not None:
+        tsa[0] = ts
+    rc = lib().ora_quantize(fmt, int(bool(rotate)), _p(x), rows, cols, _p(codes), _p(scales),
+                            _p(tsa), int(ts is not None))
+    if rc != 0:
+        raise ValueError("ora_quantize: bad arguments")
+    return codes, scales, np.float32(tsa[0])
+
+
+def dequantize(codes, scales, fmt: int, ts: float = 0.0, inverse_rotate: bool = False):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows = codes.shape[0]
+    cols = codes.shape[1] * 2
+    y = np.empty((rows, cols), dtype=np.float32)
+    rc = lib().ora_dequantize(fmt, _p(codes), _p(scales), float(ts), rows, cols,
+                              int(bool(inverse_rotate)), _p(y))
+    if rc != 0:
+        raise ValueError("ora_dequantize: bad arguments")
+    return y
+
+
+def error_sums(x, xhat) -> np.ndarray:
+    """[sum (x-x^)^2, sum x^2, sum x x^, sum x^^2] in double."""
+    x = _f32(x).reshape(-1)
+    xhat = _f32(xhat).reshape(-1)
+    assert x.size == xhat.size
+    out = np.zeros(4, dtype=np.float64)
+    lib().ora_error_sums(_p(x), _p(xhat), x.size, _p(out))
+    return out
+
+
+def nmse(x, xhat) -> float:
+    s = error_sums(x, xhat)
+    return float(s[0] / s[1])
+
+
+def cosine(x, xhat) -> float:
+    s = error_sums(x, xhat)
+    return float(s[2] / np.sqrt(s[1] * s[3]))
+
+
+def gemm_entries(fmt: int, K: int, a_codes, a_scales, a_ts, b_codes, b_scales, b_ts,
+                 rows, cols):
+    """(y, |A||B|) at the listed (row, col) pairs of Y = A B^T, in double."""
+    a_codes = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    b_codes = np.ascontiguousarray(b_codes, dtype=np.uint8)
+    a_scales = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    b_scales = np.ascontiguousarray(b_scales, dtype=np.uint8)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    assert rows.size == cols.size
+    y = np.zeros(rows.size, dtype=np.float64)
+    ab = np.zeros(rows.size, dtype=np.float64)
+    rc = lib().ora_gemm_entries(fmt, K, _p(a_codes), _p(a_scales), float(a_ts), _p(b_codes),
+                                _p(b_scales), float(b_ts), rows.size, _p(rows), _p(cols),
+                                _p(y), _p(ab))
+    if rc != 0:
+        raise ValueError("ora_gemm_entries: bad arguments")
+    return y, ab
+
+
+def gemm_full(fmt: int, K: int, a_codes, a_scales, a_ts, b_codes, b_scales, b_ts):
+    M = a_codes.shape[0]
+    N = b_codes.shape[0]
+    r, c = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    y, ab = gemm_entries(fmt, K, a_codes, a_scales, a_ts, b_codes, b_scales, b_ts,
+                         r.reshape(-1), c.reshape(-1))
+    return y.reshape(M, N), ab.reshape(M, N)

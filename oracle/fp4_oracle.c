@@ -1,0 +1,456 @@
+/*
+ * fp4_oracle.c -- plain, slow, obviously-correct CPU oracle for block-wise
+ * microscaling FP4 quantization (MXFP4, NVFP4), its dequantization, the error
+ * metrics, and the FP4 x FP4 block-scaled matrix product.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant generator with the HIP library, and it is never on
+ * the product path.
+ *
+ * Every function states the passage it follows.  Pages are cited by title:
+ *   [MRGPTQ]  "Bridging the Gap Between Promise and Performance for Microscaling
+ *             FP4 Quantization"
+ *   [VS]      "NVFP4 vs MXFP4: 4-Bit Floating Point for LLM Training and
+ *             Inference (2026)"
+ *   [PORT]    "Portable FP4 Quantization for Heterogeneous Accelerators"
+ *   [PROD]    "Microscaling Formats in Production LLM Inference: NVFP4 vs. MXFP4
+ *             Architecture, Block Quantization, Kernel Scaling, and Perplexity
+ *             Degradation"
+ *
+ * Readings where the pages are silent or disagree (each one is listed with its
+ * reason in the design notes of the repository):
+ *   - E2M1 ties go to the even code (round-to-nearest-even), following [VS]
+ *     "The training recipe, piece by piece" and [PROD] "Microscaled Residual
+ *     GPTQ"; [VS]'s emulation breaks ties toward zero but says it ignores the
+ *     tie rules.
+ *   - Values beyond 6 saturate to +-6 ([VS] emulation clips to [0, 6]).
+ *   - MXFP4 exponent = floor(log2(block amax)) - 2, taken exactly from the
+ *     binary exponent, clamped to [-127, 127]; an all-zero block gets code 0.
+ *   - NVFP4: ts = amax_tensor / (6*448) in fp32; block scale code =
+ *     E4M3(RNE, saturating at 448) of (amax_block / 6) / ts, all in fp32 in that
+ *     order; elements use q = fl32(x / s) with s = fl32(e4m3 * ts).  A block whose
+ *     s is zero stores all-zero element codes.
+ *   - Hadamard: Sylvester order, normalised by 1/sqrt(n), n = block size.
+ *   - Element 2i goes in the low nibble of byte i.
+ *   - The sign bit of an element code is the sign bit of q, so a negative value
+ *     that rounds to zero stores code 0x8.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared.
+ * Floating point follows IEEE-754 binary32/binary64 exactly as written: no
+ * contraction into FMA, no reassociation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORA_MXFP4 0
+#define ORA_NVFP4 1
+
+#define ORA_OK 0
+#define ORA_EINVAL -1
+
+/* ------------------------------------------------------------------------ */
+/* E2M1 element ([MRGPTQ] format definitions; [VS] "The E2M1 element: only   */
+/* eight magnitudes"; [PROD] "The Numerical Ceiling of Standard 4-Bit        */
+/* Floating Point", bit layout: 1 sign bit, 2 exponent bits with bias 1,     */
+/* 1 mantissa bit).                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Value of a 4-bit code, decoded from its fields. */
+double ora_e2m1_decode(int code)
+{
+    int sign = (code >> 3) & 1;
+    int exp_field = (code >> 1) & 3;
+    int man = code & 1;
+    double mag;
+    if (exp_field == 0)            /* subnormal: 0.m x 2^(1-bias) */
+        mag = 0.5 * man;
+    else                           /* normal: 1.m x 2^(e-bias) */
+        mag = ldexp(1.0 + 0.5 * man, exp_field - 1);
+    return sign ? -mag : mag;
+}
+
+/* Code of the grid point nearest to q.  |q| > 6 saturates to 6.  Ties go to
+ * the even code (mantissa bit 0).  The sign bit is signbit(q). */
+int ora_e2m1_encode(float q)
+{
+    int neg = signbit(q) ? 1 : 0;
+    double a = fabs((double)q);
+    if (a > 6.0)
+        a = 6.0;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c < 8; ++c) {
+        double d = fabs(a - ora_e2m1_decode(c));
+        if (d < bestd || (d == bestd && (c & 1) == 0)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return (neg << 3) | best;
+}
+
+/* ------------------------------------------------------------------------ */
+/* E4M3 scale ([MRGPTQ] NVFP4 definition; [VS] "Why the scale format matters */
+/* more than the element" (maximum 448) and the emulation's e4m3 rounding:   */
+/* 3 mantissa bits, minimum normal exponent -6, subnormal step 2^-9).        */
+/* OCP E4M3 "FN": bias 7, no infinities, 0x7F / 0xFF are NaN.                */
+/* ------------------------------------------------------------------------ */
+
+double ora_e4m3_decode(int code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);              /* 0.mmm x 2^(1-7) */
+    else
+        mag = ldexp(1.0 + m / 8.0, e - 7);       /* 1.mmm x 2^(e-7) */
+    return sign ? -mag : mag;
+}
+
+/* Code of the non-negative E4M3 value nearest to t, after clipping t to
+ * [0, 448].  Ties go to the even code.  t must be >= 0 (or +inf). */
+int ora_e4m3_encode(float t)
+{
+    double a = (double)t;
+    if (!(a > 0.0))
+        return 0;
+    if (a > 448.0)
+        a = 448.0;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double d = fabs(a - ora_e4m3_decode(c));
+        if (d < bestd || (d == bestd && (c & 1) == 0)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* E8M0 scale value 2^(code-127) ([MRGPTQ] MXFP4 definition; [PROD] "Format  */
+/* Specifications": exponent-only, bias 127).  Code 255 is not produced.     */
+double ora_e8m0_decode(int code)
+{
+    return ldexp(1.0, code - 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block Hadamard rotation ([MRGPTQ]: rotations at the group level, matching */
+/* the quantization group size, Q(W H_k) Q(X H_k)^T; [PORT] section 2.3:     */
+/* block-local orthogonal transform, norm preserving, eq. (2)).              */
+/* ------------------------------------------------------------------------ */
+
+/* Entry (i, j) of the unnormalised Sylvester Hadamard matrix of order 2^m. */
+static int had_entry(int i, int j)
+{
+    return (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1;
+}
+
+/* y[r, b*n + j] = fl32( (sum_i x[r, b*n + i] * H[i][j]) / sqrt(n) ), the sum
+ * and the division carried out in double.  n must be a power of two and
+ * divide cols.  x and y may not alias. */
+int ora_rotate(const float *x, float *y, long rows, long cols, int n)
+{
+    if (n <= 0 || (n & (n - 1)) != 0 || cols % n != 0)
+        return ORA_EINVAL;
+    double root = sqrt((double)n);
+    for (long r = 0; r < rows; ++r) {
+        for (long b = 0; b < cols / n; ++b) {
+            const float *xb = x + r * cols + b * n;
+            float *yb = y + r * cols + b * n;
+            for (int j = 0; j < n; ++j) {
+                double s = 0.0;
+                for (int i = 0; i < n; ++i)
+                    s += (double)xb[i] * had_entry(i, j);
+                yb[j] = (float)(s / root);
+            }
+        }
+    }
+    return ORA_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantization.                                                             */
+/* ------------------------------------------------------------------------ */
+
+static float block_amax(const float *v, int n)
+{
+    float m = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > m)
+            m = a;
+    }
+    return m;
+}
+
+/* MXFP4 shared exponent of a block: floor(log2(amax)) - 2, clamped to
+ * [-127, 127] ([VS] "A worked example, by hand" and the emulation's mxfp4;
+ * [VS] "Why the scale format matters": E8M0 spans 2^-127 .. 2^127).
+ * floor(log2(amax)) is read from frexp, which is exact: amax = f * 2^E with
+ * f in [0.5, 1), so floor(log2(amax)) = E - 1. */
+static int mx_exponent(float amax)
+{
+    if (amax == 0.0f)
+        return -127;
+    int E;
+    (void)frexp((double)amax, &E);
+    int e = (E - 1) - 2;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return e;
+}
+
+static void put_code(uint8_t *row_codes, long k, int code)
+{
+    if ((k & 1) == 0)
+        row_codes[k >> 1] = (uint8_t)((row_codes[k >> 1] & 0xF0) | (code & 0xF));
+    else
+        row_codes[k >> 1] = (uint8_t)((row_codes[k >> 1] & 0x0F) | ((code & 0xF) << 4));
+}
+
+static int get_code(const uint8_t *row_codes, long k)
+{
+    return (k & 1) ? (row_codes[k >> 1] >> 4) & 0xF : row_codes[k >> 1] & 0xF;
+}
+
+/*
+ * Quantize x [rows, cols] (fp32, row-major, blocks run along cols).
+ *   fmt     ORA_MXFP4 (block 32, E8M0) or ORA_NVFP4 (block 16, E4M3 x fp32).
+ *   rotate  0, or 1 for a block Hadamard of the block size applied first.
+ *   codes   out, [rows, cols/2] bytes, element 2i in the low nibble.
+ *   scales  out, [rows, cols/G] bytes, row-major.
+ *   ts      NVFP4 per-tensor scale: written (gs_given = 0) or read (= 1).
+ * MXFP4 follows [VS] "A worked example, by hand" and the emulation's mxfp4;
+ * NVFP4 follows [VS] Figure 2 (global amax -> fp32 tensor scale -> block amax
+ * -> E4M3 -> E2M1 -> pack) and the emulation's nvfp4.
+ */
+int ora_quantize(int fmt, int rotate, const float *x, long rows, long cols,
+                 uint8_t *codes, uint8_t *scales, float *ts, int gs_given)
+{
+    int G;
+    if (fmt == ORA_MXFP4)
+        G = 32;
+    else if (fmt == ORA_NVFP4)
+        G = 16;
+    else
+        return ORA_EINVAL;
+    if (rows < 0 || cols < 0 || cols % G != 0 || (rotate != 0 && rotate != 1))
+        return ORA_EINVAL;
+    if (fmt == ORA_NVFP4 && ts == NULL)
+        return ORA_EINVAL;
+
+    long n = rows * cols;
+    const float *y = x;
+    float *ybuf = NULL;
+    if (rotate) {
+        ybuf = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+        if (!ybuf)
+            return ORA_EINVAL;
+        ora_rotate(x, ybuf, rows, cols, G);
+        y = ybuf;
+    }
+
+    float tsv = 0.0f;
+    if (fmt == ORA_NVFP4) {
+        if (gs_given) {
+            tsv = *ts;
+        } else {
+            float gamax = 0.0f;
+            for (long i = 0; i < n; ++i) {
+                float a = fabsf(y[i]);
+                if (a > gamax)
+                    gamax = a;
+            }
+            tsv = gamax / 2688.0f;          /* 6 * 448 */
+            *ts = tsv;
+        }
+    }
+
+    long nb = cols / G;
+    for (long r = 0; r < rows; ++r) {
+        uint8_t *rc = codes + r * (cols / 2);
+        for (long b = 0; b < nb; ++b) {
+            const float *yb = y + r * cols + b * G;
+            float amax = block_amax(yb, G);
+            if (fmt == ORA_MXFP4) {
+                int e = mx_exponent(amax);
+                scales[r * nb + b] = (uint8_t)(e + 127);
+                float s = ldexpf(1.0f, e);
+                for (int i = 0; i < G; ++i) {
+                    float q = yb[i] / s;
+                    put_code(rc, b * G + i, ora_e2m1_encode(q));
+                }
+            } else {
+                int sc = 0;
+                float s = 0.0f;
+                if (tsv > 0.0f) {
+                    float t = (amax / 6.0f) / tsv;
+                    sc = ora_e4m3_encode(t);
+                    s = (float)ora_e4m3_decode(sc) * tsv;
+                }
+                scales[r * nb + b] = (uint8_t)sc;
+                for (int i = 0; i < G; ++i) {
+                    int code = 0;
+                    if (s != 0.0f) {
+                        float q = yb[i] / s;
+                        code = ora_e2m1_encode(q);
+                    }
+                    put_code(rc, b * G + i, code);
+                }
+            }
+        }
+    }
+    free(ybuf);
+    return ORA_OK;
+}
+
+/*
+ * Dequantize codes/scales back to fp32 y [rows, cols] ([VS] Figure 1: element
+ * times scale, NVFP4 applying the per-tensor factor on top; [PROD] "Format
+ * Specifications").  MXFP4: y = e2m1 * 2^(c-127).  NVFP4: y = fl32(fl32(e2m1 *
+ * e4m3) * ts) -- the inner product is exact in fp32.  inverse_rotate = 1 then
+ * applies the (self-inverse) normalised block Hadamard of the block size.
+ */
+int ora_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, float ts,
+                   long rows, long cols, int inverse_rotate, float *y)
+{
+    int G;
+    if (fmt == ORA_MXFP4)
+        G = 32;
+    else if (fmt == ORA_NVFP4)
+        G = 16;
+    else
+        return ORA_EINVAL;
+    if (rows < 0 || cols < 0 || cols % G != 0)
+        return ORA_EINVAL;
+    long nb = cols / G;
+    float *tmp = NULL;
+    float *dst = y;
+    if (inverse_rotate) {
+        tmp = (float *)malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
+        if (!tmp)
+            return ORA_EINVAL;
+        dst = tmp;
+    }
+    for (long r = 0; r < rows; ++r) {
+        const uint8_t *rc = codes + r * (cols / 2);
+        for (long k = 0; k < cols; ++k) {
+            double m = ora_e2m1_decode(get_code(rc, k));
+            int sc = scales[r * nb + k / G];
+            if (fmt == ORA_MXFP4) {
+                dst[r * cols + k] = (float)(m * ora_e8m0_decode(sc));
+            } else {
+                float inner = (float)(m * ora_e4m3_decode(sc));
+                dst[r * cols + k] = inner * ts;
+            }
+        }
+    }
+    if (inverse_rotate) {
+        ora_rotate(tmp, y, rows, cols, G);
+        free(tmp);
+    }
+    return ORA_OK;
+}
+
+/*
+ * Error sums over n values in double ([PORT] section 3.2: NMSE = ||x - x^||^2
+ * / ||x||^2 and cosine similarity; [VS] emulation: MSE and SQNR = 10 log10(
+ * mean x^2 / MSE)).  out[0] = sum (x - x^)^2, out[1] = sum x^2,
+ * out[2] = sum x * x^, out[3] = sum x^^2.
+ */
+void ora_error_sums(const float *x, const float *xhat, long n, double *out)
+{
+    double se = 0.0, sx = 0.0, sxy = 0.0, sy = 0.0;
+    for (long i = 0; i < n; ++i) {
+        double a = x[i], b = xhat[i];
+        se += (a - b) * (a - b);
+        sx += a * a;
+        sxy += a * b;
+        sy += b * b;
+    }
+    out[0] = se;
+    out[1] = sx;
+    out[2] = sxy;
+    out[3] = sy;
+}
+
+/*
+ * Selected entries of Y = A * B^T ([MRGPTQ]: the kernels compute
+ * Q(W H_k) Q(X H_k)^T; [VS] "Hardware execution": scales applied inside the
+ * product, accumulation at higher precision).  A is [M, K] and B is [N, K],
+ * both as packed codes (row-major, K/2 bytes per row) with row-major scales
+ * (K/G per row).  For each requested (row, col):
+ *   y    = sum_k a^[row][k] * b^[col][k]  in double;
+ *   absy = sum_k |a^[row][k]| * |b^[col][k]|.
+ * MXFP4: a^ = e2m1 * 2^(c-127).  NVFP4: the sum runs over (e2m1 * e4m3)
+ * products and is multiplied by a_ts * b_ts at the end.
+ */
+int ora_gemm_entries(int fmt, long K,
+                     const uint8_t *a_codes, const uint8_t *a_scales, float a_ts,
+                     const uint8_t *b_codes, const uint8_t *b_scales, float b_ts,
+                     long nent, const long *rows, const long *cols,
+                     double *y, double *absy)
+{
+    int G;
+    if (fmt == ORA_MXFP4)
+        G = 32;
+    else if (fmt == ORA_NVFP4)
+        G = 16;
+    else
+        return ORA_EINVAL;
+    if (K < 0 || K % G != 0)
+        return ORA_EINVAL;
+    long nb = K / G;
+    for (long e = 0; e < nent; ++e) {
+        const uint8_t *ac = a_codes + rows[e] * (K / 2);
+        const uint8_t *bc = b_codes + cols[e] * (K / 2);
+        const uint8_t *as = a_scales + rows[e] * nb;
+        const uint8_t *bs = b_scales + cols[e] * nb;
+        double s = 0.0, sa = 0.0;
+        for (long k = 0; k < K; ++k) {
+            double av = ora_e2m1_decode(get_code(ac, k));
+            double bv = ora_e2m1_decode(get_code(bc, k));
+            if (fmt == ORA_MXFP4) {
+                av *= ora_e8m0_decode(as[k / G]);
+                bv *= ora_e8m0_decode(bs[k / G]);
+            } else {
+                av *= ora_e4m3_decode(as[k / G]);
+                bv *= ora_e4m3_decode(bs[k / G]);
+            }
+            s += av * bv;
+            sa += fabs(av) * fabs(bv);
+        }
+        if (fmt == ORA_NVFP4) {
+            double g = (double)a_ts * (double)b_ts;
+            s *= g;
+            sa *= fabs(g);
+        }
+        y[e] = s;
+        absy[e] = sa;
+    }
+    return ORA_OK;
+}
+
+/* Array forms of the codecs, for exhaustive checks. */
+void ora_e2m1_encode_array(const float *q, long n, uint8_t *out)
+{
+    for (long i = 0; i < n; ++i)
+        out[i] = (uint8_t)ora_e2m1_encode(q[i]);
+}
+
+void ora_e4m3_encode_array(const float *t, long n, uint8_t *out)
+{
+    for (long i = 0; i < n; ++i)
+        out[i] = (uint8_t)ora_e4m3_encode(t[i]);
+}

@@ -1,0 +1,536 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each ``check_*`` function raises AssertionError on a mismatch.  They are run by
+``test_oracle_pins.py`` against the real oracle, and by the mutation test
+against deliberately broken copies of it (every planted mistake must trip at
+least one check).  None of these checks re-types the oracle's own algorithm:
+each compares it with a printed value, a closed form, a library routine, an
+invariant, or a brute-force search.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import scipy.linalg
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+FMT = _golden("format_definitions.json")
+GRID = np.array(FMT["e2m1_positive_magnitudes"])          # index = magnitude code
+
+
+# ---------------------------------------------------------------- E2M1 codec
+def check_e2m1_value_set():
+    """Format definitions: the 16 codes decode to {0, +-0.5, ..., +-6}; bit 3 is
+    the sign; exponent field bias 1 puts 1.0 at 0b0010, 2.0 at 0b0100, 4.0 at
+    0b0110 and 6.0 (=1.5 * 4) at 0b0111."""
+    vals = np.array([oracle.e2m1_decode(c) for c in range(16)])
+    assert np.array_equal(vals[:8], GRID), vals
+    assert np.array_equal(vals[8:], -GRID), vals
+    assert oracle.e2m1_decode(0b0010) == 1.0 and oracle.e2m1_decode(0b0100) == 2.0
+    assert oracle.e2m1_decode(0b0110) == 4.0 and oracle.e2m1_decode(0b0111) == 6.0
+    assert oracle.e2m1_decode(0b0001) == 0.5          # subnormal 0.1b x 2^0
+    # code 8 is negative zero
+    assert oracle.e2m1_decode(8) == 0.0 and np.signbit(oracle.e2m1_decode(8))
+
+
+def check_e2m1_midpoints():
+    """Round-to-nearest-even onto the grid (training recipe: RNE for weights and
+    activations).  Midpoints between neighbours resolve to the even code
+    (mantissa bit 0): 0.25->0, 0.75->1, 1.25->1, 1.75->2, 2.5->2, 3.5->4, 5->4."""
+    expect = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for m, v in expect.items():
+        c = oracle.e2m1_encode(m)
+        assert oracle.e2m1_decode(c) == v, (m, c)
+        assert oracle.e2m1_decode(oracle.e2m1_encode(-m)) == -v
+        up = np.nextafter(np.float32(m), np.float32(10))
+        dn = np.nextafter(np.float32(m), np.float32(0))
+        i = int(np.searchsorted(GRID, m))                   # GRID[i-1] < m < GRID[i]
+        assert oracle.e2m1_decode(oracle.e2m1_encode(up)) == GRID[i], (m, "up")
+        assert oracle.e2m1_decode(oracle.e2m1_encode(dn)) == GRID[i - 1], (m, "down")
+
+
+def _float_rne_e2m1(q: np.ndarray) -> np.ndarray:
+    """E2M1 rounding written as generic floating-point rounding: find the binade
+    of |q| (minimum exponent 1 - bias = 0), the spacing there is 2^(E-1) (one
+    mantissa bit), round to a multiple of it with ties to even (np.rint), then
+    saturate at the largest finite value 6."""
+    a = np.abs(q.astype(np.float64))
+    a = np.minimum(a, 6.0)
+    with np.errstate(divide="ignore"):
+        E = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    E = np.maximum(E, 0.0)
+    step = np.exp2(E - 1.0)
+    r = np.rint(a / step) * step
+    r = np.minimum(r, 6.0)
+    mag = np.searchsorted(GRID, r)
+    assert np.array_equal(GRID[mag], r)
+    return (np.signbit(q).astype(np.uint8) << 3) | mag.astype(np.uint8)
+
+
+def _e2m1_probe_values() -> np.ndarray:
+    bits = np.arange(65536, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)                       # every bf16 pattern
+    f = f[np.isfinite(f)]
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 8.0], np.float32)
+    more = []
+    for m in mids:
+        v = np.float32(m)
+        lo = hi = v
+        for _ in range(4):
+            lo = np.nextafter(lo, np.float32(0))
+            hi = np.nextafter(hi, np.float32(100))
+            more += [lo, hi]
+    rnd = workloads.rng(11, 11).uniform(-8, 8, 20000).astype(np.float32)
+    return np.concatenate([f, mids, -mids, np.array(more, np.float32),
+                           -np.array(more, np.float32), rnd]).astype(np.float32)
+
+
+def check_e2m1_exhaustive_vs_float_rounding():
+    """All bf16 bit patterns plus a dense neighbourhood of every midpoint: the
+    oracle's nearest-grid-point encoder equals generic binade-wise RNE with
+    saturation at 6."""
+    q = _e2m1_probe_values()
+    got = oracle.e2m1_encode_array(q)
+    ref = _float_rne_e2m1(q)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (q[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+def check_e2m1_saturation_and_sign():
+    assert oracle.e2m1_encode(1e30) == 0x7 and oracle.e2m1_encode(-1e30) == 0xF
+    assert oracle.e2m1_encode(6.5) == 0x7 and oracle.e2m1_encode(7.99) == 0x7
+    assert oracle.e2m1_encode(0.0) == 0x0
+    assert oracle.e2m1_encode(-0.1) == 0x8                  # sign of a value rounded to 0
+    assert oracle.e2m1_encode(-0.0) == 0x8
+
+
+# ---------------------------------------------------------------- E4M3 codec
+def _e4m3_values_from_definition():
+    """Non-negative finite E4M3 values from the definition: 3 mantissa bits,
+    minimum normal exponent -6 (subnormal spacing 2^-9), maximum 448."""
+    vals = [m * 2.0 ** -9 for m in range(8)]                 # subnormals (and 0)
+    for e in range(-6, 9):
+        for m in range(8):
+            v = (1 + m / 8) * 2.0 ** e
+            if v <= FMT["e4m3_max"]:
+                vals.append(v)
+    return np.array(vals)
+
+
+def check_e4m3_decode():
+    vals = _e4m3_values_from_definition()
+    assert vals.size == 127
+    got = np.array([oracle.e4m3_decode(c) for c in range(127)])
+    assert np.array_equal(got, vals), np.nonzero(got != vals)
+    assert oracle.e4m3_decode(0x7E) == 448.0
+    assert np.isnan(oracle.e4m3_decode(0x7F)) and np.isnan(oracle.e4m3_decode(0xFF))
+    assert oracle.e4m3_decode(0x08) == 2.0 ** -6 and oracle.e4m3_decode(0x01) == 2.0 ** -9
+    assert oracle.e4m3_decode(0x38) == 1.0
+    assert oracle.e4m3_decode(0x80 | 0x38) == -1.0
+
+
+def _binade_rne_e4m3(t: np.ndarray) -> np.ndarray:
+    """Generic float rounding for E4M3 (clip to [0, 448], binade exponent floored
+    at -6, spacing 2^(e-3), ties to even); returns the value."""
+    x = np.clip(t.astype(np.float64), 0, 448)
+    out = np.zeros_like(x)
+    m = x > 0
+    e = np.maximum(np.floor(np.log2(x[m])), -6)
+    step = np.exp2(e - 3)
+    out[m] = np.rint(x[m] / step) * step
+    return np.minimum(out, 448)
+
+
+def check_e4m3_encode_exhaustive():
+    vals = _e4m3_values_from_definition()
+    mids = (vals[1:] + vals[:-1]) / 2
+    probe = [vals, mids, np.array([448.0, 460.0, 464.0, 480.0, 1e4, 1e30, np.inf])]
+    for arr in (vals, mids):
+        f = arr.astype(np.float32)
+        lo, hi = f.copy(), f.copy()
+        for _ in range(3):
+            lo = np.nextafter(lo, np.float32(0))
+            hi = np.nextafter(hi, np.float32(1e9))
+            probe += [lo, hi]
+    probe.append(np.exp2(workloads.rng(12, 12).uniform(-14, 10, 50000)))
+    t = np.concatenate(probe).astype(np.float32)
+    codes = oracle.e4m3_encode_array(t)
+    got = np.array([vals[c] for c in codes])
+    ref = _binade_rne_e4m3(t)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (t[bad[:5]], got[bad[:5]], ref[bad[:5]])
+    # ties go to the even code
+    for i in range(1, 127):
+        mid = np.float32((vals[i - 1] + vals[i]) / 2)
+        if float(mid) == (vals[i - 1] + vals[i]) / 2:
+            c = oracle.e4m3_encode(mid)
+            assert c in (i - 1, i) and c % 2 == 0, (i, c)
+    assert oracle.e4m3_encode(0.0) == 0 and oracle.e4m3_encode(1e30) == 0x7E
+
+
+def check_e8m0():
+    assert oracle.e8m0_decode(127) == 1.0
+    assert oracle.e8m0_decode(0) == 2.0 ** -127 and oracle.e8m0_decode(254) == 2.0 ** 127
+    assert oracle.e8m0_decode(126) == 0.5
+
+
+# --------------------------------------------------------- worked examples
+def check_worked_example_mxfp4():
+    g = _golden("vs_worked_example.json")
+    x = np.zeros(32, np.float32)
+    x[:8] = g["values"]
+    codes, scales, _ = oracle.quantize(x, oracle.MXFP4)
+    assert scales.shape == (1, 1)
+    assert oracle.e8m0_decode(int(scales[0, 0])) == g["mxfp4"]["scale"]
+    y = oracle.dequantize(codes, scales, oracle.MXFP4)[0]
+    assert np.array_equal(y[:8], np.array(g["mxfp4"]["reconstruction_printed"], np.float32)), y[:8]
+    assert np.all(y[8:] == 0)
+    # the scaled values the page prints (x / s) round onto the same grid points
+    sv = np.array(g["mxfp4"]["scaled_values_printed"])
+    assert np.allclose(sv, np.array(g["values"]) / g["mxfp4"]["scale"], atol=1e-9)
+
+
+def check_worked_example_nvfp4():
+    g = _golden("vs_worked_example.json")
+    x = np.zeros(16, np.float32)
+    x[:8] = g["values"]
+    codes, scales, ts = oracle.quantize(x, oracle.NVFP4)
+    assert ts == np.float32(2.6) / np.float32(2688.0)
+    s = oracle.e4m3_decode(int(scales[0, 0])) * float(ts)
+    assert scales[0, 0] == 0x7E                              # 2.6 maps onto 6 exactly
+    assert abs(s - g["nvfp4"]["scale_approx"]) < 5e-4
+    y = oracle.dequantize(codes, scales, oracle.NVFP4, ts)[0]
+    d = g["nvfp4"]["printed_decimals"]
+    assert np.array_equal(np.round(y[:8].astype(np.float64), d),
+                          np.array(g["nvfp4"]["reconstruction_printed"])), y[:8]
+    assert np.all(y[8:] == 0)
+    # the printed scaled values (x / s, 2 decimals) round to the grid points used
+    sv = np.array(g["nvfp4"]["scaled_values_printed"])
+    assert np.allclose(np.array(g["values"]) / s, sv, atol=0.006)
+
+
+def check_emulation_table():
+    g = _golden("vs_emulation_table.json")
+    r = np.random.default_rng(0)
+    n = 1 << 20
+    gauss = r.standard_normal(n)
+    outl = r.standard_normal(n) * (1 + 9 * (r.random(n) < 0.002))
+    data = {"gaussian": gauss, "outliers": outl}
+    for row in g["rows"]:
+        x = data[row["data"]]
+        fmt = oracle.MXFP4 if row["format"] == "MXFP4" else oracle.NVFP4
+        c, s, ts = oracle.quantize(x.astype(np.float32), fmt)
+        y = oracle.dequantize(c, s, fmt, ts).reshape(-1)
+        # MSE and SQNR from the oracle's error sums (the input is the fp32 copy
+        # the oracle quantized; the float64 -> fp32 cast moves no printed digit)
+        se, sx, _, _ = oracle.error_sums(x.astype(np.float32), y)
+        mse = se / n
+        sqnr = 10 * np.log10(sx / se)
+        assert round(mse, 5) == row["mse"], (row, mse)
+        assert round(sqnr, 2) == row["sqnr_db"], (row, sqnr)
+
+
+# ------------------------------------------------------------------ Hadamard
+def check_hadamard_matches_sylvester():
+    for n in (16, 32):
+        H = scipy.linalg.hadamard(n).astype(np.float64)
+        eye = np.eye(n, dtype=np.float32)
+        R = oracle.rotate(eye, n).astype(np.float64)          # row j = e_j H / sqrt(n)
+        assert np.allclose(R, H / np.sqrt(n), rtol=0, atol=1e-7), n
+        assert np.allclose(R @ R.T, np.eye(n), atol=1e-6)
+        ones = np.ones((1, n), np.float32)
+        v = oracle.rotate(ones, n)[0]
+        assert abs(v[0] - np.sqrt(n)) < 1e-5 and np.all(np.abs(v[1:]) < 1e-6)
+
+
+def check_hadamard_involution_and_norm():
+    x = workloads.laplace(workloads.rng(13, 13), 64 * 96, 1.0).astype(np.float32).reshape(64, 96)
+    for n in (16, 32):
+        y = oracle.rotate(x, n)
+        z = oracle.rotate(y, n)
+        assert np.allclose(z, x, rtol=0, atol=1e-5)
+        # per block norm preservation
+        xb = x.reshape(64, -1, n).astype(np.float64)
+        yb = y.reshape(64, -1, n).astype(np.float64)
+        assert np.allclose((xb ** 2).sum(-1), (yb ** 2).sum(-1), rtol=1e-6)
+        # the transform is block-local: a change in block b only moves block b
+        x2 = x.copy()
+        x2[:, 5] += 1.0
+        d = np.abs(oracle.rotate(x2, n) - y) > 0
+        assert not d[:, n:].any() and d[:, :n].all()
+
+
+# --------------------------------------------------------------- quantizer
+def _bf16_f32(bits):
+    return workloads.bf16_bits_to_f32(bits)
+
+
+def check_mx_idempotent():
+    for x in (workloads.cfg1_tensor(3),
+              _bf16_f32(workloads.cfg2_tensor("laplace", 3, rows=64, cols=512)),
+              _bf16_f32(workloads.cfg2_tensor("gauss", 4, rows=64, cols=512))):
+        for rot in (False, True):
+            c, s, _ = oracle.quantize(x, oracle.MXFP4, rotate=rot)
+            y = oracle.dequantize(c, s, oracle.MXFP4)
+            c2, s2, _ = oracle.quantize(y, oracle.MXFP4)
+            assert np.array_equal(c, c2) and np.array_equal(s, s2)
+
+
+def check_nv_idempotent_on_normal_scales():
+    x = _bf16_f32(workloads.cfg2_tensor("laplace", 5, rows=64, cols=512))
+    for rot in (False, True):
+        c, s, ts = oracle.quantize(x, oracle.NVFP4, rotate=rot)
+        y = oracle.dequantize(c, s, oracle.NVFP4, ts)
+        c2, s2, _ = oracle.quantize(y, oracle.NVFP4, ts=ts)
+        normal = s >= 0x08
+        assert normal.mean() > 0.9
+        assert np.array_equal(s[normal], s2[normal])
+        cb = c.reshape(c.shape[0], -1, 8)
+        cb2 = c2.reshape(c.shape[0], -1, 8)
+        assert np.array_equal(cb[normal], cb2[normal])
+
+
+def check_invariants():
+    x = _bf16_f32(workloads.cfg2_tensor("laplace", 6, rows=128, cols=1024))
+    # MX: every nonzero block whose exponent is not clamped holds a code of
+    # magnitude 4 or 6 (the scaled block maximum lies in [4, 8)).
+    c, s, _ = oracle.quantize(x, oracle.MXFP4)
+    mags = np.stack([c & 7, c >> 4 & 7], -1).reshape(c.shape[0], -1, 32)
+    top = mags.max(-1)
+    live = s > 0
+    assert np.all(np.isin(top[live], [6, 7]))
+    # scale codes are monotone in the block amax
+    amax = np.abs(x.reshape(x.shape[0], -1, 32)).max(-1).reshape(-1)
+    order = np.argsort(amax, kind="stable")
+    assert np.all(np.diff(s.reshape(-1)[order].astype(int)) >= 0)
+    # NV: the block holding the tensor amax gets scale code 0x7E (448) and an
+    # element of magnitude 6; every scale code is <= 0x7E.
+    c, s, ts = oracle.quantize(x, oracle.NVFP4)
+    assert ts == np.float32(np.abs(x).max()) / np.float32(2688.0)
+    flat = np.abs(x).reshape(x.shape[0], -1, 16)
+    r, b = np.unravel_index(np.argmax(flat.max(-1)), flat.shape[:2])
+    assert s[r, b] == 0x7E and s.max() == 0x7E
+    blk = np.stack([c & 15, c >> 4], -1).reshape(c.shape[0], -1, 16)[r, b]
+    assert (blk & 7).max() == 7
+    amax = flat.max(-1).reshape(-1)
+    order = np.argsort(amax, kind="stable")
+    assert np.all(np.diff(s.reshape(-1)[order].astype(int)) >= 0)
+
+
+def check_brute_force_codes_tiny_blocks():
+    """At a fixed scale, the code vector that minimises the block SSE over all
+    16^n candidates is the element-wise nearest grid point; the oracle's codes
+    must be a minimiser (and equal to it wherever the minimiser is unique)."""
+    g = workloads.rng(14, 14)
+    allv = np.array([oracle.e2m1_decode(c) for c in range(16)])
+    for trial in range(60):
+        n = 3
+        x = g.laplace(0, 1, n).astype(np.float32)
+        xb = np.zeros(32, np.float32)
+        xb[:n] = x
+        c, s, _ = oracle.quantize(xb, oracle.MXFP4)
+        sv = oracle.e8m0_decode(int(s[0, 0]))
+        codes = np.stack([c[0] & 15, c[0] >> 4], -1).reshape(-1)[:n]
+        # brute force over every code vector
+        grid = np.array(np.meshgrid(*[np.arange(16)] * n, indexing="ij")).reshape(n, -1)
+        recon = allv[grid] * sv
+        sse = ((recon - x[:, None].astype(np.float64)) ** 2).sum(0)
+        best = sse.min()
+        mine = ((allv[codes] * sv - x.astype(np.float64)) ** 2).sum()
+        assert mine <= best * (1 + 1e-12) + 1e-300, (x, codes)
+        # the absmax exponent is never worse than saturating everything
+        assert mine <= ((x.astype(np.float64)) ** 2).sum() + 1e-12
+
+
+def check_absmax_scale_vs_best_scale():
+    """The absmax exponent is within one step of the SSE-optimal E8M0 exponent on
+    Laplace blocks, and the optimum is below absmax+2 (the scale that maps the
+    block maximum below 4 only loses resolution)."""
+    g = workloads.rng(15, 15)
+    allv = np.array([oracle.e2m1_decode(c) for c in range(8)])
+    for _ in range(200):
+        x = g.laplace(0, 1, 32).astype(np.float32)
+        c, s, _ = oracle.quantize(x, oracle.MXFP4)
+        e0 = int(s[0, 0]) - 127
+        sses = {}
+        for e in range(e0 - 3, e0 + 4):
+            sv = 2.0 ** e
+            a = np.abs(x) / sv
+            q = allv[np.abs(np.minimum(a, 6)[:, None] - allv).argmin(-1)]
+            sses[e] = ((np.sign(x) * q * sv - x) ** 2).sum()
+        best = min(sses, key=sses.get)
+        assert best in (e0, e0 + 1), (e0, sses)
+
+
+def check_directional_rotation():
+    """Under RTN, a group-sized Hadamard lowers MXFP4 error on Laplace data and
+    raises NVFP4 error ("rotations improve MXFP4 accuracy, but hurt NVFP4")."""
+    x = workloads.laplace(workloads.rng(16, 16), 1 << 18, 1.0).astype(np.float32).reshape(256, 1024)
+    res = {}
+    for fmt in (oracle.MXFP4, oracle.NVFP4):
+        for rot in (False, True):
+            c, s, ts = oracle.quantize(x, fmt, rotate=rot)
+            y = oracle.dequantize(c, s, fmt, ts, inverse_rotate=rot)
+            res[fmt, rot] = oracle.nmse(x, y)
+    assert res[oracle.MXFP4, True] < res[oracle.MXFP4, False] * 0.95, res
+    assert res[oracle.NVFP4, True] > res[oracle.NVFP4, False] * 1.02, res
+
+
+def check_nmse_domains_agree():
+    """The rotation is orthogonal, so the error measured in the rotated domain
+    equals the error in the original domain (eq. (2) of the portable-FP4 page)."""
+    x = _bf16_f32(workloads.cfg3_tensor(7, rows=32, cols=1024))
+    for fmt in (oracle.MXFP4, oracle.NVFP4):
+        c, s, ts = oracle.quantize(x, fmt, rotate=True)
+        y_rot = oracle.dequantize(c, s, fmt, ts)
+        y_orig = oracle.dequantize(c, s, fmt, ts, inverse_rotate=True)
+        xr = oracle.rotate(x, oracle.BLOCK[fmt])
+        a = oracle.nmse(xr, y_rot)
+        b = oracle.nmse(x, y_orig)
+        assert abs(a - b) <= 1e-5 * a, (a, b)
+        assert 0 < oracle.cosine(x, y_orig) <= 1.0
+
+
+def check_error_sums_closed_form():
+    """Hand-computed sums: x = (3, 4, 0, -1), x^ = (0, 4, 1, -2)."""
+    x = np.array([3, 4, 0, -1], np.float32)
+    xh = np.array([0, 4, 1, -2], np.float32)
+    se, sx, sxy, sy = oracle.error_sums(x, xh)
+    assert (se, sx, sxy, sy) == (9 + 0 + 1 + 1, 9 + 16 + 0 + 1, 0 + 16 + 0 + 2, 0 + 16 + 1 + 4)
+    assert oracle.nmse(x, xh) == 11 / 26
+    assert abs(oracle.cosine(x, xh) - 18 / np.sqrt(26 * 21)) < 1e-15
+    assert oracle.cosine(x, 2 * x) == 1.0
+
+
+def check_zero_and_tiny_inputs():
+    z = np.zeros((2, 64), np.float32)
+    c, s, _ = oracle.quantize(z, oracle.MXFP4)
+    assert np.all(c == 0) and np.all(s == 0)
+    c, s, ts = oracle.quantize(z, oracle.NVFP4)
+    assert ts == 0 and np.all(c == 0) and np.all(s == 0)
+    assert np.all(oracle.dequantize(c, s, oracle.NVFP4, ts) == 0)
+    # one zero block inside a live tensor
+    x = np.zeros((1, 64), np.float32)
+    x[0, 40] = 3.0
+    c, s, ts = oracle.quantize(x, oracle.NVFP4)
+    assert s[0, 0] == 0 and s[0, 1] == 0 and s[0, 2] == 0x7E
+    c, s, _ = oracle.quantize(x, oracle.MXFP4)
+    assert s[0, 0] == 0 and s[0, 1] == 126          # floor(log2 3) - 2 = -1
+    # tiny values clamp the exponent at -127 and stay representable
+    t = np.full((1, 32), 2.0 ** -130, np.float32)
+    c, s, _ = oracle.quantize(t, oracle.MXFP4)
+    assert s[0, 0] == 0
+    y = oracle.dequantize(c, s, oracle.MXFP4)
+    assert np.allclose(y, t, rtol=0.5)
+
+
+# --------------------------------------------------------------------- GEMM
+def _decode_codes(codes: np.ndarray) -> np.ndarray:
+    """Signed grid values of packed codes (low nibble first), from the value
+    set of the format definitions."""
+    lo = codes & 15
+    hi = codes >> 4
+    c = np.stack([lo, hi], -1).reshape(codes.shape[0], -1)
+    v = GRID[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def check_gemm_integer_closed_form():
+    """K = 32 with every E8M0 code 127 (scale 1): twice every grid value is an
+    integer, so y = (1/4) * (2A)(2B)^T exactly, in integer arithmetic."""
+    g = workloads.rng(17, 17)
+    M, N, K = 9, 7, 32
+    ac = g.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    bc = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asc = np.full((M, 1), 127, np.uint8)
+    bsc = np.full((N, 1), 127, np.uint8)
+    y, ab = oracle.gemm_full(oracle.MXFP4, K, ac, asc, 0, bc, bsc, 0)
+    A2 = (2 * _decode_codes(ac)).astype(np.int64)
+    B2 = (2 * _decode_codes(bc)).astype(np.int64)
+    assert np.array_equal(y * 4, (A2 @ B2.T).astype(np.float64))
+    assert np.array_equal(ab * 4, (np.abs(A2) @ np.abs(B2).T).astype(np.float64))
+
+
+def check_gemm_block_scaled_closed_form():
+    """Random E8M0 / E4M3 scales: y = sum over K-blocks of scaleA*scaleB times an
+    integer block dot product (NVFP4: times tsA * tsB), computed block-wise in
+    numpy from the format definitions; also y(A, B) = y(B, A)^T."""
+    g = workloads.rng(18, 18)
+    vals = _e4m3_values_from_definition()
+    for fmt, G in ((oracle.MXFP4, 32), (oracle.NVFP4, 16)):
+        M, N, K = 6, 5, 256
+        ac = g.integers(0, 256, (M, K // 2), dtype=np.uint8)
+        bc = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        if fmt == oracle.MXFP4:
+            asc = g.integers(110, 140, (M, K // G), dtype=np.uint8)
+            bsc = g.integers(110, 140, (N, K // G), dtype=np.uint8)
+            sa = np.exp2(asc.astype(np.float64) - FMT["e8m0_bias"])
+            sb = np.exp2(bsc.astype(np.float64) - FMT["e8m0_bias"])
+            ta, tb = 0.0, 0.0
+            gs = 1.0
+        else:
+            asc = g.integers(1, 127, (M, K // G), dtype=np.uint8)
+            bsc = g.integers(1, 127, (N, K // G), dtype=np.uint8)
+            sa, sb = vals[asc], vals[bsc]
+            ta, tb = np.float32(0.0123), np.float32(3.5e-4)
+            gs = float(ta) * float(tb)
+        y, ab = oracle.gemm_full(fmt, K, ac, asc, ta, bc, bsc, tb)
+        A2 = (2 * _decode_codes(ac)).astype(np.int64).reshape(M, K // G, G)
+        B2 = (2 * _decode_codes(bc)).astype(np.int64).reshape(N, K // G, G)
+        blockdot = np.einsum("mbg,nbg->mnb", A2, B2).astype(np.float64) / 4
+        absdot = np.einsum("mbg,nbg->mnb", np.abs(A2), np.abs(B2)).astype(np.float64) / 4
+        ref = (blockdot * sa[:, None, :] * sb[None, :, :]).sum(-1) * gs
+        refa = (absdot * sa[:, None, :] * sb[None, :, :]).sum(-1) * abs(gs)
+        assert np.allclose(y, ref, rtol=1e-12, atol=0), fmt
+        assert np.allclose(ab, refa, rtol=1e-12, atol=0), fmt
+        yt, _ = oracle.gemm_full(fmt, K, bc, bsc, tb, ac, asc, ta)
+        assert np.array_equal(yt, y.T)
+        # a row-local change in A moves only that row of Y
+        ac2 = ac.copy()
+        ac2[2, 3] ^= 0x11
+        y2, _ = oracle.gemm_full(fmt, K, ac2, asc, ta, bc, bsc, tb)
+        assert np.array_equal(np.delete(y2, 2, 0), np.delete(y, 2, 0))
+
+
+def check_gemm_rotation_convention():
+    """Q(X H) Q(W H)^T approximates X W^T: the block Hadamard is orthogonal, so
+    rotating both operands along K leaves the product unchanged before
+    quantization and close to it after."""
+    X = _bf16_f32(workloads.gemm_activation(16, 512, 8))
+    W = _bf16_f32(workloads.gemm_weight(24, 512, 8))
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    for fmt in (oracle.MXFP4, oracle.NVFP4):
+        G = oracle.BLOCK[fmt]
+        Xr = oracle.rotate(X, G).astype(np.float64)
+        Wr = oracle.rotate(W, G).astype(np.float64)
+        assert np.allclose(Xr @ Wr.T, ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+        ca, sa, ta = oracle.quantize(X, fmt, rotate=True)
+        cb, sb, tb = oracle.quantize(W, fmt, rotate=True)
+        y, ab = oracle.gemm_full(fmt, 512, ca, sa, ta, cb, sb, tb)
+        rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+        assert rel < 0.2, (fmt, rel)
+
+
+def check_sizes():
+    """Bits per element: 4.25 (MXFP4) and 4.5 (NVFP4) from codes plus scales."""
+    x = np.ones((4, 256), np.float32)
+    for fmt, key in ((oracle.MXFP4, "mxfp4"), (oracle.NVFP4, "nvfp4")):
+        c, s, _ = oracle.quantize(x, fmt)
+        bits = 8 * (c.nbytes + s.nbytes) / x.size
+        assert bits == FMT[key]["bits_per_element"]
+        assert 8 * (c.nbytes + s.nbytes) / (x.size / FMT[key]["block"]) == FMT[key]["bits_per_block"]
+
+
+ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

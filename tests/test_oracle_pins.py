@@ -1,0 +1,70 @@
+"""CPU-only pins of the oracle (no GPU).  See ``oracle_checks.py`` for what each
+check compares the oracle against."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_checks as oc
+
+CHECKS = oc.ALL_CHECKS
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
+def test_oracle_pin(check):
+    check()
+
+
+# Plausible mistakes, planted in a copy of the oracle's source.  Each mutant is
+# (description, text in fp4_oracle.c, replacement).  Every one of them must make
+# at least one pin fail; otherwise the pins would not be pinning that part.
+MUTANTS = [
+    ("mx exponent off by one", "int e = (E - 1) - 2;", "int e = (E - 1) - 1;"),
+    ("e2m1 ties away from even", "if (d < bestd || (d == bestd && (c & 1) == 0)) {\n            best = c;\n            bestd = d;\n        }\n    }\n    return (neg << 3) | best;",
+     "if (d < bestd || (d == bestd && (c & 1) == 1)) {\n            best = c;\n            bestd = d;\n        }\n    }\n    return (neg << 3) | best;"),
+    ("e2m1 subnormal step", "mag = 0.5 * man;", "mag = 1.0 * man;"),
+    ("e2m1 exponent bias", "mag = ldexp(1.0 + 0.5 * man, exp_field - 1);", "mag = ldexp(1.0 + 0.5 * man, exp_field);"),
+    ("e4m3 subnormal step", "mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    ("e4m3 bias", "mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
+    ("e4m3 ties", "if (d < bestd || (d == bestd && (c & 1) == 0)) {\n            best = c;\n            bestd = d;\n        }\n    }\n    return best;",
+     "if (d < bestd) {\n            best = c;\n            bestd = d;\n        }\n    }\n    return best;"),
+    ("nv tensor scale forgets the 6", "tsv = gamax / 2688.0f;", "tsv = gamax / 448.0f;"),
+    ("nv block scale order", "float t = (amax / 6.0f) / tsv;", "float t = amax / (6.0f * tsv) * 1.0001f;"),
+    ("nv dequant drops tensor scale", "dst[r * cols + k] = inner * ts;", "dst[r * cols + k] = inner;"),
+    ("nibble order swapped", "if ((k & 1) == 0)\n        row_codes[k >> 1]", "if ((k & 1) == 1)\n        row_codes[k >> 1]"),
+    ("hadamard sign pattern", "(unsigned)(i & j)", "(unsigned)(i | j)"),
+    ("hadamard normalisation", "yb[j] = (float)(s / root);", "yb[j] = (float)(s / n);"),
+    ("block amax without abs", "float a = fabsf(v[i]);", "float a = v[i];"),
+    ("mx clamp", "if (e < -127)\n        e = -127;", "if (e < -126)\n        e = -126;"),
+    ("gemm drops a sign", "s += av * bv;", "s += av * fabs(bv);"),
+    ("gemm forgets tensor scales", "s *= g;", "s *= 1.0;"),
+    ("gemm transposed scale index", "bv *= ora_e8m0_decode(bs[k / G]);", "bv *= ora_e8m0_decode(as[k / G]);"),
+    ("error sums drop a term", "se += (a - b) * (a - b);", "se += (a - b) * (a - b) * 0.5;"),
+]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(mutant):
+    name, old, new = mutant
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, "mutant anchor must be unique: " + name
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "mut.c")
+        so = os.path.join(d, "libmut.so")
+        with open(c, "w") as f:
+            f.write(src.replace(old, new))
+        subprocess.check_call(["gcc", *oracle.CFLAGS, "-o", so, c, "-lm"])
+        oracle.use_library(so)
+        failed = []
+        try:
+            for chk in CHECKS:
+                try:
+                    chk()
+                except AssertionError:
+                    failed.append(chk.__name__)
+                    break
+        finally:
+            oracle.use_library(None)
+    assert failed, "no pin caught the planted mistake: " + name
