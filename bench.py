@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X microscaling-FP4 hot path; prints ONE JSON line.
+
+Timed step (``value``): one pass of block-wise FP4 quantization over the
+4096x4096 bf16 workload in all its variants -- two seeded distributions
+(Gaussian std 0.02; Laplace b=0.02 with 16 of 4096 columns x50) x {MXFP4,
+NVFP4} x {no rotation, block Hadamard of the block size}.  NVFP4 runs its
+global-amax pass and its quantize pass as separate launches.  Inputs are
+resident in HBM; the step cycles through several copies of every input and
+output so that the 256 MB last-level cache cannot serve a repeat.
+
+``value`` = algorithmic bytes of the step (bf16 read once + codes + scales)
+divided by the step time, in GB/s.  ``roofline`` reports the kernel that takes
+the most time in the step, timed with HIP events on the launching stream.
+
+Also reported in the same line: NMSE of every variant (GPU, and oracle vs GPU
+on a sample), the oracle's own throughput on a bounded sample
+(``cpu_baseline``), and the GEMM measurements (Llama-3-8B and Llama-3-70B
+linear shapes, MXFP4 on the scaled MFMA and NVFP4 on the dequantize-to-fp16
+path, plus the layer-wise speedup of quantize+GEMM over torch's bf16 GEMM).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12         # B/s, MI355X HBM3E
+PEAK_FP4 = 10.1e15        # dense MXFP4 MFMA, flop/s
+PEAK_F16 = 2.5e15         # dense fp16/bf16 MFMA, flop/s
+METRIC = "quant GB/s (% HBM peak); FP4 GEMM TFLOPS (% MFMA peak); NMSE vs oracle"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gemm-iters", type=int, default=10)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (quantization "
+              "shards by rows with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp4_microscaling_quantization_amd as fp4
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    fp4.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    # ------------------------------------------------------------ workload
+    rows, cols = 4096, 4096
+    n = rows * cols
+    t0 = time.time()
+    host = {d: workloads.cfg2_tensor(d, 0) for d in ("gauss", "laplace")}
+    log("host inputs %.1fs" % (time.time() - t0))
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    copies = max(1, args.copies)
+    xs = {}
+    for d, b in host.items():
+        base = to_dev(b)
+        xs[d] = [base] + [base.clone() for _ in range(copies - 1)]
+
+    variants = [(d, fmt, rot) for d in ("gauss", "laplace")
+                for fmt in (fp4.FMT_MXFP4, fp4.FMT_NVFP4) for rot in (False, True)]
+    FN = {fp4.FMT_MXFP4: "mxfp4", fp4.FMT_NVFP4: "nvfp4"}
+
+    def vname(v):
+        return "%s/%s/%s" % (v[0], FN[v[1]], "h%d" % fp4.BLOCK[v[1]] if v[2] else "plain")
+
+    outs = {}
+    for v in variants:
+        d, fmt, rot = v
+        lay = fp4.SCALES_GEMM if fmt == fp4.FMT_MXFP4 else fp4.SCALES_ROWMAJOR
+        cfg = fp4.qconfig(fmt, rot, lay)
+        lst = []
+        for c in range(copies):
+            codes = torch.empty(fp4.fp4_codes_bytes(rows, cols), dtype=torch.uint8, device=dev)
+            scales = torch.empty(fp4.fp4_scales_bytes(cfg, rows, cols), dtype=torch.uint8, device=dev)
+            gs = torch.zeros(1, dtype=torch.float32, device=dev)
+            lst.append(fp4.Quantized(codes, scales, gs, cfg, rows, cols))
+        outs[v] = lst
+    ws = torch.zeros(256, dtype=torch.uint8, device=dev)
+
+    def alg_bytes(fmt):
+        G = fp4.BLOCK[fmt]
+        return n * 2 + n // 2 + n // G
+
+    # kernel labels as rocprofv3 names them
+    def klabel(kind, rot):
+        return "%s<bf16,%s>" % (kind, "rot" if rot else "plain")
+
+    def run_step(c, events):
+        for v in variants:
+            d, fmt, rot = v
+            x = xs[d][c]
+            q = outs[v][c]
+            if fmt == fp4.FMT_NVFP4:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e2 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = fp4.fp4_global_scale(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                          q.global_scale.data_ptr(), ws.data_ptr(), 256, sh)
+                e1.record(stream)
+                rc |= fp4.fp4_quantize(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                       q.codes.data_ptr(), q.scales.data_ptr(),
+                                       q.global_scale.data_ptr(), fp4.GS_GIVEN, None, 0, sh)
+                e2.record(stream)
+                if events is not None:
+                    events.append((klabel("amax_nv_kernel", rot), n * 2, e0, e1))
+                    events.append((klabel("quant_nv_kernel", rot), alg_bytes(fmt), e1, e2))
+            else:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = fp4.fp4_quantize(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                      q.codes.data_ptr(), q.scales.data_ptr(), None,
+                                      fp4.GS_COMPUTE, None, 0, sh)
+                e1.record(stream)
+                if events is not None:
+                    events.append((klabel("quant_mx_kernel", rot), alg_bytes(fmt), e0, e1))
+            if rc != 0:
+                raise RuntimeError("quantize failed: %d" % rc)
+
+    for w in range(args.warmup):
+        run_step(w % copies, None)
+    torch.cuda.synchronize()
+    events = []
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        run_step(s % copies, events)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    step_s = (t_end - t_start) / max(1, args.steps)
+    step_bytes = sum(alg_bytes(v[1]) for v in variants)
+    value_gbs = step_bytes / step_s / 1e9
+
+    # per-kernel durations from the events
+    per = {}
+    for label, nbytes, a, b in events:
+        ms = a.elapsed_time(b)
+        t = per.setdefault(label, [0.0, 0, nbytes])
+        t[0] += ms
+        t[1] += 1
+    kern = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1], "alg_bytes": v[2],
+                "gbs": v[2] / (1e-3 * v[0] / v[1]) / 1e9} for k, v in per.items()}
+    dom = max(kern, key=lambda k: kern[k]["avg_us"] * kern[k]["launches"])
+    dk = kern[dom]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dk["gbs"], 1),
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(dk["gbs"] * 1e9 / PEAK_HBM, 4),
+                "traffic": None, "alg_bytes_per_launch": dk["alg_bytes"],
+                "avg_launch_us": round(dk["avg_us"], 3)}
+    log("step %.3f ms, %.1f GB/s; dominant %s %.2f us" % (1e3 * step_s, value_gbs, dom, dk["avg_us"]))
+
+    # -------------------------------------------------------------- NMSE
+    nmse = {}
+    for v in variants:
+        d, fmt, rot = v
+        q = outs[v][0]
+        sums = fp4.error_sums(xs[d][0], q).cpu().numpy()
+        nmse[vname(v)] = {"gpu_full": float(sums[0] / sums[1])}
+
+    # -------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        sample_rows = 256
+        t_or = 0.0
+        b_or = 0
+        for v in variants:
+            d, fmt, rot = v
+            xh = workloads.bf16_bits_to_f32(host[d][:sample_rows])
+            t1 = time.perf_counter()
+            c_, s_, ts_ = oracle.quantize(xh, fmt, rotate=rot)
+            t_or += time.perf_counter() - t1
+            b_or += sample_rows * cols * 2 + sample_rows * cols // 2 + sample_rows * cols // fp4.BLOCK[fmt]
+            # NMSE of the same sample, oracle vs GPU
+            ref = oracle.dequantize(c_, s_, fmt, ts_, inverse_rotate=rot)
+            o_nmse = oracle.nmse(xh, ref)
+            xd = to_dev(np.ascontiguousarray(host[d][:sample_rows]))
+            qg = fp4.quantize(xd, fmt, rotate=rot)
+            sg = fp4.error_sums(xd, qg).cpu().numpy()
+            nmse[vname(v)].update({"oracle_sample": o_nmse, "gpu_sample": float(sg[0] / sg[1])})
+        cpu = {"value": round(b_or / t_or / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "rows 0..%d of each of the 8 variants (%d elements each), single-threaded "
+                         "plain-C oracle, one pass; same algorithmic bytes as the GPU line"
+                         % (sample_rows - 1, sample_rows * cols),
+               "seconds": round(t_or, 2)}
+        log("cpu baseline %.4f GB/s over %.1fs" % (cpu["value"], t_or))
+
+    # --------------------------------------------------------------- GEMM
+    gemm = None
+    if not args.no_gemm:
+        gemm = bench_gemm(args, torch, fp4, workloads, dev, stream)
+
+    line = {
+        "metric": METRIC, "value": round(value_gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * step_s, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "quantize 4096x4096 bf16 x {Gaussian 0.02, Laplace 0.02 + 16/4096 "
+                               "cols x50} x {MXFP4 G32, NVFP4 G16 (+global amax pass)} x {plain, "
+                               "block Hadamard 32/16}", "rows": rows, "cols": cols,
+                   "variants": len(variants), "buffer_copies": copies,
+                   "step_alg_bytes": step_bytes},
+        "frac_hbm_step": round(value_gbs * 1e9 / PEAK_HBM, 4),
+        "roofline": roofline,
+        "kernels": {k: {"avg_us": round(v["avg_us"], 3), "gbs": round(v["gbs"], 1),
+                        "frac": round(v["gbs"] * 1e9 / PEAK_HBM, 4)} for k, v in sorted(kern.items())},
+        "cpu_baseline": cpu,
+        "nmse": nmse,
+        "gemm": gemm,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_gemm(args, torch, fp4, workloads, dev, stream):
+    res = {}
+    iters = max(1, args.gemm_iters)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def time_it(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us
+
+    def quant_copies(x_bf16, fmt, rot, ncopy):
+        q0 = fp4.quantize(x_bf16, fmt, rotate=rot, scale_layout=fp4.SCALES_GEMM)
+        out = [q0]
+        for _ in range(ncopy - 1):
+            out.append(fp4.Quantized(q0.codes.clone(), q0.scales.clone(), q0.global_scale.clone(),
+                                     q0.cfg, q0.rows, q0.cols))
+        return out
+
+    # Llama-3-8B linears at M = 4096 (MXFP4, H32), plus the bf16 reference
+    M = 4096
+    for (K, N) in [(4096, 4096), (4096, 6144), (4096, 14336), (14336, 4096)]:
+        t0 = time.time()
+        w = to_dev(workloads.gemm_weight(N, K, seed=0))
+        a = to_dev(workloads.gemm_activation(M, K, seed=0))
+        qw = quant_copies(w, fp4.FMT_MXFP4, True, 2)
+        qa = fp4.quantize(a, fp4.FMT_MXFP4, rotate=True, scale_layout=fp4.SCALES_GEMM)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        wsb = fp4.fp4_gemm_workspace_bytes(fp4.FMT_MXFP4, M, N, K)
+        gw = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+
+        def g(i=0):
+            fp4.gemm(qa, qw[i % 2], out=y, workspace=gw if wsb else None)
+
+        def qfn(i=0):
+            fp4.quantize(a, fp4.FMT_MXFP4, rotate=True, scale_layout=fp4.SCALES_GEMM, out=qa)
+
+        def layer(i=0):
+            qfn()
+            g(i)
+
+        wt = w.t().contiguous()
+
+        def bf(i=0):
+            torch.mm(a, wt, out=y)
+
+        us_g = time_it(g, iters)
+        us_q = time_it(qfn, iters)
+        us_l = time_it(layer, iters)
+        us_b = time_it(bf, iters)
+        fl = 2.0 * M * N * K
+        res["llama8b_M%d_K%d_N%d" % (M, K, N)] = {
+            "fmt": "mxfp4+h32", "gemm_us": round(us_g, 2), "tflops": round(fl / us_g / 1e6, 1),
+            "frac_fp4_peak": round(fl / (us_g * 1e-6) / PEAK_FP4, 4),
+            "act_quant_us": round(us_q, 2), "layer_us": round(us_l, 2),
+            "bf16_torch_us": round(us_b, 2), "layer_speedup_vs_bf16": round(us_b / us_l, 2)}
+        del w, a, qw, qa, y, wt
+        log("gemm 8b K%d N%d %.1f us (%.0fs)" % (K, N, us_g, time.time() - t0))
+
+    # Llama-3-70B MLP linears on one GPU, MXFP4 (H32) and NVFP4 (H16)
+    for (K, N) in [(8192, 28672), (28672, 8192)]:
+        t0 = time.time()
+        w = to_dev(workloads.gemm_weight(N, K, seed=1))
+        wt = w.t().contiguous()
+        amax = to_dev(workloads.gemm_activation(8192, K, seed=1, outlier_frac=0.001))
+        for fmt in (fp4.FMT_MXFP4, fp4.FMT_NVFP4):
+            fname = "mxfp4+h32" if fmt == fp4.FMT_MXFP4 else "nvfp4+h16"
+            qw = quant_copies(w, fmt, True, 4)
+            wbytes = qw[0].codes.numel() + qw[0].scales.numel()
+            for Mm in (1, 16, 128, 8192):
+                a = amax[:Mm]
+                qa = fp4.quantize(a, fmt, rotate=True, scale_layout=fp4.SCALES_GEMM)
+                y = torch.empty(Mm, N, dtype=torch.bfloat16, device=dev)
+                wsb = fp4.fp4_gemm_workspace_bytes(fmt, Mm, N, K)
+                gw = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+
+                def g(i=0):
+                    fp4.gemm(qa, qw[i % 4], out=y, workspace=gw if wsb else None)
+
+                def layer(i=0):
+                    fp4.quantize(a, fmt, rotate=True, scale_layout=fp4.SCALES_GEMM, out=qa)
+                    g(i)
+
+                def bf(i=0):
+                    torch.mm(a, wt, out=y)
+
+                us_g = time_it(g, iters)
+                us_l = time_it(layer, iters)
+                us_b = time_it(bf, iters) if fmt == fp4.FMT_MXFP4 else None
+                fl = 2.0 * Mm * N * K
+                peak = PEAK_FP4 if fmt == fp4.FMT_MXFP4 else PEAK_F16
+                traffic = wbytes + qa.codes.numel() + qa.scales.numel() + Mm * N * 2
+                ent = {"fmt": fname, "gemm_us": round(us_g, 2),
+                       "tflops": round(fl / us_g / 1e6, 2),
+                       "frac_mfma_peak": round(fl / (us_g * 1e-6) / peak, 4),
+                       "alg_gbs": round(traffic / us_g / 1e3, 1),
+                       "frac_hbm": round(traffic / (us_g * 1e-6) / PEAK_HBM, 4),
+                       "layer_us": round(us_l, 2)}
+                if us_b is not None:
+                    ent["bf16_torch_us"] = round(us_b, 2)
+                    ent["layer_speedup_vs_bf16"] = round(us_b / us_l, 2)
+                res["llama70b_%s_M%d_K%d_N%d" % (fname.split("+")[0], Mm, K, N)] = ent
+                log("gemm 70b %s M%d K%d N%d %.1f us" % (fname, Mm, K, N, us_g))
+            del qw
+        del w, wt, amax
+        log("70b shape done (%.0fs)" % (time.time() - t0))
+    return res
+
+
+if __name__ == "__main__":
+    main()

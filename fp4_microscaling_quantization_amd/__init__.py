@@ -1,0 +1,327 @@
+"""MI355X (gfx950) microscaling FP4: Python binding over ``libfp4.so``.
+
+The binding only marshals arguments into the C ABI declared in
+``include/fp4.h``; every step of quantization, dequantization, error sums and
+the block-scaled GEMM runs in the library's HIP kernels.  PyTorch supplies
+device memory and the current HIP stream.  There is no fallback: if the library
+is not built, or no GPU is present, the calls raise.
+
+Low-level names mirror the C ABI (``fp4_quantize``, ``fp4_dequantize``,
+``fp4_error_sums``, ``fp4_gemm``, ``fp4_scales_to_gemm_layout`` and the size /
+offset helpers); ``quantize``, ``dequantize``, ``error_sums`` and ``gemm``
+allocate their outputs with torch and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfp4.so")
+
+# enums of include/fp4.h
+FP4_OK = 0
+FP4_ERR_INVALID_ARG = -1
+FP4_ERR_UNSUPPORTED = -2
+FP4_ERR_ALIGNMENT = -3
+FP4_ERR_WORKSPACE = -4
+FP4_ERR_HIP = -5
+FMT_MXFP4 = 0
+FMT_NVFP4 = 1
+DT_F32 = 0
+DT_BF16 = 1
+SCALES_ROWMAJOR = 0
+SCALES_GEMM = 1
+GS_COMPUTE = 0
+GS_GIVEN = 1
+SCALE_ABSMAX = 0
+BLOCK = {FMT_MXFP4: 32, FMT_NVFP4: 16}
+
+EXPORTED = [
+    "fp4_codes_bytes", "fp4_scales_bytes", "fp4_workspace_bytes", "fp4_scale_offset",
+    "fp4_quantize", "fp4_global_scale", "fp4_dequantize", "fp4_error_workspace_bytes", "fp4_error_sums",
+    "fp4_scales_to_gemm_layout", "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_status_str",
+    "fp4_abi_version",
+]
+
+
+class FP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, status_str(status), status))
+
+
+class QConfig(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("block", ctypes.c_int32), ("rotate", ctypes.c_int32),
+                ("rule", ctypes.c_int32), ("scale_layout", ctypes.c_int32)]
+
+
+def qconfig(fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMAJOR) -> QConfig:
+    G = BLOCK[fmt]
+    return QConfig(fmt, G, G if rotate else 0, SCALE_ABSMAX, scale_layout)
+
+
+_lib = None
+
+
+def lib():
+    """Load libfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfp4.so is not built; run __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        CP = ctypes.POINTER(QConfig)
+        L.fp4_codes_bytes.restype = SZ
+        L.fp4_codes_bytes.argtypes = [I64, I64]
+        L.fp4_scales_bytes.restype = SZ
+        L.fp4_scales_bytes.argtypes = [CP, I64, I64]
+        L.fp4_workspace_bytes.restype = SZ
+        L.fp4_workspace_bytes.argtypes = [CP, I64, I64]
+        L.fp4_scale_offset.restype = I64
+        L.fp4_scale_offset.argtypes = [CP, I64, I64, I64, I64]
+        L.fp4_quantize.restype = ctypes.c_int
+        L.fp4_quantize.argtypes = [CP, P, I32, I64, I64, I64, P, P, P, I32, P, SZ, P]
+        L.fp4_global_scale.restype = ctypes.c_int
+        L.fp4_global_scale.argtypes = [CP, P, I32, I64, I64, I64, P, P, SZ, P]
+        L.fp4_dequantize.restype = ctypes.c_int
+        L.fp4_dequantize.argtypes = [CP, P, P, P, I64, I64, P, I32, I64, I32, P]
+        L.fp4_error_workspace_bytes.restype = SZ
+        L.fp4_error_workspace_bytes.argtypes = [CP, I64, I64]
+        L.fp4_error_sums.restype = ctypes.c_int
+        L.fp4_error_sums.argtypes = [CP, P, I32, I64, I64, I64, P, P, P, P, P, SZ, P]
+        L.fp4_scales_to_gemm_layout.restype = ctypes.c_int
+        L.fp4_scales_to_gemm_layout.argtypes = [CP, P, I64, I64, P, P]
+        L.fp4_gemm_workspace_bytes.restype = SZ
+        L.fp4_gemm_workspace_bytes.argtypes = [I32, I64, I64, I64]
+        L.fp4_gemm.restype = ctypes.c_int
+        L.fp4_gemm.argtypes = [I32, I64, I64, I64, P, P, P, P, P, P, P, I32, I64, P, SZ, P]
+        L.fp4_status_str.restype = ctypes.c_char_p
+        L.fp4_status_str.argtypes = [ctypes.c_int]
+        L.fp4_abi_version.restype = ctypes.c_int
+        L.fp4_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().fp4_status_str(int(status)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != FP4_OK:
+        raise FP4Error(rc, what)
+
+
+# ----------------------------------------------------------- raw ABI names
+def fp4_codes_bytes(rows: int, cols: int) -> int:
+    return lib().fp4_codes_bytes(rows, cols)
+
+
+def fp4_scales_bytes(cfg: QConfig, rows: int, cols: int) -> int:
+    return lib().fp4_scales_bytes(ctypes.byref(cfg), rows, cols)
+
+
+def fp4_workspace_bytes(cfg: QConfig, rows: int, cols: int) -> int:
+    return lib().fp4_workspace_bytes(ctypes.byref(cfg), rows, cols)
+
+
+def fp4_scale_offset(cfg: QConfig, rows: int, cols: int, r: int, kb: int) -> int:
+    return lib().fp4_scale_offset(ctypes.byref(cfg), rows, cols, r, kb)
+
+
+def fp4_error_workspace_bytes(cfg: QConfig, rows: int, cols: int) -> int:
+    return lib().fp4_error_workspace_bytes(ctypes.byref(cfg), rows, cols)
+
+
+def fp4_gemm_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
+    return lib().fp4_gemm_workspace_bytes(fmt, M, N, K)
+
+
+def fp4_quantize(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, gs_mode, ws,
+                 ws_bytes, stream) -> int:
+    """Raw call: pointers are ints (device addresses), stream an int handle."""
+    return lib().fp4_quantize(ctypes.byref(cfg), x, xdt, rows, cols, ldx, codes, scales,
+                              global_scale, gs_mode, ws, ws_bytes, stream)
+
+
+def fp4_global_scale(cfg, x, xdt, rows, cols, ldx, global_scale, ws, ws_bytes, stream) -> int:
+    return lib().fp4_global_scale(ctypes.byref(cfg), x, xdt, rows, cols, ldx, global_scale, ws,
+                                  ws_bytes, stream)
+
+
+def fp4_dequantize(cfg, codes, scales, global_scale, rows, cols, y, ydt, ldy, inverse_rotate,
+                   stream) -> int:
+    return lib().fp4_dequantize(ctypes.byref(cfg), codes, scales, global_scale, rows, cols, y,
+                                ydt, ldy, inverse_rotate, stream)
+
+
+def fp4_error_sums(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, sums, ws,
+                   ws_bytes, stream) -> int:
+    return lib().fp4_error_sums(ctypes.byref(cfg), x, xdt, rows, cols, ldx, codes, scales,
+                                global_scale, sums, ws, ws_bytes, stream)
+
+
+def fp4_scales_to_gemm_layout(cfg, rowmajor, rows, cols, gemm_scales, stream) -> int:
+    return lib().fp4_scales_to_gemm_layout(ctypes.byref(cfg), rowmajor, rows, cols, gemm_scales,
+                                           stream)
+
+
+def fp4_gemm(fmt, M, N, K, a_codes, a_scales, a_gs, b_codes, b_scales, b_gs, y, ydt, ldy, ws,
+             ws_bytes, stream) -> int:
+    return lib().fp4_gemm(fmt, M, N, K, a_codes, a_scales, a_gs, b_codes, b_scales, b_gs, y, ydt,
+                          ldy, ws, ws_bytes, stream)
+
+
+# ----------------------------------------------------------- torch helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DT_F32
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    raise TypeError("x must be float32 or bfloat16, got %s" % t.dtype)
+
+
+_ws_cache: dict = {}
+
+
+def _zeroed_workspace(nbytes: int, device):
+    """Per-device workspace for the NVFP4 global-amax pass (the library leaves
+    it zero-filled after each call, so it is reused)."""
+    torch = _torch()
+    key = (str(device), nbytes)
+    t = _ws_cache.get(key)
+    if t is None:
+        t = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _ws_cache[key] = t
+    return t
+
+
+@dataclass
+class Quantized:
+    """Packed FP4 tensor: codes [rows, cols/2] u8, scales (layout of cfg) u8,
+    global_scale float32[1] (NVFP4) and the configuration."""
+    codes: object
+    scales: object
+    global_scale: object
+    cfg: QConfig
+    rows: int
+    cols: int
+
+
+def quantize(x, fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMAJOR,
+             global_scale=None, out: Quantized | None = None) -> Quantized:
+    """Quantize a 2-D CUDA tensor (fp32 or bf16, unit stride along the last
+    axis).  NVFP4: ``global_scale`` (a float32[1] CUDA tensor) is used as given
+    when passed, otherwise computed from the tensor's amax."""
+    torch = _torch()
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    cfg = qconfig(fmt, rotate, scale_layout)
+    if out is None:
+        codes = torch.empty(max(fp4_codes_bytes(rows, cols), 16), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(max(fp4_scales_bytes(cfg, rows, cols), 16), dtype=torch.uint8,
+                             device=x.device)
+        gs = torch.zeros(1, dtype=torch.float32, device=x.device)
+        out = Quantized(codes, scales, gs, cfg, rows, cols)
+    gs_mode = GS_COMPUTE
+    if fmt == FMT_NVFP4 and global_scale is not None:
+        out.global_scale.copy_(global_scale.reshape(1))
+        gs_mode = GS_GIVEN
+    wsb = fp4_workspace_bytes(cfg, rows, cols)
+    ws = _zeroed_workspace(wsb, x.device) if wsb else None
+    rc = fp4_quantize(cfg, x.data_ptr(), _dt(x), rows, cols, x.stride(0), out.codes.data_ptr(),
+                      out.scales.data_ptr(), out.global_scale.data_ptr(), gs_mode, _ptr(ws), wsb,
+                      _stream())
+    _check(rc, "fp4_quantize")
+    return out
+
+
+def global_scale(x, rotate: bool = False, out=None):
+    """NVFP4 per-tensor scale of a 2-D CUDA tensor (float32[1] CUDA tensor)."""
+    torch = _torch()
+    rows, cols = x.shape
+    cfg = qconfig(FMT_NVFP4, rotate)
+    if out is None:
+        out = torch.zeros(1, dtype=torch.float32, device=x.device)
+    wsb = fp4_workspace_bytes(cfg, rows, cols)
+    ws = _zeroed_workspace(wsb, x.device)
+    rc = fp4_global_scale(cfg, x.data_ptr(), _dt(x), rows, cols, x.stride(0), out.data_ptr(),
+                          ws.data_ptr(), wsb, _stream())
+    _check(rc, "fp4_global_scale")
+    return out
+
+
+def codes_view(q: Quantized):
+    return q.codes[: q.rows * q.cols // 2].view(q.rows, q.cols // 2)
+
+
+def dequantize(q: Quantized, dtype=None, inverse_rotate: bool = False):
+    torch = _torch()
+    dtype = dtype or torch.float32
+    y = torch.empty(q.rows, q.cols, dtype=dtype, device=q.codes.device)
+    rc = fp4_dequantize(q.cfg, q.codes.data_ptr(), q.scales.data_ptr(), q.global_scale.data_ptr(),
+                        q.rows, q.cols, y.data_ptr(), _dt(y), y.stride(0), int(inverse_rotate),
+                        _stream())
+    _check(rc, "fp4_dequantize")
+    return y
+
+
+def error_sums(x, q: Quantized):
+    """[sum (x-x^)^2, sum x^2, sum x x^, sum x^^2] (float64 CUDA tensor)."""
+    torch = _torch()
+    rows, cols = x.shape
+    wsb = fp4_error_workspace_bytes(q.cfg, rows, cols)
+    ws = torch.empty(max(wsb, 64), dtype=torch.uint8, device=x.device)
+    sums = torch.empty(4, dtype=torch.float64, device=x.device)
+    rc = fp4_error_sums(q.cfg, x.data_ptr(), _dt(x), rows, cols, x.stride(0), q.codes.data_ptr(),
+                        q.scales.data_ptr(), q.global_scale.data_ptr(), sums.data_ptr(),
+                        ws.data_ptr(), wsb, _stream())
+    _check(rc, "fp4_error_sums")
+    return sums
+
+
+def scales_to_gemm_layout(rowmajor, rows: int, cols: int, fmt: int = FMT_MXFP4):
+    torch = _torch()
+    cfg = qconfig(fmt, False, SCALES_GEMM)
+    out = torch.empty(max(fp4_scales_bytes(cfg, rows, cols), 16), dtype=torch.uint8,
+                      device=rowmajor.device)
+    rc = fp4_scales_to_gemm_layout(cfg, rowmajor.data_ptr(), rows, cols, out.data_ptr(), _stream())
+    _check(rc, "fp4_scales_to_gemm_layout")
+    return out
+
+
+def gemm(a: Quantized, b: Quantized, out_dtype=None, out=None, workspace=None):
+    """Y = A * B^T for two quantized operands sharing K (scales in GEMM layout)."""
+    torch = _torch()
+    fmt = a.cfg.fmt
+    assert b.cfg.fmt == fmt and a.cols == b.cols
+    M, N, K = a.rows, b.rows, a.cols
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype or torch.bfloat16, device=a.codes.device)
+    wsb = fp4_gemm_workspace_bytes(fmt, M, N, K)
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=a.codes.device)
+    rc = fp4_gemm(fmt, M, N, K, a.codes.data_ptr(), a.scales.data_ptr(),
+                  a.global_scale.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
+                  b.global_scale.data_ptr(), out.data_ptr(), _dt(out), out.stride(0),
+                  _ptr(workspace), wsb if workspace is not None else 0, _stream())
+    _check(rc, "fp4_gemm")
+    return out

@@ -1,0 +1,233 @@
+// api.cpp -- the C ABI declared in include/fp4.h: host-side validation, size
+// and layout helpers, and dispatch to the gfx950 kernels.  Nothing here
+// touches the GPU before every argument has been checked.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4.h"
+#include "fp4_device.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int dtype_bytes(int32_t dt) { return dt == FP4_DT_F32 ? 4 : (dt == FP4_DT_BF16 ? 2 : 0); }
+
+// Returns FP4_OK when cfg describes a supported quantization of [rows, cols].
+int check_cfg(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
+  if (!cfg) return FP4_ERR_INVALID_ARG;
+  if (cfg->fmt != FP4_FMT_MXFP4 && cfg->fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
+  const int G = cfg->fmt == FP4_FMT_MXFP4 ? 32 : 16;
+  if (cfg->block != G) return FP4_ERR_INVALID_ARG;
+  if (cfg->rotate != 0 && cfg->rotate != G) return FP4_ERR_INVALID_ARG;
+  if (cfg->rule != FP4_SCALE_ABSMAX) return FP4_ERR_UNSUPPORTED;
+  if (cfg->scale_layout != FP4_SCALES_ROWMAJOR && cfg->scale_layout != FP4_SCALES_GEMM)
+    return FP4_ERR_INVALID_ARG;
+  if (rows < 0 || cols < 0 || cols % G != 0) return FP4_ERR_INVALID_ARG;
+  // 32-bit block indexing inside the kernels
+  if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31 || rows * (cols / G) >= ((int64_t)1 << 32))
+    return FP4_ERR_UNSUPPORTED;
+  return FP4_OK;
+}
+
+int check_ld(const void* p, int32_t dt, int64_t rows, int64_t cols, int64_t ld) {
+  const int eb = dtype_bytes(dt);
+  if (eb == 0) return FP4_ERR_INVALID_ARG;
+  if (ld < cols) return FP4_ERR_INVALID_ARG;
+  if (rows > 0 && cols > 0) {
+    if (!p) return FP4_ERR_INVALID_ARG;
+    if (!aligned16(p)) return FP4_ERR_ALIGNMENT;
+    if (rows > 1 && (ld * eb) % 16 != 0) return FP4_ERR_ALIGNMENT;
+  }
+  return FP4_OK;
+}
+
+bool gemm_layout(const fp4_qconfig* cfg) {
+  return cfg->fmt == FP4_FMT_MXFP4 && cfg->scale_layout == FP4_SCALES_GEMM;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fp4_abi_version(void) { return FP4_ABI_VERSION; }
+
+const char* fp4_status_str(int status) {
+  switch (status) {
+    case FP4_OK: return "ok";
+    case FP4_ERR_INVALID_ARG: return "invalid argument";
+    case FP4_ERR_UNSUPPORTED: return "unsupported";
+    case FP4_ERR_ALIGNMENT: return "misaligned pointer or leading dimension";
+    case FP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP4_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t fp4_codes_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0 || cols % 2 != 0) return 0;
+  return (size_t)(rows * (cols / 2));
+}
+
+size_t fp4_scales_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
+  if (check_cfg(cfg, rows, cols) != FP4_OK) return 0;
+  if (gemm_layout(cfg)) return (size_t)(((rows + 31) / 32) * fp4k::mx_gemm_kchunks(cols) * 256);
+  return (size_t)(rows * (cols / cfg->block));
+}
+
+size_t fp4_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
+  if (check_cfg(cfg, rows, cols) != FP4_OK) return 0;
+  return cfg->fmt == FP4_FMT_NVFP4 ? 256 : 0;
+}
+
+int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols, int64_t r, int64_t kb) {
+  if (check_cfg(cfg, rows, cols) != FP4_OK) return -1;
+  const int64_t nb = cols / cfg->block;
+  if (r < 0 || r >= rows || kb < 0 || kb >= nb) return -1;
+  if (gemm_layout(cfg)) return fp4k::mx_gemm_scale_offset(r, kb, fp4k::mx_gemm_kchunks(cols));
+  return r * nb + kb;
+}
+
+int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows, int64_t cols,
+                 int64_t ldx, uint8_t* codes, uint8_t* scales, float* global_scale,
+                 int32_t gs_mode, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_cfg(cfg, rows, cols);
+  if (rc != FP4_OK) return rc;
+  rc = check_ld(x, xdt, rows, cols, ldx);
+  if (rc != FP4_OK) return rc;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty) {
+    if (!codes || !scales) return FP4_ERR_INVALID_ARG;
+    if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cfg->fmt == FP4_FMT_MXFP4) {
+    if (empty) return FP4_OK;
+    return hip_status(fp4lib::launch_quantize_mx(x, xdt, cfg->rotate != 0, rows, cols, ldx, codes,
+                                                 scales, gemm_layout(cfg) ? 1 : 0, st));
+  }
+  if (gs_mode != FP4_GS_COMPUTE && gs_mode != FP4_GS_GIVEN) return FP4_ERR_INVALID_ARG;
+  if (!global_scale) return FP4_ERR_INVALID_ARG;
+  if (gs_mode == FP4_GS_COMPUTE) {
+    if (!ws || ws_bytes < fp4_workspace_bytes(cfg, rows, cols)) return FP4_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
+    hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx,
+                                          static_cast<uint32_t*>(ws), global_scale, st);
+    if (e != hipSuccess) return FP4_ERR_HIP;
+  }
+  if (empty) return FP4_OK;
+  return hip_status(fp4lib::launch_quantize_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, codes,
+                                               scales, global_scale, st));
+}
+
+int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows,
+                     int64_t cols, int64_t ldx, float* global_scale, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int rc = check_cfg(cfg, rows, cols);
+  if (rc != FP4_OK) return rc;
+  if (cfg->fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
+  rc = check_ld(x, xdt, rows, cols, ldx);
+  if (rc != FP4_OK) return rc;
+  if (!global_scale) return FP4_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < fp4_workspace_bytes(cfg, rows, cols)) return FP4_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
+  return hip_status(fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx,
+                                           static_cast<uint32_t*>(ws), global_scale,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int fp4_dequantize(const fp4_qconfig* cfg, const uint8_t* codes, const uint8_t* scales,
+                   const float* global_scale, int64_t rows, int64_t cols, void* y, int32_t ydt,
+                   int64_t ldy, int32_t inverse_rotate, void* stream) {
+  int rc = check_cfg(cfg, rows, cols);
+  if (rc != FP4_OK) return rc;
+  rc = check_ld(y, ydt, rows, cols, ldy);
+  if (rc != FP4_OK) return rc;
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!codes || !scales) return FP4_ERR_INVALID_ARG;
+  if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
+  if (cfg->fmt == FP4_FMT_NVFP4 && !global_scale) return FP4_ERR_INVALID_ARG;
+  const int rot = (inverse_rotate != 0 && cfg->rotate != 0) ? 1 : 0;
+  return hip_status(fp4lib::launch_dequantize(cfg->fmt, rot, gemm_layout(cfg) ? 1 : 0, codes, scales,
+                                              global_scale, rows, cols, y, ydt, ldy,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+size_t fp4_error_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
+  if (check_cfg(cfg, rows, cols) != FP4_OK) return 0;
+  return (size_t)fp4lib::error_partials(rows, cols, cfg->fmt) * 4 * sizeof(double);
+}
+
+int fp4_error_sums(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows, int64_t cols,
+                   int64_t ldx, const uint8_t* codes, const uint8_t* scales,
+                   const float* global_scale, double* sums, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int rc = check_cfg(cfg, rows, cols);
+  if (rc != FP4_OK) return rc;
+  rc = check_ld(x, xdt, rows, cols, ldx);
+  if (rc != FP4_OK) return rc;
+  if (!sums) return FP4_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(sums) & 7u) != 0) return FP4_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < fp4_error_workspace_bytes(cfg, rows, cols)) return FP4_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 7u) != 0) return FP4_ERR_ALIGNMENT;
+  if (rows > 0 && cols > 0) {
+    if (!codes || !scales) return FP4_ERR_INVALID_ARG;
+    if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
+    if (cfg->fmt == FP4_FMT_NVFP4 && !global_scale) return FP4_ERR_INVALID_ARG;
+  }
+  return hip_status(fp4lib::launch_error_sums(cfg->fmt, cfg->rotate != 0, gemm_layout(cfg) ? 1 : 0,
+                                              x, xdt, ldx, codes, scales, global_scale, rows, cols,
+                                              sums, static_cast<double*>(ws),
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor, int64_t rows,
+                              int64_t cols, uint8_t* gemm_scales, void* stream) {
+  int rc = check_cfg(cfg, rows, cols);
+  if (rc != FP4_OK) return rc;
+  if (cfg->fmt != FP4_FMT_MXFP4) return FP4_ERR_UNSUPPORTED;  // NVFP4: the layouts coincide
+  if (rows == 0 || cols == 0) return FP4_OK;
+  if (!rowmajor || !gemm_scales) return FP4_ERR_INVALID_ARG;
+  return hip_status(fp4lib::launch_scales_to_gemm(rowmajor, rows, cols, gemm_scales,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return 0;
+  if (fmt == FP4_FMT_MXFP4) return fp4lib::gemm_mx_workspace(M, N, K);
+  if (fmt == FP4_FMT_NVFP4) return fp4lib::gemm_nv_workspace(M, N, K);
+  return 0;
+}
+
+int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+             const uint8_t* a_scales, const float* a_gs, const uint8_t* b_codes,
+             const uint8_t* b_scales, const float* b_gs, void* y, int32_t ydt, int64_t ldy,
+             void* ws, size_t ws_bytes, void* stream) {
+  if (fmt != FP4_FMT_MXFP4 && fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID_ARG;
+  if (K % 128 != 0) return FP4_ERR_UNSUPPORTED;
+  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
+    return FP4_ERR_UNSUPPORTED;
+  if (dtype_bytes(ydt) == 0) return FP4_ERR_INVALID_ARG;
+  if (ldy < N) return FP4_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FP4_OK;
+  if (!y) return FP4_ERR_INVALID_ARG;
+  if (K > 0) {
+    if (!a_codes || !a_scales || !b_codes || !b_scales) return FP4_ERR_INVALID_ARG;
+    if (!aligned16(a_codes) || !aligned16(b_codes)) return FP4_ERR_ALIGNMENT;
+    if ((reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(b_scales) & 3u))
+      return FP4_ERR_ALIGNMENT;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fmt == FP4_FMT_MXFP4)
+    return hip_status(fp4lib::launch_gemm_mx(M, N, K, a_codes, a_scales, b_codes, b_scales, y, ydt,
+                                             ldy, ws, ws_bytes, st));
+  if (!a_gs || !b_gs) return FP4_ERR_INVALID_ARG;
+  return hip_status(fp4lib::launch_gemm_nv(M, N, K, a_codes, a_scales, a_gs, b_codes, b_scales,
+                                           b_gs, y, ydt, ldy, ws, ws_bytes, st));
+}
+
+}  // extern "C"

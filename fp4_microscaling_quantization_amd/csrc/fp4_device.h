@@ -1,0 +1,141 @@
+// fp4_device.h -- device-side helpers shared by the gfx950 kernels of this
+// library (internal; not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4k {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// bf16 pair (low half = element 0) widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = as_u(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- E2M1 encode
+// The gfx950 conversion v_cvt_scalef32_pk_fp4_* rounds x / 2^E to the nearest
+// E2M1 value with ties to even, saturates at +-6 and keeps the sign of zero,
+// where E is taken from the exponent field of the scale operand alone (field 0
+// means 2^-127).  Passing the E8M0 code shifted into the exponent field makes
+// it divide by exactly the MXFP4 block scale.
+__device__ __forceinline__ float e8m0_as_cvt_scale(uint32_t code) { return as_f(code << 23); }
+
+// Eight fp32 values -> one dword of codes (element 0 in the low nibble).
+__device__ __forceinline__ uint32_t enc8_f32(const float* v, float scale) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0], v[1], scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], scale, 3);
+  return r;
+}
+
+// Eight bf16 values (four packed dwords) -> one dword of codes.
+__device__ __forceinline__ uint32_t enc8_bf16(const uint32_t* w, float scale) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w[0]), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w[1]), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w[2]), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, as_bf16x2(w[3]), scale, 3);
+  return r;
+}
+
+// ---------------------------------------------------------------- E2M1 decode
+// One byte of codes -> two fp32 values times 2^E (E from the scale's exponent
+// field, as above).  Exact.
+__device__ __forceinline__ f32x2 dec2_f32(uint32_t byte_src, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte_src, scale, 0);
+}
+
+// ------------------------------------------------------------------ E4M3
+// Value of a non-negative E4M3 code (0 .. 0x7E).
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  if (code < 8u) return (float)code * 0x1p-9f;
+  return as_f((((code >> 3) + 120u) << 23) | ((code & 7u) << 20));
+}
+
+// Nearest E4M3 code to t >= 0 (ties to even), after clipping t to 448.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float t) {
+  t = fminf(t, 448.0f);
+  if (t < 0x1p-6f) return (uint32_t)__builtin_rintf(t * 512.0f);
+  uint32_t u = as_u(t);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  return (u >> 20) - (120u << 3);
+}
+
+// ------------------------------------------------------------ exact quotient
+// fl32(a / b) from r = fl32(1 / b) with two FMAs (Markstein's correction: when
+// r is the correctly rounded reciprocal and q0 = fl32(a * r) is within one ulp
+// of a / b, the remainder a - q0 * b is exact and fl32(q0 + rem * r) is the
+// correctly rounded quotient).  Valid for normal a, b and a normal quotient;
+// callers route blocks with tiny scales through an IEEE division instead.
+__device__ __forceinline__ float div_rn(float a, float b, float r) {
+  float q0 = a * r;
+  float rem = __builtin_fmaf(-q0, b, a);
+  return __builtin_fmaf(rem, r, q0);
+}
+
+// --------------------------------------------------------------- Hadamard
+// In-place unnormalised Walsh-Hadamard transform (Sylvester order) of N
+// registers.
+template <int N>
+__device__ __forceinline__ void fwht(float* v) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+}
+
+// Correctly rounded (up to a ~2^-47 relative band) y = s / sqrt(32) using a
+// two-term constant: fl32(s * c_hi + fl32(s * c_lo)).
+__device__ __forceinline__ float div_sqrt32(float s) {
+  const float c_hi = 0x1.6a09e6p-3f;          // fl32(1/sqrt(32))
+  const float c_lo = 0x1.9fcef4p-29f;         // fl32(1/sqrt(32) - c_hi)
+  return __builtin_fmaf(s, c_hi, s * c_lo);
+}
+
+// ------------------------------------------------------------- scale layout
+// MXFP4 GEMM scale layout: one 256-byte tile per (32 rows) x (8 blocks of 32 =
+// 256 K).  Within a tile, dword (kb % 2) * 32 + (r % 32) holds the scales of
+// row r for blocks kb with the same parity, one byte per 64-K MFMA step: byte
+// (kb % 8) / 2.  A lane l of the 32x32x64 scaled MFMA reads dword l.
+__host__ __device__ __forceinline__ int64_t mx_gemm_scale_offset(int64_t r, int64_t kb,
+                                                                int64_t kchunks) {
+  return ((r >> 5) * kchunks + (kb >> 3)) * 256 + (((kb & 1) * 32 + (r & 31)) * 4) +
+         ((kb & 7) >> 1);
+}
+
+__host__ __device__ __forceinline__ int64_t mx_gemm_kchunks(int64_t cols) {
+  return (cols + 255) / 256;
+}
+
+}  // namespace fp4k

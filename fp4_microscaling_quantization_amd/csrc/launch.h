@@ -1,0 +1,41 @@
+// launch.h -- internal launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4.h"
+
+namespace fp4lib {
+
+hipError_t launch_quantize_mx(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
+                              int64_t ldx, uint8_t* codes, uint8_t* scales, int gemm_layout,
+                              hipStream_t st);
+hipError_t launch_amax_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
+                          int64_t ldx, uint32_t* ws, float* gs_out, hipStream_t st);
+hipError_t launch_quantize_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
+                              int64_t ldx, uint8_t* codes, uint8_t* scales, const float* gs,
+                              hipStream_t st);
+hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
+                                 hipStream_t st);
+
+hipError_t launch_dequantize(int fmt, int rotate, int gemm_layout, const uint8_t* codes,
+                             const uint8_t* scales, const float* gs, int64_t rows, int64_t cols,
+                             void* y, int ydt, int64_t ldy, hipStream_t st);
+int error_partials(int64_t rows, int64_t cols, int fmt);
+hipError_t launch_error_sums(int fmt, int rotate, int gemm_layout, const void* x, int xdt,
+                             int64_t ldx, const uint8_t* codes, const uint8_t* scales,
+                             const float* gs, int64_t rows, int64_t cols, double* sums,
+                             double* partials, hipStream_t st);
+
+size_t gemm_mx_workspace(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+                          const uint8_t* b, const uint8_t* bs, void* y, int ydt, int64_t ldy,
+                          void* ws, size_t ws_bytes, hipStream_t st);
+size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+                          const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
+                          void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                          hipStream_t st);
+
+}  // namespace fp4lib

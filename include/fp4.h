@@ -1,0 +1,203 @@
+/*
+ * fp4.h -- C ABI of the MI355X (gfx950) microscaling FP4 library.
+ *
+ * What it computes
+ *   Block-wise microscaling FP4 quantization along the contiguous (K) axis of a
+ *   row-major [rows, cols] tensor, its dequantization and error sums, and the
+ *   FP4 x FP4 block-scaled matrix product that consumes it, Y = A * B^T with
+ *   fp32 accumulation.
+ *
+ *   MXFP4: blocks of 32 elements, E2M1 elements, one E8M0 (power-of-two) scale
+ *          per block ("Bridging the Gap Between Promise and Performance for
+ *          Microscaling FP4 Quantization", format definitions: G=32, E=FP4,
+ *          S=E8M0).  Scale exponent = floor(log2(block amax)) - 2, clamped to
+ *          [-127, 127] ("NVFP4 vs MXFP4: 4-Bit Floating Point for LLM Training
+ *          and Inference (2026)", "A worked example, by hand").
+ *   NVFP4: blocks of 16 elements, E2M1 elements, one E4M3 scale per block times
+ *          one fp32 per-tensor scale ts = amax_tensor / (6 * 448) (same pages;
+ *          NVFP4 vs MXFP4 Figure 2: global amax -> fp32 tensor scale -> block
+ *          amax -> E4M3 -> E2M1 -> pack).
+ *   Optional "micro-rotation": a block-diagonal Hadamard of the block size
+ *          (Sylvester order, normalised by 1/sqrt(n)) applied to each block
+ *          before quantization ("Bridging the Gap ...": rotations at the group
+ *          level, Q(W H_k) Q(X H_k)^T, fused into activation quantization).
+ *   Elements round to nearest-even on the E2M1 grid {0, 0.5, 1, 1.5, 2, 3, 4,
+ *   6}, saturating at +-6 (NVFP4 vs MXFP4, training recipe; "Microscaling
+ *   Formats in Production LLM Inference", RTNE).  Two codes per byte, element
+ *   2i in the low nibble; the code's sign bit is the sign of x / s.
+ *
+ * Conventions
+ *   - Every pointer argument named x, y, codes, scales, global_scale, ws, sums
+ *     and the GEMM operands is a DEVICE pointer (HIP device memory of the
+ *     current device).  fp4_qconfig pointers are HOST pointers.
+ *   - stream is a hipStream_t passed as void*; NULL means the default stream.
+ *     All work is enqueued asynchronously on it; nothing synchronises.
+ *   - The caller owns and allocates every buffer.  The library allocates no
+ *     device memory and keeps no state between calls, except that the
+ *     workspace of fp4_quantize must be zero-filled before its first use; the
+ *     library leaves it zero-filled again when each call completes.
+ *   - Calls that share a workspace must not overlap in time (same stream is
+ *     enough).
+ *   - Validation happens on the host before any launch: on error nothing is
+ *     enqueued and a negative fp4_status is returned.  FP4_ERR_HIP reports a
+ *     failed launch.
+ *   - NaN and infinite inputs are outside the contract.
+ */
+#ifndef FP4_MI355X_H
+#define FP4_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4_ABI_VERSION 1
+
+typedef enum {
+    FP4_OK = 0,
+    FP4_ERR_INVALID_ARG = -1,   /* bad dims, leading dims, enum values, NULL */
+    FP4_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement */
+    FP4_ERR_ALIGNMENT = -3,     /* a pointer or leading dimension is misaligned */
+    FP4_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required */
+    FP4_ERR_HIP = -5            /* a HIP launch failed */
+} fp4_status;
+
+typedef enum { FP4_FMT_MXFP4 = 0, FP4_FMT_NVFP4 = 1 } fp4_format;
+typedef enum { FP4_SCALE_ABSMAX = 0 } fp4_scale_rule;
+typedef enum { FP4_DT_F32 = 0, FP4_DT_BF16 = 1 } fp4_dtype;
+typedef enum { FP4_SCALES_ROWMAJOR = 0, FP4_SCALES_GEMM = 1 } fp4_scale_layout;
+typedef enum { FP4_GS_COMPUTE = 0, FP4_GS_GIVEN = 1 } fp4_gs_mode;
+
+/* Quantization configuration (host struct).
+ *   fmt           fp4_format.
+ *   block         32 for MXFP4, 16 for NVFP4 (any other value is rejected).
+ *   rotate        0, or equal to block: block Hadamard of that size first.
+ *   rule          FP4_SCALE_ABSMAX (the block maximum sets the scale).
+ *   scale_layout  FP4_SCALES_ROWMAJOR: byte (r, kb) at r * (cols/block) + kb.
+ *                 FP4_SCALES_GEMM: the layout fp4_gemm reads; byte positions
+ *                 are given by fp4_scale_offset.  For NVFP4 the two layouts
+ *                 coincide. */
+typedef struct {
+    int32_t fmt;
+    int32_t block;
+    int32_t rotate;
+    int32_t rule;
+    int32_t scale_layout;
+} fp4_qconfig;
+
+/* ---------------------------------------------------------------- sizes */
+
+/* Bytes of packed codes for [rows, cols]: rows * cols / 2.  Host function. */
+size_t fp4_codes_bytes(int64_t rows, int64_t cols);
+
+/* Bytes of the scale array, including the padding of the GEMM layout
+ * (MXFP4 GEMM layout pads rows to 32 and cols to 256).  0 on invalid input.
+ * Unpadded sizes give 4.25 (MXFP4) and 4.5 (NVFP4) bits per element together
+ * with the codes ("NVFP4 vs MXFP4", storage overhead).  Host function. */
+size_t fp4_scales_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
+
+/* Workspace bytes fp4_quantize needs (NVFP4 with FP4_GS_COMPUTE: 256 bytes;
+ * otherwise 0).  Host function. */
+size_t fp4_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
+
+/* Byte index inside the scale array of the scale of (row r, block kb), for the
+ * layout named in cfg; -1 if out of range.  Host function. */
+int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols,
+                         int64_t r, int64_t kb);
+
+/* ------------------------------------------------------------- quantize */
+
+/* Quantize x [rows, cols] (row-major, leading dimension ldx elements, element
+ * type xdt) into codes [rows, cols/2] (dense) and scales (layout of cfg).
+ *   NVFP4: gs_mode FP4_GS_COMPUTE computes ts = amax(|x'|)/2688 over the whole
+ *   [rows, cols] tensor (x' = the rotated tensor when rotate != 0) and writes
+ *   it to *global_scale; FP4_GS_GIVEN reads ts from *global_scale.  A block
+ *   whose scale (e4m3 * ts) is zero stores all-zero codes.
+ *   MXFP4 ignores global_scale and gs_mode (global_scale may be NULL).
+ * ws/ws_bytes: device workspace of fp4_workspace_bytes() bytes, zero-filled
+ * before its first use (may be NULL when that size is 0).
+ * Requirements: rows >= 0, cols >= 0, cols % block == 0, ldx >= cols, x
+ * 16-byte aligned and ldx * sizeof(xdt) a multiple of 16 (when rows > 1),
+ * codes 16-byte aligned.  rows == 0 or cols == 0 is a no-op (for NVFP4 with
+ * FP4_GS_COMPUTE, ts = 0 is written). */
+int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt,
+                 int64_t rows, int64_t cols, int64_t ldx,
+                 uint8_t* codes, uint8_t* scales, float* global_scale, int32_t gs_mode,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* NVFP4 per-tensor scale only: writes ts = amax(|x'|) / 2688 to
+ * *global_scale (x' = the rotated tensor when cfg->rotate != 0), exactly as
+ * fp4_quantize does with FP4_GS_COMPUTE, which is this call followed by
+ * fp4_quantize with FP4_GS_GIVEN.  For callers that fix the tensor scale once
+ * (static scales) or schedule the two passes themselves.  Same workspace and
+ * argument rules as fp4_quantize; MXFP4 configurations are rejected with
+ * FP4_ERR_INVALID_ARG. */
+int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt,
+                     int64_t rows, int64_t cols, int64_t ldx, float* global_scale,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------- dequantize */
+
+/* y [rows, cols] (leading dimension ldy, element type ydt) =
+ *   MXFP4: e2m1 * 2^(c - 127);  NVFP4: fl32(fl32(e2m1 * e4m3) * ts),
+ * then, if inverse_rotate != 0 and cfg->rotate != 0, the block Hadamard again
+ * (it is its own inverse), giving values in the original domain.  bf16 output
+ * rounds to nearest-even.  Scales are read in cfg's layout. */
+int fp4_dequantize(const fp4_qconfig* cfg, const uint8_t* codes, const uint8_t* scales,
+                   const float* global_scale, int64_t rows, int64_t cols,
+                   void* y, int32_t ydt, int64_t ldy, int32_t inverse_rotate, void* stream);
+
+/* Error sums of the quantization of x ("Portable FP4 Quantization for
+ * Heterogeneous Accelerators", section 3.2: NMSE and cosine similarity):
+ *   sums[0] = sum (x - x^)^2, sums[1] = sum x^2, sums[2] = sum x * x^,
+ *   sums[3] = sum x^^2, in double, over all rows x cols elements, where x^ is
+ *   the dequantized value brought back to the original domain (inverse
+ *   rotation when cfg->rotate != 0).  sums is a device array of 4 doubles.
+ *   ws: device workspace of fp4_error_workspace_bytes() bytes (any contents).
+ *   The reduction order is fixed, so the sums are deterministic. */
+size_t fp4_error_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
+int fp4_error_sums(const fp4_qconfig* cfg, const void* x, int32_t xdt,
+                   int64_t rows, int64_t cols, int64_t ldx,
+                   const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                   double* sums, void* ws, size_t ws_bytes, void* stream);
+
+/* Re-lay scales from FP4_SCALES_ROWMAJOR [rows, cols/block] into
+ * FP4_SCALES_GEMM (padding bytes are written as 127, i.e. scale 1, and are
+ * never used by fp4_gemm).  For weights quantized elsewhere.  MXFP4 only:
+ * for NVFP4 the two layouts coincide and FP4_ERR_UNSUPPORTED is returned. */
+int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor,
+                              int64_t rows, int64_t cols, uint8_t* gemm_scales, void* stream);
+
+/* ----------------------------------------------------------------- GEMM */
+
+/* Y[M, N] = sum_k A[m, k] * B[n, k] ("Bridging the Gap ...": the kernels
+ * compute Q(W H_k) Q(X H_k)^T; "NVFP4 vs MXFP4", hardware execution: block
+ * scales applied inside the product, higher-precision accumulation).
+ *   A: a_codes [M, K/2] dense, a_scales in FP4_SCALES_GEMM layout for (M, K).
+ *   B: b_codes [N, K/2] dense, b_scales in FP4_SCALES_GEMM layout for (N, K).
+ *   NVFP4: a_gs / b_gs point to the fp32 per-tensor scales (device); the
+ *   product is multiplied by (*a_gs) * (*b_gs).  MXFP4 ignores them.
+ *   Accumulation is fp32.  y has leading dimension ldy >= N and type ydt
+ *   (bf16 rounds to nearest-even).  The GEMM does not rotate: the caller
+ *   quantizes both operands with the same rotation setting.
+ * ws/ws_bytes: device workspace of fp4_gemm_workspace_bytes() bytes (any
+ * contents; used for split-K partial sums).
+ * Requirements: M, N >= 0, K >= 0 with K % 128 == 0; codes 16-byte aligned. */
+size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
+int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K,
+             const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
+             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gs,
+             void* y, int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- misc */
+
+const char* fp4_status_str(int status);
+int fp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_MI355X_H */

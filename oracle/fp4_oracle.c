@@ -418,18 +418,21 @@ int ora_gemm_entries(int fmt, long K,
         const uint8_t *as = a_scales + rows[e] * nb;
         const uint8_t *bs = b_scales + cols[e] * nb;
         double s = 0.0, sa = 0.0;
-        for (long k = 0; k < K; ++k) {
-            double av = ora_e2m1_decode(get_code(ac, k));
-            double bv = ora_e2m1_decode(get_code(bc, k));
+        for (long b = 0; b < nb; ++b) {
+            double asv, bsv;            /* the two block scales */
             if (fmt == ORA_MXFP4) {
-                av *= ora_e8m0_decode(as[k / G]);
-                bv *= ora_e8m0_decode(bs[k / G]);
+                asv = ora_e8m0_decode(as[b]);
+                bsv = ora_e8m0_decode(bs[b]);
             } else {
-                av *= ora_e4m3_decode(as[k / G]);
-                bv *= ora_e4m3_decode(bs[k / G]);
+                asv = ora_e4m3_decode(as[b]);
+                bsv = ora_e4m3_decode(bs[b]);
             }
-            s += av * bv;
-            sa += fabs(av) * fabs(bv);
+            for (long k = b * G; k < (b + 1) * G; ++k) {
+                double av = ora_e2m1_decode(get_code(ac, k)) * asv;
+                double bv = ora_e2m1_decode(get_code(bc, k)) * bsv;
+                s += av * bv;
+                sa += fabs(av) * fabs(bv);
+            }
         }
         if (fmt == ORA_NVFP4) {
             double g = (double)a_ts * (double)b_ts;

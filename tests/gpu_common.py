@@ -1,0 +1,126 @@
+"""Helpers shared by the GPU parity tests (no method arithmetic here)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import fp4_microscaling_quantization_amd as fp4
+
+GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def to_dev_bf16(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev()).view(torch.bfloat16)
+
+
+def to_dev_f32(x: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev())
+
+
+def to_dev_u8(x: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(dev())
+
+
+def codes_np(q: fp4.Quantized) -> np.ndarray:
+    return fp4.codes_view(q).cpu().numpy()
+
+
+def rowmajor_scales_np(q: fp4.Quantized) -> np.ndarray:
+    """Scales of q gathered into row-major order through fp4_scale_offset."""
+    raw = q.scales.cpu().numpy()
+    G = q.cfg.block
+    nb = q.cols // G
+    if q.cfg.scale_layout == fp4.SCALES_ROWMAJOR or q.cfg.fmt == fp4.FMT_NVFP4:
+        return raw[: q.rows * nb].reshape(q.rows, nb)
+    idx = gemm_offsets(q.rows, q.cols)
+    return raw[idx]
+
+
+_off_cache = {}
+
+
+def gemm_offsets(rows: int, cols: int) -> np.ndarray:
+    """[rows, cols/32] byte offsets of the MXFP4 GEMM scale layout, from the
+    library's host-side fp4_scale_offset (sampled, then checked to be the
+    affine-in-tiles map it promises to be, then expanded)."""
+    key = (rows, cols)
+    if key in _off_cache:
+        return _off_cache[key]
+    cfg = fp4.qconfig(fp4.FMT_MXFP4, scale_layout=fp4.SCALES_GEMM)
+    nb = cols // 32
+    # offsets of one full tile (32 rows x 8 blocks) plus the tile strides
+    r = np.arange(rows)[:, None]
+    kb = np.arange(nb)[None, :]
+    tile_r = np.minimum(32, rows)
+    tile_k = np.minimum(8, nb)
+    base = np.array([[fp4.fp4_scale_offset(cfg, rows, cols, i, j) for j in range(tile_k)]
+                     for i in range(tile_r)])
+    kchunks = (cols + 255) // 256
+    off = (r // 32) * kchunks * 256 + (kb // 8) * 256 + base[r % 32, kb % 8]
+    # spot-check the expansion against the library at random points
+    g = np.random.default_rng(0)
+    for _ in range(200):
+        i, j = int(g.integers(rows)), int(g.integers(nb))
+        assert off[i, j] == fp4.fp4_scale_offset(cfg, rows, cols, i, j)
+    _off_cache[key] = off
+    return off
+
+
+def signed_values(codes: np.ndarray) -> np.ndarray:
+    c = np.stack([codes & 15, codes >> 4], -1).reshape(codes.shape[0], -1)
+    v = GRID[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def grid_index(vals: np.ndarray) -> np.ndarray:
+    """Position on the signed grid -6 .. 6 (15 points; +-0 share index 7)."""
+    full = np.concatenate([-GRID[:0:-1], GRID])
+    return np.searchsorted(full, vals)
+
+
+def assert_rotated_codes_close(got_codes, ref_codes, got_scales, ref_scales, budget=1e-4,
+                               what=""):
+    """Rotated paths: element codes may differ in at most `budget` of the
+    elements, and only between adjacent grid points; scale codes in at most
+    `budget` of the blocks, by one step."""
+    n = got_codes.size * 2
+    gv = signed_values(got_codes)
+    rv = signed_values(ref_codes)
+    diff = gv != rv
+    rate = diff.sum() / n
+    say("  %s element mismatches: %d of %d (%.2e)" % (what, diff.sum(), n, rate))
+    assert rate <= budget, (what, rate)
+    if diff.any():
+        # compare in the scale of each side's block
+        step = np.abs(grid_index(gv[diff]) - grid_index(rv[diff]))
+        scale_same = np.repeat(got_scales == ref_scales, gv.shape[1] // got_scales.shape[1], axis=1)[diff]
+        assert np.all(step[scale_same] <= 1), (what, "non-adjacent mismatch")
+    sd = got_scales != ref_scales
+    srate = sd.sum() / got_scales.size
+    say("  %s scale mismatches: %d of %d (%.2e)" % (what, sd.sum(), got_scales.size, srate))
+    assert srate <= budget, (what, srate)
+    if sd.any():
+        assert np.all(np.abs(got_scales[sd].astype(int) - ref_scales[sd].astype(int)) == 1)
+
+
+def gemm_tolerance_ok(got: np.ndarray, ref: np.ndarray, absref: np.ndarray, bf16: bool) -> np.ndarray:
+    """|y - y_ref| <= 1e-5 (|A||B|) for fp32 output; for bf16 output the same
+    plus half a bf16 ulp of the reference."""
+    err = np.abs(got - ref)
+    if not bf16:
+        return err <= 1e-5 * absref
+    return err <= 1e-5 * absref * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)

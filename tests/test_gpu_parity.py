@@ -1,0 +1,328 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Non-rotated codes, scales and tensor scales must match bit for bit; rotated
+codes within the 1e-4 adjacent-mismatch budget; dequantized values exactly
+(fp32) or to the bf16 rounding of the oracle's fp32; error sums to 1e-9
+relative; GEMMs within |y - y_ref| <= 1e-5 (|A||B|) (bf16 output: plus half a
+bf16 ulp).  Full-size workloads run in the same launch configuration as the
+benchmark; big GEMMs are checked on sampled rows and entries.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import fp4_microscaling_quantization_amd as fp4
+import oracle
+import workloads
+from gpu_common import (assert_rotated_codes_close, codes_np, gemm_tolerance_ok, rowmajor_scales_np,
+                        say, to_dev_bf16, to_dev_f32, to_dev_u8)
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [fp4.FMT_MXFP4, fp4.FMT_NVFP4]
+FNAME = {fp4.FMT_MXFP4: "mxfp4", fp4.FMT_NVFP4: "nvfp4"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fp4.lib()
+
+
+def _inputs(name):
+    """(label, host fp32 view, device tensor)."""
+    if name == "cfg1":
+        x = workloads.cfg1_tensor(0)
+        return x, to_dev_f32(x)
+    if name in ("cfg2_gauss", "cfg2_laplace"):
+        b = workloads.cfg2_tensor(name.split("_")[1], 0)
+    elif name == "cfg3":
+        b = workloads.cfg3_tensor(0)
+    elif name == "ragged":
+        b = workloads.cfg2_tensor("laplace", 9, rows=37, cols=4128)
+    elif name == "tiny_rows":
+        b = workloads.cfg2_tensor("gauss", 10, rows=3, cols=96)
+    else:
+        raise KeyError(name)
+    return workloads.bf16_bits_to_f32(b), to_dev_bf16(b)
+
+
+NONROT_CASES = ["cfg1", "cfg2_gauss", "cfg2_laplace", "cfg3", "ragged", "tiny_rows"]
+
+
+def _prefill(q):
+    q.codes.fill_(0xAA)
+    q.scales.fill_(0xAA)
+    return q
+
+
+@pytest.mark.parametrize("case", NONROT_CASES)
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_quantize_bit_exact(case, fmt):
+    say("quantize bit-exact", case, FNAME[fmt])
+    xh, xd = _inputs(case)
+    if fmt == fp4.FMT_NVFP4 and case == "cfg1":
+        pass
+    layouts = [fp4.SCALES_ROWMAJOR, fp4.SCALES_GEMM] if fmt == fp4.FMT_MXFP4 else [fp4.SCALES_ROWMAJOR]
+    rc, rs, rts = oracle.quantize(xh, fmt)
+    for lay in layouts:
+        q = fp4.quantize(xd, fmt, scale_layout=lay)
+        q2 = _prefill(fp4.quantize(xd, fmt, scale_layout=lay))
+        fp4.quantize(xd, fmt, scale_layout=lay, out=q2)
+        torch.cuda.synchronize()
+        gc = codes_np(q)
+        gs = rowmajor_scales_np(q)
+        assert np.array_equal(gc, rc), (case, lay, np.argwhere(gc != rc)[:5])
+        assert np.array_equal(gs, rs), (case, lay, np.argwhere(gs != rs)[:5])
+        if fmt == fp4.FMT_NVFP4:
+            assert q.global_scale.item() == float(rts), (q.global_scale.item(), rts)
+        # deterministic and independent of the previous buffer contents
+        assert np.array_equal(codes_np(q2), gc) and np.array_equal(rowmajor_scales_np(q2), gs)
+
+
+@pytest.mark.parametrize("case", ["cfg2_laplace", "ragged"])
+def test_nvfp4_given_global_scale(case):
+    say("nvfp4 given ts", case)
+    xh, xd = _inputs(case)
+    ts = np.float32(0.013)
+    rc, rs, _ = oracle.quantize(xh, oracle.NVFP4, ts=ts)
+    q = fp4.quantize(xd, fp4.FMT_NVFP4, global_scale=torch.tensor([ts], device="cuda"))
+    torch.cuda.synchronize()
+    assert q.global_scale.item() == float(ts)
+    assert np.array_equal(codes_np(q), rc)
+    assert np.array_equal(rowmajor_scales_np(q), rs)
+
+
+@pytest.mark.parametrize("case", ["cfg2_gauss", "cfg2_laplace", "cfg3", "ragged"])
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_quantize_rotated(case, fmt):
+    say("quantize rotated", case, FNAME[fmt])
+    xh, xd = _inputs(case)
+    rc, rs, rts = oracle.quantize(xh, fmt, rotate=True)
+    lay = fp4.SCALES_GEMM if fmt == fp4.FMT_MXFP4 else fp4.SCALES_ROWMAJOR
+    q = fp4.quantize(xd, fmt, rotate=True, scale_layout=lay)
+    torch.cuda.synchronize()
+    if fmt == fp4.FMT_NVFP4:
+        g = np.float32(q.global_scale.item())
+        assert abs(int(g.view(np.int32)) - int(np.float32(rts).view(np.int32))) <= 1, (g, rts)
+    assert_rotated_codes_close(codes_np(q), rc, rowmajor_scales_np(q), rs, what=case)
+
+
+@pytest.mark.parametrize("case", ["cfg1", "cfg2_laplace", "ragged"])
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("rot", [False, True], ids=["plain", "rot"])
+def test_dequantize_and_error_sums(case, fmt, rot):
+    say("dequantize", case, FNAME[fmt], rot)
+    xh, xd = _inputs(case)
+    lay = fp4.SCALES_GEMM if fmt == fp4.FMT_MXFP4 else fp4.SCALES_ROWMAJOR
+    q = fp4.quantize(xd, fmt, rotate=rot, scale_layout=lay)
+    torch.cuda.synchronize()
+    # the oracle dequantizes the GPU's codes only after they were shown equal
+    # to its own (non-rotated); for rotated inputs it dequantizes its own codes
+    # and the comparison runs on the blocks whose codes agree.
+    rc, rs, rts = oracle.quantize(xh, fmt, rotate=rot)
+    gc, gs = codes_np(q), rowmajor_scales_np(q)
+    ref_rot = oracle.dequantize(rc, rs, fmt, rts)
+    ref_orig = oracle.dequantize(rc, rs, fmt, rts, inverse_rotate=True) if rot else ref_rot
+    y = fp4.dequantize(q).cpu().numpy()
+    yb = fp4.dequantize(q, dtype=torch.bfloat16).float().cpu().numpy()
+    yo = fp4.dequantize(q, inverse_rotate=True).cpu().numpy()
+    sums = fp4.error_sums(xd, q).cpu().numpy()
+    torch.cuda.synchronize()
+    G = fp4.BLOCK[fmt]
+    same = np.repeat((gs == rs) & (gc.reshape(gc.shape[0], -1, G // 2) == rc.reshape(rc.shape[0], -1, G // 2)).all(-1),
+                     G, axis=1)
+    if not rot:
+        assert same.all()
+    assert same.mean() > 0.99
+    assert np.array_equal(y[same], ref_rot[same])
+    ref_b = workloads.bf16_bits_to_f32(workloads.to_bf16_bits(ref_rot))
+    assert np.array_equal(yb[same], ref_b[same])
+    if rot and fmt == fp4.FMT_NVFP4:
+        # the fp32 butterfly over 16 values with 24-bit significands rounds at
+        # each of its 4 stages: error <= 4 * 2^-24 * sum|x^| of the block
+        blk = np.abs(ref_rot).reshape(ref_rot.shape[0], -1, G).sum(-1)
+        atol = np.repeat(blk, G, axis=1) * 4 * 2.0 ** -24
+        assert np.all(np.abs(yo[same] - ref_orig[same]) <= atol[same])
+    else:
+        assert np.allclose(yo[same], ref_orig[same], rtol=3e-7, atol=0)
+    ref_sums = oracle.error_sums(xh, ref_orig)
+    tol = 1e-9 if not rot else 1e-4
+    np.testing.assert_allclose(sums, ref_sums, rtol=tol)
+    # NMSE is the same whichever side computes it
+    say("  nmse gpu %.6e oracle %.6e" % (sums[0] / sums[1], ref_sums[0] / ref_sums[1]))
+
+
+def test_edge_cases():
+    say("edge cases")
+    # all zeros
+    z = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
+    qm = fp4.quantize(z, fp4.FMT_MXFP4)
+    qn = fp4.quantize(z, fp4.FMT_NVFP4)
+    torch.cuda.synchronize()
+    assert np.all(codes_np(qm) == 0) and np.all(rowmajor_scales_np(qm) == 0)
+    assert np.all(codes_np(qn) == 0) and np.all(rowmajor_scales_np(qn) == 0)
+    assert qn.global_scale.item() == 0.0
+    # tiny, huge, negative zero and saturating values, fp32 input
+    vals = np.array([2.0 ** -130, -2.0 ** -140, 1e30, -3e29, -0.0, 0.0, 6.5, -1e-38] * 8, np.float32)
+    x = np.stack([vals, vals[::-1], vals * 1e-8, np.roll(vals, 3)]).astype(np.float32)
+    xd = to_dev_f32(x)
+    for fmt in FMTS:
+        for rot in (False, True):
+            q = fp4.quantize(xd, fmt, rotate=rot)
+            torch.cuda.synchronize()
+            rc, rs, rts = oracle.quantize(x, fmt, rotate=rot)
+            if not rot:
+                assert np.array_equal(codes_np(q), rc), (fmt, rot)
+                assert np.array_equal(rowmajor_scales_np(q), rs), (fmt, rot)
+                if fmt == fp4.FMT_NVFP4:
+                    assert q.global_scale.item() == float(rts)
+            else:
+                # fp32 butterfly sums of 1e30-sized values round: adjacent codes only
+                assert_rotated_codes_close(codes_np(q), rc, rowmajor_scales_np(q), rs, budget=0.05,
+                                           what="edge rot")
+    # a single row of one block
+    one = to_dev_bf16(workloads.cfg2_tensor("gauss", 12, rows=1, cols=32))
+    q = fp4.quantize(one, fp4.FMT_MXFP4, scale_layout=fp4.SCALES_GEMM)
+    torch.cuda.synchronize()
+    rc, rs, _ = oracle.quantize(workloads.bf16_bits_to_f32(workloads.cfg2_tensor("gauss", 12, rows=1, cols=32)), oracle.MXFP4)
+    assert np.array_equal(codes_np(q), rc) and np.array_equal(rowmajor_scales_np(q), rs)
+    # empty tensor: MXFP4 is a no-op, NVFP4 writes ts = 0
+    e = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    q = fp4.quantize(e, fp4.FMT_NVFP4)
+    torch.cuda.synchronize()
+    assert q.global_scale.item() == 0.0
+    fp4.quantize(e, fp4.FMT_MXFP4)
+
+
+def test_leading_dimension():
+    say("leading dimension")
+    b = workloads.cfg2_tensor("laplace", 13, rows=40, cols=320)
+    full = to_dev_bf16(b)
+    view = full[:, :256]
+    xh = workloads.bf16_bits_to_f32(b)[:, :256]
+    for fmt in FMTS:
+        q = fp4.quantize(view, fmt)
+        torch.cuda.synchronize()
+        rc, rs, rts = oracle.quantize(np.ascontiguousarray(xh), fmt)
+        assert np.array_equal(codes_np(q), rc) and np.array_equal(rowmajor_scales_np(q), rs)
+
+
+def test_scales_to_gemm_layout():
+    say("scale relayout")
+    for rows, cols in [(37, 4128), (64, 256), (1, 32), (300, 1024)]:
+        rm = workloads.random_scales(rows, cols // 32, 0, 254, seed=rows)
+        out = fp4.scales_to_gemm_layout(to_dev_u8(rm), rows, cols)
+        torch.cuda.synchronize()
+        raw = out.cpu().numpy()
+        cfg = fp4.qconfig(fp4.FMT_MXFP4, scale_layout=fp4.SCALES_GEMM)
+        size = fp4.fp4_scales_bytes(cfg, rows, cols)
+        seen = np.zeros(size, bool)
+        for r in range(rows):
+            for kb in range(cols // 32):
+                o = fp4.fp4_scale_offset(cfg, rows, cols, r, kb)
+                assert raw[o] == rm[r, kb]
+                seen[o] = True
+        assert np.all(raw[:size][~seen] == 127)
+
+
+# ------------------------------------------------------------------- GEMM
+def _rand_operands(fmt, M, N, K, seed):
+    """Seeded random packed codes and scale bytes (the GEMM's input domain)."""
+    G = fp4.BLOCK[fmt]
+    ac = workloads.random_codes(M, K, seed, stream=21)
+    bc = workloads.random_codes(N, K, seed, stream=22)
+    if fmt == fp4.FMT_MXFP4:
+        asc = workloads.random_scales(M, K // G, 120, 130, seed, stream=23)
+        bsc = workloads.random_scales(N, K // G, 118, 124, seed, stream=24)
+        ags = bgs = np.float32(0)
+    else:
+        asc = workloads.random_scales(M, K // G, 0x20, 0x7E, seed, stream=23)
+        bsc = workloads.random_scales(N, K // G, 0x10, 0x7E, seed, stream=24)
+        ags, bgs = np.float32(0.0371), np.float32(1.7e-5)
+    return ac, asc, ags, bc, bsc, bgs
+
+
+def _device_operand(codes, scales_rm, gs, fmt, rows, K):
+    c = to_dev_u8(codes.reshape(-1))
+    if fmt == fp4.FMT_MXFP4:
+        s = fp4.scales_to_gemm_layout(to_dev_u8(scales_rm.reshape(-1)), rows, K)
+    else:
+        s = to_dev_u8(scales_rm.reshape(-1))
+    g = torch.tensor([float(gs)], dtype=torch.float32, device="cuda")
+    cfg = fp4.qconfig(fmt, scale_layout=fp4.SCALES_GEMM)
+    return fp4.Quantized(c, s, g, cfg, rows, K)
+
+
+def _check_gemm(fmt, M, N, K, seed, out_dtype, nrows=2, nent=256):
+    say("gemm", FNAME[fmt], M, N, K, out_dtype)
+    ac, asc, ags, bc, bsc, bgs = _rand_operands(fmt, M, N, K, seed)
+    qa = _device_operand(ac, asc, ags, fmt, M, K)
+    qb = _device_operand(bc, bsc, bgs, fmt, N, K)
+    y = fp4.gemm(qa, qb, out_dtype=out_dtype)
+    y2 = fp4.gemm(qa, qb, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(seed)
+    rsel = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, nrows)]))[: max(2, nrows)]
+    rows = np.concatenate([np.repeat(rsel, N), g.integers(0, M, nent)])
+    cols = np.concatenate([np.tile(np.arange(N), rsel.size), g.integers(0, N, nent)])
+    ref, absref = oracle.gemm_entries(fmt, K, ac, asc, ags, bc, bsc, bgs, rows, cols)
+    yh = y.float().cpu().numpy()
+    got = yh[rows, cols].astype(np.float64)
+    ok = gemm_tolerance_ok(got, ref, absref, out_dtype == torch.bfloat16)
+    bad = np.nonzero(~ok)[0]
+    assert bad.size == 0, (M, N, K, rows[bad[:4]], cols[bad[:4]], got[bad[:4]], ref[bad[:4]])
+    assert torch.equal(y, y2)
+
+
+GEMM_SMALL = [(64, 96, 256), (100, 72, 384), (1, 130, 128), (33, 257, 512), (256, 256, 1024),
+              (300, 520, 640), (16, 4096, 4096), (128, 1024, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SMALL)
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_gemm_small_full_check(fmt, M, N, K):
+    _check_gemm(fmt, M, N, K, seed=M + N + K, out_dtype=torch.float32, nrows=min(M, 16), nent=512)
+
+
+LLAMA8B = [(4096, 4096, 4096), (4096, 6144, 4096), (4096, 14336, 4096), (4096, 4096, 14336)]
+
+
+@pytest.mark.parametrize("M,N,K", LLAMA8B, ids=["qkvo", "kv6144", "up", "down"])
+def test_gemm_mx_llama8b_shapes(M, N, K):
+    _check_gemm(fp4.FMT_MXFP4, M, N, K, seed=7, out_dtype=torch.bfloat16, nrows=1, nent=256)
+
+
+LLAMA70B = [(m, n, k) for m in (1, 16, 128, 8192) for (k, n) in ((8192, 28672), (28672, 8192))]
+
+
+@pytest.mark.parametrize("M,N,K", LLAMA70B, ids=["%dx%dx%d" % s for s in LLAMA70B])
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_gemm_llama70b_mlp_shapes(fmt, M, N, K):
+    _check_gemm(fmt, M, N, K, seed=11, out_dtype=torch.bfloat16, nrows=1, nent=128)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_quantize_then_gemm_end_to_end(fmt):
+    """bf16 activations and weights quantized on the GPU (non-rotated, hence
+    bit-identical to the oracle's codes), multiplied on the GPU, against the
+    oracle's quantize + product."""
+    M, N, K = 256, 384, 1024
+    say("end to end", FNAME[fmt])
+    xa = workloads.gemm_activation(M, K, seed=3)
+    xb = workloads.gemm_weight(N, K, seed=3)
+    qa = fp4.quantize(to_dev_bf16(xa), fmt, scale_layout=fp4.SCALES_GEMM)
+    qb = fp4.quantize(to_dev_bf16(xb), fmt, scale_layout=fp4.SCALES_GEMM)
+    y = fp4.gemm(qa, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ca, sa, ga = oracle.quantize(workloads.bf16_bits_to_f32(xa), fmt)
+    cb, sb, gb = oracle.quantize(workloads.bf16_bits_to_f32(xb), fmt)
+    assert np.array_equal(codes_np(qa), ca) and np.array_equal(codes_np(qb), cb)
+    rows = np.repeat(np.arange(0, M, 7), N)
+    cols = np.tile(np.arange(N), np.arange(0, M, 7).size)
+    ref, absref = oracle.gemm_entries(fmt, K, ca, sa, ga, cb, sb, gb, rows, cols)
+    got = y.cpu().numpy()[rows, cols].astype(np.float64)
+    assert np.all(gemm_tolerance_ok(got, ref, absref, False))

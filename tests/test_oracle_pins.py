@@ -40,7 +40,7 @@ MUTANTS = [
     ("mx clamp", "if (e < -127)\n        e = -127;", "if (e < -126)\n        e = -126;"),
     ("gemm drops a sign", "s += av * bv;", "s += av * fabs(bv);"),
     ("gemm forgets tensor scales", "s *= g;", "s *= 1.0;"),
-    ("gemm transposed scale index", "bv *= ora_e8m0_decode(bs[k / G]);", "bv *= ora_e8m0_decode(as[k / G]);"),
+    ("gemm transposed scale index", "bsv = ora_e8m0_decode(bs[b]);", "bsv = ora_e8m0_decode(as[b]);"),
     ("error sums drop a term", "se += (a - b) * (a - b);", "se += (a - b) * (a - b) * 0.5;"),
 ]
 
