@@ -26,7 +26,7 @@ int check_cfg(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
     return FP4_ERR_INVALID_ARG;
   if (rows < 0 || cols < 0 || cols % G != 0) return FP4_ERR_INVALID_ARG;
   // 32-bit block indexing inside the kernels
-  if (rows > (int64_t)1 << 31 || cols > (int64_t)1 << 31 || rows * (cols / G) >= ((int64_t)1 << 32))
+  if (rows >= (int64_t)1 << 31 || cols >= (int64_t)1 << 31 || rows * cols >= ((int64_t)1 << 32))
     return FP4_ERR_UNSUPPORTED;
   return FP4_OK;
 }
@@ -48,6 +48,9 @@ bool gemm_layout(const fp4_qconfig* cfg) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
+
+// NVFP4 workspace: one fp32 partial maximum per workgroup of the amax pass.
+constexpr size_t kNvWorkspace = 2048;
 
 }  // namespace
 
@@ -80,7 +83,7 @@ size_t fp4_scales_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
 
 size_t fp4_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
   if (check_cfg(cfg, rows, cols) != FP4_OK) return 0;
-  return cfg->fmt == FP4_FMT_NVFP4 ? 256 : 0;
+  return cfg->fmt == FP4_FMT_NVFP4 ? kNvWorkspace : 0;
 }
 
 int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols, int64_t r, int64_t kb) {
@@ -111,16 +114,21 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
   }
   if (gs_mode != FP4_GS_COMPUTE && gs_mode != FP4_GS_GIVEN) return FP4_ERR_INVALID_ARG;
   if (!global_scale) return FP4_ERR_INVALID_ARG;
+  float* partials = nullptr;
+  int npart = 0;
   if (gs_mode == FP4_GS_COMPUTE) {
     if (!ws || ws_bytes < fp4_workspace_bytes(cfg, rows, cols)) return FP4_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
-    hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx,
-                                          static_cast<uint32_t*>(ws), global_scale, st);
+    if (empty) return hip_status(fp4lib::launch_amax_final(nullptr, 0, global_scale, st));
+    partials = static_cast<float*>(ws);
+    npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0);
+    hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, partials,
+                                          npart, st);
     if (e != hipSuccess) return FP4_ERR_HIP;
   }
   if (empty) return FP4_OK;
   return hip_status(fp4lib::launch_quantize_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, codes,
-                                               scales, global_scale, st));
+                                               scales, global_scale, partials, npart, st));
 }
 
 int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows,
@@ -134,9 +142,13 @@ int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t
   if (!global_scale) return FP4_ERR_INVALID_ARG;
   if (!ws || ws_bytes < fp4_workspace_bytes(cfg, rows, cols)) return FP4_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
-  return hip_status(fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx,
-                                           static_cast<uint32_t*>(ws), global_scale,
-                                           static_cast<hipStream_t>(stream)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rows == 0 || cols == 0) return hip_status(fp4lib::launch_amax_final(nullptr, 0, global_scale, st));
+  float* partials = static_cast<float*>(ws);
+  const int npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0);
+  hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, partials, npart, st);
+  if (e != hipSuccess) return FP4_ERR_HIP;
+  return hip_status(fp4lib::launch_amax_final(partials, npart, global_scale, st));
 }
 
 int fp4_dequantize(const fp4_qconfig* cfg, const uint8_t* codes, const uint8_t* scales,

@@ -1,12 +1,5 @@
 // quantize.hip -- block-wise MXFP4 / NVFP4 quantization kernels for gfx950.
 //
-// One thread owns one quantization block (32 elements for MXFP4, 16 for
-// NVFP4): it loads the block with 16-byte vector loads, optionally applies the
-// block Hadamard in registers, reduces the block amax, derives the scale,
-// encodes the elements with the hardware FP4 conversion and stores the packed
-// codes with one 16-byte (MXFP4) or 8-byte (NVFP4) store, so that consecutive
-// lanes write consecutive bytes.
-//
 // Method (pages cited by title):
 //  * MXFP4: scale exponent floor(log2(amax)) - 2, E8M0 code clamped to
 //    [0, 254]; elements rounded to nearest-even on the E2M1 grid with
@@ -21,6 +14,19 @@
 //    ("Bridging the Gap ...": group-level rotations Q(X H_k); "Portable FP4
 //    Quantization for Heterogeneous Accelerators", section 2.3: the block
 //    transform fused as an activation butterfly).
+//
+// Work decomposition.  Every quantization block is computed by one thread
+// (butterfly, amax, scale and encode all in registers).  In the tiled kernel a
+// wave owns 64 consecutive blocks of one row: it loads them with fully
+// coalesced 16-byte loads (1 KB per instruction), transposes them through a
+// padded LDS buffer so that each lane holds its own block, and stores the
+// packed codes with one 16-byte (MXFP4) or 8-byte (NVFP4) store per lane, so
+// the wave writes a contiguous range.  Shapes whose rows are not a multiple of
+// 64 blocks use the direct kernel (each thread loads its own block).
+//
+// NVFP4 with a computed tensor scale runs two launches: the amax pass writes
+// one partial maximum per workgroup (no atomics), and the quantize pass
+// reduces those partials in its prologue.
 #include "fp4_device.h"
 #include "launch.h"
 
@@ -29,205 +35,340 @@ using namespace fp4k;
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kAmaxGrid = 512;  // partial maxima written by the amax pass
 
-// ---------------------------------------------------------------- loaders
-// Load the G elements of block (r, kb) as fp32.
-template <int G, int XDT>
-__device__ __forceinline__ void load_block_f32(const void* __restrict__ x, int64_t ldx, int64_t r,
-                                               int64_t kb, float* v) {
-  if constexpr (XDT == FP4_DT_BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + r * ldx +
-                                                    kb * G);
+// ------------------------------------------------------- per-block compute
+// MXFP4 block from 32 fp32 values (rotated in place when ROT); returns the
+// E8M0 code and the four code dwords.
+template <bool ROT>
+__device__ __forceinline__ uint32_t mx_block_f32(float* v, u32x4& out) {
+  if constexpr (ROT) {
+    fwht<32>(v);
 #pragma unroll
-    for (int i = 0; i < G / 8; ++i) {
-      u32x4 w = p[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = bf16_lo(w[j]);
-        v[8 * i + 2 * j + 1] = bf16_hi(w[j]);
-      }
-    }
-  } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + r * ldx + kb * G);
-#pragma unroll
-    for (int i = 0; i < G / 4; ++i) {
-      f32x4 w = p[i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[4 * i + j] = w[j];
-    }
+    for (int i = 0; i < 32; ++i) v[i] = div_sqrt32(v[i]);
   }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  // floor(log2(amax)) = exponent field - 127 for a normal amax; subnormal and
+  // zero amax clamp to the smallest scale (code 0).
+  const uint32_t code = (uint32_t)max((int)((as_u(amax) >> 23) & 0xFFu) - 2, 0);
+  const float sc = e8m0_as_cvt_scale(code);
+  out[0] = enc8_f32(&v[0], sc);
+  out[1] = enc8_f32(&v[8], sc);
+  out[2] = enc8_f32(&v[16], sc);
+  out[3] = enc8_f32(&v[24], sc);
+  return code;
 }
 
-__device__ __forceinline__ uint32_t mx_code_from_amax(float amax) {
-  // floor(log2(amax)) = exponent field - 127 for normal amax; subnormal and
-  // zero amax clamp to the smallest scale (code 0).
-  int ef = (int)((as_u(amax) >> 23) & 0xFFu);
-  return (uint32_t)max(ef - 2, 0);
+// MXFP4 block straight from 16 bf16 pairs: |x| orders like its 15 low bits.
+__device__ __forceinline__ uint32_t mx_block_bf16(const uint32_t* w, u32x4& out) {
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+  const uint32_t amax_bits = (uint32_t)max(m[0], m[1]);
+  const uint32_t code = (uint32_t)max((int)((amax_bits >> 7) & 0xFFu) - 2, 0);
+  const float sc = e8m0_as_cvt_scale(code);
+  // each call encodes 8 elements (4 input dwords) into one output dword
+  out[0] = enc8_bf16(&w[0], sc);
+  out[1] = enc8_bf16(&w[4], sc);
+  out[2] = enc8_bf16(&w[8], sc);
+  out[3] = enc8_bf16(&w[12], sc);
+  return code;
+}
+
+// Tensor-scale constants of one NVFP4 launch.
+struct NvTs {
+  float ts, inv_ts;
+  bool live, small;
+};
+
+__device__ __forceinline__ NvTs make_ts(float ts) {
+  NvTs t;
+  t.ts = ts;
+  t.live = ts > 0.0f;
+  t.small = ts < 0x1p-100f;
+  t.inv_ts = t.live ? 1.0f / ts : 0.0f;
+  return t;
+}
+
+// NVFP4 block from 16 fp32 values (rotated in place when ROT).
+template <bool ROT>
+__device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out) {
+  if constexpr (ROT) {
+    fwht<16>(v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] *= 0.25f;  // 1/sqrt(16), exact
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  uint32_t code = 0;
+  float s = 0.0f;
+  if (T.live) {
+    const float inv6 = 0x1.555556p-3f;  // fl32(1/6)
+    const float h = (amax < 0x1p-100f) ? amax / 6.0f : div_rn(amax, 6.0f, inv6);
+    const float t = (T.small || h < 0x1p-100f) ? h / T.ts : div_rn(h, T.ts, T.inv_ts);
+    code = e4m3_rne_sat(t);
+    s = e4m3_value(code) * T.ts;
+  }
+  out = u32x2{0u, 0u};
+  if (s != 0.0f) {
+    if (s >= 0x1p-100f) {
+      const float rs = 1.0f / s;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(div_rn(v[i], s, rs), v[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = v[i] / s;
+    }
+    out[0] = enc8_f32(&v[0], 1.0f);  // scale operand 2^0: the quotient is already exact
+    out[1] = enc8_f32(&v[8], 1.0f);
+  }
+  return code;
+}
+
+// Unpack a block held as raw 16-byte chunks into fp32.
+template <int XDT, int G>
+__device__ __forceinline__ void unpack(const u32x4* c, float* v) {
+  if constexpr (XDT == FP4_DT_BF16) {
+#pragma unroll
+    for (int i = 0; i < G / 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * i + 2 * j] = bf16_lo(c[i][j]);
+        v[8 * i + 2 * j + 1] = bf16_hi(c[i][j]);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < G / 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * i + j] = as_f(c[i][j]);
+  }
 }
 
 __device__ __forceinline__ void store_mx_scale(uint8_t* __restrict__ scales, int64_t r, int64_t kb,
-                                               int64_t nb, int64_t kchunks, bool gemm_layout,
+                                               int64_t nb, int64_t kchunks, int gemm_layout,
                                                uint32_t code) {
-  int64_t off = gemm_layout ? mx_gemm_scale_offset(r, kb, kchunks) : r * nb + kb;
+  const int64_t off = gemm_layout ? mx_gemm_scale_offset(r, kb, kchunks) : r * nb + kb;
   scales[off] = (uint8_t)code;
 }
 
-// ------------------------------------------------------------------ MXFP4
-template <int XDT, bool ROT>
-__global__ __launch_bounds__(kThreads) void quant_mx_kernel(
-    const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout) {
-  const uint32_t total = rows * nb;
-  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
-    const uint32_t r = b / nb;
-    const uint32_t kb = b - r * nb;
-    u32x4 out[1];
+// Quantize the block held in chunks c and store codes and scale.
+template <int FMT, int XDT, bool ROT>
+__device__ __forceinline__ void quantize_block(const u32x4* c, const NvTs& T, int64_t r, int64_t kb,
+                                               int64_t nb, uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales, int64_t kchunks,
+                                               int gemm_layout) {
+  if constexpr (FMT == FP4_FMT_MXFP4) {
+    u32x4 out;
     uint32_t code;
     if constexpr (XDT == FP4_DT_BF16 && !ROT) {
-      // Raw bf16 words: |x| compares as an unsigned 15-bit integer.
-      const u32x4* p =
-          reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + (int64_t)r * ldx +
-                                         (int64_t)kb * 32);
       uint32_t w[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x4 t = p[i];
-        w[4 * i] = t[0];
-        w[4 * i + 1] = t[1];
-        w[4 * i + 2] = t[2];
-        w[4 * i + 3] = t[3];
-      }
-      u16x2 m = {0, 0};
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
-      uint32_t amax_bits = (uint32_t)max(m[0], m[1]);
-      int ef = (int)((amax_bits >> 7) & 0xFFu);
-      code = (uint32_t)max(ef - 2, 0);
-      const float sc = e8m0_as_cvt_scale(code);
-      // each enc8 call encodes 8 elements (4 input dwords) into one dword
-      out[0][0] = enc8_bf16(&w[0], sc);
-      out[0][1] = enc8_bf16(&w[4], sc);
-      out[0][2] = enc8_bf16(&w[8], sc);
-      out[0][3] = enc8_bf16(&w[12], sc);
+        for (int j = 0; j < 4; ++j) w[4 * i + j] = c[i][j];
+      code = mx_block_bf16(w, out);
     } else {
       float v[32];
-      load_block_f32<32, XDT>(x, ldx, r, kb, v);
-      if constexpr (ROT) {
-        fwht<32>(v);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = div_sqrt32(v[i]);
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      code = mx_code_from_amax(amax);
-      const float sc = e8m0_as_cvt_scale(code);
-      out[0][0] = enc8_f32(&v[0], sc);
-      out[0][1] = enc8_f32(&v[8], sc);
-      out[0][2] = enc8_f32(&v[16], sc);
-      out[0][3] = enc8_f32(&v[24], sc);
+      unpack<XDT, 32>(c, v);
+      code = mx_block_f32<ROT>(v, out);
     }
-    *reinterpret_cast<u32x4*>(codes + (int64_t)r * (nb * 16) + (int64_t)kb * 16) = out[0];
-    store_mx_scale(scales, r, kb, nb, kchunks, gemm_layout != 0, code);
+    *reinterpret_cast<u32x4*>(codes + r * (nb * 16) + kb * 16) = out;
+    store_mx_scale(scales, r, kb, nb, kchunks, gemm_layout, code);
+  } else {
+    float v[16];
+    unpack<XDT, 16>(c, v);
+    u32x2 out;
+    const uint32_t code = nv_block<ROT>(v, T, out);
+    *reinterpret_cast<u32x2*>(codes + r * (nb * 8) + kb * 8) = out;
+    scales[r * nb + kb] = (uint8_t)code;
   }
 }
 
-// ------------------------------------------------------------------ NVFP4
-// Per-block scale code and scale value s = e4m3 * ts (fp32).
-__device__ __forceinline__ uint32_t nv_block_scale(float amax, float ts, float inv_ts,
-                                                   bool ts_exact_path, float* s_out) {
-  const float inv6 = 0x1.555556p-3f;  // fl32(1/6)
-  float h = (amax < 0x1p-100f) ? amax / 6.0f : div_rn(amax, 6.0f, inv6);
-  float t = (ts_exact_path || h < 0x1p-100f) ? h / ts : div_rn(h, ts, inv_ts);
-  uint32_t c = e4m3_rne_sat(t);
-  *s_out = e4m3_value(c) * ts;
-  return c;
+// Max of a workgroup (all threads must call); valid in every thread.
+__device__ __forceinline__ float wg_max(float m) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float red[kThreads / 64];
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+  return r;
 }
 
-template <int XDT, bool ROT>
-__global__ __launch_bounds__(kThreads) void quant_nv_kernel(
+// NVFP4 tensor scale for this launch: either given (*gs), or reduced from the
+// amax pass's partial maxima (workgroup 0 then publishes it to *gs).
+__device__ __forceinline__ NvTs nv_launch_ts(float* __restrict__ gs,
+                                             const float* __restrict__ partials, int npart) {
+  if (npart <= 0) return make_ts(*gs);
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < npart; i += kThreads) m = fmaxf(m, partials[i]);
+  m = wg_max(m);
+  const float ts = m / 2688.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gs = ts;
+  return make_ts(ts);
+}
+
+// ----------------------------------------------------------- tiled kernel
+// Requires nb % 64 == 0.  Wave w of the grid-stride loop owns row r, blocks
+// [64 g, 64 g + 64).
+template <int FMT, int XDT, bool ROT>
+__global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ gs) {
-  const float ts = *gs;
-  const bool live = ts > 0.0f;
-  const bool ts_small = ts < 0x1p-100f;
-  const float inv_ts = live ? 1.0f / ts : 0.0f;
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
+    float* __restrict__ gs, const float* __restrict__ partials, int npart) {
+  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
+  constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
+  constexpr int BB = G * ES;       // bytes per block
+  constexpr int CH = BB / 16;      // 16-byte chunks per block
+  constexpr int STRIDE = BB + 16;  // padded LDS stride: conflict-free 16-byte reads
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][64 * STRIDE];
+
+  NvTs T{};
+  if constexpr (FMT == FP4_FMT_NVFP4) T = nv_launch_ts(gs, partials, npart);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t groups = nb / 64;
+  const uint32_t tiles = rows * groups;
+  uint8_t* l = lds[wave];
+  for (uint32_t base = blockIdx.x * (kThreads / 64); base < tiles; base += gridDim.x * (kThreads / 64)) {
+    const uint32_t tile = base + wave;
+    const bool active = tile < tiles;
+    const uint32_t r = active ? tile / groups : 0;
+    const uint32_t g = active ? tile - r * groups : 0;
+    if (active) {
+      const uint8_t* src = static_cast<const uint8_t*>(x) + ((int64_t)r * ldx + (int64_t)g * 64 * G) * ES;
+      u32x4 t[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) t[j] = *reinterpret_cast<const u32x4*>(src + (j * 64 + lane) * 16);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int c = j * 64 + lane;
+        *reinterpret_cast<u32x4*>(l + (c / CH) * STRIDE + (c % CH) * 16) = t[j];
+      }
+    }
+    __syncthreads();
+    if (active) {
+      u32x4 c[CH];
+#pragma unroll
+      for (int k = 0; k < CH; ++k) c[k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
+      quantize_block<FMT, XDT, ROT>(c, T, r, (int64_t)g * 64 + lane, nb, codes, scales, kchunks,
+                                    gemm_layout);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------- direct kernel
+// Any shape: each thread loads its own block.
+template <int FMT, int XDT, bool ROT>
+__global__ __launch_bounds__(kThreads) void quant_direct_kernel(
+    const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
+    float* __restrict__ gs, const float* __restrict__ partials, int npart) {
+  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
+  constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
+  constexpr int CH = G * ES / 16;
+  NvTs T{};
+  if constexpr (FMT == FP4_FMT_NVFP4) T = nv_launch_ts(gs, partials, npart);
   const uint32_t total = rows * nb;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
     const uint32_t r = b / nb;
     const uint32_t kb = b - r * nb;
-    float v[16];
-    load_block_f32<16, XDT>(x, ldx, r, kb, v);
-    if constexpr (ROT) {
-      fwht<16>(v);
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(x) +
+                                                    ((int64_t)r * ldx + (int64_t)kb * G) * ES);
+    u32x4 c[CH];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] *= 0.25f;  // 1/sqrt(16), exact
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    uint32_t code = 0;
-    float s = 0.0f;
-    if (live) code = nv_block_scale(amax, ts, inv_ts, ts_small, &s);
-    u32x2 out = {0u, 0u};
-    if (s != 0.0f) {
-      const float one = 1.0f;  // scale operand 2^0: the quotient is already exact
-      if (s >= 0x1p-100f) {
-        const float rs = 1.0f / s;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(div_rn(v[i], s, rs), v[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = v[i] / s;
-      }
-      out[0] = enc8_f32(&v[0], one);
-      out[1] = enc8_f32(&v[8], one);
-    }
-    *reinterpret_cast<u32x2*>(codes + (int64_t)r * (nb * 8) + (int64_t)kb * 8) = out;
-    scales[(int64_t)r * nb + kb] = (uint8_t)code;
+    for (int k = 0; k < CH; ++k) c[k] = p[k];
+    quantize_block<FMT, XDT, ROT>(c, T, r, kb, nb, codes, scales, kchunks, gemm_layout);
   }
 }
 
-// Global amax of the (optionally rotated) tensor, then ts = amax / 2688 written
-// to gs_out by the last workgroup to finish, which also returns ws[0..1] to 0.
-template <int XDT, bool ROT>
-__global__ __launch_bounds__(kThreads) void amax_nv_kernel(const void* __restrict__ x, int64_t ldx,
-                                                           uint32_t rows, uint32_t nb,
-                                                           uint32_t* __restrict__ ws,
-                                                           float* __restrict__ gs_out) {
+// --------------------------------------------------------------- amax pass
+// Plain tensor: the maximum |x| needs no block structure, so every 16-byte
+// chunk of every row is read once, fully coalesced.  One partial per workgroup.
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void amax_plain_kernel(const void* __restrict__ x,
+                                                              int64_t ldx, uint32_t rows,
+                                                              uint32_t cpr,
+                                                              float* __restrict__ partials) {
+  constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
+  const uint32_t total = rows * cpr;  // 16-byte chunks
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t mb = 0;  // bf16: max of |x| bits (15 bits)
+  float mf = 0.0f;
+  for (uint32_t i0 = blockIdx.x * kThreads + threadIdx.x; i0 < total; i0 += 4 * stride) {
+    u32x4 t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = i0 + u * stride;
+      if (i < total) {
+        const uint32_t r = i / cpr, c = i - r * cpr;
+        t[u] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(x) + (int64_t)r * ldx * ES + (int64_t)c * 16);
+      } else {
+        t[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (XDT == FP4_DT_BF16) {
+        u16x2 m = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, t[u][j] & 0x7FFF7FFFu));
+        mb = max(mb, (uint32_t)max(m[0], m[1]));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mf = fmaxf(mf, fabsf(as_f(t[u][j])));
+      }
+    }
+  }
+  float m = XDT == FP4_DT_BF16 ? as_f(mb << 16) : mf;
+  m = wg_max(m);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// Rotated tensor: the maximum of the block-Hadamard outputs, block by block.
+template <int XDT>
+__global__ __launch_bounds__(kThreads) void amax_rot_kernel(const void* __restrict__ x, int64_t ldx,
+                                                            uint32_t rows, uint32_t nb,
+                                                            float* __restrict__ partials) {
+  constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
+  constexpr int CH = 16 * ES / 16;
   float m = 0.0f;
   const uint32_t total = rows * nb;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
     const uint32_t r = b / nb;
     const uint32_t kb = b - r * nb;
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(x) +
+                                                    ((int64_t)r * ldx + (int64_t)kb * 16) * ES);
+    u32x4 c[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) c[k] = p[k];
     float v[16];
-    load_block_f32<16, XDT>(x, ldx, r, kb, v);
-    if constexpr (ROT) fwht<16>(v);
+    unpack<XDT, 16>(c, v);
+    fwht<16>(v);
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
   }
-  if constexpr (ROT) m *= 0.25f;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  __shared__ float red[kThreads / 64];
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float mm = red[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) mm = fmaxf(mm, red[i]);
-    atomicMax(&ws[0], as_u(mm));
-    __threadfence();
-    uint32_t ticket = atomicAdd(&ws[1], 1u);
-    if (ticket == gridDim.x - 1) {
-      __threadfence();
-      uint32_t g = atomicExch(&ws[0], 0u);
-      atomicExch(&ws[1], 0u);
-      *gs_out = as_f(g) / 2688.0f;
-    }
-  }
+  m = wg_max(m) * 0.25f;  // 1/sqrt(16), exact
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// Reduce the partial maxima into ts = amax / 2688 (one workgroup).
+__global__ __launch_bounds__(kThreads) void amax_final_kernel(const float* __restrict__ partials,
+                                                              int npart, float* __restrict__ gs) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < npart; i += kThreads) m = fmaxf(m, partials[i]);
+  m = wg_max(m);
+  if (threadIdx.x == 0) *gs = m / 2688.0f;
 }
 
 __global__ void set_scalar_kernel(float* p, float v) { *p = v; }
@@ -239,82 +380,103 @@ __global__ __launch_bounds__(kThreads) void scales_to_gemm_kernel(const uint8_t*
                                                                   uint8_t* __restrict__ dst,
                                                                   uint32_t total) {
   for (uint32_t p = blockIdx.x * kThreads + threadIdx.x; p < total; p += gridDim.x * kThreads) {
-    uint32_t tile = p >> 8, within = p & 255u;
-    uint32_t dw = within >> 2, j = within & 3u;
-    uint32_t h = dw >> 5, rr = dw & 31u;
-    uint32_t rt = tile / kchunks, kc = tile - rt * kchunks;
-    uint32_t r = rt * 32 + rr, kb = kc * 8 + 2 * j + h;
+    const uint32_t tile = p >> 8, within = p & 255u;
+    const uint32_t dw = within >> 2, j = within & 3u;
+    const uint32_t h = dw >> 5, rr = dw & 31u;
+    const uint32_t rt = tile / kchunks, kc = tile - rt * kchunks;
+    const uint32_t r = rt * 32 + rr, kb = kc * 8 + 2 * j + h;
     dst[p] = (r < rows && kb < nb) ? src[(int64_t)r * nb + kb] : (uint8_t)127;
   }
 }
 
-int grid_for(int64_t total) {
-  int64_t g = (total + kThreads - 1) / kThreads;
-  if (g > 8192) g = 8192;
+int grid_cap(int64_t items, int cap) {
+  int64_t g = (items + kThreads - 1) / kThreads;
+  if (g > cap) g = cap;
   if (g < 1) g = 1;
   return (int)g;
+}
+
+template <int FMT, int XDT, bool ROT>
+hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                    uint8_t* scales, int gemm_layout, float* gs, const float* partials, int npart,
+                    hipStream_t st) {
+  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
+  const uint32_t nb = (uint32_t)(cols / G);
+  const int64_t kchunks = mx_gemm_kchunks(cols);
+  if (nb % 64 == 0) {
+    const int64_t waves = rows * (int64_t)(nb / 64);
+    int64_t g = (waves + 3) / 4;
+    if (g > 4096) g = 4096;
+    quant_tile_kernel<FMT, XDT, ROT><<<(int)g, kThreads, 0, st>>>(
+        x, ldx, (uint32_t)rows, nb, codes, scales, kchunks, gemm_layout, gs, partials, npart);
+  } else {
+    quant_direct_kernel<FMT, XDT, ROT><<<grid_cap(rows * (int64_t)nb, 8192), kThreads, 0, st>>>(
+        x, ldx, (uint32_t)rows, nb, codes, scales, kchunks, gemm_layout, gs, partials, npart);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 namespace fp4lib {
 
+int amax_partials(int64_t rows, int64_t cols, int rotate) {
+  // one partial per workgroup of the amax pass
+  const int64_t items = rotate ? rows * (cols / 16) : rows * ((cols + 7) / 8);
+  return grid_cap(items / 4 + 1, kAmaxGrid);
+}
+
 hipError_t launch_quantize_mx(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
                               int64_t ldx, uint8_t* codes, uint8_t* scales, int gemm_layout,
                               hipStream_t st) {
-  const uint32_t nb = (uint32_t)(cols / 32);
-  const int64_t total = rows * (int64_t)nb;
-  const int64_t kchunks = mx_gemm_kchunks(cols);
-  const int grid = grid_for(total);
-#define FP4_QMX(XDT, ROT)                                                                   \
-  quant_mx_kernel<XDT, ROT><<<grid, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, nb, codes, scales, \
-                                                       kchunks, gemm_layout)
   if (xdt == FP4_DT_BF16) {
-    if (rotate) FP4_QMX(FP4_DT_BF16, true); else FP4_QMX(FP4_DT_BF16, false);
-  } else {
-    if (rotate) FP4_QMX(FP4_DT_F32, true); else FP4_QMX(FP4_DT_F32, false);
+    if (rotate)
+      return launch_q<FP4_FMT_MXFP4, FP4_DT_BF16, true>(x, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
+    return launch_q<FP4_FMT_MXFP4, FP4_DT_BF16, false>(x, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
   }
-#undef FP4_QMX
-  return hipGetLastError();
+  if (rotate)
+    return launch_q<FP4_FMT_MXFP4, FP4_DT_F32, true>(x, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
+  return launch_q<FP4_FMT_MXFP4, FP4_DT_F32, false>(x, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
 }
 
 hipError_t launch_amax_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
-                          int64_t ldx, uint32_t* ws, float* gs_out, hipStream_t st) {
-  const uint32_t nb = (uint32_t)(cols / 16);
-  const int64_t total = rows * (int64_t)nb;
-  if (total == 0) {
-    set_scalar_kernel<<<1, 1, 0, st>>>(gs_out, 0.0f);
-    return hipGetLastError();
-  }
-  int64_t g = (total + kThreads - 1) / kThreads;
-  if (g > 2048) g = 2048;
-  const int grid = (int)g;
-#define FP4_AMX(XDT, ROT) \
-  amax_nv_kernel<XDT, ROT><<<grid, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, nb, ws, gs_out)
-  if (xdt == FP4_DT_BF16) {
-    if (rotate) FP4_AMX(FP4_DT_BF16, true); else FP4_AMX(FP4_DT_BF16, false);
+                          int64_t ldx, float* partials, int npart, hipStream_t st) {
+  const int es = xdt == FP4_DT_BF16 ? 2 : 4;
+  if (rotate) {
+    if (xdt == FP4_DT_BF16)
+      amax_rot_kernel<FP4_DT_BF16><<<npart, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, (uint32_t)(cols / 16), partials);
+    else
+      amax_rot_kernel<FP4_DT_F32><<<npart, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, (uint32_t)(cols / 16), partials);
   } else {
-    if (rotate) FP4_AMX(FP4_DT_F32, true); else FP4_AMX(FP4_DT_F32, false);
+    const uint32_t cpr = (uint32_t)(cols * es / 16);
+    if (xdt == FP4_DT_BF16)
+      amax_plain_kernel<FP4_DT_BF16><<<npart, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, cpr, partials);
+    else
+      amax_plain_kernel<FP4_DT_F32><<<npart, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, cpr, partials);
   }
-#undef FP4_AMX
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_final(const float* partials, int npart, float* gs, hipStream_t st) {
+  if (npart <= 0) {
+    set_scalar_kernel<<<1, 1, 0, st>>>(gs, 0.0f);
+  } else {
+    amax_final_kernel<<<1, kThreads, 0, st>>>(partials, npart, gs);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
-                              int64_t ldx, uint8_t* codes, uint8_t* scales, const float* gs,
-                              hipStream_t st) {
-  const uint32_t nb = (uint32_t)(cols / 16);
-  const int64_t total = rows * (int64_t)nb;
-  const int grid = grid_for(total);
-#define FP4_QNV(XDT, ROT) \
-  quant_nv_kernel<XDT, ROT><<<grid, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, nb, codes, scales, gs)
+                              int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
+                              const float* partials, int npart, hipStream_t st) {
   if (xdt == FP4_DT_BF16) {
-    if (rotate) FP4_QNV(FP4_DT_BF16, true); else FP4_QNV(FP4_DT_BF16, false);
-  } else {
-    if (rotate) FP4_QNV(FP4_DT_F32, true); else FP4_QNV(FP4_DT_F32, false);
+    if (rotate)
+      return launch_q<FP4_FMT_NVFP4, FP4_DT_BF16, true>(x, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
+    return launch_q<FP4_FMT_NVFP4, FP4_DT_BF16, false>(x, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
   }
-#undef FP4_QNV
-  return hipGetLastError();
+  if (rotate)
+    return launch_q<FP4_FMT_NVFP4, FP4_DT_F32, true>(x, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
+  return launch_q<FP4_FMT_NVFP4, FP4_DT_F32, false>(x, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
 }
 
 hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
@@ -323,9 +485,9 @@ hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols,
   const int64_t kchunks = mx_gemm_kchunks(cols);
   const int64_t total = ((rows + 31) / 32) * kchunks * 256;
   if (total == 0) return hipSuccess;
-  scales_to_gemm_kernel<<<grid_for(total), kThreads, 0, st>>>(src, (uint32_t)rows, nb,
-                                                              (uint32_t)kchunks, dst,
-                                                              (uint32_t)total);
+  scales_to_gemm_kernel<<<grid_cap(total, 8192), kThreads, 0, st>>>(src, (uint32_t)rows, nb,
+                                                                    (uint32_t)kchunks, dst,
+                                                                    (uint32_t)total);
   return hipGetLastError();
 }
 

@@ -33,9 +33,8 @@
  *   - stream is a hipStream_t passed as void*; NULL means the default stream.
  *     All work is enqueued asynchronously on it; nothing synchronises.
  *   - The caller owns and allocates every buffer.  The library allocates no
- *     device memory and keeps no state between calls, except that the
- *     workspace of fp4_quantize must be zero-filled before its first use; the
- *     library leaves it zero-filled again when each call completes.
+ *     device memory and keeps no state between calls.  Workspaces may hold any
+ *     contents on entry.
  *   - Calls that share a workspace must not overlap in time (same stream is
  *     enough).
  *   - Validation happens on the host before any launch: on error nothing is
@@ -98,8 +97,9 @@ size_t fp4_codes_bytes(int64_t rows, int64_t cols);
  * with the codes ("NVFP4 vs MXFP4", storage overhead).  Host function. */
 size_t fp4_scales_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
 
-/* Workspace bytes fp4_quantize needs (NVFP4 with FP4_GS_COMPUTE: 256 bytes;
- * otherwise 0).  Host function. */
+/* Workspace bytes fp4_quantize and fp4_global_scale need (NVFP4: 2048 bytes,
+ * holding the partial maxima of the global-amax pass; MXFP4: 0).  Host
+ * function. */
 size_t fp4_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
 
 /* Byte index inside the scale array of the scale of (row r, block kb), for the
@@ -116,8 +116,8 @@ int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols,
  *   it to *global_scale; FP4_GS_GIVEN reads ts from *global_scale.  A block
  *   whose scale (e4m3 * ts) is zero stores all-zero codes.
  *   MXFP4 ignores global_scale and gs_mode (global_scale may be NULL).
- * ws/ws_bytes: device workspace of fp4_workspace_bytes() bytes, zero-filled
- * before its first use (may be NULL when that size is 0).
+ * ws/ws_bytes: device workspace of fp4_workspace_bytes() bytes, any contents
+ * (needed only by NVFP4 with FP4_GS_COMPUTE; may be NULL otherwise).
  * Requirements: rows >= 0, cols >= 0, cols % block == 0, ldx >= cols, x
  * 16-byte aligned and ldx * sizeof(xdt) a multiple of 16 (when rows > 1),
  * codes 16-byte aligned.  rows == 0 or cols == 0 is a no-op (for NVFP4 with

@@ -37,7 +37,7 @@ def test_sizes_give_the_formats_bits_per_element(fmt):
     rows, cols = 64, 4096
     bits = 8 * (fp4.fp4_codes_bytes(rows, cols) + fp4.fp4_scales_bytes(cfg, rows, cols)) / (rows * cols)
     assert bits == {fp4.FMT_MXFP4: 4.25, fp4.FMT_NVFP4: 4.5}[fmt]
-    assert fp4.fp4_workspace_bytes(cfg, rows, cols) == (256 if fmt == fp4.FMT_NVFP4 else 0)
+    assert fp4.fp4_workspace_bytes(cfg, rows, cols) == (2048 if fmt == fp4.FMT_NVFP4 else 0)
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 32), (31, 64), (33, 256), (100, 4096 + 128), (257, 288)])
@@ -62,7 +62,7 @@ def test_gemm_scale_layout_is_a_bijection(rows, cols):
 
 def _q(cfg, **kw):
     a = dict(x=FAKE, xdt=fp4.DT_BF16, rows=64, cols=256, ldx=256, codes=FAKE, scales=FAKE,
-             gs=FAKE, gs_mode=fp4.GS_COMPUTE, ws=FAKE, ws_bytes=256, stream=None)
+             gs=FAKE, gs_mode=fp4.GS_COMPUTE, ws=FAKE, ws_bytes=2048, stream=None)
     a.update(kw)
     return fp4.fp4_quantize(cfg, a["x"], a["xdt"], a["rows"], a["cols"], a["ldx"], a["codes"],
                             a["scales"], a["gs"], a["gs_mode"], a["ws"], a["ws_bytes"], a["stream"])
@@ -86,9 +86,9 @@ def test_quantize_rejects_bad_arguments_on_host():
     assert _q(nv, ws=None) == E.FP4_ERR_WORKSPACE
     assert _q(nv, ws_bytes=8) == E.FP4_ERR_WORKSPACE
     assert _q(nv, gs_mode=5) == E.FP4_ERR_INVALID_ARG
-    assert fp4.fp4_global_scale(mx, FAKE, fp4.DT_BF16, 64, 256, 256, FAKE, FAKE, 256, None) == E.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_global_scale(mx, FAKE, fp4.DT_BF16, 64, 256, 256, FAKE, FAKE, 2048, None) == E.FP4_ERR_INVALID_ARG
     assert fp4.fp4_global_scale(nv, FAKE, fp4.DT_BF16, 64, 256, 256, FAKE, None, 0, None) == E.FP4_ERR_WORKSPACE
-    assert fp4.fp4_global_scale(nv, MIS, fp4.DT_BF16, 64, 256, 256, FAKE, FAKE, 256, None) == E.FP4_ERR_ALIGNMENT
+    assert fp4.fp4_global_scale(nv, MIS, fp4.DT_BF16, 64, 256, 256, FAKE, FAKE, 2048, None) == E.FP4_ERR_ALIGNMENT
     assert fp4.fp4_global_scale(nv, FAKE, fp4.DT_BF16, 64, 256, 256, None, FAKE, 256, None) == E.FP4_ERR_INVALID_ARG
     bad = fp4.QConfig(fp4.FMT_MXFP4, 16, 0, 0, 0)
     assert _q(bad) == E.FP4_ERR_INVALID_ARG                  # MXFP4 block must be 32
