@@ -61,203 +61,74 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& 
   tn = in_group / gsize;
 }
 
-// Block tile BM x BN, K-stage of 128 (64 bytes of codes per row), waves each
-// owning a WM x WN sub-tile made of 32x32 MFMA tiles.  Software pipeline:
-// global loads run two stages ahead through two register sets, LDS is double
-// buffered, and the scale dwords (one per 256-K chunk, four MFMA steps) run
-// one chunk ahead.  With PARTIAL, blockIdx.y selects a K-slice (an even number
-// of stages) and fp32 partial sums go to the workspace.
-template <int BM, int BN, int WM, int WN, int YDT, bool PARTIAL>
-__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_mx_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
-    const uint8_t* __restrict__ Bs, void* __restrict__ Y, int64_t ldy, int M, int N, int K,
-    int kchunks, int tiles_n, int kt_per_split, float* __restrict__ part) {
-  constexpr int WAVES_N = BN / WN;
-  constexpr int NT = 64 * (BM / WM) * (BN / WN);  // threads per workgroup
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_CHUNKS = BM * 4, B_CHUNKS = BN * 4;  // 16-byte chunks per stage
-  constexpr int A_PER = (A_CHUNKS + NT - 1) / NT;
-  constexpr int B_PER = (B_CHUNKS + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * 64];
+// MXFP4 GEMM.  Block tile BM x BN, four waves each owning a WM x WN sub-tile
+// of 32x32 MFMA tiles (v_mfma_scale_f32_32x32x64_f8f6f4, accumulators in
+// AGPRs), K-stages of 128 (64 bytes of codes per row, two MFMA steps).
+//
+// Codes and scale tiles stream straight from global memory into an NS-slot
+// LDS ring with global_load_lds_dwordx4 (no staging registers).  A slot holds
+// [A codes BM x 64 B | B codes BN x 64 B | A scale tiles | B scale tiles]
+// (one 256-byte GEMM-layout scale tile per 32 rows for the stage's 256-K
+// chunk), rounded up to whole 4 KB rounds: in each round every thread moves
+// 16 bytes, and the source of each (thread, round) is fixed at kernel start;
+// code rows are 64-byte LDS rows whose 16-byte chunks are XOR-swizzled by
+// choosing the source chunk.  Every iteration issues the same number of DMAs
+// (stages past the end re-load the last stage into the slot that is free), so
+// one exact wait (the later stages' DMAs may stay in flight) and one barrier
+// per stage suffice.  Fragment reads for the next MFMA step and the DMAs are
+// slotted between the MFMAs.  With PARTIAL, blockIdx.y selects a K-slice of
+// an even number of stages and fp32 partial sums go to the workspace.
+template <int BM, int BN, int WM, int WN, int NS>
+struct MxCfg {
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int B_CODES = BM * 64;
+  static constexpr int A_SC = B_CODES + BN * 64;
+  static constexpr int B_SC = A_SC + (BM / 32) * 256;
+  static constexpr int USED = B_SC + (BN / 32) * 256;
+  static constexpr int ROUNDS = (USED + 4095) / 4096;
+  static constexpr int STAGE = ROUNDS * 4096;
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int IN_FLIGHT = (NS - 2) * ROUNDS;  // DMAs allowed after the awaited stage
+  static_assert((BM / WM) * (BN / WN) == 4, "four waves");
+  static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  int tm, tn;
-  tile_of((M + BM - 1) / BM, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int64_t rowbytes = K / 2;
-  const int KT_total = K / 128;
-  const int kt0 = PARTIAL ? blockIdx.y * kt_per_split : 0;
-  const int kt1 = PARTIAL ? min(KT_total, kt0 + kt_per_split) : KT_total;
+// Operand registers of one 64-K MFMA step of a wave: TM A and TN B fragments
+// (16 bytes each) and their scale dwords.
+template <int TM, int TN>
+struct MxFrags {
+  u32x4 a[TM], b[TN];
+};
+template <int TM, int TN>
+struct MxScales {
+  uint32_t a[TM], b[TN];
+};
 
-  // per-thread source rows (clamped into the matrix) and chunk columns
-  const uint8_t* a_src[A_PER];
-  const uint8_t* b_src[B_PER];
-#pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int c = tid + i * NT;
-    a_src[i] = A + (int64_t)min(m0 + (c >> 2), M - 1) * rowbytes + (c & 3) * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    const int c = tid + i * NT;
-    b_src[i] = B + (int64_t)min(n0 + (c >> 2), N - 1) * rowbytes + (c & 3) * 16;
-  }
-
-  u32x4 ra[2][A_PER], rb[2][B_PER];
-  auto gload = [&](int kt, int slot) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-      if (A_CHUNKS % NT == 0 || tid + i * NT < A_CHUNKS)
-        ra[slot][i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * 64);
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i)
-      if (B_CHUNKS % NT == 0 || tid + i * NT < B_CHUNKS)
-        rb[slot][i] = *reinterpret_cast<const u32x4*>(b_src[i] + kt * 64);
-  };
-  auto lstore = [&](int slot, int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int c = tid + i * NT;
-      if (A_CHUNKS % NT == 0 || c < A_CHUNKS) {
-        const int row = c >> 2;
-        *reinterpret_cast<u32x4*>(&lds[buf][row * 64 + (((c & 3) ^ swz4(row)) * 16)]) = ra[slot][i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int c = tid + i * NT;
-      if (B_CHUNKS % NT == 0 || c < B_CHUNKS) {
-        const int row = c >> 2;
-        *reinterpret_cast<u32x4*>(&lds[buf][BM * 64 + row * 64 + (((c & 3) ^ swz4(row)) * 16)]) = rb[slot][i];
-      }
-    }
-  };
-  // Scale dwords of this wave's 32-row tiles for 256-K chunk kc.
-  const uint8_t* as_src[TM];
-  const uint8_t* bs_src[TN];
-  const int rt_max = (M - 1) >> 5, ct_max = (N - 1) >> 5;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-    as_src[i] = As + (int64_t)min((m0 + wm * WM + i * 32) >> 5, rt_max) * kchunks * 256 + lane * 4;
-#pragma unroll
-  for (int j = 0; j < TN; ++j)
-    bs_src[j] = Bs + (int64_t)min((n0 + wn * WN + j * 32) >> 5, ct_max) * kchunks * 256 + lane * 4;
-  uint32_t sa_cur[TM], sb_cur[TN], sa_nxt[TM], sb_nxt[TN];
-  auto sload = [&](int kc) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sa_nxt[i] = *reinterpret_cast<const uint32_t*>(as_src[i] + kc * 256);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sb_nxt[j] = *reinterpret_cast<const uint32_t*>(bs_src[j] + kc * 256);
-  };
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // two MFMA K-steps (sel = first scale byte) from LDS buffer buf
-  auto compute = [&](int buf, int sel0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      i32x8 af[TM], bf[TN];
-      const int q = s * 2 + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        const u32x4 t = *reinterpret_cast<const u32x4*>(&lds[buf][row * 64 + ((q ^ swz4(row)) * 16)]);
-        af[i] = i32x8{(int)t[0], (int)t[1], (int)t[2], (int)t[3], 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = wn * WN + j * 32 + (lane & 31);
-        const u32x4 t = *reinterpret_cast<const u32x4*>(&lds[buf][BM * 64 + row * 64 + ((q ^ swz4(row)) * 16)]);
-        bf[j] = i32x8{(int)t[0], (int)t[1], (int)t[2], (int)t[3], 0, 0, 0, 0};
-      }
-      const int sh = 8 * (sel0 + s);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af[i], bf[j], acc[i][j], 4, 4, 0, (int)(sa_cur[i] >> sh), 0, (int)(sb_cur[j] >> sh));
-    }
-  };
-
-  if (kt0 < kt1) {
-    sload(kt0 >> 1);
-    gload(kt0, 0);
-    if (kt0 + 1 < kt1) gload(kt0 + 1, 1);
-    lstore(0, 0);
-  }
-  __syncthreads();
-  for (int kt = kt0; kt < kt1; kt += 2) {
-    // even stage kt: LDS buffer 0, scale bytes 0 and 1 of chunk kt/2
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sa_cur[i] = sa_nxt[i];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sb_cur[j] = sb_nxt[j];
-    if (kt + 2 < kt1) {
-      sload((kt >> 1) + 1);
-      gload(kt + 2, 0);
-    }
-    compute(0, 0);
-    if (kt + 1 < kt1) lstore(1, 1);
-    __syncthreads();
-    if (kt + 1 >= kt1) break;
-    // odd stage kt+1: LDS buffer 1, scale bytes 2 and 3
-    if (kt + 3 < kt1) gload(kt + 3, 1);
-    compute(1, 2);
-    if (kt + 2 < kt1) lstore(0, 0);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * WM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        const int col = n0 + wn * WN + j * 32 + (lane & 31);
-        if (row < M && col < N) {
-          if constexpr (PARTIAL)
-            part[((int64_t)blockIdx.y * M + row) * N + col] = acc[i][j][e];
-          else
-            store_out<YDT>(Y, ldy, row, col, acc[i][j][e]);
-        }
-      }
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (lds must be the same for the whole wave).  Kept out of the kernel templates:
+// the builtin must not see template-dependent arguments.
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds, 16, 0, 0);
 }
 
-// Large-tile MXFP4 kernel: 256 x 256 block tile, four waves of 128 x 128
-// (4 x 4 MFMA tiles, accumulators in AGPRs).  Codes and scale tiles stream
-// straight from global memory into a 4-slot LDS ring
-// (global_load_lds_dwordx4, no staging registers) three 128-K stages ahead of
-// the MFMAs.  Each lane picks the source chunk that belongs at its LDS
-// position, which applies the XOR swizzle.  A slot holds the stage's A and B
-// codes (2 x 16 KB) and the 16 scale tiles of its 256-K chunk (4 KB): nine
-// 16-byte DMAs per thread per stage and no other global loads in the loop, so
-// one exact wait (vmcnt = the two later stages' 18 loads) and one barrier per
-// stage suffice.  Stages past the end re-load the last stage into the slot
-// that is free, keeping the count constant.
-constexpr int kDmaStages = 4;
-constexpr int kDmaCodeBytes = (256 + 256) * 64;
-constexpr int kDmaStageBytes = kDmaCodeBytes + 16 * 256;
+// gfx9 s_waitcnt immediate: vmcnt in bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]; a field at its maximum does not wait.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
+}
 
-template <int YDT, bool PARTIAL>
-__global__ __launch_bounds__(256) void gemm_mx_dma_kernel(
+template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
+__global__ __launch_bounds__(256) void gemm_mx_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, void* __restrict__ Y, int64_t ldy, int M, int N, int K,
     int kchunks, int tiles_n, int kt_per_split, float* __restrict__ part) {
-  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 4, TN = 4;
+  using C = MxCfg<BM, BN, WM, WN, NS>;
+  constexpr int TM = C::TM, TN = C::TN, ROUNDS = C::ROUNDS;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
-  typedef __attribute__((address_space(3))) void* lds_ptr;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (BN / WN), wn = wave % (BN / WN);
   int tm, tn;
   tile_of((M + BM - 1) / BM, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -266,36 +137,42 @@ __global__ __launch_bounds__(256) void gemm_mx_dma_kernel(
   const int kt0 = PARTIAL ? blockIdx.y * kt_per_split : 0;
   const int kt1 = PARTIAL ? min(KT_total, kt0 + kt_per_split) : KT_total;
 
-  // Code DMAs: instruction i (0..7) of this thread fills slot bytes
-  // [(i*4 + wave)*1024 + lane*16, +16), i.e. row (i*4 + wave)*16 + lane/4
-  // (A rows 0..255, then B rows), chunk lane%4.
-  const uint8_t* src[8];
+  // DMA sources of this thread, one per round: slot byte p = r*4096 + tid*16.
+  const uint8_t* src[ROUNDS];
+  bool code_src[ROUNDS];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = (i * 4 + wave) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz4(row);
-    if (i < 4)
-      src[i] = A + (int64_t)min(m0 + row, M - 1) * rowbytes + chunk * 16;
-    else
-      src[i] = B + (int64_t)min(n0 + row - 256, N - 1) * rowbytes + chunk * 16;
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int p = r * 4096 + tid * 16;
+    if (p < C::B_CODES) {
+      const int row = p >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
+      src[r] = A + (int64_t)min(m0 + row, M - 1) * rowbytes + chunk * 16;
+      code_src[r] = true;
+    } else if (p < C::A_SC) {
+      const int row = (p - C::B_CODES) >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
+      src[r] = B + (int64_t)min(n0 + row, N - 1) * rowbytes + chunk * 16;
+      code_src[r] = true;
+    } else if (p < C::B_SC) {
+      const int t = (p - C::A_SC) >> 8;
+      src[r] = As + (int64_t)min((m0 >> 5) + t, (M - 1) >> 5) * kchunks * 256 + (p & 255);
+      code_src[r] = false;
+    } else if (p < C::USED) {
+      const int t = (p - C::B_SC) >> 8;
+      src[r] = Bs + (int64_t)min((n0 >> 5) + t, (N - 1) >> 5) * kchunks * 256 + (p & 255);
+      code_src[r] = false;
+    } else {  // slot padding: any valid address
+      src[r] = As + (p & 255);
+      code_src[r] = false;
+    }
   }
-  // Scale DMA: scale tile t = wave*4 + lane/16 (A row tiles 0..7, then B row
-  // tiles), bytes (lane%16)*16 of the tile's 256 for the stage's chunk.
-  const uint8_t* ssrc;
-  {
-    const int t = wave * 4 + (lane >> 4);
-    const int64_t rt = t < 8 ? min((m0 >> 5) + t, (M - 1) >> 5) : min((n0 >> 5) + t - 8, (N - 1) >> 5);
-    ssrc = (t < 8 ? As : Bs) + rt * kchunks * 256 + (lane & 15) * 16;
-  }
+  auto slot_of = [&](int kt) __attribute__((always_inline)) {
+    return dyn_lds + (kt % NS) * C::STAGE;
+  };
   auto dma = [&](int kt) __attribute__((always_inline)) {
     const int ks = min(kt, kt1 - 1);  // past the end: reload the last stage
-    uint8_t* slot = dyn_lds + (kt % kDmaStages) * kDmaStageBytes;
+    uint8_t* slot = slot_of(kt);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(src[i] + ks * 64, (lds_ptr)(slot + (i * 4 + wave) * 1024),
-                                       16, 0, 0);
-    __builtin_amdgcn_global_load_lds(ssrc + (ks >> 1) * 256, (lds_ptr)(slot + kDmaCodeBytes + wave * 1024),
-                                     16, 0, 0);
+    for (int r = 0; r < ROUNDS; ++r)
+      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * 4096 + wave * 1024);
   };
 
   f32x16 acc[TM][TN];
@@ -306,54 +183,96 @@ __global__ __launch_bounds__(256) void gemm_mx_dma_kernel(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  auto compute = [&](const uint8_t* slot, int sel0) __attribute__((always_inline)) {
-    uint32_t sa[TM], sb[TN];
+  using Frags = MxFrags<TM, TN>;
+  using Scales = MxScales<TM, TN>;
+  auto read_frags = [&](const uint8_t* slot, int s, Frags& f) __attribute__((always_inline)) {
+    const int q = s * 2 + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      sa[i] = *reinterpret_cast<const uint32_t*>(slot + kDmaCodeBytes + (wm * 4 + i) * 256 + lane * 4);
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * WM + i * 32 + (lane & 31);
+      f.a[i] = *reinterpret_cast<const u32x4*>(slot + row * 64 + ((q ^ swz4(row)) * 16));
+    }
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      sb[j] = *reinterpret_cast<const uint32_t*>(slot + kDmaCodeBytes + (8 + wn * 4 + j) * 256 + lane * 4);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      i32x8 af[TM], bf[TN];
-      const int q = s * 2 + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        const u32x4 t = *reinterpret_cast<const u32x4*>(slot + row * 64 + ((q ^ swz4(row)) * 16));
-        af[i] = i32x8{(int)t[0], (int)t[1], (int)t[2], (int)t[3], 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = BM + wn * WN + j * 32 + (lane & 31);
-        const u32x4 t = *reinterpret_cast<const u32x4*>(slot + row * 64 + ((q ^ swz4(row)) * 16));
-        bf[j] = i32x8{(int)t[0], (int)t[1], (int)t[2], (int)t[3], 0, 0, 0, 0};
-      }
-      const int sh = 8 * (sel0 + s);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af[i], bf[j], acc[i][j], 4, 4, 0, (int)(sa[i] >> sh), 0, (int)(sb[j] >> sh));
+    for (int j = 0; j < TN; ++j) {
+      const int row = wn * WN + j * 32 + (lane & 31);
+      f.b[j] = *reinterpret_cast<const u32x4*>(slot + C::B_CODES + row * 64 + ((q ^ swz4(row)) * 16));
     }
   };
+  auto read_scales = [&](const uint8_t* slot, Scales& sc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      sc.a[i] = *reinterpret_cast<const uint32_t*>(slot + C::A_SC + ((wm * WM) / 32 + i) * 256 + lane * 4);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      sc.b[j] = *reinterpret_cast<const uint32_t*>(slot + C::B_SC + ((wn * WN) / 32 + j) * 256 + lane * 4);
+  };
+  auto mfmas = [&](const Frags& f, const Scales& sc, int sel) __attribute__((always_inline)) {
+    const int sh = 8 * sel;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const i32x8 av = {(int)f.a[i][0], (int)f.a[i][1], (int)f.a[i][2], (int)f.a[i][3], 0, 0, 0, 0};
+        const i32x8 bv = {(int)f.b[j][0], (int)f.b[j][1], (int)f.b[j][2], (int)f.b[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            av, bv, acc[i][j], 4, 4, 0, (int)(sc.a[i] >> sh), 0, (int)(sc.b[j] >> sh));
+      }
+  };
+
+  constexpr int NMF = TM * TN;                       // MFMAs per step
+  constexpr int NRD = TM + TN;                       // fragment reads per step
+  constexpr int PA = NMF < NRD ? NMF : NRD;          // phase A (MFMA, read) pairs
+  constexpr int VPM = (ROUNDS + NMF - 1) / NMF;      // phase B: DMAs per MFMA
+  constexpr int RPM = (NRD + NRD + NMF - 1) / NMF;   // phase B: LDS reads per MFMA
 
   if (kt0 < kt1) {
-    dma(kt0);
-    dma(kt0 + 1);
-    dma(kt0 + 2);
+    // In iteration kt the registers hold step 0 of stage kt (F0, S).  Step
+    // 1's reads go out with step 0's MFMAs; each wave then waits for its own
+    // DMA of stage kt+1 and its LDS reads, the workgroup syncs (stage kt+1
+    // complete everywhere, slot kt read by nobody), the DMA of stage kt+NS
+    // goes into slot kt, and stage kt+1's step-0 reads go out with step 1's
+    // MFMAs.
+#pragma unroll
+    for (int i = 0; i < NS; ++i) dma(kt0 + i);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 1) * ROUNDS, 15));
+    __builtin_amdgcn_s_barrier();
+    Frags F0, F1;
+    Scales S, S1;
+    read_frags(slot_of(kt0), 0, F0);
+    read_scales(slot_of(kt0), S);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     for (int kt = kt0; kt < kt1; ++kt) {
-      // wait for this wave's DMA of stage kt: 18 later loads may stay in
-      // flight (gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14], expcnt and
-      // lgkmcnt at their maxima), and for its own LDS reads of stage kt-1
-      __builtin_amdgcn_s_waitcnt((18 & 15) | (7 << 4) | (0 << 8) | ((18 >> 4) << 14));
+      const int sel0 = (kt & 1) * 2;
+      read_frags(slot_of(kt), 1, F1);
+      mfmas(F0, S, sel0);
+#pragma unroll
+      for (int k = 0; k < PA; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      }
+      if constexpr (NMF > PA) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PA, 0);
+      if constexpr (NRD > PA) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::IN_FLIGHT, 0));
       __builtin_amdgcn_s_barrier();
-      dma(kt + 3);
-      compute(dyn_lds + (kt % kDmaStages) * kDmaStageBytes, (kt & 1) * 2);
+      __builtin_amdgcn_sched_barrier(0);
+      dma(kt + NS);
+      read_frags(slot_of(kt + 1), 0, F0);
+      read_scales(slot_of(kt + 1), S1);
+      mfmas(F1, S, sel0 + 1);
+#pragma unroll
+      for (int k = 0; k < NMF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);  // DMA
+        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // LDS reads
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) S.a[i] = S1.a[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) S.b[j] = S1.b[j];
     }
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));  // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   }
 
 #pragma unroll
@@ -373,13 +292,50 @@ __global__ __launch_bounds__(256) void gemm_mx_dma_kernel(
       }
 }
 
-// The DMA kernel uses more than the default 64 KB of LDS; raise its limit once.
-template <int YDT, bool PARTIAL>
-hipError_t dma_lds_attr(size_t bytes) {
+// The ring needs more than the default 64 KB of LDS; raise the limit once.
+template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
+hipError_t mx_lds_attr() {
   static hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_mx_dma_kernel<YDT, PARTIAL>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+      reinterpret_cast<const void*>(&gemm_mx_kernel<BM, BN, WM, WN, NS, YDT, PARTIAL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, MxCfg<BM, BN, WM, WN, NS>::LDS);
   return status;
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+hipError_t launch_mx_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+                         const uint8_t* b, const uint8_t* bs, void* y, int ydt, int64_t ldy,
+                         int splits, int kt_per, float* part, hipStream_t st) {
+  const int tiles_n = (int)((N + BN - 1) / BN);
+  const dim3 grid((unsigned)(((M + BM - 1) / BM) * tiles_n), (unsigned)splits);
+  const int kchunks = (int)mx_gemm_kchunks(K);
+  const size_t lds = MxCfg<BM, BN, WM, WN, NS>::LDS;
+  hipError_t e;
+  if (splits > 1) {
+    if ((e = mx_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, true>()) != hipSuccess) return e;
+    gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, true><<<grid, 256, lds, st>>>(
+        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+  } else if (ydt == FP4_DT_F32) {
+    if ((e = mx_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, false>()) != hipSuccess) return e;
+    gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, false><<<grid, 256, lds, st>>>(
+        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+  } else {
+    if ((e = mx_lds_attr<BM, BN, WM, WN, NS, FP4_DT_BF16, false>()) != hipSuccess) return e;
+    gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_BF16, false><<<grid, 256, lds, st>>>(
+        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+  }
+  return hipGetLastError();
+}
+
+// Y = 0 (a product over an empty K range).
+__global__ __launch_bounds__(kThreads) void zero_out_kernel(void* __restrict__ Y, int ydt, int M,
+                                                            int N, int64_t ldy) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kThreads) {
+    const int row = (int)(i / N), col = (int)(i - (int64_t)row * N);
+    if (ydt == FP4_DT_F32) store_out<FP4_DT_F32>(Y, ldy, row, col, 0.0f);
+    else store_out<FP4_DT_BF16>(Y, ldy, row, col, 0.0f);
+  }
 }
 
 // Y = sum over splits of the fp32 partials (fixed order), times gscale.
@@ -509,27 +465,29 @@ __global__ __launch_bounds__(kThreads) void gemm_nv_kernel(
 }
 
 struct MxPlan {
-  int cfg;     // 0: 256x256, 1: 128x128, 2: 32x128
+  int cfg;     // 0: 256x256 (large M and N), 1: 128x128, 2: 32x256 (M <= 32)
   int splits;  // split-K factor (1 = none)
-  int kt_per;  // K-stages per split
+  int kt_per;  // K-stages per split (even: slices start on a 256-K scale chunk)
 };
 
 MxPlan plan_mx(int64_t M, int64_t N, int64_t K) {
   MxPlan p{1, 1, (int)(K / 128)};
-  if (M >= 1024 && N >= 1024) p.cfg = 0;
-  else if (M <= 32) p.cfg = 2;
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (M <= 32) p.cfg = 2;
+  else if (big_tiles >= 256) p.cfg = 0;
   else p.cfg = 1;
   const int bm = p.cfg == 0 ? 256 : (p.cfg == 1 ? 128 : 32);
-  const int bn = p.cfg == 0 ? 256 : 128;
+  const int bn = p.cfg == 1 ? 128 : 256;
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int KT = (int)(K / 128);
-  // split K until there are enough workgroups to cover the chip
-  // (only for skinny M, where the partial sums are small next to the weights)
+  // Split K while fewer than 512 workgroups (two per CU) would run, keeping
+  // at least 4 stages per slice.  Only for tiles that leave the chip idle.
   int splits = 1;
-  while (M <= 256 && tiles * splits < 512 && splits < 8 && KT / (splits * 2) >= 4) splits *= 2;
+  if (p.cfg != 0)
+    while (tiles * splits * 2 <= 512 && splits < 16 && KT / (splits * 2) >= 4) splits *= 2;
   p.splits = splits;
   p.kt_per = (KT + splits - 1) / splits;
-  p.kt_per += p.kt_per & 1;  // slices start on a 256-K scale chunk
+  p.kt_per += p.kt_per & 1;
   return p;
 }
 
@@ -546,52 +504,22 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
                           const uint8_t* b, const uint8_t* bs, void* y, int ydt, int64_t ldy,
                           void* ws, size_t ws_bytes, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (K == 0) {  // empty sum
+    zero_out_kernel<<<256, kThreads, 0, st>>>(y, ydt, (int)M, (int)N, ldy);
+    return hipGetLastError();
+  }
   MxPlan p = plan_mx(M, N, K);
-  const int kchunks = (int)mx_gemm_kchunks(K);
   const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_mx_workspace(M, N, K);
   const int splits = split ? p.splits : 1;
   const int kt_per = split ? p.kt_per : (int)(K / 128);
   float* part = static_cast<float*>(ws);
-#define FP4_GMX(BM_, BN_, WM_, WN_)                                                                 \
-  do {                                                                                              \
-    const int tiles_n = (int)((N + BN_ - 1) / BN_);                                                 \
-    dim3 grid((unsigned)(((M + BM_ - 1) / BM_) * tiles_n), (unsigned)splits);                      \
-    const int nt = 64 * (BM_ / WM_) * (BN_ / WN_);                                                  \
-    if (split)                                                                                      \
-      gemm_mx_kernel<BM_, BN_, WM_, WN_, FP4_DT_F32, true><<<grid, nt, 0, st>>>(                    \
-          a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);           \
-    else if (ydt == FP4_DT_F32)                                                                     \
-      gemm_mx_kernel<BM_, BN_, WM_, WN_, FP4_DT_F32, false><<<grid, nt, 0, st>>>(                   \
-          a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);           \
-    else                                                                                            \
-      gemm_mx_kernel<BM_, BN_, WM_, WN_, FP4_DT_BF16, false><<<grid, nt, 0, st>>>(                  \
-          a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);           \
-  } while (0)
-  if (p.cfg == 0) {
-    const int tiles_n = (int)((N + 255) / 256);
-    dim3 grid((unsigned)(((M + 255) / 256) * tiles_n), (unsigned)splits);
-    const size_t lds = (size_t)kDmaStages * kDmaStageBytes;
-    hipError_t e;
-    if (split) {
-      if ((e = dma_lds_attr<FP4_DT_F32, true>(lds)) != hipSuccess) return e;
-      gemm_mx_dma_kernel<FP4_DT_F32, true><<<grid, 256, lds, st>>>(
-          a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
-    } else if (ydt == FP4_DT_F32) {
-      if ((e = dma_lds_attr<FP4_DT_F32, false>(lds)) != hipSuccess) return e;
-      gemm_mx_dma_kernel<FP4_DT_F32, false><<<grid, 256, lds, st>>>(
-          a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
-    } else {
-      if ((e = dma_lds_attr<FP4_DT_BF16, false>(lds)) != hipSuccess) return e;
-      gemm_mx_dma_kernel<FP4_DT_BF16, false><<<grid, 256, lds, st>>>(
-          a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
-    }
-  } else if (p.cfg == 1) {
-    FP4_GMX(128, 128, 64, 64);
-  } else {
-    FP4_GMX(32, 128, 32, 32);
-  }
-#undef FP4_GMX
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (p.cfg == 0)
+    e = launch_mx_cfg<256, 256, 128, 128, 4>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
+  else if (p.cfg == 1)
+    e = launch_mx_cfg<128, 128, 64, 64, 3>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
+  else
+    e = launch_mx_cfg<32, 256, 32, 64, 3>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
   int64_t total = M * N;
   int64_t g = (total + kThreads - 1) / kThreads;
