@@ -121,7 +121,7 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
     if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
     if (empty) return hip_status(fp4lib::launch_amax_final(nullptr, 0, global_scale, st));
     partials = static_cast<float*>(ws);
-    npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0);
+    npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0, xdt);
     hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, partials,
                                           npart, st);
     if (e != hipSuccess) return FP4_ERR_HIP;
@@ -145,7 +145,7 @@ int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (rows == 0 || cols == 0) return hip_status(fp4lib::launch_amax_final(nullptr, 0, global_scale, st));
   float* partials = static_cast<float*>(ws);
-  const int npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0);
+  const int npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0, xdt);
   hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, partials, npart, st);
   if (e != hipSuccess) return FP4_ERR_HIP;
   return hip_status(fp4lib::launch_amax_final(partials, npart, global_scale, st));

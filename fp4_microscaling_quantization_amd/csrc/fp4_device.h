@@ -123,6 +123,31 @@ __device__ __forceinline__ float div_sqrt32(float s) {
   return __builtin_fmaf(s, c_hi, s * c_lo);
 }
 
+// ------------------------------------------------------- quad lane exchange
+// DPP quad permutations: lane i of every group of four reads lane i^1 / i^2.
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+}
+__device__ __forceinline__ float quad_xor1(float v) { return as_f(quad_xor1(as_u(v))); }
+__device__ __forceinline__ float quad_xor2(float v) { return as_f(quad_xor2(as_u(v))); }
+
+// One butterfly stage of the Walsh-Hadamard transform across lanes: element i
+// of lane l pairs with element i of lane l ^ B (B = 1 or 2).  The lower lane
+// keeps a + b, the upper one a - b (a = lower lane's value), as the in-register
+// stage does for the pair (j, j + h).
+template <int B>
+__device__ __forceinline__ void fwht_lane_stage(float* v, int lane) {
+  const bool up = (lane & B) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = B == 1 ? quad_xor1(v[i]) : quad_xor2(v[i]);
+    v[i] = up ? p - v[i] : v[i] + p;
+  }
+}
+
 // ------------------------------------------------------------- scale layout
 // MXFP4 GEMM scale layout: one 256-byte tile per (32 rows) x (8 blocks of 32 =
 // 256 K).  Within a tile, dword (kb % 2) * 32 + (r % 32) holds the scales of

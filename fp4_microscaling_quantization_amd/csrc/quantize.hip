@@ -93,6 +93,36 @@ __device__ __forceinline__ NvTs make_ts(float ts) {
   return t;
 }
 
+// NVFP4 block scale from the block's amax: returns the E4M3 code and sets s
+// to the decoded scale e4m3 * ts (0 when the tensor scale or the block is 0).
+__device__ __forceinline__ uint32_t nv_scale(float amax, const NvTs& T, float& s) {
+  uint32_t code = 0;
+  s = 0.0f;
+  if (T.live) {
+    const float inv6 = 0x1.555556p-3f;  // fl32(1/6)
+    const float h = (amax < 0x1p-100f) ? amax / 6.0f : div_rn(amax, 6.0f, inv6);
+    const float t = (T.small || h < 0x1p-100f) ? h / T.ts : div_rn(h, T.ts, T.inv_ts);
+    code = e4m3_rne_sat(t);
+    s = e4m3_value(code) * T.ts;
+  }
+  return code;
+}
+
+// Eight values of an NVFP4 block -> one dword of codes, q = fl32(v / s)
+// rounded to E2M1 (in place: v is overwritten with the quotients).
+__device__ __forceinline__ uint32_t nv_enc8(float* v, float s) {
+  if (s == 0.0f) return 0u;
+  if (s >= 0x1p-100f) {
+    const float rs = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_copysignf(div_rn(v[i], s, rs), v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] / s;
+  }
+  return enc8_f32(v, 1.0f);  // scale operand 2^0: the quotient is already exact
+}
+
 // NVFP4 block from 16 fp32 values (rotated in place when ROT).
 template <bool ROT>
 __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out) {
@@ -104,28 +134,10 @@ __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  uint32_t code = 0;
-  float s = 0.0f;
-  if (T.live) {
-    const float inv6 = 0x1.555556p-3f;  // fl32(1/6)
-    const float h = (amax < 0x1p-100f) ? amax / 6.0f : div_rn(amax, 6.0f, inv6);
-    const float t = (T.small || h < 0x1p-100f) ? h / T.ts : div_rn(h, T.ts, T.inv_ts);
-    code = e4m3_rne_sat(t);
-    s = e4m3_value(code) * T.ts;
-  }
-  out = u32x2{0u, 0u};
-  if (s != 0.0f) {
-    if (s >= 0x1p-100f) {
-      const float rs = 1.0f / s;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = __builtin_copysignf(div_rn(v[i], s, rs), v[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = v[i] / s;
-    }
-    out[0] = enc8_f32(&v[0], 1.0f);  // scale operand 2^0: the quotient is already exact
-    out[1] = enc8_f32(&v[8], 1.0f);
-  }
+  float s;
+  const uint32_t code = nv_scale(amax, T, s);
+  out[0] = nv_enc8(&v[0], s);
+  out[1] = nv_enc8(&v[8], s);
   return code;
 }
 
@@ -155,37 +167,56 @@ __device__ __forceinline__ void store_mx_scale(uint8_t* __restrict__ scales, int
   scales[off] = (uint8_t)code;
 }
 
-// Quantize the block held in chunks c and store codes and scale.
+// Quantize the block held in chunks c: codes in out (four dwords for MXFP4,
+// the first two for NVFP4), scale code returned.
 template <int FMT, int XDT, bool ROT>
-__device__ __forceinline__ void quantize_block(const u32x4* c, const NvTs& T, int64_t r, int64_t kb,
-                                               int64_t nb, uint8_t* __restrict__ codes,
-                                               uint8_t* __restrict__ scales, int64_t kchunks,
-                                               int gemm_layout) {
+__device__ __forceinline__ uint32_t compute_block(const u32x4* c, const NvTs& T, u32x4& out) {
   if constexpr (FMT == FP4_FMT_MXFP4) {
-    u32x4 out;
-    uint32_t code;
     if constexpr (XDT == FP4_DT_BF16 && !ROT) {
       uint32_t w[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) w[4 * i + j] = c[i][j];
-      code = mx_block_bf16(w, out);
+      return mx_block_bf16(w, out);
     } else {
       float v[32];
       unpack<XDT, 32>(c, v);
-      code = mx_block_f32<ROT>(v, out);
+      return mx_block_f32<ROT>(v, out);
     }
-    *reinterpret_cast<u32x4*>(codes + r * (nb * 16) + kb * 16) = out;
-    store_mx_scale(scales, r, kb, nb, kchunks, gemm_layout, code);
   } else {
     float v[16];
     unpack<XDT, 16>(c, v);
-    u32x2 out;
-    const uint32_t code = nv_block<ROT>(v, T, out);
-    *reinterpret_cast<u32x2*>(codes + r * (nb * 8) + kb * 8) = out;
+    u32x2 o;
+    const uint32_t code = nv_block<ROT>(v, T, o);
+    out = u32x4{o[0], o[1], 0u, 0u};
+    return code;
+  }
+}
+
+// Store the codes and scale of block (r, kb).
+template <int FMT>
+__device__ __forceinline__ void store_block(const u32x4& out, uint32_t code, int64_t r, int64_t kb,
+                                            int64_t nb, uint8_t* __restrict__ codes,
+                                            uint8_t* __restrict__ scales, int64_t kchunks,
+                                            int gemm_layout) {
+  if constexpr (FMT == FP4_FMT_MXFP4) {
+    *reinterpret_cast<u32x4*>(codes + r * (nb * 16) + kb * 16) = out;
+    store_mx_scale(scales, r, kb, nb, kchunks, gemm_layout, code);
+  } else {
+    *reinterpret_cast<u32x2*>(codes + r * (nb * 8) + kb * 8) = u32x2{out[0], out[1]};
     scales[r * nb + kb] = (uint8_t)code;
   }
+}
+
+template <int FMT, int XDT, bool ROT>
+__device__ __forceinline__ void quantize_block(const u32x4* c, const NvTs& T, int64_t r, int64_t kb,
+                                               int64_t nb, uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales, int64_t kchunks,
+                                               int gemm_layout) {
+  u32x4 out;
+  const uint32_t code = compute_block<FMT, XDT, ROT>(c, T, out);
+  store_block<FMT>(out, code, r, kb, nb, codes, scales, kchunks, gemm_layout);
 }
 
 // Max of a workgroup (all threads must call); valid in every thread.
@@ -263,6 +294,246 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
                                     gemm_layout);
     }
     __syncthreads();
+  }
+}
+
+// ------------------------------------------------------- bf16 tile kernels
+// bf16 input, any shape (cols a multiple of the block size, rows 16-byte
+// aligned).  Every quantization block is computed by one lane, in registers;
+// the input arrives with fully coalesced 16-byte non-temporal loads and is
+// transposed through a padded per-wave LDS buffer (stride block + 16 bytes, so
+// both the scattered writes and the per-lane block reads are conflict-free).
+// Only the wave itself touches its LDS buffer: a wave-scope fence and wave
+// barrier order the writes before the reads, with no workgroup barrier.
+// Lanes past the edge of the tensor load an in-bounds chunk again and store
+// nothing.
+__device__ __forceinline__ u32x4 load_nt16(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void unpack8_bf16(const u32x4& w, float* v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = bf16_lo(w[j]);
+    v[2 * j + 1] = bf16_hi(w[j]);
+  }
+}
+
+// NVFP4 tensor scale for one wave, in two steps so that the loads of the
+// partial maxima (or of the given scale) are issued before the tile loads and
+// waiting for them never waits for the tile: nv_ts_issue loads the given
+// *gs, or the amax pass's partials (npart <= kAmaxGrid = 8 x 64: eight loads
+// per lane; indices past the end re-read the last partial, which leaves the
+// maximum unchanged); nv_ts_finish reduces them (wave 0 of workgroup 0
+// publishes the computed scale to *gs).
+struct NvTsLoads {
+  float p[kAmaxGrid / 64];
+};
+
+__device__ __forceinline__ NvTsLoads nv_ts_issue(const float* __restrict__ gs,
+                                                 const float* __restrict__ partials, int npart) {
+  NvTsLoads L;
+  if (npart <= 0) {
+    L.p[0] = *gs;
+  } else {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < kAmaxGrid / 64; ++k) L.p[k] = partials[min(lane + 64 * k, npart - 1)];
+  }
+  return L;
+}
+
+__device__ __forceinline__ NvTs nv_ts_finish(const NvTsLoads& L, float* __restrict__ gs, int npart,
+                                             bool publish) {
+  if (npart <= 0) return make_ts(L.p[0]);
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kAmaxGrid / 64; ++k) m = fmaxf(m, L.p[k]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const float ts = m / 2688.0f;
+  if (publish && (threadIdx.x & 63) == 0) *gs = ts;
+  return make_ts(ts);
+}
+
+// Row tiles (row-major scales: NVFP4, and MXFP4 when asked for row-major
+// scales).  Wave tile (r, w) = blocks [64 w, 64 w + 64) of row r; each wave
+// issues the loads of TPW tiles before any arithmetic, then runs them one by
+// one through its LDS buffer.  The scale bytes of a wave tile are 64
+// consecutive bytes of its row.
+template <int FMT, bool ROT, int TPW>
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(
+    const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t wpr,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
+    float* __restrict__ gs, const float* __restrict__ partials, int npart) {
+  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
+  constexpr int BB = G * 2;        // bytes per block
+  constexpr int CH = BB / 16;      // 16-byte chunks per block
+  constexpr int STRIDE = BB + 16;  // padded LDS stride
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][64 * STRIDE];
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t tiles = rows * wpr;
+  const uint32_t step = gridDim.x * (kThreads / 64) * TPW;
+  uint32_t t0 = (blockIdx.x * (kThreads / 64) + wave) * TPW;
+  if (t0 >= tiles) return;
+  const uint32_t last_chunk = nb * CH - 1;
+  uint8_t* l = lds[wave];
+  u32x4 t[TPW][CH];
+  auto load = [&](uint32_t first) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const uint32_t tile = min(first + u, tiles - 1);
+      const uint32_t r = tile / wpr, w = tile - r * wpr;
+      const uint8_t* row = x + (int64_t)r * ldx_bytes;
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        t[u][j] = load_nt16(row + (int64_t)min(w * 64 * CH + j * 64 + lane, last_chunk) * 16);
+    }
+  };
+  NvTsLoads tsl{};
+  if constexpr (FMT == FP4_FMT_NVFP4) tsl = nv_ts_issue(gs, partials, npart);
+  load(t0);
+  NvTs T{};
+  if constexpr (FMT == FP4_FMT_NVFP4) T = nv_ts_finish(tsl, gs, npart, blockIdx.x == 0 && wave == 0);
+  for (;;) {
+    // all tiles computed before any store, so no store sits between a tile
+    // load and the wait for it
+    u32x4 out[TPW];
+    uint32_t code[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int c = j * 64 + lane;
+        *reinterpret_cast<u32x4*>(l + (c / CH) * STRIDE + (c % CH) * 16) = t[u][j];
+      }
+      wave_lds_sync();
+      u32x4 c[CH];
+#pragma unroll
+      for (int k = 0; k < CH; ++k) c[k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
+      wave_lds_sync();
+      code[u] = compute_block<FMT, FP4_DT_BF16, ROT>(c, T, out[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const uint32_t tile = t0 + u;
+      const uint32_t r = tile / wpr, w = tile - r * wpr;
+      const uint32_t kb = w * 64 + lane;
+      if (tile < tiles && kb < nb)
+        store_block<FMT>(out[u], code[u], r, kb, nb, codes, scales, kchunks, gemm_layout);
+    }
+    t0 += step;
+    if (t0 >= tiles) break;
+    load(t0);
+  }
+}
+
+// MXFP4 with GEMM-layout scales.  A workgroup tile is 32 rows x 256 columns,
+// exactly the rows and K range of one 256-byte scale tile, so the workgroup
+// writes whole scale tiles (from one CU, merged in one L2) instead of
+// scattering bytes over tiles that other workgroups share.  Wave w takes rows
+// 8w .. 8w + 7 of the tile; load j brings rows 2j, 2j + 1 (512 bytes each);
+// after the LDS transpose lane l holds block l % 8 of row l / 8, and the
+// codes of each row (8 blocks) are 128 contiguous bytes.
+template <bool ROT>
+__global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
+    const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t kcs,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks) {
+  constexpr int STRIDE = 64 + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][64 * STRIDE];
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t tiles = ((rows + 31) / 32) * kcs;
+  const uint32_t cpr = nb * 4;  // 16-byte chunks per row
+  uint8_t* l = lds[wave];
+  for (uint32_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const uint32_t rt = tile / kcs, kc = tile - rt * kcs;
+    const uint32_t r0 = rt * 32 + wave * 8;
+    u32x4 t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t r = min(r0 + 2 * j + (lane >> 5), rows - 1);
+      const uint32_t q = min(kc * 32 + (lane & 31), cpr - 1);
+      t[j] = load_nt16(x + (int64_t)r * ldx_bytes + (int64_t)q * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = j * 64 + lane;  // row c / 32 of the wave, chunk c % 32
+      const int blk = (c >> 5) * 8 + ((c & 31) >> 2);
+      *reinterpret_cast<u32x4*>(l + blk * STRIDE + (c & 3) * 16) = t[j];
+    }
+    wave_lds_sync();
+    u32x4 c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
+    wave_lds_sync();
+    const uint32_t r = r0 + (lane >> 3), kb = kc * 8 + (lane & 7);
+    if (r < rows && kb < nb)
+      quantize_block<FP4_FMT_MXFP4, FP4_DT_BF16, ROT>(c, NvTs{}, r, kb, nb, codes, scales, kchunks, 1);
+  }
+}
+
+// NVFP4 tensor amax over bf16 input in the same wave tiles, 16 waves per
+// workgroup, one partial maximum per workgroup.  Rotated: the maximum of the
+// block-Hadamard outputs (8-point transform in registers, then the cross-lane
+// stage; the exact 1/4 is applied to the final maximum).
+constexpr int kAmaxThreads = 1024;
+
+template <bool ROT>
+__global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t* __restrict__ x,
+                                                                  int64_t ldx_bytes, uint32_t rows,
+                                                                  uint32_t cpr, uint32_t wpr,
+                                                                  float* __restrict__ partials) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t tiles = rows * wpr;
+  const uint32_t step = gridDim.x * (kAmaxThreads / 64);
+  uint32_t mb = 0;   // plain: max of |x| bf16 bits
+  float mf = 0.0f;   // rotated: max of |H x| before the 1/4
+  for (uint32_t tile = blockIdx.x * (kAmaxThreads / 64) + wave; tile < tiles; tile += step) {
+    const uint32_t r = tile / wpr;
+    const uint32_t q0 = (tile - r * wpr) * 256 + lane;
+    const uint8_t* row = x + (int64_t)r * ldx_bytes;
+    u32x4 t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = load_nt16(row + (int64_t)min(q0 + 64 * j, cpr - 1) * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (q0 + 64 * j >= cpr) t[j] = u32x4{0u, 0u, 0u, 0u};  // past the row end
+      if constexpr (!ROT) {
+        u16x2 m = __builtin_bit_cast(u16x2, t[j][0] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int k = 1; k < 4; ++k)
+          m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, t[j][k] & 0x7FFF7FFFu));
+        mb = max(mb, (uint32_t)max(m[0], m[1]));
+      } else {
+        float v[8];
+        unpack8_bf16(t[j], v);
+        fwht<8>(v);
+        fwht_lane_stage<1>(v, lane);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mf = fmaxf(mf, fabsf(v[i]));
+      }
+    }
+  }
+  float m = ROT ? mf : as_f(mb << 16);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float red[kAmaxThreads / 64];
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < kAmaxThreads / 64; ++i) r = fmaxf(r, red[i]);
+    partials[blockIdx.x] = ROT ? r * 0.25f : r;  // 1/sqrt(16), exact
   }
 }
 
@@ -403,6 +674,25 @@ hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint
   constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
   const uint32_t nb = (uint32_t)(cols / G);
   const int64_t kchunks = mx_gemm_kchunks(cols);
+  if constexpr (XDT == FP4_DT_BF16) {
+    const uint8_t* xb = static_cast<const uint8_t*>(x);
+    if (FMT == FP4_FMT_MXFP4 && gemm_layout) {
+      const uint32_t kcs = (nb + 7) / 8;
+      int64_t g = ((rows + 31) / 32) * (int64_t)kcs;
+      if (g > 16384) g = 16384;
+      quant_mx_gemm_kernel<ROT><<<(int)g, kThreads, 0, st>>>(xb, ldx * 2, (uint32_t)rows, nb, kcs,
+                                                            codes, scales, kchunks);
+      return hipGetLastError();
+    }
+    constexpr int TPW = FMT == FP4_FMT_MXFP4 ? 1 : 2;
+    const uint32_t wpr = (nb + 63) / 64;
+    const int64_t waves = (rows * (int64_t)wpr + TPW - 1) / TPW;
+    int64_t g = (waves + kThreads / 64 - 1) / (kThreads / 64);
+    if (g > 8192) g = 8192;
+    quant_rows_kernel<FMT, ROT, TPW><<<(int)g, kThreads, 0, st>>>(
+        xb, ldx * 2, (uint32_t)rows, nb, wpr, codes, scales, kchunks, gemm_layout, gs, partials, npart);
+    return hipGetLastError();
+  }
   if (nb % 64 == 0) {
     const int64_t waves = rows * (int64_t)(nb / 64);
     int64_t g = (waves + 3) / 4;
@@ -420,8 +710,14 @@ hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint
 
 namespace fp4lib {
 
-int amax_partials(int64_t rows, int64_t cols, int rotate) {
+int amax_partials(int64_t rows, int64_t cols, int rotate, int xdt) {
   // one partial per workgroup of the amax pass
+  if (xdt == FP4_DT_BF16) {
+    const int64_t tiles = rows * ((cols / 8 + 255) / 256);
+    int64_t g = (tiles + kAmaxThreads / 64 - 1) / (kAmaxThreads / 64);
+    if (g > kAmaxGrid) g = kAmaxGrid;
+    return (int)(g < 1 ? 1 : g);
+  }
   const int64_t items = rotate ? rows * (cols / 16) : rows * ((cols + 7) / 8);
   return grid_cap(items / 4 + 1, kAmaxGrid);
 }
@@ -442,6 +738,16 @@ hipError_t launch_quantize_mx(const void* x, int xdt, int rotate, int64_t rows, 
 hipError_t launch_amax_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
                           int64_t ldx, float* partials, int npart, hipStream_t st) {
   const int es = xdt == FP4_DT_BF16 ? 2 : 4;
+  if (xdt == FP4_DT_BF16) {
+    const uint32_t cpr = (uint32_t)(cols / 8);
+    const uint32_t wpr = (cpr + 255) / 256;
+    const uint8_t* xb = static_cast<const uint8_t*>(x);
+    if (rotate)
+      amax_chunk_kernel<true><<<npart, kAmaxThreads, 0, st>>>(xb, ldx * 2, (uint32_t)rows, cpr, wpr, partials);
+    else
+      amax_chunk_kernel<false><<<npart, kAmaxThreads, 0, st>>>(xb, ldx * 2, (uint32_t)rows, cpr, wpr, partials);
+    return hipGetLastError();
+  }
   if (rotate) {
     if (xdt == FP4_DT_BF16)
       amax_rot_kernel<FP4_DT_BF16><<<npart, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, (uint32_t)(cols / 16), partials);
