@@ -10,9 +10,12 @@ resident in HBM; the step cycles through several copies of every input and
 output so that the 256 MB last-level cache cannot serve a repeat.
 
 ``value`` = algorithmic bytes of the step (bf16 read once + codes + scales)
-divided by the step time, in GB/s.  ``roofline`` reports the slowest kernel
-of the step; its launch duration is measured live with HIP events on
-the launching stream over back-to-back launches of that kernel.
+divided by the step time, in GB/s, over K eagerly launched steps; the same
+step recorded as a HIP graph and replayed is reported beside it
+(``ms_per_step_graph``).  ``roofline`` reports the slowest kernel of the step;
+its launch duration is measured live with HIP events on the launching stream
+around a graph of back-to-back launches of that kernel (a Python loop of
+single launches would be bound by the host).
 
 Also reported in the same line: NMSE of every variant (GPU, and oracle vs GPU
 on a sample), the oracle's own throughput on a bounded sample
@@ -53,7 +56,29 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemm-iters", type=int, default=10)
+    ap.add_argument("--no-copy-probe", action="store_true",
+                    help="skip the untimed 64 MiB device copy used to calibrate HBM byte counters")
     return ap.parse_args()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the recorded PMC runs, or None when
+    no record exists or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "fp4_microscaling_quantization_amd", "traffic_pmc.json")
+    try:
+        rec = json.load(open(path))
+    except OSError:
+        return None, "no PMC record"
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None, "kernel sources changed since the PMC record was taken"
+    b = rec["bytes_per_launch"].get(kernel)
+    if b is None:
+        return None, "no PMC record for this kernel"
+    return b, "FETCH_SIZE + WRITE_SIZE per launch, calibrated by a 64 MiB copy (%s)" % rec["profile"]
 
 
 def main():
@@ -73,7 +98,22 @@ def main():
     dev = torch.device("cuda:0")
     fp4.lib()
     stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
+
+    def sh_now():
+        # the launching stream: torch's current stream (the capture stream
+        # while a graph is being recorded)
+        return torch.cuda.current_stream().cuda_stream
+
+    # Untimed plain device copy of known size (64 MiB read + 64 MiB written):
+    # under a rocprofv3 --pmc run its FETCH_SIZE / WRITE_SIZE readings give the
+    # factor that converts those counters to bytes for the kernels below.
+    if not args.no_copy_probe:
+        src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------------------ workload
     rows, cols = 4096, 4096
@@ -127,16 +167,16 @@ def main():
         if fmt == fp4.FMT_MXFP4:
             rc = fp4.fp4_quantize(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
                                   q.codes.data_ptr(), q.scales.data_ptr(), None, fp4.GS_COMPUTE,
-                                  None, 0, sh)
+                                  None, 0, sh_now())
         elif mode == "amax":
             rc = fp4.fp4_global_scale(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
-                                      q.global_scale.data_ptr(), ws.data_ptr(), 2048, sh)
+                                      q.global_scale.data_ptr(), ws.data_ptr(), 2048, sh_now())
         else:
             rc = fp4.fp4_quantize(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
                                   q.codes.data_ptr(), q.scales.data_ptr(),
                                   q.global_scale.data_ptr(),
                                   fp4.GS_GIVEN if mode == "given" else fp4.GS_COMPUTE,
-                                  ws.data_ptr(), 2048, sh)
+                                  ws.data_ptr(), 2048, sh_now())
         if rc != 0:
             raise RuntimeError("quantize failed: %d" % rc)
 
@@ -144,21 +184,48 @@ def main():
         for v in variants:
             call(v, c, "step")
 
+    def capture(fn):
+        # the step's kernels recorded once; replays launch them with no host work
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    # the same step as one HIP graph per buffer copy, replayed
+    step_graphs = [capture(lambda c=c: run_step(c)) for c in range(copies)]
+    for w in range(args.warmup):
+        step_graphs[w % copies].replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s_ in range(args.steps):
+        step_graphs[s_ % copies].replay()
+    torch.cuda.synchronize()
+    graph_s = (time.perf_counter() - t_start) / max(1, args.steps)
+    del step_graphs
+
+    # timed region of the reported value: K eager steps between two
+    # synchronisations (HIP events on the launching stream alongside)
     for w in range(args.warmup):
         run_step(w % copies)
     torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
-    for s in range(args.steps):
-        run_step(s % copies)
+    ev0.record(stream)
+    for s_ in range(args.steps):
+        run_step(s_ % copies)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     step_s = (t_end - t_start) / max(1, args.steps)
+    step_s_events = ev0.elapsed_time(ev1) * 1e-3 / max(1, args.steps)
     step_bytes = sum(alg_bytes(v[1]) for v in variants)
     value_gbs = step_bytes / step_s / 1e9
 
-    # Per-kernel launch durations, live: each kernel of the step launched
-    # back-to-back over the rotating buffer copies between one pair of HIP
-    # events on the launching stream (average = kernel time + dispatch gap).
+    # Per-kernel launch durations, live: a graph of back-to-back launches of
+    # one kernel over the rotating buffer copies, replayed between one pair of
+    # HIP events on the launching stream (average = kernel time + the gap
+    # between graph nodes).
     reps = 4 * copies
     kern = {}
     for (d, fmt, rot) in variants:
@@ -167,30 +234,35 @@ def main():
         v = (d, fmt, rot)
         tag = "rot" if rot else "plain"
         if fmt == fp4.FMT_MXFP4:
-            parts = [("quant_tile_kernel<mxfp4,bf16,%s>" % tag, "step", alg_bytes(fmt))]
+            parts = [("quant_mx_gemm_kernel<%s>" % tag, "step", alg_bytes(fmt))]
         else:
-            parts = [("amax_%s_kernel<bf16> + amax_final_kernel" % ("rot" if rot else "plain"), "amax", n * 2),
-                     ("quant_tile_kernel<nvfp4,bf16,%s>" % tag, "given", alg_bytes(fmt))]
+            parts = [("amax_chunk_kernel<%s> + amax_final_kernel" % tag, "amax", n * 2),
+                     ("quant_rows_kernel<nvfp4,%s,2>" % tag, "given", alg_bytes(fmt))]
         for label, mode, nbytes in parts:
             call(v, 0, mode)
+            torch.cuda.synchronize()
+            g = capture(lambda: [call(v, i % copies, mode) for i in range(reps)])
+            g.replay()
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for i in range(reps):
-                call(v, i % copies, mode)
+            g.replay()
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / reps
             kern[label] = {"avg_us": us, "alg_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
                            "launches": reps}
+            del g
     dom = max(kern, key=lambda k: kern[k]["avg_us"])
     dk = kern[dom]
+    traffic, traffic_note = measured_traffic(dom.split(" + ")[0])
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dk["gbs"], 1),
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(dk["gbs"] * 1e9 / PEAK_HBM, 4),
-                "traffic": None, "alg_bytes_per_launch": dk["alg_bytes"],
-                "avg_launch_us": round(dk["avg_us"], 3)}
-    log("step %.3f ms, %.1f GB/s; dominant %s %.2f us" % (1e3 * step_s, value_gbs, dom, dk["avg_us"]))
+                "traffic": traffic, "traffic_note": traffic_note,
+                "alg_bytes_per_launch": dk["alg_bytes"], "avg_launch_us": round(dk["avg_us"], 3)}
+    log("step %.3f ms (eager), %.3f ms (graph), %.1f GB/s; dominant %s %.2f us"
+        % (1e3 * step_s, 1e3 * graph_s, value_gbs, dom, dk["avg_us"]))
 
     # -------------------------------------------------------------- NMSE
     nmse = {}
@@ -204,29 +276,34 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        sample_rows = 256
+        # the oracle on the complete step (all rows of every variant), timed
         t_or = 0.0
         b_or = 0
         for v in variants:
             d, fmt, rot = v
-            xh = workloads.bf16_bits_to_f32(host[d][:sample_rows])
+            xh = workloads.bf16_bits_to_f32(host[d])
             t1 = time.perf_counter()
-            c_, s_, ts_ = oracle.quantize(xh, fmt, rotate=rot)
+            oracle.quantize(xh, fmt, rotate=rot)
             t_or += time.perf_counter() - t1
-            b_or += sample_rows * cols * 2 + sample_rows * cols // 2 + sample_rows * cols // fp4.BLOCK[fmt]
-            # NMSE of the same sample, oracle vs GPU
+            b_or += alg_bytes(fmt)
+        cpu = {"value": round(b_or / t_or / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "one complete step: all 4096 rows of each of the 8 variants, single-threaded "
+                         "plain-C oracle (NVFP4 includes its amax pass); same algorithmic bytes as "
+                         "the GPU line",
+               "seconds": round(t_or, 2)}
+        log("cpu baseline %.4f GB/s over %.1fs" % (cpu["value"], t_or))
+        # NMSE of a 256-row sample, oracle vs GPU on the same rows (untimed)
+        sample_rows = 256
+        for v in variants:
+            d, fmt, rot = v
+            xh = workloads.bf16_bits_to_f32(host[d][:sample_rows])
+            c_, s_, ts_ = oracle.quantize(xh, fmt, rotate=rot)
             ref = oracle.dequantize(c_, s_, fmt, ts_, inverse_rotate=rot)
-            o_nmse = oracle.nmse(xh, ref)
             xd = to_dev(np.ascontiguousarray(host[d][:sample_rows]))
             qg = fp4.quantize(xd, fmt, rotate=rot)
             sg = fp4.error_sums(xd, qg).cpu().numpy()
-            nmse[vname(v)].update({"oracle_sample": o_nmse, "gpu_sample": float(sg[0] / sg[1])})
-        cpu = {"value": round(b_or / t_or / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "rows 0..%d of each of the 8 variants (%d elements each), single-threaded "
-                         "plain-C oracle, one pass; same algorithmic bytes as the GPU line"
-                         % (sample_rows - 1, sample_rows * cols),
-               "seconds": round(t_or, 2)}
-        log("cpu baseline %.4f GB/s over %.1fs" % (cpu["value"], t_or))
+            nmse[vname(v)].update({"oracle_sample": oracle.nmse(xh, ref),
+                                   "gpu_sample": float(sg[0] / sg[1])})
 
     # --------------------------------------------------------------- GEMM
     gemm = None
@@ -236,6 +313,10 @@ def main():
     line = {
         "metric": METRIC, "value": round(value_gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * step_s, 4),
+        "ms_per_step_events": round(1e3 * step_s_events, 4),
+        "ms_per_step_graph": round(1e3 * graph_s, 4),
+        "launch": "eager: 12 kernel launches per step through the C ABI (ms_per_step_graph: the "
+                  "same step as one replayed HIP graph)",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "quantize 4096x4096 bf16 x {Gaussian 0.02, Laplace 0.02 + 16/4096 "
@@ -247,8 +328,9 @@ def main():
         "roofline": roofline,
         "kernels": {k: {"avg_us": round(v["avg_us"], 3), "gbs": round(v["gbs"], 1),
                         "frac": round(v["gbs"] * 1e9 / PEAK_HBM, 4)} for k, v in sorted(kern.items())},
-        "kernel_timing": "per-kernel: %d back-to-back launches over rotating copies between one "
-                         "HIP event pair (Gaussian input; both inputs run the same kernels)" % reps,
+        "kernel_timing": "per-kernel: a HIP graph of %d back-to-back launches over rotating copies, "
+                         "replayed between one HIP event pair (Gaussian input; both inputs run the "
+                         "same kernels)" % reps,
         "cpu_baseline": cpu,
         "nmse": nmse,
         "gemm": gemm,
@@ -263,15 +345,28 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    def time_it(fn, reps):
+    def time_it(fn, reps, graph=True):
+        """Average us per call: reps calls recorded as one HIP graph and replayed
+        between two HIP events (graph=False: launched eagerly from Python)."""
         fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            fn(i)
-        e1.record(stream)
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        else:
+            e0.record(stream)
+            for i in range(reps):
+                fn(i)
+            e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps  # us
 
@@ -313,7 +408,7 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
         us_g = time_it(g, iters)
         us_q = time_it(qfn, iters)
         us_l = time_it(layer, iters)
-        us_b = time_it(bf, iters)
+        us_b = time_it(bf, iters, graph=False)
         fl = 2.0 * M * N * K
         res["llama8b_M%d_K%d_N%d" % (M, K, N)] = {
             "fmt": "mxfp4+h32", "gemm_us": round(us_g, 2), "tflops": round(fl / us_g / 1e6, 1),
@@ -352,7 +447,7 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
 
                 us_g = time_it(g, iters)
                 us_l = time_it(layer, iters)
-                us_b = time_it(bf, iters) if fmt == fp4.FMT_MXFP4 else None
+                us_b = time_it(bf, iters, graph=False) if fmt == fp4.FMT_MXFP4 else None
                 fl = 2.0 * Mm * N * K
                 peak = PEAK_FP4 if fmt == fp4.FMT_MXFP4 else PEAK_F16
                 traffic = wbytes + qa.codes.numel() + qa.scales.numel() + Mm * N * 2

@@ -202,9 +202,10 @@ def _dt(t) -> int:
 _ws_cache: dict = {}
 
 
-def _zeroed_workspace(nbytes: int, device):
-    """Per-device workspace for the NVFP4 global-amax pass (the library leaves
-    it zero-filled after each call, so it is reused)."""
+def _scratch_workspace(nbytes: int, device):
+    """Per-device scratch for the NVFP4 global-amax pass (partial maxima; any
+    contents).  One buffer per device and size is reused by every call, so
+    calls that use it must not overlap in time (they do not on one stream)."""
     torch = _torch()
     key = (str(device), nbytes)
     t = _ws_cache.get(key)
@@ -246,7 +247,7 @@ def quantize(x, fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMA
         out.global_scale.copy_(global_scale.reshape(1))
         gs_mode = GS_GIVEN
     wsb = fp4_workspace_bytes(cfg, rows, cols)
-    ws = _zeroed_workspace(wsb, x.device) if wsb else None
+    ws = _scratch_workspace(wsb, x.device) if wsb else None
     rc = fp4_quantize(cfg, x.data_ptr(), _dt(x), rows, cols, x.stride(0), out.codes.data_ptr(),
                       out.scales.data_ptr(), out.global_scale.data_ptr(), gs_mode, _ptr(ws), wsb,
                       _stream())
@@ -262,7 +263,7 @@ def global_scale(x, rotate: bool = False, out=None):
     if out is None:
         out = torch.zeros(1, dtype=torch.float32, device=x.device)
     wsb = fp4_workspace_bytes(cfg, rows, cols)
-    ws = _zeroed_workspace(wsb, x.device)
+    ws = _scratch_workspace(wsb, x.device)
     rc = fp4_global_scale(cfg, x.data_ptr(), _dt(x), rows, cols, x.stride(0), out.data_ptr(),
                           ws.data_ptr(), wsb, _stream())
     _check(rc, "fp4_global_scale")

@@ -96,6 +96,17 @@ __device__ __forceinline__ float div_rn(float a, float b, float r) {
   return __builtin_fmaf(rem, r, q0);
 }
 
+// -fl32(a / b) for b > 0, zero sign included (a = +0 gives -0, a = -0 gives
+// +0), as -rem * r - q0 with one rounding: round-to-nearest-even is
+// symmetric, so every non-zero result is the negated quotient above.  E2M1
+// is sign-magnitude, so encoding the negated quotient and flipping every
+// code's sign bit gives the codes of the quotient itself.
+__device__ __forceinline__ float neg_div_rn(float a, float b, float r) {
+  float q0 = a * r;
+  float rem = __builtin_fmaf(-q0, b, a);
+  return __builtin_fmaf(-rem, r, -q0);
+}
+
 // --------------------------------------------------------------- Hadamard
 // In-place unnormalised Walsh-Hadamard transform (Sylvester order) of N
 // registers.

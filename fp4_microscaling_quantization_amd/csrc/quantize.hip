@@ -109,18 +109,19 @@ __device__ __forceinline__ uint32_t nv_scale(float amax, const NvTs& T, float& s
 }
 
 // Eight values of an NVFP4 block -> one dword of codes, q = fl32(v / s)
-// rounded to E2M1 (in place: v is overwritten with the quotients).
+// rounded to E2M1 (v is overwritten).  For normal scales the quotients are
+// formed negated and the eight sign bits flipped afterwards.
 __device__ __forceinline__ uint32_t nv_enc8(float* v, float s) {
   if (s == 0.0f) return 0u;
   if (s >= 0x1p-100f) {
     const float rs = 1.0f / s;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = __builtin_copysignf(div_rn(v[i], s, rs), v[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = v[i] / s;
+    for (int i = 0; i < 8; ++i) v[i] = neg_div_rn(v[i], s, rs);
+    return enc8_f32(v, 1.0f) ^ 0x88888888u;  // scale operand 2^0: the quotient is exact
   }
-  return enc8_f32(v, 1.0f);  // scale operand 2^0: the quotient is already exact
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = v[i] / s;
+  return enc8_f32(v, 1.0f);
 }
 
 // NVFP4 block from 16 fp32 values (rotated in place when ROT).
