@@ -25,10 +25,12 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// XOR swizzle of 16-byte chunks within a 64-byte LDS row (4 chunks): rows 2r
-// and 2r+1 fall on different banks and 8 (or 16) consecutive rows read by one
-// ds_read_b128 group hit distinct banks.
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// XOR swizzle of 16-byte chunks within a 64-byte LDS row (4 chunks): four
+// consecutive rows share a 256-byte bank line, so rows 4i .. 4i+3 keep their
+// chunk order and each group of four rows rotates it by i.  The fragment reads
+// (lane l: row l % 32, one chunk) then see no bank conflicts (measured with
+// SQ_LDS_BANK_CONFLICT on gfx950; a rotation by bits 1-2 of the row was 2-way).
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
 // Same for 128-byte rows (8 chunks).
 __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 
@@ -61,15 +63,15 @@ __device__ __forceinline__ void tile_of(int tiles_m, int tiles_n, int& tm, int& 
   tn = in_group / gsize;
 }
 
-// MXFP4 GEMM.  Block tile BM x BN, four waves each owning a WM x WN sub-tile
-// of 32x32 MFMA tiles (v_mfma_scale_f32_32x32x64_f8f6f4, accumulators in
+// MXFP4 GEMM.  Block tile BM x BN, four or eight waves each owning a WM x WN
+// sub-tile of 32x32 MFMA tiles (v_mfma_scale_f32_32x32x64_f8f6f4, accumulators in
 // AGPRs), K-stages of 128 (64 bytes of codes per row, two MFMA steps).
 //
 // Codes and scale tiles stream straight from global memory into an NS-slot
 // LDS ring with global_load_lds_dwordx4 (no staging registers).  A slot holds
 // [A codes BM x 64 B | B codes BN x 64 B | A scale tiles | B scale tiles]
 // (one 256-byte GEMM-layout scale tile per 32 rows for the stage's 256-K
-// chunk), rounded up to whole 4 KB rounds: in each round every thread moves
+// chunk), rounded up to whole rounds of 1 KB per wave: in each round every thread moves
 // 16 bytes, and the source of each (thread, round) is fixed at kernel start;
 // code rows are 64-byte LDS rows whose 16-byte chunks are XOR-swizzled by
 // choosing the source chunk.  Every iteration issues the same number of DMAs
@@ -85,11 +87,13 @@ struct MxCfg {
   static constexpr int A_SC = B_CODES + BN * 64;
   static constexpr int B_SC = A_SC + (BM / 32) * 256;
   static constexpr int USED = B_SC + (BN / 32) * 256;
-  static constexpr int ROUNDS = (USED + 4095) / 4096;
-  static constexpr int STAGE = ROUNDS * 4096;
+  static constexpr int NW = (BM / WM) * (BN / WN);          // waves per workgroup
+  static constexpr int RB = NW * 1024;                      // bytes per DMA round
+  static constexpr int ROUNDS = (USED + RB - 1) / RB;
+  static constexpr int STAGE = ROUNDS * RB;
   static constexpr int LDS = NS * STAGE;
   static constexpr int IN_FLIGHT = (NS - 2) * ROUNDS;  // DMAs allowed after the awaited stage
-  static_assert((BM / WM) * (BN / WN) == 4, "four waves");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
 };
 
@@ -112,6 +116,13 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds, 16, 0, 0);
 }
 
+// The scaled MFMA (E2M1 x E2M1, fp32 accumulate) with byte 0 of each scale
+// dword as the E8M0 scale.  A non-template wrapper: the builtin must not see
+// template-dependent arguments.
+__device__ __forceinline__ f32x16 mfma_mx(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, sa, 0, sb);
+}
+
 // gfx9 s_waitcnt immediate: vmcnt in bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]; a field at its maximum does not wait.
 constexpr int waitcnt_imm(int vm, int lgkm) {
@@ -119,7 +130,7 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
-__global__ __launch_bounds__(256) void gemm_mx_kernel(
+__global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, void* __restrict__ Y, int64_t ldy, int M, int N, int K,
     int kchunks, int tiles_n, int kt_per_split, float* __restrict__ part) {
@@ -137,12 +148,12 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(
   const int kt0 = PARTIAL ? blockIdx.y * kt_per_split : 0;
   const int kt1 = PARTIAL ? min(KT_total, kt0 + kt_per_split) : KT_total;
 
-  // DMA sources of this thread, one per round: slot byte p = r*4096 + tid*16.
+  // DMA sources of this thread, one per round: slot byte p = r*RB + tid*16.
   const uint8_t* src[ROUNDS];
   bool code_src[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
-    const int p = r * 4096 + tid * 16;
+    const int p = r * C::RB + tid * 16;
     if (p < C::B_CODES) {
       const int row = p >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
       src[r] = A + (int64_t)min(m0 + row, M - 1) * rowbytes + chunk * 16;
@@ -167,12 +178,23 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(
   auto slot_of = [&](int kt) __attribute__((always_inline)) {
     return dyn_lds + (kt % NS) * C::STAGE;
   };
-  auto dma = [&](int kt) __attribute__((always_inline)) {
+  // A stage's DMA goes out in two parts: rounds [0, H) in the second half of
+  // one iteration and rounds [H, ROUNDS) in the first half of the next, so
+  // that each half iteration asks the address unit for about half a stage.
+  constexpr int H = ROUNDS / 2;
+  auto dma_head = [&](int kt) __attribute__((always_inline)) {
     const int ks = min(kt, kt1 - 1);  // past the end: reload the last stage
     uint8_t* slot = slot_of(kt);
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r)
-      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * 4096 + wave * 1024);
+    for (int r = 0; r < H; ++r)
+      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * C::RB + wave * 1024);
+  };
+  auto dma_tail = [&](int kt) __attribute__((always_inline)) {
+    const int ks = min(kt, kt1 - 1);
+    uint8_t* slot = slot_of(kt);
+#pragma unroll
+    for (int r = H; r < ROUNDS; ++r)
+      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * C::RB + wave * 1024);
   };
 
   f32x16 acc[TM][TN];
@@ -207,34 +229,38 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(
       sc.b[j] = *reinterpret_cast<const uint32_t*>(slot + C::B_SC + ((wn * WN) / 32 + j) * 256 + lane * 4);
   };
   auto mfmas = [&](const Frags& f, const Scales& sc, int sel) __attribute__((always_inline)) {
-    const int sh = 8 * sel;
+    const int sh = 8 * sel;  // byte of the scale dword for this 64-K step
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const i32x8 av = {(int)f.a[i][0], (int)f.a[i][1], (int)f.a[i][2], (int)f.a[i][3], 0, 0, 0, 0};
         const i32x8 bv = {(int)f.b[j][0], (int)f.b[j][1], (int)f.b[j][2], (int)f.b[j][3], 0, 0, 0, 0};
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            av, bv, acc[i][j], 4, 4, 0, (int)(sc.a[i] >> sh), 0, (int)(sc.b[j] >> sh));
+        acc[i][j] = mfma_mx(av, bv, acc[i][j], (int)(sc.a[i] >> sh), (int)(sc.b[j] >> sh));
       }
   };
 
-  constexpr int NMF = TM * TN;                       // MFMAs per step
-  constexpr int NRD = TM + TN;                       // fragment reads per step
-  constexpr int PA = NMF < NRD ? NMF : NRD;          // phase A (MFMA, read) pairs
-  constexpr int VPM = (ROUNDS + NMF - 1) / NMF;      // phase B: DMAs per MFMA
-  constexpr int RPM = (NRD + NRD + NMF - 1) / NMF;   // phase B: LDS reads per MFMA
+  constexpr int NMF = TM * TN;             // MFMAs per 64-K step
+  constexpr int NRD = TM + TN;             // fragment reads per step
+  constexpr int NSC = (TM + TN + 1) / 2;   // scale reads (paired dwords)
+  constexpr int NVA = ROUNDS - H;          // DMAs in the first half iteration
+  constexpr int NVB = H;                   // DMAs in the second half
 
   if (kt0 < kt1) {
-    // In iteration kt the registers hold step 0 of stage kt (F0, S).  Step
-    // 1's reads go out with step 0's MFMAs; each wave then waits for its own
-    // DMA of stage kt+1 and its LDS reads, the workgroup syncs (stage kt+1
-    // complete everywhere, slot kt read by nobody), the DMA of stage kt+NS
-    // goes into slot kt, and stage kt+1's step-0 reads go out with step 1's
-    // MFMAs.
+    // In iteration kt the registers hold step 0 of stage kt (F0, S).  First
+    // half: step 1's reads and the tail of stage kt+NS-1's DMA go out with
+    // step 0's MFMAs.  Each wave then waits for its own DMA of stage kt+1 and
+    // its LDS reads, and the workgroup syncs (stage kt+1 complete everywhere,
+    // slot kt read by nobody).  Second half: the head of stage kt+NS's DMA
+    // into slot kt and stage kt+1's step-0 and scale reads go out with step
+    // 1's MFMAs.
 #pragma unroll
-    for (int i = 0; i < NS; ++i) dma(kt0 + i);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 1) * ROUNDS, 15));
+    for (int i = 0; i < NS - 1; ++i) {
+      dma_head(kt0 + i);
+      dma_tail(kt0 + i);
+    }
+    dma_head(kt0 + NS - 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * ROUNDS + H, 15));
     __builtin_amdgcn_s_barrier();
     Frags F0, F1;
     Scales S, S1;
@@ -244,27 +270,27 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(
     for (int kt = kt0; kt < kt1; ++kt) {
       const int sel0 = (kt & 1) * 2;
       read_frags(slot_of(kt), 1, F1);
+      dma_tail(kt + NS - 1);
       mfmas(F0, S, sel0);
 #pragma unroll
-      for (int k = 0; k < PA; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      for (int k = 0; k < NMF; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+        if (k < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+        if (k < NVA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // DMA
       }
-      if constexpr (NMF > PA) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PA, 0);
-      if constexpr (NRD > PA) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PA, 0);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::IN_FLIGHT, 0));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      dma(kt + NS);
+      dma_head(kt + NS);
       read_frags(slot_of(kt + 1), 0, F0);
       read_scales(slot_of(kt + 1), S1);
       mfmas(F1, S, sel0 + 1);
 #pragma unroll
       for (int k = 0; k < NMF; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);  // DMA
-        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+        if (k < NRD + NSC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (k < NVB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -275,6 +301,8 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   }
 
+  // Epilogue: whole tiles store without bounds checks.
+  const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -283,12 +311,14 @@ __global__ __launch_bounds__(256) void gemm_mx_kernel(
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + wm * WM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
         const int col = n0 + wn * WN + j * 32 + (lane & 31);
-        if (row < M && col < N) {
+        if (full || (row < M && col < N)) {
           if constexpr (PARTIAL)
             part[((int64_t)blockIdx.y * M + row) * N + col] = acc[i][j][e];
           else
             store_out<YDT>(Y, ldy, row, col, acc[i][j][e]);
         }
+        // one accumulator tile at a time (keeps the register footprint small)
+        if (e == 15) __builtin_amdgcn_sched_barrier(0);
       }
 }
 
@@ -312,15 +342,15 @@ hipError_t launch_mx_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, cons
   hipError_t e;
   if (splits > 1) {
     if ((e = mx_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, true>()) != hipSuccess) return e;
-    gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, true><<<grid, 256, lds, st>>>(
+    gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, true><<<grid, (MxCfg<BM, BN, WM, WN, NS>::NW * 64), lds, st>>>(
         a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
   } else if (ydt == FP4_DT_F32) {
     if ((e = mx_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, false>()) != hipSuccess) return e;
-    gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, false><<<grid, 256, lds, st>>>(
+    gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, false><<<grid, (MxCfg<BM, BN, WM, WN, NS>::NW * 64), lds, st>>>(
         a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
   } else {
     if ((e = mx_lds_attr<BM, BN, WM, WN, NS, FP4_DT_BF16, false>()) != hipSuccess) return e;
-    gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_BF16, false><<<grid, 256, lds, st>>>(
+    gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_BF16, false><<<grid, (MxCfg<BM, BN, WM, WN, NS>::NW * 64), lds, st>>>(
         a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
   }
   return hipGetLastError();
@@ -465,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nv_kernel(
 }
 
 struct MxPlan {
-  int cfg;     // 0: 256x256 (large M and N), 1: 128x128, 2: 32x256 (M <= 32)
+  int cfg;     // 0: 256x256, 8 waves (large M and N), 1: 128x128, 2: 32x256 (M <= 32)
   int splits;  // split-K factor (1 = none)
   int kt_per;  // K-stages per split (even: slices start on a 256-K scale chunk)
 };
@@ -515,7 +545,7 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   float* part = static_cast<float*>(ws);
   hipError_t e;
   if (p.cfg == 0)
-    e = launch_mx_cfg<256, 256, 128, 128, 4>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_mx_cfg<256, 256, 128, 64, 4>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
   else if (p.cfg == 1)
     e = launch_mx_cfg<128, 128, 64, 64, 3>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
   else
