@@ -230,8 +230,7 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_code
   if (K > 0) {
     if (!a_codes || !a_scales || !b_codes || !b_scales) return FP4_ERR_INVALID_ARG;
     if (!aligned16(a_codes) || !aligned16(b_codes)) return FP4_ERR_ALIGNMENT;
-    if ((reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(b_scales) & 3u))
-      return FP4_ERR_ALIGNMENT;
+    if (!aligned16(a_scales) || !aligned16(b_scales)) return FP4_ERR_ALIGNMENT;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (fmt == FP4_FMT_MXFP4)

@@ -322,6 +322,227 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
       }
 }
 
+// ------------------------------------------------------------------ NVFP4
+// NVFP4 GEMM on the fp16 MFMA (v_mfma_f32_32x32x16_f16), same ring as the
+// MXFP4 kernel: FP4 codes and E4M3 scales stream into LDS by DMA and each
+// wave expands its own fragments to fp16 in registers (e2m1 * e4m3 is exact
+// in fp16: at most 6 significant bits, magnitudes in [2^-10, 2688]), so LDS
+// holds 4-bit codes and the expansion overlaps the MFMAs.  A stage is K = 128
+// (64 bytes of codes per row); the per-row scale chunk is 16 bytes (16 blocks,
+// K = 256), reloaded with each stage of the pair.  Requires K % 256 == 0.
+//
+// K order inside an MFMA is free as long as A and B agree: a lane reads the
+// same 16 bytes (32 codes, K = 32h .. 32h + 31 of the 64-K step, h = lane /
+// 32) as in the MXFP4 kernel and feeds dword t of them to MFMA t of the step,
+// for A rows and B columns alike.  The fp32 tensor scales multiply the
+// accumulators in the epilogue.
+template <int BM, int BN, int WM, int WN, int NS>
+struct NvCfg {
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int B_CODES = BM * 64;
+  static constexpr int A_SC = B_CODES + BN * 64;
+  static constexpr int B_SC = A_SC + BM * 16;
+  static constexpr int USED = B_SC + BN * 16;
+  static constexpr int NW = (BM / WM) * (BN / WN);
+  static constexpr int RB = NW * 1024;
+  static constexpr int ROUNDS = (USED + RB - 1) / RB;
+  static constexpr int STAGE = ROUNDS * RB;
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int IN_FLIGHT = (NS - 2) * ROUNDS;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
+};
+
+__device__ __forceinline__ f32x16 mfma_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Eight E2M1 codes (one dword, low nibble first) times an fp16 scale.
+__device__ __forceinline__ f16x8 expand8(uint32_t w, _Float16 s) {
+  const f16x2 s2 = {s, s};
+  const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+template <int TM, int TN>
+struct NvFrags {
+  u32x4 a[TM], b[TN];
+  uint32_t sa[TM], sb[TN];  // two E4M3 scale bytes per fragment (blocks of the lane's 32 codes)
+};
+
+template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
+__global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_nv_ring_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ ags,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ bgs,
+    void* __restrict__ Y, int64_t ldy, int M, int N, int K, int tiles_n, int kt_per_split,
+    float* __restrict__ part) {
+  using C = NvCfg<BM, BN, WM, WN, NS>;
+  constexpr int TM = C::TM, TN = C::TN, ROUNDS = C::ROUNDS;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / (BN / WN), wn = wave % (BN / WN);
+  int tm, tn;
+  tile_of((M + BM - 1) / BM, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t rowbytes = K / 2, srow = K / 16;
+  const int KT_total = K / 128;
+  const int kt0 = PARTIAL ? blockIdx.y * kt_per_split : 0;
+  const int kt1 = PARTIAL ? min(KT_total, kt0 + kt_per_split) : KT_total;
+
+  const uint8_t* src[ROUNDS];
+  bool code_src[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int p = r * C::RB + tid * 16;
+    if (p < C::B_CODES) {
+      const int row = p >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
+      src[r] = A + (int64_t)min(m0 + row, M - 1) * rowbytes + chunk * 16;
+      code_src[r] = true;
+    } else if (p < C::A_SC) {
+      const int row = (p - C::B_CODES) >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
+      src[r] = B + (int64_t)min(n0 + row, N - 1) * rowbytes + chunk * 16;
+      code_src[r] = true;
+    } else if (p < C::B_SC) {
+      const int row = (p - C::A_SC) >> 4;
+      src[r] = As + (int64_t)min(m0 + row, M - 1) * srow;
+      code_src[r] = false;
+    } else if (p < C::USED) {
+      const int row = (p - C::B_SC) >> 4;
+      src[r] = Bs + (int64_t)min(n0 + row, N - 1) * srow;
+      code_src[r] = false;
+    } else {
+      src[r] = As;
+      code_src[r] = false;
+    }
+  }
+  auto slot_of = [&](int kt) __attribute__((always_inline)) {
+    return dyn_lds + (kt % NS) * C::STAGE;
+  };
+  constexpr int H = ROUNDS / 2;
+  auto dma_head = [&](int kt) __attribute__((always_inline)) {
+    const int ks = min(kt, kt1 - 1);
+    uint8_t* slot = slot_of(kt);
+#pragma unroll
+    for (int r = 0; r < H; ++r)
+      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 16), slot + r * C::RB + wave * 1024);
+  };
+  auto dma_tail = [&](int kt) __attribute__((always_inline)) {
+    const int ks = min(kt, kt1 - 1);
+    uint8_t* slot = slot_of(kt);
+#pragma unroll
+    for (int r = H; r < ROUNDS; ++r)
+      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 16), slot + r * C::RB + wave * 1024);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  using Frags = NvFrags<TM, TN>;
+  // fragments and scale bytes of step s (0, 1) of stage kt
+  auto read_step = [&](int kt, int s, Frags& f) __attribute__((always_inline)) {
+    const uint8_t* slot = slot_of(kt);
+    const int q = s * 2 + (lane >> 5);
+    const int sb = 8 * (kt & 1) + 4 * s + 2 * (lane >> 5);  // first block of the lane's 32 codes
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * WM + i * 32 + (lane & 31);
+      f.a[i] = *reinterpret_cast<const u32x4*>(slot + row * 64 + ((q ^ swz4(row)) * 16));
+      f.sa[i] = *reinterpret_cast<const uint16_t*>(slot + C::A_SC + row * 16 + sb);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int row = wn * WN + j * 32 + (lane & 31);
+      f.b[j] = *reinterpret_cast<const u32x4*>(slot + C::B_CODES + row * 64 + ((q ^ swz4(row)) * 16));
+      f.sb[j] = *reinterpret_cast<const uint16_t*>(slot + C::B_SC + row * 16 + sb);
+    }
+  };
+  auto mfmas = [&](const Frags& f) __attribute__((always_inline)) {
+    _Float16 sa[TM][2], sbv[TN][2];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      sa[i][0] = (_Float16)e4m3_value(f.sa[i] & 0xFFu);
+      sa[i][1] = (_Float16)e4m3_value((f.sa[i] >> 8) & 0xFFu);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      sbv[j][0] = (_Float16)e4m3_value(f.sb[j] & 0xFFu);
+      sbv[j][1] = (_Float16)e4m3_value((f.sb[j] >> 8) & 0xFFu);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f16x8 av[TM], bv[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) av[i] = expand8(f.a[i][t], sa[i][t >> 1]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bv[j] = expand8(f.b[j][t], sbv[j][t >> 1]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_f16(av[i], bv[j], acc[i][j]);
+    }
+  };
+
+  if (kt0 < kt1) {
+    // Same schedule as the MXFP4 kernel: step 1's reads and the tail of
+    // stage kt+NS-1's DMA with step 0's MFMAs; wait for stage kt+1 and sync;
+    // the head of stage kt+NS's DMA and stage kt+1's step-0 reads with step
+    // 1's MFMAs.
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) {
+      dma_head(kt0 + i);
+      dma_tail(kt0 + i);
+    }
+    dma_head(kt0 + NS - 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * ROUNDS + H, 15));
+    __builtin_amdgcn_s_barrier();
+    Frags F0, F1;
+    read_step(kt0, 0, F0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    for (int kt = kt0; kt < kt1; ++kt) {
+      read_step(kt, 1, F1);
+      dma_tail(kt + NS - 1);
+      mfmas(F0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::IN_FLIGHT, 0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      dma_head(kt + NS);
+      read_step(kt + 1, 0, F0);
+      mfmas(F1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+  }
+
+  const float g = PARTIAL ? 1.0f : (*ags) * (*bgs);
+  const bool full = m0 + BM <= M && n0 + BN <= N;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * WM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        const int col = n0 + wn * WN + j * 32 + (lane & 31);
+        if (full || (row < M && col < N)) {
+          if constexpr (PARTIAL)
+            part[((int64_t)blockIdx.y * M + row) * N + col] = acc[i][j][e];
+          else
+            store_out<YDT>(Y, ldy, row, col, acc[i][j][e] * g);
+        }
+        if (e == 15) __builtin_amdgcn_sched_barrier(0);
+      }
+}
+
 // The ring needs more than the default 64 KB of LDS; raise the limit once.
 template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
 hipError_t mx_lds_attr() {
@@ -356,6 +577,39 @@ hipError_t launch_mx_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, cons
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
+hipError_t nv_lds_attr() {
+  static hipError_t status = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_nv_ring_kernel<BM, BN, WM, WN, NS, YDT, PARTIAL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, NvCfg<BM, BN, WM, WN, NS>::LDS);
+  return status;
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+hipError_t launch_nv_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+                         const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
+                         void* y, int ydt, int64_t ldy, int splits, int kt_per, float* part,
+                         hipStream_t st) {
+  using C = NvCfg<BM, BN, WM, WN, NS>;
+  const int tiles_n = (int)((N + BN - 1) / BN);
+  const dim3 grid((unsigned)(((M + BM - 1) / BM) * tiles_n), (unsigned)splits);
+  hipError_t e;
+  if (splits > 1) {
+    if ((e = nv_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, true>()) != hipSuccess) return e;
+    gemm_nv_ring_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, true><<<grid, C::NW * 64, C::LDS, st>>>(
+        a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
+  } else if (ydt == FP4_DT_F32) {
+    if ((e = nv_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, false>()) != hipSuccess) return e;
+    gemm_nv_ring_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, false><<<grid, C::NW * 64, C::LDS, st>>>(
+        a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
+  } else {
+    if ((e = nv_lds_attr<BM, BN, WM, WN, NS, FP4_DT_BF16, false>()) != hipSuccess) return e;
+    gemm_nv_ring_kernel<BM, BN, WM, WN, NS, FP4_DT_BF16, false><<<grid, C::NW * 64, C::LDS, st>>>(
+        a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
+  }
+  return hipGetLastError();
+}
+
 // Y = 0 (a product over an empty K range).
 __global__ __launch_bounds__(kThreads) void zero_out_kernel(void* __restrict__ Y, int ydt, int M,
                                                             int N, int64_t ldy) {
@@ -368,20 +622,36 @@ __global__ __launch_bounds__(kThreads) void zero_out_kernel(void* __restrict__ Y
   }
 }
 
-// Y = sum over splits of the fp32 partials (fixed order), times gscale.
+// Y = sum over splits of the fp32 partials (fixed order), times
+// (*ga) * (*gb) when the tensor scales are given (NVFP4).
 template <int YDT>
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __restrict__ part,
                                                                  int splits, int M, int N,
                                                                  void* __restrict__ Y,
-                                                                 int64_t ldy) {
+                                                                 int64_t ldy,
+                                                                 const float* __restrict__ ga,
+                                                                 const float* __restrict__ gb) {
   const int64_t total = (int64_t)M * N;
+  const float g = ga ? (*ga) * (*gb) : 1.0f;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * kThreads) {
     float s = 0.0f;
     for (int k = 0; k < splits; ++k) s += part[(int64_t)k * total + i];
     const int row = (int)(i / N), col = (int)(i - (int64_t)row * N);
-    store_out<YDT>(Y, ldy, row, col, s);
+    store_out<YDT>(Y, ldy, row, col, ga ? s * g : s);
   }
+}
+
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t N, void* y,
+                                int ydt, int64_t ldy, const float* ga, const float* gb,
+                                hipStream_t st) {
+  int64_t g = (M * N + kThreads - 1) / kThreads;
+  if (g > 8192) g = 8192;
+  if (ydt == FP4_DT_F32)
+    splitk_reduce_kernel<FP4_DT_F32><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy, ga, gb);
+  else
+    splitk_reduce_kernel<FP4_DT_BF16><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy, ga, gb);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ NVFP4
@@ -551,22 +821,36 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   else
     e = launch_mx_cfg<32, 256, 32, 64, 3>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
-  int64_t total = M * N;
-  int64_t g = (total + kThreads - 1) / kThreads;
-  if (g > 8192) g = 8192;
-  if (ydt == FP4_DT_F32)
-    splitk_reduce_kernel<FP4_DT_F32><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy);
-  else
-    splitk_reduce_kernel<FP4_DT_BF16><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy);
-  return hipGetLastError();
+  return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, nullptr, nullptr, st);
 }
 
-size_t gemm_nv_workspace(int64_t, int64_t, int64_t) { return 0; }
+size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K) {
+  if (K % 256 != 0 || K == 0) return 0;
+  MxPlan p = plan_mx(M, N, K);
+  return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
 
 hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                           const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
-                          void* y, int ydt, int64_t ldy, void*, size_t, hipStream_t st) {
+                          void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (K % 256 == 0 && K > 0) {
+    // LDS ring with in-register fp16 expansion; tiles and split-K as for MXFP4
+    MxPlan p = plan_mx(M, N, K);
+    const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_nv_workspace(M, N, K);
+    const int splits = split ? p.splits : 1;
+    const int kt_per = split ? p.kt_per : (int)(K / 128);
+    float* part = static_cast<float*>(ws);
+    hipError_t e;
+    if (p.cfg == 0)
+      e = launch_nv_cfg<256, 256, 128, 128, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    else if (p.cfg == 1)
+      e = launch_nv_cfg<128, 128, 64, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    else
+      e = launch_nv_cfg<32, 256, 32, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    if (e != hipSuccess || !split) return e;
+    return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, ags, bgs, st);
+  }
   const int tiles_n = (int)((N + 127) / 128);
   const unsigned grid = (unsigned)(((M + 127) / 128) * tiles_n);
   if (ydt == FP4_DT_F32)

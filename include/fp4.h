@@ -184,7 +184,8 @@ int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor,
  *   quantizes both operands with the same rotation setting.
  * ws/ws_bytes: device workspace of fp4_gemm_workspace_bytes() bytes (any
  * contents; used for split-K partial sums).
- * Requirements: M, N >= 0, K >= 0 with K % 128 == 0; codes 16-byte aligned. */
+ * Requirements: M, N >= 0, K >= 0 with K % 128 == 0; codes and scales
+ * 16-byte aligned (both stream into LDS in 16-byte pieces). */
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
 int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K,
              const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,

@@ -140,6 +140,7 @@ def test_gemm_rejects_bad_arguments_on_host():
     assert _g(ydt=9) == E.FP4_ERR_INVALID_ARG
     assert _g(a=MIS) == E.FP4_ERR_ALIGNMENT
     assert _g(bsc=FAKE + 2) == E.FP4_ERR_ALIGNMENT
+    assert _g(asc=FAKE + 4) == E.FP4_ERR_ALIGNMENT  # scales: 16-byte aligned
     assert _g(y=None) == E.FP4_ERR_INVALID_ARG
     assert _g(b=None) == E.FP4_ERR_INVALID_ARG
     assert _g(fmt=fp4.FMT_NVFP4, ags=None) == E.FP4_ERR_INVALID_ARG
