@@ -460,6 +460,19 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
                 if us_b is not None:
                     ent["bf16_torch_us"] = round(us_b, 2)
                     ent["layer_speedup_vs_bf16"] = round(us_b / us_l, 2)
+                if Mm <= 128:
+                    # weight-only product: bf16 activations, the same FP4 weights
+                    w4b = fp4.fp4_gemm_w4a16_workspace_bytes(fmt, Mm, N, K)
+                    w4w = torch.empty(max(w4b, 16), dtype=torch.uint8, device=dev)
+
+                    def w4(i=0):
+                        fp4.gemm_w4a16(a, qw[i % 4], out=y, workspace=w4w if w4b else None)
+
+                    us_w4 = time_it(w4, iters)
+                    t_w4 = wbytes + Mm * K * 2 + Mm * N * 2
+                    ent["w4a16_us"] = round(us_w4, 2)
+                    ent["w4a16_frac_hbm"] = round(t_w4 / (us_w4 * 1e-6) / PEAK_HBM, 4)
+                    ent["w4a16_frac_bf16_peak"] = round(fl / (us_w4 * 1e-6) / PEAK_F16, 4)
                 res["llama70b_%s_M%d_K%d_N%d" % (fname.split("+")[0], Mm, K, N)] = ent
                 log("gemm 70b %s M%d K%d N%d %.1f us" % (fname, Mm, K, N, us_g))
             del qw

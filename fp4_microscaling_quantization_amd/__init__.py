@@ -41,8 +41,8 @@ BLOCK = {FMT_MXFP4: 32, FMT_NVFP4: 16}
 EXPORTED = [
     "fp4_codes_bytes", "fp4_scales_bytes", "fp4_workspace_bytes", "fp4_scale_offset",
     "fp4_quantize", "fp4_global_scale", "fp4_dequantize", "fp4_error_workspace_bytes", "fp4_error_sums",
-    "fp4_scales_to_gemm_layout", "fp4_gemm_workspace_bytes", "fp4_gemm", "fp4_status_str",
-    "fp4_abi_version",
+    "fp4_scales_to_gemm_layout", "fp4_gemm_workspace_bytes", "fp4_gemm",
+    "fp4_gemm_w4a16_workspace_bytes", "fp4_gemm_w4a16", "fp4_status_str", "fp4_abi_version",
 ]
 
 
@@ -99,6 +99,10 @@ def lib():
         L.fp4_gemm_workspace_bytes.argtypes = [I32, I64, I64, I64]
         L.fp4_gemm.restype = ctypes.c_int
         L.fp4_gemm.argtypes = [I32, I64, I64, I64, P, P, P, P, P, P, P, I32, I64, P, SZ, P]
+        L.fp4_gemm_w4a16_workspace_bytes.restype = SZ
+        L.fp4_gemm_w4a16_workspace_bytes.argtypes = [I32, I64, I64, I64]
+        L.fp4_gemm_w4a16.restype = ctypes.c_int
+        L.fp4_gemm_w4a16.argtypes = [I32, I64, I64, I64, P, I64, P, P, P, P, I32, I64, P, SZ, P]
         L.fp4_status_str.restype = ctypes.c_char_p
         L.fp4_status_str.argtypes = [ctypes.c_int]
         L.fp4_abi_version.restype = ctypes.c_int
@@ -174,6 +178,16 @@ def fp4_gemm(fmt, M, N, K, a_codes, a_scales, a_gs, b_codes, b_scales, b_gs, y, 
              ws_bytes, stream) -> int:
     return lib().fp4_gemm(fmt, M, N, K, a_codes, a_scales, a_gs, b_codes, b_scales, b_gs, y, ydt,
                           ldy, ws, ws_bytes, stream)
+
+
+def fp4_gemm_w4a16_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
+    return lib().fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K)
+
+
+def fp4_gemm_w4a16(fmt, M, N, K, a, lda, b_codes, b_scales, b_gs, y, ydt, ldy, ws, ws_bytes,
+                   stream) -> int:
+    return lib().fp4_gemm_w4a16(fmt, M, N, K, a, lda, b_codes, b_scales, b_gs, y, ydt, ldy, ws,
+                                ws_bytes, stream)
 
 
 # ----------------------------------------------------------- torch helpers
@@ -306,6 +320,28 @@ def scales_to_gemm_layout(rowmajor, rows: int, cols: int, fmt: int = FMT_MXFP4):
                       device=rowmajor.device)
     rc = fp4_scales_to_gemm_layout(cfg, rowmajor.data_ptr(), rows, cols, out.data_ptr(), _stream())
     _check(rc, "fp4_scales_to_gemm_layout")
+    return out
+
+
+def gemm_w4a16(a, b: Quantized, out_dtype=None, out=None, workspace=None):
+    """Y = A * dequant(B)^T for bf16 activations A [M, K] (unit stride along K)
+    and quantized weights B (scales in GEMM layout)."""
+    torch = _torch()
+    assert a.dim() == 2 and a.stride(1) == 1 and a.dtype == torch.bfloat16
+    M, K = a.shape
+    fmt, N = b.cfg.fmt, b.rows
+    assert b.cols == K
+    assert fmt == FMT_NVFP4 or b.cfg.scale_layout == SCALES_GEMM, "weights need GEMM-layout scales"
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype or torch.bfloat16, device=a.device)
+    wsb = fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K)
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=a.device)
+    rc = fp4_gemm_w4a16(fmt, M, N, K, a.data_ptr(), a.stride(0), b.codes.data_ptr(),
+                        b.scales.data_ptr(), b.global_scale.data_ptr(), out.data_ptr(), _dt(out),
+                        out.stride(0), _ptr(workspace), wsb if workspace is not None else 0,
+                        _stream())
+    _check(rc, "fp4_gemm_w4a16")
     return out
 
 

@@ -232,6 +232,7 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_code
     if (!aligned16(a_codes) || !aligned16(b_codes)) return FP4_ERR_ALIGNMENT;
     if (!aligned16(a_scales) || !aligned16(b_scales)) return FP4_ERR_ALIGNMENT;
   }
+  if (ws && !aligned16(ws)) return FP4_ERR_ALIGNMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (fmt == FP4_FMT_MXFP4)
     return hip_status(fp4lib::launch_gemm_mx(M, N, K, a_codes, a_scales, b_codes, b_scales, y, ydt,
@@ -239,6 +240,37 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_code
   if (!a_gs || !b_gs) return FP4_ERR_INVALID_ARG;
   return hip_status(fp4lib::launch_gemm_nv(M, N, K, a_codes, a_scales, a_gs, b_codes, b_scales,
                                            b_gs, y, ydt, ldy, ws, ws_bytes, st));
+}
+
+size_t fp4_gemm_w4a16_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
+  if (fmt != FP4_FMT_MXFP4 && fmt != FP4_FMT_NVFP4) return 0;
+  if (M < 0 || N < 0 || K < 0 || K % 256 != 0) return 0;
+  return fp4lib::gemm_w4a16_workspace(M, N, K);
+}
+
+int fp4_gemm_w4a16(int32_t fmt, int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
+                   const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gs, void* y,
+                   int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  if (fmt != FP4_FMT_MXFP4 && fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID_ARG;
+  if (K % 256 != 0) return FP4_ERR_UNSUPPORTED;
+  if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
+    return FP4_ERR_UNSUPPORTED;
+  if (dtype_bytes(ydt) == 0) return FP4_ERR_INVALID_ARG;
+  if (ldy < N) return FP4_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FP4_OK;
+  if (!y) return FP4_ERR_INVALID_ARG;
+  if (K > 0) {
+    if (!a || !b_codes || !b_scales) return FP4_ERR_INVALID_ARG;
+    if (lda < K) return FP4_ERR_INVALID_ARG;
+    if (!aligned16(a) || (M > 1 && (lda * 2) % 16 != 0)) return FP4_ERR_ALIGNMENT;
+    if (!aligned16(b_codes) || !aligned16(b_scales)) return FP4_ERR_ALIGNMENT;
+    if (fmt == FP4_FMT_NVFP4 && !b_gs) return FP4_ERR_INVALID_ARG;
+  }
+  if (ws && !aligned16(ws)) return FP4_ERR_ALIGNMENT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(fp4lib::launch_gemm_w4a16(fmt, M, N, K, a, lda, b_codes, b_scales, b_gs, y,
+                                              ydt, ldy, ws, ws_bytes, st));
 }
 
 }  // extern "C"

@@ -543,6 +543,200 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_nv_
       }
 }
 
+// ------------------------------------------------------------------ W4A16
+// Weight-only FP4: Y[M, N] = A[M, K] (bf16) * dequant(B)[N, K]^T with fp32
+// accumulation on v_mfma_f32_32x32x16_bf16 ("Bridging the Gap ...": the
+// W4A16 control of the FP4 weight formats; decode streams the weights).  The
+// weights' codes and scales go through the same DMA ring as above; each wave
+// expands its own B fragments to bf16 in registers (MXFP4: the hardware
+// decode applies the E8M0 scale exactly; NVFP4: e2m1 * e4m3 in fp32, exact in
+// bf16).  Row tiles are 32 activations high (M is small in decode); the 32
+// rows' bf16 activations come straight from global memory into registers,
+// one stage ahead.  B's K order within a 64-K step is the FP4 kernels' (lane
+// half h, dword t of its 32 codes); A's lane reads the same K positions.
+template <int FMT, int BN, int NS>
+struct W4Cfg {
+  static constexpr int WN = BN / 4, TN = WN / 32;
+  static constexpr int SC_BYTES = FMT == FP4_FMT_MXFP4 ? (BN / 32) * 256 : BN * 16;
+  static constexpr int USED = BN * 64 + SC_BYTES;
+  static constexpr int RB = 4096;  // four waves, 1 KB each per round
+  static constexpr int ROUNDS = (USED + RB - 1) / RB;
+  static constexpr int STAGE = ROUNDS * RB;
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int A_LOADS = 8;  // 16-byte activation loads per lane per stage
+  // vector-memory operations a wave may leave pending once stage kt + 1 has
+  // landed: the later stages' DMA (NS - 2 stages) and the next stage's
+  // activation loads (the activations run only one stage ahead)
+  static constexpr int IN_FLIGHT = (NS - 2) * ROUNDS + A_LOADS;
+  static_assert(NS >= 3 && IN_FLIGHT <= 63, "vmcnt range");
+};
+
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Eight E2M1 codes -> eight bf16 times 2^E (E8M0 scale as the operand's exponent).
+__device__ __forceinline__ u32x4 expand8_bf16_mx(uint32_t w, float scale) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
+}
+
+// Eight E2M1 codes times an E4M3 value (exact products, rounded to bf16 exactly).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+}
+__device__ __forceinline__ u32x4 expand8_bf16_nv(uint32_t w, float s) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  return u32x4{pack_bf16(v0[0] * s, v0[1] * s), pack_bf16(v1[0] * s, v1[1] * s),
+               pack_bf16(v2[0] * s, v2[1] * s), pack_bf16(v3[0] * s, v3[1] * s)};
+}
+
+template <int FMT, int BN, int NS, int YDT, bool PARTIAL>
+__global__ __launch_bounds__(256) void gemm_w4a16_kernel(
+    const uint8_t* __restrict__ A, int64_t lda_bytes, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const float* __restrict__ bgs, void* __restrict__ Y,
+    int64_t ldy, int M, int N, int K, int kchunks, int tiles_n, int kt_per_split,
+    float* __restrict__ part) {
+  using C = W4Cfg<FMT, BN, NS>;
+  constexpr int TN = C::TN, WN = C::WN, ROUNDS = C::ROUNDS;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  tile_of((M + 31) / 32, tiles_n, tm, tn);
+  const int m0 = tm * 32, n0 = tn * BN;
+  const int64_t rowbytes = K / 2;
+  const int KT_total = K / 128;
+  const int kt0 = PARTIAL ? blockIdx.y * kt_per_split : 0;
+  const int kt1 = PARTIAL ? min(KT_total, kt0 + kt_per_split) : KT_total;
+
+  // DMA sources: B code rows, then the scale pieces of the stage.
+  const uint8_t* src[ROUNDS];
+  int kind[ROUNDS];  // 0 codes, 1 MX scale tile, 2 NV scale chunk
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int p = r * C::RB + tid * 16;
+    if (p < BN * 64) {
+      const int row = p >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
+      src[r] = B + (int64_t)min(n0 + row, N - 1) * rowbytes + chunk * 16;
+      kind[r] = 0;
+    } else if (p < C::USED) {
+      const int q = p - BN * 64;
+      if constexpr (FMT == FP4_FMT_MXFP4)
+        src[r] = Bs + (int64_t)min((n0 >> 5) + (q >> 8), (N - 1) >> 5) * kchunks * 256 + (q & 255);
+      else
+        src[r] = Bs + (int64_t)min(n0 + (q >> 4), N - 1) * (K / 16);
+      kind[r] = FMT == FP4_FMT_MXFP4 ? 1 : 2;
+    } else {
+      src[r] = Bs;
+      kind[r] = 2;
+    }
+  }
+  auto slot_of = [&](int kt) __attribute__((always_inline)) {
+    return dyn_lds + (kt % NS) * C::STAGE;
+  };
+  constexpr int H = ROUNDS / 2;
+  auto dma_part = [&](int kt, int r) __attribute__((always_inline)) {
+    const int ks = min(kt, kt1 - 1);
+    const int64_t adv = kind[r] == 0 ? ks * 64 : (kind[r] == 1 ? (ks >> 1) * 256 : (ks >> 1) * 16);
+    dma16(src[r] + adv, slot_of(kt) + r * C::RB + wave * 1024);
+  };
+
+  // activations: lane row m0 + lane % 32 (clamped), K half h = lane / 32
+  const uint8_t* arow = A + (int64_t)min(m0 + (lane & 31), M - 1) * lda_bytes + (lane >> 5) * 64;
+  u32x4 a_cur[8], a_nxt[8];
+  auto load_a = [&](int kt, u32x4* dst) __attribute__((always_inline)) {
+    const int ks = min(kt, kt1 - 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        dst[s * 4 + t] = *reinterpret_cast<const u32x4*>(arow + (int64_t)ks * 256 + s * 128 + t * 16);
+  };
+
+  f32x16 acc[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+
+  // one 64-K step: B fragments of the step from LDS, expanded per MFMA
+  auto step = [&](int kt, int s, const u32x4* a) __attribute__((always_inline)) {
+    const uint8_t* slot = slot_of(kt);
+    const int q = s * 2 + (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int row = wave * WN + j * 32 + (lane & 31);
+      const u32x4 codes = *reinterpret_cast<const u32x4*>(slot + row * 64 + ((q ^ swz4(row)) * 16));
+      if constexpr (FMT == FP4_FMT_MXFP4) {
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(slot + BN * 64 + (row >> 5) * 256 + (lane & 31) * 4 +
+                                                                (lane >> 5) * 128);
+        const float scale = e8m0_as_cvt_scale((sc >> (8 * (2 * (kt & 1) + s))) & 0xFFu);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[j] = mfma_bf16(a[s * 4 + t], expand8_bf16_mx(codes[t], scale), acc[j]);
+      } else {
+        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(
+            slot + BN * 64 + row * 16 + 8 * (kt & 1) + 4 * s + 2 * (lane >> 5));
+        const float s0 = e4m3_value(sc2 & 0xFFu), s1 = e4m3_value(sc2 >> 8);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[j] = mfma_bf16(a[s * 4 + t], expand8_bf16_nv(codes[t], t < 2 ? s0 : s1), acc[j]);
+      }
+    }
+  };
+
+  if (kt0 < kt1) {
+    load_a(kt0, a_cur);
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i)
+#pragma unroll
+      for (int r = 0; r < ROUNDS; ++r) dma_part(kt0 + i, r);
+#pragma unroll
+    for (int r = 0; r < H; ++r) dma_part(kt0 + NS - 1, r);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * ROUNDS + H, 15));
+    __builtin_amdgcn_s_barrier();
+    for (int kt = kt0; kt < kt1; ++kt) {
+      // first half: next stage's activations, the tail of stage kt+NS-1's
+      // DMA, step 0; then wait for stage kt+1 and sync; second half: the
+      // head of stage kt+NS's DMA (into slot kt, read by nobody after the
+      // sync of the next iteration) and step 1.
+      load_a(kt + 1, a_nxt);
+#pragma unroll
+      for (int r = H; r < ROUNDS; ++r) dma_part(kt + NS - 1, r);
+      step(kt, 0, a_cur);
+      step(kt, 1, a_cur);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::IN_FLIGHT, 0));
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int r = 0; r < H; ++r) dma_part(kt + NS, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a_cur[i] = a_nxt[i];
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+  }
+
+  const float g = (FMT == FP4_FMT_NVFP4 && !PARTIAL) ? *bgs : 1.0f;
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = m0 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+      const int col = n0 + wave * WN + j * 32 + (lane & 31);
+      if (row < M && col < N) {
+        if constexpr (PARTIAL)
+          part[((int64_t)blockIdx.y * M + row) * N + col] = acc[j][e];
+        else
+          store_out<YDT>(Y, ldy, row, col, acc[j][e] * g);
+      }
+    }
+}
+
 // The ring needs more than the default 64 KB of LDS; raise the limit once.
 template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
 hipError_t mx_lds_attr() {
@@ -610,6 +804,55 @@ hipError_t launch_nv_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, cons
   return hipGetLastError();
 }
 
+template <int FMT, int YDT, bool PARTIAL>
+hipError_t w4_lds_attr() {
+  static hipError_t status = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_w4a16_kernel<FMT, 256, 3, YDT, PARTIAL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, W4Cfg<FMT, 256, 3>::LDS);
+  return status;
+}
+
+template <int FMT>
+hipError_t launch_w4_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda_bytes,
+                         const uint8_t* b, const uint8_t* bs, const float* bgs, void* y, int ydt,
+                         int64_t ldy, int splits, int kt_per, float* part, hipStream_t st) {
+  using C = W4Cfg<FMT, 256, 3>;
+  const int tiles_n = (int)((N + 255) / 256);
+  const dim3 grid((unsigned)(((M + 31) / 32) * tiles_n), (unsigned)splits);
+  const int kchunks = (int)mx_gemm_kchunks(K);
+  hipError_t e;
+  if (splits > 1) {
+    if ((e = w4_lds_attr<FMT, FP4_DT_F32, true>()) != hipSuccess) return e;
+    gemm_w4a16_kernel<FMT, 256, 3, FP4_DT_F32, true><<<grid, 256, C::LDS, st>>>(
+        a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+  } else if (ydt == FP4_DT_F32) {
+    if ((e = w4_lds_attr<FMT, FP4_DT_F32, false>()) != hipSuccess) return e;
+    gemm_w4a16_kernel<FMT, 256, 3, FP4_DT_F32, false><<<grid, 256, C::LDS, st>>>(
+        a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+  } else {
+    if ((e = w4_lds_attr<FMT, FP4_DT_BF16, false>()) != hipSuccess) return e;
+    gemm_w4a16_kernel<FMT, 256, 3, FP4_DT_BF16, false><<<grid, 256, C::LDS, st>>>(
+        a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+  }
+  return hipGetLastError();
+}
+
+// Split factor of the weight-only GEMM: 32-row tiles, split K while fewer than
+// 512 workgroups would run (at least 4 stages per slice, slices of whole
+// 256-K scale chunks).
+struct W4Plan {
+  int splits, kt_per;
+};
+W4Plan plan_w4(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 31) / 32) * ((N + 255) / 256);
+  const int KT = (int)(K / 128);
+  int splits = 1;
+  while (tiles * splits * 2 <= 512 && splits < 16 && KT / (splits * 2) >= 4) splits *= 2;
+  int kt_per = (KT + splits - 1) / splits;
+  kt_per += kt_per & 1;
+  return W4Plan{splits, kt_per};
+}
+
 // Y = 0 (a product over an empty K range).
 __global__ __launch_bounds__(kThreads) void zero_out_kernel(void* __restrict__ Y, int ydt, int M,
                                                             int N, int64_t ldy) {
@@ -622,8 +865,8 @@ __global__ __launch_bounds__(kThreads) void zero_out_kernel(void* __restrict__ Y
   }
 }
 
-// Y = sum over splits of the fp32 partials (fixed order), times
-// (*ga) * (*gb) when the tensor scales are given (NVFP4).
+// Y = sum over splits of the fp32 partials (fixed order), times the tensor
+// scales that are given (NVFP4: (*ga) * (*gb); weight-only NVFP4: *ga).
 template <int YDT>
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __restrict__ part,
                                                                  int splits, int M, int N,
@@ -632,13 +875,14 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __
                                                                  const float* __restrict__ ga,
                                                                  const float* __restrict__ gb) {
   const int64_t total = (int64_t)M * N;
-  const float g = ga ? (*ga) * (*gb) : 1.0f;
+  const bool scaled = ga != nullptr || gb != nullptr;
+  const float g = (ga ? *ga : 1.0f) * (gb ? *gb : 1.0f);
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * kThreads) {
     float s = 0.0f;
     for (int k = 0; k < splits; ++k) s += part[(int64_t)k * total + i];
     const int row = (int)(i / N), col = (int)(i - (int64_t)row * N);
-    store_out<YDT>(Y, ldy, row, col, ga ? s * g : s);
+    store_out<YDT>(Y, ldy, row, col, scaled ? s * g : s);
   }
 }
 
@@ -860,6 +1104,34 @@ hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
     gemm_nv_kernel<FP4_DT_BF16><<<grid, kThreads, 0, st>>>(a, as, ags, b, bs, bgs, y, ldy, (int)M,
                                                            (int)N, (int)K, tiles_n);
   return hipGetLastError();
+}
+
+size_t gemm_w4a16_workspace(int64_t M, int64_t N, int64_t K) {
+  if (K % 256 != 0 || K == 0 || M == 0 || N == 0) return 0;
+  W4Plan p = plan_w4(M, N, K);
+  return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_w4a16(int fmt, int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
+                             const uint8_t* b, const uint8_t* bs, const float* bgs, void* y, int ydt,
+                             int64_t ldy, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K == 0) {
+    zero_out_kernel<<<256, kThreads, 0, st>>>(y, ydt, (int)M, (int)N, ldy);
+    return hipGetLastError();
+  }
+  W4Plan p = plan_w4(M, N, K);
+  const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_w4a16_workspace(M, N, K);
+  const int splits = split ? p.splits : 1;
+  const int kt_per = split ? p.kt_per : (int)(K / 128);
+  float* part = static_cast<float*>(ws);
+  const uint8_t* ab = static_cast<const uint8_t*>(a);
+  hipError_t e = fmt == FP4_FMT_MXFP4
+                     ? launch_w4_fmt<FP4_FMT_MXFP4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st)
+                     : launch_w4_fmt<FP4_FMT_NVFP4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  if (e != hipSuccess || !split) return e;
+  return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy,
+                              fmt == FP4_FMT_NVFP4 ? bgs : nullptr, nullptr, st);
 }
 
 }  // namespace fp4lib

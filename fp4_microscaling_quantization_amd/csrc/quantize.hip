@@ -125,20 +125,31 @@ __device__ __forceinline__ uint32_t nv_enc8(float* v, float s) {
 }
 
 // NVFP4 block from 16 fp32 values (rotated in place when ROT).
+// With ROT the 1/sqrt(16) = 1/4 of the rotation is folded into the divisor
+// when the tensor scale is at least 2^-100: every block scale is then at
+// least 2^-109, a butterfly sum S that can round to a non-zero code has
+// |S| > s, so y = S/4 is a normal float (exact), fl32(S / (4 s)) equals
+// fl32(y / s), and max|y| = max|S| / 4 (rounding is monotone).  Smaller
+// tensor scales take the division by 4 first, as the definition orders it.
 template <bool ROT>
 __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out) {
+  const bool fold = ROT && !T.small;
   if constexpr (ROT) {
     fwht<16>(v);
+    if (T.small) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] *= 0.25f;  // 1/sqrt(16), exact
+      for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
+    }
   }
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  if (fold) amax *= 0.25f;
   float s;
   const uint32_t code = nv_scale(amax, T, s);
-  out[0] = nv_enc8(&v[0], s);
-  out[1] = nv_enc8(&v[8], s);
+  const float d = fold ? 4.0f * s : s;
+  out[0] = nv_enc8(&v[0], d);
+  out[1] = nv_enc8(&v[8], d);
   return code;
 }
 

@@ -183,7 +183,7 @@ int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor,
  *   (bf16 rounds to nearest-even).  The GEMM does not rotate: the caller
  *   quantizes both operands with the same rotation setting.
  * ws/ws_bytes: device workspace of fp4_gemm_workspace_bytes() bytes (any
- * contents; used for split-K partial sums).
+ * contents; used for split-K partial sums; 16-byte aligned).
  * Requirements: M, N >= 0, K >= 0 with K % 128 == 0; codes and scales
  * 16-byte aligned (both stream into LDS in 16-byte pieces). */
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
@@ -191,6 +191,27 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K,
              const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gs,
              const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gs,
              void* y, int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
+
+/* Weight-only GEMM (W4A16): Y[M, N] = sum_k A[m, k] * dequant(B)[n, k]
+ * ("Bridging the Gap ...": the W4A16 control, 16-bit activations times FP4
+ * weights; decode, where the weights stream from HBM once per token, is the
+ * serving case the pages emphasise).
+ *   A: bf16 activations [M, K], row stride lda (elements), unquantized.
+ *   B: b_codes [N, K/2] dense, b_scales in FP4_SCALES_GEMM layout for (N, K)
+ *      (NVFP4: row-major), b_gs the NVFP4 tensor scale (device fp32; MXFP4
+ *      ignores it).  B is dequantized exactly (e2m1 * scale is exact in bf16)
+ *      and multiplied on bf16 MFMA with fp32 accumulation.
+ *   No rotation is applied: a caller that quantized B with the block
+ *   Hadamard passes activations rotated the same way.
+ * ws/ws_bytes: device workspace of fp4_gemm_w4a16_workspace_bytes() bytes
+ * (any contents, 16-byte aligned; split-K partial sums; without it the call
+ * runs unsplit).
+ * Requirements: M, N >= 0, K >= 0 with K % 256 == 0; lda >= K; a, b_codes and
+ * b_scales 16-byte aligned, lda * 2 a multiple of 16 (when M > 1). */
+size_t fp4_gemm_w4a16_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
+int fp4_gemm_w4a16(int32_t fmt, int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
+                   const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gs,
+                   void* y, int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- misc */
 

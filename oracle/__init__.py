@@ -70,6 +70,9 @@ def _load(path: str):
     L.ora_gemm_entries.restype = ctypes.c_int
     L.ora_gemm_entries.argtypes = [ctypes.c_int, l, P, P, ctypes.c_float, P, P,
                                    ctypes.c_float, l, P, P, P, P]
+    L.ora_gemm_w4a16_entries.restype = ctypes.c_int
+    L.ora_gemm_w4a16_entries.argtypes = [ctypes.c_int, l, P, l, P, P, ctypes.c_float, l, P, P,
+                                         P, P]
     L.ora_e2m1_encode_array.restype = None
     L.ora_e2m1_encode_array.argtypes = [P, l, P]
     L.ora_e4m3_encode_array.restype = None
@@ -216,6 +219,32 @@ def gemm_entries(fmt: int, K: int, a_codes, a_scales, a_ts, b_codes, b_scales, b
     if rc != 0:
         raise ValueError("ora_gemm_entries: bad arguments")
     return y, ab
+
+
+def gemm_w4a16_entries(fmt: int, K: int, a, b_codes, b_scales, b_ts, rows, cols):
+    """(y, |A||B|) of the weight-only product Y = A dequant(B)^T at the listed
+    (row, col) pairs, in double; a is the [M, K] activation array (fp32 values)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b_codes = np.ascontiguousarray(b_codes, dtype=np.uint8)
+    b_scales = np.ascontiguousarray(b_scales, dtype=np.uint8)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    assert rows.size == cols.size and a.ndim == 2 and a.shape[1] == K
+    y = np.zeros(rows.size, dtype=np.float64)
+    ab = np.zeros(rows.size, dtype=np.float64)
+    rc = lib().ora_gemm_w4a16_entries(fmt, K, _p(a), K, _p(b_codes), _p(b_scales), float(b_ts),
+                                      rows.size, _p(rows), _p(cols), _p(y), _p(ab))
+    if rc != 0:
+        raise ValueError("ora_gemm_w4a16_entries: bad arguments")
+    return y, ab
+
+
+def gemm_w4a16_full(fmt: int, K: int, a, b_codes, b_scales, b_ts):
+    M = a.shape[0]
+    N = b_codes.shape[0]
+    r, c = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    y, ab = gemm_w4a16_entries(fmt, K, a, b_codes, b_scales, b_ts, r.reshape(-1), c.reshape(-1))
+    return y.reshape(M, N), ab.reshape(M, N)
 
 
 def gemm_full(fmt: int, K: int, a_codes, a_scales, a_ts, b_codes, b_scales, b_ts):

@@ -445,6 +445,54 @@ int ora_gemm_entries(int fmt, long K,
     return ORA_OK;
 }
 
+/*
+ * Weight-only GEMM entries ("Bridging the Gap Between Promise and Performance
+ * for Microscaling FP4 Quantization", W4A16: 16-bit activations times FP4
+ * weights).  The plain definition:
+ *   y    = sum_k a[row][k] * b^[col][k]  in double;
+ *   absy = sum_k |a[row][k]| * |b^[col][k]|,
+ * with a[M, K] given as fp32 values (the bf16 activations, exactly) and
+ * b^ the dequantized weights (MXFP4: e2m1 * 2^(c-127); NVFP4: e2m1 * e4m3,
+ * the sum multiplied by b_ts at the end).  b_scales row-major [N, K/G].
+ */
+int ora_gemm_w4a16_entries(int fmt, long K, const float *a, long lda,
+                           const uint8_t *b_codes, const uint8_t *b_scales, float b_ts,
+                           long nent, const long *rows, const long *cols,
+                           double *y, double *absy)
+{
+    int G;
+    if (fmt == ORA_MXFP4)
+        G = 32;
+    else if (fmt == ORA_NVFP4)
+        G = 16;
+    else
+        return ORA_EINVAL;
+    if (K < 0 || K % G != 0 || lda < K)
+        return ORA_EINVAL;
+    long nb = K / G;
+    for (long e = 0; e < nent; ++e) {
+        const float *ar = a + rows[e] * lda;
+        const uint8_t *bc = b_codes + cols[e] * (K / 2);
+        const uint8_t *bs = b_scales + cols[e] * nb;
+        double s = 0.0, sa = 0.0;
+        for (long b = 0; b < nb; ++b) {
+            double bsv = fmt == ORA_MXFP4 ? ora_e8m0_decode(bs[b]) : ora_e4m3_decode(bs[b]);
+            for (long k = b * G; k < (b + 1) * G; ++k) {
+                double bv = ora_e2m1_decode(get_code(bc, k)) * bsv;
+                s += (double)ar[k] * bv;
+                sa += fabs((double)ar[k]) * fabs(bv);
+            }
+        }
+        if (fmt == ORA_NVFP4) {
+            s *= (double)b_ts;
+            sa *= fabs((double)b_ts);
+        }
+        y[e] = s;
+        absy[e] = sa;
+    }
+    return ORA_OK;
+}
+
 /* Array forms of the codecs, for exhaustive checks. */
 void ora_e2m1_encode_array(const float *q, long n, uint8_t *out)
 {

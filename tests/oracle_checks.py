@@ -523,6 +523,61 @@ def check_gemm_rotation_convention():
         assert rel < 0.2, (fmt, rel)
 
 
+def check_gemm_w4a16_integer_closed_form():
+    """Weight-only GEMM, K = 32 with every E8M0 code 127: with integer
+    activations, y = (1/2) * A (2B)^T exactly in integer arithmetic."""
+    g = workloads.rng(19, 19)
+    M, N, K = 5, 7, 32
+    A = g.integers(-9, 10, (M, K)).astype(np.float32)
+    bc = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    bsc = np.full((N, 1), 127, np.uint8)
+    y, ab = oracle.gemm_w4a16_full(oracle.MXFP4, K, A, bc, bsc, 0.0)
+    B2 = (2 * _decode_codes(bc)).astype(np.int64)
+    Ai = A.astype(np.int64)
+    assert np.array_equal(y * 2, (Ai @ B2.T).astype(np.float64))
+    assert np.array_equal(ab * 2, (np.abs(Ai) @ np.abs(B2).T).astype(np.float64))
+
+
+def check_gemm_w4a16_one_hot():
+    """One-hot activation rows pick single dequantized weights: with A[m, k] =
+    v_m at k = j_m (0 elsewhere), y[m, n] = v_m * dequant(B)[n, j_m], for both
+    formats (NVFP4 including the weight tensor scale)."""
+    g = workloads.rng(20, 20)
+    W = _bf16_f32(workloads.gemm_weight(12, 256, 20))
+    for fmt in (oracle.MXFP4, oracle.NVFP4):
+        cb, sb, tb = oracle.quantize(W, fmt)
+        Wh = oracle.dequantize(cb, sb, fmt, tb).astype(np.float64)
+        M = 6
+        j = g.integers(0, 256, M)
+        v = np.array([1.0, -2.0, 0.5, 3.0, -0.25, 8.0], np.float32)
+        A = np.zeros((M, 256), np.float32)
+        A[np.arange(M), j] = v
+        y, ab = oracle.gemm_w4a16_full(fmt, 256, A, cb, sb, tb)
+        ref = v[:, None].astype(np.float64) * Wh[:, j].T
+        assert np.allclose(y, ref, rtol=1e-6, atol=0), fmt
+        assert np.allclose(ab, np.abs(ref), rtol=1e-6, atol=0), fmt
+
+
+def check_gemm_w4a16_matches_fp4_gemm():
+    """When the activations are exactly representable MXFP4 values (the
+    dequantized codes of a random quantized tensor), the weight-only product
+    equals the FP4 x FP4 product bit for bit; for NVFP4 (activation values
+    rounded to fp32 through their tensor scale) to 1e-6 relative."""
+    M, N, K = 4, 9, 512
+    for fmt in (oracle.MXFP4, oracle.NVFP4):
+        X = _bf16_f32(workloads.gemm_activation(M, K, 21))
+        W = _bf16_f32(workloads.gemm_weight(N, K, 21))
+        ca, sa, ta = oracle.quantize(X, fmt)
+        cb, sb, tb = oracle.quantize(W, fmt)
+        Xh = oracle.dequantize(ca, sa, fmt, ta)
+        y4, _ = oracle.gemm_full(fmt, K, ca, sa, ta, cb, sb, tb)
+        y16, _ = oracle.gemm_w4a16_full(fmt, K, Xh, cb, sb, tb)
+        if fmt == oracle.MXFP4:
+            assert np.array_equal(y16, y4)
+        else:
+            assert np.allclose(y16, y4, rtol=1e-6, atol=1e-6 * np.abs(y4).max())
+
+
 def check_sizes():
     """Bits per element: 4.25 (MXFP4) and 4.5 (NVFP4) from codes plus scales."""
     x = np.ones((4, 256), np.float32)

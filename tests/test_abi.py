@@ -147,3 +147,36 @@ def test_gemm_rejects_bad_arguments_on_host():
     assert _g(M=0, y=None) == E.FP4_OK                       # empty output: nothing to do
     assert fp4.fp4_gemm_workspace_bytes(fp4.FMT_MXFP4, 1, 8192, 28672) > 0
     assert fp4.fp4_gemm_workspace_bytes(fp4.FMT_MXFP4, 4096, 4096, 4096) == 0
+    assert _g(ws=FAKE + 8, wsb=1 << 20) == E.FP4_ERR_ALIGNMENT  # split-K partials: 16-byte aligned
+
+
+def _w(**kw):
+    a = dict(fmt=fp4.FMT_MXFP4, M=16, N=64, K=512, a=FAKE, lda=512, b=FAKE, bsc=FAKE, bgs=FAKE,
+             y=FAKE, ydt=fp4.DT_BF16, ldy=64, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return fp4.fp4_gemm_w4a16(a["fmt"], a["M"], a["N"], a["K"], a["a"], a["lda"], a["b"], a["bsc"],
+                              a["bgs"], a["y"], a["ydt"], a["ldy"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_gemm_w4a16_rejects_bad_arguments_on_host():
+    E = fp4
+    assert _w(K=128) == E.FP4_ERR_UNSUPPORTED                # K must be a multiple of 256
+    assert _w(fmt=2) == E.FP4_ERR_INVALID_ARG
+    assert _w(M=-1) == E.FP4_ERR_INVALID_ARG
+    assert _w(ldy=32) == E.FP4_ERR_INVALID_ARG
+    assert _w(lda=256) == E.FP4_ERR_INVALID_ARG              # lda < K
+    assert _w(ydt=9) == E.FP4_ERR_INVALID_ARG
+    assert _w(a=MIS) == E.FP4_ERR_ALIGNMENT
+    assert _w(lda=516) == E.FP4_ERR_ALIGNMENT                # 1032-byte activation rows
+    assert _w(b=MIS) == E.FP4_ERR_ALIGNMENT
+    assert _w(bsc=FAKE + 4) == E.FP4_ERR_ALIGNMENT
+    assert _w(ws=FAKE + 4, wsb=1 << 20) == E.FP4_ERR_ALIGNMENT
+    assert _w(a=None) == E.FP4_ERR_INVALID_ARG
+    assert _w(y=None) == E.FP4_ERR_INVALID_ARG
+    assert _w(fmt=fp4.FMT_NVFP4, bgs=None) == E.FP4_ERR_INVALID_ARG
+    assert _w(M=0, y=None) == E.FP4_OK                       # empty output: nothing to do
+    assert _w(N=0, y=None) == E.FP4_OK
+    assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXFP4, 1, 8192, 28672) > 0
+    assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_NVFP4, 16, 28672, 8192) > 0
+    assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXFP4, 1, 8192, 1000) == 0
+    assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXFP4, 4096, 4096, 4096) == 0

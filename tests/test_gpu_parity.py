@@ -45,12 +45,16 @@ def _inputs(name):
         b = workloads.cfg2_tensor("laplace", 9, rows=37, cols=4128)
     elif name == "tiny_rows":
         b = workloads.cfg2_tensor("gauss", 10, rows=3, cols=96)
+    elif name == "tiny_scale":
+        # amax near 2^-113: NVFP4 tensor scale near 2^-125 (below 2^-100)
+        g = workloads.bf16_bits_to_f32(workloads.cfg2_tensor("gauss", 13, rows=64, cols=1024))
+        b = workloads.to_bf16_bits((g * np.float32(2.0 ** -110)).astype(np.float32))
     else:
         raise KeyError(name)
     return workloads.bf16_bits_to_f32(b), to_dev_bf16(b)
 
 
-NONROT_CASES = ["cfg1", "cfg2_gauss", "cfg2_laplace", "cfg3", "ragged", "tiny_rows"]
+NONROT_CASES = ["cfg1", "cfg2_gauss", "cfg2_laplace", "cfg3", "ragged", "tiny_rows", "tiny_scale"]
 
 
 def _prefill(q):
@@ -96,7 +100,7 @@ def test_nvfp4_given_global_scale(case):
     assert np.array_equal(rowmajor_scales_np(q), rs)
 
 
-@pytest.mark.parametrize("case", ["cfg2_gauss", "cfg2_laplace", "cfg3", "ragged"])
+@pytest.mark.parametrize("case", ["cfg2_gauss", "cfg2_laplace", "cfg3", "ragged", "tiny_scale"])
 @pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
 def test_quantize_rotated(case, fmt):
     say("quantize rotated", case, FNAME[fmt])
@@ -326,3 +330,97 @@ def test_quantize_then_gemm_end_to_end(fmt):
     ref, absref = oracle.gemm_entries(fmt, K, ca, sa, ga, cb, sb, gb, rows, cols)
     got = y.cpu().numpy()[rows, cols].astype(np.float64)
     assert np.all(gemm_tolerance_ok(got, ref, absref, False))
+
+
+# ---------------------------------------------------------------- W4A16
+
+
+def _check_w4a16(fmt, M, N, K, seed, out_dtype, lda_pad=0, nrows=2, nent=256, split=True):
+    say("w4a16", FNAME[fmt], M, N, K, out_dtype, "lda+%d" % lda_pad, "split" if split else "unsplit")
+    _, _, _, bc, bsc, bgs = _rand_operands(fmt, M, N, K, seed)
+    qb = _device_operand(bc, bsc, bgs, fmt, N, K)
+    abits = workloads.gemm_activation(M, K + lda_pad, seed=seed)
+    a_full = to_dev_bf16(abits)
+    a = a_full[:, :K]
+    y = torch.empty(M, N, dtype=out_dtype, device="cuda")
+    if split:
+        fp4.gemm_w4a16(a, qb, out=y)
+    else:
+        rc = fp4.fp4_gemm_w4a16(fmt, M, N, K, a.data_ptr(), a.stride(0), qb.codes.data_ptr(),
+                                qb.scales.data_ptr(), qb.global_scale.data_ptr(), y.data_ptr(),
+                                fp4.DT_F32 if out_dtype == torch.float32 else fp4.DT_BF16, N, None, 0,
+                                torch.cuda.current_stream().cuda_stream)
+        assert rc == fp4.FP4_OK
+    torch.cuda.synchronize()
+    g = np.random.default_rng(seed)
+    rsel = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, nrows)]))[: max(2, nrows)]
+    rows = np.concatenate([np.repeat(rsel, N), g.integers(0, M, nent)])
+    cols = np.concatenate([np.tile(np.arange(N), rsel.size), g.integers(0, N, nent)])
+    av = workloads.bf16_bits_to_f32(abits)[:, :K]
+    ref, absref = oracle.gemm_w4a16_entries(fmt, K, av, bc, bsc, bgs, rows, cols)
+    got = y.float().cpu().numpy()[rows, cols].astype(np.float64)
+    ok = gemm_tolerance_ok(got, ref, absref, out_dtype == torch.bfloat16)
+    bad = np.nonzero(~ok)[0]
+    assert bad.size == 0, (M, N, K, rows[bad[:4]], cols[bad[:4]], got[bad[:4]], ref[bad[:4]])
+    return y
+
+
+W4_SMALL = [(1, 64, 256), (7, 96, 512), (16, 300, 768), (33, 520, 1024), (100, 256, 256),
+            (257, 130, 512), (1, 4096, 4096), (16, 1024, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", W4_SMALL, ids=["%dx%dx%d" % s for s in W4_SMALL])
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_gemm_w4a16_small_full_check(fmt, M, N, K):
+    _check_w4a16(fmt, M, N, K, seed=M + N + K, out_dtype=torch.float32, nrows=min(M, 16), nent=512)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_gemm_w4a16_strided_activations_and_unsplit(fmt):
+    """A row-strided activation view (lda > K), and the call without a
+    workspace (one pass over K) against the oracle and the split result."""
+    M, N, K = 16, 768, 4096
+    y1 = _check_w4a16(fmt, M, N, K, seed=5, out_dtype=torch.float32, lda_pad=64, nrows=16)
+    y2 = _check_w4a16(fmt, M, N, K, seed=5, out_dtype=torch.float32, lda_pad=64, nrows=16, split=False)
+    assert fp4.fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K) > 0
+    assert torch.allclose(y1, y2, rtol=0, atol=1e-3 * float(y1.abs().max()))
+
+
+LLAMA70B_DECODE = [(m, n, k) for m in (1, 16, 128) for (k, n) in ((8192, 28672), (28672, 8192))]
+
+
+@pytest.mark.parametrize("M,N,K", LLAMA70B_DECODE, ids=["%dx%dx%d" % s for s in LLAMA70B_DECODE])
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_gemm_w4a16_llama70b_mlp_shapes(fmt, M, N, K):
+    _check_w4a16(fmt, M, N, K, seed=13, out_dtype=torch.bfloat16, nrows=1, nent=128)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_gemm_w4a16_quantized_weights_end_to_end(fmt):
+    """bf16 weights quantized on the GPU (bit-identical to the oracle's codes),
+    then the weight-only product against the oracle's."""
+    M, N, K = 16, 384, 1024
+    say("w4a16 end to end", FNAME[fmt])
+    xa = workloads.gemm_activation(M, K, seed=4)
+    xb = workloads.gemm_weight(N, K, seed=4)
+    qb = fp4.quantize(to_dev_bf16(xb), fmt, scale_layout=fp4.SCALES_GEMM)
+    y = fp4.gemm_w4a16(to_dev_bf16(xa), qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    cb, sb, gb = oracle.quantize(workloads.bf16_bits_to_f32(xb), fmt)
+    assert np.array_equal(codes_np(qb), cb)
+    r, c = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ref, absref = oracle.gemm_w4a16_entries(fmt, K, workloads.bf16_bits_to_f32(xa), cb, sb, gb,
+                                            r.reshape(-1), c.reshape(-1))
+    got = y.cpu().numpy().reshape(-1).astype(np.float64)
+    assert np.all(gemm_tolerance_ok(got, ref, absref, False))
+
+
+def test_gemm_w4a16_empty_k_writes_zeros():
+    say("w4a16 K=0")
+    y = torch.full((3, 5), 7.0, dtype=torch.float32, device="cuda")
+    a = torch.zeros(3, 0, dtype=torch.bfloat16, device="cuda")
+    rc = fp4.fp4_gemm_w4a16(fp4.FMT_NVFP4, 3, 5, 0, a.data_ptr(), 0, None, None, None, y.data_ptr(),
+                            fp4.DT_F32, 5, None, 0, torch.cuda.current_stream().cuda_stream)
+    assert rc == fp4.FP4_OK
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0

@@ -42,6 +42,10 @@ MUTANTS = [
     ("gemm forgets tensor scales", "s *= g;", "s *= 1.0;"),
     ("gemm transposed scale index", "bsv = ora_e8m0_decode(bs[b]);", "bsv = ora_e8m0_decode(as[b]);"),
     ("error sums drop a term", "se += (a - b) * (a - b);", "se += (a - b) * (a - b) * 0.5;"),
+    ("w4a16 drops the weight tensor scale", "s *= (double)b_ts;", "s *= 1.0;"),
+    ("w4a16 loses the activation sign", "s += (double)ar[k] * bv;", "s += fabs((double)ar[k]) * bv;"),
+    ("w4a16 scale of the next block", "double bsv = fmt == ORA_MXFP4 ? ora_e8m0_decode(bs[b]) : ora_e4m3_decode(bs[b]);",
+     "double bsv = fmt == ORA_MXFP4 ? ora_e8m0_decode(bs[(b + 1) % nb]) : ora_e4m3_decode(bs[(b + 1) % nb]);"),
 ]
 
 
