@@ -584,9 +584,11 @@ __device__ __forceinline__ u32x4 expand8_bf16_mx(uint32_t w, float scale) {
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3))};
 }
 
-// Eight E2M1 codes times an E4M3 value (exact products, rounded to bf16 exactly).
+// Eight E2M1 codes times an E4M3 value.  Each product has at most six
+// significant bits and lies in [2^-10, 2688], so its fp32 form has sixteen
+// zero low bits and the bf16 value is the high half, taken without rounding.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+  return (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u);
 }
 __device__ __forceinline__ u32x4 expand8_bf16_nv(uint32_t w, float s) {
   const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
