@@ -63,6 +63,9 @@ def _load(path: str):
     L.ora_rotate.argtypes = [P, P, l, l, ctypes.c_int]
     L.ora_quantize.restype = ctypes.c_int
     L.ora_quantize.argtypes = [ctypes.c_int, ctypes.c_int, P, l, l, P, P, P, ctypes.c_int]
+    L.ora_quantize_rule.restype = ctypes.c_int
+    L.ora_quantize_rule.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, l, l, P, P, P,
+                                    ctypes.c_int]
     L.ora_dequantize.restype = ctypes.c_int
     L.ora_dequantize.argtypes = [ctypes.c_int, P, P, ctypes.c_float, l, l, ctypes.c_int, P]
     L.ora_error_sums.restype = None
@@ -149,8 +152,15 @@ def rotate(x, n: int) -> np.ndarray:
     return y
 
 
-def quantize(x, fmt: int, rotate: bool = False, ts: float | None = None):
-    """Returns (codes [rows, cols/2] u8, scales [rows, cols/G] u8, ts float32)."""
+SCALE_ABSMAX = 0
+SCALE_MSE = 1
+SCALE_FOUR_OVER_SIX = 2
+
+
+def quantize(x, fmt: int, rotate: bool = False, ts: float | None = None, rule: int = SCALE_ABSMAX):
+    """Returns (codes [rows, cols/2] u8, scales [rows, cols/G] u8, ts float32).
+    rule: SCALE_ABSMAX, SCALE_MSE (windowed squared-error search over the
+    block-scale code) or SCALE_FOUR_OVER_SIX (NVFP4: maximum onto 6 or 4)."""
     x = _f32(x)
     if x.ndim == 1:
         x = x.reshape(1, -1)
@@ -161,10 +171,10 @@ def quantize(x, fmt: int, rotate: bool = False, ts: float | None = None):
     tsa = np.zeros(1, dtype=np.float32)
     if ts is not None:
         tsa[0] = ts
-    rc = lib().ora_quantize(fmt, int(bool(rotate)), _p(x), rows, cols, _p(codes), _p(scales),
-                            _p(tsa), int(ts is not None))
+    rc = lib().ora_quantize_rule(fmt, int(bool(rotate)), int(rule), _p(x), rows, cols, _p(codes),
+                                 _p(scales), _p(tsa), int(ts is not None))
     if rc != 0:
-        raise ValueError("ora_quantize: bad arguments")
+        raise ValueError("ora_quantize_rule: bad arguments")
     return codes, scales, np.float32(tsa[0])
 
 

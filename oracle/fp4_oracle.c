@@ -224,19 +224,82 @@ static int get_code(const uint8_t *row_codes, long k)
     return (k & 1) ? (row_codes[k >> 1] >> 4) & 0xF : row_codes[k >> 1] & 0xF;
 }
 
+/* Scale-selection rules ([MRGPTQ] section 4.1 and the W4A4 baselines:
+ * absmax scales for RTN, "MSE scale optimization" / "format-specific scale
+ * search" for MR-GPTQ's weights; [VS] "The E2M1 element": the best scale does
+ * not always put the block maximum on 6, and "Follow-on research": Four Over
+ * Six maps the maximum of some blocks to 4 instead of 6). */
+#define ORA_SCALE_ABSMAX 0
+#define ORA_SCALE_MSE 1
+#define ORA_SCALE_FOUR_OVER_SIX 2
+
+/* Element codes of the G values yb at scale code sc: q = fl32(y / s) rounded
+ * onto the E2M1 grid.  MXFP4: s = 2^(sc-127).  NVFP4: s = fl32(e4m3(sc) * ts);
+ * a zero s gives all-zero codes. */
+static void block_encode(int fmt, const float *yb, int G, int sc, float tsv, int *code)
+{
+    float s = fmt == ORA_MXFP4 ? ldexpf(1.0f, sc - 127) : (float)ora_e4m3_decode(sc) * tsv;
+    for (int i = 0; i < G; ++i)
+        code[i] = s != 0.0f ? ora_e2m1_encode(yb[i] / s) : 0;
+}
+
+/* Dequantized value of one element (as ora_dequantize computes it, in fp32). */
+static float element_value(int fmt, int code, int sc, float tsv)
+{
+    if (fmt == ORA_MXFP4)
+        return (float)ora_e2m1_decode(code) * ldexpf(1.0f, sc - 127);
+    float inner = (float)(ora_e2m1_decode(code) * ora_e4m3_decode(sc));
+    return inner * tsv;
+}
+
+/* Squared reconstruction error of a block quantized at scale code sc, in
+ * fp32: d = fl32(y - y^), acc = fma(d, d, acc) in element order.  This is
+ * the number the search compares, so the decision is taken in the precision
+ * the GPU kernel uses (one lane holds one block). */
+static float block_sse(int fmt, const float *yb, int G, int sc, float tsv, const int *code)
+{
+    float acc = 0.0f;
+    for (int i = 0; i < G; ++i) {
+        float d = yb[i] - element_value(fmt, code[i], sc, tsv);
+        acc = fmaf(d, d, acc);
+    }
+    return acc;
+}
+
+/* NVFP4 E4M3 block-scale code that maps the block maximum amax onto `top`
+ * (6 for the standard rule, 4 for the alternative of Four Over Six):
+ * E4M3(fl32(fl32(amax / top) / ts)). */
+static int nv_scale_code(float amax, float top, float tsv)
+{
+    float t = (amax / top) / tsv;
+    return ora_e4m3_encode(t);
+}
+
 /*
  * Quantize x [rows, cols] (fp32, row-major, blocks run along cols).
  *   fmt     ORA_MXFP4 (block 32, E8M0) or ORA_NVFP4 (block 16, E4M3 x fp32).
  *   rotate  0, or 1 for a block Hadamard of the block size applied first.
+ *   rule    ORA_SCALE_ABSMAX: the block maximum sets the scale.
+ *           ORA_SCALE_MSE: among candidate scale codes around the absmax code
+ *             c0, the one whose block has the smallest squared error
+ *             (block_sse).  MXFP4 candidates: c0, c0 + 1.  NVFP4: c0, c0 + 1,
+ *             c0 - 1, c0 + 2, c0 - 2, c0 + 3, c0 + 4, c0 + 5, c0 + 6 (codes
+ *             outside 0 .. 0x7E skipped).  A later candidate replaces the best
+ *             one only with a strictly smaller error, so ties keep the
+ *             earliest (the absmax code first).
+ *           ORA_SCALE_FOUR_OVER_SIX (NVFP4 only): candidates c0 (maximum onto
+ *             6), then the code that maps the maximum onto 4; the smaller
+ *             error wins, ties keep c0.
  *   codes   out, [rows, cols/2] bytes, element 2i in the low nibble.
  *   scales  out, [rows, cols/G] bytes, row-major.
  *   ts      NVFP4 per-tensor scale: written (gs_given = 0) or read (= 1).
+ *           Every rule uses the same tensor scale, amax / (6 * 448).
  * MXFP4 follows [VS] "A worked example, by hand" and the emulation's mxfp4;
  * NVFP4 follows [VS] Figure 2 (global amax -> fp32 tensor scale -> block amax
  * -> E4M3 -> E2M1 -> pack) and the emulation's nvfp4.
  */
-int ora_quantize(int fmt, int rotate, const float *x, long rows, long cols,
-                 uint8_t *codes, uint8_t *scales, float *ts, int gs_given)
+int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, long cols,
+                      uint8_t *codes, uint8_t *scales, float *ts, int gs_given)
 {
     int G;
     if (fmt == ORA_MXFP4)
@@ -248,6 +311,9 @@ int ora_quantize(int fmt, int rotate, const float *x, long rows, long cols,
     if (rows < 0 || cols < 0 || cols % G != 0 || (rotate != 0 && rotate != 1))
         return ORA_EINVAL;
     if (fmt == ORA_NVFP4 && ts == NULL)
+        return ORA_EINVAL;
+    if (rule != ORA_SCALE_ABSMAX && rule != ORA_SCALE_MSE &&
+        !(rule == ORA_SCALE_FOUR_OVER_SIX && fmt == ORA_NVFP4))
         return ORA_EINVAL;
 
     long n = rows * cols;
@@ -277,42 +343,65 @@ int ora_quantize(int fmt, int rotate, const float *x, long rows, long cols,
         }
     }
 
+    static const int nv_window[9] = {0, 1, -1, 2, -2, 3, 4, 5, 6};
     long nb = cols / G;
+    int code[32], cand_code[32];
     for (long r = 0; r < rows; ++r) {
         uint8_t *rc = codes + r * (cols / 2);
         for (long b = 0; b < nb; ++b) {
             const float *yb = y + r * cols + b * G;
             float amax = block_amax(yb, G);
+            int sc;
             if (fmt == ORA_MXFP4) {
-                int e = mx_exponent(amax);
-                scales[r * nb + b] = (uint8_t)(e + 127);
-                float s = ldexpf(1.0f, e);
-                for (int i = 0; i < G; ++i) {
-                    float q = yb[i] / s;
-                    put_code(rc, b * G + i, ora_e2m1_encode(q));
-                }
+                sc = mx_exponent(amax) + 127;
             } else {
-                int sc = 0;
-                float s = 0.0f;
+                sc = 0;
                 if (tsv > 0.0f) {
                     float t = (amax / 6.0f) / tsv;
                     sc = ora_e4m3_encode(t);
-                    s = (float)ora_e4m3_decode(sc) * tsv;
-                }
-                scales[r * nb + b] = (uint8_t)sc;
-                for (int i = 0; i < G; ++i) {
-                    int code = 0;
-                    if (s != 0.0f) {
-                        float q = yb[i] / s;
-                        code = ora_e2m1_encode(q);
-                    }
-                    put_code(rc, b * G + i, code);
                 }
             }
+            block_encode(fmt, yb, G, sc, tsv, code);
+            if (rule != ORA_SCALE_ABSMAX && !(fmt == ORA_NVFP4 && !(tsv > 0.0f))) {
+                int cands[9], nc = 0;
+                if (rule == ORA_SCALE_MSE && fmt == ORA_MXFP4) {
+                    cands[nc++] = sc + 1;
+                } else if (rule == ORA_SCALE_MSE) {
+                    for (int w = 1; w < 9; ++w)
+                        cands[nc++] = sc + nv_window[w];
+                } else {
+                    cands[nc++] = nv_scale_code(amax, 4.0f, tsv);
+                }
+                int maxcode = fmt == ORA_MXFP4 ? 254 : 0x7E;
+                float best = block_sse(fmt, yb, G, sc, tsv, code);
+                for (int k = 0; k < nc; ++k) {
+                    int c = cands[k];
+                    if (c < 0 || c > maxcode)
+                        continue;
+                    block_encode(fmt, yb, G, c, tsv, cand_code);
+                    float e = block_sse(fmt, yb, G, c, tsv, cand_code);
+                    if (e < best) {
+                        best = e;
+                        sc = c;
+                        memcpy(code, cand_code, sizeof(int) * (size_t)G);
+                    }
+                }
+            }
+            scales[r * nb + b] = (uint8_t)sc;
+            for (int i = 0; i < G; ++i)
+                put_code(rc, b * G + i, code[i]);
         }
     }
     free(ybuf);
     return ORA_OK;
+}
+
+/* The absmax rule ([VS] "A worked example, by hand"; Figure 2). */
+int ora_quantize(int fmt, int rotate, const float *x, long rows, long cols,
+                 uint8_t *codes, uint8_t *scales, float *ts, int gs_given)
+{
+    return ora_quantize_rule(fmt, rotate, ORA_SCALE_ABSMAX, x, rows, cols, codes, scales, ts,
+                             gs_given);
 }
 
 /*

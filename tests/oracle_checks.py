@@ -374,6 +374,156 @@ def check_absmax_scale_vs_best_scale():
         assert best in (e0, e0 + 1), (e0, sses)
 
 
+# ------------------------------------------------ scale search (MSE, 4/6)
+MX_WINDOW = (0, 1)
+NV_WINDOW = (0, 1, -1, 2, -2, 3, 4, 5, 6)
+
+
+def _block_values(x: np.ndarray, G: int, rotate: bool) -> np.ndarray:
+    """[blocks, G] float64 of the values the block scales see: x itself, or the
+    block Hadamard (scipy's Sylvester matrix / sqrt(G)) rounded to fp32."""
+    y = x.astype(np.float64).reshape(-1, G)
+    if rotate:
+        y = (y @ (scipy.linalg.hadamard(G) / np.sqrt(G))).astype(np.float32).astype(np.float64)
+    return y
+
+
+def _best_sse_at(y: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Brute force: for blocks y [nb, G] and scales s [nb, C] (float64), the
+    smallest possible squared error of each block at each scale, every element
+    taking the best of the eight grid magnitudes (its sign is free)."""
+    a = np.abs(y)[:, None, :, None]                           # nb, 1, G, 1
+    cand = GRID[None, None, None, :] * s[:, :, None, None]    # nb, C, 1, 8
+    return ((a - cand) ** 2).min(-1).sum(-1)                  # nb, C
+
+
+def _scale_values(fmt, codes, ts):
+    if fmt == oracle.MXFP4:
+        return np.exp2(codes.astype(np.float64) - 127)
+    e4 = _e4m3_values_from_definition()
+    return (e4[codes].astype(np.float32) * np.float32(ts)).astype(np.float64)
+
+
+def _search_inputs():
+    g = workloads.rng(41, 41)
+    lap = workloads.laplace(g, 32 * 1024, 1.0).astype(np.float32).reshape(32, 1024)
+    gau = workloads.normal(g, 32 * 1024, 0.02).astype(np.float32).reshape(32, 1024)
+    return [("laplace", lap), ("gauss", gau)]
+
+
+def check_mse_scale_is_the_window_optimum():
+    """FP4_SCALE_MSE ("MSE scale optimization", "format-specific scale search";
+    the best scale need not put the block maximum on 6): each block's scale code
+    is the absmax code c0 or one of its window neighbours (MXFP4 c0, c0+1;
+    NVFP4 c0-2 .. c0+6), its squared error (brute force over the grid, double)
+    is the smallest in the window, and where the window minimum is clear by
+    1e-4 it is that code exactly.  Codes at the chosen scale are nearest grid
+    points.  The tensor scale is the absmax rule's."""
+    for name, x in _search_inputs():
+        for fmt in (oracle.MXFP4, oracle.NVFP4):
+            G = oracle.BLOCK[fmt]
+            win = np.array(MX_WINDOW if fmt == oracle.MXFP4 else NV_WINDOW)
+            top = 254 if fmt == oracle.MXFP4 else 0x7E
+            for rot in (False, True):
+                _, s0, ts0 = oracle.quantize(x, fmt, rot)
+                c, s, ts = oracle.quantize(x, fmt, rot, rule=oracle.SCALE_MSE)
+                assert ts == ts0, (name, fmt, rot)
+                y = _block_values(x, G, rot)
+                c0 = s0.reshape(-1).astype(np.int64)
+                ch = s.reshape(-1).astype(np.int64)
+                cand = c0[:, None] + win[None, :]
+                valid = (cand >= 0) & (cand <= top)
+                e = _best_sse_at(y, _scale_values(fmt, np.clip(cand, 0, top), ts))
+                e = np.where(valid, e, np.inf)
+                assert np.all(np.any(cand == ch[:, None], axis=1)), (name, fmt, rot)
+                e_ch = _best_sse_at(y, _scale_values(fmt, ch[:, None], ts))[:, 0]
+                best = e.min(1)
+                assert np.all(e_ch <= best * (1 + 1e-5) + 1e-300), (name, fmt, rot)
+                srt = np.sort(e, 1)
+                clear = srt[:, 1] > srt[:, 0] * (1 + 1e-4)
+                arg = cand[np.arange(cand.shape[0]), e.argmin(1)]
+                assert np.array_equal(ch[clear], arg[clear]), (name, fmt, rot)
+                # the element codes are the nearest grid points at that scale (the
+                # dequantized NVFP4 value rounds e2m1 * e4m3 * ts once: a 2^-24
+                # relative change of each reconstruction)
+                xh = oracle.dequantize(c, s, fmt, ts).astype(np.float64).reshape(-1, G)
+                got = ((xh - y) ** 2).sum(1)
+                slack = 2.0 ** -22 * np.sqrt(e_ch * (y ** 2).sum(1)) + 1e-300
+                assert np.all(np.abs(got - e_ch) <= 1e-9 * e_ch + slack), (name, fmt, rot)
+                # and the search lowers the error of the tensor
+                c_a, s_a, _ = oracle.quantize(x, fmt, rot)
+                xa = oracle.dequantize(c_a, s_a, fmt, ts).astype(np.float64).reshape(-1, G)
+                assert got.sum() < ((xa - y) ** 2).sum(), (name, fmt, rot)
+
+
+def check_mse_window_holds_the_global_optimum():
+    """The window is wide enough: over every representable scale code the
+    squared-error optimum lies inside it for at least 99.9 % of Laplace and
+    Gaussian blocks (plain and rotated)."""
+    for name, x in _search_inputs():
+        for fmt in (oracle.MXFP4, oracle.NVFP4):
+            G = oracle.BLOCK[fmt]
+            win = np.array(MX_WINDOW if fmt == oracle.MXFP4 else NV_WINDOW)
+            for rot in (False, True):
+                _, s0, ts = oracle.quantize(x, fmt, rot)
+                y = _block_values(x, G, rot)
+                c0 = s0.reshape(-1).astype(np.int64)
+                if fmt == oracle.MXFP4:
+                    allc = np.clip(c0[:, None] + np.arange(-8, 9)[None, :], 0, 254)
+                else:
+                    allc = np.tile(np.arange(0x7F), (c0.size, 1))
+                e = _best_sse_at(y, _scale_values(fmt, allc, ts))
+                opt = allc[np.arange(allc.shape[0]), e.argmin(1)] - c0
+                inside = np.isin(opt, win).mean()
+                assert inside >= 0.999, (name, fmt, rot, inside)
+
+
+def check_four_over_six():
+    """FP4_SCALE_FOUR_OVER_SIX (NVFP4; "Four Over Six": some blocks map their
+    maximum to 4 instead of 6): the scale code is c6 = E4M3((amax/6)/ts) or
+    c4 = E4M3((amax/4)/ts) (E4M3 rounding from the format definition), the one
+    with the smaller squared error where the two differ by 1e-4, and the
+    tensor error is below the absmax rule's."""
+    e4 = _e4m3_values_from_definition()
+    for name, x in _search_inputs():
+        for rot in (False, True):
+            _, s6, ts = oracle.quantize(x, oracle.NVFP4, rot)
+            c, s, ts2 = oracle.quantize(x, oracle.NVFP4, rot, rule=oracle.SCALE_FOUR_OVER_SIX)
+            assert ts2 == ts
+            y = _block_values(x, 16, rot)
+            amax = np.abs(y).max(1).astype(np.float32)
+            t4 = (amax / np.float32(4)) / np.float32(ts)
+            c4 = np.searchsorted(e4, _binade_rne_e4m3(t4))
+            c6 = s6.reshape(-1).astype(np.int64)
+            assert np.array_equal(e4[c6], _binade_rne_e4m3((amax / np.float32(6)) / np.float32(ts)))
+            ch = s.reshape(-1).astype(np.int64)
+            assert np.all((ch == c6) | (ch == c4)), (name, rot)
+            e = _best_sse_at(y, _scale_values(oracle.NVFP4, np.stack([c6, c4], 1), ts))
+            clear = np.abs(e[:, 0] - e[:, 1]) > 1e-4 * np.maximum(e[:, 0], e[:, 1])
+            want = np.where(e[:, 1] < e[:, 0], c4, c6)
+            assert np.array_equal(ch[clear], want[clear]), (name, rot)
+            assert (c4 != c6).mean() > 0.9
+            xh = oracle.dequantize(c, s, oracle.NVFP4, ts).astype(np.float64).reshape(-1, 16)
+            xa = oracle.dequantize(*oracle.quantize(x, oracle.NVFP4, rot)[:2], oracle.NVFP4, ts)
+            assert ((xh - y) ** 2).sum() < ((xa.astype(np.float64).reshape(-1, 16) - y) ** 2).sum()
+
+
+def check_scale_search_ties_keep_the_absmax_code():
+    """Equal errors keep the absmax code: a block exact at both 2^e0 and
+    2^(e0+1) (MXFP4), all-zero blocks, and an NVFP4 block exact at its absmax
+    scale keep c0 under every rule."""
+    x = np.zeros((2, 64), np.float32)
+    x[0, :4] = [4.0, 2.0, -1.0, 2.0]          # exact at 2^0 and at 2^1
+    c, s, _ = oracle.quantize(x, oracle.MXFP4, rule=oracle.SCALE_MSE)
+    assert s[0, 0] == 127 and s[0, 1] == 0 and np.all(s[1] == 0), s
+    xn = np.zeros((2, 32), np.float32)
+    xn[0, :3] = [6.0, 3.0, -1.5]                 # ts = 6/2688: c0 = 448 exact
+    for rule in (oracle.SCALE_MSE, oracle.SCALE_FOUR_OVER_SIX):
+        c, s, ts = oracle.quantize(xn, oracle.NVFP4, rule=rule)
+        assert s[0, 0] == 0x7E and s[0, 1] == 0 and np.all(s[1] == 0), (rule, s)
+        assert np.all(c[1] == 0)
+
+
 def check_directional_rotation():
     """Under RTN, a group-sized Hadamard lowers MXFP4 error on Laplace data and
     raises NVFP4 error ("rotations improve MXFP4 accuracy, but hurt NVFP4")."""

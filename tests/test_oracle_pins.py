@@ -46,6 +46,13 @@ MUTANTS = [
     ("w4a16 loses the activation sign", "s += (double)ar[k] * bv;", "s += fabs((double)ar[k]) * bv;"),
     ("w4a16 scale of the next block", "double bsv = fmt == ORA_MXFP4 ? ora_e8m0_decode(bs[b]) : ora_e4m3_decode(bs[b]);",
      "double bsv = fmt == ORA_MXFP4 ? ora_e8m0_decode(bs[(b + 1) % nb]) : ora_e4m3_decode(bs[(b + 1) % nb]);"),
+    ("mse window skips e0+1", "cands[nc++] = sc + 1;", "cands[nc++] = sc + 2;"),
+    ("mse nv window loses c0-1", "nv_window[9] = {0, 1, -1, 2,", "nv_window[9] = {0, 1, 1, 2,"),
+    ("mse ties go to later candidates", "if (e < best) {", "if (e <= best) {"),
+    ("mse error not squared", "acc = fmaf(d, d, acc);", "acc = acc + fabsf(d);"),
+    ("mse scores a candidate with the old codes", "float e = block_sse(fmt, yb, G, c, tsv, cand_code);",
+     "float e = block_sse(fmt, yb, G, c, tsv, code);"),
+    ("four over six maps to 3", "nv_scale_code(amax, 4.0f, tsv)", "nv_scale_code(amax, 3.0f, tsv)"),
 ]
 
 
