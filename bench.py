@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-search", action="store_true",
+                    help="skip the timings of the searching block-scale rules")
     ap.add_argument("--gemm-iters", type=int, default=10)
     ap.add_argument("--no-copy-probe", action="store_true",
                     help="skip the untimed 64 MiB device copy used to calibrate HBM byte counters")
@@ -264,6 +266,57 @@ def main():
     log("step %.3f ms (eager), %.3f ms (graph), %.1f GB/s; dominant %s %.2f us"
         % (1e3 * step_s, 1e3 * graph_s, value_gbs, dom, dk["avg_us"]))
 
+    # ------------------------------------------------- block-scale search
+    # The searching rules (MSE window, Four Over Six) on the same input: the
+    # quantize kernel alone (NVFP4 with its tensor scale given), per launch,
+    # and the reconstruction error against absmax.
+    search = {}
+    if not args.no_search:
+        rules = [(fp4.FMT_MXFP4, fp4.SCALE_MSE, "mse"), (fp4.FMT_NVFP4, fp4.SCALE_MSE, "mse"),
+                 (fp4.FMT_NVFP4, fp4.SCALE_FOUR_OVER_SIX, "4over6")]
+        for fmt, rule, rname in rules:
+            for rot in (False, True):
+                lay = fp4.SCALES_GEMM if fmt == fp4.FMT_MXFP4 else fp4.SCALES_ROWMAJOR
+                cfg = fp4.qconfig(fmt, rot, lay, rule)
+                qs = []
+                for c in range(copies):
+                    base = outs[("gauss", fmt, rot)][c]
+                    qs.append(fp4.Quantized(torch.empty_like(base.codes), torch.empty_like(base.scales),
+                                            base.global_scale.clone(), cfg, rows, cols))
+
+                def qcall(c, d="gauss", qs=qs, fmt=fmt):
+                    q = qs[c]
+                    rc = fp4.fp4_quantize(q.cfg, xs[d][c].data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                          q.codes.data_ptr(), q.scales.data_ptr(),
+                                          q.global_scale.data_ptr(), fp4.GS_GIVEN, None, 0, sh_now())
+                    if rc != 0:
+                        raise RuntimeError("quantize failed: %d" % rc)
+
+                qcall(0)
+                torch.cuda.synchronize()
+                g = capture(lambda: [qcall(i % copies) for i in range(reps)])
+                g.replay()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                del g
+                ent = {"avg_us": round(us, 3), "gbs": round(alg_bytes(fmt) / (us * 1e-6) / 1e9, 1),
+                       "frac": round(alg_bytes(fmt) / (us * 1e-6) / PEAK_HBM, 4)}
+                for d in ("gauss", "laplace"):
+                    qd = fp4.quantize(xs[d][0], fmt, rotate=rot, scale_layout=lay, rule=rule)
+                    sd = fp4.error_sums(xs[d][0], qd).cpu().numpy()
+                    qa = outs[(d, fmt, rot)][0]
+                    sa = fp4.error_sums(xs[d][0], qa).cpu().numpy()
+                    ent["nmse_" + d] = float(sd[0] / sd[1])
+                    ent["nmse_absmax_" + d] = float(sa[0] / sa[1])
+                search["%s/%s/%s" % (FN[fmt], rname, "h%d" % fp4.BLOCK[fmt] if rot else "plain")] = ent
+        log("scale search timings done")
+
     # -------------------------------------------------------------- NMSE
     nmse = {}
     for v in variants:
@@ -333,6 +386,7 @@ def main():
                          "same kernels)" % reps,
         "cpu_baseline": cpu,
         "nmse": nmse,
+        "scale_search": search,
         "gemm": gemm,
     }
     print(json.dumps(line), flush=True)

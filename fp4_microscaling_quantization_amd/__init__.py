@@ -36,6 +36,8 @@ SCALES_GEMM = 1
 GS_COMPUTE = 0
 GS_GIVEN = 1
 SCALE_ABSMAX = 0
+SCALE_MSE = 1
+SCALE_FOUR_OVER_SIX = 2
 BLOCK = {FMT_MXFP4: 32, FMT_NVFP4: 16}
 
 EXPORTED = [
@@ -57,9 +59,10 @@ class QConfig(ctypes.Structure):
                 ("rule", ctypes.c_int32), ("scale_layout", ctypes.c_int32)]
 
 
-def qconfig(fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMAJOR) -> QConfig:
+def qconfig(fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMAJOR,
+            rule: int = SCALE_ABSMAX) -> QConfig:
     G = BLOCK[fmt]
-    return QConfig(fmt, G, G if rotate else 0, SCALE_ABSMAX, scale_layout)
+    return QConfig(fmt, G, G if rotate else 0, rule, scale_layout)
 
 
 _lib = None
@@ -242,14 +245,16 @@ class Quantized:
 
 
 def quantize(x, fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMAJOR,
-             global_scale=None, out: Quantized | None = None) -> Quantized:
+             global_scale=None, out: Quantized | None = None,
+             rule: int = SCALE_ABSMAX) -> Quantized:
     """Quantize a 2-D CUDA tensor (fp32 or bf16, unit stride along the last
     axis).  NVFP4: ``global_scale`` (a float32[1] CUDA tensor) is used as given
-    when passed, otherwise computed from the tensor's amax."""
+    when passed, otherwise computed from the tensor's amax.  ``rule`` selects
+    the block-scale rule (SCALE_ABSMAX, SCALE_MSE, SCALE_FOUR_OVER_SIX)."""
     torch = _torch()
     assert x.dim() == 2 and x.stride(1) == 1
     rows, cols = x.shape
-    cfg = qconfig(fmt, rotate, scale_layout)
+    cfg = qconfig(fmt, rotate, scale_layout, rule)
     if out is None:
         codes = torch.empty(max(fp4_codes_bytes(rows, cols), 16), dtype=torch.uint8, device=x.device)
         scales = torch.empty(max(fp4_scales_bytes(cfg, rows, cols), 16), dtype=torch.uint8,

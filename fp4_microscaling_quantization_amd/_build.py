@@ -18,7 +18,7 @@ HIPCC_FLAGS = [
     "-shared",
     "-fno-gpu-rdc",
     "-fno-fast-math",
-    "-ffp-contract=fast",
+    "-ffp-contract=fast-honor-pragmas",  # fp contract(off) regions stay unfused
     "-fno-gpu-flush-denormals-to-zero",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -21,7 +21,10 @@ int check_cfg(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
   const int G = cfg->fmt == FP4_FMT_MXFP4 ? 32 : 16;
   if (cfg->block != G) return FP4_ERR_INVALID_ARG;
   if (cfg->rotate != 0 && cfg->rotate != G) return FP4_ERR_INVALID_ARG;
-  if (cfg->rule != FP4_SCALE_ABSMAX) return FP4_ERR_UNSUPPORTED;
+  if (cfg->rule != FP4_SCALE_ABSMAX && cfg->rule != FP4_SCALE_MSE &&
+      cfg->rule != FP4_SCALE_FOUR_OVER_SIX)
+    return FP4_ERR_INVALID_ARG;
+  if (cfg->rule == FP4_SCALE_FOUR_OVER_SIX && cfg->fmt != FP4_FMT_NVFP4) return FP4_ERR_UNSUPPORTED;
   if (cfg->scale_layout != FP4_SCALES_ROWMAJOR && cfg->scale_layout != FP4_SCALES_GEMM)
     return FP4_ERR_INVALID_ARG;
   if (rows < 0 || cols < 0 || cols % G != 0) return FP4_ERR_INVALID_ARG;
@@ -109,7 +112,7 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (cfg->fmt == FP4_FMT_MXFP4) {
     if (empty) return FP4_OK;
-    return hip_status(fp4lib::launch_quantize_mx(x, xdt, cfg->rotate != 0, rows, cols, ldx, codes,
+    return hip_status(fp4lib::launch_quantize_mx(x, xdt, cfg->rotate != 0, cfg->rule, rows, cols, ldx, codes,
                                                  scales, gemm_layout(cfg) ? 1 : 0, st));
   }
   if (gs_mode != FP4_GS_COMPUTE && gs_mode != FP4_GS_GIVEN) return FP4_ERR_INVALID_ARG;
@@ -127,7 +130,7 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
     if (e != hipSuccess) return FP4_ERR_HIP;
   }
   if (empty) return FP4_OK;
-  return hip_status(fp4lib::launch_quantize_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, codes,
+  return hip_status(fp4lib::launch_quantize_nv(x, xdt, cfg->rotate != 0, cfg->rule, rows, cols, ldx, codes,
                                                scales, global_scale, partials, npart, st));
 }
 

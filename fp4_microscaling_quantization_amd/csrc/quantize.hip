@@ -38,9 +38,64 @@ constexpr int kThreads = 256;
 constexpr int kAmaxGrid = 512;  // partial maxima written by the amax pass
 
 // ------------------------------------------------------- per-block compute
+// Block-scale rules: FP4_SCALE_ABSMAX (the block maximum sets the scale),
+// FP4_SCALE_MSE (the candidate code with the smallest block squared error:
+// MXFP4 c0, c0 + 1; NVFP4 c0 - 2 .. c0 + 6), FP4_SCALE_FOUR_OVER_SIX (NVFP4:
+// the block maximum onto 6 or onto 4, the smaller error) -- "Bridging the Gap
+// ...", MR-GPTQ's MSE-optimised scales; "NVFP4 vs MXFP4 ...", the E2M1 grid
+// section and Four Over Six.  The error is summed in fp32 in element order with
+// one fma per element: d = fl32(y - y^), acc = fma(d, d, acc); a candidate
+// replaces the best only with a strictly smaller sum, so ties keep the earlier
+// one (the absmax code first).
+
+// Eight codes (one dword) -> their E2M1 grid values (exact, zero sign kept).
+__device__ __forceinline__ void decode8(uint32_t w, float* m) {
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  m[0] = a[0]; m[1] = a[1]; m[2] = b[0]; m[3] = b[1];
+  m[4] = c[0]; m[5] = c[1]; m[6] = d[0]; m[7] = d[1];
+}
+
+// Squared error of eight values against codes w dequantized as m * p (MXFP4:
+// p = 2^e exactly) or fl32(fl32(m * p) * ts) (NVFP4: p = the E4M3 value),
+// accumulated onto acc.  No contraction: y - y^ is rounded before the fma.
+template <int FMT>
+__device__ __forceinline__ float sse8(const float* v, uint32_t w, float p, float ts, float acc) {
+#pragma clang fp contract(off)
+  float m[8];
+  decode8(w, m);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float xh = FMT == FP4_FMT_MXFP4 ? m[i] * p : (m[i] * p) * ts;
+    const float d = v[i] - xh;
+    acc = __builtin_fmaf(d, d, acc);
+  }
+  return acc;
+}
+
+// 2^(code - 127) as an fp32 value (code 0: the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t code) {
+  return code == 0u ? as_f(0x00400000u) : as_f(code << 23);
+}
+
+__device__ __forceinline__ u32x4 mx_enc32(const float* v, uint32_t code) {
+  const float sc = e8m0_as_cvt_scale(code);
+  return u32x4{enc8_f32(&v[0], sc), enc8_f32(&v[8], sc), enc8_f32(&v[16], sc), enc8_f32(&v[24], sc)};
+}
+
+__device__ __forceinline__ float mx_sse32(const float* v, const u32x4& w, uint32_t code) {
+  const float p = e8m0_value(code);
+  float acc = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc = sse8<FP4_FMT_MXFP4>(&v[8 * t], w[t], p, 0.0f, acc);
+  return acc;
+}
+
 // MXFP4 block from 32 fp32 values (rotated in place when ROT); returns the
 // E8M0 code and the four code dwords.
-template <bool ROT>
+template <bool ROT, int RULE>
 __device__ __forceinline__ uint32_t mx_block_f32(float* v, u32x4& out) {
   if constexpr (ROT) {
     fwht<32>(v);
@@ -53,11 +108,16 @@ __device__ __forceinline__ uint32_t mx_block_f32(float* v, u32x4& out) {
   // floor(log2(amax)) = exponent field - 127 for a normal amax; subnormal and
   // zero amax clamp to the smallest scale (code 0).
   const uint32_t code = (uint32_t)max((int)((as_u(amax) >> 23) & 0xFFu) - 2, 0);
-  const float sc = e8m0_as_cvt_scale(code);
-  out[0] = enc8_f32(&v[0], sc);
-  out[1] = enc8_f32(&v[8], sc);
-  out[2] = enc8_f32(&v[16], sc);
-  out[3] = enc8_f32(&v[24], sc);
+  out = mx_enc32(v, code);
+  if constexpr (RULE == FP4_SCALE_MSE) {
+    if (code < 254u) {
+      const u32x4 o1 = mx_enc32(v, code + 1u);
+      if (mx_sse32(v, o1, code + 1u) < mx_sse32(v, out, code)) {
+        out = o1;
+        return code + 1u;
+      }
+    }
+  }
   return code;
 }
 
@@ -95,14 +155,20 @@ __device__ __forceinline__ NvTs make_ts(float ts) {
 
 // NVFP4 block scale from the block's amax: returns the E4M3 code and sets s
 // to the decoded scale e4m3 * ts (0 when the tensor scale or the block is 0).
+// E4M3 code of t = fl32(h / ts) (h = fl32(amax / 6), or amax / 4 for the
+// alternative of Four Over Six).
+__device__ __forceinline__ uint32_t nv_code_of(float h, const NvTs& T) {
+  const float t = (T.small || h < 0x1p-100f) ? h / T.ts : div_rn(h, T.ts, T.inv_ts);
+  return e4m3_rne_sat(t);
+}
+
 __device__ __forceinline__ uint32_t nv_scale(float amax, const NvTs& T, float& s) {
   uint32_t code = 0;
   s = 0.0f;
   if (T.live) {
     const float inv6 = 0x1.555556p-3f;  // fl32(1/6)
     const float h = (amax < 0x1p-100f) ? amax / 6.0f : div_rn(amax, 6.0f, inv6);
-    const float t = (T.small || h < 0x1p-100f) ? h / T.ts : div_rn(h, T.ts, T.inv_ts);
-    code = e4m3_rne_sat(t);
+    code = nv_code_of(h, T);
     s = e4m3_value(code) * T.ts;
   }
   return code;
@@ -131,8 +197,62 @@ __device__ __forceinline__ uint32_t nv_enc8(float* v, float s) {
 // |S| > s, so y = S/4 is a normal float (exact), fl32(S / (4 s)) equals
 // fl32(y / s), and max|y| = max|S| / 4 (rounding is monotone).  Smaller
 // tensor scales take the division by 4 first, as the definition orders it.
-template <bool ROT>
+// Codes of 16 values at scale s (v is kept).
+__device__ __forceinline__ u32x2 nv_enc16(const float* v, float s) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = v[i];
+  return u32x2{nv_enc8(&t[0], s), nv_enc8(&t[8], s)};
+}
+
+__device__ __forceinline__ float nv_sse16(const float* v, const u32x2& w, uint32_t code, float ts) {
+  const float p = e4m3_value(code);
+  return sse8<FP4_FMT_NVFP4>(&v[8], w[1], p, ts, sse8<FP4_FMT_NVFP4>(&v[0], w[0], p, ts, 0.0f));
+}
+
+// NVFP4 block under a searching rule (values already rotated and normalised):
+// the absmax code c0, then the rule's candidates in order.
+template <int RULE>
+__device__ __forceinline__ uint32_t nv_block_search(const float* v, float amax, const NvTs& T,
+                                                    u32x2& out) {
+  float s;
+  uint32_t best = nv_scale(amax, T, s);
+  out = nv_enc16(v, s);
+  if (!T.live) return best;
+  float best_e = nv_sse16(v, out, best, T.ts);
+  const int c0 = (int)best;
+  constexpr int NC = RULE == FP4_SCALE_MSE ? 8 : 1;
+  constexpr int kWindow[8] = {1, -1, 2, -2, 3, 4, 5, 6};
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    int c;
+    if constexpr (RULE == FP4_SCALE_MSE) c = c0 + kWindow[k];
+    else c = (int)nv_code_of(amax * 0.25f, T);  // maximum onto 4
+    if (c < 0 || c > 0x7E) continue;
+    const u32x2 o = nv_enc16(v, e4m3_value((uint32_t)c) * T.ts);
+    const float e = nv_sse16(v, o, (uint32_t)c, T.ts);
+    if (e < best_e) {
+      best_e = e;
+      best = (uint32_t)c;
+      out = o;
+    }
+  }
+  return best;
+}
+
+template <bool ROT, int RULE>
 __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out) {
+  if constexpr (RULE != FP4_SCALE_ABSMAX) {
+    if constexpr (ROT) {
+      fwht<16>(v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    return nv_block_search<RULE>(v, amax, T, out);
+  }
   const bool fold = ROT && !T.small;
   if constexpr (ROT) {
     fwht<16>(v);
@@ -181,10 +301,10 @@ __device__ __forceinline__ void store_mx_scale(uint8_t* __restrict__ scales, int
 
 // Quantize the block held in chunks c: codes in out (four dwords for MXFP4,
 // the first two for NVFP4), scale code returned.
-template <int FMT, int XDT, bool ROT>
+template <int FMT, int XDT, bool ROT, int RULE>
 __device__ __forceinline__ uint32_t compute_block(const u32x4* c, const NvTs& T, u32x4& out) {
   if constexpr (FMT == FP4_FMT_MXFP4) {
-    if constexpr (XDT == FP4_DT_BF16 && !ROT) {
+    if constexpr (XDT == FP4_DT_BF16 && !ROT && RULE == FP4_SCALE_ABSMAX) {
       uint32_t w[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -194,13 +314,13 @@ __device__ __forceinline__ uint32_t compute_block(const u32x4* c, const NvTs& T,
     } else {
       float v[32];
       unpack<XDT, 32>(c, v);
-      return mx_block_f32<ROT>(v, out);
+      return mx_block_f32<ROT, RULE>(v, out);
     }
   } else {
     float v[16];
     unpack<XDT, 16>(c, v);
     u32x2 o;
-    const uint32_t code = nv_block<ROT>(v, T, o);
+    const uint32_t code = nv_block<ROT, RULE>(v, T, o);
     out = u32x4{o[0], o[1], 0u, 0u};
     return code;
   }
@@ -221,13 +341,13 @@ __device__ __forceinline__ void store_block(const u32x4& out, uint32_t code, int
   }
 }
 
-template <int FMT, int XDT, bool ROT>
+template <int FMT, int XDT, bool ROT, int RULE>
 __device__ __forceinline__ void quantize_block(const u32x4* c, const NvTs& T, int64_t r, int64_t kb,
                                                int64_t nb, uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales, int64_t kchunks,
                                                int gemm_layout) {
   u32x4 out;
-  const uint32_t code = compute_block<FMT, XDT, ROT>(c, T, out);
+  const uint32_t code = compute_block<FMT, XDT, ROT, RULE>(c, T, out);
   store_block<FMT>(out, code, r, kb, nb, codes, scales, kchunks, gemm_layout);
 }
 
@@ -262,7 +382,7 @@ __device__ __forceinline__ NvTs nv_launch_ts(float* __restrict__ gs,
 // ----------------------------------------------------------- tiled kernel
 // Requires nb % 64 == 0.  Wave w of the grid-stride loop owns row r, blocks
 // [64 g, 64 g + 64).
-template <int FMT, int XDT, bool ROT>
+template <int FMT, int XDT, bool ROT, int RULE>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
@@ -302,8 +422,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
       u32x4 c[CH];
 #pragma unroll
       for (int k = 0; k < CH; ++k) c[k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
-      quantize_block<FMT, XDT, ROT>(c, T, r, (int64_t)g * 64 + lane, nb, codes, scales, kchunks,
-                                    gemm_layout);
+      quantize_block<FMT, XDT, ROT, RULE>(c, T, r, (int64_t)g * 64 + lane, nb, codes, scales,
+                                          kchunks, gemm_layout);
     }
     __syncthreads();
   }
@@ -379,7 +499,7 @@ __device__ __forceinline__ NvTs nv_ts_finish(const NvTsLoads& L, float* __restri
 // issues the loads of TPW tiles before any arithmetic, then runs them one by
 // one through its LDS buffer.  The scale bytes of a wave tile are 64
 // consecutive bytes of its row.
-template <int FMT, bool ROT, int TPW>
+template <int FMT, bool ROT, int TPW, int RULE>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t wpr,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
@@ -431,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 #pragma unroll
       for (int k = 0; k < CH; ++k) c[k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
       wave_lds_sync();
-      code[u] = compute_block<FMT, FP4_DT_BF16, ROT>(c, T, out[u]);
+      code[u] = compute_block<FMT, FP4_DT_BF16, ROT, RULE>(c, T, out[u]);
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -454,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 // 8w .. 8w + 7 of the tile; load j brings rows 2j, 2j + 1 (512 bytes each);
 // after the LDS transpose lane l holds block l % 8 of row l / 8, and the
 // codes of each row (8 blocks) are 128 contiguous bytes.
-template <bool ROT>
+template <bool ROT, int RULE>
 __global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
     const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t kcs,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks) {
@@ -488,7 +608,8 @@ __global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
     wave_lds_sync();
     const uint32_t r = r0 + (lane >> 3), kb = kc * 8 + (lane & 7);
     if (r < rows && kb < nb)
-      quantize_block<FP4_FMT_MXFP4, FP4_DT_BF16, ROT>(c, NvTs{}, r, kb, nb, codes, scales, kchunks, 1);
+      quantize_block<FP4_FMT_MXFP4, FP4_DT_BF16, ROT, RULE>(c, NvTs{}, r, kb, nb, codes, scales,
+                                                           kchunks, 1);
   }
 }
 
@@ -551,7 +672,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t*
 
 // ---------------------------------------------------------- direct kernel
 // Any shape: each thread loads its own block.
-template <int FMT, int XDT, bool ROT>
+template <int FMT, int XDT, bool ROT, int RULE>
 __global__ __launch_bounds__(kThreads) void quant_direct_kernel(
     const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
@@ -570,7 +691,7 @@ __global__ __launch_bounds__(kThreads) void quant_direct_kernel(
     u32x4 c[CH];
 #pragma unroll
     for (int k = 0; k < CH; ++k) c[k] = p[k];
-    quantize_block<FMT, XDT, ROT>(c, T, r, kb, nb, codes, scales, kchunks, gemm_layout);
+    quantize_block<FMT, XDT, ROT, RULE>(c, T, r, kb, nb, codes, scales, kchunks, gemm_layout);
   }
 }
 
@@ -679,7 +800,7 @@ int grid_cap(int64_t items, int cap) {
   return (int)g;
 }
 
-template <int FMT, int XDT, bool ROT>
+template <int FMT, int XDT, bool ROT, int RULE>
 hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
                     uint8_t* scales, int gemm_layout, float* gs, const float* partials, int npart,
                     hipStream_t st) {
@@ -688,20 +809,22 @@ hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint
   const int64_t kchunks = mx_gemm_kchunks(cols);
   if constexpr (XDT == FP4_DT_BF16) {
     const uint8_t* xb = static_cast<const uint8_t*>(x);
-    if (FMT == FP4_FMT_MXFP4 && gemm_layout) {
-      const uint32_t kcs = (nb + 7) / 8;
-      int64_t g = ((rows + 31) / 32) * (int64_t)kcs;
-      if (g > 16384) g = 16384;
-      quant_mx_gemm_kernel<ROT><<<(int)g, kThreads, 0, st>>>(xb, ldx * 2, (uint32_t)rows, nb, kcs,
-                                                            codes, scales, kchunks);
-      return hipGetLastError();
+    if constexpr (FMT == FP4_FMT_MXFP4) {
+      if (gemm_layout) {
+        const uint32_t kcs = (nb + 7) / 8;
+        int64_t g = ((rows + 31) / 32) * (int64_t)kcs;
+        if (g > 16384) g = 16384;
+        quant_mx_gemm_kernel<ROT, RULE><<<(int)g, kThreads, 0, st>>>(
+            xb, ldx * 2, (uint32_t)rows, nb, kcs, codes, scales, kchunks);
+        return hipGetLastError();
+      }
     }
     constexpr int TPW = FMT == FP4_FMT_MXFP4 ? 1 : 2;
     const uint32_t wpr = (nb + 63) / 64;
     const int64_t waves = (rows * (int64_t)wpr + TPW - 1) / TPW;
     int64_t g = (waves + kThreads / 64 - 1) / (kThreads / 64);
     if (g > 8192) g = 8192;
-    quant_rows_kernel<FMT, ROT, TPW><<<(int)g, kThreads, 0, st>>>(
+    quant_rows_kernel<FMT, ROT, TPW, RULE><<<(int)g, kThreads, 0, st>>>(
         xb, ldx * 2, (uint32_t)rows, nb, wpr, codes, scales, kchunks, gemm_layout, gs, partials, npart);
     return hipGetLastError();
   }
@@ -709,10 +832,10 @@ hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint
     const int64_t waves = rows * (int64_t)(nb / 64);
     int64_t g = (waves + 3) / 4;
     if (g > 4096) g = 4096;
-    quant_tile_kernel<FMT, XDT, ROT><<<(int)g, kThreads, 0, st>>>(
+    quant_tile_kernel<FMT, XDT, ROT, RULE><<<(int)g, kThreads, 0, st>>>(
         x, ldx, (uint32_t)rows, nb, codes, scales, kchunks, gemm_layout, gs, partials, npart);
   } else {
-    quant_direct_kernel<FMT, XDT, ROT><<<grid_cap(rows * (int64_t)nb, 8192), kThreads, 0, st>>>(
+    quant_direct_kernel<FMT, XDT, ROT, RULE><<<grid_cap(rows * (int64_t)nb, 8192), kThreads, 0, st>>>(
         x, ldx, (uint32_t)rows, nb, codes, scales, kchunks, gemm_layout, gs, partials, npart);
   }
   return hipGetLastError();
@@ -734,17 +857,27 @@ int amax_partials(int64_t rows, int64_t cols, int rotate, int xdt) {
   return grid_cap(items / 4 + 1, kAmaxGrid);
 }
 
-hipError_t launch_quantize_mx(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
-                              int64_t ldx, uint8_t* codes, uint8_t* scales, int gemm_layout,
-                              hipStream_t st) {
+// Instantiate launch_q for one format over input type x rotation x rule.
+template <int FMT, int RULE>
+hipError_t launch_q_rule(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
+                         int64_t ldx, uint8_t* codes, uint8_t* scales, int gemm_layout, float* gs,
+                         const float* partials, int npart, hipStream_t st) {
   if (xdt == FP4_DT_BF16) {
     if (rotate)
-      return launch_q<FP4_FMT_MXFP4, FP4_DT_BF16, true>(x, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
-    return launch_q<FP4_FMT_MXFP4, FP4_DT_BF16, false>(x, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
+      return launch_q<FMT, FP4_DT_BF16, true, RULE>(x, rows, cols, ldx, codes, scales, gemm_layout, gs, partials, npart, st);
+    return launch_q<FMT, FP4_DT_BF16, false, RULE>(x, rows, cols, ldx, codes, scales, gemm_layout, gs, partials, npart, st);
   }
   if (rotate)
-    return launch_q<FP4_FMT_MXFP4, FP4_DT_F32, true>(x, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
-  return launch_q<FP4_FMT_MXFP4, FP4_DT_F32, false>(x, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
+    return launch_q<FMT, FP4_DT_F32, true, RULE>(x, rows, cols, ldx, codes, scales, gemm_layout, gs, partials, npart, st);
+  return launch_q<FMT, FP4_DT_F32, false, RULE>(x, rows, cols, ldx, codes, scales, gemm_layout, gs, partials, npart, st);
+}
+
+hipError_t launch_quantize_mx(const void* x, int xdt, int rotate, int rule, int64_t rows,
+                              int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales,
+                              int gemm_layout, hipStream_t st) {
+  if (rule == FP4_SCALE_MSE)
+    return launch_q_rule<FP4_FMT_MXFP4, FP4_SCALE_MSE>(x, xdt, rotate, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
+  return launch_q_rule<FP4_FMT_MXFP4, FP4_SCALE_ABSMAX>(x, xdt, rotate, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
 }
 
 hipError_t launch_amax_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
@@ -784,17 +917,14 @@ hipError_t launch_amax_final(const float* partials, int npart, float* gs, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
-                              int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
+hipError_t launch_quantize_nv(const void* x, int xdt, int rotate, int rule, int64_t rows,
+                              int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
                               const float* partials, int npart, hipStream_t st) {
-  if (xdt == FP4_DT_BF16) {
-    if (rotate)
-      return launch_q<FP4_FMT_NVFP4, FP4_DT_BF16, true>(x, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
-    return launch_q<FP4_FMT_NVFP4, FP4_DT_BF16, false>(x, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
-  }
-  if (rotate)
-    return launch_q<FP4_FMT_NVFP4, FP4_DT_F32, true>(x, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
-  return launch_q<FP4_FMT_NVFP4, FP4_DT_F32, false>(x, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
+  if (rule == FP4_SCALE_MSE)
+    return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_MSE>(x, xdt, rotate, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
+  if (rule == FP4_SCALE_FOUR_OVER_SIX)
+    return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_FOUR_OVER_SIX>(x, xdt, rotate, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
+  return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_ABSMAX>(x, xdt, rotate, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
 }
 
 hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,

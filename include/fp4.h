@@ -64,7 +64,11 @@ typedef enum {
 } fp4_status;
 
 typedef enum { FP4_FMT_MXFP4 = 0, FP4_FMT_NVFP4 = 1 } fp4_format;
-typedef enum { FP4_SCALE_ABSMAX = 0 } fp4_scale_rule;
+typedef enum {
+    FP4_SCALE_ABSMAX = 0,       /* the block maximum sets the scale */
+    FP4_SCALE_MSE = 1,          /* smallest block squared error in a window */
+    FP4_SCALE_FOUR_OVER_SIX = 2 /* NVFP4: block maximum onto 6 or onto 4 */
+} fp4_scale_rule;
 typedef enum { FP4_DT_F32 = 0, FP4_DT_BF16 = 1 } fp4_dtype;
 typedef enum { FP4_SCALES_ROWMAJOR = 0, FP4_SCALES_GEMM = 1 } fp4_scale_layout;
 typedef enum { FP4_GS_COMPUTE = 0, FP4_GS_GIVEN = 1 } fp4_gs_mode;
@@ -73,7 +77,26 @@ typedef enum { FP4_GS_COMPUTE = 0, FP4_GS_GIVEN = 1 } fp4_gs_mode;
  *   fmt           fp4_format.
  *   block         32 for MXFP4, 16 for NVFP4 (any other value is rejected).
  *   rotate        0, or equal to block: block Hadamard of that size first.
- *   rule          FP4_SCALE_ABSMAX (the block maximum sets the scale).
+ *   rule          FP4_SCALE_ABSMAX: the block maximum sets the scale ("NVFP4 vs
+ *                 MXFP4 ...", the worked example and Figure 2).
+ *                 FP4_SCALE_MSE: the block-scale code with the smallest block
+ *                 squared error among candidates around the absmax code c0
+ *                 (MXFP4: c0, c0 + 1; NVFP4: c0 - 2 .. c0 + 6, tried in the
+ *                 order c0, +1, -1, +2, -2, +3, +4, +5, +6 and kept within
+ *                 0 .. 0x7E) ("Bridging the Gap ...", section 4.1: MR-GPTQ's
+ *                 MSE-optimised scales; "NVFP4 vs MXFP4 ...": the best scale
+ *                 does not always put the maximum on 6).
+ *                 FP4_SCALE_FOUR_OVER_SIX (NVFP4 only, else
+ *                 FP4_ERR_UNSUPPORTED): c0 or the code that maps the block
+ *                 maximum onto 4, whichever has the smaller error ("NVFP4 vs
+ *                 MXFP4 ...", follow-on research: Four Over Six).
+ *                 The error of a candidate is summed in fp32 over the block in
+ *                 element order, d = fl32(y - y^), acc = fma(d, d, acc), where
+ *                 y^ is the value fp4_dequantize returns (in the rotated domain
+ *                 when rotate != 0); a later candidate wins only with a
+ *                 strictly smaller sum.  The NVFP4 tensor scale is the same
+ *                 under every rule (amax / (6 * 448)). Blocks whose tensor
+ *                 scale is 0 store zeros as under the absmax rule.
  *   scale_layout  FP4_SCALES_ROWMAJOR: byte (r, kb) at r * (cols/block) + kb.
  *                 FP4_SCALES_GEMM: the layout fp4_gemm reads; byte positions
  *                 are given by fp4_scale_offset.  For NVFP4 the two layouts

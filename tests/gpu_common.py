@@ -124,3 +124,36 @@ def gemm_tolerance_ok(got: np.ndarray, ref: np.ndarray, absref: np.ndarray, bf16
     if not bf16:
         return err <= 1e-5 * absref
     return err <= 1e-5 * absref * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref)
+
+
+def assert_search_close(got_codes, got_scales, ref_codes, ref_scales, fmt, ts, y_ref,
+                        block_budget=1e-3, elem_budget=1e-4, what=""):
+    """Rotated paths under a searching scale rule: the GPU's butterfly sums may
+    differ from the oracle's exact ones by an ulp, which can flip a near-tie
+    between two candidate scales.  At most `block_budget` of the blocks may
+    take another scale, and each such block's squared error (against the
+    oracle's rotated values, dequantized by the oracle) must be within 1e-4 of
+    the oracle's choice; where the scales agree, element codes follow the
+    rotated budget (adjacent points only)."""
+    import oracle
+    G = fp4.BLOCK[fmt]
+    sd = got_scales != ref_scales
+    srate = sd.mean()
+    say("  %s scale choices differing: %d of %d (%.2e)" % (what, sd.sum(), sd.size, srate))
+    assert srate <= block_budget, (what, srate)
+    if sd.any():
+        yg = oracle.dequantize(got_codes, got_scales, fmt, ts).astype(np.float64)
+        yr = oracle.dequantize(ref_codes, ref_scales, fmt, ts).astype(np.float64)
+        y = y_ref.astype(np.float64)
+        eg = ((yg - y) ** 2).reshape(y.shape[0], -1, G).sum(-1)[sd]
+        er = ((yr - y) ** 2).reshape(y.shape[0], -1, G).sum(-1)[sd]
+        assert np.all(eg <= er * (1 + 1e-4) + 1e-300), (what, eg[:4], er[:4])
+    same = np.repeat(~sd, G // 2, axis=1)
+    gv = signed_values(got_codes)
+    rv = signed_values(ref_codes)
+    diff = (gv != rv) & np.repeat(same, 2, axis=1)
+    rate = diff.sum() / gv.size
+    say("  %s element mismatches in same-scale blocks: %d (%.2e)" % (what, diff.sum(), rate))
+    assert rate <= elem_budget, (what, rate)
+    if diff.any():
+        assert np.all(np.abs(grid_index(gv[diff]) - grid_index(rv[diff])) <= 1), what

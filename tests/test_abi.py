@@ -94,8 +94,14 @@ def test_quantize_rejects_bad_arguments_on_host():
     assert _q(bad) == E.FP4_ERR_INVALID_ARG                  # MXFP4 block must be 32
     bad = fp4.QConfig(fp4.FMT_MXFP4, 32, 16, 0, 0)
     assert _q(bad) == E.FP4_ERR_INVALID_ARG                  # rotation size must equal block
-    bad = fp4.QConfig(fp4.FMT_NVFP4, 16, 0, 1, 0)
-    assert _q(bad) == E.FP4_ERR_UNSUPPORTED                  # only the absmax scale rule
+    ok = fp4.QConfig(fp4.FMT_NVFP4, 16, 0, fp4.SCALE_MSE, 0)
+    assert fp4.fp4_scales_bytes(ok, 64, 256) == 64 * 16       # the MSE rule is a valid config
+    ok = fp4.QConfig(fp4.FMT_NVFP4, 16, 0, fp4.SCALE_FOUR_OVER_SIX, 0)
+    assert fp4.fp4_scales_bytes(ok, 64, 256) == 64 * 16
+    bad = fp4.QConfig(fp4.FMT_MXFP4, 32, 0, fp4.SCALE_FOUR_OVER_SIX, 0)
+    assert _q(bad) == E.FP4_ERR_UNSUPPORTED                  # Four Over Six is NVFP4's
+    bad = fp4.QConfig(fp4.FMT_NVFP4, 16, 0, 3, 0)
+    assert _q(bad) == E.FP4_ERR_INVALID_ARG                  # no such rule
     bad = fp4.QConfig(3, 32, 0, 0, 0)
     assert _q(bad) == E.FP4_ERR_INVALID_ARG
     bad = fp4.QConfig(fp4.FMT_MXFP4, 32, 0, 0, 9)

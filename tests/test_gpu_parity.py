@@ -16,8 +16,8 @@ torch = pytest.importorskip("torch")
 import fp4_microscaling_quantization_amd as fp4
 import oracle
 import workloads
-from gpu_common import (assert_rotated_codes_close, codes_np, gemm_tolerance_ok, rowmajor_scales_np,
-                        say, to_dev_bf16, to_dev_f32, to_dev_u8)
+from gpu_common import (assert_rotated_codes_close, assert_search_close, codes_np, gemm_tolerance_ok,
+                        rowmajor_scales_np, say, to_dev_bf16, to_dev_f32, to_dev_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +113,76 @@ def test_quantize_rotated(case, fmt):
         g = np.float32(q.global_scale.item())
         assert abs(int(g.view(np.int32)) - int(np.float32(rts).view(np.int32))) <= 1, (g, rts)
     assert_rotated_codes_close(codes_np(q), rc, rowmajor_scales_np(q), rs, what=case)
+
+
+RULES = [(fp4.FMT_MXFP4, fp4.SCALE_MSE), (fp4.FMT_NVFP4, fp4.SCALE_MSE),
+         (fp4.FMT_NVFP4, fp4.SCALE_FOUR_OVER_SIX)]
+RULE_IDS = ["mxfp4-mse", "nvfp4-mse", "nvfp4-4over6"]
+
+
+@pytest.mark.parametrize("case", ["cfg1", "cfg2_gauss", "cfg2_laplace", "ragged", "tiny_rows",
+                                  "tiny_scale"])
+@pytest.mark.parametrize("fmt,rule", RULES, ids=RULE_IDS)
+def test_quantize_scale_search_bit_exact(case, fmt, rule):
+    """Searching block-scale rules, non-rotated: codes, scale codes and the
+    NVFP4 tensor scale bit for bit (the error sums that decide are fp32 in a
+    fixed order on both sides)."""
+    say("quantize scale search", case, FNAME[fmt], rule)
+    xh, xd = _inputs(case)
+    rc, rs, rts = oracle.quantize(xh, fmt, rule=rule)
+    lays = [fp4.SCALES_GEMM, fp4.SCALES_ROWMAJOR] if fmt == fp4.FMT_MXFP4 else [fp4.SCALES_ROWMAJOR]
+    for lay in lays:
+        q = _prefill(fp4.quantize(xd, fmt, scale_layout=lay, rule=rule))
+        q = fp4.quantize(xd, fmt, scale_layout=lay, rule=rule, out=q)
+        torch.cuda.synchronize()
+        gc, gs = codes_np(q), rowmajor_scales_np(q)
+        bad = np.nonzero(gs != rs)
+        assert bad[0].size == 0, (case, lay, bad[0][:4], bad[1][:4], gs[bad][:4], rs[bad][:4])
+        assert np.array_equal(gc, rc), (case, lay)
+        if fmt == fp4.FMT_NVFP4:
+            assert q.global_scale.item() == float(rts)
+
+
+@pytest.mark.parametrize("case", ["cfg2_laplace", "ragged"])
+@pytest.mark.parametrize("fmt,rule", RULES, ids=RULE_IDS)
+def test_quantize_scale_search_rotated(case, fmt, rule):
+    say("quantize scale search rotated", case, FNAME[fmt], rule)
+    xh, xd = _inputs(case)
+    rc, rs, rts = oracle.quantize(xh, fmt, rotate=True, rule=rule)
+    lay = fp4.SCALES_GEMM if fmt == fp4.FMT_MXFP4 else fp4.SCALES_ROWMAJOR
+    q = fp4.quantize(xd, fmt, rotate=True, scale_layout=lay, rule=rule)
+    torch.cuda.synchronize()
+    ts = rts
+    if fmt == fp4.FMT_NVFP4:
+        g = np.float32(q.global_scale.item())
+        assert abs(int(g.view(np.int32)) - int(np.float32(rts).view(np.int32))) <= 1, (g, rts)
+        ts = g
+        if g != rts:   # the tensor scales differ by an ulp: compare against the oracle at the GPU's
+            rc, rs, _ = oracle.quantize(xh, fmt, rotate=True, ts=g, rule=rule)
+    y = oracle.rotate(xh, fp4.BLOCK[fmt])
+    assert_search_close(codes_np(q), rowmajor_scales_np(q), rc, rs, fmt, ts, y, what=case)
+
+
+def test_scale_search_lowers_the_error():
+    """On the same tensor the searching rules give a smaller reconstruction
+    error than absmax (GPU error sums), and rotation plus MSE scales brings
+    NVFP4 below its absmax error ("MR-GPTQ-NVFP4": an MSE-optimised grid on
+    rotated weights)."""
+    xh, xd = _inputs("cfg2_laplace")
+    res = {}
+    for fmt, rule in [(fp4.FMT_MXFP4, fp4.SCALE_ABSMAX)] + RULES[:1] + [
+            (fp4.FMT_NVFP4, fp4.SCALE_ABSMAX)] + RULES[1:]:
+        for rot in (False, True):
+            q = fp4.quantize(xd, fmt, rotate=rot, rule=rule)
+            s = fp4.error_sums(xd, q).cpu().numpy()
+            res[(fmt, rule, rot)] = s[0] / s[1]
+    say("  nmse " + " ".join("%s/%d/%s=%.5f" % (FNAME[f], r, "rot" if o else "plain", v)
+                              for (f, r, o), v in res.items()))
+    for rot in (False, True):
+        assert res[(fp4.FMT_MXFP4, fp4.SCALE_MSE, rot)] < res[(fp4.FMT_MXFP4, fp4.SCALE_ABSMAX, rot)]
+        assert res[(fp4.FMT_NVFP4, fp4.SCALE_MSE, rot)] < res[(fp4.FMT_NVFP4, fp4.SCALE_FOUR_OVER_SIX, rot)]
+        assert res[(fp4.FMT_NVFP4, fp4.SCALE_FOUR_OVER_SIX, rot)] < res[(fp4.FMT_NVFP4, fp4.SCALE_ABSMAX, rot)]
+    assert res[(fp4.FMT_NVFP4, fp4.SCALE_MSE, True)] < res[(fp4.FMT_NVFP4, fp4.SCALE_ABSMAX, False)]
 
 
 @pytest.mark.parametrize("case", ["cfg1", "cfg2_laplace", "ragged"])
