@@ -28,7 +28,9 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 MXFP4 = 0
 NVFP4 = 1
-BLOCK = {MXFP4: 32, NVFP4: 16}
+MXINT4 = 2
+NVINT4 = 3
+BLOCK = {MXFP4: 32, NVFP4: 16, MXINT4: 32, NVINT4: 16}
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
@@ -78,6 +80,12 @@ def _load(path: str):
                                          P, P]
     L.ora_e2m1_encode_array.restype = None
     L.ora_e2m1_encode_array.argtypes = [P, l, P]
+    L.ora_int4_decode.restype = ctypes.c_double
+    L.ora_int4_decode.argtypes = [ctypes.c_int]
+    L.ora_int4_encode.restype = ctypes.c_int
+    L.ora_int4_encode.argtypes = [ctypes.c_float]
+    L.ora_int4_encode_array.restype = None
+    L.ora_int4_encode_array.argtypes = [P, l, P]
     L.ora_e4m3_encode_array.restype = None
     L.ora_e4m3_encode_array.argtypes = [P, l, P]
     return L
@@ -119,6 +127,21 @@ def e2m1_encode_array(q) -> np.ndarray:
     q = _f32(q).reshape(-1)
     out = np.empty(q.size, dtype=np.uint8)
     lib().ora_e2m1_encode_array(_p(q), q.size, _p(out))
+    return out
+
+
+def int4_decode(code: int) -> float:
+    return lib().ora_int4_decode(int(code))
+
+
+def int4_encode(q: float) -> int:
+    return lib().ora_int4_encode(float(q))
+
+
+def int4_encode_array(q) -> np.ndarray:
+    q = _f32(q).reshape(-1)
+    out = np.empty(q.size, dtype=np.uint8)
+    lib().ora_int4_encode_array(_p(q), q.size, _p(out))
     return out
 
 

@@ -47,6 +47,8 @@
 
 #define ORA_MXFP4 0
 #define ORA_NVFP4 1
+#define ORA_MXINT4 2
+#define ORA_NVINT4 3
 
 #define ORA_OK 0
 #define ORA_EINVAL -1
@@ -140,6 +142,69 @@ int ora_e4m3_encode(float t)
 double ora_e8m0_decode(int code)
 {
     return ldexp(1.0, code - 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT4 element ([MRGPTQ] "MXINT4 and NVINT4": the MXFP4 / NVFP4 layouts     */
+/* with a 4-bit integer element).  Reading: a signed two's-complement nibble */
+/* used symmetrically, values -7 .. 7 (the pattern 0x8 = -8 is never         */
+/* produced), nearest integer with ties to even, saturating at +-7.  There  */
+/* is no negative zero.                                                      */
+/* ------------------------------------------------------------------------ */
+
+double ora_int4_decode(int code)
+{
+    int c = code & 15;
+    return c >= 8 ? (double)(c - 16) : (double)c;
+}
+
+int ora_int4_encode(float q)
+{
+    double a = fabs((double)q);
+    if (a > 7.0)
+        a = 7.0;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int m = 0; m <= 7; ++m) {
+        double d = fabs(a - (double)m);
+        if (d < bestd || (d == bestd && (m & 1) == 0)) {
+            best = m;
+            bestd = d;
+        }
+    }
+    int v = signbit(q) ? -best : best;
+    return v & 15;
+}
+
+/* Block size of a format (0: not a format). */
+static int fmt_block(int fmt)
+{
+    if (fmt == ORA_MXFP4 || fmt == ORA_MXINT4)
+        return 32;
+    if (fmt == ORA_NVFP4 || fmt == ORA_NVINT4)
+        return 16;
+    return 0;
+}
+
+/* E8M0 block scales (MX) rather than E4M3 block scales and a tensor scale. */
+static int fmt_mx(int fmt)
+{
+    return fmt == ORA_MXFP4 || fmt == ORA_MXINT4;
+}
+
+static int fmt_int(int fmt)
+{
+    return fmt == ORA_MXINT4 || fmt == ORA_NVINT4;
+}
+
+static double elem_decode(int fmt, int code)
+{
+    return fmt_int(fmt) ? ora_int4_decode(code) : ora_e2m1_decode(code);
+}
+
+static int elem_encode(int fmt, float q)
+{
+    return fmt_int(fmt) ? ora_int4_encode(q) : ora_e2m1_encode(q);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -238,17 +303,17 @@ static int get_code(const uint8_t *row_codes, long k)
  * a zero s gives all-zero codes. */
 static void block_encode(int fmt, const float *yb, int G, int sc, float tsv, int *code)
 {
-    float s = fmt == ORA_MXFP4 ? ldexpf(1.0f, sc - 127) : (float)ora_e4m3_decode(sc) * tsv;
+    float s = fmt_mx(fmt) ? ldexpf(1.0f, sc - 127) : (float)ora_e4m3_decode(sc) * tsv;
     for (int i = 0; i < G; ++i)
-        code[i] = s != 0.0f ? ora_e2m1_encode(yb[i] / s) : 0;
+        code[i] = s != 0.0f ? elem_encode(fmt, yb[i] / s) : 0;
 }
 
 /* Dequantized value of one element (as ora_dequantize computes it, in fp32). */
 static float element_value(int fmt, int code, int sc, float tsv)
 {
-    if (fmt == ORA_MXFP4)
-        return (float)ora_e2m1_decode(code) * ldexpf(1.0f, sc - 127);
-    float inner = (float)(ora_e2m1_decode(code) * ora_e4m3_decode(sc));
+    if (fmt_mx(fmt))
+        return (float)elem_decode(fmt, code) * ldexpf(1.0f, sc - 127);
+    float inner = (float)(elem_decode(fmt, code) * ora_e4m3_decode(sc));
     return inner * tsv;
 }
 
@@ -277,7 +342,11 @@ static int nv_scale_code(float amax, float top, float tsv)
 
 /*
  * Quantize x [rows, cols] (fp32, row-major, blocks run along cols).
- *   fmt     ORA_MXFP4 (block 32, E8M0) or ORA_NVFP4 (block 16, E4M3 x fp32).
+ *   fmt     ORA_MXFP4 (block 32, E8M0) or ORA_NVFP4 (block 16, E4M3 x fp32),
+ *           or their INT4-element twins ORA_MXINT4 / ORA_NVINT4 ([MRGPTQ]:
+ *           identical except for the element; the NVINT4 tensor scale is
+ *           amax / (7 * 448) and its block scale maps the block maximum onto 7;
+ *           only the absmax rule).
  *   rotate  0, or 1 for a block Hadamard of the block size applied first.
  *   rule    ORA_SCALE_ABSMAX: the block maximum sets the scale.
  *           ORA_SCALE_MSE: among candidate scale codes around the absmax code
@@ -301,19 +370,15 @@ static int nv_scale_code(float amax, float top, float tsv)
 int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, long cols,
                       uint8_t *codes, uint8_t *scales, float *ts, int gs_given)
 {
-    int G;
-    if (fmt == ORA_MXFP4)
-        G = 32;
-    else if (fmt == ORA_NVFP4)
-        G = 16;
-    else
+    int G = fmt_block(fmt);
+    if (G == 0)
         return ORA_EINVAL;
     if (rows < 0 || cols < 0 || cols % G != 0 || (rotate != 0 && rotate != 1))
         return ORA_EINVAL;
-    if (fmt == ORA_NVFP4 && ts == NULL)
+    if (!fmt_mx(fmt) && ts == NULL)
         return ORA_EINVAL;
-    if (rule != ORA_SCALE_ABSMAX && rule != ORA_SCALE_MSE &&
-        !(rule == ORA_SCALE_FOUR_OVER_SIX && fmt == ORA_NVFP4))
+    if (rule != ORA_SCALE_ABSMAX && (fmt_int(fmt) || (rule != ORA_SCALE_MSE &&
+        !(rule == ORA_SCALE_FOUR_OVER_SIX && fmt == ORA_NVFP4))))
         return ORA_EINVAL;
 
     long n = rows * cols;
@@ -328,7 +393,7 @@ int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, 
     }
 
     float tsv = 0.0f;
-    if (fmt == ORA_NVFP4) {
+    if (!fmt_mx(fmt)) {
         if (gs_given) {
             tsv = *ts;
         } else {
@@ -338,7 +403,10 @@ int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, 
                 if (a > gamax)
                     gamax = a;
             }
-            tsv = gamax / 2688.0f;          /* 6 * 448 */
+            if (fmt == ORA_NVFP4)
+                tsv = gamax / 2688.0f;          /* 6 * 448 */
+            else
+                tsv = gamax / 3136.0f;          /* 7 * 448: the INT4 maximum */
             *ts = tsv;
         }
     }
@@ -352,17 +420,24 @@ int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, 
             const float *yb = y + r * cols + b * G;
             float amax = block_amax(yb, G);
             int sc;
-            if (fmt == ORA_MXFP4) {
+            if (fmt_mx(fmt)) {
+                /* floor(log2 amax) - 2 for both elements: 4 = 2^2 is the
+                 * largest power of two of E2M1 (max 6) and of INT4 (max 7) */
                 sc = mx_exponent(amax) + 127;
             } else {
                 sc = 0;
                 if (tsv > 0.0f) {
-                    float t = (amax / 6.0f) / tsv;
-                    sc = ora_e4m3_encode(t);
+                    if (fmt == ORA_NVFP4) {
+                        float t = (amax / 6.0f) / tsv;
+                        sc = ora_e4m3_encode(t);
+                    } else {
+                        float t = (amax / 7.0f) / tsv;
+                        sc = ora_e4m3_encode(t);
+                    }
                 }
             }
             block_encode(fmt, yb, G, sc, tsv, code);
-            if (rule != ORA_SCALE_ABSMAX && !(fmt == ORA_NVFP4 && !(tsv > 0.0f))) {
+            if (rule != ORA_SCALE_ABSMAX && !(!fmt_mx(fmt) && !(tsv > 0.0f))) {
                 int cands[9], nc = 0;
                 if (rule == ORA_SCALE_MSE && fmt == ORA_MXFP4) {
                     cands[nc++] = sc + 1;
@@ -372,7 +447,7 @@ int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, 
                 } else {
                     cands[nc++] = nv_scale_code(amax, 4.0f, tsv);
                 }
-                int maxcode = fmt == ORA_MXFP4 ? 254 : 0x7E;
+                int maxcode = fmt_mx(fmt) ? 254 : 0x7E;
                 float best = block_sse(fmt, yb, G, sc, tsv, code);
                 for (int k = 0; k < nc; ++k) {
                     int c = cands[k];
@@ -414,12 +489,8 @@ int ora_quantize(int fmt, int rotate, const float *x, long rows, long cols,
 int ora_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, float ts,
                    long rows, long cols, int inverse_rotate, float *y)
 {
-    int G;
-    if (fmt == ORA_MXFP4)
-        G = 32;
-    else if (fmt == ORA_NVFP4)
-        G = 16;
-    else
+    int G = fmt_block(fmt);
+    if (G == 0)
         return ORA_EINVAL;
     if (rows < 0 || cols < 0 || cols % G != 0)
         return ORA_EINVAL;
@@ -435,9 +506,9 @@ int ora_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, float t
     for (long r = 0; r < rows; ++r) {
         const uint8_t *rc = codes + r * (cols / 2);
         for (long k = 0; k < cols; ++k) {
-            double m = ora_e2m1_decode(get_code(rc, k));
+            double m = elem_decode(fmt, get_code(rc, k));
             int sc = scales[r * nb + k / G];
-            if (fmt == ORA_MXFP4) {
+            if (fmt_mx(fmt)) {
                 dst[r * cols + k] = (float)(m * ora_e8m0_decode(sc));
             } else {
                 float inner = (float)(m * ora_e4m3_decode(sc));
@@ -491,12 +562,8 @@ int ora_gemm_entries(int fmt, long K,
                      long nent, const long *rows, const long *cols,
                      double *y, double *absy)
 {
-    int G;
-    if (fmt == ORA_MXFP4)
-        G = 32;
-    else if (fmt == ORA_NVFP4)
-        G = 16;
-    else
+    int G = fmt_block(fmt);
+    if (G == 0)
         return ORA_EINVAL;
     if (K < 0 || K % G != 0)
         return ORA_EINVAL;
@@ -509,7 +576,7 @@ int ora_gemm_entries(int fmt, long K,
         double s = 0.0, sa = 0.0;
         for (long b = 0; b < nb; ++b) {
             double asv, bsv;            /* the two block scales */
-            if (fmt == ORA_MXFP4) {
+            if (fmt_mx(fmt)) {
                 asv = ora_e8m0_decode(as[b]);
                 bsv = ora_e8m0_decode(bs[b]);
             } else {
@@ -517,13 +584,13 @@ int ora_gemm_entries(int fmt, long K,
                 bsv = ora_e4m3_decode(bs[b]);
             }
             for (long k = b * G; k < (b + 1) * G; ++k) {
-                double av = ora_e2m1_decode(get_code(ac, k)) * asv;
-                double bv = ora_e2m1_decode(get_code(bc, k)) * bsv;
+                double av = elem_decode(fmt, get_code(ac, k)) * asv;
+                double bv = elem_decode(fmt, get_code(bc, k)) * bsv;
                 s += av * bv;
                 sa += fabs(av) * fabs(bv);
             }
         }
-        if (fmt == ORA_NVFP4) {
+        if (!fmt_mx(fmt)) {
             double g = (double)a_ts * (double)b_ts;
             s *= g;
             sa *= fabs(g);
@@ -549,12 +616,8 @@ int ora_gemm_w4a16_entries(int fmt, long K, const float *a, long lda,
                            long nent, const long *rows, const long *cols,
                            double *y, double *absy)
 {
-    int G;
-    if (fmt == ORA_MXFP4)
-        G = 32;
-    else if (fmt == ORA_NVFP4)
-        G = 16;
-    else
+    int G = fmt_block(fmt);
+    if (G == 0)
         return ORA_EINVAL;
     if (K < 0 || K % G != 0 || lda < K)
         return ORA_EINVAL;
@@ -565,14 +628,14 @@ int ora_gemm_w4a16_entries(int fmt, long K, const float *a, long lda,
         const uint8_t *bs = b_scales + cols[e] * nb;
         double s = 0.0, sa = 0.0;
         for (long b = 0; b < nb; ++b) {
-            double bsv = fmt == ORA_MXFP4 ? ora_e8m0_decode(bs[b]) : ora_e4m3_decode(bs[b]);
+            double bsv = fmt_mx(fmt) ? ora_e8m0_decode(bs[b]) : ora_e4m3_decode(bs[b]);
             for (long k = b * G; k < (b + 1) * G; ++k) {
-                double bv = ora_e2m1_decode(get_code(bc, k)) * bsv;
+                double bv = elem_decode(fmt, get_code(bc, k)) * bsv;
                 s += (double)ar[k] * bv;
                 sa += fabs((double)ar[k]) * fabs(bv);
             }
         }
-        if (fmt == ORA_NVFP4) {
+        if (!fmt_mx(fmt)) {
             s *= (double)b_ts;
             sa *= fabs((double)b_ts);
         }
@@ -587,6 +650,12 @@ void ora_e2m1_encode_array(const float *q, long n, uint8_t *out)
 {
     for (long i = 0; i < n; ++i)
         out[i] = (uint8_t)ora_e2m1_encode(q[i]);
+}
+
+void ora_int4_encode_array(const float *q, long n, uint8_t *out)
+{
+    for (long i = 0; i < n; ++i)
+        out[i] = (uint8_t)ora_int4_encode(q[i]);
 }
 
 void ora_e4m3_encode_array(const float *t, long n, uint8_t *out)

@@ -374,6 +374,136 @@ def check_absmax_scale_vs_best_scale():
         assert best in (e0, e0 + 1), (e0, sses)
 
 
+# ------------------------------------------------------ INT4 element formats
+def check_int4_codec():
+    """MXINT4 / NVINT4 element ([MRGPTQ]: the MX / NV formats with an INT4
+    element): a two's-complement nibble decodes to -8 .. 7; encoding is the
+    nearest integer (numpy's rint: ties to even) clipped to +-7, stored as
+    value & 15 (so -8 is never produced and zero has one code)."""
+    vals = np.array([oracle.int4_decode(c) for c in range(16)])
+    assert np.array_equal(vals, np.array(list(range(8)) + list(range(-8, 0)), dtype=float)), vals
+    g = workloads.rng(42, 42)
+    ints = np.arange(-9, 10, dtype=np.float64)
+    mids = ints[:-1] + 0.5
+    probe = [ints, mids, g.uniform(-12, 12, 20000), np.array([1e30, -1e30, 0.0, -0.0, 7.4999, 7.5])]
+    for arr in (ints, mids):
+        f = arr.astype(np.float32)
+        probe += [np.nextafter(f, np.float32(-1e9)), np.nextafter(f, np.float32(1e9))]
+    q = np.concatenate(probe).astype(np.float32)
+    codes = oracle.int4_encode_array(q)
+    ref = np.clip(np.rint(q.astype(np.float64)), -7, 7).astype(np.int64) & 15
+    bad = np.nonzero(codes != ref)[0]
+    assert bad.size == 0, (q[bad[:5]], codes[bad[:5]], ref[bad[:5]])
+    assert not np.any(codes == 8)
+    assert oracle.int4_encode(-0.0) == 0 and oracle.int4_encode(-0.4) == 0
+    assert oracle.int4_encode(2.5) == 2 and oracle.int4_encode(-3.5) == (-4 & 15)
+
+
+def check_int4_worked_blocks():
+    """Hand-checked blocks.  MXINT4: [7, -3, 2, 0.5, 0 ...] has floor(log2 7) - 2
+    = 0, scale 2^0, codes 7, -3, 2, 0 (0.5 ties to even).  NVINT4: a tensor whose
+    maximum is 7 has ts = 7 / 3136, the block holding it takes E4M3 code 0x7E
+    (448) and codes 7, -3, 1, 3 for [7, -3, 1.2, 2.6]."""
+    x = np.zeros(32, np.float32)
+    x[:4] = [7.0, -3.0, 2.0, 0.5]
+    c, s, _ = oracle.quantize(x, oracle.MXINT4)
+    assert s[0, 0] == 127, s
+    codes = np.stack([c[0] & 15, c[0] >> 4], -1).reshape(-1)
+    assert list(codes[:5]) == [7, 13, 2, 0, 0], codes[:5]
+    y = oracle.dequantize(c, s, oracle.MXINT4)
+    assert list(y[0, :4]) == [7.0, -3.0, 2.0, 0.0]
+    xn = np.zeros(32, np.float32)
+    xn[:4] = [7.0, -3.0, 1.2, 2.6]
+    xn[16:18] = [0.7, -0.35]
+    c, s, ts = oracle.quantize(xn, oracle.NVINT4)
+    assert ts == np.float32(np.float32(7.0) / np.float32(3136.0))
+    assert s[0, 0] == 0x7E, s
+    codes = np.stack([c[0] & 15, c[0] >> 4], -1).reshape(-1)
+    assert list(codes[:4]) == [7, 13, 1, 3], codes[:4]
+    # second block: amax 0.7 -> (0.7 / 7) / ts = 44.8 -> the nearest E4M3 value
+    e4 = _e4m3_values_from_definition()
+    t = (np.float32(0.7) / np.float32(7.0)) / ts
+    assert e4[s[0, 1]] == _binade_rne_e4m3(np.array([t], np.float32))[0]
+
+
+def check_int4_invariants():
+    """MXINT4: every block not clamped at the smallest scale has a code of
+    magnitude 4..7 (the scaled maximum lies in [4, 8)); NVINT4: the block that
+    holds the tensor maximum has scale code 0x7E and a code of magnitude 7;
+    neither format produces the pattern 0x8; MXINT4 is idempotent
+    (Q(D(Q(x))) = Q(x))."""
+    x = workloads.laplace(workloads.rng(43, 43), 64 * 512, 1.0).astype(np.float32).reshape(64, 512)
+    for rot in (False, True):
+        c, s, _ = oracle.quantize(x, oracle.MXINT4, rot)
+        v = np.stack([c & 15, c >> 4], -1).reshape(64, -1).astype(np.int64)
+        sv = np.where(v >= 8, v - 16, v)
+        assert not np.any(v == 8)
+        mx = np.abs(sv).reshape(64, -1, 32).max(-1)
+        assert np.all((mx >= 4) & (mx <= 7)), np.unique(mx)
+        if not rot:
+            y = oracle.dequantize(c, s, oracle.MXINT4)
+            c2, s2, _ = oracle.quantize(y, oracle.MXINT4)
+            assert np.array_equal(c2, c) and np.array_equal(s2, s)
+        c, s, ts = oracle.quantize(x, oracle.NVINT4, rot)
+        v = np.stack([c & 15, c >> 4], -1).reshape(64, -1).astype(np.int64)
+        assert not np.any(v == 8)
+        y = x if not rot else _block_values(x, 16, True).reshape(64, -1)
+        r, b = np.unravel_index(np.abs(y).argmax(), y.shape)
+        assert s[r, b // 16] == 0x7E
+        blk = np.where(v[r, (b // 16) * 16:(b // 16) * 16 + 16] >= 8,
+                       v[r, (b // 16) * 16:(b // 16) * 16 + 16] - 16, v[r, (b // 16) * 16:(b // 16) * 16 + 16])
+        assert np.abs(blk).max() == 7
+
+
+def check_int4_error_ordering():
+    """[MRGPTQ]'s error analysis predicts that NVINT4 profits from the block
+    Hadamard and beats the other formats: on Laplace data NVINT4 + H16 has the
+    lowest NMSE of {MXFP4, NVFP4, MXINT4, NVINT4} x {plain, rotated}, below
+    plain NVINT4; on Gaussian data NVINT4 is below NVFP4 (uniform grid)."""
+    g = workloads.rng(44, 44)
+    lap = workloads.laplace(g, 256 * 1024, 1.0).astype(np.float32).reshape(256, 1024)
+    gau = workloads.normal(g, 256 * 1024, 1.0).astype(np.float32).reshape(256, 1024)
+
+    def nm(x, fmt, rot):
+        c, s, t = oracle.quantize(x, fmt, rot)
+        y = oracle.dequantize(c, s, fmt, t, inverse_rotate=rot).astype(np.float64)
+        return ((x - y) ** 2).sum() / (x.astype(np.float64) ** 2).sum()
+
+    res = {(f, r): nm(lap, f, r) for f in (0, 1, 2, 3) for r in (False, True)}
+    best = min(res, key=res.get)
+    assert best == (oracle.NVINT4, True), res
+    assert res[(oracle.NVINT4, True)] < res[(oracle.NVINT4, False)]
+    assert nm(gau, oracle.NVINT4, False) < nm(gau, oracle.NVFP4, False)
+
+
+def check_gemm_int4_closed_forms():
+    """MXINT4 with every scale code 127 is an integer dot product (numpy int64
+    matmul of the two's-complement nibbles); NVINT4 sums int x E4M3 products
+    (E4M3 values from the definition) and multiplies by a_ts * b_ts."""
+    g = workloads.rng(45, 45)
+    M, N, K = 5, 7, 64
+    ac = g.integers(0, 256, (M, K // 2)).astype(np.uint8)
+    bc = g.integers(0, 256, (N, K // 2)).astype(np.uint8)
+
+    def ints(c):
+        v = np.stack([c & 15, c >> 4], -1).reshape(c.shape[0], -1).astype(np.int64)
+        return np.where(v >= 8, v - 16, v)
+
+    ones = np.full((M, K // 32), 127, np.uint8), np.full((N, K // 32), 127, np.uint8)
+    y, ab = oracle.gemm_full(oracle.MXINT4, K, ac, ones[0], 0.0, bc, ones[1], 0.0)
+    assert np.array_equal(y, (ints(ac) @ ints(bc).T).astype(np.float64))
+    assert np.array_equal(ab, (np.abs(ints(ac)) @ np.abs(ints(bc)).T).astype(np.float64))
+    e4 = _e4m3_values_from_definition()
+    asc = g.integers(0x20, 0x70, (M, K // 16)).astype(np.uint8)
+    bsc = g.integers(0x20, 0x70, (N, K // 16)).astype(np.uint8)
+    ats, bts = np.float32(0.013), np.float32(2.5e-3)
+    y, _ = oracle.gemm_full(oracle.NVINT4, K, ac, asc, ats, bc, bsc, bts)
+    av = ints(ac) * np.repeat(e4[asc], 16, axis=1)
+    bv = ints(bc) * np.repeat(e4[bsc], 16, axis=1)
+    ref = (av @ bv.T) * (float(ats) * float(bts))
+    assert np.allclose(y, ref, rtol=1e-13, atol=0)
+
+
 # ------------------------------------------------ scale search (MSE, 4/6)
 MX_WINDOW = (0, 1)
 NV_WINDOW = (0, 1, -1, 2, -2, 3, 4, 5, 6)

@@ -44,8 +44,8 @@ MUTANTS = [
     ("error sums drop a term", "se += (a - b) * (a - b);", "se += (a - b) * (a - b) * 0.5;"),
     ("w4a16 drops the weight tensor scale", "s *= (double)b_ts;", "s *= 1.0;"),
     ("w4a16 loses the activation sign", "s += (double)ar[k] * bv;", "s += fabs((double)ar[k]) * bv;"),
-    ("w4a16 scale of the next block", "double bsv = fmt == ORA_MXFP4 ? ora_e8m0_decode(bs[b]) : ora_e4m3_decode(bs[b]);",
-     "double bsv = fmt == ORA_MXFP4 ? ora_e8m0_decode(bs[(b + 1) % nb]) : ora_e4m3_decode(bs[(b + 1) % nb]);"),
+    ("w4a16 scale of the next block", "double bsv = fmt_mx(fmt) ? ora_e8m0_decode(bs[b]) : ora_e4m3_decode(bs[b]);",
+     "double bsv = fmt_mx(fmt) ? ora_e8m0_decode(bs[(b + 1) % nb]) : ora_e4m3_decode(bs[(b + 1) % nb]);"),
     ("mse window skips e0+1", "cands[nc++] = sc + 1;", "cands[nc++] = sc + 2;"),
     ("mse nv window loses c0-1", "nv_window[9] = {0, 1, -1, 2,", "nv_window[9] = {0, 1, 1, 2,"),
     ("mse ties go to later candidates", "if (e < best) {", "if (e <= best) {"),
@@ -53,6 +53,17 @@ MUTANTS = [
     ("mse scores a candidate with the old codes", "float e = block_sse(fmt, yb, G, c, tsv, cand_code);",
      "float e = block_sse(fmt, yb, G, c, tsv, code);"),
     ("four over six maps to 3", "nv_scale_code(amax, 4.0f, tsv)", "nv_scale_code(amax, 3.0f, tsv)"),
+    ("int4 ties away from even", "if (d < bestd || (d == bestd && (m & 1) == 0)) {",
+     "if (d < bestd || (d == bestd && (m & 1) == 1)) {"),
+    ("int4 saturates at 8 (two's-complement range)",
+     "if (a > 7.0)\n        a = 7.0;\n    int best = 0;\n    double bestd = INFINITY;\n    for (int m = 0; m <= 7; ++m) {",
+     "if (a > 8.0)\n        a = 8.0;\n    int best = 0;\n    double bestd = INFINITY;\n    for (int m = 0; m <= 8; ++m) {"),
+    ("int4 decode without sign extension", "return c >= 8 ? (double)(c - 16) : (double)c;",
+     "return c >= 8 ? (double)(8 - c) : (double)c;"),
+    ("nvint4 tensor scale uses the FP4 maximum", "tsv = gamax / 3136.0f;", "tsv = gamax / 2688.0f;"),
+    ("nvint4 block scale divides by 6", "float t = (amax / 7.0f) / tsv;", "float t = (amax / 6.0f) / tsv;"),
+    ("int4 formats decode as E2M1", "return fmt_int(fmt) ? ora_int4_decode(code) : ora_e2m1_decode(code);",
+     "return ora_e2m1_decode(code);"),
 ]
 
 
