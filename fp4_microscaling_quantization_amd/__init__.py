@@ -29,6 +29,8 @@ FP4_ERR_WORKSPACE = -4
 FP4_ERR_HIP = -5
 FMT_MXFP4 = 0
 FMT_NVFP4 = 1
+FMT_MXINT4 = 2
+FMT_NVINT4 = 3
 DT_F32 = 0
 DT_BF16 = 1
 SCALES_ROWMAJOR = 0
@@ -38,7 +40,8 @@ GS_GIVEN = 1
 SCALE_ABSMAX = 0
 SCALE_MSE = 1
 SCALE_FOUR_OVER_SIX = 2
-BLOCK = {FMT_MXFP4: 32, FMT_NVFP4: 16}
+BLOCK = {FMT_MXFP4: 32, FMT_NVFP4: 16, FMT_MXINT4: 32, FMT_NVINT4: 16}
+MX_FORMATS = (FMT_MXFP4, FMT_MXINT4)
 
 EXPORTED = [
     "fp4_codes_bytes", "fp4_scales_bytes", "fp4_workspace_bytes", "fp4_scale_offset",
@@ -262,7 +265,7 @@ def quantize(x, fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMA
         gs = torch.zeros(1, dtype=torch.float32, device=x.device)
         out = Quantized(codes, scales, gs, cfg, rows, cols)
     gs_mode = GS_COMPUTE
-    if fmt == FMT_NVFP4 and global_scale is not None:
+    if fmt not in MX_FORMATS and global_scale is not None:
         out.global_scale.copy_(global_scale.reshape(1))
         gs_mode = GS_GIVEN
     wsb = fp4_workspace_bytes(cfg, rows, cols)
@@ -274,11 +277,12 @@ def quantize(x, fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMA
     return out
 
 
-def global_scale(x, rotate: bool = False, out=None):
-    """NVFP4 per-tensor scale of a 2-D CUDA tensor (float32[1] CUDA tensor)."""
+def global_scale(x, rotate: bool = False, out=None, fmt: int = FMT_NVFP4):
+    """NVFP4 (or NVINT4) per-tensor scale of a 2-D CUDA tensor (float32[1]
+    CUDA tensor)."""
     torch = _torch()
     rows, cols = x.shape
-    cfg = qconfig(FMT_NVFP4, rotate)
+    cfg = qconfig(fmt, rotate)
     if out is None:
         out = torch.zeros(1, dtype=torch.float32, device=x.device)
     wsb = fp4_workspace_bytes(cfg, rows, cols)
@@ -336,7 +340,7 @@ def gemm_w4a16(a, b: Quantized, out_dtype=None, out=None, workspace=None):
     M, K = a.shape
     fmt, N = b.cfg.fmt, b.rows
     assert b.cols == K
-    assert fmt == FMT_NVFP4 or b.cfg.scale_layout == SCALES_GEMM, "weights need GEMM-layout scales"
+    assert fmt not in MX_FORMATS or b.cfg.scale_layout == SCALES_GEMM, "weights need GEMM-layout scales"
     if out is None:
         out = torch.empty(M, N, dtype=out_dtype or torch.bfloat16, device=a.device)
     wsb = fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K)

@@ -17,14 +17,15 @@ int dtype_bytes(int32_t dt) { return dt == FP4_DT_F32 ? 4 : (dt == FP4_DT_BF16 ?
 // Returns FP4_OK when cfg describes a supported quantization of [rows, cols].
 int check_cfg(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
   if (!cfg) return FP4_ERR_INVALID_ARG;
-  if (cfg->fmt != FP4_FMT_MXFP4 && cfg->fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
-  const int G = cfg->fmt == FP4_FMT_MXFP4 ? 32 : 16;
+  if (cfg->fmt < FP4_FMT_MXFP4 || cfg->fmt > FP4_FMT_NVINT4) return FP4_ERR_INVALID_ARG;
+  const int G = fp4k::fmt_block(cfg->fmt);
   if (cfg->block != G) return FP4_ERR_INVALID_ARG;
   if (cfg->rotate != 0 && cfg->rotate != G) return FP4_ERR_INVALID_ARG;
   if (cfg->rule != FP4_SCALE_ABSMAX && cfg->rule != FP4_SCALE_MSE &&
       cfg->rule != FP4_SCALE_FOUR_OVER_SIX)
     return FP4_ERR_INVALID_ARG;
   if (cfg->rule == FP4_SCALE_FOUR_OVER_SIX && cfg->fmt != FP4_FMT_NVFP4) return FP4_ERR_UNSUPPORTED;
+  if (cfg->rule != FP4_SCALE_ABSMAX && fp4k::fmt_int(cfg->fmt)) return FP4_ERR_UNSUPPORTED;
   if (cfg->scale_layout != FP4_SCALES_ROWMAJOR && cfg->scale_layout != FP4_SCALES_GEMM)
     return FP4_ERR_INVALID_ARG;
   if (rows < 0 || cols < 0 || cols % G != 0) return FP4_ERR_INVALID_ARG;
@@ -47,7 +48,7 @@ int check_ld(const void* p, int32_t dt, int64_t rows, int64_t cols, int64_t ld) 
 }
 
 bool gemm_layout(const fp4_qconfig* cfg) {
-  return cfg->fmt == FP4_FMT_MXFP4 && cfg->scale_layout == FP4_SCALES_GEMM;
+  return fp4k::fmt_mx(cfg->fmt) && cfg->scale_layout == FP4_SCALES_GEMM;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
@@ -86,7 +87,7 @@ size_t fp4_scales_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
 
 size_t fp4_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
   if (check_cfg(cfg, rows, cols) != FP4_OK) return 0;
-  return cfg->fmt == FP4_FMT_NVFP4 ? kNvWorkspace : 0;
+  return fp4k::fmt_mx(cfg->fmt) ? 0 : kNvWorkspace;
 }
 
 int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols, int64_t r, int64_t kb) {
@@ -110,10 +111,11 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
     if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (cfg->fmt == FP4_FMT_MXFP4) {
+  if (fp4k::fmt_mx(cfg->fmt)) {
     if (empty) return FP4_OK;
-    return hip_status(fp4lib::launch_quantize_mx(x, xdt, cfg->rotate != 0, cfg->rule, rows, cols, ldx, codes,
-                                                 scales, gemm_layout(cfg) ? 1 : 0, st));
+    return hip_status(fp4lib::launch_quantize_mx(cfg->fmt, x, xdt, cfg->rotate != 0, cfg->rule, rows,
+                                                 cols, ldx, codes, scales, gemm_layout(cfg) ? 1 : 0,
+                                                 st));
   }
   if (gs_mode != FP4_GS_COMPUTE && gs_mode != FP4_GS_GIVEN) return FP4_ERR_INVALID_ARG;
   if (!global_scale) return FP4_ERR_INVALID_ARG;
@@ -122,7 +124,7 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
   if (gs_mode == FP4_GS_COMPUTE) {
     if (!ws || ws_bytes < fp4_workspace_bytes(cfg, rows, cols)) return FP4_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
-    if (empty) return hip_status(fp4lib::launch_amax_final(nullptr, 0, global_scale, st));
+    if (empty) return hip_status(fp4lib::launch_amax_final(cfg->fmt, nullptr, 0, global_scale, st));
     partials = static_cast<float*>(ws);
     npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0, xdt);
     hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, partials,
@@ -130,8 +132,9 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
     if (e != hipSuccess) return FP4_ERR_HIP;
   }
   if (empty) return FP4_OK;
-  return hip_status(fp4lib::launch_quantize_nv(x, xdt, cfg->rotate != 0, cfg->rule, rows, cols, ldx, codes,
-                                               scales, global_scale, partials, npart, st));
+  return hip_status(fp4lib::launch_quantize_nv(cfg->fmt, x, xdt, cfg->rotate != 0, cfg->rule, rows,
+                                               cols, ldx, codes, scales, global_scale, partials,
+                                               npart, st));
 }
 
 int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows,
@@ -139,19 +142,20 @@ int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t
                      void* stream) {
   int rc = check_cfg(cfg, rows, cols);
   if (rc != FP4_OK) return rc;
-  if (cfg->fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
+  if (fp4k::fmt_mx(cfg->fmt)) return FP4_ERR_INVALID_ARG;
   rc = check_ld(x, xdt, rows, cols, ldx);
   if (rc != FP4_OK) return rc;
   if (!global_scale) return FP4_ERR_INVALID_ARG;
   if (!ws || ws_bytes < fp4_workspace_bytes(cfg, rows, cols)) return FP4_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (rows == 0 || cols == 0) return hip_status(fp4lib::launch_amax_final(nullptr, 0, global_scale, st));
+  if (rows == 0 || cols == 0)
+    return hip_status(fp4lib::launch_amax_final(cfg->fmt, nullptr, 0, global_scale, st));
   float* partials = static_cast<float*>(ws);
   const int npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0, xdt);
   hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, partials, npart, st);
   if (e != hipSuccess) return FP4_ERR_HIP;
-  return hip_status(fp4lib::launch_amax_final(partials, npart, global_scale, st));
+  return hip_status(fp4lib::launch_amax_final(cfg->fmt, partials, npart, global_scale, st));
 }
 
 int fp4_dequantize(const fp4_qconfig* cfg, const uint8_t* codes, const uint8_t* scales,
@@ -164,7 +168,7 @@ int fp4_dequantize(const fp4_qconfig* cfg, const uint8_t* codes, const uint8_t* 
   if (rows == 0 || cols == 0) return FP4_OK;
   if (!codes || !scales) return FP4_ERR_INVALID_ARG;
   if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
-  if (cfg->fmt == FP4_FMT_NVFP4 && !global_scale) return FP4_ERR_INVALID_ARG;
+  if (!fp4k::fmt_mx(cfg->fmt) && !global_scale) return FP4_ERR_INVALID_ARG;
   const int rot = (inverse_rotate != 0 && cfg->rotate != 0) ? 1 : 0;
   return hip_status(fp4lib::launch_dequantize(cfg->fmt, rot, gemm_layout(cfg) ? 1 : 0, codes, scales,
                                               global_scale, rows, cols, y, ydt, ldy,
@@ -191,7 +195,7 @@ int fp4_error_sums(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t r
   if (rows > 0 && cols > 0) {
     if (!codes || !scales) return FP4_ERR_INVALID_ARG;
     if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
-    if (cfg->fmt == FP4_FMT_NVFP4 && !global_scale) return FP4_ERR_INVALID_ARG;
+    if (!fp4k::fmt_mx(cfg->fmt) && !global_scale) return FP4_ERR_INVALID_ARG;
   }
   return hip_status(fp4lib::launch_error_sums(cfg->fmt, cfg->rotate != 0, gemm_layout(cfg) ? 1 : 0,
                                               x, xdt, ldx, codes, scales, global_scale, rows, cols,
@@ -203,7 +207,7 @@ int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor, i
                               int64_t cols, uint8_t* gemm_scales, void* stream) {
   int rc = check_cfg(cfg, rows, cols);
   if (rc != FP4_OK) return rc;
-  if (cfg->fmt != FP4_FMT_MXFP4) return FP4_ERR_UNSUPPORTED;  // NVFP4: the layouts coincide
+  if (!fp4k::fmt_mx(cfg->fmt)) return FP4_ERR_UNSUPPORTED;  // NV formats: the layouts coincide
   if (rows == 0 || cols == 0) return FP4_OK;
   if (!rowmajor || !gemm_scales) return FP4_ERR_INVALID_ARG;
   return hip_status(fp4lib::launch_scales_to_gemm(rowmajor, rows, cols, gemm_scales,
@@ -221,6 +225,7 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_code
              const uint8_t* a_scales, const float* a_gs, const uint8_t* b_codes,
              const uint8_t* b_scales, const float* b_gs, void* y, int32_t ydt, int64_t ldy,
              void* ws, size_t ws_bytes, void* stream) {
+  if (fmt == FP4_FMT_MXINT4 || fmt == FP4_FMT_NVINT4) return FP4_ERR_UNSUPPORTED;
   if (fmt != FP4_FMT_MXFP4 && fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID_ARG;
   if (K % 128 != 0) return FP4_ERR_UNSUPPORTED;
@@ -254,6 +259,7 @@ size_t fp4_gemm_w4a16_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t
 int fp4_gemm_w4a16(int32_t fmt, int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gs, void* y,
                    int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  if (fmt == FP4_FMT_MXINT4 || fmt == FP4_FMT_NVINT4) return FP4_ERR_UNSUPPORTED;
   if (fmt != FP4_FMT_MXFP4 && fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID_ARG;
   if (K % 256 != 0) return FP4_ERR_UNSUPPORTED;

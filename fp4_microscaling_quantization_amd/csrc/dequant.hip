@@ -20,44 +20,60 @@ namespace {
 constexpr int kThreads = 256;
 
 // Decode block (r, kb) into fp32 values (original domain if INV).
+//   MXFP4: e2m1 * 2^e (hardware decode with the E8M0 code as its scale).
+//   MXINT4: q * 2^e.  NVFP4 / NVINT4: fl32(fl32(element * e4m3) * ts), the
+//   inner product exact.
 template <int FMT, bool INV>
 __device__ __forceinline__ void decode_block(const uint8_t* __restrict__ codes,
                                              const uint8_t* __restrict__ scales, float ts,
                                              uint32_t r, uint32_t kb, uint32_t nb,
                                              int64_t kchunks, bool gemm_layout, float* v) {
-  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
+  constexpr int G = fmt_block(FMT);
   constexpr int NDW = G / 8;
   uint32_t w[NDW];
-  if constexpr (FMT == FP4_FMT_MXFP4) {
-    u32x4 t = *reinterpret_cast<const u32x4*>(codes + (int64_t)r * (nb * 16) + (int64_t)kb * 16);
+  if constexpr (fmt_mx(FMT)) {
+    const u32x4 t = *reinterpret_cast<const u32x4*>(codes + (int64_t)r * (nb * 16) + (int64_t)kb * 16);
     w[0] = t[0];
     w[1] = t[1];
     w[2] = t[2];
     w[3] = t[3];
-    int64_t off = gemm_layout ? mx_gemm_scale_offset(r, kb, kchunks) : (int64_t)r * nb + kb;
-    const float sc = e8m0_as_cvt_scale(scales[off]);
+    const int64_t off = gemm_layout ? mx_gemm_scale_offset(r, kb, kchunks) : (int64_t)r * nb + kb;
+    if constexpr (fmt_int(FMT)) {
+      const float p = e8m0_value(scales[off]);
 #pragma unroll
-    for (int i = 0; i < NDW; ++i) {
+      for (int i = 0; i < NDW; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x2 p = dec2_f32(w[i] >> (8 * j), sc);
-        v[8 * i + 2 * j] = p[0];
-        v[8 * i + 2 * j + 1] = p[1];
-      }
+        for (int j = 0; j < 8; ++j) v[8 * i + j] = int4_value(w[i], j) * p;
+    } else {
+      const float sc = e8m0_as_cvt_scale(scales[off]);
+#pragma unroll
+      for (int i = 0; i < NDW; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x2 p = dec2_f32(w[i] >> (8 * j), sc);
+          v[8 * i + 2 * j] = p[0];
+          v[8 * i + 2 * j + 1] = p[1];
+        }
     }
   } else {
-    u32x2 t = *reinterpret_cast<const u32x2*>(codes + (int64_t)r * (nb * 8) + (int64_t)kb * 8);
+    const u32x2 t = *reinterpret_cast<const u32x2*>(codes + (int64_t)r * (nb * 8) + (int64_t)kb * 8);
     w[0] = t[0];
     w[1] = t[1];
     const float e4 = e4m3_value(scales[(int64_t)r * nb + kb]);
+    if constexpr (fmt_int(FMT)) {
 #pragma unroll
-    for (int i = 0; i < NDW; ++i) {
+      for (int i = 0; i < NDW; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x2 p = dec2_f32(w[i] >> (8 * j), 1.0f);
-        v[8 * i + 2 * j] = (p[0] * e4) * ts;
-        v[8 * i + 2 * j + 1] = (p[1] * e4) * ts;
-      }
+        for (int j = 0; j < 8; ++j) v[8 * i + j] = (int4_value(w[i], j) * e4) * ts;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NDW; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x2 p = dec2_f32(w[i] >> (8 * j), 1.0f);
+          v[8 * i + 2 * j] = (p[0] * e4) * ts;
+          v[8 * i + 2 * j + 1] = (p[1] * e4) * ts;
+        }
     }
   }
   if constexpr (INV) {
@@ -77,8 +93,8 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ gs, uint32_t rows, uint32_t nb, int64_t kchunks, int gemm_layout,
     void* __restrict__ y, int64_t ldy) {
-  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
-  const float ts = FMT == FP4_FMT_NVFP4 ? *gs : 0.0f;
+  constexpr int G = fmt_block(FMT);
+  const float ts = fmt_mx(FMT) ? 0.0f : *gs;
   const uint32_t total = rows * nb;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
     const uint32_t r = b / nb;
@@ -140,8 +156,8 @@ __global__ __launch_bounds__(kThreads) void error_partial_kernel(
     const void* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ gs, uint32_t rows, uint32_t nb,
     int64_t kchunks, int gemm_layout, double* __restrict__ partials) {
-  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
-  const float ts = FMT == FP4_FMT_NVFP4 ? *gs : 0.0f;
+  constexpr int G = fmt_block(FMT);
+  const float ts = fmt_mx(FMT) ? 0.0f : *gs;
   double se = 0.0, sx = 0.0, sxy = 0.0, sy = 0.0;
   const uint32_t total = rows * nb;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
@@ -220,7 +236,7 @@ namespace fp4lib {
 hipError_t launch_dequantize(int fmt, int rotate, int gemm_layout, const uint8_t* codes,
                              const uint8_t* scales, const float* gs, int64_t rows, int64_t cols,
                              void* y, int ydt, int64_t ldy, hipStream_t st) {
-  const int G = fmt == FP4_FMT_MXFP4 ? 32 : 16;
+  const int G = fmt_block(fmt);
   const uint32_t nb = (uint32_t)(cols / G);
   const int64_t total = rows * (int64_t)nb;
   if (total == 0) return hipSuccess;
@@ -236,8 +252,12 @@ hipError_t launch_dequantize(int fmt, int rotate, int gemm_layout, const uint8_t
   } while (0)
   if (fmt == FP4_FMT_MXFP4) {
     if (rotate) FP4_DQ_Y(FP4_FMT_MXFP4, true); else FP4_DQ_Y(FP4_FMT_MXFP4, false);
-  } else {
+  } else if (fmt == FP4_FMT_NVFP4) {
     if (rotate) FP4_DQ_Y(FP4_FMT_NVFP4, true); else FP4_DQ_Y(FP4_FMT_NVFP4, false);
+  } else if (fmt == FP4_FMT_MXINT4) {
+    if (rotate) FP4_DQ_Y(FP4_FMT_MXINT4, true); else FP4_DQ_Y(FP4_FMT_MXINT4, false);
+  } else {
+    if (rotate) FP4_DQ_Y(FP4_FMT_NVINT4, true); else FP4_DQ_Y(FP4_FMT_NVINT4, false);
   }
 #undef FP4_DQ_Y
 #undef FP4_DQ
@@ -245,7 +265,7 @@ hipError_t launch_dequantize(int fmt, int rotate, int gemm_layout, const uint8_t
 }
 
 int error_partials(int64_t rows, int64_t cols, int fmt) {
-  const int G = fmt == FP4_FMT_MXFP4 ? 32 : 16;
+  const int G = fmt_block(fmt);
   return grid_for(rows * (cols / G), 1024);
 }
 
@@ -253,7 +273,7 @@ hipError_t launch_error_sums(int fmt, int rotate, int gemm_layout, const void* x
                              int64_t ldx, const uint8_t* codes, const uint8_t* scales,
                              const float* gs, int64_t rows, int64_t cols, double* sums,
                              double* partials, hipStream_t st) {
-  const int G = fmt == FP4_FMT_MXFP4 ? 32 : 16;
+  const int G = fmt_block(fmt);
   const uint32_t nb = (uint32_t)(cols / G);
   const int64_t kchunks = mx_gemm_kchunks(cols);
   const int grid = error_partials(rows, cols, fmt);
@@ -272,8 +292,12 @@ hipError_t launch_error_sums(int fmt, int rotate, int gemm_layout, const void* x
   } while (0)
   if (fmt == FP4_FMT_MXFP4) {
     if (rotate) FP4_ER_X(FP4_FMT_MXFP4, true); else FP4_ER_X(FP4_FMT_MXFP4, false);
-  } else {
+  } else if (fmt == FP4_FMT_NVFP4) {
     if (rotate) FP4_ER_X(FP4_FMT_NVFP4, true); else FP4_ER_X(FP4_FMT_NVFP4, false);
+  } else if (fmt == FP4_FMT_MXINT4) {
+    if (rotate) FP4_ER_X(FP4_FMT_MXINT4, true); else FP4_ER_X(FP4_FMT_MXINT4, false);
+  } else {
+    if (rotate) FP4_ER_X(FP4_FMT_NVINT4, true); else FP4_ER_X(FP4_FMT_NVINT4, false);
   }
 #undef FP4_ER_X
 #undef FP4_ER

@@ -19,6 +19,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+// Formats: E8M0 block scales (MX) or E4M3 block scales with an fp32 tensor
+// scale (NV); E2M1 or INT4 element.
+__host__ __device__ constexpr bool fmt_mx(int f) { return f == 0 || f == 2; }
+__host__ __device__ constexpr bool fmt_int(int f) { return f == 2 || f == 3; }
+__host__ __device__ constexpr int fmt_block(int f) { return fmt_mx(f) ? 32 : 16; }
+// Largest element magnitude: 6 (E2M1) or 7 (INT4).
+__host__ __device__ constexpr float fmt_qmax(int f) { return fmt_int(f) ? 7.0f : 6.0f; }
+
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 
@@ -67,6 +75,31 @@ __device__ __forceinline__ uint32_t enc8_bf16(const uint32_t* w, float scale) {
 // field, as above).  Exact.
 __device__ __forceinline__ f32x2 dec2_f32(uint32_t byte_src, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte_src, scale, 0);
+}
+
+// 2^(code - 127) as an fp32 value (code 0: the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t code) {
+  return code == 0u ? as_f(0x00400000u) : as_f(code << 23);
+}
+
+// ---------------------------------------------------------------- INT4
+// Nearest integer (ties to even) of q clipped to [-7, 7], as a nibble.
+__device__ __forceinline__ uint32_t int4_nibble(float q) {
+  const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(q), -7.0f, 7.0f);
+  return (uint32_t)(int)r & 15u;
+}
+
+// Eight quotients -> one dword of INT4 codes (element 0 in the low nibble).
+__device__ __forceinline__ uint32_t int4_pack8(const float* q) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r |= int4_nibble(q[i]) << (4 * i);
+  return r;
+}
+
+// INT4 code i of a dword (sign-extended) as fp32.
+__device__ __forceinline__ float int4_value(uint32_t w, int i) {
+  return (float)((int32_t)(w << (28 - 4 * i)) >> 28);
 }
 
 // ------------------------------------------------------------------ E4M3

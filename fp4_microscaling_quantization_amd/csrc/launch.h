@@ -8,14 +8,14 @@
 
 namespace fp4lib {
 
-hipError_t launch_quantize_mx(const void* x, int xdt, int rotate, int rule, int64_t rows,
+hipError_t launch_quantize_mx(int fmt, const void* x, int xdt, int rotate, int rule, int64_t rows,
                               int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales,
                               int gemm_layout, hipStream_t st);
 int amax_partials(int64_t rows, int64_t cols, int rotate, int xdt);
 hipError_t launch_amax_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
                           int64_t ldx, float* partials, int npart, hipStream_t st);
-hipError_t launch_amax_final(const float* partials, int npart, float* gs, hipStream_t st);
-hipError_t launch_quantize_nv(const void* x, int xdt, int rotate, int rule, int64_t rows,
+hipError_t launch_amax_final(int fmt, const float* partials, int npart, float* gs, hipStream_t st);
+hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int rule, int64_t rows,
                               int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
                               const float* partials, int npart, hipStream_t st);
 hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,

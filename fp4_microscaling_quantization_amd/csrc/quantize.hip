@@ -75,10 +75,6 @@ __device__ __forceinline__ float sse8(const float* v, uint32_t w, float p, float
   return acc;
 }
 
-// 2^(code - 127) as an fp32 value (code 0: the subnormal 2^-127).
-__device__ __forceinline__ float e8m0_value(uint32_t code) {
-  return code == 0u ? as_f(0x00400000u) : as_f(code << 23);
-}
 
 __device__ __forceinline__ u32x4 mx_enc32(const float* v, uint32_t code) {
   const float sc = e8m0_as_cvt_scale(code);
@@ -135,6 +131,27 @@ __device__ __forceinline__ uint32_t mx_block_bf16(const uint32_t* w, u32x4& out)
   out[1] = enc8_bf16(&w[4], sc);
   out[2] = enc8_bf16(&w[8], sc);
   out[3] = enc8_bf16(&w[12], sc);
+  return code;
+}
+
+// MXINT4 block from 32 fp32 values (rotated in place when ROT): the MXFP4
+// E8M0 code, elements round(y / 2^e) clipped to +-7 ("Bridging the Gap ...",
+// MXINT4).  y * 2^-e is the correctly rounded quotient (a power-of-two factor).
+template <bool ROT>
+__device__ __forceinline__ uint32_t mxint_block_f32(float* v, u32x4& out) {
+  if constexpr (ROT) {
+    fwht<32>(v);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = div_sqrt32(v[i]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t code = (uint32_t)max((int)((as_u(amax) >> 23) & 0xFFu) - 2, 0);
+  const float inv = e8m0_value(254u - code);  // 2^-(code - 127)
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] *= inv;
+  out = u32x4{int4_pack8(&v[0]), int4_pack8(&v[8]), int4_pack8(&v[16]), int4_pack8(&v[24])};
   return code;
 }
 
@@ -273,6 +290,40 @@ __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out
   return code;
 }
 
+// NVINT4 block from 16 fp32 values (rotated in place when ROT): E4M3 code of
+// (amax / 7) / ts, elements round(fl32(y / s)) clipped to +-7.
+template <bool ROT>
+__device__ __forceinline__ uint32_t nvint_block(float* v, const NvTs& T, u32x2& out) {
+  if constexpr (ROT) {
+    fwht<16>(v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  uint32_t code = 0;
+  float s = 0.0f;
+  if (T.live) {
+    code = nv_code_of(amax / 7.0f, T);
+    s = e4m3_value(code) * T.ts;
+  }
+  if (s == 0.0f) {
+    out = u32x2{0u, 0u};
+    return code;
+  }
+  if (s >= 0x1p-100f) {
+    const float rs = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = div_rn(v[i], s, rs);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = v[i] / s;
+  }
+  out = u32x2{int4_pack8(&v[0]), int4_pack8(&v[8])};
+  return code;
+}
+
 // Unpack a block held as raw 16-byte chunks into fp32.
 template <int XDT, int G>
 __device__ __forceinline__ void unpack(const u32x4* c, float* v) {
@@ -303,7 +354,18 @@ __device__ __forceinline__ void store_mx_scale(uint8_t* __restrict__ scales, int
 // the first two for NVFP4), scale code returned.
 template <int FMT, int XDT, bool ROT, int RULE>
 __device__ __forceinline__ uint32_t compute_block(const u32x4* c, const NvTs& T, u32x4& out) {
-  if constexpr (FMT == FP4_FMT_MXFP4) {
+  if constexpr (FMT == FP4_FMT_MXINT4) {
+    float v[32];
+    unpack<XDT, 32>(c, v);
+    return mxint_block_f32<ROT>(v, out);
+  } else if constexpr (FMT == FP4_FMT_NVINT4) {
+    float v[16];
+    unpack<XDT, 16>(c, v);
+    u32x2 o;
+    const uint32_t code = nvint_block<ROT>(v, T, o);
+    out = u32x4{o[0], o[1], 0u, 0u};
+    return code;
+  } else if constexpr (FMT == FP4_FMT_MXFP4) {
     if constexpr (XDT == FP4_DT_BF16 && !ROT && RULE == FP4_SCALE_ABSMAX) {
       uint32_t w[16];
 #pragma unroll
@@ -332,7 +394,7 @@ __device__ __forceinline__ void store_block(const u32x4& out, uint32_t code, int
                                             int64_t nb, uint8_t* __restrict__ codes,
                                             uint8_t* __restrict__ scales, int64_t kchunks,
                                             int gemm_layout) {
-  if constexpr (FMT == FP4_FMT_MXFP4) {
+  if constexpr (fmt_mx(FMT)) {
     *reinterpret_cast<u32x4*>(codes + r * (nb * 16) + kb * 16) = out;
     store_mx_scale(scales, r, kb, nb, kchunks, gemm_layout, code);
   } else {
@@ -368,13 +430,16 @@ __device__ __forceinline__ float wg_max(float m) {
 
 // NVFP4 tensor scale for this launch: either given (*gs), or reduced from the
 // amax pass's partial maxima (workgroup 0 then publishes it to *gs).
+// The tensor scale maps the tensor maximum onto 448 * qmax: 2688 for the E2M1
+// element, 3136 for INT4.
+template <int FMT>
 __device__ __forceinline__ NvTs nv_launch_ts(float* __restrict__ gs,
                                              const float* __restrict__ partials, int npart) {
   if (npart <= 0) return make_ts(*gs);
   float m = 0.0f;
   for (int i = threadIdx.x; i < npart; i += kThreads) m = fmaxf(m, partials[i]);
   m = wg_max(m);
-  const float ts = m / 2688.0f;
+  const float ts = m / (448.0f * fmt_qmax(FMT));
   if (blockIdx.x == 0 && threadIdx.x == 0) *gs = ts;
   return make_ts(ts);
 }
@@ -387,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
     float* __restrict__ gs, const float* __restrict__ partials, int npart) {
-  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
+  constexpr int G = fmt_block(FMT);
   constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
   constexpr int BB = G * ES;       // bytes per block
   constexpr int CH = BB / 16;      // 16-byte chunks per block
@@ -395,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][64 * STRIDE];
 
   NvTs T{};
-  if constexpr (FMT == FP4_FMT_NVFP4) T = nv_launch_ts(gs, partials, npart);
+  if constexpr (!fmt_mx(FMT)) T = nv_launch_ts<FMT>(gs, partials, npart);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t groups = nb / 64;
@@ -481,6 +546,7 @@ __device__ __forceinline__ NvTsLoads nv_ts_issue(const float* __restrict__ gs,
   return L;
 }
 
+template <int FMT>
 __device__ __forceinline__ NvTs nv_ts_finish(const NvTsLoads& L, float* __restrict__ gs, int npart,
                                              bool publish) {
   if (npart <= 0) return make_ts(L.p[0]);
@@ -489,7 +555,7 @@ __device__ __forceinline__ NvTs nv_ts_finish(const NvTsLoads& L, float* __restri
   for (int k = 0; k < kAmaxGrid / 64; ++k) m = fmaxf(m, L.p[k]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  const float ts = m / 2688.0f;
+  const float ts = m / (448.0f * fmt_qmax(FMT));
   if (publish && (threadIdx.x & 63) == 0) *gs = ts;
   return make_ts(ts);
 }
@@ -504,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t wpr,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
     float* __restrict__ gs, const float* __restrict__ partials, int npart) {
-  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
+  constexpr int G = fmt_block(FMT);
   constexpr int BB = G * 2;        // bytes per block
   constexpr int CH = BB / 16;      // 16-byte chunks per block
   constexpr int STRIDE = BB + 16;  // padded LDS stride
@@ -530,10 +596,10 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     }
   };
   NvTsLoads tsl{};
-  if constexpr (FMT == FP4_FMT_NVFP4) tsl = nv_ts_issue(gs, partials, npart);
+  if constexpr (!fmt_mx(FMT)) tsl = nv_ts_issue(gs, partials, npart);
   load(t0);
   NvTs T{};
-  if constexpr (FMT == FP4_FMT_NVFP4) T = nv_ts_finish(tsl, gs, npart, blockIdx.x == 0 && wave == 0);
+  if constexpr (!fmt_mx(FMT)) T = nv_ts_finish<FMT>(tsl, gs, npart, blockIdx.x == 0 && wave == 0);
   for (;;) {
     // all tiles computed before any store, so no store sits between a tile
     // load and the wait for it
@@ -574,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 // 8w .. 8w + 7 of the tile; load j brings rows 2j, 2j + 1 (512 bytes each);
 // after the LDS transpose lane l holds block l % 8 of row l / 8, and the
 // codes of each row (8 blocks) are 128 contiguous bytes.
-template <bool ROT, int RULE>
+template <int FMT, bool ROT, int RULE>
 __global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
     const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t kcs,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks) {
@@ -608,8 +674,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
     wave_lds_sync();
     const uint32_t r = r0 + (lane >> 3), kb = kc * 8 + (lane & 7);
     if (r < rows && kb < nb)
-      quantize_block<FP4_FMT_MXFP4, FP4_DT_BF16, ROT, RULE>(c, NvTs{}, r, kb, nb, codes, scales,
-                                                           kchunks, 1);
+      quantize_block<FMT, FP4_DT_BF16, ROT, RULE>(c, NvTs{}, r, kb, nb, codes, scales, kchunks, 1);
   }
 }
 
@@ -677,11 +742,11 @@ __global__ __launch_bounds__(kThreads) void quant_direct_kernel(
     const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
     float* __restrict__ gs, const float* __restrict__ partials, int npart) {
-  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
+  constexpr int G = fmt_block(FMT);
   constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
   constexpr int CH = G * ES / 16;
   NvTs T{};
-  if constexpr (FMT == FP4_FMT_NVFP4) T = nv_launch_ts(gs, partials, npart);
+  if constexpr (!fmt_mx(FMT)) T = nv_launch_ts<FMT>(gs, partials, npart);
   const uint32_t total = rows * nb;
   for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
     const uint32_t r = b / nb;
@@ -766,13 +831,15 @@ __global__ __launch_bounds__(kThreads) void amax_rot_kernel(const void* __restri
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// Reduce the partial maxima into ts = amax / 2688 (one workgroup).
+// Reduce the partial maxima into ts = amax / tdiv (one workgroup; tdiv =
+// 448 * qmax of the element).
 __global__ __launch_bounds__(kThreads) void amax_final_kernel(const float* __restrict__ partials,
-                                                              int npart, float* __restrict__ gs) {
+                                                              int npart, float* __restrict__ gs,
+                                                              float tdiv) {
   float m = 0.0f;
   for (int i = threadIdx.x; i < npart; i += kThreads) m = fmaxf(m, partials[i]);
   m = wg_max(m);
-  if (threadIdx.x == 0) *gs = m / 2688.0f;
+  if (threadIdx.x == 0) *gs = m / tdiv;
 }
 
 __global__ void set_scalar_kernel(float* p, float v) { *p = v; }
@@ -804,22 +871,22 @@ template <int FMT, int XDT, bool ROT, int RULE>
 hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
                     uint8_t* scales, int gemm_layout, float* gs, const float* partials, int npart,
                     hipStream_t st) {
-  constexpr int G = FMT == FP4_FMT_MXFP4 ? 32 : 16;
+  constexpr int G = fmt_block(FMT);
   const uint32_t nb = (uint32_t)(cols / G);
   const int64_t kchunks = mx_gemm_kchunks(cols);
   if constexpr (XDT == FP4_DT_BF16) {
     const uint8_t* xb = static_cast<const uint8_t*>(x);
-    if constexpr (FMT == FP4_FMT_MXFP4) {
+    if constexpr (fmt_mx(FMT)) {
       if (gemm_layout) {
         const uint32_t kcs = (nb + 7) / 8;
         int64_t g = ((rows + 31) / 32) * (int64_t)kcs;
         if (g > 16384) g = 16384;
-        quant_mx_gemm_kernel<ROT, RULE><<<(int)g, kThreads, 0, st>>>(
+        quant_mx_gemm_kernel<FMT, ROT, RULE><<<(int)g, kThreads, 0, st>>>(
             xb, ldx * 2, (uint32_t)rows, nb, kcs, codes, scales, kchunks);
         return hipGetLastError();
       }
     }
-    constexpr int TPW = FMT == FP4_FMT_MXFP4 ? 1 : 2;
+    constexpr int TPW = fmt_mx(FMT) ? 1 : 2;
     const uint32_t wpr = (nb + 63) / 64;
     const int64_t waves = (rows * (int64_t)wpr + TPW - 1) / TPW;
     int64_t g = (waves + kThreads / 64 - 1) / (kThreads / 64);
@@ -872,9 +939,11 @@ hipError_t launch_q_rule(const void* x, int xdt, int rotate, int64_t rows, int64
   return launch_q<FMT, FP4_DT_F32, false, RULE>(x, rows, cols, ldx, codes, scales, gemm_layout, gs, partials, npart, st);
 }
 
-hipError_t launch_quantize_mx(const void* x, int xdt, int rotate, int rule, int64_t rows,
+hipError_t launch_quantize_mx(int fmt, const void* x, int xdt, int rotate, int rule, int64_t rows,
                               int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales,
                               int gemm_layout, hipStream_t st) {
+  if (fmt == FP4_FMT_MXINT4)
+    return launch_q_rule<FP4_FMT_MXINT4, FP4_SCALE_ABSMAX>(x, xdt, rotate, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
   if (rule == FP4_SCALE_MSE)
     return launch_q_rule<FP4_FMT_MXFP4, FP4_SCALE_MSE>(x, xdt, rotate, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
   return launch_q_rule<FP4_FMT_MXFP4, FP4_SCALE_ABSMAX>(x, xdt, rotate, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
@@ -908,18 +977,20 @@ hipError_t launch_amax_nv(const void* x, int xdt, int rotate, int64_t rows, int6
   return hipGetLastError();
 }
 
-hipError_t launch_amax_final(const float* partials, int npart, float* gs, hipStream_t st) {
+hipError_t launch_amax_final(int fmt, const float* partials, int npart, float* gs, hipStream_t st) {
   if (npart <= 0) {
     set_scalar_kernel<<<1, 1, 0, st>>>(gs, 0.0f);
   } else {
-    amax_final_kernel<<<1, kThreads, 0, st>>>(partials, npart, gs);
+    amax_final_kernel<<<1, kThreads, 0, st>>>(partials, npart, gs, 448.0f * fmt_qmax(fmt));
   }
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_nv(const void* x, int xdt, int rotate, int rule, int64_t rows,
+hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int rule, int64_t rows,
                               int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
                               const float* partials, int npart, hipStream_t st) {
+  if (fmt == FP4_FMT_NVINT4)
+    return launch_q_rule<FP4_FMT_NVINT4, FP4_SCALE_ABSMAX>(x, xdt, rotate, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
   if (rule == FP4_SCALE_MSE)
     return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_MSE>(x, xdt, rotate, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
   if (rule == FP4_SCALE_FOUR_OVER_SIX)

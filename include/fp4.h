@@ -63,7 +63,18 @@ typedef enum {
     FP4_ERR_HIP = -5            /* a HIP launch failed */
 } fp4_status;
 
-typedef enum { FP4_FMT_MXFP4 = 0, FP4_FMT_NVFP4 = 1 } fp4_format;
+/* MXINT4 / NVINT4 ("Bridging the Gap ...", MXINT4 and NVINT4): the MXFP4 /
+ * NVFP4 layouts with a 4-bit two's-complement integer element used
+ * symmetrically (values -7 .. 7, nearest integer with ties to even, saturating;
+ * the pattern 0x8 is never written).  MXINT4 keeps the E8M0 rule
+ * floor(log2 amax) - 2; NVINT4 uses ts = amax / (7 * 448) and maps each block
+ * maximum onto 7.  Only FP4_SCALE_ABSMAX applies to them. */
+typedef enum {
+    FP4_FMT_MXFP4 = 0,
+    FP4_FMT_NVFP4 = 1,
+    FP4_FMT_MXINT4 = 2,
+    FP4_FMT_NVINT4 = 3
+} fp4_format;
 typedef enum {
     FP4_SCALE_ABSMAX = 0,       /* the block maximum sets the scale */
     FP4_SCALE_MSE = 1,          /* smallest block squared error in a window */

@@ -44,7 +44,7 @@ def rowmajor_scales_np(q: fp4.Quantized) -> np.ndarray:
     raw = q.scales.cpu().numpy()
     G = q.cfg.block
     nb = q.cols // G
-    if q.cfg.scale_layout == fp4.SCALES_ROWMAJOR or q.cfg.fmt == fp4.FMT_NVFP4:
+    if q.cfg.scale_layout == fp4.SCALES_ROWMAJOR or q.cfg.fmt not in fp4.MX_FORMATS:
         return raw[: q.rows * nb].reshape(q.rows, nb)
     idx = gemm_offsets(q.rows, q.cols)
     return raw[idx]
@@ -157,3 +157,28 @@ def assert_search_close(got_codes, got_scales, ref_codes, ref_scales, fmt, ts, y
     assert rate <= elem_budget, (what, rate)
     if diff.any():
         assert np.all(np.abs(grid_index(gv[diff]) - grid_index(rv[diff])) <= 1), what
+
+
+def int4_values(codes: np.ndarray) -> np.ndarray:
+    """[rows, cols] integer values of packed two's-complement nibbles."""
+    c = np.stack([codes & 15, codes >> 4], -1).reshape(codes.shape[0], -1).astype(np.int64)
+    return np.where(c >= 8, c - 16, c)
+
+
+def assert_rotated_int4_close(got_codes, ref_codes, got_scales, ref_scales, budget=1e-4, what=""):
+    """Rotated INT4 paths: element values may differ in at most `budget` of
+    the elements, by one integer step, where the block scales agree; scale
+    codes in at most `budget` of the blocks, by one step."""
+    gv, rv = int4_values(got_codes), int4_values(ref_codes)
+    G = gv.shape[1] // got_scales.shape[1]
+    same = np.repeat(got_scales == ref_scales, G, axis=1)
+    diff = gv != rv
+    rate = diff.sum() / gv.size
+    say("  %s element mismatches: %d of %d (%.2e)" % (what, diff.sum(), gv.size, rate))
+    assert rate <= budget, (what, rate)
+    assert np.all(np.abs(gv - rv)[diff & same] <= 1), (what, "non-adjacent mismatch")
+    sd = got_scales != ref_scales
+    say("  %s scale mismatches: %d of %d" % (what, sd.sum(), sd.size))
+    assert sd.mean() <= budget, what
+    if sd.any():
+        assert np.all(np.abs(got_scales[sd].astype(int) - ref_scales[sd].astype(int)) == 1)

@@ -102,6 +102,16 @@ def test_quantize_rejects_bad_arguments_on_host():
     assert _q(bad) == E.FP4_ERR_UNSUPPORTED                  # Four Over Six is NVFP4's
     bad = fp4.QConfig(fp4.FMT_NVFP4, 16, 0, 3, 0)
     assert _q(bad) == E.FP4_ERR_INVALID_ARG                  # no such rule
+    # INT4-element formats: the MX / NV layouts, absmax scales only
+    mxi = fp4.qconfig(fp4.FMT_MXINT4, scale_layout=fp4.SCALES_GEMM)
+    nvi = fp4.qconfig(fp4.FMT_NVINT4)
+    assert fp4.fp4_scales_bytes(mxi, 64, 256) == 2 * 256
+    assert fp4.fp4_workspace_bytes(nvi, 64, 256) == 2048 and fp4.fp4_workspace_bytes(mxi, 64, 256) == 0
+    assert _q(fp4.QConfig(fp4.FMT_MXINT4, 16, 0, 0, 0)) == E.FP4_ERR_INVALID_ARG
+    assert _q(fp4.QConfig(fp4.FMT_NVINT4, 16, 0, fp4.SCALE_MSE, 0)) == E.FP4_ERR_UNSUPPORTED
+    assert _q(nvi, gs=None) == E.FP4_ERR_INVALID_ARG
+    assert _q(fp4.QConfig(4, 16, 0, 0, 0)) == E.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_global_scale(mxi, FAKE, fp4.DT_BF16, 64, 256, 256, FAKE, FAKE, 2048, None) == E.FP4_ERR_INVALID_ARG
     bad = fp4.QConfig(3, 32, 0, 0, 0)
     assert _q(bad) == E.FP4_ERR_INVALID_ARG
     bad = fp4.QConfig(fp4.FMT_MXFP4, 32, 0, 0, 9)
@@ -141,7 +151,7 @@ def test_gemm_rejects_bad_arguments_on_host():
     E = fp4
     assert _g(K=96) == E.FP4_ERR_UNSUPPORTED                 # K must be a multiple of 128
     assert _g(M=-1) == E.FP4_ERR_INVALID_ARG
-    assert _g(fmt=2) == E.FP4_ERR_INVALID_ARG
+    assert _g(fmt=7) == E.FP4_ERR_INVALID_ARG
     assert _g(ldy=32) == E.FP4_ERR_INVALID_ARG
     assert _g(ydt=9) == E.FP4_ERR_INVALID_ARG
     assert _g(a=MIS) == E.FP4_ERR_ALIGNMENT
@@ -167,7 +177,7 @@ def _w(**kw):
 def test_gemm_w4a16_rejects_bad_arguments_on_host():
     E = fp4
     assert _w(K=128) == E.FP4_ERR_UNSUPPORTED                # K must be a multiple of 256
-    assert _w(fmt=2) == E.FP4_ERR_INVALID_ARG
+    assert _w(fmt=7) == E.FP4_ERR_INVALID_ARG
     assert _w(M=-1) == E.FP4_ERR_INVALID_ARG
     assert _w(ldy=32) == E.FP4_ERR_INVALID_ARG
     assert _w(lda=256) == E.FP4_ERR_INVALID_ARG              # lda < K

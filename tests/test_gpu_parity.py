@@ -16,13 +16,16 @@ torch = pytest.importorskip("torch")
 import fp4_microscaling_quantization_amd as fp4
 import oracle
 import workloads
-from gpu_common import (assert_rotated_codes_close, assert_search_close, codes_np, gemm_tolerance_ok,
-                        rowmajor_scales_np, say, to_dev_bf16, to_dev_f32, to_dev_u8)
+from gpu_common import (assert_rotated_codes_close, assert_rotated_int4_close, assert_search_close,
+                        codes_np, gemm_tolerance_ok, rowmajor_scales_np, say, to_dev_bf16, to_dev_f32,
+                        to_dev_u8)
 
 pytestmark = pytest.mark.gpu
 
 FMTS = [fp4.FMT_MXFP4, fp4.FMT_NVFP4]
-FNAME = {fp4.FMT_MXFP4: "mxfp4", fp4.FMT_NVFP4: "nvfp4"}
+FNAME = {fp4.FMT_MXFP4: "mxfp4", fp4.FMT_NVFP4: "nvfp4", fp4.FMT_MXINT4: "mxint4",
+         fp4.FMT_NVINT4: "nvint4"}
+INT4 = [fp4.FMT_MXINT4, fp4.FMT_NVINT4]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -113,6 +116,75 @@ def test_quantize_rotated(case, fmt):
         g = np.float32(q.global_scale.item())
         assert abs(int(g.view(np.int32)) - int(np.float32(rts).view(np.int32))) <= 1, (g, rts)
     assert_rotated_codes_close(codes_np(q), rc, rowmajor_scales_np(q), rs, what=case)
+
+
+@pytest.mark.parametrize("case", NONROT_CASES)
+@pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
+def test_quantize_int4_bit_exact(case, fmt):
+    """MXINT4 / NVINT4, non-rotated: codes, scale codes and the tensor scale bit
+    for bit, in every scale layout."""
+    say("quantize int4", case, FNAME[fmt])
+    xh, xd = _inputs(case)
+    rc, rs, rts = oracle.quantize(xh, fmt)
+    lays = [fp4.SCALES_GEMM, fp4.SCALES_ROWMAJOR] if fmt == fp4.FMT_MXINT4 else [fp4.SCALES_ROWMAJOR]
+    for lay in lays:
+        q = _prefill(fp4.quantize(xd, fmt, scale_layout=lay))
+        q = fp4.quantize(xd, fmt, scale_layout=lay, out=q)
+        torch.cuda.synchronize()
+        gc, gs = codes_np(q), rowmajor_scales_np(q)
+        assert np.array_equal(gs, rs), (case, lay)
+        bad = np.nonzero(gc != rc)
+        assert bad[0].size == 0, (case, lay, bad[0][:4], bad[1][:4], gc[bad][:4], rc[bad][:4])
+        if fmt == fp4.FMT_NVINT4:
+            assert q.global_scale.item() == float(rts)
+
+
+@pytest.mark.parametrize("case", ["cfg2_laplace", "ragged"])
+@pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
+def test_quantize_int4_rotated(case, fmt):
+    say("quantize int4 rotated", case, FNAME[fmt])
+    xh, xd = _inputs(case)
+    rc, rs, rts = oracle.quantize(xh, fmt, rotate=True)
+    lay = fp4.SCALES_GEMM if fmt == fp4.FMT_MXINT4 else fp4.SCALES_ROWMAJOR
+    q = fp4.quantize(xd, fmt, rotate=True, scale_layout=lay)
+    torch.cuda.synchronize()
+    if fmt == fp4.FMT_NVINT4:
+        g = np.float32(q.global_scale.item())
+        assert abs(int(g.view(np.int32)) - int(np.float32(rts).view(np.int32))) <= 1, (g, rts)
+    assert_rotated_int4_close(codes_np(q), rc, rowmajor_scales_np(q), rs, what=case)
+
+
+@pytest.mark.parametrize("case", ["cfg1", "cfg2_laplace", "ragged"])
+@pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
+@pytest.mark.parametrize("rot", [False, True], ids=["plain", "rot"])
+def test_int4_dequantize_and_error_sums(case, fmt, rot):
+    """Dequantized INT4 values (of the GPU's own codes) exactly as the oracle
+    decodes them; error sums against the oracle's on the same values."""
+    say("int4 dequantize", case, FNAME[fmt], rot)
+    xh, xd = _inputs(case)
+    lay = fp4.SCALES_GEMM if fmt == fp4.FMT_MXINT4 else fp4.SCALES_ROWMAJOR
+    q = fp4.quantize(xd, fmt, rotate=rot, scale_layout=lay)
+    torch.cuda.synchronize()
+    gc, gs = codes_np(q), rowmajor_scales_np(q)
+    ts = np.float32(q.global_scale.item()) if fmt == fp4.FMT_NVINT4 else np.float32(0)
+    ref = oracle.dequantize(gc, gs, fmt, ts)
+    y = fp4.dequantize(q).cpu().numpy()
+    assert np.array_equal(y, ref)
+    yb = fp4.dequantize(q, dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.array_equal(yb, workloads.bf16_bits_to_f32(workloads.to_bf16_bits(ref)))
+    ref_o = oracle.dequantize(gc, gs, fmt, ts, inverse_rotate=rot)
+    yo = fp4.dequantize(q, inverse_rotate=rot).cpu().numpy()
+    G = fp4.BLOCK[fmt]
+    if rot:
+        blk = np.abs(ref).reshape(ref.shape[0], -1, G).sum(-1)
+        atol = np.repeat(blk, G, axis=1) * 5 * 2.0 ** -24
+        assert np.all(np.abs(yo - ref_o) <= atol)
+    else:
+        assert np.array_equal(yo, ref_o)
+    sums = fp4.error_sums(xd, q).cpu().numpy()
+    ref_sums = oracle.error_sums(xh, ref_o)
+    np.testing.assert_allclose(sums, ref_sums, rtol=1e-9 if not rot else 1e-5)
+    say("  nmse %.6e" % (sums[0] / sums[1]))
 
 
 RULES = [(fp4.FMT_MXFP4, fp4.SCALE_MSE), (fp4.FMT_NVFP4, fp4.SCALE_MSE),
