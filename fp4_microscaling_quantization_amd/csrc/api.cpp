@@ -217,7 +217,8 @@ int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor, i
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return 0;
   if (fmt == FP4_FMT_MXFP4) return fp4lib::gemm_mx_workspace(M, N, K);
-  if (fmt == FP4_FMT_NVFP4) return fp4lib::gemm_nv_workspace(M, N, K);
+  if (fmt == FP4_FMT_NVFP4 || fmt == FP4_FMT_MXINT4 || fmt == FP4_FMT_NVINT4)
+    return fp4lib::gemm_nv_workspace(M, N, K);
   return 0;
 }
 
@@ -225,10 +226,10 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_code
              const uint8_t* a_scales, const float* a_gs, const uint8_t* b_codes,
              const uint8_t* b_scales, const float* b_gs, void* y, int32_t ydt, int64_t ldy,
              void* ws, size_t ws_bytes, void* stream) {
-  if (fmt == FP4_FMT_MXINT4 || fmt == FP4_FMT_NVINT4) return FP4_ERR_UNSUPPORTED;
-  if (fmt != FP4_FMT_MXFP4 && fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
+  if (fmt < FP4_FMT_MXFP4 || fmt > FP4_FMT_NVINT4) return FP4_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID_ARG;
   if (K % 128 != 0) return FP4_ERR_UNSUPPORTED;
+  if (fp4k::fmt_int(fmt) && K % 256 != 0) return FP4_ERR_UNSUPPORTED;
   if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
     return FP4_ERR_UNSUPPORTED;
   if (dtype_bytes(ydt) == 0) return FP4_ERR_INVALID_ARG;
@@ -245,13 +246,19 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_code
   if (fmt == FP4_FMT_MXFP4)
     return hip_status(fp4lib::launch_gemm_mx(M, N, K, a_codes, a_scales, b_codes, b_scales, y, ydt,
                                              ldy, ws, ws_bytes, st));
+  if (fmt == FP4_FMT_MXINT4)
+    return hip_status(fp4lib::launch_gemm_int4(fmt, M, N, K, a_codes, a_scales, nullptr, b_codes,
+                                               b_scales, nullptr, y, ydt, ldy, ws, ws_bytes, st));
   if (!a_gs || !b_gs) return FP4_ERR_INVALID_ARG;
+  if (fmt == FP4_FMT_NVINT4)
+    return hip_status(fp4lib::launch_gemm_int4(fmt, M, N, K, a_codes, a_scales, a_gs, b_codes,
+                                               b_scales, b_gs, y, ydt, ldy, ws, ws_bytes, st));
   return hip_status(fp4lib::launch_gemm_nv(M, N, K, a_codes, a_scales, a_gs, b_codes, b_scales,
                                            b_gs, y, ydt, ldy, ws, ws_bytes, st));
 }
 
 size_t fp4_gemm_w4a16_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
-  if (fmt != FP4_FMT_MXFP4 && fmt != FP4_FMT_NVFP4) return 0;
+  if (fmt < FP4_FMT_MXFP4 || fmt > FP4_FMT_NVINT4) return 0;
   if (M < 0 || N < 0 || K < 0 || K % 256 != 0) return 0;
   return fp4lib::gemm_w4a16_workspace(M, N, K);
 }
@@ -259,8 +266,7 @@ size_t fp4_gemm_w4a16_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t
 int fp4_gemm_w4a16(int32_t fmt, int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gs, void* y,
                    int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
-  if (fmt == FP4_FMT_MXINT4 || fmt == FP4_FMT_NVINT4) return FP4_ERR_UNSUPPORTED;
-  if (fmt != FP4_FMT_MXFP4 && fmt != FP4_FMT_NVFP4) return FP4_ERR_INVALID_ARG;
+  if (fmt < FP4_FMT_MXFP4 || fmt > FP4_FMT_NVINT4) return FP4_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID_ARG;
   if (K % 256 != 0) return FP4_ERR_UNSUPPORTED;
   if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
@@ -274,7 +280,7 @@ int fp4_gemm_w4a16(int32_t fmt, int64_t M, int64_t N, int64_t K, const void* a, 
     if (lda < K) return FP4_ERR_INVALID_ARG;
     if (!aligned16(a) || (M > 1 && (lda * 2) % 16 != 0)) return FP4_ERR_ALIGNMENT;
     if (!aligned16(b_codes) || !aligned16(b_scales)) return FP4_ERR_ALIGNMENT;
-    if (fmt == FP4_FMT_NVFP4 && !b_gs) return FP4_ERR_INVALID_ARG;
+    if (!fp4k::fmt_mx(fmt) && !b_gs) return FP4_ERR_INVALID_ARG;
   }
   if (ws && !aligned16(ws)) return FP4_ERR_ALIGNMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -336,13 +336,18 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
 // 32) as in the MXFP4 kernel and feeds dword t of them to MFMA t of the step,
 // for A rows and B columns alike.  The fp32 tensor scales multiply the
 // accumulators in the epilogue.
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, int FMT = FP4_FMT_NVFP4>
 struct NvCfg {
+  // MX: E8M0 scales in the GEMM layout (one 256-byte tile per 32 rows per
+  // 256 K, re-loaded with each stage of the pair); NV: each row's 16 E4M3
+  // scales of the 256-K chunk.
+  static constexpr bool MX = fmt_mx(FMT);
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int B_CODES = BM * 64;
   static constexpr int A_SC = B_CODES + BN * 64;
-  static constexpr int B_SC = A_SC + BM * 16;
-  static constexpr int USED = B_SC + BN * 16;
+  static constexpr int B_SC = A_SC + (MX ? BM * 8 : BM * 16);
+  static constexpr int USED = B_SC + (MX ? BN * 8 : BN * 16);
+  static constexpr int SC_ADV = MX ? 256 : 16;  // scale bytes per 256-K chunk and source
   static constexpr int NW = (BM / WM) * (BN / WN);
   static constexpr int RB = NW * 1024;
   static constexpr int ROUNDS = (USED + RB - 1) / RB;
@@ -357,6 +362,11 @@ __device__ __forceinline__ f32x16 mfma_f16(const f16x8& a, const f16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // Eight E2M1 codes (one dword, low nibble first) times an fp16 scale.
 __device__ __forceinline__ f16x8 expand8(uint32_t w, _Float16 s) {
   const f16x2 s2 = {s, s};
@@ -367,24 +377,54 @@ __device__ __forceinline__ f16x8 expand8(uint32_t w, _Float16 s) {
   return f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
+// Eight INT4 codes (two's complement, low nibble first) times an fp16 scale,
+// exactly: with u = n + 8 in 0 .. 15, the fp16 word 0x6400 | u is 1024 + u, so
+// (word - 1032) is n and n * s (at most 7 significant bits) is exact.  The
+// lanes come out in the order 0, 4, 1, 5, 2, 6, 3, 7: a permutation within the
+// K range of one MFMA, applied alike to both operands.
+__device__ __forceinline__ f16x8 expand8_i4_f16(uint32_t w, _Float16 s) {
+  const uint32_t t = w ^ 0x88888888u;
+  const f16x2 s2 = {s, s};
+  const f16x2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 v0 = (__builtin_bit_cast(f16x2, (t & 0x000F000Fu) | 0x64006400u) - off) * s2;
+  const f16x2 v1 = (__builtin_bit_cast(f16x2, ((t >> 4) & 0x000F000Fu) | 0x64006400u) - off) * s2;
+  const f16x2 v2 = (__builtin_bit_cast(f16x2, ((t >> 8) & 0x000F000Fu) | 0x64006400u) - off) * s2;
+  const f16x2 v3 = (__builtin_bit_cast(f16x2, ((t >> 12) & 0x000F000Fu) | 0x64006400u) - off) * s2;
+  return f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+// Eight INT4 codes times an fp32 scale p as bf16, in element order.  Exact
+// when n * p has at most 8 significant bits and lies in bf16's range (p a
+// power of two or an E4M3 value): the fp32 product's low 16 bits are zero.
+__device__ __forceinline__ u32x4 expand8_i4_bf16(uint32_t w, float p) {
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = int4_value(w, 2 * k) * p, b = int4_value(w, 2 * k + 1) * p;
+    r[k] = (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xFFFF0000u);
+  }
+  return r;
+}
+
 template <int TM, int TN>
 struct NvFrags {
   u32x4 a[TM], b[TN];
   uint32_t sa[TM], sb[TN];  // two E4M3 scale bytes per fragment (blocks of the lane's 32 codes)
 };
 
-template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
-__global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_nv_ring_kernel(
+template <int FMT, int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
+__global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT>::NW * 64)) void gemm_nv_ring_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ ags,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ bgs,
     void* __restrict__ Y, int64_t ldy, int M, int N, int K, int tiles_n, int kt_per_split,
     float* __restrict__ part) {
-  using C = NvCfg<BM, BN, WM, WN, NS>;
+  using C = NvCfg<BM, BN, WM, WN, NS, FMT>;
   constexpr int TM = C::TM, TN = C::TN, ROUNDS = C::ROUNDS;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / (BN / WN), wn = wave % (BN / WN);
+  const int64_t kchunks = K / 256;
   int tm, tn;
   tile_of((M + BM - 1) / BM, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -407,12 +447,18 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_nv_
       src[r] = B + (int64_t)min(n0 + row, N - 1) * rowbytes + chunk * 16;
       code_src[r] = true;
     } else if (p < C::B_SC) {
-      const int row = (p - C::A_SC) >> 4;
-      src[r] = As + (int64_t)min(m0 + row, M - 1) * srow;
+      const int q = p - C::A_SC;
+      if constexpr (C::MX)
+        src[r] = As + (int64_t)min((m0 >> 5) + (q >> 8), (M - 1) >> 5) * kchunks * 256 + (q & 255);
+      else
+        src[r] = As + (int64_t)min(m0 + (q >> 4), M - 1) * srow;
       code_src[r] = false;
     } else if (p < C::USED) {
-      const int row = (p - C::B_SC) >> 4;
-      src[r] = Bs + (int64_t)min(n0 + row, N - 1) * srow;
+      const int q = p - C::B_SC;
+      if constexpr (C::MX)
+        src[r] = Bs + (int64_t)min((n0 >> 5) + (q >> 8), (N - 1) >> 5) * kchunks * 256 + (q & 255);
+      else
+        src[r] = Bs + (int64_t)min(n0 + (q >> 4), N - 1) * srow;
       code_src[r] = false;
     } else {
       src[r] = As;
@@ -428,14 +474,14 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_nv_
     uint8_t* slot = slot_of(kt);
 #pragma unroll
     for (int r = 0; r < H; ++r)
-      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 16), slot + r * C::RB + wave * 1024);
+      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * C::SC_ADV), slot + r * C::RB + wave * 1024);
   };
   auto dma_tail = [&](int kt) __attribute__((always_inline)) {
     const int ks = min(kt, kt1 - 1);
     uint8_t* slot = slot_of(kt);
 #pragma unroll
     for (int r = H; r < ROUNDS; ++r)
-      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 16), slot + r * C::RB + wave * 1024);
+      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * C::SC_ADV), slot + r * C::RB + wave * 1024);
   };
 
   f32x16 acc[TM][TN];
@@ -452,20 +498,49 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_nv_
     const uint8_t* slot = slot_of(kt);
     const int q = s * 2 + (lane >> 5);
     const int sb = 8 * (kt & 1) + 4 * s + 2 * (lane >> 5);  // first block of the lane's 32 codes
+    // MX: the lane's scale dword of the tile and the byte of this step
+    const int mxo = (lane & 31) * 4 + (lane >> 5) * 128, mxb = 8 * (2 * (kt & 1) + s);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = wm * WM + i * 32 + (lane & 31);
       f.a[i] = *reinterpret_cast<const u32x4*>(slot + row * 64 + ((q ^ swz4(row)) * 16));
-      f.sa[i] = *reinterpret_cast<const uint16_t*>(slot + C::A_SC + row * 16 + sb);
+      if constexpr (C::MX)
+        f.sa[i] = (*reinterpret_cast<const uint32_t*>(slot + C::A_SC + (row >> 5) * 256 + mxo) >> mxb) & 0xFFu;
+      else
+        f.sa[i] = *reinterpret_cast<const uint16_t*>(slot + C::A_SC + row * 16 + sb);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int row = wn * WN + j * 32 + (lane & 31);
       f.b[j] = *reinterpret_cast<const u32x4*>(slot + C::B_CODES + row * 64 + ((q ^ swz4(row)) * 16));
-      f.sb[j] = *reinterpret_cast<const uint16_t*>(slot + C::B_SC + row * 16 + sb);
+      if constexpr (C::MX)
+        f.sb[j] = (*reinterpret_cast<const uint32_t*>(slot + C::B_SC + (row >> 5) * 256 + mxo) >> mxb) & 0xFFu;
+      else
+        f.sb[j] = *reinterpret_cast<const uint16_t*>(slot + C::B_SC + row * 16 + sb);
     }
   };
   auto mfmas = [&](const Frags& f) __attribute__((always_inline)) {
+    if constexpr (C::MX) {
+      // MXINT4: q * 2^e exact in bf16, bf16 MFMA
+      float pa[TM], pb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) pa[i] = e8m0_value(f.sa[i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) pb[j] = e8m0_value(f.sb[j]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4 av[TM], bv[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) av[i] = expand8_i4_bf16(f.a[i][t], pa[i]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bv[j] = expand8_i4_bf16(f.b[j][t], pb[j]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma_bf16(av[i], bv[j], acc[i][j]);
+      }
+      return;
+    }
     _Float16 sa[TM][2], sbv[TN][2];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -481,9 +556,11 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_nv_
     for (int t = 0; t < 4; ++t) {
       f16x8 av[TM], bv[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) av[i] = expand8(f.a[i][t], sa[i][t >> 1]);
+      for (int i = 0; i < TM; ++i)
+        av[i] = FMT == FP4_FMT_NVINT4 ? expand8_i4_f16(f.a[i][t], sa[i][t >> 1]) : expand8(f.a[i][t], sa[i][t >> 1]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bv[j] = expand8(f.b[j][t], sbv[j][t >> 1]);
+      for (int j = 0; j < TN; ++j)
+        bv[j] = FMT == FP4_FMT_NVINT4 ? expand8_i4_f16(f.b[j][t], sbv[j][t >> 1]) : expand8(f.b[j][t], sbv[j][t >> 1]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -523,7 +600,7 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_nv_
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   }
 
-  const float g = PARTIAL ? 1.0f : (*ags) * (*bgs);
+  const float g = (PARTIAL || C::MX) ? 1.0f : (*ags) * (*bgs);
   const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -557,7 +634,7 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_nv_
 template <int FMT, int BN, int NS>
 struct W4Cfg {
   static constexpr int WN = BN / 4, TN = WN / 32;
-  static constexpr int SC_BYTES = FMT == FP4_FMT_MXFP4 ? (BN / 32) * 256 : BN * 16;
+  static constexpr int SC_BYTES = fmt_mx(FMT) ? (BN / 32) * 256 : BN * 16;
   static constexpr int USED = BN * 64 + SC_BYTES;
   static constexpr int RB = 4096;  // four waves, 1 KB each per round
   static constexpr int ROUNDS = (USED + RB - 1) / RB;
@@ -571,10 +648,6 @@ struct W4Cfg {
   static_assert(NS >= 3 && IN_FLIGHT <= 63, "vmcnt range");
 };
 
-__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 // Eight E2M1 codes -> eight bf16 times 2^E (E8M0 scale as the operand's exponent).
 __device__ __forceinline__ u32x4 expand8_bf16_mx(uint32_t w, float scale) {
@@ -630,11 +703,11 @@ __global__ __launch_bounds__(256) void gemm_w4a16_kernel(
       kind[r] = 0;
     } else if (p < C::USED) {
       const int q = p - BN * 64;
-      if constexpr (FMT == FP4_FMT_MXFP4)
+      if constexpr (fmt_mx(FMT))
         src[r] = Bs + (int64_t)min((n0 >> 5) + (q >> 8), (N - 1) >> 5) * kchunks * 256 + (q & 255);
       else
         src[r] = Bs + (int64_t)min(n0 + (q >> 4), N - 1) * (K / 16);
-      kind[r] = FMT == FP4_FMT_MXFP4 ? 1 : 2;
+      kind[r] = fmt_mx(FMT) ? 1 : 2;
     } else {
       src[r] = Bs;
       kind[r] = 2;
@@ -676,19 +749,29 @@ __global__ __launch_bounds__(256) void gemm_w4a16_kernel(
     for (int j = 0; j < TN; ++j) {
       const int row = wave * WN + j * 32 + (lane & 31);
       const u32x4 codes = *reinterpret_cast<const u32x4*>(slot + row * 64 + ((q ^ swz4(row)) * 16));
-      if constexpr (FMT == FP4_FMT_MXFP4) {
+      if constexpr (fmt_mx(FMT)) {
         const uint32_t sc = *reinterpret_cast<const uint32_t*>(slot + BN * 64 + (row >> 5) * 256 + (lane & 31) * 4 +
                                                                 (lane >> 5) * 128);
-        const float scale = e8m0_as_cvt_scale((sc >> (8 * (2 * (kt & 1) + s))) & 0xFFu);
+        const uint32_t code = (sc >> (8 * (2 * (kt & 1) + s))) & 0xFFu;
+        if constexpr (fmt_int(FMT)) {
+          const float p = e8m0_value(code);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[j] = mfma_bf16(a[s * 4 + t], expand8_bf16_mx(codes[t], scale), acc[j]);
+          for (int t = 0; t < 4; ++t) acc[j] = mfma_bf16(a[s * 4 + t], expand8_i4_bf16(codes[t], p), acc[j]);
+        } else {
+          const float scale = e8m0_as_cvt_scale(code);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[j] = mfma_bf16(a[s * 4 + t], expand8_bf16_mx(codes[t], scale), acc[j]);
+        }
       } else {
         const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(
             slot + BN * 64 + row * 16 + 8 * (kt & 1) + 4 * s + 2 * (lane >> 5));
         const float s0 = e4m3_value(sc2 & 0xFFu), s1 = e4m3_value(sc2 >> 8);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          acc[j] = mfma_bf16(a[s * 4 + t], expand8_bf16_nv(codes[t], t < 2 ? s0 : s1), acc[j]);
+          acc[j] = mfma_bf16(a[s * 4 + t],
+                             fmt_int(FMT) ? expand8_i4_bf16(codes[t], t < 2 ? s0 : s1)
+                                          : expand8_bf16_nv(codes[t], t < 2 ? s0 : s1),
+                             acc[j]);
       }
     }
   };
@@ -723,7 +806,7 @@ __global__ __launch_bounds__(256) void gemm_w4a16_kernel(
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   }
 
-  const float g = (FMT == FP4_FMT_NVFP4 && !PARTIAL) ? *bgs : 1.0f;
+  const float g = (!fmt_mx(FMT) && !PARTIAL) ? *bgs : 1.0f;
 #pragma unroll
   for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -773,34 +856,34 @@ hipError_t launch_mx_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, cons
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
+template <int FMT, int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
 hipError_t nv_lds_attr() {
   static hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_nv_ring_kernel<BM, BN, WM, WN, NS, YDT, PARTIAL>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, NvCfg<BM, BN, WM, WN, NS>::LDS);
+      reinterpret_cast<const void*>(&gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, YDT, PARTIAL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, NvCfg<BM, BN, WM, WN, NS, FMT>::LDS);
   return status;
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, int FMT = FP4_FMT_NVFP4>
 hipError_t launch_nv_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                          const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
                          void* y, int ydt, int64_t ldy, int splits, int kt_per, float* part,
                          hipStream_t st) {
-  using C = NvCfg<BM, BN, WM, WN, NS>;
+  using C = NvCfg<BM, BN, WM, WN, NS, FMT>;
   const int tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(((M + BM - 1) / BM) * tiles_n), (unsigned)splits);
   hipError_t e;
   if (splits > 1) {
-    if ((e = nv_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, true>()) != hipSuccess) return e;
-    gemm_nv_ring_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, true><<<grid, C::NW * 64, C::LDS, st>>>(
+    if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, true>()) != hipSuccess) return e;
+    gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, true><<<grid, C::NW * 64, C::LDS, st>>>(
         a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
   } else if (ydt == FP4_DT_F32) {
-    if ((e = nv_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, false>()) != hipSuccess) return e;
-    gemm_nv_ring_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, false><<<grid, C::NW * 64, C::LDS, st>>>(
+    if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, false>()) != hipSuccess) return e;
+    gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, false><<<grid, C::NW * 64, C::LDS, st>>>(
         a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
   } else {
-    if ((e = nv_lds_attr<BM, BN, WM, WN, NS, FP4_DT_BF16, false>()) != hipSuccess) return e;
-    gemm_nv_ring_kernel<BM, BN, WM, WN, NS, FP4_DT_BF16, false><<<grid, C::NW * 64, C::LDS, st>>>(
+    if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_BF16, false>()) != hipSuccess) return e;
+    gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_BF16, false><<<grid, C::NW * 64, C::LDS, st>>>(
         a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
   }
   return hipGetLastError();
@@ -1076,6 +1159,44 @@ size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K) {
   return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+// The ring GEMM with expanded operands for INT4 elements: NVINT4 on fp16
+// MFMA (n * e4m3 exact in fp16), MXINT4 on bf16 MFMA (n * 2^e exact in bf16).
+template <int FMT>
+hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
+                            const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
+                            void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                            hipStream_t st) {
+  MxPlan p = plan_mx(M, N, K);
+  const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_nv_workspace(M, N, K);
+  const int splits = split ? p.splits : 1;
+  const int kt_per = split ? p.kt_per : (int)(K / 128);
+  float* part = static_cast<float*>(ws);
+  hipError_t e;
+  if (p.cfg == 0)
+    e = launch_nv_cfg<256, 256, 128, 128, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  else if (p.cfg == 1)
+    e = launch_nv_cfg<128, 128, 64, 64, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  else
+    e = launch_nv_cfg<32, 256, 32, 64, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  if (e != hipSuccess || !split) return e;
+  return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, fmt_mx(FMT) ? nullptr : ags,
+                              fmt_mx(FMT) ? nullptr : bgs, st);
+}
+
+hipError_t launch_gemm_int4(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                            const uint8_t* as, const float* ags, const uint8_t* b, const uint8_t* bs,
+                            const float* bgs, void* y, int ydt, int64_t ldy, void* ws,
+                            size_t ws_bytes, hipStream_t st) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K == 0) {
+    zero_out_kernel<<<256, kThreads, 0, st>>>(y, ydt, (int)M, (int)N, ldy);
+    return hipGetLastError();
+  }
+  if (fmt == FP4_FMT_MXINT4)
+    return launch_ring_int4<FP4_FMT_MXINT4>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, ws, ws_bytes, st);
+  return launch_ring_int4<FP4_FMT_NVINT4>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, ws, ws_bytes, st);
+}
+
 hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                           const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
                           void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t st) {
@@ -1128,12 +1249,18 @@ hipError_t launch_gemm_w4a16(int fmt, int64_t M, int64_t N, int64_t K, const voi
   const int kt_per = split ? p.kt_per : (int)(K / 128);
   float* part = static_cast<float*>(ws);
   const uint8_t* ab = static_cast<const uint8_t*>(a);
-  hipError_t e = fmt == FP4_FMT_MXFP4
-                     ? launch_w4_fmt<FP4_FMT_MXFP4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st)
-                     : launch_w4_fmt<FP4_FMT_NVFP4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  hipError_t e;
+  if (fmt == FP4_FMT_MXFP4)
+    e = launch_w4_fmt<FP4_FMT_MXFP4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  else if (fmt == FP4_FMT_NVFP4)
+    e = launch_w4_fmt<FP4_FMT_NVFP4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  else if (fmt == FP4_FMT_MXINT4)
+    e = launch_w4_fmt<FP4_FMT_MXINT4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  else
+    e = launch_w4_fmt<FP4_FMT_NVINT4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy,
-                              fmt == FP4_FMT_NVFP4 ? bgs : nullptr, nullptr, st);
+                              fmt_mx(fmt) ? nullptr : bgs, nullptr, st);
 }
 
 }  // namespace fp4lib

@@ -40,6 +40,11 @@ hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
                           void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
                           hipStream_t st);
 
+hipError_t launch_gemm_int4(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                            const uint8_t* as, const float* ags, const uint8_t* b, const uint8_t* bs,
+                            const float* bgs, void* y, int ydt, int64_t ldy, void* ws,
+                            size_t ws_bytes, hipStream_t st);
+
 size_t gemm_w4a16_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_w4a16(int fmt, int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
                              const uint8_t* b, const uint8_t* bs, const float* bgs, void* y, int ydt,

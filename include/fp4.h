@@ -218,6 +218,10 @@ int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor,
  *   quantizes both operands with the same rotation setting.
  * ws/ws_bytes: device workspace of fp4_gemm_workspace_bytes() bytes (any
  * contents; used for split-K partial sums; 16-byte aligned).
+ * MXINT4 / NVINT4 operands: the same call with fmt = FP4_FMT_MXINT4 (GEMM-
+ * layout E8M0 scales; n * 2^e expanded exactly to bf16, bf16 MFMA) or
+ * FP4_FMT_NVINT4 (n * e4m3 expanded exactly to fp16, fp16 MFMA, tensor scales
+ * in the epilogue); K % 256 == 0 for them.
  * Requirements: M, N >= 0, K >= 0 with K % 128 == 0; codes and scales
  * 16-byte aligned (both stream into LDS in 16-byte pieces). */
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K);
@@ -233,7 +237,8 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K,
  *   A: bf16 activations [M, K], row stride lda (elements), unquantized.
  *   B: b_codes [N, K/2] dense, b_scales in FP4_SCALES_GEMM layout for (N, K)
  *      (NVFP4: row-major), b_gs the NVFP4 tensor scale (device fp32; MXFP4
- *      ignores it).  B is dequantized exactly (e2m1 * scale is exact in bf16)
+ *      ignores it).  MXINT4 / NVINT4 weights take the same call (the integer
+ *      element times its scale is exact in bf16).  B is dequantized exactly (e2m1 * scale is exact in bf16)
  *      and multiplied on bf16 MFMA with fp32 accumulation.
  *   No rotation is applied: a caller that quantized B with the block
  *   Hadamard passes activations rotated the same way.

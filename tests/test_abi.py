@@ -161,6 +161,9 @@ def test_gemm_rejects_bad_arguments_on_host():
     assert _g(b=None) == E.FP4_ERR_INVALID_ARG
     assert _g(fmt=fp4.FMT_NVFP4, ags=None) == E.FP4_ERR_INVALID_ARG
     assert _g(M=0, y=None) == E.FP4_OK                       # empty output: nothing to do
+    assert _g(fmt=fp4.FMT_MXINT4, K=384) == E.FP4_ERR_UNSUPPORTED  # INT4 elements: K % 256
+    assert _g(fmt=fp4.FMT_NVINT4, bgs=None) == E.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_gemm_workspace_bytes(fp4.FMT_NVINT4, 1, 8192, 28672) > 0
     assert fp4.fp4_gemm_workspace_bytes(fp4.FMT_MXFP4, 1, 8192, 28672) > 0
     assert fp4.fp4_gemm_workspace_bytes(fp4.FMT_MXFP4, 4096, 4096, 4096) == 0
     assert _g(ws=FAKE + 8, wsb=1 << 20) == E.FP4_ERR_ALIGNMENT  # split-K partials: 16-byte aligned
@@ -196,3 +199,5 @@ def test_gemm_w4a16_rejects_bad_arguments_on_host():
     assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_NVFP4, 16, 28672, 8192) > 0
     assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXFP4, 1, 8192, 1000) == 0
     assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXFP4, 4096, 4096, 4096) == 0
+    assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXINT4, 1, 8192, 28672) > 0
+    assert _w(fmt=fp4.FMT_NVINT4, bgs=None) == E.FP4_ERR_INVALID_ARG

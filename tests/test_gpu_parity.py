@@ -381,7 +381,7 @@ def _rand_operands(fmt, M, N, K, seed):
     G = fp4.BLOCK[fmt]
     ac = workloads.random_codes(M, K, seed, stream=21)
     bc = workloads.random_codes(N, K, seed, stream=22)
-    if fmt == fp4.FMT_MXFP4:
+    if fmt in fp4.MX_FORMATS:
         asc = workloads.random_scales(M, K // G, 120, 130, seed, stream=23)
         bsc = workloads.random_scales(N, K // G, 118, 124, seed, stream=24)
         ags = bgs = np.float32(0)
@@ -394,8 +394,8 @@ def _rand_operands(fmt, M, N, K, seed):
 
 def _device_operand(codes, scales_rm, gs, fmt, rows, K):
     c = to_dev_u8(codes.reshape(-1))
-    if fmt == fp4.FMT_MXFP4:
-        s = fp4.scales_to_gemm_layout(to_dev_u8(scales_rm.reshape(-1)), rows, K)
+    if fmt in fp4.MX_FORMATS:
+        s = fp4.scales_to_gemm_layout(to_dev_u8(scales_rm.reshape(-1)), rows, K, fmt)
     else:
         s = to_dev_u8(scales_rm.reshape(-1))
     g = torch.tensor([float(gs)], dtype=torch.float32, device="cuda")
@@ -566,3 +566,49 @@ def test_gemm_w4a16_empty_k_writes_zeros():
     assert rc == fp4.FP4_OK
     torch.cuda.synchronize()
     assert torch.count_nonzero(y).item() == 0
+
+
+# ------------------------------------------------------ INT4 element GEMMs
+INT4_GEMM = [(64, 96, 256), (1, 130, 512), (33, 257, 512), (256, 256, 1024), (300, 520, 768),
+             (16, 4096, 4096), (128, 1024, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", INT4_GEMM, ids=["%dx%dx%d" % s for s in INT4_GEMM])
+@pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
+def test_gemm_int4_small_full_check(fmt, M, N, K):
+    """MXINT4 / NVINT4 operands (every nibble, -8 included) against the
+    oracle's double-precision product."""
+    _check_gemm(fmt, M, N, K, seed=M + N + K, out_dtype=torch.float32, nrows=min(M, 16), nent=512)
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 28672, 8192), (16, 8192, 28672)], ids=["8192x28672x8192", "16x8192x28672"])
+@pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
+def test_gemm_int4_llama70b_shapes(fmt, M, N, K):
+    _check_gemm(fmt, M, N, K, seed=17, out_dtype=torch.bfloat16, nrows=1, nent=128)
+
+
+@pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
+def test_int4_quantize_then_gemm_end_to_end(fmt):
+    M, N, K = 256, 384, 1024
+    say("int4 end to end", FNAME[fmt])
+    xa = workloads.gemm_activation(M, K, seed=5)
+    xb = workloads.gemm_weight(N, K, seed=5)
+    qa = fp4.quantize(to_dev_bf16(xa), fmt, scale_layout=fp4.SCALES_GEMM)
+    qb = fp4.quantize(to_dev_bf16(xb), fmt, scale_layout=fp4.SCALES_GEMM)
+    y = fp4.gemm(qa, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ca, sa, ga = oracle.quantize(workloads.bf16_bits_to_f32(xa), fmt)
+    cb, sb, gb = oracle.quantize(workloads.bf16_bits_to_f32(xb), fmt)
+    assert np.array_equal(codes_np(qa), ca) and np.array_equal(codes_np(qb), cb)
+    rows = np.repeat(np.arange(0, M, 7), N)
+    cols = np.tile(np.arange(N), np.arange(0, M, 7).size)
+    ref, absref = oracle.gemm_entries(fmt, K, ca, sa, ga, cb, sb, gb, rows, cols)
+    got = y.cpu().numpy()[rows, cols].astype(np.float64)
+    assert np.all(gemm_tolerance_ok(got, ref, absref, False))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (16, 300, 768), (33, 520, 1024), (1, 8192, 28672)],
+                         ids=["1x64x256", "16x300x768", "33x520x1024", "1x8192x28672"])
+@pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
+def test_gemm_w4a16_int4_weights(fmt, M, N, K):
+    _check_w4a16(fmt, M, N, K, seed=M + N + K, out_dtype=torch.float32, nrows=min(M, 8), nent=256)
