@@ -135,7 +135,8 @@ def main():
 
     variants = [(d, fmt, rot) for d in ("gauss", "laplace")
                 for fmt in (fp4.FMT_MXFP4, fp4.FMT_NVFP4) for rot in (False, True)]
-    FN = {fp4.FMT_MXFP4: "mxfp4", fp4.FMT_NVFP4: "nvfp4"}
+    FN = {fp4.FMT_MXFP4: "mxfp4", fp4.FMT_NVFP4: "nvfp4", fp4.FMT_MXINT4: "mxint4",
+          fp4.FMT_NVINT4: "nvint4"}
 
     def vname(v):
         return "%s/%s/%s" % (v[0], FN[v[1]], "h%d" % fp4.BLOCK[v[1]] if v[2] else "plain")
@@ -273,14 +274,16 @@ def main():
     search = {}
     if not args.no_search:
         rules = [(fp4.FMT_MXFP4, fp4.SCALE_MSE, "mse"), (fp4.FMT_NVFP4, fp4.SCALE_MSE, "mse"),
-                 (fp4.FMT_NVFP4, fp4.SCALE_FOUR_OVER_SIX, "4over6")]
+                 (fp4.FMT_NVFP4, fp4.SCALE_FOUR_OVER_SIX, "4over6"),
+                 (fp4.FMT_MXINT4, fp4.SCALE_ABSMAX, "absmax"), (fp4.FMT_NVINT4, fp4.SCALE_ABSMAX, "absmax")]
         for fmt, rule, rname in rules:
             for rot in (False, True):
-                lay = fp4.SCALES_GEMM if fmt == fp4.FMT_MXFP4 else fp4.SCALES_ROWMAJOR
+                lay = fp4.SCALES_GEMM if fmt in fp4.MX_FORMATS else fp4.SCALES_ROWMAJOR
                 cfg = fp4.qconfig(fmt, rot, lay, rule)
+                fp_twin = fp4.FMT_MXFP4 if fmt in fp4.MX_FORMATS else fp4.FMT_NVFP4
                 qs = []
                 for c in range(copies):
-                    base = outs[("gauss", fmt, rot)][c]
+                    base = outs[("gauss", fp_twin, rot)][c]
                     qs.append(fp4.Quantized(torch.empty_like(base.codes), torch.empty_like(base.scales),
                                             base.global_scale.clone(), cfg, rows, cols))
 
@@ -292,6 +295,9 @@ def main():
                     if rc != 0:
                         raise RuntimeError("quantize failed: %d" % rc)
 
+                if fmt == fp4.FMT_NVINT4:  # its own tensor scale (amax / 3136), set once
+                    for q_ in qs:
+                        fp4.global_scale(xs["gauss"][0], rotate=rot, out=q_.global_scale, fmt=fmt)
                 qcall(0)
                 torch.cuda.synchronize()
                 g = capture(lambda: [qcall(i % copies) for i in range(reps)])
@@ -310,11 +316,12 @@ def main():
                 for d in ("gauss", "laplace"):
                     qd = fp4.quantize(xs[d][0], fmt, rotate=rot, scale_layout=lay, rule=rule)
                     sd = fp4.error_sums(xs[d][0], qd).cpu().numpy()
-                    qa = outs[(d, fmt, rot)][0]
+                    qa = outs[(d, fp_twin, rot)][0]
                     sa = fp4.error_sums(xs[d][0], qa).cpu().numpy()
                     ent["nmse_" + d] = float(sd[0] / sd[1])
                     ent["nmse_absmax_" + d] = float(sa[0] / sa[1])
                 search["%s/%s/%s" % (FN[fmt], rname, "h%d" % fp4.BLOCK[fmt] if rot else "plain")] = ent
+                # nmse_absmax_*: the FP4 format with the same layout and absmax scales
         log("scale search timings done")
 
     # -------------------------------------------------------------- NMSE
@@ -478,11 +485,12 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
         w = to_dev(workloads.gemm_weight(N, K, seed=1))
         wt = w.t().contiguous()
         amax = to_dev(workloads.gemm_activation(8192, K, seed=1, outlier_frac=0.001))
-        for fmt in (fp4.FMT_MXFP4, fp4.FMT_NVFP4):
-            fname = "mxfp4+h32" if fmt == fp4.FMT_MXFP4 else "nvfp4+h16"
+        for fmt in (fp4.FMT_MXFP4, fp4.FMT_NVFP4, fp4.FMT_MXINT4, fp4.FMT_NVINT4):
+            fname = {fp4.FMT_MXFP4: "mxfp4+h32", fp4.FMT_NVFP4: "nvfp4+h16",
+                     fp4.FMT_MXINT4: "mxint4+h32", fp4.FMT_NVINT4: "nvint4+h16"}[fmt]
             qw = quant_copies(w, fmt, True, 4)
             wbytes = qw[0].codes.numel() + qw[0].scales.numel()
-            for Mm in (1, 16, 128, 8192):
+            for Mm in ((1, 16, 128, 8192) if fmt in (fp4.FMT_MXFP4, fp4.FMT_NVFP4) else (1, 8192)):
                 a = amax[:Mm]
                 qa = fp4.quantize(a, fmt, rotate=True, scale_layout=fp4.SCALES_GEMM)
                 y = torch.empty(Mm, N, dtype=torch.bfloat16, device=dev)
@@ -503,7 +511,7 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
                 us_l = time_it(layer, iters)
                 us_b = time_it(bf, iters, graph=False) if fmt == fp4.FMT_MXFP4 else None
                 fl = 2.0 * Mm * N * K
-                peak = PEAK_FP4 if fmt == fp4.FMT_MXFP4 else PEAK_F16
+                peak = PEAK_FP4 if fmt == fp4.FMT_MXFP4 else PEAK_F16  # INT4: bf16 / fp16 MFMA
                 traffic = wbytes + qa.codes.numel() + qa.scales.numel() + Mm * N * 2
                 ent = {"fmt": fname, "gemm_us": round(us_g, 2),
                        "tflops": round(fl / us_g / 1e6, 2),
