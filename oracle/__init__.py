@@ -26,6 +26,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fp4_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
+class QSpec(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int), ("rot_n", ctypes.c_int), ("signs", ctypes.c_uint32 * 4),
+                ("rule", ctypes.c_int), ("rounding", ctypes.c_int), ("seed", ctypes.c_uint32 * 2),
+                ("block_rows", ctypes.c_int)]
+
+
 MXFP4 = 0
 NVFP4 = 1
 MXINT4 = 2
@@ -68,6 +74,16 @@ def _load(path: str):
     L.ora_quantize_rule.restype = ctypes.c_int
     L.ora_quantize_rule.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, l, l, P, P, P,
                                     ctypes.c_int]
+    L.ora_quantize_spec.restype = ctypes.c_int
+    L.ora_quantize_spec.argtypes = [ctypes.POINTER(QSpec), P, l, l, P, P, P, ctypes.c_int]
+    L.ora_dequantize_rot.restype = ctypes.c_int
+    L.ora_dequantize_rot.argtypes = [ctypes.c_int, P, P, ctypes.c_float, l, l, ctypes.c_int, P, P]
+    L.ora_rotate_signed.restype = ctypes.c_int
+    L.ora_rotate_signed.argtypes = [P, P, l, l, ctypes.c_int, P, ctypes.c_int]
+    L.ora_philox4x32_10.restype = None
+    L.ora_philox4x32_10.argtypes = [P, P, P]
+    L.ora_e2m1_encode_sr.restype = ctypes.c_int
+    L.ora_e2m1_encode_sr.argtypes = [ctypes.c_float, ctypes.c_double]
     L.ora_dequantize.restype = ctypes.c_int
     L.ora_dequantize.argtypes = [ctypes.c_int, P, P, ctypes.c_float, l, l, ctypes.c_int, P]
     L.ora_error_sums.restype = None
@@ -178,6 +194,86 @@ def rotate(x, n: int) -> np.ndarray:
 SCALE_ABSMAX = 0
 SCALE_MSE = 1
 SCALE_FOUR_OVER_SIX = 2
+ROUND_NEAREST = 0
+ROUND_STOCHASTIC = 1
+
+
+def _signs_array(signs) -> np.ndarray:
+    """Sign mask of a rotation group as four uint32 words (bit i: element i
+    negated); accepts None, an int (up to 128 bits) or four words."""
+    if signs is None:
+        return np.zeros(4, dtype=np.uint32)
+    if isinstance(signs, (int, np.integer)):
+        v = int(signs)
+        return np.array([(v >> (32 * k)) & 0xFFFFFFFF for k in range(4)], dtype=np.uint32)
+    return np.ascontiguousarray(signs, dtype=np.uint32).reshape(4)
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(ctr, dtype=np.uint32).reshape(4)
+    k = np.ascontiguousarray(key, dtype=np.uint32).reshape(2)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().ora_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def e2m1_encode_sr(q: float, u: float) -> int:
+    return lib().ora_e2m1_encode_sr(float(q), float(u))
+
+
+def rotate_signed(x, n: int, signs=None, inverse: bool = False) -> np.ndarray:
+    x = _f32(x)
+    rows, cols = (1, x.size) if x.ndim == 1 else x.shape
+    y = np.empty_like(x)
+    sg = _signs_array(signs)
+    rc = lib().ora_rotate_signed(_p(x), _p(y), rows, cols, int(n), _p(sg), int(bool(inverse)))
+    if rc != 0:
+        raise ValueError("ora_rotate_signed: bad arguments")
+    return y
+
+
+def quantize_spec(x, fmt: int, rot_n: int = 0, signs=None, rule: int = SCALE_ABSMAX,
+                  rounding: int = ROUND_NEAREST, seed=(0, 0), block_rows: int = 1,
+                  ts: float | None = None):
+    """The general quantizer: rotation of size rot_n (0, the block size, or 64 /
+    128 for MX formats) with a sign mask, scale rule, nearest or stochastic
+    rounding (Philox4x32-10 keyed by seed), NVFP4 16x16 blocks.  Returns
+    (codes, scales, ts)."""
+    x = _f32(x)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    rows, cols = x.shape
+    G = BLOCK[fmt]
+    q = QSpec()
+    q.fmt, q.rot_n, q.rule, q.rounding, q.block_rows = fmt, int(rot_n), int(rule), int(rounding), int(block_rows)
+    sg = _signs_array(signs)
+    for k in range(4):
+        q.signs[k] = int(sg[k])
+    q.seed[0], q.seed[1] = int(seed[0]) & 0xFFFFFFFF, int(seed[1]) & 0xFFFFFFFF
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // G), dtype=np.uint8)
+    tsa = np.zeros(1, dtype=np.float32)
+    if ts is not None:
+        tsa[0] = ts
+    rc = lib().ora_quantize_spec(ctypes.byref(q), _p(x), rows, cols, _p(codes), _p(scales), _p(tsa),
+                                 int(ts is not None))
+    if rc != 0:
+        raise ValueError("ora_quantize_spec: bad arguments")
+    return codes, scales, np.float32(tsa[0])
+
+
+def dequantize_rot(codes, scales, fmt: int, ts: float = 0.0, rot_n: int = 0, signs=None):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows = codes.shape[0]
+    cols = codes.shape[1] * 2
+    y = np.empty((rows, cols), dtype=np.float32)
+    sg = _signs_array(signs)
+    rc = lib().ora_dequantize_rot(fmt, _p(codes), _p(scales), float(ts), rows, cols, int(rot_n),
+                                  _p(sg), _p(y))
+    if rc != 0:
+        raise ValueError("ora_dequantize_rot: bad arguments")
+    return y
 
 
 def quantize(x, fmt: int, rotate: bool = False, ts: float | None = None, rule: int = SCALE_ABSMAX):

@@ -53,6 +53,9 @@
 #define ORA_OK 0
 #define ORA_EINVAL -1
 
+int ora_dequantize_rot(int fmt, const uint8_t *codes, const uint8_t *scales, float ts,
+                       long rows, long cols, int rot_n, const uint32_t *signs, float *y);
+
 /* ------------------------------------------------------------------------ */
 /* E2M1 element ([MRGPTQ] format definitions; [VS] "The E2M1 element: only   */
 /* eight magnitudes"; [PROD] "The Numerical Ceiling of Standard 4-Bit        */
@@ -176,6 +179,73 @@ int ora_int4_encode(float q)
     return v & 15;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Counter-based random numbers for stochastic rounding: Philox4x32-10       */
+/* (J. Salmon, M. Moraes, R. Dror, D. Shaw, "Parallel random numbers: as     */
+/* easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64-bit multiplies and  */
+/* xors with the key, the key advanced by two Weyl constants between rounds. */
+/* ------------------------------------------------------------------------ */
+
+void ora_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* The uniform number in [0, 1) of element e of a tensor for stochastic
+ * rounding: counter (e / 4 low word, e / 4 high word, 0, 0), key = seed, word
+ * e % 4 of the output, top 24 bits times 2^-24 (exact). */
+static double sr_uniform(uint64_t e, const uint32_t seed[2])
+{
+    uint32_t ctr[4] = {(uint32_t)(e >> 2), (uint32_t)(e >> 34), 0u, 0u};
+    uint32_t out[4];
+    ora_philox4x32_10(ctr, seed, out);
+    return (double)(out[e & 3] >> 8) * 0x1p-24;
+}
+
+/* Stochastic rounding onto the E2M1 grid ([VS] "Stochastic rounding": up or
+ * down with probability proportional to proximity, so the expected value is
+ * the input): a = min(|q|, 6) between neighbours lo <= a < hi rounds up when
+ * u < (a - lo) / (hi - lo).  Grid points stay put; the sign bit is signbit(q). */
+int ora_e2m1_encode_sr(float q, double u)
+{
+    int neg = signbit(q) ? 1 : 0;
+    double a = fabs((double)q);
+    if (a > 6.0)
+        a = 6.0;
+    int lo = 0;
+    for (int c = 0; c < 8; ++c)
+        if (ora_e2m1_decode(c) <= a)
+            lo = c;
+    int mag = lo;
+    if (lo < 7 && ora_e2m1_decode(lo) < a) {
+        double glo = ora_e2m1_decode(lo), ghi = ora_e2m1_decode(lo + 1);
+        double p = (a - glo) / (ghi - glo);
+        if (u < p)
+            mag = lo + 1;
+    }
+    return (neg << 3) | mag;
+}
+
 /* Block size of a format (0: not a format). */
 static int fmt_block(int fmt)
 {
@@ -219,12 +289,25 @@ static int had_entry(int i, int j)
     return (__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1;
 }
 
-/* y[r, b*n + j] = fl32( (sum_i x[r, b*n + i] * H[i][j]) / sqrt(n) ), the sum
- * and the division carried out in double.  n must be a power of two and
- * divide cols.  x and y may not alias. */
-int ora_rotate(const float *x, float *y, long rows, long cols, int n)
+/* Sign of element i of a rotation group: bit i of the 128-bit mask (word
+ * i / 32, bit i % 32) set means negative ("randomized Hadamard": a random
+ * diagonal of +-1 before the transform, [PROD] "Orthogonal Rotations" and
+ * [VS] "Random Hadamard transforms").  A NULL mask is all positive. */
+static double sign_of(const uint32_t *signs, int i)
 {
-    if (n <= 0 || (n & (n - 1)) != 0 || cols % n != 0)
+    if (!signs)
+        return 1.0;
+    return ((signs[i >> 5] >> (i & 31)) & 1u) ? -1.0 : 1.0;
+}
+
+/* Forward (inverse = 0): y = fl32( (H D x) / sqrt(n) ) per group of n, with D
+ * the sign diagonal; inverse = 1: y = D fl32( (H x) / sqrt(n) ), the inverse
+ * of the forward map (H symmetric, H H = n I, D D = I).  Sums and the division
+ * in double, one rounding.  n a power of two dividing cols; no aliasing. */
+int ora_rotate_signed(const float *x, float *y, long rows, long cols, int n,
+                      const uint32_t *signs, int inverse)
+{
+    if (n <= 0 || n > 128 || (n & (n - 1)) != 0 || cols % n != 0)
         return ORA_EINVAL;
     double root = sqrt((double)n);
     for (long r = 0; r < rows; ++r) {
@@ -233,13 +316,26 @@ int ora_rotate(const float *x, float *y, long rows, long cols, int n)
             float *yb = y + r * cols + b * n;
             for (int j = 0; j < n; ++j) {
                 double s = 0.0;
-                for (int i = 0; i < n; ++i)
-                    s += (double)xb[i] * had_entry(i, j);
-                yb[j] = (float)(s / root);
+                for (int i = 0; i < n; ++i) {
+                    double xi = (double)xb[i];
+                    if (!inverse)
+                        xi *= sign_of(signs, i);
+                    s += xi * had_entry(i, j);
+                }
+                float v = (float)(s / root);
+                yb[j] = inverse ? (float)(sign_of(signs, j) * v) : v;
             }
         }
     }
     return ORA_OK;
+}
+
+/* y[r, b*n + j] = fl32( (sum_i x[r, b*n + i] * H[i][j]) / sqrt(n) ), the sum
+ * and the division carried out in double.  n must be a power of two and
+ * divide cols.  x and y may not alias. */
+int ora_rotate(const float *x, float *y, long rows, long cols, int n)
+{
+    return ora_rotate_signed(x, y, rows, cols, n, NULL, 0);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -367,28 +463,62 @@ static int nv_scale_code(float amax, float top, float tsv)
  * NVFP4 follows [VS] Figure 2 (global amax -> fp32 tensor scale -> block amax
  * -> E4M3 -> E2M1 -> pack) and the emulation's nvfp4.
  */
-int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, long cols,
+/* Quantization specification of the oracle (its own struct).
+ *   rot_n       0, or the Hadamard size: the block size (16 or 32); MX
+ *               formats also 64 or 128 ([MRGPTQ]: larger rotations help
+ *               MXFP4).  A rotation group of rot_n elements along the row.
+ *   signs       the sign diagonal applied before the Hadamard (bit i: element
+ *               i of the group negated); all zero = the plain transform.
+ *   rule        ORA_SCALE_* (searching rules: FP4 elements, block_rows 1).
+ *   rounding    0: nearest, ties to even; 1: stochastic (E2M1 elements,
+ *               absmax rule), uniform numbers from sr_uniform(seed).
+ *   block_rows  1, or 16 for NVFP4: the scale of a 16x16 tile (16 rows x one
+ *               16-column block) is taken from the tile's maximum and stored
+ *               for each of its rows ([VS] "Two-dimensional weight scaling":
+ *               a tile and its transpose share one scale). */
+typedef struct {
+    int fmt;
+    int rot_n;
+    uint32_t signs[4];
+    int rule;
+    int rounding;
+    uint32_t seed[2];
+    int block_rows;
+} ora_qspec;
+
+int ora_quantize_spec(const ora_qspec *q, const float *x, long rows, long cols,
                       uint8_t *codes, uint8_t *scales, float *ts, int gs_given)
 {
+    int fmt = q->fmt, rule = q->rule;
     int G = fmt_block(fmt);
     if (G == 0)
         return ORA_EINVAL;
-    if (rows < 0 || cols < 0 || cols % G != 0 || (rotate != 0 && rotate != 1))
+    if (rows < 0 || cols < 0 || cols % G != 0)
         return ORA_EINVAL;
     if (!fmt_mx(fmt) && ts == NULL)
         return ORA_EINVAL;
     if (rule != ORA_SCALE_ABSMAX && (fmt_int(fmt) || (rule != ORA_SCALE_MSE &&
         !(rule == ORA_SCALE_FOUR_OVER_SIX && fmt == ORA_NVFP4))))
         return ORA_EINVAL;
+    int rn = q->rot_n;
+    if (rn != 0 && rn != G && !(fmt_mx(fmt) && (rn == 64 || rn == 128)))
+        return ORA_EINVAL;
+    if (rn != 0 && cols % rn != 0)
+        return ORA_EINVAL;
+    if (q->rounding != 0 && (q->rounding != 1 || fmt_int(fmt) || rule != ORA_SCALE_ABSMAX))
+        return ORA_EINVAL;
+    if (q->block_rows != 1 && (q->block_rows != 16 || fmt != ORA_NVFP4 || rn != 0 ||
+                               rule != ORA_SCALE_ABSMAX))
+        return ORA_EINVAL;
 
     long n = rows * cols;
     const float *y = x;
     float *ybuf = NULL;
-    if (rotate) {
+    if (rn) {
         ybuf = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
         if (!ybuf)
             return ORA_EINVAL;
-        ora_rotate(x, ybuf, rows, cols, G);
+        ora_rotate_signed(x, ybuf, rows, cols, rn, q->signs, 0);
         y = ybuf;
     }
 
@@ -419,6 +549,14 @@ int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, 
         for (long b = 0; b < nb; ++b) {
             const float *yb = y + r * cols + b * G;
             float amax = block_amax(yb, G);
+            if (q->block_rows > 1) {           /* the 16x16 tile's maximum */
+                long r0 = r - r % q->block_rows;
+                for (long rr = r0; rr < r0 + q->block_rows && rr < rows; ++rr) {
+                    float m = block_amax(y + rr * cols + b * G, G);
+                    if (m > amax)
+                        amax = m;
+                }
+            }
             int sc;
             if (fmt_mx(fmt)) {
                 /* floor(log2 amax) - 2 for both elements: 4 = 2^2 is the
@@ -437,6 +575,13 @@ int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, 
                 }
             }
             block_encode(fmt, yb, G, sc, tsv, code);
+            if (q->rounding == 1) {
+                float s = fmt_mx(fmt) ? ldexpf(1.0f, sc - 127) : (float)ora_e4m3_decode(sc) * tsv;
+                for (int i = 0; i < G; ++i) {
+                    double u = sr_uniform((uint64_t)r * (uint64_t)cols + (uint64_t)(b * G + i), q->seed);
+                    code[i] = s != 0.0f ? ora_e2m1_encode_sr(yb[i] / s, u) : 0;
+                }
+            }
             if (rule != ORA_SCALE_ABSMAX && !(!fmt_mx(fmt) && !(tsv > 0.0f))) {
                 int cands[9], nc = 0;
                 if (rule == ORA_SCALE_MSE && fmt == ORA_MXFP4) {
@@ -471,6 +616,21 @@ int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, 
     return ORA_OK;
 }
 
+/* A block-size rotation (or none), nearest rounding, one-row blocks. */
+int ora_quantize_rule(int fmt, int rotate, int rule, const float *x, long rows, long cols,
+                      uint8_t *codes, uint8_t *scales, float *ts, int gs_given)
+{
+    if (rotate != 0 && rotate != 1)
+        return ORA_EINVAL;
+    ora_qspec q;
+    memset(&q, 0, sizeof q);
+    q.fmt = fmt;
+    q.rot_n = rotate ? fmt_block(fmt) : 0;
+    q.rule = rule;
+    q.block_rows = 1;
+    return ora_quantize_spec(&q, x, rows, cols, codes, scales, ts, gs_given);
+}
+
 /* The absmax rule ([VS] "A worked example, by hand"; Figure 2). */
 int ora_quantize(int fmt, int rotate, const float *x, long rows, long cols,
                  uint8_t *codes, uint8_t *scales, float *ts, int gs_given)
@@ -489,6 +649,16 @@ int ora_quantize(int fmt, int rotate, const float *x, long rows, long cols,
 int ora_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, float ts,
                    long rows, long cols, int inverse_rotate, float *y)
 {
+    return ora_dequantize_rot(fmt, codes, scales, ts, rows, cols,
+                              inverse_rotate ? fmt_block(fmt) : 0, NULL, y);
+}
+
+/* As ora_dequantize, with the inverse of a rotation of size rot_n (0: none)
+ * and sign mask signs (see ora_rotate_signed). */
+int ora_dequantize_rot(int fmt, const uint8_t *codes, const uint8_t *scales, float ts,
+                       long rows, long cols, int rot_n, const uint32_t *signs, float *y)
+{
+    int inverse_rotate = rot_n != 0;
     int G = fmt_block(fmt);
     if (G == 0)
         return ORA_EINVAL;
@@ -517,8 +687,9 @@ int ora_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales, float t
         }
     }
     if (inverse_rotate) {
-        ora_rotate(tmp, y, rows, cols, G);
+        int rc = ora_rotate_signed(tmp, y, rows, cols, rot_n, signs, 1);
         free(tmp);
+        return rc;
     }
     return ORA_OK;
 }

@@ -504,6 +504,139 @@ def check_gemm_int4_closed_forms():
     assert np.allclose(y, ref, rtol=1e-13, atol=0)
 
 
+# ------------------------------------- rotation and rounding variants
+KAT = _golden("philox4x32_10_kat.json")
+MASK = 0x0123456789ABCDEF0FEDCBA987654321
+
+
+def check_philox_known_answers():
+    """Philox4x32-10, the counter-based generator behind stochastic rounding,
+    reproduces its published known-answer vectors."""
+    for v in KAT["vectors"]:
+        out = oracle.philox4x32_10([int(c, 16) for c in v["ctr"]], [int(k, 16) for k in v["key"]])
+        assert [int(o) for o in out] == [int(o, 16) for o in v["out"]], (v, [hex(o) for o in out])
+
+
+def check_signed_rotation_is_the_matrix_product():
+    """Rotation groups of 16 .. 128 with a random sign diagonal D: the oracle's
+    y equals (x D) H_n / sqrt(n) from scipy's Sylvester matrix (double, then
+    fp32) up to one ulp in at most 1e-4 of the elements; the inverse returns x;
+    an all-zero mask is the plain transform."""
+    g = workloads.rng(47, 47)
+    x = g.normal(0, 1, (8, 256)).astype(np.float32)
+    for n in (16, 32, 64, 128):
+        bits = np.array([(MASK >> i) & 1 for i in range(n)])
+        d = np.where(bits == 1, -1.0, 1.0)
+        ref = ((x.astype(np.float64).reshape(-1, n) * d) @ scipy.linalg.hadamard(n) / np.sqrt(n))
+        ref = ref.astype(np.float32).reshape(x.shape)
+        y = oracle.rotate_signed(x, n, MASK)
+        ulp = np.abs(y.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+        assert ulp.max() <= 1 and (ulp > 0).mean() <= 1e-4, (n, ulp.max())
+        back = oracle.rotate_signed(y, n, MASK, inverse=True)
+        assert np.allclose(back, x, rtol=0, atol=1e-5 * np.abs(x).max()), n
+        assert np.array_equal(oracle.rotate_signed(x, n, 0), oracle.rotate(x, n))
+
+
+def check_mx_rotation_sizes():
+    """MXFP4 with a 64- or 128-point rotation quantizes the rotated values with
+    the usual 32-element scales: equal to quantizing rotate_signed(x) without a
+    rotation, and dequantize with the inverse rotation gives back x up to the
+    quantization error."""
+    x = workloads.laplace(workloads.rng(48, 48), 32 * 512, 1.0).astype(np.float32).reshape(32, 512)
+    for n in (64, 128):
+        c, s, _ = oracle.quantize_spec(x, oracle.MXFP4, rot_n=n, signs=MASK)
+        c2, s2, _ = oracle.quantize(oracle.rotate_signed(x, n, MASK), oracle.MXFP4)
+        assert np.array_equal(c, c2) and np.array_equal(s, s2), n
+        y = oracle.dequantize_rot(c, s, oracle.MXFP4, 0.0, rot_n=n, signs=MASK)
+        assert ((y - x) ** 2).sum() / (x ** 2).sum() < 0.02
+
+
+def check_stochastic_rounding_definition():
+    """Stochastic rounding ([VS]: up or down with probability proportional to
+    proximity): grid points never move; between neighbours lo < a < hi the value
+    rounds up exactly when u < (a - lo) / (hi - lo); saturation at 6; the sign
+    bit is kept."""
+    enc = oracle.e2m1_encode_sr
+    for c in range(8):
+        v = oracle.e2m1_decode(c)
+        for u in (0.0, 0.3, 0.999):
+            assert enc(v, u) == c and enc(-v, u) == (8 | c)
+    assert enc(0.75, 0.49) == 2 and enc(0.75, 0.5) == 1          # p = 1/2
+    assert enc(2.25, 0.2) == 5 and enc(2.25, 0.25) == 4          # p = 1/4 between 2 and 3
+    assert enc(5.0, 0.4999) == 7 and enc(5.0, 0.5) == 6          # between 4 and 6
+    assert enc(-0.3, 0.1) == 0x9 and enc(-0.3, 0.9) == 0x8       # p = 0.6 between 0 and 0.5
+    assert enc(7.5, 0.0) == 7 and enc(1e30, 0.9) == 7
+
+
+def check_stochastic_rounding_stream():
+    """Tensor-level stochastic rounding: element e uses word e % 4 of
+    Philox4x32-10(counter = e / 4, key = seed); with seed 0 the first four
+    elements see the first known-answer vector.  Every code is a neighbour of
+    the quotient; the rounding is unbiased on a 0.3 plateau; the same seed
+    repeats, another seed changes the codes."""
+    x = np.zeros((64, 32 * 16), np.float32)
+    x[0, :4] = [0.75, 6.0, 0.75, 2.5]         # scale 2^0; p = 1/2, grid, 1/2, 1/2
+    c, s, _ = oracle.quantize_spec(x, oracle.MXFP4, rounding=oracle.ROUND_STOCHASTIC, seed=(0, 0))
+    u = [int(w, 16) >> 8 for w in KAT["vectors"][0]["out"]]
+    u = [v * 2.0 ** -24 for v in u]           # 0.399, 0.880, 0.736, 0.607
+    codes = np.stack([c[0] & 15, c[0] >> 4], -1).reshape(-1)[:4]
+    want = [2 if u[0] < 0.5 else 1, 7, 2 if u[2] < 0.5 else 1, 5 if u[3] < 0.5 else 4]
+    assert list(codes) == want, (list(codes), want)
+    # a plateau of 0.3 (p = 0.6 of rounding up to 0.5) next to a 6 in every block
+    y = np.full((64, 32 * 16), 0.3, np.float32)
+    y[:, ::16] = 6.0
+    for fmt in (oracle.MXFP4, oracle.NVFP4):
+        c1, s1, t1 = oracle.quantize_spec(y, fmt, rounding=oracle.ROUND_STOCHASTIC, seed=(7, 9))
+        d = oracle.dequantize(c1, s1, fmt, t1)
+        scale = d[:, ::16].mean() / 6.0
+        vals = np.round(np.delete(d, np.s_[::16], axis=1) / scale, 5)   # NVFP4: s = 448 ts ~ 1
+        assert set(np.unique(vals)) <= {0.0, 0.5}, np.unique(vals)
+        n = vals.size
+        assert abs(vals.mean() - 0.3) < 5 * 0.5 * np.sqrt(0.24 / n), vals.mean()
+        c2, _, _ = oracle.quantize_spec(y, fmt, rounding=oracle.ROUND_STOCHASTIC, seed=(7, 9))
+        c3, _, _ = oracle.quantize_spec(y, fmt, rounding=oracle.ROUND_STOCHASTIC, seed=(8, 9))
+        assert np.array_equal(c1, c2) and (c1 != c3).mean() > 0.3
+    # codes are neighbours of the quotient on generic data
+    z = workloads.laplace(workloads.rng(49, 49), 16 * 512, 1.0).astype(np.float32).reshape(16, 512)
+    c, s, _ = oracle.quantize_spec(z, oracle.MXFP4, rounding=oracle.ROUND_STOCHASTIC, seed=(1, 2))
+    cn, sn, _ = oracle.quantize(z, oracle.MXFP4)
+    assert np.array_equal(s, sn)
+    q = z / np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+    full = np.concatenate([-GRID[:0:-1], GRID])
+    v = np.stack([c & 15, c >> 4], -1).reshape(16, -1)
+    val = np.where(v & 8, -GRID[v & 7], GRID[v & 7])
+    qc = np.clip(q, -6, 6)
+    lo = full[np.searchsorted(full, qc, side="right") - 1]
+    hi = full[np.minimum(np.searchsorted(full, qc, side="left"), full.size - 1)]
+    assert np.all((val == lo) | (val == hi))
+
+
+def check_two_dimensional_nvfp4_blocks():
+    """NVFP4 16x16 weight blocks ([VS] "Two-dimensional weight scaling"): the 16
+    rows of a tile share the scale E4M3((tile max / 6) / ts) (E4M3 rounding from
+    the format definition), a tile and its transpose get the same scale, and
+    the codes are nearest grid points at that scale.  A partial last tile
+    (40 rows) uses the rows it has."""
+    e4 = _e4m3_values_from_definition()
+    w = workloads.laplace(workloads.rng(50, 50), 64 * 256, 1.0).astype(np.float32).reshape(64, 256)
+    c, s, ts = oracle.quantize_spec(w, oracle.NVFP4, block_rows=16)
+    ct, st, tst = oracle.quantize_spec(np.ascontiguousarray(w.T), oracle.NVFP4, block_rows=16)
+    assert ts == tst
+    tiles = np.abs(w).reshape(4, 16, 16, 16).max(axis=(1, 3))          # [row tile, col block]
+    want = np.searchsorted(e4, _binade_rne_e4m3((tiles.astype(np.float32) / np.float32(6)) / ts))
+    assert np.array_equal(s.reshape(4, 16, 16), np.repeat(want[:, None, :], 16, axis=1))
+    assert np.array_equal(st.reshape(16, 16, 4), np.repeat(want.T[:, None, :], 16, axis=1))
+    y = oracle.dequantize(c, s, oracle.NVFP4, ts).astype(np.float64)
+    sv = np.repeat((e4[s].astype(np.float32) * np.float32(ts)).astype(np.float64), 16, axis=1)
+    best = np.abs(np.abs(w)[..., None] - GRID[None, None, :] * sv[..., None]).min(-1)
+    # y rounds e2m1 * e4m3 * ts once: within 2^-22 |w| of the brute-force distance
+    assert np.all(np.abs(np.abs(y - w) - best) <= 2.0 ** -22 * np.abs(w) + 1e-30)
+    c4, s4, _ = oracle.quantize_spec(w[:40], oracle.NVFP4, block_rows=16, ts=ts)
+    assert np.array_equal(s4[:32], s[:32])
+    last = np.abs(w[32:40]).reshape(8, 16, 16).max(axis=(0, 2))
+    assert np.array_equal(s4[32], np.searchsorted(e4, _binade_rne_e4m3((last / np.float32(6)) / ts)))
+
+
 # ------------------------------------------------ scale search (MSE, 4/6)
 MX_WINDOW = (0, 1)
 NV_WINDOW = (0, 1, -1, 2, -2, 3, 4, 5, 6)

@@ -35,7 +35,7 @@ MUTANTS = [
     ("nv dequant drops tensor scale", "dst[r * cols + k] = inner * ts;", "dst[r * cols + k] = inner;"),
     ("nibble order swapped", "if ((k & 1) == 0)\n        row_codes[k >> 1]", "if ((k & 1) == 1)\n        row_codes[k >> 1]"),
     ("hadamard sign pattern", "(unsigned)(i & j)", "(unsigned)(i | j)"),
-    ("hadamard normalisation", "yb[j] = (float)(s / root);", "yb[j] = (float)(s / n);"),
+    ("hadamard normalisation", "float v = (float)(s / root);", "float v = (float)(s / n);"),
     ("block amax without abs", "float a = fabsf(v[i]);", "float a = v[i];"),
     ("mx clamp", "if (e < -127)\n        e = -127;", "if (e < -126)\n        e = -126;"),
     ("gemm drops a sign", "s += av * bv;", "s += av * fabs(bv);"),
@@ -62,6 +62,15 @@ MUTANTS = [
      "return c >= 8 ? (double)(8 - c) : (double)c;"),
     ("nvint4 tensor scale uses the FP4 maximum", "tsv = gamax / 3136.0f;", "tsv = gamax / 2688.0f;"),
     ("nvint4 block scale divides by 6", "float t = (amax / 7.0f) / tsv;", "float t = (amax / 6.0f) / tsv;"),
+    ("philox multiplier", "(uint64_t)0xD2511F53u * c0", "(uint64_t)0xD2511F55u * c0"),
+    ("philox key schedule", "k1 += 0xBB67AE85u;", "k1 += 0xBB67AE86u;"),
+    ("stochastic rounding ties up", "if (u < p)\n            mag = lo + 1;", "if (u <= p)\n            mag = lo + 1;"),
+    ("stochastic rounding reuses one word", "return (double)(out[e & 3] >> 8) * 0x1p-24;",
+     "return (double)(out[0] >> 8) * 0x1p-24;"),
+    ("rotation signs indexed by output", "xi *= sign_of(signs, i);", "xi *= sign_of(signs, j);"),
+    ("rotation sign bit within a word", "return ((signs[i >> 5] >> (i & 31)) & 1u) ? -1.0 : 1.0;",
+     "return ((signs[i >> 5] >> (i & 15)) & 1u) ? -1.0 : 1.0;"),
+    ("two-dimensional tile of 8 rows", "long r0 = r - r % q->block_rows;", "long r0 = r - r % 8;"),
     ("int4 formats decode as E2M1", "return fmt_int(fmt) ? ora_int4_decode(code) : ora_e2m1_decode(code);",
      "return ora_e2m1_decode(code);"),
 ]
