@@ -40,6 +40,8 @@ GS_GIVEN = 1
 SCALE_ABSMAX = 0
 SCALE_MSE = 1
 SCALE_FOUR_OVER_SIX = 2
+ROUND_NEAREST = 0
+ROUND_STOCHASTIC = 1
 BLOCK = {FMT_MXFP4: 32, FMT_NVFP4: 16, FMT_MXINT4: 32, FMT_NVINT4: 16}
 MX_FORMATS = (FMT_MXFP4, FMT_MXINT4)
 
@@ -59,13 +61,24 @@ class FP4Error(RuntimeError):
 
 class QConfig(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("block", ctypes.c_int32), ("rotate", ctypes.c_int32),
-                ("rule", ctypes.c_int32), ("scale_layout", ctypes.c_int32)]
+                ("rule", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
+                ("rounding", ctypes.c_int32), ("block_rows", ctypes.c_int32),
+                ("rot_signs", ctypes.c_uint32 * 4), ("seed", ctypes.c_uint32 * 2)]
 
 
-def qconfig(fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMAJOR,
-            rule: int = SCALE_ABSMAX) -> QConfig:
+def qconfig(fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
+            rule: int = SCALE_ABSMAX, rounding: int = ROUND_NEAREST, block_rows: int = 1,
+            signs: int = 0, seed=(0, 0)) -> QConfig:
+    """rotate: False / True (a rotation of the block size) or the rotation size
+    (MX formats: 32, 64, 128).  signs: the rotation's sign mask as an integer
+    (bit i negates element i of each group).  seed: stochastic-rounding key."""
     G = BLOCK[fmt]
-    return QConfig(fmt, G, G if rotate else 0, rule, scale_layout)
+    rot = 0 if rotate is False or rotate is None else (G if rotate is True else int(rotate))
+    q = QConfig(fmt, G, rot, rule, scale_layout, rounding, block_rows)
+    for k in range(4):
+        q.rot_signs[k] = (int(signs) >> (32 * k)) & 0xFFFFFFFF
+    q.seed[0], q.seed[1] = int(seed[0]) & 0xFFFFFFFF, int(seed[1]) & 0xFFFFFFFF
+    return q
 
 
 _lib = None
@@ -247,9 +260,10 @@ class Quantized:
     cols: int
 
 
-def quantize(x, fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMAJOR,
+def quantize(x, fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
              global_scale=None, out: Quantized | None = None,
-             rule: int = SCALE_ABSMAX) -> Quantized:
+             rule: int = SCALE_ABSMAX, rounding: int = ROUND_NEAREST, block_rows: int = 1,
+             signs: int = 0, seed=(0, 0)) -> Quantized:
     """Quantize a 2-D CUDA tensor (fp32 or bf16, unit stride along the last
     axis).  NVFP4: ``global_scale`` (a float32[1] CUDA tensor) is used as given
     when passed, otherwise computed from the tensor's amax.  ``rule`` selects
@@ -257,7 +271,7 @@ def quantize(x, fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMA
     torch = _torch()
     assert x.dim() == 2 and x.stride(1) == 1
     rows, cols = x.shape
-    cfg = qconfig(fmt, rotate, scale_layout, rule)
+    cfg = qconfig(fmt, rotate, scale_layout, rule, rounding, block_rows, signs, seed)
     if out is None:
         codes = torch.empty(max(fp4_codes_bytes(rows, cols), 16), dtype=torch.uint8, device=x.device)
         scales = torch.empty(max(fp4_scales_bytes(cfg, rows, cols), 16), dtype=torch.uint8,
@@ -277,12 +291,12 @@ def quantize(x, fmt: int, rotate: bool = False, scale_layout: int = SCALES_ROWMA
     return out
 
 
-def global_scale(x, rotate: bool = False, out=None, fmt: int = FMT_NVFP4):
+def global_scale(x, rotate=False, out=None, fmt: int = FMT_NVFP4, signs: int = 0):
     """NVFP4 (or NVINT4) per-tensor scale of a 2-D CUDA tensor (float32[1]
     CUDA tensor)."""
     torch = _torch()
     rows, cols = x.shape
-    cfg = qconfig(fmt, rotate)
+    cfg = qconfig(fmt, rotate, signs=signs)
     if out is None:
         out = torch.zeros(1, dtype=torch.float32, device=x.device)
     wsb = fp4_workspace_bytes(cfg, rows, cols)

@@ -20,7 +20,8 @@ int check_cfg(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
   if (cfg->fmt < FP4_FMT_MXFP4 || cfg->fmt > FP4_FMT_NVINT4) return FP4_ERR_INVALID_ARG;
   const int G = fp4k::fmt_block(cfg->fmt);
   if (cfg->block != G) return FP4_ERR_INVALID_ARG;
-  if (cfg->rotate != 0 && cfg->rotate != G) return FP4_ERR_INVALID_ARG;
+  const bool big_rot = fp4k::fmt_mx(cfg->fmt) && (cfg->rotate == 64 || cfg->rotate == 128);
+  if (cfg->rotate != 0 && cfg->rotate != G && !big_rot) return FP4_ERR_INVALID_ARG;
   if (cfg->rule != FP4_SCALE_ABSMAX && cfg->rule != FP4_SCALE_MSE &&
       cfg->rule != FP4_SCALE_FOUR_OVER_SIX)
     return FP4_ERR_INVALID_ARG;
@@ -29,6 +30,17 @@ int check_cfg(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
   if (cfg->scale_layout != FP4_SCALES_ROWMAJOR && cfg->scale_layout != FP4_SCALES_GEMM)
     return FP4_ERR_INVALID_ARG;
   if (rows < 0 || cols < 0 || cols % G != 0) return FP4_ERR_INVALID_ARG;
+  if (cfg->rotate != 0 && cols % cfg->rotate != 0) return FP4_ERR_INVALID_ARG;
+  if (cfg->rounding != FP4_ROUND_NEAREST && cfg->rounding != FP4_ROUND_STOCHASTIC)
+    return FP4_ERR_INVALID_ARG;
+  if (cfg->rounding == FP4_ROUND_STOCHASTIC &&
+      (fp4k::fmt_int(cfg->fmt) || cfg->rule != FP4_SCALE_ABSMAX))
+    return FP4_ERR_UNSUPPORTED;
+  if (cfg->block_rows != 0 && cfg->block_rows != 1 && cfg->block_rows != 16)
+    return FP4_ERR_INVALID_ARG;
+  if (cfg->block_rows == 16 &&
+      (cfg->fmt != FP4_FMT_NVFP4 || cfg->rotate != 0 || cfg->rule != FP4_SCALE_ABSMAX))
+    return FP4_ERR_UNSUPPORTED;
   // 32-bit block indexing inside the kernels
   if (rows >= (int64_t)1 << 31 || cols >= (int64_t)1 << 31 || rows * cols >= ((int64_t)1 << 32))
     return FP4_ERR_UNSUPPORTED;
@@ -45,6 +57,25 @@ int check_ld(const void* p, int32_t dt, int64_t rows, int64_t cols, int64_t ld) 
     if (rows > 1 && (ld * eb) % 16 != 0) return FP4_ERR_ALIGNMENT;
   }
   return FP4_OK;
+}
+
+// Rotation group in blocks (0: no rotation).
+int rot_blocks(const fp4_qconfig* cfg) { return cfg->rotate / cfg->block; }
+
+fp4k::QParams qparams(const fp4_qconfig* cfg, int64_t cols) {
+  fp4k::QParams P{};
+  for (int i = 0; i < 4; ++i) P.signs[i] = cfg->rot_signs[i];
+  P.any_sign = (cfg->rot_signs[0] | cfg->rot_signs[1] | cfg->rot_signs[2] | cfg->rot_signs[3]) != 0u;
+  if (cfg->rotate == 16) {  // a 16-point group: only the low 16 bits are positions
+    P.signs[0] &= 0xFFFFu;
+    P.any_sign = P.signs[0] != 0u;
+  }
+  if (cfg->rotate == 32) P.any_sign = P.signs[0] != 0u;
+  if (cfg->rotate == 64) P.any_sign = (P.signs[0] | P.signs[1]) != 0u;
+  P.seed0 = cfg->seed[0];
+  P.seed1 = cfg->seed[1];
+  P.cols = cols;
+  return P;
 }
 
 bool gemm_layout(const fp4_qconfig* cfg) {
@@ -113,9 +144,9 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (fp4k::fmt_mx(cfg->fmt)) {
     if (empty) return FP4_OK;
-    return hip_status(fp4lib::launch_quantize_mx(cfg->fmt, x, xdt, cfg->rotate != 0, cfg->rule, rows,
-                                                 cols, ldx, codes, scales, gemm_layout(cfg) ? 1 : 0,
-                                                 st));
+    return hip_status(fp4lib::launch_quantize_mx(cfg->fmt, x, xdt, rot_blocks(cfg), cfg->rule,
+                                                 cfg->rounding, rows, cols, ldx, codes, scales,
+                                                 gemm_layout(cfg) ? 1 : 0, qparams(cfg, cols), st));
   }
   if (gs_mode != FP4_GS_COMPUTE && gs_mode != FP4_GS_GIVEN) return FP4_ERR_INVALID_ARG;
   if (!global_scale) return FP4_ERR_INVALID_ARG;
@@ -127,14 +158,15 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
     if (empty) return hip_status(fp4lib::launch_amax_final(cfg->fmt, nullptr, 0, global_scale, st));
     partials = static_cast<float*>(ws);
     npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0, xdt);
-    hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, partials,
-                                          npart, st);
+    hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, qparams(cfg, cols).signs[0],
+                                          rows, cols, ldx, partials, npart, st);
     if (e != hipSuccess) return FP4_ERR_HIP;
   }
   if (empty) return FP4_OK;
-  return hip_status(fp4lib::launch_quantize_nv(cfg->fmt, x, xdt, cfg->rotate != 0, cfg->rule, rows,
-                                               cols, ldx, codes, scales, global_scale, partials,
-                                               npart, st));
+  return hip_status(fp4lib::launch_quantize_nv(cfg->fmt, x, xdt, cfg->rotate != 0, cfg->rule,
+                                               cfg->rounding, cfg->block_rows, rows, cols, ldx,
+                                               codes, scales, global_scale, partials, npart,
+                                               qparams(cfg, cols), st));
 }
 
 int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows,
@@ -153,7 +185,8 @@ int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t
     return hip_status(fp4lib::launch_amax_final(cfg->fmt, nullptr, 0, global_scale, st));
   float* partials = static_cast<float*>(ws);
   const int npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0, xdt);
-  hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, rows, cols, ldx, partials, npart, st);
+  hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, qparams(cfg, cols).signs[0], rows,
+                                        cols, ldx, partials, npart, st);
   if (e != hipSuccess) return FP4_ERR_HIP;
   return hip_status(fp4lib::launch_amax_final(cfg->fmt, partials, npart, global_scale, st));
 }
@@ -169,10 +202,10 @@ int fp4_dequantize(const fp4_qconfig* cfg, const uint8_t* codes, const uint8_t* 
   if (!codes || !scales) return FP4_ERR_INVALID_ARG;
   if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
   if (!fp4k::fmt_mx(cfg->fmt) && !global_scale) return FP4_ERR_INVALID_ARG;
-  const int rot = (inverse_rotate != 0 && cfg->rotate != 0) ? 1 : 0;
+  const int rot = inverse_rotate != 0 ? rot_blocks(cfg) : 0;
   return hip_status(fp4lib::launch_dequantize(cfg->fmt, rot, gemm_layout(cfg) ? 1 : 0, codes, scales,
                                               global_scale, rows, cols, y, ydt, ldy,
-                                              static_cast<hipStream_t>(stream)));
+                                              qparams(cfg, cols), static_cast<hipStream_t>(stream)));
 }
 
 size_t fp4_error_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
@@ -197,9 +230,9 @@ int fp4_error_sums(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t r
     if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
     if (!fp4k::fmt_mx(cfg->fmt) && !global_scale) return FP4_ERR_INVALID_ARG;
   }
-  return hip_status(fp4lib::launch_error_sums(cfg->fmt, cfg->rotate != 0, gemm_layout(cfg) ? 1 : 0,
+  return hip_status(fp4lib::launch_error_sums(cfg->fmt, rot_blocks(cfg), gemm_layout(cfg) ? 1 : 0,
                                               x, xdt, ldx, codes, scales, global_scale, rows, cols,
-                                              sums, static_cast<double*>(ws),
+                                              sums, static_cast<double*>(ws), qparams(cfg, cols),
                                               static_cast<hipStream_t>(stream)));
 }
 

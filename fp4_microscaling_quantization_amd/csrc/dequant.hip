@@ -23,11 +23,14 @@ constexpr int kThreads = 256;
 //   MXFP4: e2m1 * 2^e (hardware decode with the E8M0 code as its scale).
 //   MXINT4: q * 2^e.  NVFP4 / NVINT4: fl32(fl32(element * e4m3) * ts), the
 //   inner product exact.
-template <int FMT, bool INV>
+//   INV != 0: back to the original domain through the inverse of a rotation
+//   group of INV blocks (the lanes of a group are consecutive blocks).
+template <int FMT, int INV>
 __device__ __forceinline__ void decode_block(const uint8_t* __restrict__ codes,
                                              const uint8_t* __restrict__ scales, float ts,
                                              uint32_t r, uint32_t kb, uint32_t nb,
-                                             int64_t kchunks, bool gemm_layout, float* v) {
+                                             int64_t kchunks, bool gemm_layout, float* v,
+                                             const QParams& P) {
   constexpr int G = fmt_block(FMT);
   constexpr int NDW = G / 8;
   uint32_t w[NDW];
@@ -76,23 +79,14 @@ __device__ __forceinline__ void decode_block(const uint8_t* __restrict__ codes,
         }
     }
   }
-  if constexpr (INV) {
-    fwht<G>(v);
-    if constexpr (G == 32) {
-#pragma unroll
-      for (int i = 0; i < G; ++i) v[i] = div_sqrt32(v[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < G; ++i) v[i] *= 0.25f;
-    }
-  }
+  if constexpr (INV != 0) unrotate_block<G, INV>(v, kb, P);
 }
 
-template <int FMT, bool INV, int YDT>
+template <int FMT, int INV, int YDT>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ gs, uint32_t rows, uint32_t nb, int64_t kchunks, int gemm_layout,
-    void* __restrict__ y, int64_t ldy) {
+    void* __restrict__ y, int64_t ldy, QParams P) {
   constexpr int G = fmt_block(FMT);
   const float ts = fmt_mx(FMT) ? 0.0f : *gs;
   const uint32_t total = rows * nb;
@@ -100,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint32_t r = b / nb;
     const uint32_t kb = b - r * nb;
     float v[G];
-    decode_block<FMT, INV>(codes, scales, ts, r, kb, nb, kchunks, gemm_layout != 0, v);
+    decode_block<FMT, INV>(codes, scales, ts, r, kb, nb, kchunks, gemm_layout != 0, v, P);
     if constexpr (YDT == FP4_DT_F32) {
       f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(y) + (int64_t)r * ldy + (int64_t)kb * G);
 #pragma unroll
@@ -151,11 +145,11 @@ __device__ __forceinline__ double shfl_xor_d(double v, int off) {
 }
 
 // Per-workgroup partial sums [gridDim.x][4] in double.
-template <int FMT, bool INV, int XDT>
+template <int FMT, int INV, int XDT>
 __global__ __launch_bounds__(kThreads) void error_partial_kernel(
     const void* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ gs, uint32_t rows, uint32_t nb,
-    int64_t kchunks, int gemm_layout, double* __restrict__ partials) {
+    int64_t kchunks, int gemm_layout, double* __restrict__ partials, QParams P) {
   constexpr int G = fmt_block(FMT);
   const float ts = fmt_mx(FMT) ? 0.0f : *gs;
   double se = 0.0, sx = 0.0, sxy = 0.0, sy = 0.0;
@@ -164,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void error_partial_kernel(
     const uint32_t r = b / nb;
     const uint32_t kb = b - r * nb;
     float v[G], xv[G];
-    decode_block<FMT, INV>(codes, scales, ts, r, kb, nb, kchunks, gemm_layout != 0, v);
+    decode_block<FMT, INV>(codes, scales, ts, r, kb, nb, kchunks, gemm_layout != 0, v, P);
     load_x<XDT, G>(x, ldx, r, kb, xv);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -233,9 +227,9 @@ int grid_for(int64_t total, int cap) {
 
 namespace fp4lib {
 
-hipError_t launch_dequantize(int fmt, int rotate, int gemm_layout, const uint8_t* codes,
+hipError_t launch_dequantize(int fmt, int rot_blocks, int gemm_layout, const uint8_t* codes,
                              const uint8_t* scales, const float* gs, int64_t rows, int64_t cols,
-                             void* y, int ydt, int64_t ldy, hipStream_t st) {
+                             void* y, int ydt, int64_t ldy, const QParams& P, hipStream_t st) {
   const int G = fmt_block(fmt);
   const uint32_t nb = (uint32_t)(cols / G);
   const int64_t total = rows * (int64_t)nb;
@@ -244,21 +238,24 @@ hipError_t launch_dequantize(int fmt, int rotate, int gemm_layout, const uint8_t
   const int grid = grid_for(total, 8192);
 #define FP4_DQ(F, I, Y)                                                                    \
   dequant_kernel<F, I, Y><<<grid, kThreads, 0, st>>>(codes, scales, gs, (uint32_t)rows, nb, \
-                                                     kchunks, gemm_layout, y, ldy)
+                                                     kchunks, gemm_layout, y, ldy, P)
 #define FP4_DQ_Y(F, I)                                   \
   do {                                                   \
     if (ydt == FP4_DT_F32) FP4_DQ(F, I, FP4_DT_F32);     \
     else FP4_DQ(F, I, FP4_DT_BF16);                      \
   } while (0)
-  if (fmt == FP4_FMT_MXFP4) {
-    if (rotate) FP4_DQ_Y(FP4_FMT_MXFP4, true); else FP4_DQ_Y(FP4_FMT_MXFP4, false);
-  } else if (fmt == FP4_FMT_NVFP4) {
-    if (rotate) FP4_DQ_Y(FP4_FMT_NVFP4, true); else FP4_DQ_Y(FP4_FMT_NVFP4, false);
-  } else if (fmt == FP4_FMT_MXINT4) {
-    if (rotate) FP4_DQ_Y(FP4_FMT_MXINT4, true); else FP4_DQ_Y(FP4_FMT_MXINT4, false);
-  } else {
-    if (rotate) FP4_DQ_Y(FP4_FMT_NVINT4, true); else FP4_DQ_Y(FP4_FMT_NVINT4, false);
-  }
+#define FP4_DQ_R(F)                                                  \
+  do {                                                               \
+    if (rot_blocks == 0) FP4_DQ_Y(F, 0);                             \
+    else if (rot_blocks == 1) FP4_DQ_Y(F, 1);                        \
+    else if (fmt_mx(F) && rot_blocks == 2) FP4_DQ_Y(F, 2);           \
+    else if (fmt_mx(F) && rot_blocks == 4) FP4_DQ_Y(F, 4);           \
+  } while (0)
+  if (fmt == FP4_FMT_MXFP4) FP4_DQ_R(FP4_FMT_MXFP4);
+  else if (fmt == FP4_FMT_NVFP4) FP4_DQ_R(FP4_FMT_NVFP4);
+  else if (fmt == FP4_FMT_MXINT4) FP4_DQ_R(FP4_FMT_MXINT4);
+  else FP4_DQ_R(FP4_FMT_NVINT4);
+#undef FP4_DQ_R
 #undef FP4_DQ_Y
 #undef FP4_DQ
   return hipGetLastError();
@@ -269,10 +266,10 @@ int error_partials(int64_t rows, int64_t cols, int fmt) {
   return grid_for(rows * (cols / G), 1024);
 }
 
-hipError_t launch_error_sums(int fmt, int rotate, int gemm_layout, const void* x, int xdt,
+hipError_t launch_error_sums(int fmt, int rot_blocks, int gemm_layout, const void* x, int xdt,
                              int64_t ldx, const uint8_t* codes, const uint8_t* scales,
                              const float* gs, int64_t rows, int64_t cols, double* sums,
-                             double* partials, hipStream_t st) {
+                             double* partials, const QParams& P, hipStream_t st) {
   const int G = fmt_block(fmt);
   const uint32_t nb = (uint32_t)(cols / G);
   const int64_t kchunks = mx_gemm_kchunks(cols);
@@ -284,21 +281,24 @@ hipError_t launch_error_sums(int fmt, int rotate, int gemm_layout, const void* x
 #define FP4_ER(F, I, X)                                                                        \
   error_partial_kernel<F, I, X><<<grid, kThreads, 0, st>>>(x, ldx, codes, scales, gs,           \
                                                            (uint32_t)rows, nb, kchunks,         \
-                                                           gemm_layout, partials)
+                                                           gemm_layout, partials, P)
 #define FP4_ER_X(F, I)                                   \
   do {                                                   \
     if (xdt == FP4_DT_F32) FP4_ER(F, I, FP4_DT_F32);     \
     else FP4_ER(F, I, FP4_DT_BF16);                      \
   } while (0)
-  if (fmt == FP4_FMT_MXFP4) {
-    if (rotate) FP4_ER_X(FP4_FMT_MXFP4, true); else FP4_ER_X(FP4_FMT_MXFP4, false);
-  } else if (fmt == FP4_FMT_NVFP4) {
-    if (rotate) FP4_ER_X(FP4_FMT_NVFP4, true); else FP4_ER_X(FP4_FMT_NVFP4, false);
-  } else if (fmt == FP4_FMT_MXINT4) {
-    if (rotate) FP4_ER_X(FP4_FMT_MXINT4, true); else FP4_ER_X(FP4_FMT_MXINT4, false);
-  } else {
-    if (rotate) FP4_ER_X(FP4_FMT_NVINT4, true); else FP4_ER_X(FP4_FMT_NVINT4, false);
-  }
+#define FP4_ER_R(F)                                                  \
+  do {                                                               \
+    if (rot_blocks == 0) FP4_ER_X(F, 0);                             \
+    else if (rot_blocks == 1) FP4_ER_X(F, 1);                        \
+    else if (fmt_mx(F) && rot_blocks == 2) FP4_ER_X(F, 2);           \
+    else if (fmt_mx(F) && rot_blocks == 4) FP4_ER_X(F, 4);           \
+  } while (0)
+  if (fmt == FP4_FMT_MXFP4) FP4_ER_R(FP4_FMT_MXFP4);
+  else if (fmt == FP4_FMT_NVFP4) FP4_ER_R(FP4_FMT_NVFP4);
+  else if (fmt == FP4_FMT_MXINT4) FP4_ER_R(FP4_FMT_MXINT4);
+  else FP4_ER_R(FP4_FMT_NVINT4);
+#undef FP4_ER_R
 #undef FP4_ER_X
 #undef FP4_ER
   hipError_t e = hipGetLastError();

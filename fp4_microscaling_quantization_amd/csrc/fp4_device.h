@@ -193,6 +193,148 @@ __device__ __forceinline__ void fwht_lane_stage(float* v, int lane) {
   }
 }
 
+// ----------------------------------------------- rotation groups and signs
+// Launch parameters beyond the format: the sign diagonal of the rotation
+// (bit i of the 128-bit mask: element i of each rotation group negated before
+// the transform) and the stochastic-rounding key.
+struct QParams {
+  uint32_t signs[4];
+  uint32_t any_sign;  // nonzero when some sign bit is set
+  uint32_t seed0, seed1;
+  uint32_t pad;
+  int64_t cols;       // row length, for the element index of stochastic rounding
+};
+
+// Negate element i of the N values when bit i of m is set.
+template <int N>
+__device__ __forceinline__ void apply_signs(float* v, uint32_t m) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = as_f(as_u(v[i]) ^ (((m >> i) & 1u) << 31));
+}
+
+// The sign bits of block kb of a row (blocks of G elements, rotation groups of
+// RN blocks): word kb % RN of the mask for G = 32, the low 16 bits for G = 16.
+template <int G, int RN>
+__device__ __forceinline__ uint32_t block_signs(const QParams& P, uint32_t kb) {
+  return P.signs[RN >= 2 ? (kb & (RN - 1)) : 0];
+}
+
+// Unnormalised Walsh-Hadamard transform of a rotation group of RN blocks: the
+// in-register transform of the lane's block, then log2(RN) butterfly stages
+// across the lanes that hold the group's other blocks (consecutive lanes hold
+// consecutive blocks, so the partner of block kb for stage d is lane ^ d;
+// every lane of a group takes part).  H_(RN G) = H_RN (x) H_G, Sylvester order.
+template <int G, int RN>
+__device__ __forceinline__ void fwht_group(float* v, uint32_t kb) {
+  fwht<G>(v);
+  if constexpr (RN >= 2) {
+    const bool up = (kb & 1u) != 0;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float p = quad_xor1(v[i]);
+      v[i] = up ? p - v[i] : v[i] + p;
+    }
+  }
+  if constexpr (RN >= 4) {
+    const bool up = (kb & 2u) != 0;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float p = quad_xor2(v[i]);
+      v[i] = up ? p - v[i] : v[i] + p;
+    }
+  }
+}
+
+// y = S / sqrt(N) for N = 16 .. 128 (exact for 16 and 64; the two-term
+// constant for 32; for 128 that result halved, exactly).
+template <int N>
+__device__ __forceinline__ float div_sqrt_n(float s) {
+  if constexpr (N == 16) return s * 0.25f;
+  else if constexpr (N == 32) return div_sqrt32(s);
+  else if constexpr (N == 64) return s * 0.125f;
+  else return div_sqrt32(s) * 0.5f;
+}
+
+// Forward rotation of the lane's block (signs, transform, normalisation).
+template <int G, int RN>
+__device__ __forceinline__ void rotate_block(float* v, uint32_t kb, const QParams& P) {
+  if (P.any_sign) apply_signs<G>(v, block_signs<G, RN>(P, kb));
+  fwht_group<G, RN>(v, kb);
+#pragma unroll
+  for (int i = 0; i < G; ++i) v[i] = div_sqrt_n<G * RN>(v[i]);
+}
+
+// Inverse rotation: transform, normalisation, then the signs.
+template <int G, int RN>
+__device__ __forceinline__ void unrotate_block(float* v, uint32_t kb, const QParams& P) {
+  fwht_group<G, RN>(v, kb);
+#pragma unroll
+  for (int i = 0; i < G; ++i) v[i] = div_sqrt_n<G * RN>(v[i]);
+  if (P.any_sign) apply_signs<G>(v, block_signs<G, RN>(P, kb));
+}
+
+// ------------------------------------------------------ stochastic rounding
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32 x 32 -> 64-bit products and xors with the key; the key advances by two
+// Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t* c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+    const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// Random words of elements base .. base + N - 1 of the tensor (base a multiple
+// of 4): word e % 4 of Philox4x32-10(counter = (e / 4, high half, 0, 0),
+// key = seed).
+template <int N>
+__device__ __forceinline__ void sr_words(uint64_t base, const QParams& P, uint32_t* w) {
+#pragma unroll
+  for (int j = 0; j < N / 4; ++j) {
+    const uint64_t g = (base >> 2) + (uint64_t)j;
+    uint32_t c[4] = {(uint32_t)g, (uint32_t)(g >> 32), 0u, 0u};
+    philox4x32_10(c, P.seed0, P.seed1);
+    w[4 * j] = c[0];
+    w[4 * j + 1] = c[1];
+    w[4 * j + 2] = c[2];
+    w[4 * j + 3] = c[3];
+  }
+}
+
+// Stochastic rounding of quotient q onto the E2M1 grid with the random word w:
+// a = min(|q|, 6) between neighbours lo <= a < lo + step rounds up when
+// u = (w >> 8) 2^-24 < (a - lo) / step.  Every step is exact (power-of-two
+// spacings), so the decision equals the exact comparison.  Returns the grid
+// value with the sign of q.
+__device__ __forceinline__ float sr_e2m1(float q, uint32_t w) {
+  const float a = fminf(fabsf(q), 6.0f);
+  const float step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);
+  const float inv = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+  const float lo = floorf(a * inv) * step;
+  const float p = (a - lo) * inv;
+  const float u = (float)(w >> 8) * 0x1p-24f;
+  return copysignf(u < p ? lo + step : lo, q);
+}
+
+// Eight quotients rounded stochastically, as one dword of E2M1 codes (the
+// hardware conversion of exact grid values, scale 2^0).
+__device__ __forceinline__ uint32_t enc8_sr(const float* q, const uint32_t* w) {
+  float g[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) g[i] = sr_e2m1(q[i], w[i]);
+  return enc8_f32(g, 1.0f);
+}
+
 // ------------------------------------------------------------- scale layout
 // MXFP4 GEMM scale layout: one 256-byte tile per (32 rows) x (8 blocks of 32 =
 // 256 K).  Within a tile, dword (kb % 2) * 32 + (r % 32) holds the scales of

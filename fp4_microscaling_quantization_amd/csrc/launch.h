@@ -5,30 +5,33 @@
 #include <stdint.h>
 
 #include "fp4.h"
+#include "fp4_device.h"
 
 namespace fp4lib {
 
-hipError_t launch_quantize_mx(int fmt, const void* x, int xdt, int rotate, int rule, int64_t rows,
-                              int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales,
-                              int gemm_layout, hipStream_t st);
+hipError_t launch_quantize_mx(int fmt, const void* x, int xdt, int rot_blocks, int rule,
+                              int rounding, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                              uint8_t* scales, int gemm_layout, const fp4k::QParams& P,
+                              hipStream_t st);
 int amax_partials(int64_t rows, int64_t cols, int rotate, int xdt);
-hipError_t launch_amax_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
-                          int64_t ldx, float* partials, int npart, hipStream_t st);
+hipError_t launch_amax_nv(const void* x, int xdt, int rotate, uint32_t sign_mask, int64_t rows,
+                          int64_t cols, int64_t ldx, float* partials, int npart, hipStream_t st);
 hipError_t launch_amax_final(int fmt, const float* partials, int npart, float* gs, hipStream_t st);
-hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int rule, int64_t rows,
-                              int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
-                              const float* partials, int npart, hipStream_t st);
+hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int rule, int rounding,
+                              int block_rows, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* codes, uint8_t* scales, float* gs, const float* partials,
+                              int npart, const fp4k::QParams& P, hipStream_t st);
 hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
                                  hipStream_t st);
 
-hipError_t launch_dequantize(int fmt, int rotate, int gemm_layout, const uint8_t* codes,
+hipError_t launch_dequantize(int fmt, int rot_blocks, int gemm_layout, const uint8_t* codes,
                              const uint8_t* scales, const float* gs, int64_t rows, int64_t cols,
-                             void* y, int ydt, int64_t ldy, hipStream_t st);
+                             void* y, int ydt, int64_t ldy, const fp4k::QParams& P, hipStream_t st);
 int error_partials(int64_t rows, int64_t cols, int fmt);
-hipError_t launch_error_sums(int fmt, int rotate, int gemm_layout, const void* x, int xdt,
+hipError_t launch_error_sums(int fmt, int rot_blocks, int gemm_layout, const void* x, int xdt,
                              int64_t ldx, const uint8_t* codes, const uint8_t* scales,
                              const float* gs, int64_t rows, int64_t cols, double* sums,
-                             double* partials, hipStream_t st);
+                             double* partials, const fp4k::QParams& P, hipStream_t st);
 
 size_t gemm_mx_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,

@@ -89,21 +89,30 @@ __device__ __forceinline__ float mx_sse32(const float* v, const u32x4& w, uint32
   return acc;
 }
 
-// MXFP4 block from 32 fp32 values (rotated in place when ROT); returns the
-// E8M0 code and the four code dwords.
-template <bool ROT, int RULE>
-__device__ __forceinline__ uint32_t mx_block_f32(float* v, u32x4& out) {
-  if constexpr (ROT) {
-    fwht<32>(v);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = div_sqrt32(v[i]);
-  }
+// MXFP4 block from 32 fp32 values (rotated in place when RN != 0: a group of
+// RN blocks, RN = 1, 2 or 4 for 32-, 64- and 128-point rotations); returns the
+// E8M0 code and the four code dwords.  RND: stochastic rounding of the exact
+// quotients y * 2^-e, element indices base .. base + 31.
+template <int RN, int RULE, int RND>
+__device__ __forceinline__ uint32_t mx_block_f32(float* v, u32x4& out, uint32_t kb, uint64_t base,
+                                                 const QParams& P) {
+  if constexpr (RN != 0) rotate_block<32, RN>(v, kb, P);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
   // floor(log2(amax)) = exponent field - 127 for a normal amax; subnormal and
   // zero amax clamp to the smallest scale (code 0).
   const uint32_t code = (uint32_t)max((int)((as_u(amax) >> 23) & 0xFFu) - 2, 0);
+  if constexpr (RND != 0) {
+    const float inv = e8m0_value(254u - code);  // 2^-(code - 127)
+    uint32_t w[32];
+    sr_words<32>(base, P, w);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] *= inv;
+    out = u32x4{enc8_sr(&v[0], &w[0]), enc8_sr(&v[8], &w[8]), enc8_sr(&v[16], &w[16]),
+                enc8_sr(&v[24], &w[24])};
+    return code;
+  }
   out = mx_enc32(v, code);
   if constexpr (RULE == FP4_SCALE_MSE) {
     if (code < 254u) {
@@ -137,13 +146,10 @@ __device__ __forceinline__ uint32_t mx_block_bf16(const uint32_t* w, u32x4& out)
 // MXINT4 block from 32 fp32 values (rotated in place when ROT): the MXFP4
 // E8M0 code, elements round(y / 2^e) clipped to +-7 ("Bridging the Gap ...",
 // MXINT4).  y * 2^-e is the correctly rounded quotient (a power-of-two factor).
-template <bool ROT>
-__device__ __forceinline__ uint32_t mxint_block_f32(float* v, u32x4& out) {
-  if constexpr (ROT) {
-    fwht<32>(v);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = div_sqrt32(v[i]);
-  }
+template <int RN>
+__device__ __forceinline__ uint32_t mxint_block_f32(float* v, u32x4& out, uint32_t kb,
+                                                    const QParams& P) {
+  if constexpr (RN != 0) rotate_block<32, RN>(v, kb, P);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -257,21 +263,19 @@ __device__ __forceinline__ uint32_t nv_block_search(const float* v, float amax, 
   return best;
 }
 
-template <bool ROT, int RULE>
-__device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out) {
+template <int ROT, int RULE, int RND>
+__device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out, uint32_t kb,
+                                             uint64_t base, const QParams& P) {
   if constexpr (RULE != FP4_SCALE_ABSMAX) {
-    if constexpr (ROT) {
-      fwht<16>(v);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
-    }
+    if constexpr (ROT != 0) rotate_block<16, 1>(v, kb, P);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
     return nv_block_search<RULE>(v, amax, T, out);
   }
   const bool fold = ROT && !T.small;
-  if constexpr (ROT) {
+  if constexpr (ROT != 0) {
+    if (P.any_sign) apply_signs<16>(v, P.signs[0]);
     fwht<16>(v);
     if (T.small) {
 #pragma unroll
@@ -285,6 +289,25 @@ __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out
   float s;
   const uint32_t code = nv_scale(amax, T, s);
   const float d = fold ? 4.0f * s : s;
+  if constexpr (RND != 0) {
+    // stochastic rounding of the exact quotients fl32(y / s)
+    if (d == 0.0f) {
+      out = u32x2{0u, 0u};
+      return code;
+    }
+    if (d >= 0x1p-100f) {
+      const float rd = 1.0f / d;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = div_rn(v[i], d, rd);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = v[i] / d;
+    }
+    uint32_t w[16];
+    sr_words<16>(base, P, w);
+    out = u32x2{enc8_sr(&v[0], &w[0]), enc8_sr(&v[8], &w[8])};
+    return code;
+  }
   out[0] = nv_enc8(&v[0], d);
   out[1] = nv_enc8(&v[8], d);
   return code;
@@ -292,13 +315,10 @@ __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out
 
 // NVINT4 block from 16 fp32 values (rotated in place when ROT): E4M3 code of
 // (amax / 7) / ts, elements round(fl32(y / s)) clipped to +-7.
-template <bool ROT>
-__device__ __forceinline__ uint32_t nvint_block(float* v, const NvTs& T, u32x2& out) {
-  if constexpr (ROT) {
-    fwht<16>(v);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
-  }
+template <int ROT>
+__device__ __forceinline__ uint32_t nvint_block(float* v, const NvTs& T, u32x2& out, uint32_t kb,
+                                                const QParams& P) {
+  if constexpr (ROT != 0) rotate_block<16, 1>(v, kb, P);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -352,21 +372,25 @@ __device__ __forceinline__ void store_mx_scale(uint8_t* __restrict__ scales, int
 
 // Quantize the block held in chunks c: codes in out (four dwords for MXFP4,
 // the first two for NVFP4), scale code returned.
-template <int FMT, int XDT, bool ROT, int RULE>
-__device__ __forceinline__ uint32_t compute_block(const u32x4* c, const NvTs& T, u32x4& out) {
+// Block kb of row r (element index r * cols + kb * G, for stochastic rounding).
+template <int FMT, int XDT, int ROT, int RULE, int RND>
+__device__ __forceinline__ uint32_t compute_block(const u32x4* c, const NvTs& T, u32x4& out,
+                                                  uint32_t r, uint32_t kb, const QParams& P) {
+  constexpr int G = fmt_block(FMT);
+  const uint64_t base = (uint64_t)r * (uint64_t)P.cols + (uint64_t)kb * G;
   if constexpr (FMT == FP4_FMT_MXINT4) {
     float v[32];
     unpack<XDT, 32>(c, v);
-    return mxint_block_f32<ROT>(v, out);
+    return mxint_block_f32<ROT>(v, out, kb, P);
   } else if constexpr (FMT == FP4_FMT_NVINT4) {
     float v[16];
     unpack<XDT, 16>(c, v);
     u32x2 o;
-    const uint32_t code = nvint_block<ROT>(v, T, o);
+    const uint32_t code = nvint_block<ROT>(v, T, o, kb, P);
     out = u32x4{o[0], o[1], 0u, 0u};
     return code;
   } else if constexpr (FMT == FP4_FMT_MXFP4) {
-    if constexpr (XDT == FP4_DT_BF16 && !ROT && RULE == FP4_SCALE_ABSMAX) {
+    if constexpr (XDT == FP4_DT_BF16 && !ROT && RULE == FP4_SCALE_ABSMAX && RND == 0) {
       uint32_t w[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -376,13 +400,13 @@ __device__ __forceinline__ uint32_t compute_block(const u32x4* c, const NvTs& T,
     } else {
       float v[32];
       unpack<XDT, 32>(c, v);
-      return mx_block_f32<ROT, RULE>(v, out);
+      return mx_block_f32<ROT, RULE, RND>(v, out, kb, base, P);
     }
   } else {
     float v[16];
     unpack<XDT, 16>(c, v);
     u32x2 o;
-    const uint32_t code = nv_block<ROT, RULE>(v, T, o);
+    const uint32_t code = nv_block<ROT, RULE, RND>(v, T, o, kb, base, P);
     out = u32x4{o[0], o[1], 0u, 0u};
     return code;
   }
@@ -403,13 +427,13 @@ __device__ __forceinline__ void store_block(const u32x4& out, uint32_t code, int
   }
 }
 
-template <int FMT, int XDT, bool ROT, int RULE>
+template <int FMT, int XDT, int ROT, int RULE, int RND>
 __device__ __forceinline__ void quantize_block(const u32x4* c, const NvTs& T, int64_t r, int64_t kb,
                                                int64_t nb, uint8_t* __restrict__ codes,
                                                uint8_t* __restrict__ scales, int64_t kchunks,
-                                               int gemm_layout) {
+                                               int gemm_layout, const QParams& P) {
   u32x4 out;
-  const uint32_t code = compute_block<FMT, XDT, ROT, RULE>(c, T, out);
+  const uint32_t code = compute_block<FMT, XDT, ROT, RULE, RND>(c, T, out, (uint32_t)r, (uint32_t)kb, P);
   store_block<FMT>(out, code, r, kb, nb, codes, scales, kchunks, gemm_layout);
 }
 
@@ -447,11 +471,11 @@ __device__ __forceinline__ NvTs nv_launch_ts(float* __restrict__ gs,
 // ----------------------------------------------------------- tiled kernel
 // Requires nb % 64 == 0.  Wave w of the grid-stride loop owns row r, blocks
 // [64 g, 64 g + 64).
-template <int FMT, int XDT, bool ROT, int RULE>
+template <int FMT, int XDT, int ROT, int RULE, int RND>
 __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
     const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
-    float* __restrict__ gs, const float* __restrict__ partials, int npart) {
+    float* __restrict__ gs, const float* __restrict__ partials, int npart, QParams P) {
   constexpr int G = fmt_block(FMT);
   constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
   constexpr int BB = G * ES;       // bytes per block
@@ -487,8 +511,8 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
       u32x4 c[CH];
 #pragma unroll
       for (int k = 0; k < CH; ++k) c[k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
-      quantize_block<FMT, XDT, ROT, RULE>(c, T, r, (int64_t)g * 64 + lane, nb, codes, scales,
-                                          kchunks, gemm_layout);
+      quantize_block<FMT, XDT, ROT, RULE, RND>(c, T, r, (int64_t)g * 64 + lane, nb, codes, scales,
+                                               kchunks, gemm_layout, P);
     }
     __syncthreads();
   }
@@ -565,11 +589,11 @@ __device__ __forceinline__ NvTs nv_ts_finish(const NvTsLoads& L, float* __restri
 // issues the loads of TPW tiles before any arithmetic, then runs them one by
 // one through its LDS buffer.  The scale bytes of a wave tile are 64
 // consecutive bytes of its row.
-template <int FMT, bool ROT, int TPW, int RULE>
+template <int FMT, int ROT, int TPW, int RULE, int RND>
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t wpr,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
-    float* __restrict__ gs, const float* __restrict__ partials, int npart) {
+    float* __restrict__ gs, const float* __restrict__ partials, int npart, QParams P) {
   constexpr int G = fmt_block(FMT);
   constexpr int BB = G * 2;        // bytes per block
   constexpr int CH = BB / 16;      // 16-byte chunks per block
@@ -617,7 +641,10 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 #pragma unroll
       for (int k = 0; k < CH; ++k) c[k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
       wave_lds_sync();
-      code[u] = compute_block<FMT, FP4_DT_BF16, ROT, RULE>(c, T, out[u]);
+      const uint32_t tile_u = min(t0 + u, tiles - 1);
+      const uint32_t r_u = tile_u / wpr;
+      code[u] = compute_block<FMT, FP4_DT_BF16, ROT, RULE, RND>(c, T, out[u], r_u,
+                                                                (tile_u - r_u * wpr) * 64 + lane, P);
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -640,10 +667,10 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 // 8w .. 8w + 7 of the tile; load j brings rows 2j, 2j + 1 (512 bytes each);
 // after the LDS transpose lane l holds block l % 8 of row l / 8, and the
 // codes of each row (8 blocks) are 128 contiguous bytes.
-template <int FMT, bool ROT, int RULE>
+template <int FMT, int ROT, int RULE, int RND>
 __global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
     const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t kcs,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, QParams P) {
   constexpr int STRIDE = 64 + 16;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][64 * STRIDE];
   const int lane = threadIdx.x & 63;
@@ -674,7 +701,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
     wave_lds_sync();
     const uint32_t r = r0 + (lane >> 3), kb = kc * 8 + (lane & 7);
     if (r < rows && kb < nb)
-      quantize_block<FMT, FP4_DT_BF16, ROT, RULE>(c, NvTs{}, r, kb, nb, codes, scales, kchunks, 1);
+      quantize_block<FMT, FP4_DT_BF16, ROT, RULE, RND>(c, NvTs{}, r, kb, nb, codes, scales, kchunks, 1, P);
   }
 }
 
@@ -688,7 +715,8 @@ template <bool ROT>
 __global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t* __restrict__ x,
                                                                   int64_t ldx_bytes, uint32_t rows,
                                                                   uint32_t cpr, uint32_t wpr,
-                                                                  float* __restrict__ partials) {
+                                                                  float* __restrict__ partials,
+                                                                  uint32_t sign_mask) {
   const int lane = threadIdx.x & 63;
   const uint32_t wave = threadIdx.x >> 6;
   const uint32_t tiles = rows * wpr;
@@ -714,6 +742,8 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t*
       } else {
         float v[8];
         unpack8_bf16(t[j], v);
+        // the lane's 8 elements are positions 8 (lane & 1) .. + 7 of the 16-group
+        if (sign_mask) apply_signs<8>(v, sign_mask >> (8 * (lane & 1)));
         fwht<8>(v);
         fwht_lane_stage<1>(v, lane);
 #pragma unroll
@@ -737,11 +767,11 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t*
 
 // ---------------------------------------------------------- direct kernel
 // Any shape: each thread loads its own block.
-template <int FMT, int XDT, bool ROT, int RULE>
+template <int FMT, int XDT, int ROT, int RULE, int RND>
 __global__ __launch_bounds__(kThreads) void quant_direct_kernel(
     const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
-    float* __restrict__ gs, const float* __restrict__ partials, int npart) {
+    float* __restrict__ gs, const float* __restrict__ partials, int npart, QParams P) {
   constexpr int G = fmt_block(FMT);
   constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
   constexpr int CH = G * ES / 16;
@@ -756,7 +786,7 @@ __global__ __launch_bounds__(kThreads) void quant_direct_kernel(
     u32x4 c[CH];
 #pragma unroll
     for (int k = 0; k < CH; ++k) c[k] = p[k];
-    quantize_block<FMT, XDT, ROT, RULE>(c, T, r, kb, nb, codes, scales, kchunks, gemm_layout);
+    quantize_block<FMT, XDT, ROT, RULE, RND>(c, T, r, kb, nb, codes, scales, kchunks, gemm_layout, P);
   }
 }
 
@@ -808,7 +838,8 @@ __global__ __launch_bounds__(kThreads) void amax_plain_kernel(const void* __rest
 template <int XDT>
 __global__ __launch_bounds__(kThreads) void amax_rot_kernel(const void* __restrict__ x, int64_t ldx,
                                                             uint32_t rows, uint32_t nb,
-                                                            float* __restrict__ partials) {
+                                                            float* __restrict__ partials,
+                                                            uint32_t sign_mask) {
   constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
   constexpr int CH = 16 * ES / 16;
   float m = 0.0f;
@@ -823,6 +854,7 @@ __global__ __launch_bounds__(kThreads) void amax_rot_kernel(const void* __restri
     for (int k = 0; k < CH; ++k) c[k] = p[k];
     float v[16];
     unpack<XDT, 16>(c, v);
+    if (sign_mask) apply_signs<16>(v, sign_mask);
     fwht<16>(v);
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -867,10 +899,10 @@ int grid_cap(int64_t items, int cap) {
   return (int)g;
 }
 
-template <int FMT, int XDT, bool ROT, int RULE>
+template <int FMT, int XDT, int ROT, int RULE, int RND>
 hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
                     uint8_t* scales, int gemm_layout, float* gs, const float* partials, int npart,
-                    hipStream_t st) {
+                    const QParams& P, hipStream_t st) {
   constexpr int G = fmt_block(FMT);
   const uint32_t nb = (uint32_t)(cols / G);
   const int64_t kchunks = mx_gemm_kchunks(cols);
@@ -881,8 +913,8 @@ hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint
         const uint32_t kcs = (nb + 7) / 8;
         int64_t g = ((rows + 31) / 32) * (int64_t)kcs;
         if (g > 16384) g = 16384;
-        quant_mx_gemm_kernel<FMT, ROT, RULE><<<(int)g, kThreads, 0, st>>>(
-            xb, ldx * 2, (uint32_t)rows, nb, kcs, codes, scales, kchunks);
+        quant_mx_gemm_kernel<FMT, ROT, RULE, RND><<<(int)g, kThreads, 0, st>>>(
+            xb, ldx * 2, (uint32_t)rows, nb, kcs, codes, scales, kchunks, P);
         return hipGetLastError();
       }
     }
@@ -891,21 +923,93 @@ hipError_t launch_q(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint
     const int64_t waves = (rows * (int64_t)wpr + TPW - 1) / TPW;
     int64_t g = (waves + kThreads / 64 - 1) / (kThreads / 64);
     if (g > 8192) g = 8192;
-    quant_rows_kernel<FMT, ROT, TPW, RULE><<<(int)g, kThreads, 0, st>>>(
-        xb, ldx * 2, (uint32_t)rows, nb, wpr, codes, scales, kchunks, gemm_layout, gs, partials, npart);
+    quant_rows_kernel<FMT, ROT, TPW, RULE, RND><<<(int)g, kThreads, 0, st>>>(
+        xb, ldx * 2, (uint32_t)rows, nb, wpr, codes, scales, kchunks, gemm_layout, gs, partials,
+        npart, P);
     return hipGetLastError();
   }
   if (nb % 64 == 0) {
     const int64_t waves = rows * (int64_t)(nb / 64);
     int64_t g = (waves + 3) / 4;
     if (g > 4096) g = 4096;
-    quant_tile_kernel<FMT, XDT, ROT, RULE><<<(int)g, kThreads, 0, st>>>(
-        x, ldx, (uint32_t)rows, nb, codes, scales, kchunks, gemm_layout, gs, partials, npart);
+    quant_tile_kernel<FMT, XDT, ROT, RULE, RND><<<(int)g, kThreads, 0, st>>>(
+        x, ldx, (uint32_t)rows, nb, codes, scales, kchunks, gemm_layout, gs, partials, npart, P);
   } else {
-    quant_direct_kernel<FMT, XDT, ROT, RULE><<<grid_cap(rows * (int64_t)nb, 8192), kThreads, 0, st>>>(
-        x, ldx, (uint32_t)rows, nb, codes, scales, kchunks, gemm_layout, gs, partials, npart);
+    quant_direct_kernel<FMT, XDT, ROT, RULE, RND><<<grid_cap(rows * (int64_t)nb, 8192), kThreads, 0, st>>>(
+        x, ldx, (uint32_t)rows, nb, codes, scales, kchunks, gemm_layout, gs, partials, npart, P);
   }
   return hipGetLastError();
+}
+
+// -------------------------------------------------- NVFP4 16x16 weight blocks
+// One scale per tile of 16 rows x one 16-column block, stored for each of
+// its rows ("NVFP4 vs MXFP4 ...", two-dimensional weight scaling: a tile and
+// its transpose share the scale).  Wave tile = 16 rows x 64 blocks; lane l
+// owns block 64 w + l of the 16 rows: a first sweep over the rows takes the
+// tile maximum, a second re-reads each row (from cache), encodes and stores.
+// Each lane loads its own 32 bytes (bf16) or 64 bytes (fp32) per row, so a
+// wave reads 2 or 4 KB of one row contiguously.
+template <int XDT, int RND>
+__global__ __launch_bounds__(kThreads) void quant_nv2d_kernel(
+    const void* __restrict__ x, int64_t ldx, uint32_t rows, uint32_t nb, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gs, const float* __restrict__ partials,
+    int npart, QParams P) {
+  constexpr int ES = XDT == FP4_DT_BF16 ? 2 : 4;
+  constexpr int CH = 16 * ES / 16;  // 16-byte chunks per block
+  const NvTs T = nv_launch_ts<FP4_FMT_NVFP4>(gs, partials, npart);
+  const int lane = threadIdx.x & 63;
+  const uint32_t wpr = (nb + 63) / 64, rts = (rows + 15) / 16;
+  const uint32_t tiles = rts * wpr;
+  for (uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile < tiles;
+       tile += gridDim.x * (kThreads / 64)) {
+    const uint32_t rt = tile / wpr, w = tile - rt * wpr;
+    const uint32_t kb = w * 64 + lane;
+    if (kb >= nb) continue;
+    const uint32_t r0 = rt * 16, r1 = min(r0 + 16, rows);
+    auto load = [&](uint32_t r, float* v) __attribute__((always_inline)) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(x) +
+                                                      ((int64_t)r * ldx + (int64_t)kb * 16) * ES);
+      u32x4 c[CH];
+#pragma unroll
+      for (int k = 0; k < CH; ++k) c[k] = p[k];
+      unpack<XDT, 16>(c, v);
+    };
+    float amax = 0.0f;
+    for (uint32_t r = r0; r < r1; ++r) {
+      float v[16];
+      load(r, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    float s;
+    const uint32_t code = nv_scale(amax, T, s);
+    for (uint32_t r = r0; r < r1; ++r) {
+      float v[16];
+      load(r, v);
+      u32x2 o;
+      if constexpr (RND != 0) {
+        if (s == 0.0f) {
+          o = u32x2{0u, 0u};
+        } else {
+          if (s >= 0x1p-100f) {
+            const float rs = 1.0f / s;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = div_rn(v[i], s, rs);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = v[i] / s;
+          }
+          uint32_t wds[16];
+          sr_words<16>((uint64_t)r * (uint64_t)P.cols + (uint64_t)kb * 16, P, wds);
+          o = u32x2{enc8_sr(&v[0], &wds[0]), enc8_sr(&v[8], &wds[8])};
+        }
+      } else {
+        o = u32x2{nv_enc8(&v[0], s), nv_enc8(&v[8], s)};
+      }
+      *reinterpret_cast<u32x2*>(codes + (int64_t)r * (nb * 8) + (int64_t)kb * 8) = o;
+      scales[(int64_t)r * nb + kb] = (uint8_t)code;
+    }
+  }
 }
 
 }  // namespace
@@ -924,49 +1028,59 @@ int amax_partials(int64_t rows, int64_t cols, int rotate, int xdt) {
   return grid_cap(items / 4 + 1, kAmaxGrid);
 }
 
-// Instantiate launch_q for one format over input type x rotation x rule.
-template <int FMT, int RULE>
-hipError_t launch_q_rule(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
+// Instantiate launch_q for one format over input type x rotation size.
+template <int FMT, int RULE, int RND>
+hipError_t launch_q_rule(const void* x, int xdt, int rot_blocks, int64_t rows, int64_t cols,
                          int64_t ldx, uint8_t* codes, uint8_t* scales, int gemm_layout, float* gs,
-                         const float* partials, int npart, hipStream_t st) {
-  if (xdt == FP4_DT_BF16) {
-    if (rotate)
-      return launch_q<FMT, FP4_DT_BF16, true, RULE>(x, rows, cols, ldx, codes, scales, gemm_layout, gs, partials, npart, st);
-    return launch_q<FMT, FP4_DT_BF16, false, RULE>(x, rows, cols, ldx, codes, scales, gemm_layout, gs, partials, npart, st);
+                         const float* partials, int npart, const QParams& P, hipStream_t st) {
+#define FP4_LQ(X, R)                                                                              \
+  return launch_q<FMT, X, R, RULE, RND>(x, rows, cols, ldx, codes, scales, gemm_layout, gs,        \
+                                        partials, npart, P, st)
+#define FP4_LQ_X(R)                           \
+  do {                                        \
+    if (xdt == FP4_DT_BF16) FP4_LQ(FP4_DT_BF16, R); \
+    FP4_LQ(FP4_DT_F32, R);                    \
+  } while (0)
+  if (rot_blocks == 0) FP4_LQ_X(0);
+  if constexpr (fmt_mx(FMT)) {
+    if (rot_blocks == 2) FP4_LQ_X(2);
+    if (rot_blocks == 4) FP4_LQ_X(4);
   }
-  if (rotate)
-    return launch_q<FMT, FP4_DT_F32, true, RULE>(x, rows, cols, ldx, codes, scales, gemm_layout, gs, partials, npart, st);
-  return launch_q<FMT, FP4_DT_F32, false, RULE>(x, rows, cols, ldx, codes, scales, gemm_layout, gs, partials, npart, st);
+  FP4_LQ_X(1);
+#undef FP4_LQ_X
+#undef FP4_LQ
 }
 
-hipError_t launch_quantize_mx(int fmt, const void* x, int xdt, int rotate, int rule, int64_t rows,
-                              int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales,
-                              int gemm_layout, hipStream_t st) {
+hipError_t launch_quantize_mx(int fmt, const void* x, int xdt, int rot_blocks, int rule,
+                              int rounding, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                              uint8_t* scales, int gemm_layout, const QParams& P, hipStream_t st) {
   if (fmt == FP4_FMT_MXINT4)
-    return launch_q_rule<FP4_FMT_MXINT4, FP4_SCALE_ABSMAX>(x, xdt, rotate, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
+    return launch_q_rule<FP4_FMT_MXINT4, FP4_SCALE_ABSMAX, 0>(x, xdt, rot_blocks, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, P, st);
+  if (rounding != 0)
+    return launch_q_rule<FP4_FMT_MXFP4, FP4_SCALE_ABSMAX, 1>(x, xdt, rot_blocks, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, P, st);
   if (rule == FP4_SCALE_MSE)
-    return launch_q_rule<FP4_FMT_MXFP4, FP4_SCALE_MSE>(x, xdt, rotate, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
-  return launch_q_rule<FP4_FMT_MXFP4, FP4_SCALE_ABSMAX>(x, xdt, rotate, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, st);
+    return launch_q_rule<FP4_FMT_MXFP4, FP4_SCALE_MSE, 0>(x, xdt, rot_blocks, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, P, st);
+  return launch_q_rule<FP4_FMT_MXFP4, FP4_SCALE_ABSMAX, 0>(x, xdt, rot_blocks, rows, cols, ldx, codes, scales, gemm_layout, nullptr, nullptr, 0, P, st);
 }
 
-hipError_t launch_amax_nv(const void* x, int xdt, int rotate, int64_t rows, int64_t cols,
-                          int64_t ldx, float* partials, int npart, hipStream_t st) {
+hipError_t launch_amax_nv(const void* x, int xdt, int rotate, uint32_t sign_mask, int64_t rows,
+                          int64_t cols, int64_t ldx, float* partials, int npart, hipStream_t st) {
   const int es = xdt == FP4_DT_BF16 ? 2 : 4;
   if (xdt == FP4_DT_BF16) {
     const uint32_t cpr = (uint32_t)(cols / 8);
     const uint32_t wpr = (cpr + 255) / 256;
     const uint8_t* xb = static_cast<const uint8_t*>(x);
     if (rotate)
-      amax_chunk_kernel<true><<<npart, kAmaxThreads, 0, st>>>(xb, ldx * 2, (uint32_t)rows, cpr, wpr, partials);
+      amax_chunk_kernel<true><<<npart, kAmaxThreads, 0, st>>>(xb, ldx * 2, (uint32_t)rows, cpr, wpr, partials, sign_mask);
     else
-      amax_chunk_kernel<false><<<npart, kAmaxThreads, 0, st>>>(xb, ldx * 2, (uint32_t)rows, cpr, wpr, partials);
+      amax_chunk_kernel<false><<<npart, kAmaxThreads, 0, st>>>(xb, ldx * 2, (uint32_t)rows, cpr, wpr, partials, 0u);
     return hipGetLastError();
   }
   if (rotate) {
     if (xdt == FP4_DT_BF16)
-      amax_rot_kernel<FP4_DT_BF16><<<npart, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, (uint32_t)(cols / 16), partials);
+      amax_rot_kernel<FP4_DT_BF16><<<npart, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, (uint32_t)(cols / 16), partials, sign_mask);
     else
-      amax_rot_kernel<FP4_DT_F32><<<npart, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, (uint32_t)(cols / 16), partials);
+      amax_rot_kernel<FP4_DT_F32><<<npart, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, (uint32_t)(cols / 16), partials, sign_mask);
   } else {
     const uint32_t cpr = (uint32_t)(cols * es / 16);
     if (xdt == FP4_DT_BF16)
@@ -986,16 +1100,36 @@ hipError_t launch_amax_final(int fmt, const float* partials, int npart, float* g
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int rule, int64_t rows,
-                              int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
-                              const float* partials, int npart, hipStream_t st) {
+hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int rule, int rounding,
+                              int block_rows, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* codes, uint8_t* scales, float* gs, const float* partials,
+                              int npart, const QParams& P, hipStream_t st) {
+  if (block_rows == 16) {
+    const uint32_t nb = (uint32_t)(cols / 16);
+    const int64_t tiles = ((rows + 15) / 16) * (int64_t)((nb + 63) / 64);
+    int64_t g = (tiles + 3) / 4;
+    if (g > 8192) g = 8192;
+    if (g < 1) g = 1;
+#define FP4_2D(X, R) \
+    quant_nv2d_kernel<X, R><<<(int)g, kThreads, 0, st>>>(x, ldx, (uint32_t)rows, nb, codes, scales, gs, partials, npart, P)
+    if (xdt == FP4_DT_BF16) {
+      if (rounding) FP4_2D(FP4_DT_BF16, 1); else FP4_2D(FP4_DT_BF16, 0);
+    } else {
+      if (rounding) FP4_2D(FP4_DT_F32, 1); else FP4_2D(FP4_DT_F32, 0);
+    }
+#undef FP4_2D
+    return hipGetLastError();
+  }
+  const int rb = rotate ? 1 : 0;
   if (fmt == FP4_FMT_NVINT4)
-    return launch_q_rule<FP4_FMT_NVINT4, FP4_SCALE_ABSMAX>(x, xdt, rotate, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
+    return launch_q_rule<FP4_FMT_NVINT4, FP4_SCALE_ABSMAX, 0>(x, xdt, rb, rows, cols, ldx, codes, scales, 0, gs, partials, npart, P, st);
+  if (rounding != 0)
+    return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_ABSMAX, 1>(x, xdt, rb, rows, cols, ldx, codes, scales, 0, gs, partials, npart, P, st);
   if (rule == FP4_SCALE_MSE)
-    return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_MSE>(x, xdt, rotate, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
+    return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_MSE, 0>(x, xdt, rb, rows, cols, ldx, codes, scales, 0, gs, partials, npart, P, st);
   if (rule == FP4_SCALE_FOUR_OVER_SIX)
-    return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_FOUR_OVER_SIX>(x, xdt, rotate, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
-  return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_ABSMAX>(x, xdt, rotate, rows, cols, ldx, codes, scales, 0, gs, partials, npart, st);
+    return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_FOUR_OVER_SIX, 0>(x, xdt, rb, rows, cols, ldx, codes, scales, 0, gs, partials, npart, P, st);
+  return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_ABSMAX, 0>(x, xdt, rb, rows, cols, ldx, codes, scales, 0, gs, partials, npart, P, st);
 }
 
 hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,

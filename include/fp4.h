@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP4_ABI_VERSION 1
+#define FP4_ABI_VERSION 2
 
 typedef enum {
     FP4_OK = 0,
@@ -111,13 +111,43 @@ typedef enum { FP4_GS_COMPUTE = 0, FP4_GS_GIVEN = 1 } fp4_gs_mode;
  *   scale_layout  FP4_SCALES_ROWMAJOR: byte (r, kb) at r * (cols/block) + kb.
  *                 FP4_SCALES_GEMM: the layout fp4_gemm reads; byte positions
  *                 are given by fp4_scale_offset.  For NVFP4 the two layouts
- *                 coincide. */
+ *                 coincide.
+ *   rounding      FP4_ROUND_NEAREST (ties to even), or FP4_ROUND_STOCHASTIC
+ *                 ("NVFP4 vs MXFP4 ...", the training recipe: up or down with
+ *                 probability proportional to proximity, so the expected value
+ *                 is the input) for E2M1 elements with FP4_SCALE_ABSMAX: the
+ *                 quotient a = min(|q|, 6) between grid neighbours lo < a < hi
+ *                 rounds up when u < (a - lo) / (hi - lo), with u = (w >> 8) *
+ *                 2^-24 and w word e % 4 of Philox4x32-10 (Salmon et al.,
+ *                 SC'11) at counter (e / 4 low 32 bits, high 32 bits, 0, 0)
+ *                 and key (seed[0], seed[1]), e = r * cols + c the element.
+ *   block_rows    0 or 1: blocks along a row.  16 (NVFP4, rotate 0,
+ *                 FP4_SCALE_ABSMAX): each 16 x 16 tile (16 rows x one 16-column
+ *                 block) takes its scale from the tile maximum, stored in the
+ *                 scale byte of each of its rows ("NVFP4 vs MXFP4 ...",
+ *                 two-dimensional weight scaling: a tile and its transpose
+ *                 share the scale).  A last tile of fewer rows uses those rows.
+ *   rot_signs     sign diagonal of the rotation: bit i of the 128-bit mask
+ *                 (word i / 32, bit i % 32) negates element i of each rotation
+ *                 group before the Hadamard (a randomised Hadamard transform,
+ *                 "Microscaling Formats in Production ...", orthogonal
+ *                 rotations); all zero is the plain transform.  The inverse
+ *                 (fp4_dequantize, fp4_error_sums) applies it after.
+ *   seed          stochastic-rounding key.
+ * rotate may also be 64 or 128 for MXFP4 / MXINT4 ("Bridging the Gap ...":
+ * larger rotations help MXFP4): rotation groups of 2 or 4 blocks, cols a
+ * multiple of rotate; scales stay per 32-element block. */
+typedef enum { FP4_ROUND_NEAREST = 0, FP4_ROUND_STOCHASTIC = 1 } fp4_rounding;
 typedef struct {
     int32_t fmt;
     int32_t block;
     int32_t rotate;
     int32_t rule;
     int32_t scale_layout;
+    int32_t rounding;
+    int32_t block_rows;
+    uint32_t rot_signs[4];
+    uint32_t seed[2];
 } fp4_qconfig;
 
 /* ---------------------------------------------------------------- sizes */

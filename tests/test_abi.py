@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(fp4.EXPORTED)
-    assert L.fp4_abi_version() == 1
+    assert L.fp4_abi_version() == 2
     assert fp4.status_str(fp4.FP4_ERR_ALIGNMENT).startswith("misaligned")
 
 
@@ -102,6 +102,19 @@ def test_quantize_rejects_bad_arguments_on_host():
     assert _q(bad) == E.FP4_ERR_UNSUPPORTED                  # Four Over Six is NVFP4's
     bad = fp4.QConfig(fp4.FMT_NVFP4, 16, 0, 3, 0)
     assert _q(bad) == E.FP4_ERR_INVALID_ARG                  # no such rule
+    # rotation sizes, stochastic rounding and 16x16 blocks
+    assert _q(fp4.qconfig(fp4.FMT_MXFP4, 128), cols=384) == E.FP4_ERR_INVALID_ARG  # cols % 128
+    assert _q(fp4.qconfig(fp4.FMT_NVFP4, 64)) == E.FP4_ERR_INVALID_ARG    # NV rotations are 16-point
+    assert _q(fp4.qconfig(fp4.FMT_MXFP4, 48)) == E.FP4_ERR_INVALID_ARG
+    assert _q(fp4.qconfig(fp4.FMT_NVFP4, rounding=2)) == E.FP4_ERR_INVALID_ARG
+    assert _q(fp4.qconfig(fp4.FMT_NVFP4, rounding=1, rule=fp4.SCALE_MSE)) == E.FP4_ERR_UNSUPPORTED
+    assert _q(fp4.qconfig(fp4.FMT_NVINT4, rounding=1)) == E.FP4_ERR_UNSUPPORTED
+    assert _q(fp4.qconfig(fp4.FMT_NVFP4, block_rows=8)) == E.FP4_ERR_INVALID_ARG
+    assert _q(fp4.qconfig(fp4.FMT_MXFP4, block_rows=16)) == E.FP4_ERR_UNSUPPORTED
+    assert _q(fp4.qconfig(fp4.FMT_NVFP4, True, block_rows=16)) == E.FP4_ERR_UNSUPPORTED
+    assert fp4.fp4_scales_bytes(fp4.qconfig(fp4.FMT_NVFP4, block_rows=16), 64, 256) == 64 * 16
+    assert fp4.fp4_scales_bytes(fp4.qconfig(fp4.FMT_MXFP4, 128, fp4.SCALES_GEMM, signs=5), 64, 256) == 512
+    assert ctypes.sizeof(fp4.QConfig) == 52
     # INT4-element formats: the MX / NV layouts, absmax scales only
     mxi = fp4.qconfig(fp4.FMT_MXINT4, scale_layout=fp4.SCALES_GEMM)
     nvi = fp4.qconfig(fp4.FMT_NVINT4)

@@ -612,3 +612,95 @@ def test_int4_quantize_then_gemm_end_to_end(fmt):
 @pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
 def test_gemm_w4a16_int4_weights(fmt, M, N, K):
     _check_w4a16(fmt, M, N, K, seed=M + N + K, out_dtype=torch.float32, nrows=min(M, 8), nent=256)
+
+
+# ------------------------------------------- rotation and rounding variants
+MASK = 0x0123456789ABCDEF0FEDCBA987654321
+ROTS = [(fp4.FMT_MXFP4, 32, MASK), (fp4.FMT_MXFP4, 64, 0), (fp4.FMT_MXFP4, 64, MASK),
+        (fp4.FMT_MXFP4, 128, 0), (fp4.FMT_MXFP4, 128, MASK), (fp4.FMT_NVFP4, 16, MASK),
+        (fp4.FMT_MXINT4, 128, MASK), (fp4.FMT_NVINT4, 16, MASK)]
+ROT_IDS = ["%s-h%d%s" % (FNAME[f], n, "-signed" if m else "") for f, n, m in ROTS]
+
+
+@pytest.mark.parametrize("case", ["cfg2_laplace", "ragged"])
+@pytest.mark.parametrize("fmt,n,mask", ROTS, ids=ROT_IDS)
+def test_quantize_rotation_variants(case, fmt, n, mask):
+    """Sign-randomised rotations and 64 / 128-point MX rotations (cross-lane
+    butterflies): codes within the rotated budget of the oracle's."""
+    say("quantize rotation", case, FNAME[fmt], n, hex(mask))
+    xh, xd = _inputs(case)
+    if xh.shape[1] % n:
+        pytest.skip("cols not a multiple of the rotation")
+    rc, rs, rts = oracle.quantize_spec(xh, fmt, rot_n=n, signs=mask)
+    lay = fp4.SCALES_GEMM if fmt in fp4.MX_FORMATS else fp4.SCALES_ROWMAJOR
+    for layout in ([lay, fp4.SCALES_ROWMAJOR] if lay == fp4.SCALES_GEMM else [lay]):
+        q = fp4.quantize(xd, fmt, rotate=n, scale_layout=layout, signs=mask)
+        torch.cuda.synchronize()
+        if fmt not in fp4.MX_FORMATS:
+            g = np.float32(q.global_scale.item())
+            assert abs(int(g.view(np.int32)) - int(np.float32(rts).view(np.int32))) <= 1, (g, rts)
+        if fmt in INT4:
+            assert_rotated_int4_close(codes_np(q), rc, rowmajor_scales_np(q), rs, what=case)
+        else:
+            assert_rotated_codes_close(codes_np(q), rc, rowmajor_scales_np(q), rs, what=case)
+    # back to the original domain: inverse rotation of the GPU's codes
+    gc, gs = codes_np(q), rowmajor_scales_np(q)
+    ts = np.float32(q.global_scale.item()) if fmt not in fp4.MX_FORMATS else np.float32(0)
+    ref = oracle.dequantize_rot(gc, gs, fmt, ts, rot_n=n, signs=mask)
+    yo = fp4.dequantize(q, inverse_rotate=True).cpu().numpy()
+    grp = np.abs(oracle.dequantize(gc, gs, fmt, ts)).reshape(ref.shape[0], -1, n).sum(-1)
+    atol = np.repeat(grp, n, axis=1) * 8 * 2.0 ** -24
+    assert np.all(np.abs(yo - ref) <= atol)
+    sums = fp4.error_sums(xd, q).cpu().numpy()
+    np.testing.assert_allclose(sums, oracle.error_sums(xh, ref), rtol=1e-5)
+
+
+SR_CASES = ["cfg1", "cfg2_gauss", "ragged", "tiny_rows", "tiny_scale"]
+
+
+@pytest.mark.parametrize("case", SR_CASES)
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_quantize_stochastic_rounding_bit_exact(case, fmt):
+    """Stochastic rounding, non-rotated: the Philox4x32-10 stream and every
+    rounding decision match the oracle bit for bit."""
+    say("quantize stochastic", case, FNAME[fmt])
+    xh, xd = _inputs(case)
+    seed = (0x12345678, 0x9ABCDEF0)
+    rc, rs, rts = oracle.quantize_spec(xh, fmt, rounding=oracle.ROUND_STOCHASTIC, seed=seed)
+    lays = [fp4.SCALES_GEMM, fp4.SCALES_ROWMAJOR] if fmt == fp4.FMT_MXFP4 else [fp4.SCALES_ROWMAJOR]
+    for lay in lays:
+        q = _prefill(fp4.quantize(xd, fmt, scale_layout=lay, rounding=fp4.ROUND_STOCHASTIC, seed=seed))
+        q = fp4.quantize(xd, fmt, scale_layout=lay, rounding=fp4.ROUND_STOCHASTIC, seed=seed, out=q)
+        torch.cuda.synchronize()
+        gc, gs = codes_np(q), rowmajor_scales_np(q)
+        assert np.array_equal(gs, rs), (case, lay)
+        bad = np.nonzero(gc != rc)
+        assert bad[0].size == 0, (case, lay, bad[0][:4], bad[1][:4], gc[bad][:4], rc[bad][:4])
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_quantize_stochastic_rounding_rotated(fmt):
+    say("quantize stochastic rotated", FNAME[fmt])
+    xh, xd = _inputs("cfg2_laplace")
+    seed = (7, 11)
+    rc, rs, _ = oracle.quantize_spec(xh, fmt, rot_n=fp4.BLOCK[fmt], signs=MASK,
+                                     rounding=oracle.ROUND_STOCHASTIC, seed=seed)
+    q = fp4.quantize(xd, fmt, rotate=True, signs=MASK, rounding=fp4.ROUND_STOCHASTIC, seed=seed)
+    torch.cuda.synchronize()
+    assert_rotated_codes_close(codes_np(q), rc, rowmajor_scales_np(q), rs, what="sr rot")
+
+
+@pytest.mark.parametrize("case", ["cfg1", "cfg2_gauss", "cfg2_laplace", "ragged", "tiny_rows", "tiny_scale"])
+@pytest.mark.parametrize("rnd", [0, 1], ids=["nearest", "stochastic"])
+def test_quantize_nvfp4_16x16_blocks(case, rnd):
+    """NVFP4 16x16 weight blocks: scale codes, element codes and the tensor scale
+    bit for bit (ragged row counts included)."""
+    say("quantize nvfp4 16x16", case, rnd)
+    xh, xd = _inputs(case)
+    rc, rs, rts = oracle.quantize_spec(xh, fp4.FMT_NVFP4, block_rows=16, rounding=rnd, seed=(3, 4))
+    q = _prefill(fp4.quantize(xd, fp4.FMT_NVFP4, block_rows=16, rounding=rnd, seed=(3, 4)))
+    q = fp4.quantize(xd, fp4.FMT_NVFP4, block_rows=16, rounding=rnd, seed=(3, 4), out=q)
+    torch.cuda.synchronize()
+    assert q.global_scale.item() == float(rts)
+    assert np.array_equal(rowmajor_scales_np(q), rs)
+    assert np.array_equal(codes_np(q), rc)
