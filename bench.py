@@ -267,62 +267,78 @@ def main():
     log("step %.3f ms (eager), %.3f ms (graph), %.1f GB/s; dominant %s %.2f us"
         % (1e3 * step_s, 1e3 * graph_s, value_gbs, dom, dk["avg_us"]))
 
-    # ------------------------------------------------- block-scale search
-    # The searching rules (MSE window, Four Over Six) on the same input: the
-    # quantize kernel alone (NVFP4 with its tensor scale given), per launch,
-    # and the reconstruction error against absmax.
+    # ------------------------------------- scale rules, formats and variants
+    # The other quantizer configurations on the same input: the searching
+    # rules (MSE window, Four Over Six), the INT4-element formats, 64/128-point
+    # MX rotations with a sign diagonal, stochastic rounding and NVFP4 16x16
+    # blocks.  The quantize kernel alone (NV formats with their tensor scale
+    # given), per launch, and the reconstruction error next to the FP4 format
+    # with the same layout and absmax scales, nearest rounding.
     search = {}
     if not args.no_search:
-        rules = [(fp4.FMT_MXFP4, fp4.SCALE_MSE, "mse"), (fp4.FMT_NVFP4, fp4.SCALE_MSE, "mse"),
-                 (fp4.FMT_NVFP4, fp4.SCALE_FOUR_OVER_SIX, "4over6"),
-                 (fp4.FMT_MXINT4, fp4.SCALE_ABSMAX, "absmax"), (fp4.FMT_NVINT4, fp4.SCALE_ABSMAX, "absmax")]
-        for fmt, rule, rname in rules:
-            for rot in (False, True):
-                lay = fp4.SCALES_GEMM if fmt in fp4.MX_FORMATS else fp4.SCALES_ROWMAJOR
-                cfg = fp4.qconfig(fmt, rot, lay, rule)
-                fp_twin = fp4.FMT_MXFP4 if fmt in fp4.MX_FORMATS else fp4.FMT_NVFP4
-                qs = []
-                for c in range(copies):
-                    base = outs[("gauss", fp_twin, rot)][c]
-                    qs.append(fp4.Quantized(torch.empty_like(base.codes), torch.empty_like(base.scales),
-                                            base.global_scale.clone(), cfg, rows, cols))
+        mask = 0x0123456789ABCDEF0FEDCBA987654321
+        variants_x = []   # (name, fmt, rot, qconfig keyword arguments)
+        for rot in (False, True):
+            tag = "h" if rot else "plain"
+            variants_x += [("mxfp4/mse/" + tag, fp4.FMT_MXFP4, rot, dict(rule=fp4.SCALE_MSE)),
+                           ("nvfp4/mse/" + tag, fp4.FMT_NVFP4, rot, dict(rule=fp4.SCALE_MSE)),
+                           ("nvfp4/4over6/" + tag, fp4.FMT_NVFP4, rot, dict(rule=fp4.SCALE_FOUR_OVER_SIX)),
+                           ("mxint4/absmax/" + tag, fp4.FMT_MXINT4, rot, {}),
+                           ("nvint4/absmax/" + tag, fp4.FMT_NVINT4, rot, {}),
+                           ("mxfp4/stochastic/" + tag, fp4.FMT_MXFP4, rot, dict(rounding=1, seed=(1, 2))),
+                           ("nvfp4/stochastic/" + tag, fp4.FMT_NVFP4, rot, dict(rounding=1, seed=(1, 2)))]
+        variants_x += [("mxfp4/h64-signed", fp4.FMT_MXFP4, 64, dict(signs=mask)),
+                       ("mxfp4/h128", fp4.FMT_MXFP4, 128, {}),
+                       ("mxfp4/h128-signed", fp4.FMT_MXFP4, 128, dict(signs=mask)),
+                       ("nvfp4/h16-signed", fp4.FMT_NVFP4, True, dict(signs=mask)),
+                       ("nvfp4/16x16-blocks", fp4.FMT_NVFP4, False, dict(block_rows=16))]
+        for name, fmt, rot, kw in variants_x:
+            lay = fp4.SCALES_GEMM if fmt in fp4.MX_FORMATS else fp4.SCALES_ROWMAJOR
+            cfg = fp4.qconfig(fmt, rot, lay, **kw)
+            twin_rot = rot is not False
+            fp_twin = fp4.FMT_MXFP4 if fmt in fp4.MX_FORMATS else fp4.FMT_NVFP4
+            qs = []
+            for c in range(copies):
+                base = outs[("gauss", fp_twin, twin_rot)][c]
+                qs.append(fp4.Quantized(torch.empty_like(base.codes), torch.empty_like(base.scales),
+                                        base.global_scale.clone(), cfg, rows, cols))
 
-                def qcall(c, d="gauss", qs=qs, fmt=fmt):
-                    q = qs[c]
-                    rc = fp4.fp4_quantize(q.cfg, xs[d][c].data_ptr(), fp4.DT_BF16, rows, cols, cols,
-                                          q.codes.data_ptr(), q.scales.data_ptr(),
-                                          q.global_scale.data_ptr(), fp4.GS_GIVEN, None, 0, sh_now())
-                    if rc != 0:
-                        raise RuntimeError("quantize failed: %d" % rc)
+            def qcall(c, d="gauss", qs=qs):
+                q = qs[c]
+                rc = fp4.fp4_quantize(q.cfg, xs[d][c].data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                      q.codes.data_ptr(), q.scales.data_ptr(),
+                                      q.global_scale.data_ptr(), fp4.GS_GIVEN, None, 0, sh_now())
+                if rc != 0:
+                    raise RuntimeError("quantize failed: %d" % rc)
 
-                if fmt == fp4.FMT_NVINT4:  # its own tensor scale (amax / 3136), set once
-                    for q_ in qs:
-                        fp4.global_scale(xs["gauss"][0], rotate=rot, out=q_.global_scale, fmt=fmt)
-                qcall(0)
-                torch.cuda.synchronize()
-                g = capture(lambda: [qcall(i % copies) for i in range(reps)])
-                g.replay()
-                torch.cuda.synchronize()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / reps
-                del g
-                ent = {"avg_us": round(us, 3), "gbs": round(alg_bytes(fmt) / (us * 1e-6) / 1e9, 1),
-                       "frac": round(alg_bytes(fmt) / (us * 1e-6) / PEAK_HBM, 4)}
-                for d in ("gauss", "laplace"):
-                    qd = fp4.quantize(xs[d][0], fmt, rotate=rot, scale_layout=lay, rule=rule)
-                    sd = fp4.error_sums(xs[d][0], qd).cpu().numpy()
-                    qa = outs[(d, fp_twin, rot)][0]
-                    sa = fp4.error_sums(xs[d][0], qa).cpu().numpy()
-                    ent["nmse_" + d] = float(sd[0] / sd[1])
-                    ent["nmse_absmax_" + d] = float(sa[0] / sa[1])
-                search["%s/%s/%s" % (FN[fmt], rname, "h%d" % fp4.BLOCK[fmt] if rot else "plain")] = ent
-                # nmse_absmax_*: the FP4 format with the same layout and absmax scales
-        log("scale search timings done")
+            if fmt not in fp4.MX_FORMATS:  # its own tensor scale, set once
+                for q_ in qs:
+                    fp4.global_scale(xs["gauss"][0], rotate=rot, out=q_.global_scale, fmt=fmt,
+                                     signs=kw.get("signs", 0))
+            qcall(0)
+            torch.cuda.synchronize()
+            g = capture(lambda: [qcall(i % copies) for i in range(reps)])
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            del g
+            ent = {"avg_us": round(us, 3), "gbs": round(alg_bytes(fmt) / (us * 1e-6) / 1e9, 1),
+                   "frac": round(alg_bytes(fmt) / (us * 1e-6) / PEAK_HBM, 4)}
+            for d in ("gauss", "laplace"):
+                qd = fp4.quantize(xs[d][0], fmt, rotate=rot, scale_layout=lay, **kw)
+                sd = fp4.error_sums(xs[d][0], qd).cpu().numpy()
+                qa = outs[(d, fp_twin, twin_rot)][0]
+                sa = fp4.error_sums(xs[d][0], qa).cpu().numpy()
+                ent["nmse_" + d] = float(sd[0] / sd[1])
+                ent["nmse_fp4_absmax_" + d] = float(sa[0] / sa[1])
+            search[name] = ent
+        log("variant timings done")
 
     # -------------------------------------------------------------- NMSE
     nmse = {}
@@ -393,7 +409,7 @@ def main():
                          "same kernels)" % reps,
         "cpu_baseline": cpu,
         "nmse": nmse,
-        "scale_search": search,
+        "quantizer_variants": search,
         "gemm": gemm,
     }
     print(json.dumps(line), flush=True)
