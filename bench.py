@@ -465,7 +465,7 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
         qa = fp4.quantize(a, fp4.FMT_MXFP4, rotate=True, scale_layout=fp4.SCALES_GEMM)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         wsb = fp4.fp4_gemm_workspace_bytes(fp4.FMT_MXFP4, M, N, K)
-        gw = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        gw = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
 
         def g(i=0):
             fp4.gemm(qa, qw[i % 2], out=y, workspace=gw if wsb else None)
@@ -511,7 +511,7 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
                 qa = fp4.quantize(a, fmt, rotate=True, scale_layout=fp4.SCALES_GEMM)
                 y = torch.empty(Mm, N, dtype=torch.bfloat16, device=dev)
                 wsb = fp4.fp4_gemm_workspace_bytes(fmt, Mm, N, K)
-                gw = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+                gw = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
 
                 def g(i=0):
                     fp4.gemm(qa, qw[i % 4], out=y, workspace=gw if wsb else None)
@@ -541,7 +541,7 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
                 if Mm <= 128:
                     # weight-only product: bf16 activations, the same FP4 weights
                     w4b = fp4.fp4_gemm_w4a16_workspace_bytes(fmt, Mm, N, K)
-                    w4w = torch.empty(max(w4b, 16), dtype=torch.uint8, device=dev)
+                    w4w = torch.zeros(max(w4b, 16), dtype=torch.uint8, device=dev)
 
                     def w4(i=0):
                         fp4.gemm_w4a16(a, qw[i % 4], out=y, workspace=w4w if w4b else None)

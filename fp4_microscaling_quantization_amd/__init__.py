@@ -248,6 +248,30 @@ def _scratch_workspace(nbytes: int, device):
     return t
 
 
+_gemm_ws_cache = {}
+
+
+def _gemm_workspace(nbytes: int, device):
+    """Per-device GEMM split-K workspace (fp32 partial sums; any contents),
+    grown to the largest size asked for and reused by every call on the
+    device, so calls that use it must not overlap (they do not on one
+    stream)."""
+    torch = _torch()
+    key = str(device)
+    t = _gemm_ws_cache.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _gemm_ws_cache[key] = t
+    return t
+
+
+def gemm_workspace(nbytes: int, device):
+    """A fresh GEMM workspace of nbytes (for callers that keep their own, e.g.
+    one per stream or per captured graph)."""
+    torch = _torch()
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
 @dataclass
 class Quantized:
     """Packed FP4 tensor: codes [rows, cols/2] u8, scales (layout of cfg) u8,
@@ -359,7 +383,7 @@ def gemm_w4a16(a, b: Quantized, out_dtype=None, out=None, workspace=None):
         out = torch.empty(M, N, dtype=out_dtype or torch.bfloat16, device=a.device)
     wsb = fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K)
     if workspace is None and wsb:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=a.device)
+        workspace = _gemm_workspace(wsb, a.device)
     rc = fp4_gemm_w4a16(fmt, M, N, K, a.data_ptr(), a.stride(0), b.codes.data_ptr(),
                         b.scales.data_ptr(), b.global_scale.data_ptr(), out.data_ptr(), _dt(out),
                         out.stride(0), _ptr(workspace), wsb if workspace is not None else 0,
@@ -378,7 +402,7 @@ def gemm(a: Quantized, b: Quantized, out_dtype=None, out=None, workspace=None):
         out = torch.empty(M, N, dtype=out_dtype or torch.bfloat16, device=a.codes.device)
     wsb = fp4_gemm_workspace_bytes(fmt, M, N, K)
     if workspace is None and wsb:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=a.codes.device)
+        workspace = _gemm_workspace(wsb, a.codes.device)
     rc = fp4_gemm(fmt, M, N, K, a.codes.data_ptr(), a.scales.data_ptr(),
                   a.global_scale.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
                   b.global_scale.data_ptr(), out.data_ptr(), _dt(out), out.stride(0),

@@ -42,7 +42,7 @@ def test_graph_replays_match_eager():
     wss = []
     for (f, _), y in zip(plans, ys):
         wsb = fp4.fp4_gemm_workspace_bytes(f, rows, n, cols)
-        wss.append(torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None)
+        wss.append(torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda") if wsb else None)
 
     def step():
         for i, (f, r) in enumerate(plans):
@@ -76,3 +76,54 @@ def test_graph_replays_match_eager():
         for i, (y0, y1) in enumerate(zip(ref_y, got_y)):
             assert np.array_equal(y0, y1), "replay %d plan %d GEMM output differs" % (rep, i)
     say("graph replays: 4 x identical to eager")
+
+
+def test_graph_split_k_decode_replays():
+    """Decode-shaped products split along K (partials in the workspace, then
+    the fixed-order reduction): MXFP4, NVFP4 and weight-only GEMMs recorded in
+    one graph, replayed with eager work between replays, every replay
+    identical to the eager result; a second graph on the same workspaces as
+    well."""
+    say("case: graph replay, split-K decode GEMMs (M = 1 and 16, N = 4096, K = 8192)")
+    K, n = 8192, 4096
+    w = to_dev_bf16(workloads.gemm_weight(n, K, seed=6))
+    a16 = to_dev_bf16(workloads.gemm_activation(16, K, seed=6))
+    calls = []
+    for f in (fp4.FMT_MXFP4, fp4.FMT_NVFP4):
+        qw = fp4.quantize(w, f, scale_layout=fp4.SCALES_GEMM)
+        for m in (1, 16):
+            a = a16[:m]
+            qa = fp4.quantize(a, f, scale_layout=fp4.SCALES_GEMM)
+            assert fp4.fp4_gemm_workspace_bytes(f, m, n, K) > 0
+            assert fp4.fp4_gemm_w4a16_workspace_bytes(f, m, n, K) > 0
+            y = torch.empty(m, n, dtype=torch.float32, device="cuda")
+            y4 = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+            ws = fp4.gemm_workspace(fp4.fp4_gemm_workspace_bytes(f, m, n, K), "cuda")
+            ws4 = fp4.gemm_workspace(fp4.fp4_gemm_w4a16_workspace_bytes(f, m, n, K), "cuda")
+            calls.append((lambda qa=qa, qw=qw, y=y, ws=ws: fp4.gemm(qa, qw, out=y, workspace=ws), y))
+            calls.append((lambda a=a, qw=qw, y4=y4, ws4=ws4: fp4.gemm_w4a16(a, qw, out=y4, workspace=ws4), y4))
+
+    def step():
+        for fn, _ in calls:
+            fn()
+
+    step()
+    torch.cuda.synchronize()
+    ref = [y.float().cpu().numpy().copy() for _, y in calls]
+    graphs = []
+    for _ in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        graphs.append(g)
+    for rep in range(6):
+        for _, y in calls:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graphs[rep % 2].replay()
+        torch.cuda.synchronize()
+        for i, (_, y) in enumerate(calls):
+            assert np.array_equal(y.float().cpu().numpy(), ref[i]), "replay %d call %d differs" % (rep, i)
+        step()  # eager calls on the same workspaces between replays
+        torch.cuda.synchronize()
+    say("split-K graph replays: 6 x identical to eager")
