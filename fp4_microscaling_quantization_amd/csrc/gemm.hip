@@ -1094,19 +1094,21 @@ __global__ __launch_bounds__(kThreads) void gemm_nv_kernel(
 }
 
 struct MxPlan {
-  int cfg;     // 0: 256x256, 8 waves (large M and N), 1: 128x128, 2: 32x256 (M <= 32)
+  int cfg;     // 0: 256x256, 8 waves (large M and N), 1: 128x128, 2: 32 x bn2 (M <= 32)
   int splits;  // split-K factor (1 = none)
   int kt_per;  // K-stages per split (even: slices start on a 256-K scale chunk)
 };
 
-MxPlan plan_mx(int64_t M, int64_t N, int64_t K) {
+// bn2: width of the M <= 32 tiles (MXFP4 128: measured 5-10 % faster at
+// decode than 256 with a 6-stage ring; the NVFP4 ring keeps 256).
+MxPlan plan_mx(int64_t M, int64_t N, int64_t K, int bn2 = 256) {
   MxPlan p{1, 1, (int)(K / 128)};
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (M <= 32) p.cfg = 2;
   else if (big_tiles >= 256) p.cfg = 0;
   else p.cfg = 1;
   const int bm = p.cfg == 0 ? 256 : (p.cfg == 1 ? 128 : 32);
-  const int bn = p.cfg == 1 ? 128 : 256;
+  const int bn = p.cfg == 1 ? 128 : (p.cfg == 2 ? bn2 : 256);
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int KT = (int)(K / 128);
   // Split K while fewer than 512 workgroups (two per CU) would run, keeping
@@ -1129,7 +1131,7 @@ MxPlan plan_mx(int64_t M, int64_t N, int64_t K) {
 namespace fp4lib {
 
 size_t gemm_mx_workspace(int64_t M, int64_t N, int64_t K) {
-  MxPlan p = plan_mx(M, N, K);
+  MxPlan p = plan_mx(M, N, K, 128);
   return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -1141,7 +1143,7 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
     zero_out_kernel<<<256, kThreads, 0, st>>>(y, ydt, (int)M, (int)N, ldy);
     return hipGetLastError();
   }
-  MxPlan p = plan_mx(M, N, K);
+  MxPlan p = plan_mx(M, N, K, 128);
   const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_mx_workspace(M, N, K);
   const int splits = split ? p.splits : 1;
   const int kt_per = split ? p.kt_per : (int)(K / 128);
@@ -1152,7 +1154,7 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   else if (p.cfg == 1)
     e = launch_mx_cfg<128, 128, 64, 64, 3>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
   else
-    e = launch_mx_cfg<32, 256, 32, 64, 3>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_mx_cfg<32, 128, 32, 32, 6>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, nullptr, nullptr, st);
 }
