@@ -153,7 +153,10 @@ def main():
             gs = torch.zeros(1, dtype=torch.float32, device=dev)
             lst.append(fp4.Quantized(codes, scales, gs, cfg, rows, cols))
         outs[v] = lst
-    ws = torch.zeros(2048, dtype=torch.uint8, device=dev)
+    # NVFP4 workspace: amax-pass partials, then the single-pass exchange
+    # region (zero before its first use)
+    wsb = fp4.fp4_workspace_bytes(fp4.qconfig(fp4.FMT_NVFP4), rows, cols)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
 
     def alg_bytes(fmt):
         G = fp4.BLOCK[fmt]
@@ -161,7 +164,8 @@ def main():
 
     def call(v, c, mode):
         """One C-ABI call of variant v on buffer copy c.  mode 'step' is the
-        production path (NVFP4 computes its tensor scale: amax pass + quantize);
+        production path (NVFP4 computes its tensor scale and encodes in one
+        launch); 'two_pass' the same with the amax pass and the quantize pass;
         'amax' runs only the NVFP4 tensor-scale pass; 'given' only the NVFP4
         quantize kernel with the tensor scale already in place."""
         d, fmt, rot = v
@@ -173,19 +177,22 @@ def main():
                                   None, 0, sh_now())
         elif mode == "amax":
             rc = fp4.fp4_global_scale(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
-                                      q.global_scale.data_ptr(), ws.data_ptr(), 2048, sh_now())
+                                      q.global_scale.data_ptr(), ws.data_ptr(), wsb, sh_now())
         else:
+            gs_mode = {"given": fp4.GS_GIVEN, "two_pass": fp4.GS_COMPUTE}.get(
+                mode, fp4.GS_COMPUTE_ONE_PASS)
             rc = fp4.fp4_quantize(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
                                   q.codes.data_ptr(), q.scales.data_ptr(),
-                                  q.global_scale.data_ptr(),
-                                  fp4.GS_GIVEN if mode == "given" else fp4.GS_COMPUTE,
-                                  ws.data_ptr(), 2048, sh_now())
+                                  q.global_scale.data_ptr(), gs_mode, ws.data_ptr(), wsb, sh_now())
         if rc != 0:
             raise RuntimeError("quantize failed: %d" % rc)
 
-    def run_step(c):
+    def run_step(c, mode="step"):
         for v in variants:
-            call(v, c, "step")
+            call(v, c, mode)
+
+    one_pass = all(fp4.fp4_quantize_one_pass_fits(outs[v][0].cfg, fp4.DT_BF16, rows, cols, cols)
+                   for v in variants if v[1] == fp4.FMT_NVFP4)
 
     def capture(fn):
         # the step's kernels recorded once; replays launch them with no host work
@@ -224,6 +231,15 @@ def main():
     step_s_events = ev0.elapsed_time(ev1) * 1e-3 / max(1, args.steps)
     step_bytes = sum(alg_bytes(v[1]) for v in variants)
     value_gbs = step_bytes / step_s / 1e9
+    # the same step with the NVFP4 tensor scale from a separate amax pass
+    for w in range(args.warmup):
+        run_step(w % copies, "two_pass")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s_ in range(args.steps):
+        run_step(s_ % copies, "two_pass")
+    torch.cuda.synchronize()
+    two_pass_s = (time.perf_counter() - t_start) / max(1, args.steps)
 
     # Per-kernel launch durations, live: a graph of back-to-back launches of
     # one kernel over the rotating buffer copies, replayed between one pair of
@@ -237,11 +253,13 @@ def main():
         v = (d, fmt, rot)
         tag = "rot" if rot else "plain"
         if fmt == fp4.FMT_MXFP4:
-            parts = [("quant_mx_gemm_kernel<%s>" % tag, "step", alg_bytes(fmt))]
+            parts = [("quant_mx_gemm_kernel<%s>" % tag, "step", alg_bytes(fmt), True)]
         else:
-            parts = [("amax_chunk_kernel<%s> + amax_final_kernel" % tag, "amax", n * 2),
-                     ("quant_rows_kernel<nvfp4,%s,2>" % tag, "given", alg_bytes(fmt))]
-        for label, mode, nbytes in parts:
+            # the step's single launch, then the two passes it replaces
+            parts = [("quant_nv_fused_kernel<nvfp4,%s,4>" % tag, "step", alg_bytes(fmt), one_pass),
+                     ("amax_chunk_kernel<%s>" % tag, "amax", n * 2, not one_pass),
+                     ("quant_rows_kernel<nvfp4,%s,2>" % tag, "given", alg_bytes(fmt), not one_pass)]
+        for label, mode, nbytes, in_step in parts:
             call(v, 0, mode)
             torch.cuda.synchronize()
             g = capture(lambda: [call(v, i % copies, mode) for i in range(reps)])
@@ -255,9 +273,9 @@ def main():
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / reps
             kern[label] = {"avg_us": us, "alg_bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
-                           "launches": reps}
+                           "launches": reps, "in_step": in_step}
             del g
-    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    dom = max((k for k in kern if kern[k]["in_step"]), key=lambda k: kern[k]["avg_us"])
     dk = kern[dom]
     traffic, traffic_note = measured_traffic(dom.split(" + ")[0])
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dk["gbs"], 1),
@@ -391,19 +409,23 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * step_s, 4),
         "ms_per_step_events": round(1e3 * step_s_events, 4),
         "ms_per_step_graph": round(1e3 * graph_s, 4),
-        "launch": "eager: 12 kernel launches per step through the C ABI (ms_per_step_graph: the "
-                  "same step as one replayed HIP graph)",
+        "ms_per_step_two_pass": round(1e3 * two_pass_s, 4),
+        "launch": ("eager: %d kernel launches per step through the C ABI (NVFP4: tensor amax and "
+                   "encoding in one launch; ms_per_step_two_pass: with a separate amax pass; "
+                   "ms_per_step_graph: the step as one replayed HIP graph)"
+                   % (len(variants) if one_pass else len(variants) + 4)),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "quantize 4096x4096 bf16 x {Gaussian 0.02, Laplace 0.02 + 16/4096 "
-                               "cols x50} x {MXFP4 G32, NVFP4 G16 (+global amax pass)} x {plain, "
+                               "cols x50} x {MXFP4 G32, NVFP4 G16 (tensor amax in the same launch)} x {plain, "
                                "block Hadamard 32/16}", "rows": rows, "cols": cols,
                    "variants": len(variants), "buffer_copies": copies,
                    "step_alg_bytes": step_bytes},
         "frac_hbm_step": round(value_gbs * 1e9 / PEAK_HBM, 4),
         "roofline": roofline,
         "kernels": {k: {"avg_us": round(v["avg_us"], 3), "gbs": round(v["gbs"], 1),
-                        "frac": round(v["gbs"] * 1e9 / PEAK_HBM, 4)} for k, v in sorted(kern.items())},
+                        "frac": round(v["gbs"] * 1e9 / PEAK_HBM, 4), "in_step": v["in_step"]}
+                    for k, v in sorted(kern.items())},
         "kernel_timing": "per-kernel: a HIP graph of %d back-to-back launches over rotating copies, "
                          "replayed between one HIP event pair (Gaussian input; both inputs run the "
                          "same kernels)" % reps,

@@ -37,6 +37,7 @@ SCALES_ROWMAJOR = 0
 SCALES_GEMM = 1
 GS_COMPUTE = 0
 GS_GIVEN = 1
+GS_COMPUTE_ONE_PASS = 2
 SCALE_ABSMAX = 0
 SCALE_MSE = 1
 SCALE_FOUR_OVER_SIX = 2
@@ -47,7 +48,7 @@ MX_FORMATS = (FMT_MXFP4, FMT_MXINT4)
 
 EXPORTED = [
     "fp4_codes_bytes", "fp4_scales_bytes", "fp4_workspace_bytes", "fp4_scale_offset",
-    "fp4_quantize", "fp4_global_scale", "fp4_dequantize", "fp4_error_workspace_bytes", "fp4_error_sums",
+    "fp4_quantize", "fp4_quantize_one_pass_fits", "fp4_global_scale", "fp4_dequantize", "fp4_error_workspace_bytes", "fp4_error_sums",
     "fp4_scales_to_gemm_layout", "fp4_gemm_workspace_bytes", "fp4_gemm",
     "fp4_gemm_w4a16_workspace_bytes", "fp4_gemm_w4a16", "fp4_status_str", "fp4_abi_version",
 ]
@@ -104,6 +105,8 @@ def lib():
         L.fp4_scale_offset.argtypes = [CP, I64, I64, I64, I64]
         L.fp4_quantize.restype = ctypes.c_int
         L.fp4_quantize.argtypes = [CP, P, I32, I64, I64, I64, P, P, P, I32, P, SZ, P]
+        L.fp4_quantize_one_pass_fits.restype = ctypes.c_int
+        L.fp4_quantize_one_pass_fits.argtypes = [CP, I32, I64, I64, I64]
         L.fp4_global_scale.restype = ctypes.c_int
         L.fp4_global_scale.argtypes = [CP, P, I32, I64, I64, I64, P, P, SZ, P]
         L.fp4_dequantize.restype = ctypes.c_int
@@ -171,6 +174,10 @@ def fp4_quantize(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, gs_m
                               global_scale, gs_mode, ws, ws_bytes, stream)
 
 
+def fp4_quantize_one_pass_fits(cfg, xdt, rows, cols, ldx) -> int:
+    return lib().fp4_quantize_one_pass_fits(ctypes.byref(cfg), xdt, rows, cols, ldx)
+
+
 def fp4_global_scale(cfg, x, xdt, rows, cols, ldx, global_scale, ws, ws_bytes, stream) -> int:
     return lib().fp4_global_scale(ctypes.byref(cfg), x, xdt, rows, cols, ldx, global_scale, ws,
                                   ws_bytes, stream)
@@ -236,9 +243,10 @@ _ws_cache: dict = {}
 
 
 def _scratch_workspace(nbytes: int, device):
-    """Per-device scratch for the NVFP4 global-amax pass (partial maxima; any
-    contents).  One buffer per device and size is reused by every call, so
-    calls that use it must not overlap in time (they do not on one stream)."""
+    """Per-device scratch for the NVFP4 global-amax pass (partial maxima) and
+    the single-pass exchange region (zero when allocated, left ready by every
+    call).  One buffer per device and size is reused by every call, so calls
+    that use it must not overlap in time (they do not on one stream)."""
     torch = _torch()
     key = (str(device), nbytes)
     t = _ws_cache.get(key)
@@ -287,11 +295,13 @@ class Quantized:
 def quantize(x, fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
              global_scale=None, out: Quantized | None = None,
              rule: int = SCALE_ABSMAX, rounding: int = ROUND_NEAREST, block_rows: int = 1,
-             signs: int = 0, seed=(0, 0)) -> Quantized:
+             signs: int = 0, seed=(0, 0), one_pass: bool = False) -> Quantized:
     """Quantize a 2-D CUDA tensor (fp32 or bf16, unit stride along the last
     axis).  NVFP4: ``global_scale`` (a float32[1] CUDA tensor) is used as given
-    when passed, otherwise computed from the tensor's amax.  ``rule`` selects
-    the block-scale rule (SCALE_ABSMAX, SCALE_MSE, SCALE_FOUR_OVER_SIX)."""
+    when passed, otherwise computed from the tensor's amax (``one_pass``: the
+    amax and the encoding in one launch when the tensor fits, the same
+    results).  ``rule`` selects the block-scale rule (SCALE_ABSMAX, SCALE_MSE,
+    SCALE_FOUR_OVER_SIX)."""
     torch = _torch()
     assert x.dim() == 2 and x.stride(1) == 1
     rows, cols = x.shape
@@ -302,7 +312,7 @@ def quantize(x, fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
                              device=x.device)
         gs = torch.zeros(1, dtype=torch.float32, device=x.device)
         out = Quantized(codes, scales, gs, cfg, rows, cols)
-    gs_mode = GS_COMPUTE
+    gs_mode = GS_COMPUTE_ONE_PASS if one_pass else GS_COMPUTE
     if fmt not in MX_FORMATS and global_scale is not None:
         out.global_scale.copy_(global_scale.reshape(1))
         gs_mode = GS_GIVEN

@@ -84,8 +84,12 @@ bool gemm_layout(const fp4_qconfig* cfg) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
 
-// NVFP4 workspace: one fp32 partial maximum per workgroup of the amax pass.
-constexpr size_t kNvWorkspace = 2048;
+// NVFP4 workspace: bytes [0, 2048) one fp32 partial maximum per workgroup of
+// the amax pass (any contents); bytes [4096, 8192) the exchange region of the
+// single-pass kernel (a call number, then one 64-bit slot per workgroup).
+constexpr size_t kNvWorkspace = 8192;
+constexpr size_t kNvExchange = 4096;
+constexpr int kNvExchangeSlots = (int)((kNvWorkspace - kNvExchange - 64) / 8);
 
 }  // namespace
 
@@ -148,14 +152,23 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
                                                  cfg->rounding, rows, cols, ldx, codes, scales,
                                                  gemm_layout(cfg) ? 1 : 0, qparams(cfg, cols), st));
   }
-  if (gs_mode != FP4_GS_COMPUTE && gs_mode != FP4_GS_GIVEN) return FP4_ERR_INVALID_ARG;
+  if (gs_mode != FP4_GS_COMPUTE && gs_mode != FP4_GS_GIVEN && gs_mode != FP4_GS_COMPUTE_ONE_PASS)
+    return FP4_ERR_INVALID_ARG;
   if (!global_scale) return FP4_ERR_INVALID_ARG;
   float* partials = nullptr;
   int npart = 0;
-  if (gs_mode == FP4_GS_COMPUTE) {
+  if (gs_mode != FP4_GS_GIVEN) {
     if (!ws || ws_bytes < fp4_workspace_bytes(cfg, rows, cols)) return FP4_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
+    const uintptr_t amask = gs_mode == FP4_GS_COMPUTE_ONE_PASS ? 7u : 3u;  // 64-bit slots
+    if ((reinterpret_cast<uintptr_t>(ws) & amask) != 0) return FP4_ERR_ALIGNMENT;
     if (empty) return hip_status(fp4lib::launch_amax_final(cfg->fmt, nullptr, 0, global_scale, st));
+    if (gs_mode == FP4_GS_COMPUTE_ONE_PASS) {
+      uint32_t* xchg = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kNvExchange);
+      const hipError_t e = fp4lib::launch_quantize_nv_one_pass(
+          cfg->fmt, x, xdt, cfg->rotate != 0, cfg->rule, cfg->rounding, cfg->block_rows, rows, cols,
+          ldx, codes, scales, global_scale, xchg, kNvExchangeSlots, qparams(cfg, cols), st);
+      if (e != hipErrorNotSupported) return hip_status(e);
+    }
     partials = static_cast<float*>(ws);
     npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0, xdt);
     hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, qparams(cfg, cols).signs[0],
@@ -167,6 +180,12 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
                                                cfg->rounding, cfg->block_rows, rows, cols, ldx,
                                                codes, scales, global_scale, partials, npart,
                                                qparams(cfg, cols), st));
+}
+
+int fp4_quantize_one_pass_fits(const fp4_qconfig* cfg, int32_t xdt, int64_t rows, int64_t cols,
+                               int64_t ldx) {
+  if (check_cfg(cfg, rows, cols) != FP4_OK || fp4k::fmt_mx(cfg->fmt) || ldx < cols) return 0;
+  return fp4lib::quantize_nv_one_pass_tpw(xdt, cfg->block_rows, rows, cols, ldx, kNvExchangeSlots) != 0;
 }
 
 int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows,

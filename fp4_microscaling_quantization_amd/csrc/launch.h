@@ -21,6 +21,18 @@ hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int r
                               int block_rows, int64_t rows, int64_t cols, int64_t ldx,
                               uint8_t* codes, uint8_t* scales, float* gs, const float* partials,
                               int npart, const fp4k::QParams& P, hipStream_t st);
+// Single pass (tensor maximum and encoding in one launch); hipErrorNotSupported
+// (nothing launched) when the shape or configuration does not fit it.
+// xchg: the exchange region (zero before its first use), max_grid slots.
+// quantize_nv_one_pass_tpw: wave tiles per wave the single pass would use
+// (4 or 8), 0 when it does not apply.
+int quantize_nv_one_pass_tpw(int xdt, int block_rows, int64_t rows, int64_t cols, int64_t ldx,
+                             int max_grid);
+hipError_t launch_quantize_nv_one_pass(int fmt, const void* x, int xdt, int rotate, int rule,
+                                       int rounding, int block_rows, int64_t rows, int64_t cols,
+                                       int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
+                                       uint32_t* xchg, int max_grid, const fp4k::QParams& P,
+                                       hipStream_t st);
 hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
                                  hipStream_t st);
 

@@ -29,6 +29,7 @@
 // reduces those partials in its prologue.
 #include "fp4_device.h"
 #include "launch.h"
+#include <atomic>
 
 using namespace fp4k;
 
@@ -200,14 +201,16 @@ __device__ __forceinline__ uint32_t nv_scale(float amax, const NvTs& T, float& s
 // Eight values of an NVFP4 block -> one dword of codes, q = fl32(v / s)
 // rounded to E2M1 (v is overwritten).  For normal scales the quotients are
 // formed negated and the eight sign bits flipped afterwards.
+// nv_enc8_rs: the normal-scale case (s >= 2^-100) with rs = fl32(1 / s) given.
+__device__ __forceinline__ uint32_t nv_enc8_rs(float* v, float s, float rs) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = neg_div_rn(v[i], s, rs);
+  return enc8_f32(v, 1.0f) ^ 0x88888888u;  // scale operand 2^0: the quotient is exact
+}
+
 __device__ __forceinline__ uint32_t nv_enc8(float* v, float s) {
   if (s == 0.0f) return 0u;
-  if (s >= 0x1p-100f) {
-    const float rs = 1.0f / s;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = neg_div_rn(v[i], s, rs);
-    return enc8_f32(v, 1.0f) ^ 0x88888888u;  // scale operand 2^0: the quotient is exact
-  }
+  if (s >= 0x1p-100f) return nv_enc8_rs(v, s, 1.0f / s);
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = v[i] / s;
   return enc8_f32(v, 1.0f);
@@ -286,6 +289,27 @@ __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   if (fold) amax *= 0.25f;
+  if constexpr (RND == 0) {
+    // The common case with no branches: when every lane of the wave has a
+    // normal block maximum, quotient and E4M3 block scale and a divisor of at
+    // least 2^-100, the steps of nv_scale and nv_enc8 below reduce to these
+    // (same operations, same results), with one reciprocal per block.
+    const float h = div_rn(amax, 6.0f, 0x1.555556p-3f);
+    const float t = fminf(div_rn(h, T.ts, T.inv_ts), 448.0f);
+    uint32_t u = as_u(t);
+    u += 0x7FFFFu + ((u >> 20) & 1u);
+    const uint32_t code = (u >> 20) - (120u << 3);
+    const float s = as_f((((code >> 3) + 120u) << 23) | ((code & 7u) << 20)) * T.ts;
+    const float d = fold ? 4.0f * s : s;
+    const bool fast = T.live && !T.small && amax >= 0x1p-100f && h >= 0x1p-100f &&
+                      t >= 0x1p-6f && d >= 0x1p-100f;
+    if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+      const float rd = 1.0f / d;
+      out[0] = nv_enc8_rs(&v[0], d, rd);
+      out[1] = nv_enc8_rs(&v[8], d, rd);
+      return code;
+    }
+  }
   float s;
   const uint32_t code = nv_scale(amax, T, s);
   const float d = fold ? 4.0f * s : s;
@@ -657,6 +681,154 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     t0 += step;
     if (t0 >= tiles) break;
     load(t0);
+  }
+}
+
+// NVFP4 / NVINT4 with the tensor scale computed in the same launch, for a
+// tensor small enough to sit in the registers of one co-resident grid.  Each
+// wave loads all of its wave tiles (tile gw + u * waves for u < TPW), moves
+// them into per-lane blocks through its LDS buffer and takes the maximum of
+// the block values (rotated with ROT, as the encoder rotates them); the
+// workgroups exchange their maxima; then every workgroup encodes its tiles
+// from registers.  The input crosses HBM once instead of twice (maximum
+// pass, then encode pass).
+//
+// Exchange: xchg[0] is a call number E - 1, then (from xchg + 16) one 64-bit
+// slot per workgroup.  A workgroup reads E at its start, stores (E, its
+// maximum) to its slot in one single-copy-atomic 64-bit store, and polls all
+// slots until each carries E; the values are then this call's maxima, so no
+// other ordering is needed.  Workgroup 0 finally stores E to xchg[0].  The
+// region must be zero before its first use (later calls find it as the last
+// call left it).  The host caps the grid at one workgroup per CU, so the
+// whole grid is resident at once when no other grid-synchronising kernel
+// shares the device.  A wait that outlasts its bound (seconds) gives up: that
+// workgroup encodes with a NaN tensor scale (all-zero codes) and stores NaN
+// to *gs; the region then needs zeroing again.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / 64;
+constexpr int kMaxDevices = 64;
+constexpr uint32_t kExchangeSpin = 1u << 22;
+
+template <int FMT, int ROT, int TPW, int RULE, int RND>
+__global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
+    const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t wpr,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gs,
+    uint32_t* __restrict__ xchg, QParams P) {
+  constexpr int CH = 2;            // 16-byte chunks of a 16-element bf16 block
+  constexpr int STRIDE = 32 + 16;  // padded LDS stride
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFusedWaves][64 * STRIDE];
+  __shared__ float red[kFusedWaves];
+  __shared__ float ts_shared;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t tiles = rows * wpr;
+  const uint32_t waves = gridDim.x * kFusedWaves;
+  const uint32_t gw = blockIdx.x * kFusedWaves + wave;
+  const uint32_t last_chunk = nb * CH - 1;
+  uint64_t* slots = reinterpret_cast<uint64_t*>(xchg + 16);
+  uint8_t* l = lds[wave];
+
+  uint32_t E = 0;
+  if (wave == 0) E = __hip_atomic_load(&xchg[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  u32x4 c[TPW][CH];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const uint32_t tile = min(gw + u * waves, tiles - 1);
+    const uint32_t r = tile / wpr, w = tile - r * wpr;
+    const uint8_t* row = x + (int64_t)r * ldx_bytes;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      c[u][j] = load_nt16(row + (int64_t)min(w * 64 * CH + j * 64 + lane, last_chunk) * 16);
+  }
+  // Maximum over the wave's blocks.  Tiles past the end re-read the last
+  // tile, which leaves the maximum unchanged; lanes past the row end hold
+  // re-read chunks, not blocks of the tensor, and are left out.  Plain: the
+  // largest magnitude's bf16 bits, as the separate maximum pass takes it.
+  uint32_t mb = 0;
+  float mf = 0.0f;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int q = j * 64 + lane;
+      *reinterpret_cast<u32x4*>(l + (q / CH) * STRIDE + (q % CH) * 16) = c[u][j];
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < CH; ++k) c[u][k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
+    wave_lds_sync();
+    const uint32_t tile = min(gw + u * waves, tiles - 1);
+    if ((tile - (tile / wpr) * wpr) * 64 + lane >= nb) continue;
+    if constexpr (ROT == 0) {
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        u16x2 m = __builtin_bit_cast(u16x2, c[u][k][0] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int e = 1; e < 4; ++e)
+          m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, c[u][k][e] & 0x7FFF7FFFu));
+        mb = max(mb, (uint32_t)max(m[0], m[1]));
+      }
+    } else {
+      float v[16];
+      unpack<FP4_DT_BF16, 16>(c[u], v);
+      if (P.any_sign) apply_signs<16>(v, P.signs[0]);
+      fwht<16>(v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mf = fmaxf(mf, fabsf(v[i]));
+    }
+  }
+  float m = ROT ? mf : as_f(mb << 16);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+
+  if (wave == 0) {
+    float wm = red[0];
+#pragma unroll
+    for (int i = 1; i < kFusedWaves; ++i) wm = fmaxf(wm, red[i]);
+    if (ROT) wm *= 0.25f;  // 1/sqrt(16), exact
+    if (lane == 0)
+      __hip_atomic_store(&slots[blockIdx.x], ((uint64_t)E << 32) | __builtin_bit_cast(uint32_t, wm),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+    float t = 0.0f;
+    for (uint32_t n = 0;; ++n) {
+      bool mine = true;
+      t = 0.0f;
+      for (uint32_t i = lane; i < gridDim.x; i += 64) {
+        const uint64_t v = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mine &= (uint32_t)(v >> 32) == E;
+        t = fmaxf(t, __builtin_bit_cast(float, (uint32_t)v));
+      }
+      if (__builtin_amdgcn_ballot_w64(!mine) == 0) break;
+      if (n == kExchangeSpin) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) t = fmaxf(t, __shfl_xor(t, off, 64));
+    const float ts = ok ? t / (448.0f * fmt_qmax(FMT)) : __builtin_nanf("");
+    if (lane == 0) {
+      ts_shared = ts;
+      if (blockIdx.x == 0 || !ok) *gs = ts;
+      if (blockIdx.x == 0) __hip_atomic_store(&xchg[0], E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  const NvTs T = make_ts(ts_shared);
+
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const uint32_t tile = gw + u * waves;
+    if (tile >= tiles) break;
+    const uint32_t r = tile / wpr, w = tile - r * wpr;
+    const uint32_t kb = w * 64 + lane;
+    u32x4 out;
+    const uint32_t code = compute_block<FMT, FP4_DT_BF16, ROT, RULE, RND>(c[u], T, out, r, kb, P);
+    if (kb < nb) store_block<FMT>(out, code, r, kb, nb, codes, scales, 0, 0);
   }
 }
 
@@ -1098,6 +1270,76 @@ hipError_t launch_amax_final(int fmt, const float* partials, int npart, float* g
     amax_final_kernel<<<1, kThreads, 0, st>>>(partials, npart, gs, 448.0f * fmt_qmax(fmt));
   }
   return hipGetLastError();
+}
+
+// CU count of the current device (queried once per device); 0 on failure.
+int device_cus() {
+  static std::atomic<int> cus_of[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cus = cus_of[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus_of[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+
+template <int FMT, int ROT, int RULE, int RND>
+hipError_t fused_launch(int tpw, const uint8_t* x, int64_t rows, int64_t ldx_bytes, uint32_t nb,
+                        uint32_t wpr, uint8_t* codes, uint8_t* scales, float* gs, uint32_t* xchg,
+                        const QParams& P, hipStream_t st) {
+  const int64_t tiles = rows * (int64_t)wpr;
+  const int64_t grid = (tiles + (int64_t)kFusedWaves * tpw - 1) / ((int64_t)kFusedWaves * tpw);
+  if (tpw == 4)
+    quant_nv_fused_kernel<FMT, ROT, 4, RULE, RND><<<(unsigned)grid, kFusedThreads, 0, st>>>(
+        x, ldx_bytes, (uint32_t)rows, nb, wpr, codes, scales, gs, xchg, P);
+  else
+    quant_nv_fused_kernel<FMT, ROT, 8, RULE, RND><<<(unsigned)grid, kFusedThreads, 0, st>>>(
+        x, ldx_bytes, (uint32_t)rows, nb, wpr, codes, scales, gs, xchg, P);
+  return hipGetLastError();
+}
+
+template <int FMT, int RULE, int RND>
+hipError_t fused_rule(int tpw, const uint8_t* x, int rotate, int64_t rows, int64_t ldx_bytes,
+                      uint32_t nb, uint32_t wpr, uint8_t* codes, uint8_t* scales, float* gs,
+                      uint32_t* xchg, const QParams& P, hipStream_t st) {
+  if (rotate)
+    return fused_launch<FMT, 1, RULE, RND>(tpw, x, rows, ldx_bytes, nb, wpr, codes, scales, gs, xchg, P, st);
+  return fused_launch<FMT, 0, RULE, RND>(tpw, x, rows, ldx_bytes, nb, wpr, codes, scales, gs, xchg, P, st);
+}
+
+int quantize_nv_one_pass_tpw(int xdt, int block_rows, int64_t rows, int64_t cols, int64_t ldx,
+                             int max_grid) {
+  if (xdt != FP4_DT_BF16 || block_rows == 16 || rows <= 0 || cols <= 0 || (ldx * 2) % 16 != 0)
+    return 0;
+  const int cus = device_cus();
+  const int64_t cap = cus < max_grid ? cus : max_grid;  // one workgroup per CU
+  const int64_t tiles = rows * ((cols / 16 + 63) / 64);
+  for (int tpw = 4; tpw <= 8; tpw *= 2)
+    if ((tiles + (int64_t)kFusedWaves * tpw - 1) / ((int64_t)kFusedWaves * tpw) <= cap) return tpw;
+  return 0;
+}
+
+hipError_t launch_quantize_nv_one_pass(int fmt, const void* x, int xdt, int rotate, int rule,
+                                       int rounding, int block_rows, int64_t rows, int64_t cols,
+                                       int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
+                                       uint32_t* xchg, int max_grid, const QParams& P,
+                                       hipStream_t st) {
+  const int tpw = quantize_nv_one_pass_tpw(xdt, block_rows, rows, cols, ldx, max_grid);
+  if (tpw == 0) return hipErrorNotSupported;
+  const uint32_t nb = (uint32_t)(cols / 16), wpr = (nb + 63) / 64;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  const int64_t lb = ldx * 2;
+  if (fmt == FP4_FMT_NVINT4)
+    return fused_rule<FP4_FMT_NVINT4, FP4_SCALE_ABSMAX, 0>(tpw, xb, rotate, rows, lb, nb, wpr, codes, scales, gs, xchg, P, st);
+  if (rounding != 0)
+    return fused_rule<FP4_FMT_NVFP4, FP4_SCALE_ABSMAX, 1>(tpw, xb, rotate, rows, lb, nb, wpr, codes, scales, gs, xchg, P, st);
+  if (rule == FP4_SCALE_MSE)
+    return fused_rule<FP4_FMT_NVFP4, FP4_SCALE_MSE, 0>(tpw, xb, rotate, rows, lb, nb, wpr, codes, scales, gs, xchg, P, st);
+  if (rule == FP4_SCALE_FOUR_OVER_SIX)
+    return fused_rule<FP4_FMT_NVFP4, FP4_SCALE_FOUR_OVER_SIX, 0>(tpw, xb, rotate, rows, lb, nb, wpr, codes, scales, gs, xchg, P, st);
+  return fused_rule<FP4_FMT_NVFP4, FP4_SCALE_ABSMAX, 0>(tpw, xb, rotate, rows, lb, nb, wpr, codes, scales, gs, xchg, P, st);
 }
 
 hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int rule, int rounding,

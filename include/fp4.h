@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP4_ABI_VERSION 2
+#define FP4_ABI_VERSION 3
 
 typedef enum {
     FP4_OK = 0,
@@ -82,7 +82,11 @@ typedef enum {
 } fp4_scale_rule;
 typedef enum { FP4_DT_F32 = 0, FP4_DT_BF16 = 1 } fp4_dtype;
 typedef enum { FP4_SCALES_ROWMAJOR = 0, FP4_SCALES_GEMM = 1 } fp4_scale_layout;
-typedef enum { FP4_GS_COMPUTE = 0, FP4_GS_GIVEN = 1 } fp4_gs_mode;
+typedef enum {
+    FP4_GS_COMPUTE = 0,          /* tensor scale from the tensor: maximum pass, then encode */
+    FP4_GS_GIVEN = 1,            /* tensor scale read from *global_scale */
+    FP4_GS_COMPUTE_ONE_PASS = 2  /* as FP4_GS_COMPUTE, both in one launch when it fits */
+} fp4_gs_mode;
 
 /* Quantization configuration (host struct).
  *   fmt           fp4_format.
@@ -161,9 +165,10 @@ size_t fp4_codes_bytes(int64_t rows, int64_t cols);
  * with the codes ("NVFP4 vs MXFP4", storage overhead).  Host function. */
 size_t fp4_scales_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
 
-/* Workspace bytes fp4_quantize and fp4_global_scale need (NVFP4: 2048 bytes,
- * holding the partial maxima of the global-amax pass; MXFP4: 0).  Host
- * function. */
+/* Workspace bytes fp4_quantize and fp4_global_scale need (NVFP4 and NVINT4:
+ * 8192 bytes; MXFP4 and MXINT4: 0).  Bytes [0, 2048) hold the partial maxima
+ * of the global-amax pass (any contents); bytes [4096, 8192) are the exchange
+ * region of FP4_GS_COMPUTE_ONE_PASS (see fp4_quantize).  Host function. */
 size_t fp4_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
 
 /* Byte index inside the scale array of the scale of (row r, block kb), for the
@@ -179,9 +184,22 @@ int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols,
  *   [rows, cols] tensor (x' = the rotated tensor when rotate != 0) and writes
  *   it to *global_scale; FP4_GS_GIVEN reads ts from *global_scale.  A block
  *   whose scale (e4m3 * ts) is zero stores all-zero codes.
+ *   FP4_GS_COMPUTE_ONE_PASS gives the same codes, scales and ts as
+ *   FP4_GS_COMPUTE, reading x once: for bf16 input without 16x16 blocks, when
+ *   the tensor fits one workgroup per CU at 16 x 8 x 1024 elements per
+ *   workgroup (about 32 M elements on 256 CUs), a single launch takes the
+ *   maximum, exchanges it across the grid and encodes from registers;
+ *   otherwise it runs the two passes of FP4_GS_COMPUTE.  Its grid waits for
+ *   all of its workgroups, so no other FP4_GS_COMPUTE_ONE_PASS call (nor any
+ *   other kernel that waits for a whole grid) may run on the device at the
+ *   same time; a wait that outlasts a few seconds gives up and writes NaN to
+ *   *global_scale.  Bytes [4096, 8192) of ws must be zero before the first
+ *   call that uses this ws (every call leaves them ready for the next; after
+ *   a NaN give-up they need zeroing again); ws 8-byte aligned.
  *   MXFP4 ignores global_scale and gs_mode (global_scale may be NULL).
  * ws/ws_bytes: device workspace of fp4_workspace_bytes() bytes, any contents
- * (needed only by NVFP4 with FP4_GS_COMPUTE; may be NULL otherwise).
+ * except as above (needed only by NVFP4 with a computed scale; may be NULL
+ * otherwise).
  * Requirements: rows >= 0, cols >= 0, cols % block == 0, ldx >= cols, x
  * 16-byte aligned and ldx * sizeof(xdt) a multiple of 16 (when rows > 1),
  * codes 16-byte aligned.  rows == 0 or cols == 0 is a no-op (for NVFP4 with
@@ -190,6 +208,14 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt,
                  int64_t rows, int64_t cols, int64_t ldx,
                  uint8_t* codes, uint8_t* scales, float* global_scale, int32_t gs_mode,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* 1 when fp4_quantize with FP4_GS_COMPUTE_ONE_PASS would quantize this
+ * configuration and shape in one launch on the current device, 0 when it
+ * would fall back to the two passes (MX formats, fp32 input, 16x16 blocks,
+ * misaligned rows, tensors past the one-launch capacity) or on any error.
+ * Host function; it queries the device's CU count once. */
+int fp4_quantize_one_pass_fits(const fp4_qconfig* cfg, int32_t xdt, int64_t rows, int64_t cols,
+                               int64_t ldx);
 
 /* NVFP4 per-tensor scale only: writes ts = amax(|x'|) / 2688 to
  * *global_scale (x' = the rotated tensor when cfg->rotate != 0), exactly as

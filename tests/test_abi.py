@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(fp4.EXPORTED)
-    assert L.fp4_abi_version() == 2
+    assert L.fp4_abi_version() == 3
     assert fp4.status_str(fp4.FP4_ERR_ALIGNMENT).startswith("misaligned")
 
 
@@ -37,7 +37,7 @@ def test_sizes_give_the_formats_bits_per_element(fmt):
     rows, cols = 64, 4096
     bits = 8 * (fp4.fp4_codes_bytes(rows, cols) + fp4.fp4_scales_bytes(cfg, rows, cols)) / (rows * cols)
     assert bits == {fp4.FMT_MXFP4: 4.25, fp4.FMT_NVFP4: 4.5}[fmt]
-    assert fp4.fp4_workspace_bytes(cfg, rows, cols) == (2048 if fmt == fp4.FMT_NVFP4 else 0)
+    assert fp4.fp4_workspace_bytes(cfg, rows, cols) == (8192 if fmt == fp4.FMT_NVFP4 else 0)
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 32), (31, 64), (33, 256), (100, 4096 + 128), (257, 288)])
@@ -62,7 +62,7 @@ def test_gemm_scale_layout_is_a_bijection(rows, cols):
 
 def _q(cfg, **kw):
     a = dict(x=FAKE, xdt=fp4.DT_BF16, rows=64, cols=256, ldx=256, codes=FAKE, scales=FAKE,
-             gs=FAKE, gs_mode=fp4.GS_COMPUTE, ws=FAKE, ws_bytes=2048, stream=None)
+             gs=FAKE, gs_mode=fp4.GS_COMPUTE, ws=FAKE, ws_bytes=8192, stream=None)
     a.update(kw)
     return fp4.fp4_quantize(cfg, a["x"], a["xdt"], a["rows"], a["cols"], a["ldx"], a["codes"],
                             a["scales"], a["gs"], a["gs_mode"], a["ws"], a["ws_bytes"], a["stream"])
@@ -86,6 +86,11 @@ def test_quantize_rejects_bad_arguments_on_host():
     assert _q(nv, ws=None) == E.FP4_ERR_WORKSPACE
     assert _q(nv, ws_bytes=8) == E.FP4_ERR_WORKSPACE
     assert _q(nv, gs_mode=5) == E.FP4_ERR_INVALID_ARG
+    assert _q(nv, ws_bytes=2048) == E.FP4_ERR_WORKSPACE
+    # the single-pass exchange region holds 64-bit slots
+    assert _q(nv, gs_mode=fp4.GS_COMPUTE_ONE_PASS, ws=FAKE + 4) == E.FP4_ERR_ALIGNMENT
+    assert _q(nv, gs_mode=fp4.GS_COMPUTE_ONE_PASS, ws=None) == E.FP4_ERR_WORKSPACE
+    assert _q(nv, gs_mode=fp4.GS_COMPUTE_ONE_PASS, gs=None) == E.FP4_ERR_INVALID_ARG
     assert fp4.fp4_global_scale(mx, FAKE, fp4.DT_BF16, 64, 256, 256, FAKE, FAKE, 2048, None) == E.FP4_ERR_INVALID_ARG
     assert fp4.fp4_global_scale(nv, FAKE, fp4.DT_BF16, 64, 256, 256, FAKE, None, 0, None) == E.FP4_ERR_WORKSPACE
     assert fp4.fp4_global_scale(nv, MIS, fp4.DT_BF16, 64, 256, 256, FAKE, FAKE, 2048, None) == E.FP4_ERR_ALIGNMENT
@@ -119,7 +124,7 @@ def test_quantize_rejects_bad_arguments_on_host():
     mxi = fp4.qconfig(fp4.FMT_MXINT4, scale_layout=fp4.SCALES_GEMM)
     nvi = fp4.qconfig(fp4.FMT_NVINT4)
     assert fp4.fp4_scales_bytes(mxi, 64, 256) == 2 * 256
-    assert fp4.fp4_workspace_bytes(nvi, 64, 256) == 2048 and fp4.fp4_workspace_bytes(mxi, 64, 256) == 0
+    assert fp4.fp4_workspace_bytes(nvi, 64, 256) == 8192 and fp4.fp4_workspace_bytes(mxi, 64, 256) == 0
     assert _q(fp4.QConfig(fp4.FMT_MXINT4, 16, 0, 0, 0)) == E.FP4_ERR_INVALID_ARG
     assert _q(fp4.QConfig(fp4.FMT_NVINT4, 16, 0, fp4.SCALE_MSE, 0)) == E.FP4_ERR_UNSUPPORTED
     assert _q(nvi, gs=None) == E.FP4_ERR_INVALID_ARG
