@@ -266,6 +266,47 @@ __device__ __forceinline__ uint32_t nv_block_search(const float* v, float amax, 
   return best;
 }
 
+// Absmax block scale and nearest rounding of 16 values (rotated already) with
+// block maximum amax; the divisor is 4 s when fold (the rotation's 1/4 moved
+// into it).
+// The common case of nv_scale with no branches: when the block maximum, the
+// quotients and the E4M3 block scale are normal and the divisor d (4 s when
+// fold) is at least 2^-100, nv_scale and nv_enc8 reduce to these steps (same
+// operations, same results).  Returns whether the case applies.
+__device__ __forceinline__ bool nv_scale_fast(float amax, bool fold, const NvTs& T, uint32_t& code,
+                                              float& d) {
+  const float h = div_rn(amax, 6.0f, 0x1.555556p-3f);
+  const float t = fminf(div_rn(h, T.ts, T.inv_ts), 448.0f);
+  uint32_t u = as_u(t);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  code = (u >> 20) - (120u << 3);
+  const float s = as_f((((code >> 3) + 120u) << 23) | ((code & 7u) << 20)) * T.ts;
+  d = fold ? 4.0f * s : s;
+  return T.live && !T.small && amax >= 0x1p-100f && h >= 0x1p-100f && t >= 0x1p-6f &&
+         d >= 0x1p-100f;
+}
+
+__device__ __forceinline__ uint32_t nv_encode_amax(float* v, float amax, bool fold, const NvTs& T,
+                                                   u32x2& out) {
+  // branch-free when every lane of the wave takes the common case, with one
+  // reciprocal per block
+  uint32_t fcode;
+  float fd;
+  const bool fast = nv_scale_fast(amax, fold, T, fcode, fd);
+  if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+    const float rd = 1.0f / fd;
+    out[0] = nv_enc8_rs(&v[0], fd, rd);
+    out[1] = nv_enc8_rs(&v[8], fd, rd);
+    return fcode;
+  }
+  float s;
+  const uint32_t code = nv_scale(amax, T, s);
+  const float d = fold ? 4.0f * s : s;
+  out[0] = nv_enc8(&v[0], d);
+  out[1] = nv_enc8(&v[8], d);
+  return code;
+}
+
 template <int ROT, int RULE, int RND>
 __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out, uint32_t kb,
                                              uint64_t base, const QParams& P) {
@@ -289,51 +330,26 @@ __device__ __forceinline__ uint32_t nv_block(float* v, const NvTs& T, u32x2& out
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   if (fold) amax *= 0.25f;
-  if constexpr (RND == 0) {
-    // The common case with no branches: when every lane of the wave has a
-    // normal block maximum, quotient and E4M3 block scale and a divisor of at
-    // least 2^-100, the steps of nv_scale and nv_enc8 below reduce to these
-    // (same operations, same results), with one reciprocal per block.
-    const float h = div_rn(amax, 6.0f, 0x1.555556p-3f);
-    const float t = fminf(div_rn(h, T.ts, T.inv_ts), 448.0f);
-    uint32_t u = as_u(t);
-    u += 0x7FFFFu + ((u >> 20) & 1u);
-    const uint32_t code = (u >> 20) - (120u << 3);
-    const float s = as_f((((code >> 3) + 120u) << 23) | ((code & 7u) << 20)) * T.ts;
-    const float d = fold ? 4.0f * s : s;
-    const bool fast = T.live && !T.small && amax >= 0x1p-100f && h >= 0x1p-100f &&
-                      t >= 0x1p-6f && d >= 0x1p-100f;
-    if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
-      const float rd = 1.0f / d;
-      out[0] = nv_enc8_rs(&v[0], d, rd);
-      out[1] = nv_enc8_rs(&v[8], d, rd);
-      return code;
-    }
-  }
+  if constexpr (RND == 0) return nv_encode_amax(v, amax, fold, T, out);
+  // stochastic rounding of the exact quotients fl32(y / s)
   float s;
   const uint32_t code = nv_scale(amax, T, s);
   const float d = fold ? 4.0f * s : s;
-  if constexpr (RND != 0) {
-    // stochastic rounding of the exact quotients fl32(y / s)
-    if (d == 0.0f) {
-      out = u32x2{0u, 0u};
-      return code;
-    }
-    if (d >= 0x1p-100f) {
-      const float rd = 1.0f / d;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = div_rn(v[i], d, rd);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = v[i] / d;
-    }
-    uint32_t w[16];
-    sr_words<16>(base, P, w);
-    out = u32x2{enc8_sr(&v[0], &w[0]), enc8_sr(&v[8], &w[8])};
+  if (d == 0.0f) {
+    out = u32x2{0u, 0u};
     return code;
   }
-  out[0] = nv_enc8(&v[0], d);
-  out[1] = nv_enc8(&v[8], d);
+  if (d >= 0x1p-100f) {
+    const float rd = 1.0f / d;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = div_rn(v[i], d, rd);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = v[i] / d;
+  }
+  uint32_t w[16];
+  sr_words<16>(base, P, w);
+  out = u32x2{enc8_sr(&v[0], &w[0]), enc8_sr(&v[8], &w[8])};
   return code;
 }
 
@@ -744,6 +760,12 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
   // tile, which leaves the maximum unchanged; lanes past the row end hold
   // re-read chunks, not blocks of the tensor, and are left out.  Plain: the
   // largest magnitude's bf16 bits, as the separate maximum pass takes it.
+  // PREP (NVFP4, absmax, nearest, 4 tiles per wave): phase 1 also keeps each
+  // block's fp32 values (rotated, not yet divided by 4) and their maximum, so
+  // the encoding after the exchange starts from them.
+  constexpr bool PREP = FMT == FP4_FMT_NVFP4 && RULE == FP4_SCALE_ABSMAX && RND == 0 && TPW == 4;
+  float vv[PREP ? TPW : 1][16];
+  float am[PREP ? TPW : 1];
   uint32_t mb = 0;
   float mf = 0.0f;
 #pragma unroll
@@ -757,9 +779,21 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
 #pragma unroll
     for (int k = 0; k < CH; ++k) c[u][k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
     wave_lds_sync();
+    if constexpr (PREP) {
+      unpack<FP4_DT_BF16, 16>(c[u], vv[u]);
+      if constexpr (ROT != 0) {
+        if (P.any_sign) apply_signs<16>(vv[u], P.signs[0]);
+        fwht<16>(vv[u]);
+      }
+      am[u] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) am[u] = fmaxf(am[u], fabsf(vv[u][i]));
+    }
     const uint32_t tile = min(gw + u * waves, tiles - 1);
     if ((tile - (tile / wpr) * wpr) * 64 + lane >= nb) continue;
-    if constexpr (ROT == 0) {
+    if constexpr (PREP && ROT != 0) {
+      mf = fmaxf(mf, am[u]);
+    } else if constexpr (ROT == 0) {
 #pragma unroll
       for (int k = 0; k < CH; ++k) {
         u16x2 m = __builtin_bit_cast(u16x2, c[u][k][0] & 0x7FFF7FFFu);
@@ -820,6 +854,32 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
   __syncthreads();
   const NvTs T = make_ts(ts_shared);
 
+  if constexpr (PREP) {
+    // Common case for all tiles at once, straight-line so that the tiles'
+    // steps interleave: every block of every tile of the wave normal (tiles
+    // past the end and lanes past a row's end hold re-read tensor values,
+    // computed and not stored).
+    uint32_t fc[TPW];
+    float fd[TPW];
+    bool fast = !(ROT != 0 && T.small);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+      fast &= nv_scale_fast(ROT != 0 ? am[u] * 0.25f : am[u], ROT != 0, T, fc[u], fd[u]);
+    if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const float rd = 1.0f / fd[u];
+        const uint32_t o0 = nv_enc8_rs(&vv[u][0], fd[u], rd);
+        const uint32_t o1 = nv_enc8_rs(&vv[u][8], fd[u], rd);
+        const uint32_t tile = gw + u * waves;
+        const uint32_t r = tile / wpr, w = tile - r * wpr;
+        const uint32_t kb = w * 64 + lane;
+        if (tile < tiles && kb < nb) store_block<FMT>(u32x4{o0, o1, 0u, 0u}, fc[u], r, kb, nb, codes, scales, 0, 0);
+      }
+      return;
+    }
+  }
+
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const uint32_t tile = gw + u * waves;
@@ -827,7 +887,26 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
     const uint32_t r = tile / wpr, w = tile - r * wpr;
     const uint32_t kb = w * 64 + lane;
     u32x4 out;
-    const uint32_t code = compute_block<FMT, FP4_DT_BF16, ROT, RULE, RND>(c[u], T, out, r, kb, P);
+    uint32_t code;
+    if constexpr (PREP) {
+      // the steps of nv_block after its rotation and maximum (the uncommon
+      // cases; the common one ran above for all tiles at once)
+      u32x2 o;
+      if (ROT != 0 && T.small) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          vv[u][i] *= 0.25f;
+          a = fmaxf(a, fabsf(vv[u][i]));
+        }
+        code = nv_encode_amax(vv[u], a, false, T, o);
+      } else {
+        code = nv_encode_amax(vv[u], ROT != 0 ? am[u] * 0.25f : am[u], ROT != 0, T, o);
+      }
+      out = u32x4{o[0], o[1], 0u, 0u};
+    } else {
+      code = compute_block<FMT, FP4_DT_BF16, ROT, RULE, RND>(c[u], T, out, r, kb, P);
+    }
     if (kb < nb) store_block<FMT>(out, code, r, kb, nb, codes, scales, 0, 0);
   }
 }
