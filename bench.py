@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--streams", type=int, default=2, choices=(1, 2, 3),
+                    help="streams of the eager step: 2 or 3 issue the MXFP4 quantizations on "
+                         "the other stream(s) beside the NVFP4 ones")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true",
@@ -162,7 +165,7 @@ def main():
         G = fp4.BLOCK[fmt]
         return n * 2 + n // 2 + n // G
 
-    def call(v, c, mode):
+    def call(v, c, mode, sh=None):
         """One C-ABI call of variant v on buffer copy c.  mode 'step' is the
         production path (NVFP4 computes its tensor scale and encodes in one
         launch); 'two_pass' the same with the amax pass and the quantize pass;
@@ -174,22 +177,40 @@ def main():
         if fmt == fp4.FMT_MXFP4:
             rc = fp4.fp4_quantize(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
                                   q.codes.data_ptr(), q.scales.data_ptr(), None, fp4.GS_COMPUTE,
-                                  None, 0, sh_now())
+                                  None, 0, sh or sh_now())
         elif mode == "amax":
             rc = fp4.fp4_global_scale(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
-                                      q.global_scale.data_ptr(), ws.data_ptr(), wsb, sh_now())
+                                      q.global_scale.data_ptr(), ws.data_ptr(), wsb, sh or sh_now())
         else:
             gs_mode = {"given": fp4.GS_GIVEN, "two_pass": fp4.GS_COMPUTE}.get(
                 mode, fp4.GS_COMPUTE_ONE_PASS)
             rc = fp4.fp4_quantize(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
                                   q.codes.data_ptr(), q.scales.data_ptr(),
-                                  q.global_scale.data_ptr(), gs_mode, ws.data_ptr(), wsb, sh_now())
+                                  q.global_scale.data_ptr(), gs_mode, ws.data_ptr(), wsb, sh or sh_now())
         if rc != 0:
             raise RuntimeError("quantize failed: %d" % rc)
 
     def run_step(c, mode="step"):
         for v in variants:
             call(v, c, mode)
+
+    # The step's eight quantizations are independent.  With more than one
+    # stream the MXFP4 ones go round-robin to the other stream(s) (default
+    # priority) and overlap the NVFP4 single-pass launches, which stay in order
+    # on the main stream (two of them must never run at once).
+    sides = [torch.cuda.Stream() for _ in range(args.streams - 1)]
+
+    def run_step_eager(c):
+        if not sides:
+            run_step(c)
+            return
+        k = 0
+        for v in variants:
+            if v[1] == fp4.FMT_MXFP4:
+                call(v, c, "step", sides[k % len(sides)].cuda_stream)
+                k += 1
+            else:
+                call(v, c, "step")
 
     one_pass = all(fp4.fp4_quantize_one_pass_fits(outs[v][0].cfg, fp4.DT_BF16, rows, cols, cols)
                    for v in variants if v[1] == fp4.FMT_NVFP4)
@@ -216,19 +237,32 @@ def main():
     # timed region of the reported value: K eager steps between two
     # synchronisations (HIP events on the launching stream alongside)
     for w in range(args.warmup):
-        run_step(w % copies)
+        run_step_eager(w % copies)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
     ev0.record(stream)
+    for sd in sides:
+        sd.wait_stream(stream)
     for s_ in range(args.steps):
-        run_step(s_ % copies)
+        run_step_eager(s_ % copies)
+    for sd in sides:
+        stream.wait_stream(sd)
     ev1.record(stream)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     step_s = (t_end - t_start) / max(1, args.steps)
     step_s_events = ev0.elapsed_time(ev1) * 1e-3 / max(1, args.steps)
+    # the same step on one stream
+    for w in range(args.warmup):
+        run_step(w % copies)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s_ in range(args.steps):
+        run_step(s_ % copies)
+    torch.cuda.synchronize()
+    one_stream_s = (time.perf_counter() - t_start) / max(1, args.steps)
     step_bytes = sum(alg_bytes(v[1]) for v in variants)
     value_gbs = step_bytes / step_s / 1e9
     # the same step with the NVFP4 tensor scale from a separate amax pass
@@ -409,11 +443,14 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * step_s, 4),
         "ms_per_step_events": round(1e3 * step_s_events, 4),
         "ms_per_step_graph": round(1e3 * graph_s, 4),
+        "ms_per_step_one_stream": round(1e3 * one_stream_s, 4),
         "ms_per_step_two_pass": round(1e3 * two_pass_s, 4),
-        "launch": ("eager: %d kernel launches per step through the C ABI (NVFP4: tensor amax and "
-                   "encoding in one launch; ms_per_step_two_pass: with a separate amax pass; "
-                   "ms_per_step_graph: the step as one replayed HIP graph)"
-                   % (len(variants) if one_pass else len(variants) + 4)),
+        "launch": ("eager: %d kernel launches per step through the C ABI on %d stream(s) (MXFP4 "
+                   "on a second stream beside NVFP4; NVFP4: tensor amax and encoding in one "
+                   "launch); ms_per_step_one_stream: all on one stream; ms_per_step_two_pass: one "
+                   "stream, NVFP4 with a separate amax pass; ms_per_step_graph: the one-stream "
+                   "step as one replayed HIP graph"
+                   % (len(variants) if one_pass else len(variants) + 4, args.streams)),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "quantize 4096x4096 bf16 x {Gaussian 0.02, Laplace 0.02 + 16/4096 "
