@@ -48,7 +48,7 @@ MX_FORMATS = (FMT_MXFP4, FMT_MXINT4)
 
 EXPORTED = [
     "fp4_codes_bytes", "fp4_scales_bytes", "fp4_workspace_bytes", "fp4_scale_offset",
-    "fp4_quantize", "fp4_quantize_one_pass_fits", "fp4_global_scale", "fp4_dequantize", "fp4_error_workspace_bytes", "fp4_error_sums",
+    "fp4_quantize", "fp4_quantize_one_pass_fits", "fp4_workspace_init", "fp4_global_scale", "fp4_dequantize", "fp4_error_workspace_bytes", "fp4_error_sums",
     "fp4_scales_to_gemm_layout", "fp4_gemm_workspace_bytes", "fp4_gemm",
     "fp4_gemm_w4a16_workspace_bytes", "fp4_gemm_w4a16", "fp4_status_str", "fp4_abi_version",
 ]
@@ -105,6 +105,8 @@ def lib():
         L.fp4_scale_offset.argtypes = [CP, I64, I64, I64, I64]
         L.fp4_quantize.restype = ctypes.c_int
         L.fp4_quantize.argtypes = [CP, P, I32, I64, I64, I64, P, P, P, I32, P, SZ, P]
+        L.fp4_workspace_init.restype = ctypes.c_int
+        L.fp4_workspace_init.argtypes = [P, SZ, P]
         L.fp4_quantize_one_pass_fits.restype = ctypes.c_int
         L.fp4_quantize_one_pass_fits.argtypes = [CP, I32, I64, I64, I64]
         L.fp4_global_scale.restype = ctypes.c_int
@@ -172,6 +174,10 @@ def fp4_quantize(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, gs_m
     """Raw call: pointers are ints (device addresses), stream an int handle."""
     return lib().fp4_quantize(ctypes.byref(cfg), x, xdt, rows, cols, ldx, codes, scales,
                               global_scale, gs_mode, ws, ws_bytes, stream)
+
+
+def fp4_workspace_init(ws, ws_bytes, stream) -> int:
+    return lib().fp4_workspace_init(ws, ws_bytes, stream)
 
 
 def fp4_quantize_one_pass_fits(cfg, xdt, rows, cols, ldx) -> int:

@@ -182,6 +182,13 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
                                                qparams(cfg, cols), st));
 }
 
+int fp4_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes == 0) return FP4_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 7u) != 0 || (ws_bytes & 3u) != 0) return FP4_ERR_ALIGNMENT;
+  return hip_status(fp4lib::launch_zero_words(static_cast<uint32_t*>(ws), (int64_t)(ws_bytes / 4),
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int fp4_quantize_one_pass_fits(const fp4_qconfig* cfg, int32_t xdt, int64_t rows, int64_t cols,
                                int64_t ldx) {
   if (check_cfg(cfg, rows, cols) != FP4_OK || fp4k::fmt_mx(cfg->fmt) || ldx < cols) return 0;

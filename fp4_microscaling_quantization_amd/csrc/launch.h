@@ -33,6 +33,7 @@ hipError_t launch_quantize_nv_one_pass(int fmt, const void* x, int xdt, int rota
                                        int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
                                        uint32_t* xchg, int max_grid, const fp4k::QParams& P,
                                        hipStream_t st);
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t st);
 hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
                                  hipStream_t st);
 

@@ -1156,6 +1156,12 @@ __global__ __launch_bounds__(kThreads) void amax_final_kernel(const float* __res
 
 __global__ void set_scalar_kernel(float* p, float v) { *p = v; }
 
+// Zero n dwords (a workspace; a kernel rather than a memset so that it can sit
+// in a captured graph).
+__global__ __launch_bounds__(kThreads) void zero_words_kernel(uint32_t* __restrict__ p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) p[i] = 0u;
+}
+
 // Row-major [rows, nb] MXFP4 scales -> GEMM layout (padding filled with 127).
 __global__ __launch_bounds__(kThreads) void scales_to_gemm_kernel(const uint8_t* __restrict__ src,
                                                                   uint32_t rows, uint32_t nb,
@@ -1480,6 +1486,12 @@ hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int r
   if (rule == FP4_SCALE_FOUR_OVER_SIX)
     return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_FOUR_OVER_SIX, 0>(x, xdt, rb, rows, cols, ldx, codes, scales, 0, gs, partials, npart, P, st);
   return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_ABSMAX, 0>(x, xdt, rb, rows, cols, ldx, codes, scales, 0, gs, partials, npart, P, st);
+}
+
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  zero_words_kernel<<<grid_cap(n, 64), kThreads, 0, st>>>(p, (uint32_t)n);
+  return hipGetLastError();
 }
 
 hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,

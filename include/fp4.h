@@ -171,6 +171,13 @@ size_t fp4_scales_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
  * region of FP4_GS_COMPUTE_ONE_PASS (see fp4_quantize).  Host function. */
 size_t fp4_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
 
+/* Zero-fill ws_bytes of device workspace on the stream (a kernel, so it may be
+ * captured in a graph): the preparation the single-pass exchange region needs
+ * before its first use (FP4_GS_COMPUTE_ONE_PASS).  Requirements: ws 8-byte
+ * aligned, ws_bytes a multiple of 4.  Asynchronous; FP4_ERR_INVALID_ARG for
+ * NULL or zero bytes. */
+int fp4_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
 /* Byte index inside the scale array of the scale of (row r, block kb), for the
  * layout named in cfg; -1 if out of range.  Host function. */
 int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols,
@@ -195,7 +202,8 @@ int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols,
  *   same time; a wait that outlasts a few seconds gives up and writes NaN to
  *   *global_scale.  Bytes [4096, 8192) of ws must be zero before the first
  *   call that uses this ws (every call leaves them ready for the next; after
- *   a NaN give-up they need zeroing again); ws 8-byte aligned.
+ *   a NaN give-up they need zeroing again; fp4_workspace_init does it); ws
+ *   8-byte aligned.
  *   MXFP4 ignores global_scale and gs_mode (global_scale may be NULL).
  * ws/ws_bytes: device workspace of fp4_workspace_bytes() bytes, any contents
  * except as above (needed only by NVFP4 with a computed scale; may be NULL

@@ -91,6 +91,10 @@ def test_quantize_rejects_bad_arguments_on_host():
     assert _q(nv, gs_mode=fp4.GS_COMPUTE_ONE_PASS, ws=FAKE + 4) == E.FP4_ERR_ALIGNMENT
     assert _q(nv, gs_mode=fp4.GS_COMPUTE_ONE_PASS, ws=None) == E.FP4_ERR_WORKSPACE
     assert _q(nv, gs_mode=fp4.GS_COMPUTE_ONE_PASS, gs=None) == E.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_workspace_init(None, 8192, None) == E.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_workspace_init(FAKE, 0, None) == E.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_workspace_init(FAKE + 4, 8192, None) == E.FP4_ERR_ALIGNMENT
+    assert fp4.fp4_workspace_init(FAKE, 8190, None) == E.FP4_ERR_ALIGNMENT
     assert fp4.fp4_global_scale(mx, FAKE, fp4.DT_BF16, 64, 256, 256, FAKE, FAKE, 2048, None) == E.FP4_ERR_INVALID_ARG
     assert fp4.fp4_global_scale(nv, FAKE, fp4.DT_BF16, 64, 256, 256, FAKE, None, 0, None) == E.FP4_ERR_WORKSPACE
     assert fp4.fp4_global_scale(nv, MIS, fp4.DT_BF16, 64, 256, 256, FAKE, FAKE, 2048, None) == E.FP4_ERR_ALIGNMENT

@@ -156,6 +156,31 @@ def test_one_pass_graph_replays():
         _same(q, ref, ("replay", r))
 
 
+def test_one_pass_workspace_init_through_the_c_abi():
+    """A workspace full of garbage, prepared with fp4_workspace_init, then
+    single-pass calls straight through the C ABI on it: each equals the
+    two-pass result (the call numbering starts from the zeroed region)."""
+    say("one pass workspace init")
+    b = _bits("cfg2_laplace")
+    x = to_dev_bf16(b)
+    rows, cols = b.shape
+    cfg = fp4.qconfig(fp4.FMT_NVFP4, True)
+    wsb = fp4.fp4_workspace_bytes(cfg, rows, cols)
+    ws = torch.full((wsb,), 0xA5, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    assert fp4.fp4_workspace_init(ws.data_ptr(), wsb, stream) == 0
+    ref = fp4.quantize(x, fp4.FMT_NVFP4, rotate=True)
+    for rep in range(2):
+        q = _prefilled(x, fp4.FMT_NVFP4, True, {})
+        rc = fp4.fp4_quantize(cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols, q.codes.data_ptr(),
+                              q.scales.data_ptr(), q.global_scale.data_ptr(),
+                              fp4.GS_COMPUTE_ONE_PASS, ws.data_ptr(), wsb, stream)
+        assert rc == 0
+        torch.cuda.synchronize()
+        _same(q, ref, ("ws init", rep))
+    assert int(ws[4096:4100].view(torch.int32).item()) == 2  # two calls numbered from zero
+
+
 def test_one_pass_falls_back_when_it_does_not_fit():
     """Shapes and inputs the single launch does not take run the two passes:
     same results, and the fit query says so."""
