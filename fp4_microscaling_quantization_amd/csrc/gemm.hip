@@ -16,6 +16,8 @@
 // multiply the accumulator in the epilogue ("Portable FP4 Quantization for
 // Heterogeneous Accelerators", section 2.5: conversion fused with GEMM entry
 // instead of materialising a full-precision copy).
+#include <type_traits>
+
 #include "fp4_device.h"
 #include "launch.h"
 
@@ -92,7 +94,10 @@ struct MxCfg {
   static constexpr int ROUNDS = (USED + RB - 1) / RB;
   static constexpr int STAGE = ROUNDS * RB;
   static constexpr int LDS = NS * STAGE;
-  static constexpr int IN_FLIGHT = (NS - 2) * ROUNDS;  // DMAs allowed after the awaited stage
+  // Waves whose share of the last round is all slot padding skip that DMA
+  // (and count one DMA less per stage in their waits).
+  static constexpr int LAST_W = (USED - (ROUNDS - 1) * RB + 1023) / 1024;
+  static constexpr bool SKIP = LAST_W < NW;
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
 };
@@ -189,11 +194,13 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
     for (int r = 0; r < H; ++r)
       dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * C::RB + wave * 1024);
   };
-  auto dma_tail = [&](int kt) __attribute__((always_inline)) {
+  // SHORT: this wave's part of the last round is slot padding, not loaded.
+  auto dma_tail = [&](int kt, auto short_tag) __attribute__((always_inline)) {
+    constexpr int RE = decltype(short_tag)::value ? ROUNDS - 1 : ROUNDS;
     const int ks = min(kt, kt1 - 1);
     uint8_t* slot = slot_of(kt);
 #pragma unroll
-    for (int r = H; r < ROUNDS; ++r)
+    for (int r = H; r < RE; ++r)
       dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * C::RB + wave * 1024);
   };
 
@@ -246,7 +253,10 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
   constexpr int NVA = ROUNDS - H;          // DMAs in the first half iteration
   constexpr int NVB = H;                   // DMAs in the second half
 
-  if (kt0 < kt1) {
+  // The ring, for waves that load every round of a stage (PER = ROUNDS DMAs
+  // per stage) or all but the last (PER = ROUNDS - 1).
+  auto ring = [&](auto short_tag) __attribute__((always_inline)) {
+    constexpr int PER = decltype(short_tag)::value ? ROUNDS - 1 : ROUNDS;
     // In iteration kt the registers hold step 0 of stage kt (F0, S).  First
     // half: step 1's reads and the tail of stage kt+NS-1's DMA go out with
     // step 0's MFMAs.  Each wave then waits for its own DMA of stage kt+1 and
@@ -257,10 +267,10 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i) {
       dma_head(kt0 + i);
-      dma_tail(kt0 + i);
+      dma_tail(kt0 + i, short_tag);
     }
     dma_head(kt0 + NS - 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * ROUNDS + H, 15));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER + H, 15));
     __builtin_amdgcn_s_barrier();
     Frags F0, F1;
     Scales S, S1;
@@ -270,7 +280,7 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
     for (int kt = kt0; kt < kt1; ++kt) {
       const int sel0 = (kt & 1) * 2;
       read_frags(slot_of(kt), 1, F1);
-      dma_tail(kt + NS - 1);
+      dma_tail(kt + NS - 1, short_tag);
       mfmas(F0, S, sel0);
 #pragma unroll
       for (int k = 0; k < NMF; ++k) {
@@ -279,7 +289,7 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
         if (k < NVA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // DMA
       }
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::IN_FLIGHT, 0));
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER, 0));  // DMAs after stage kt+1
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       dma_head(kt + NS);
@@ -299,6 +309,16 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
       for (int j = 0; j < TN; ++j) S.b[j] = S1.b[j];
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+  };
+  if (kt0 < kt1) {
+    if constexpr (C::SKIP) {
+      if (__builtin_amdgcn_readfirstlane(wave) >= C::LAST_W)
+        ring(std::true_type{});
+      else
+        ring(std::false_type{});
+    } else {
+      ring(std::false_type{});
+    }
   }
 
   // Epilogue: whole tiles store without bounds checks.
