@@ -174,43 +174,48 @@ def main():
         d, fmt, rot = v
         x = xs[d][c]
         q = outs[v][c]
+        h = sh if sh is not None else sh_now()
         if fmt == fp4.FMT_MXFP4:
             rc = fp4.fp4_quantize(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
                                   q.codes.data_ptr(), q.scales.data_ptr(), None, fp4.GS_COMPUTE,
-                                  None, 0, sh or sh_now())
+                                  None, 0, h)
         elif mode == "amax":
             rc = fp4.fp4_global_scale(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
-                                      q.global_scale.data_ptr(), ws.data_ptr(), wsb, sh or sh_now())
+                                      q.global_scale.data_ptr(), ws.data_ptr(), wsb, h)
         else:
             gs_mode = {"given": fp4.GS_GIVEN, "two_pass": fp4.GS_COMPUTE}.get(
                 mode, fp4.GS_COMPUTE_ONE_PASS)
             rc = fp4.fp4_quantize(q.cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
                                   q.codes.data_ptr(), q.scales.data_ptr(),
-                                  q.global_scale.data_ptr(), gs_mode, ws.data_ptr(), wsb, sh or sh_now())
+                                  q.global_scale.data_ptr(), gs_mode, ws.data_ptr(), wsb, h)
         if rc != 0:
             raise RuntimeError("quantize failed: %d" % rc)
 
-    def run_step(c, mode="step"):
+    def run_step(c, mode="step", sh=None):
         for v in variants:
-            call(v, c, mode)
+            call(v, c, mode, sh)
 
     # The step's eight quantizations are independent.  With more than one
     # stream the MXFP4 ones go round-robin to the other stream(s) (default
     # priority) and overlap the NVFP4 single-pass launches, which stay in order
     # on the main stream (two of them must never run at once).
     sides = [torch.cuda.Stream() for _ in range(args.streams - 1)]
+    # stream handles looked up once (torch's current-stream query costs about
+    # as much host time as a launch)
+    h_main = stream.cuda_stream
+    h_sides = [sd.cuda_stream for sd in sides]
 
     def run_step_eager(c):
         if not sides:
-            run_step(c)
+            run_step(c, "step", h_main)
             return
         k = 0
         for v in variants:
             if v[1] == fp4.FMT_MXFP4:
-                call(v, c, "step", sides[k % len(sides)].cuda_stream)
+                call(v, c, "step", h_sides[k % len(h_sides)])
                 k += 1
             else:
-                call(v, c, "step")
+                call(v, c, "step", h_main)
 
     one_pass = all(fp4.fp4_quantize_one_pass_fits(outs[v][0].cfg, fp4.DT_BF16, rows, cols, cols)
                    for v in variants if v[1] == fp4.FMT_NVFP4)
@@ -256,22 +261,22 @@ def main():
     step_s_events = ev0.elapsed_time(ev1) * 1e-3 / max(1, args.steps)
     # the same step on one stream
     for w in range(args.warmup):
-        run_step(w % copies)
+        run_step(w % copies, "step", h_main)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s_ in range(args.steps):
-        run_step(s_ % copies)
+        run_step(s_ % copies, "step", h_main)
     torch.cuda.synchronize()
     one_stream_s = (time.perf_counter() - t_start) / max(1, args.steps)
     step_bytes = sum(alg_bytes(v[1]) for v in variants)
     value_gbs = step_bytes / step_s / 1e9
     # the same step with the NVFP4 tensor scale from a separate amax pass
     for w in range(args.warmup):
-        run_step(w % copies, "two_pass")
+        run_step(w % copies, "two_pass", h_main)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s_ in range(args.steps):
-        run_step(s_ % copies, "two_pass")
+        run_step(s_ % copies, "two_pass", h_main)
     torch.cuda.synchronize()
     two_pass_s = (time.perf_counter() - t_start) / max(1, args.steps)
 

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void error_partial_kernel(
     sy += shfl_xor_d(sy, off);
   }
   __shared__ double red[kThreads / 64][4];
-  const int wave = threadIdx.x >> 6;
+  const int wave = (int)wave_index();
   if ((threadIdx.x & 63) == 0) {
     red[wave][0] = se;
     red[wave][1] = sx;

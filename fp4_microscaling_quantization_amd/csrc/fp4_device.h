@@ -102,6 +102,12 @@ __device__ __forceinline__ float int4_value(uint32_t w, int i) {
   return (float)((int32_t)(w << (28 - 4 * i)) >> 28);
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: tile arithmetic derived from it runs on the scalar unit.
+__device__ __forceinline__ uint32_t wave_index() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 // ------------------------------------------------------------------ E4M3
 // Value of a non-negative E4M3 code (0 .. 0x7E).
 __device__ __forceinline__ float e4m3_value(uint32_t code) {

@@ -273,13 +273,20 @@ __device__ __forceinline__ uint32_t nv_block_search(const float* v, float amax, 
 // quotients and the E4M3 block scale are normal and the divisor d (4 s when
 // fold) is at least 2^-100, nv_scale and nv_enc8 reduce to these steps (same
 // operations, same results).  Returns whether the case applies.
-__device__ __forceinline__ bool nv_scale_fast(float amax, bool fold, const NvTs& T, uint32_t& code,
-                                              float& d) {
-  const float h = div_rn(amax, 6.0f, 0x1.555556p-3f);
-  const float t = fminf(div_rn(h, T.ts, T.inv_ts), 448.0f);
+// nv_code_fast: the E4M3 code of that case, with h = fl32(amax / 6) and
+// t = min(fl32(h / ts), 448) (a meaningless code when t < 2^-6).
+__device__ __forceinline__ uint32_t nv_code_fast(float amax, const NvTs& T, float& h, float& t) {
+  h = div_rn(amax, 6.0f, 0x1.555556p-3f);
+  t = fminf(div_rn(h, T.ts, T.inv_ts), 448.0f);
   uint32_t u = as_u(t);
   u += 0x7FFFFu + ((u >> 20) & 1u);
-  code = (u >> 20) - (120u << 3);
+  return (u >> 20) - (120u << 3);
+}
+
+__device__ __forceinline__ bool nv_scale_fast(float amax, bool fold, const NvTs& T, uint32_t& code,
+                                              float& d) {
+  float h, t;
+  code = nv_code_fast(amax, T, h, t);
   const float s = as_f((((code >> 3) + 120u) << 23) | ((code & 7u) << 20)) * T.ts;
   d = fold ? 4.0f * s : s;
   return T.live && !T.small && amax >= 0x1p-100f && h >= 0x1p-100f && t >= 0x1p-6f &&
@@ -407,7 +414,7 @@ __device__ __forceinline__ void unpack(const u32x4* c, float* v) {
 // unpacked; with ROT signed and put through the butterflies but not yet
 // divided by 4) with their maximum am, for the single-pass kernel, which
 // prepares them before the exchange.  nv_prep_block prepares one block;
-// nv_encode_prepped encodes one as nv_block would; nv_encode_tiles_fast
+// nv_encode_prepped encodes one as nv_block would; nv_encode_tiles_tab
 // encodes N blocks (one per tile of the wave) in one branch-free sequence when
 // every block of the wave takes nv_scale_fast's common case, and returns
 // false (wave-uniform, nothing done) otherwise.  (The two-pass kernel keeps
@@ -439,21 +446,40 @@ __device__ __forceinline__ uint32_t nv_encode_prepped(float* v, float am, const 
   return nv_encode_amax(v, ROT != 0 ? am * 0.25f : am, ROT != 0, T, out);
 }
 
+// Divisor table of one launch for nv_encode_tiles_tab: entry c holds
+// d = e4m3(c) * ts (times 4 with ROT, the fold) and fl32(1 / d), the values
+// nv_scale_fast and nv_encode_amax derive per block.
+template <int ROT>
+__device__ __forceinline__ void nv_divisor_entry(uint32_t c, float ts, float (&tab)[128][2]) {
+  const float s = e4m3_value(c) * ts;
+  const float d = ROT != 0 ? 4.0f * s : s;
+  tab[c][0] = d;
+  tab[c][1] = 1.0f / d;
+}
+
+// The common case for N blocks with the block divisors and their reciprocals
+// looked up in the launch's divisor table: the values nv_scale_fast and
+// nv_encode_amax would compute per block.
 template <int ROT, int N>
-__device__ __forceinline__ bool nv_encode_tiles_fast(float (&v)[N][16], const float (&am)[N],
-                                                     const NvTs& T, uint32_t (&code)[N],
-                                                     u32x2 (&out)[N]) {
-  float d[N];
-  bool fast = !(ROT != 0 && T.small);
-#pragma unroll
-  for (int u = 0; u < N; ++u)
-    fast &= nv_scale_fast(ROT != 0 ? am[u] * 0.25f : am[u], ROT != 0, T, code[u], d[u]);
-  if (__builtin_amdgcn_ballot_w64(!fast) != 0) return false;
+__device__ __forceinline__ bool nv_encode_tiles_tab(float (&v)[N][16], const float (&am)[N],
+                                                    const NvTs& T, const float (&tab)[128][2],
+                                                    uint32_t (&code)[N], u32x2 (&out)[N]) {
+  float d[N], rd[N];
+  bool fast = T.live && !T.small;
 #pragma unroll
   for (int u = 0; u < N; ++u) {
-    const float rd = 1.0f / d[u];
-    out[u] = u32x2{nv_enc8_rs(&v[u][0], d[u], rd), nv_enc8_rs(&v[u][8], d[u], rd)};
+    const float a = ROT != 0 ? am[u] * 0.25f : am[u];
+    float h, t;
+    code[u] = nv_code_fast(a, T, h, t);
+    const uint32_t c = min(code[u], 127u);
+    d[u] = tab[c][0];
+    rd[u] = tab[c][1];
+    fast &= a >= 0x1p-100f && h >= 0x1p-100f && t >= 0x1p-6f && d[u] >= 0x1p-100f;
   }
+  if (__builtin_amdgcn_ballot_w64(!fast) != 0) return false;
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    out[u] = u32x2{nv_enc8_rs(&v[u][0], d[u], rd[u]), nv_enc8_rs(&v[u][8], d[u], rd[u])};
   return true;
 }
 
@@ -536,7 +562,7 @@ __device__ __forceinline__ float wg_max(float m) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   __shared__ float red[kThreads / 64];
-  const int wave = threadIdx.x >> 6;
+  const int wave = (int)wave_index();
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[wave] = m;
   __syncthreads();
@@ -580,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void quant_tile_kernel(
   NvTs T{};
   if constexpr (!fmt_mx(FMT)) T = nv_launch_ts<FMT>(gs, partials, npart);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = (int)wave_index();
   const uint32_t groups = nb / 64;
   const uint32_t tiles = rows * groups;
   uint8_t* l = lds[wave];
@@ -694,7 +720,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
   constexpr int STRIDE = BB + 16;  // padded LDS stride
   __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][64 * STRIDE];
   const int lane = threadIdx.x & 63;
-  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t wave = wave_index();
   const uint32_t tiles = rows * wpr;
   const uint32_t step = gridDim.x * (kThreads / 64) * TPW;
   uint32_t t0 = (blockIdx.x * (kThreads / 64) + wave) * TPW;
@@ -789,8 +815,9 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[kFusedWaves][64 * STRIDE];
   __shared__ float red[kFusedWaves];
   __shared__ float ts_shared;
+  __shared__ float dtab[128][2];
   const int lane = threadIdx.x & 63;
-  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t wave = wave_index();
   const uint32_t tiles = rows * wpr;
   const uint32_t waves = gridDim.x * kFusedWaves;
   const uint32_t gw = blockIdx.x * kFusedWaves + wave;
@@ -833,20 +860,32 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
 #pragma unroll
     for (int k = 0; k < CH; ++k) c[u][k] = *reinterpret_cast<const u32x4*>(l + lane * STRIDE + k * 16);
     wave_lds_sync();
-    if constexpr (PREP) nv_prep_block<ROT>(c[u], vv[u], am[u], P);
-    const uint32_t tile = min(gw + u * waves, tiles - 1);
-    if ((tile - (tile / wpr) * wpr) * 64 + lane >= nb) continue;
-    if constexpr (PREP && ROT != 0) {
-      mf = fmaxf(mf, am[u]);
-    } else if constexpr (ROT == 0) {
+    uint32_t bm = 0;  // plain: the block's largest magnitude as bf16 bits
+    if constexpr (ROT == 0) {
 #pragma unroll
       for (int k = 0; k < CH; ++k) {
         u16x2 m = __builtin_bit_cast(u16x2, c[u][k][0] & 0x7FFF7FFFu);
 #pragma unroll
         for (int e = 1; e < 4; ++e)
           m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, c[u][k][e] & 0x7FFF7FFFu));
-        mb = max(mb, (uint32_t)max(m[0], m[1]));
+        bm = max(bm, (uint32_t)max(m[0], m[1]));
       }
+      if constexpr (PREP) {
+        // the block maximum from the same bits, computed here so that the
+        // encoding after the exchange starts from it (it differs from a
+        // float maximum only for NaN inputs, which the contract excludes)
+        unpack<FP4_DT_BF16, 16>(c[u], vv[u]);
+        am[u] = as_f(bm << 16);
+      }
+    } else if constexpr (PREP) {
+      nv_prep_block<ROT>(c[u], vv[u], am[u], P);
+    }
+    const uint32_t tile = min(gw + u * waves, tiles - 1);
+    if ((tile - (tile / wpr) * wpr) * 64 + lane >= nb) continue;
+    if constexpr (PREP && ROT != 0) {
+      mf = fmaxf(mf, am[u]);
+    } else if constexpr (ROT == 0) {
+      mb = max(mb, bm);
     } else {
       float v[16];
       unpack<FP4_DT_BF16, 16>(c[u], v);
@@ -890,6 +929,10 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) t = fmaxf(t, __shfl_xor(t, off, 64));
     const float ts = ok ? t / (448.0f * fmt_qmax(FMT)) : __builtin_nanf("");
+    if constexpr (PREP) {
+      nv_divisor_entry<ROT>(lane, ts, dtab);
+      nv_divisor_entry<ROT>(lane + 64, ts, dtab);
+    }
     if (lane == 0) {
       ts_shared = ts;
       if (blockIdx.x == 0 || !ok) *gs = ts;
@@ -906,7 +949,7 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
     // computed and not stored).
     uint32_t fc[TPW];
     u32x2 fo[TPW];
-    if (nv_encode_tiles_fast<ROT, TPW>(vv, am, T, fc, fo)) {
+    if (nv_encode_tiles_tab<ROT, TPW>(vv, am, T, dtab, fc, fo)) {
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const uint32_t tile = gw + u * waves;
@@ -954,7 +997,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
   constexpr int STRIDE = 64 + 16;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][64 * STRIDE];
   const int lane = threadIdx.x & 63;
-  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t wave = wave_index();
   const uint32_t tiles = ((rows + 31) / 32) * kcs;
   const uint32_t cpr = nb * 4;  // 16-byte chunks per row
   uint8_t* l = lds[wave];
@@ -998,7 +1041,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t*
                                                                   float* __restrict__ partials,
                                                                   uint32_t sign_mask) {
   const int lane = threadIdx.x & 63;
-  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t wave = wave_index();
   const uint32_t tiles = rows * wpr;
   const uint32_t step = gridDim.x * (kAmaxThreads / 64);
   uint32_t mb = 0;   // plain: max of |x| bf16 bits
@@ -1246,7 +1289,7 @@ __global__ __launch_bounds__(kThreads) void quant_nv2d_kernel(
   const int lane = threadIdx.x & 63;
   const uint32_t wpr = (nb + 63) / 64, rts = (rows + 15) / 16;
   const uint32_t tiles = rts * wpr;
-  for (uint32_t tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); tile < tiles;
+  for (uint32_t tile = blockIdx.x * (kThreads / 64) + wave_index(); tile < tiles;
        tile += gridDim.x * (kThreads / 64)) {
     const uint32_t rt = tile / wpr, w = tile - rt * wpr;
     const uint32_t kb = w * 64 + lane;
