@@ -4,18 +4,21 @@
 Timed step (``value``): one pass of block-wise FP4 quantization over the
 4096x4096 bf16 workload in all its variants -- two seeded distributions
 (Gaussian std 0.02; Laplace b=0.02 with 16 of 4096 columns x50) x {MXFP4,
-NVFP4} x {no rotation, block Hadamard of the block size}.  NVFP4 runs its
-global-amax pass and its quantize pass as separate launches.  Inputs are
-resident in HBM; the step cycles through several copies of every input and
-output so that the 256 MB last-level cache cannot serve a repeat.
+NVFP4} x {no rotation, block Hadamard of the block size}, as one
+fp4_quantize_batch call: two launches of the grouped kernel (the four MXFP4
+encodings and the four NVFP4 tensor maxima, then the four NVFP4 encodings).
+Inputs are resident in HBM; the step cycles through several copies of every
+input and output so that the 256 MB last-level cache cannot serve a repeat.
 
 ``value`` = algorithmic bytes of the step (bf16 read once + codes + scales)
-divided by the step time, in GB/s, over K eagerly launched steps; the same
-step recorded as a HIP graph and replayed is reported beside it
-(``ms_per_step_graph``).  ``roofline`` reports the slowest kernel of the step;
-its launch duration is measured live with HIP events on the launching stream
-around a graph of back-to-back launches of that kernel (a Python loop of
-single launches would be bound by the host).
+divided by the step time, in GB/s, over K eagerly issued steps (after W
+warmup steps and an untimed settle of ``--settle`` seconds of steps); the same
+step recorded as a HIP graph and replayed, and the step as eight separate
+fp4_quantize calls (one stream; two streams; NVFP4 in two passes) are
+reported beside it.  ``roofline`` reports the grouped kernel (its two launches
+per step); their duration is measured live with HIP events on the launching
+stream around a graph of back-to-back steps (a Python loop of single calls
+would be bound by the host).
 
 Also reported in the same line: NMSE of every variant (GPU, and oracle vs GPU
 on a sample), the oracle's own throughput on a bounded sample
@@ -38,6 +41,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12         # B/s, MI355X HBM3E
+BATCH_KERNEL = "quant_batch_kernel (2 launches per step)"
 PEAK_FP4 = 10.1e15        # dense MXFP4 MFMA, flop/s
 PEAK_F16 = 2.5e15         # dense fp16/bf16 MFMA, flop/s
 METRIC = "quant GB/s (% HBM peak); FP4 GEMM TFLOPS (% MFMA peak); NMSE vs oracle"
@@ -50,8 +54,11 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed steps before the measurements (the first few "
+                         "hundred steps after idle run up to 15%% slower)")
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--streams", type=int, default=2, choices=(1, 2, 3),
                     help="streams of the eager step: 2 or 3 issue the MXFP4 quantizations on "
@@ -160,6 +167,24 @@ def main():
     # region (zero before its first use)
     wsb = fp4.fp4_workspace_bytes(fp4.qconfig(fp4.FMT_NVFP4), rows, cols)
     ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    # the step as one batch per buffer copy (NVFP4 computes its tensor scale)
+    bwsb = fp4.fp4_quantize_batch_workspace_bytes(len(variants))
+    bws = torch.zeros(bwsb, dtype=torch.uint8, device=dev)
+    batch_jobs = []
+    for c in range(copies):
+        jl = []
+        for v in variants:
+            q = outs[v][c]
+            jl.append(fp4.quant_job(q.cfg, xs[v[0]][c].data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                    q.codes.data_ptr(), q.scales.data_ptr(),
+                                    q.global_scale.data_ptr(), fp4.GS_COMPUTE))
+        batch_jobs.append(fp4.job_array(jl))
+
+    def run_batch(c, sh=None):
+        rc = fp4.fp4_quantize_batch(len(variants), batch_jobs[c], bws.data_ptr(), bwsb,
+                                    sh if sh is not None else sh_now())
+        if rc != 0:
+            raise RuntimeError("quantize batch failed: %d" % rc)
 
     def alg_bytes(fmt):
         G = fp4.BLOCK[fmt]
@@ -227,8 +252,18 @@ def main():
             fn()
         return g
 
+    # untimed steps until the device has run the step for args.settle seconds
+    t_settle = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(20):
+            run_batch(k % copies)
+            k += 1
+        torch.cuda.synchronize()
+    log("settled after %d untimed steps" % k)
+
     # the same step as one HIP graph per buffer copy, replayed
-    step_graphs = [capture(lambda c=c: run_step(c)) for c in range(copies)]
+    step_graphs = [capture(lambda c=c: run_batch(c)) for c in range(copies)]
     for w in range(args.warmup):
         step_graphs[w % copies].replay()
     torch.cuda.synchronize()
@@ -239,26 +274,36 @@ def main():
     graph_s = (time.perf_counter() - t_start) / max(1, args.steps)
     del step_graphs
 
-    # timed region of the reported value: K eager steps between two
-    # synchronisations (HIP events on the launching stream alongside)
+    # timed region of the reported value: K eager steps (one batch call each)
+    # between two synchronisations (HIP events on the launching stream
+    # alongside)
     for w in range(args.warmup):
-        run_step_eager(w % copies)
+        run_batch(w % copies, h_main)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
     ev0.record(stream)
+    for s_ in range(args.steps):
+        run_batch(s_ % copies, h_main)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    step_s = (t_end - t_start) / max(1, args.steps)
+    step_s_events = ev0.elapsed_time(ev1) * 1e-3 / max(1, args.steps)
+    # the step as eight separate calls, the MXFP4 ones on other stream(s)
+    for w in range(args.warmup):
+        run_step_eager(w % copies)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
     for sd in sides:
         sd.wait_stream(stream)
     for s_ in range(args.steps):
         run_step_eager(s_ % copies)
     for sd in sides:
         stream.wait_stream(sd)
-    ev1.record(stream)
     torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    step_s = (t_end - t_start) / max(1, args.steps)
-    step_s_events = ev0.elapsed_time(ev1) * 1e-3 / max(1, args.steps)
+    calls_streams_s = (time.perf_counter() - t_start) / max(1, args.steps)
     # the same step on one stream
     for w in range(args.warmup):
         run_step(w % copies, "step", h_main)
@@ -286,18 +331,36 @@ def main():
     # between graph nodes).
     reps = 4 * copies
     kern = {}
+    # the grouped kernel: two launches per step, timed over a graph of steps
+    amax_reads = n * 2 * sum(1 for v in variants if v[1] != fp4.FMT_MXFP4)
+    run_batch(0)
+    torch.cuda.synchronize()
+    g = capture(lambda: [run_batch(i % copies) for i in range(reps)])
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del g
+    kern[BATCH_KERNEL] = {"avg_us": us, "alg_bytes": step_bytes + amax_reads,
+                          "gbs": (step_bytes + amax_reads) / (us * 1e-6) / 1e9, "launches": 2 * reps,
+                          "in_step": True}
     for (d, fmt, rot) in variants:
         if d != "gauss":
             continue
         v = (d, fmt, rot)
         tag = "rot" if rot else "plain"
         if fmt == fp4.FMT_MXFP4:
-            parts = [("quant_mx_gemm_kernel<%s>" % tag, "step", alg_bytes(fmt), True)]
+            parts = [("quant_mx_gemm_kernel<%s>" % tag, "step", alg_bytes(fmt), False)]
         else:
             # the step's single launch, then the two passes it replaces
-            parts = [("quant_nv_fused_kernel<nvfp4,%s,4>" % tag, "step", alg_bytes(fmt), one_pass),
-                     ("amax_chunk_kernel<%s>" % tag, "amax", n * 2, not one_pass),
-                     ("quant_rows_kernel<nvfp4,%s,2>" % tag, "given", alg_bytes(fmt), not one_pass)]
+            parts = [("quant_nv_fused_kernel<nvfp4,%s,4>" % tag, "step", alg_bytes(fmt), False),
+                     ("amax_chunk_kernel<%s>" % tag, "amax", n * 2, False),
+                     ("quant_rows_kernel<nvfp4,%s,2>" % tag, "given", alg_bytes(fmt), False)]
         for label, mode, nbytes, in_step in parts:
             call(v, 0, mode)
             torch.cuda.synchronize()
@@ -320,7 +383,11 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dk["gbs"], 1),
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(dk["gbs"] * 1e9 / PEAK_HBM, 4),
                 "traffic": traffic, "traffic_note": traffic_note,
-                "alg_bytes_per_launch": dk["alg_bytes"], "avg_launch_us": round(dk["avg_us"], 3)}
+                "alg_bytes_per_step": dk["alg_bytes"], "avg_step_us": round(dk["avg_us"], 3),
+                "launches_per_step": 2,
+                "alg_bytes_note": "the step's bytes (each input read once, codes, scales) plus the "
+                                  "second read of the four NVFP4 inputs by their tensor-maximum "
+                                  "pass"}
     log("step %.3f ms (eager), %.3f ms (graph), %.1f GB/s; dominant %s %.2f us"
         % (1e3 * step_s, 1e3 * graph_s, value_gbs, dom, dk["avg_us"]))
 
@@ -448,18 +515,20 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * step_s, 4),
         "ms_per_step_events": round(1e3 * step_s_events, 4),
         "ms_per_step_graph": round(1e3 * graph_s, 4),
-        "ms_per_step_one_stream": round(1e3 * one_stream_s, 4),
-        "ms_per_step_two_pass": round(1e3 * two_pass_s, 4),
-        "launch": ("eager: %d kernel launches per step through the C ABI on %d stream(s) (MXFP4 "
-                   "on a second stream beside NVFP4; NVFP4: tensor amax and encoding in one "
-                   "launch); ms_per_step_one_stream: all on one stream; ms_per_step_two_pass: one "
-                   "stream, NVFP4 with a separate amax pass; ms_per_step_graph: the one-stream "
-                   "step as one replayed HIP graph"
-                   % (len(variants) if one_pass else len(variants) + 4, args.streams)),
+        "ms_per_step_calls": round(1e3 * one_stream_s, 4),
+        "ms_per_step_calls_streams": round(1e3 * calls_streams_s, 4),
+        "ms_per_step_calls_two_pass": round(1e3 * two_pass_s, 4),
+        "launch": ("eager: one fp4_quantize_batch call per step (2 launches of the grouped "
+                   "kernel: 4 MXFP4 encodings + 4 NVFP4 tensor maxima, then 4 NVFP4 encodings); "
+                   "ms_per_step_graph: that step as a replayed HIP graph; ms_per_step_calls: 8 "
+                   "fp4_quantize calls on one stream (NVFP4 tensor amax and encoding in one "
+                   "launch%s); ms_per_step_calls_streams: the same with the MXFP4 calls on %d "
+                   "other stream(s); ms_per_step_calls_two_pass: 8 calls, NVFP4 with a separate "
+                   "amax pass" % ("" if one_pass else ": not taken, two passes", args.streams - 1)),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "quantize 4096x4096 bf16 x {Gaussian 0.02, Laplace 0.02 + 16/4096 "
-                               "cols x50} x {MXFP4 G32, NVFP4 G16 (tensor amax in the same launch)} x {plain, "
+                               "cols x50} x {MXFP4 G32, NVFP4 G16 (tensor amax computed)} x {plain, "
                                "block Hadamard 32/16}", "rows": rows, "cols": cols,
                    "variants": len(variants), "buffer_copies": copies,
                    "step_alg_bytes": step_bytes},

@@ -48,7 +48,9 @@ MX_FORMATS = (FMT_MXFP4, FMT_MXINT4)
 
 EXPORTED = [
     "fp4_codes_bytes", "fp4_scales_bytes", "fp4_workspace_bytes", "fp4_scale_offset",
-    "fp4_quantize", "fp4_quantize_one_pass_fits", "fp4_workspace_init", "fp4_global_scale", "fp4_dequantize", "fp4_error_workspace_bytes", "fp4_error_sums",
+    "fp4_quantize", "fp4_quantize_one_pass_fits", "fp4_workspace_init", "fp4_global_scale",
+    "fp4_quantize_batch_workspace_bytes", "fp4_quantize_batch", "fp4_dequantize",
+    "fp4_error_workspace_bytes", "fp4_error_sums",
     "fp4_scales_to_gemm_layout", "fp4_gemm_workspace_bytes", "fp4_gemm",
     "fp4_gemm_w4a16_workspace_bytes", "fp4_gemm_w4a16", "fp4_status_str", "fp4_abi_version",
 ]
@@ -65,6 +67,14 @@ class QConfig(ctypes.Structure):
                 ("rule", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
                 ("rounding", ctypes.c_int32), ("block_rows", ctypes.c_int32),
                 ("rot_signs", ctypes.c_uint32 * 4), ("seed", ctypes.c_uint32 * 2)]
+
+
+class QuantJob(ctypes.Structure):
+    """fp4_quant_job: the arguments of one fp4_quantize call (pointers as ints)."""
+    _fields_ = [("cfg", QConfig), ("x", ctypes.c_void_p), ("xdt", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ldx", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p), ("gs_mode", ctypes.c_int32)]
 
 
 def qconfig(fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
@@ -111,6 +121,10 @@ def lib():
         L.fp4_quantize_one_pass_fits.argtypes = [CP, I32, I64, I64, I64]
         L.fp4_global_scale.restype = ctypes.c_int
         L.fp4_global_scale.argtypes = [CP, P, I32, I64, I64, I64, P, P, SZ, P]
+        L.fp4_quantize_batch_workspace_bytes.restype = SZ
+        L.fp4_quantize_batch_workspace_bytes.argtypes = [I32]
+        L.fp4_quantize_batch.restype = ctypes.c_int
+        L.fp4_quantize_batch.argtypes = [I32, ctypes.POINTER(QuantJob), P, SZ, P]
         L.fp4_dequantize.restype = ctypes.c_int
         L.fp4_dequantize.argtypes = [CP, P, P, P, I64, I64, P, I32, I64, I32, P]
         L.fp4_error_workspace_bytes.restype = SZ
@@ -187,6 +201,25 @@ def fp4_quantize_one_pass_fits(cfg, xdt, rows, cols, ldx) -> int:
 def fp4_global_scale(cfg, x, xdt, rows, cols, ldx, global_scale, ws, ws_bytes, stream) -> int:
     return lib().fp4_global_scale(ctypes.byref(cfg), x, xdt, rows, cols, ldx, global_scale, ws,
                                   ws_bytes, stream)
+
+
+def fp4_quantize_batch_workspace_bytes(n: int) -> int:
+    return lib().fp4_quantize_batch_workspace_bytes(n)
+
+
+def quant_job(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, gs_mode) -> QuantJob:
+    """One job for fp4_quantize_batch (pointers are ints, None for NULL)."""
+    return QuantJob(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, gs_mode)
+
+
+def job_array(jobs):
+    """A ctypes array of QuantJob for fp4_quantize_batch."""
+    return (QuantJob * len(jobs))(*jobs)
+
+
+def fp4_quantize_batch(n, jobs, ws, ws_bytes, stream) -> int:
+    """Raw call: jobs is a ctypes array of QuantJob (job_array) or None."""
+    return lib().fp4_quantize_batch(n, jobs, ws, ws_bytes, stream)
 
 
 def fp4_dequantize(cfg, codes, scales, global_scale, rows, cols, y, ydt, ldy, inverse_rotate,
@@ -329,6 +362,47 @@ def quantize(x, fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
                       _stream())
     _check(rc, "fp4_quantize")
     return out
+
+
+def quantize_batch(items: list) -> list:
+    """Several quantizations in one fp4_quantize_batch call.  items: dicts
+    with the arguments of quantize() ("x" and "fmt", optionally "rotate",
+    "scale_layout", "global_scale", "rule", "rounding", "block_rows",
+    "signs", "seed", "out").  Returns one Quantized per item, the same as
+    quantize() would give."""
+    torch = _torch()
+    outs, jobs = [], []
+    dev = None
+    for it in items:
+        x, fmt = it["x"], it["fmt"]
+        assert x.dim() == 2 and x.stride(1) == 1
+        dev = x.device
+        rows, cols = x.shape
+        cfg = qconfig(fmt, it.get("rotate", False), it.get("scale_layout", SCALES_ROWMAJOR),
+                      it.get("rule", SCALE_ABSMAX), it.get("rounding", ROUND_NEAREST),
+                      it.get("block_rows", 1), it.get("signs", 0), it.get("seed", (0, 0)))
+        out = it.get("out")
+        if out is None:
+            codes = torch.empty(max(fp4_codes_bytes(rows, cols), 16), dtype=torch.uint8, device=dev)
+            scales = torch.empty(max(fp4_scales_bytes(cfg, rows, cols), 16), dtype=torch.uint8,
+                                 device=dev)
+            out = Quantized(codes, scales, torch.zeros(1, dtype=torch.float32, device=dev), cfg,
+                            rows, cols)
+        gs_mode = GS_COMPUTE
+        if fmt not in MX_FORMATS and it.get("global_scale") is not None:
+            out.global_scale.copy_(it["global_scale"].reshape(1))
+            gs_mode = GS_GIVEN
+        outs.append(out)
+        jobs.append(quant_job(cfg, x.data_ptr(), _dt(x), rows, cols, x.stride(0),
+                              out.codes.data_ptr(), out.scales.data_ptr(),
+                              out.global_scale.data_ptr(), gs_mode))
+    if not jobs:
+        return outs
+    wsb = fp4_quantize_batch_workspace_bytes(len(jobs))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    rc = fp4_quantize_batch(len(jobs), job_array(jobs), ws.data_ptr(), wsb, _stream())
+    _check(rc, "fp4_quantize_batch")
+    return outs
 
 
 def global_scale(x, rotate=False, out=None, fmt: int = FMT_NVFP4, signs: int = 0):

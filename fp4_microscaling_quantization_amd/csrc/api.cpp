@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "fp4.h"
 #include "fp4_device.h"
 #include "launch.h"
@@ -90,6 +92,65 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
 constexpr size_t kNvWorkspace = 8192;
 constexpr size_t kNvExchange = 4096;
 constexpr int kNvExchangeSlots = (int)((kNvWorkspace - kNvExchange - 64) / 8);
+// Batch workspace per job: the partial maxima of its tensor-scale pass.
+constexpr size_t kBatchJobWorkspace = 2048;
+
+// fp4_quantize's argument checks, apart from the workspace.
+int check_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows, int64_t cols,
+                   int64_t ldx, const uint8_t* codes, const uint8_t* scales,
+                   const float* global_scale, int32_t gs_mode) {
+  int rc = check_cfg(cfg, rows, cols);
+  if (rc != FP4_OK) return rc;
+  rc = check_ld(x, xdt, rows, cols, ldx);
+  if (rc != FP4_OK) return rc;
+  if (rows != 0 && cols != 0) {
+    if (!codes || !scales) return FP4_ERR_INVALID_ARG;
+    if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
+  }
+  if (fp4k::fmt_mx(cfg->fmt)) return FP4_OK;
+  if (gs_mode != FP4_GS_COMPUTE && gs_mode != FP4_GS_GIVEN && gs_mode != FP4_GS_COMPUTE_ONE_PASS)
+    return FP4_ERR_INVALID_ARG;
+  if (!global_scale) return FP4_ERR_INVALID_ARG;
+  return FP4_OK;
+}
+
+int quantize_mx(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows, int64_t cols,
+                int64_t ldx, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return FP4_OK;
+  return hip_status(fp4lib::launch_quantize_mx(cfg->fmt, x, xdt, rot_blocks(cfg), cfg->rule,
+                                               cfg->rounding, rows, cols, ldx, codes, scales,
+                                               gemm_layout(cfg) ? 1 : 0, qparams(cfg, cols), st));
+}
+
+// NVFP4 / NVINT4 in two passes: with partials (room for 512 floats) the
+// tensor-maximum pass first, then the encoding; without, the encoding with
+// the tensor scale read from *global_scale.
+int quantize_nv_passes(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows,
+                       int64_t cols, int64_t ldx, uint8_t* codes, uint8_t* scales,
+                       float* global_scale, float* partials, hipStream_t st) {
+  const bool empty = rows == 0 || cols == 0;
+  int npart = 0;
+  if (partials) {
+    if (empty) return hip_status(fp4lib::launch_amax_final(cfg->fmt, nullptr, 0, global_scale, st));
+    npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0, xdt);
+    hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, qparams(cfg, cols).signs[0],
+                                          rows, cols, ldx, partials, npart, st);
+    if (e != hipSuccess) return FP4_ERR_HIP;
+  }
+  if (empty) return FP4_OK;
+  return hip_status(fp4lib::launch_quantize_nv(cfg->fmt, x, xdt, cfg->rotate != 0, cfg->rule,
+                                               cfg->rounding, cfg->block_rows, rows, cols, ldx,
+                                               codes, scales, global_scale, partials, npart,
+                                               qparams(cfg, cols), st));
+}
+
+// Jobs that the grouped launches take (see fp4_quantize_batch).
+bool batch_mergeable(const fp4_quant_job& j) {
+  const fp4_qconfig& c = j.cfg;
+  return j.xdt == FP4_DT_BF16 && j.rows > 0 && j.cols > 0 && c.rule == FP4_SCALE_ABSMAX &&
+         c.rounding == FP4_ROUND_NEAREST && c.block_rows <= 1 &&
+         (c.rotate == 0 || c.rotate == c.block);
+}
 
 }  // namespace
 
@@ -136,33 +197,16 @@ int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols, int
 int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t rows, int64_t cols,
                  int64_t ldx, uint8_t* codes, uint8_t* scales, float* global_scale,
                  int32_t gs_mode, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_cfg(cfg, rows, cols);
+  const int rc = check_quantize(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, gs_mode);
   if (rc != FP4_OK) return rc;
-  rc = check_ld(x, xdt, rows, cols, ldx);
-  if (rc != FP4_OK) return rc;
-  const bool empty = rows == 0 || cols == 0;
-  if (!empty) {
-    if (!codes || !scales) return FP4_ERR_INVALID_ARG;
-    if (!aligned16(codes)) return FP4_ERR_ALIGNMENT;
-  }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (fp4k::fmt_mx(cfg->fmt)) {
-    if (empty) return FP4_OK;
-    return hip_status(fp4lib::launch_quantize_mx(cfg->fmt, x, xdt, rot_blocks(cfg), cfg->rule,
-                                                 cfg->rounding, rows, cols, ldx, codes, scales,
-                                                 gemm_layout(cfg) ? 1 : 0, qparams(cfg, cols), st));
-  }
-  if (gs_mode != FP4_GS_COMPUTE && gs_mode != FP4_GS_GIVEN && gs_mode != FP4_GS_COMPUTE_ONE_PASS)
-    return FP4_ERR_INVALID_ARG;
-  if (!global_scale) return FP4_ERR_INVALID_ARG;
+  if (fp4k::fmt_mx(cfg->fmt)) return quantize_mx(cfg, x, xdt, rows, cols, ldx, codes, scales, st);
   float* partials = nullptr;
-  int npart = 0;
   if (gs_mode != FP4_GS_GIVEN) {
     if (!ws || ws_bytes < fp4_workspace_bytes(cfg, rows, cols)) return FP4_ERR_WORKSPACE;
     const uintptr_t amask = gs_mode == FP4_GS_COMPUTE_ONE_PASS ? 7u : 3u;  // 64-bit slots
     if ((reinterpret_cast<uintptr_t>(ws) & amask) != 0) return FP4_ERR_ALIGNMENT;
-    if (empty) return hip_status(fp4lib::launch_amax_final(cfg->fmt, nullptr, 0, global_scale, st));
-    if (gs_mode == FP4_GS_COMPUTE_ONE_PASS) {
+    if (gs_mode == FP4_GS_COMPUTE_ONE_PASS && rows != 0 && cols != 0) {
       uint32_t* xchg = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kNvExchange);
       const hipError_t e = fp4lib::launch_quantize_nv_one_pass(
           cfg->fmt, x, xdt, cfg->rotate != 0, cfg->rule, cfg->rounding, cfg->block_rows, rows, cols,
@@ -170,16 +214,63 @@ int fp4_quantize(const fp4_qconfig* cfg, const void* x, int32_t xdt, int64_t row
       if (e != hipErrorNotSupported) return hip_status(e);
     }
     partials = static_cast<float*>(ws);
-    npart = fp4lib::amax_partials(rows, cols, cfg->rotate != 0, xdt);
-    hipError_t e = fp4lib::launch_amax_nv(x, xdt, cfg->rotate != 0, qparams(cfg, cols).signs[0],
-                                          rows, cols, ldx, partials, npart, st);
-    if (e != hipSuccess) return FP4_ERR_HIP;
   }
-  if (empty) return FP4_OK;
-  return hip_status(fp4lib::launch_quantize_nv(cfg->fmt, x, xdt, cfg->rotate != 0, cfg->rule,
-                                               cfg->rounding, cfg->block_rows, rows, cols, ldx,
-                                               codes, scales, global_scale, partials, npart,
-                                               qparams(cfg, cols), st));
+  return quantize_nv_passes(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, partials, st);
+}
+
+size_t fp4_quantize_batch_workspace_bytes(int32_t n) {
+  return n > 0 ? (size_t)n * kBatchJobWorkspace : 0;
+}
+
+int fp4_quantize_batch(int32_t n, const fp4_quant_job* jobs, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (n < 0) return FP4_ERR_INVALID_ARG;
+  if (n == 0) return FP4_OK;
+  if (!jobs) return FP4_ERR_INVALID_ARG;
+  bool need_ws = false;
+  for (int32_t i = 0; i < n; ++i) {
+    const fp4_quant_job& j = jobs[i];
+    const int rc = check_quantize(&j.cfg, j.x, j.xdt, j.rows, j.cols, j.ldx, j.codes, j.scales,
+                                  j.global_scale, j.gs_mode);
+    if (rc != FP4_OK) return rc;
+    if (!fp4k::fmt_mx(j.cfg.fmt) && j.gs_mode != FP4_GS_GIVEN) need_ws = true;
+  }
+  if (need_ws) {
+    if (!ws || ws_bytes < fp4_quantize_batch_workspace_bytes(n)) return FP4_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<fp4lib::BatchItem> items;
+  items.reserve((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const fp4_quant_job& j = jobs[i];
+    const bool mx = fp4k::fmt_mx(j.cfg.fmt);
+    float* part = !mx && j.gs_mode != FP4_GS_GIVEN
+                      ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + i * kBatchJobWorkspace)
+                      : nullptr;
+    if (batch_mergeable(j)) {
+      fp4lib::BatchItem it{};
+      it.fmt = j.cfg.fmt;
+      it.rotate = j.cfg.rotate != 0 ? 1 : 0;
+      it.gemm_layout = gemm_layout(&j.cfg) ? 1 : 0;
+      it.x = j.x;
+      it.rows = j.rows;
+      it.cols = j.cols;
+      it.ldx = j.ldx;
+      it.codes = j.codes;
+      it.scales = j.scales;
+      it.gs = mx ? nullptr : j.global_scale;
+      it.partials = part;
+      it.P = qparams(&j.cfg, j.cols);
+      items.push_back(it);
+      continue;
+    }
+    const int rc = mx ? quantize_mx(&j.cfg, j.x, j.xdt, j.rows, j.cols, j.ldx, j.codes, j.scales, st)
+                      : quantize_nv_passes(&j.cfg, j.x, j.xdt, j.rows, j.cols, j.ldx, j.codes,
+                                           j.scales, j.global_scale, part, st);
+    if (rc != FP4_OK) return rc;
+  }
+  return hip_status(fp4lib::launch_quantize_batch(items.data(), (int)items.size(), st));
 }
 
 int fp4_workspace_init(void* ws, size_t ws_bytes, void* stream) {

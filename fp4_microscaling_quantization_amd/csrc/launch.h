@@ -33,6 +33,25 @@ hipError_t launch_quantize_nv_one_pass(int fmt, const void* x, int xdt, int rota
                                        int64_t ldx, uint8_t* codes, uint8_t* scales, float* gs,
                                        uint32_t* xchg, int max_grid, const fp4k::QParams& P,
                                        hipStream_t st);
+// One quantization of a grouped launch: bf16 input, absmax block scales,
+// nearest rounding, one-row blocks, no rotation or the block-sized one
+// (rotate != 0), rows > 0 and cols > 0.  partials: nullptr for the MX
+// formats and for NVFP4 / NVINT4 with the tensor scale given in *gs;
+// otherwise 2048 bytes for the maxima of the tensor-scale pass (the first
+// launch writes them, the second launch encodes from them and stores *gs).
+struct BatchItem {
+  int fmt, rotate, gemm_layout;
+  const void* x;
+  int64_t rows, cols, ldx;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* gs;
+  float* partials;
+  fp4k::QParams P;
+};
+// All items in at most two launches of one kernel (more when there are more
+// than 16 per launch).
+hipError_t launch_quantize_batch(const BatchItem* items, int n, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t st);
 hipError_t launch_scales_to_gemm(const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
                                  hipStream_t st);

@@ -709,24 +709,31 @@ __device__ __forceinline__ NvTs nv_ts_finish(const NvTsLoads& L, float* __restri
 // issues the loads of TPW tiles before any arithmetic, then runs them one by
 // one through its LDS buffer.  The scale bytes of a wave tile are 64
 // consecutive bytes of its row.
+// LDS bytes of a quant_rows workgroup.
+template <int FMT>
+constexpr int rows_lds_bytes() {
+  return (kThreads / 64) * 64 * (fmt_block(FMT) * 2 + 16);
+}
+
+// Body of the row-tile kernel for workgroup bid of nbid, LDS at lds.
 template <int FMT, int ROT, int TPW, int RULE, int RND>
-__global__ __launch_bounds__(kThreads) void quant_rows_kernel(
-    const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t wpr,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
-    float* __restrict__ gs, const float* __restrict__ partials, int npart, QParams P) {
+__device__ __forceinline__ void quant_rows_body(
+    uint8_t* lds, uint32_t bid, uint32_t nbid, const uint8_t* __restrict__ x, int64_t ldx_bytes,
+    uint32_t rows, uint32_t nb, uint32_t wpr, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout, float* __restrict__ gs,
+    const float* __restrict__ partials, int npart, const QParams& P) {
   constexpr int G = fmt_block(FMT);
   constexpr int BB = G * 2;        // bytes per block
   constexpr int CH = BB / 16;      // 16-byte chunks per block
   constexpr int STRIDE = BB + 16;  // padded LDS stride
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][64 * STRIDE];
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_index();
   const uint32_t tiles = rows * wpr;
-  const uint32_t step = gridDim.x * (kThreads / 64) * TPW;
-  uint32_t t0 = (blockIdx.x * (kThreads / 64) + wave) * TPW;
+  const uint32_t step = nbid * (kThreads / 64) * TPW;
+  uint32_t t0 = (bid * (kThreads / 64) + wave) * TPW;
   if (t0 >= tiles) return;
   const uint32_t last_chunk = nb * CH - 1;
-  uint8_t* l = lds[wave];
+  uint8_t* l = lds + wave * (64 * STRIDE);
   u32x4 t[TPW][CH];
   auto load = [&](uint32_t first) {
 #pragma unroll
@@ -743,7 +750,7 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
   if constexpr (!fmt_mx(FMT)) tsl = nv_ts_issue(gs, partials, npart);
   load(t0);
   NvTs T{};
-  if constexpr (!fmt_mx(FMT)) T = nv_ts_finish<FMT>(tsl, gs, npart, blockIdx.x == 0 && wave == 0);
+  if constexpr (!fmt_mx(FMT)) T = nv_ts_finish<FMT>(tsl, gs, npart, bid == 0 && wave == 0);
   for (;;) {
     // all tiles computed before any store, so no store sits between a tile
     // load and the wait for it
@@ -778,6 +785,17 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     if (t0 >= tiles) break;
     load(t0);
   }
+}
+
+template <int FMT, int ROT, int TPW, int RULE, int RND>
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(
+    const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t wpr,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, int gemm_layout,
+    float* __restrict__ gs, const float* __restrict__ partials, int npart, QParams P) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[rows_lds_bytes<FMT>()];
+  quant_rows_body<FMT, ROT, TPW, RULE, RND>(lds, blockIdx.x, gridDim.x, x, ldx_bytes, rows, nb, wpr,
+                                            codes, scales, kchunks, gemm_layout, gs, partials,
+                                            npart, P);
 }
 
 // NVFP4 / NVINT4 with the tensor scale computed in the same launch, for a
@@ -990,18 +1008,20 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
 // 8w .. 8w + 7 of the tile; load j brings rows 2j, 2j + 1 (512 bytes each);
 // after the LDS transpose lane l holds block l % 8 of row l / 8, and the
 // codes of each row (8 blocks) are 128 contiguous bytes.
+constexpr int kMxGemmLds = (kThreads / 64) * 64 * (64 + 16);
+
 template <int FMT, int ROT, int RULE, int RND>
-__global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
-    const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t kcs,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, QParams P) {
+__device__ __forceinline__ void quant_mx_gemm_body(
+    uint8_t* lds, uint32_t bid, uint32_t nbid, const uint8_t* __restrict__ x, int64_t ldx_bytes,
+    uint32_t rows, uint32_t nb, uint32_t kcs, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t kchunks, const QParams& P) {
   constexpr int STRIDE = 64 + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kThreads / 64][64 * STRIDE];
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_index();
   const uint32_t tiles = ((rows + 31) / 32) * kcs;
   const uint32_t cpr = nb * 4;  // 16-byte chunks per row
-  uint8_t* l = lds[wave];
-  for (uint32_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+  uint8_t* l = lds + wave * (64 * STRIDE);
+  for (uint32_t tile = bid; tile < tiles; tile += nbid) {
     const uint32_t rt = tile / kcs, kc = tile - rt * kcs;
     const uint32_t r0 = rt * 32 + wave * 8;
     u32x4 t[4];
@@ -1028,25 +1048,34 @@ __global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
   }
 }
 
+template <int FMT, int ROT, int RULE, int RND>
+__global__ __launch_bounds__(kThreads) void quant_mx_gemm_kernel(
+    const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t rows, uint32_t nb, uint32_t kcs,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t kchunks, QParams P) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMxGemmLds];
+  quant_mx_gemm_body<FMT, ROT, RULE, RND>(lds, blockIdx.x, gridDim.x, x, ldx_bytes, rows, nb, kcs,
+                                          codes, scales, kchunks, P);
+}
+
 // NVFP4 tensor amax over bf16 input in the same wave tiles, 16 waves per
 // workgroup, one partial maximum per workgroup.  Rotated: the maximum of the
 // block-Hadamard outputs (8-point transform in registers, then the cross-lane
 // stage; the exact 1/4 is applied to the final maximum).
 constexpr int kAmaxThreads = 1024;
 
-template <bool ROT>
-__global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t* __restrict__ x,
-                                                                  int64_t ldx_bytes, uint32_t rows,
-                                                                  uint32_t cpr, uint32_t wpr,
-                                                                  float* __restrict__ partials,
-                                                                  uint32_t sign_mask) {
+// Body for workgroup bid of nbid with NW waves; red: NW floats of LDS.
+template <bool ROT, int NW>
+__device__ __forceinline__ void amax_chunk_body(float* red, uint32_t bid, uint32_t nbid,
+                                                const uint8_t* __restrict__ x, int64_t ldx_bytes,
+                                                uint32_t rows, uint32_t cpr, uint32_t wpr,
+                                                float* __restrict__ partials, uint32_t sign_mask) {
   const int lane = threadIdx.x & 63;
   const uint32_t wave = wave_index();
   const uint32_t tiles = rows * wpr;
-  const uint32_t step = gridDim.x * (kAmaxThreads / 64);
+  const uint32_t step = nbid * NW;
   uint32_t mb = 0;   // plain: max of |x| bf16 bits
   float mf = 0.0f;   // rotated: max of |H x| before the 1/4
-  for (uint32_t tile = blockIdx.x * (kAmaxThreads / 64) + wave; tile < tiles; tile += step) {
+  for (uint32_t tile = bid * NW + wave; tile < tiles; tile += step) {
     const uint32_t r = tile / wpr;
     const uint32_t q0 = (tile - r * wpr) * 256 + lane;
     const uint8_t* row = x + (int64_t)r * ldx_bytes;
@@ -1077,14 +1106,113 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t*
   float m = ROT ? mf : as_f(mb << 16);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  __shared__ float red[kAmaxThreads / 64];
   if (lane == 0) red[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     float r = red[0];
 #pragma unroll
-    for (int i = 1; i < kAmaxThreads / 64; ++i) r = fmaxf(r, red[i]);
-    partials[blockIdx.x] = ROT ? r * 0.25f : r;  // 1/sqrt(16), exact
+    for (int i = 1; i < NW; ++i) r = fmaxf(r, red[i]);
+    partials[bid] = ROT ? r * 0.25f : r;  // 1/sqrt(16), exact
+  }
+}
+
+template <bool ROT>
+__global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t* __restrict__ x,
+                                                                  int64_t ldx_bytes, uint32_t rows,
+                                                                  uint32_t cpr, uint32_t wpr,
+                                                                  float* __restrict__ partials,
+                                                                  uint32_t sign_mask) {
+  __shared__ float red[kAmaxThreads / 64];
+  amax_chunk_body<ROT, kAmaxThreads / 64>(red, blockIdx.x, gridDim.x, x, ldx_bytes, rows, cpr, wpr,
+                                          partials, sign_mask);
+}
+
+// ---------------------------------------------------------- grouped launch
+// Several quantizations in one launch: segment s owns workgroups
+// [first_wg, first_wg + nwg) and runs one of the three bodies above (MXFP4 /
+// MXINT4 GEMM-layout tiles, row tiles, or the NVFP4 / NVINT4 tensor-maximum
+// pass with four waves per workgroup) on its own tensor, with the work split
+// of that body's own launch.  One ramp-up and one drain for the whole group
+// instead of one per tensor.
+constexpr int kSegMxGemm = 0, kSegRows = 1, kSegAmax = 2;
+constexpr int kBatchSegs = 16;
+constexpr int kBatchLds = kMxGemmLds > rows_lds_bytes<FP4_FMT_MXFP4>()
+                              ? kMxGemmLds
+                              : rows_lds_bytes<FP4_FMT_MXFP4>();
+static_assert(kBatchLds >= rows_lds_bytes<FP4_FMT_NVFP4>(), "LDS of the grouped kernel");
+
+constexpr uint32_t seg_sel(int kind, int fmt, int rot) {
+  return (uint32_t)kind | ((uint32_t)fmt << 4) | ((uint32_t)rot << 8);
+}
+
+struct BatchSeg {
+  const uint8_t* x;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* gs;
+  float* partials;  // amax: written; rows (NVFP4 / NVINT4): read when npart > 0
+  int64_t ldx_bytes;
+  int64_t kchunks;
+  uint32_t first_wg, nwg;
+  uint32_t rows, nb;
+  uint32_t aux;     // kcs (GEMM-layout tiles), wpr (row tiles), cpr (amax)
+  uint32_t aux2;    // wpr (amax)
+  int32_t npart;
+  uint32_t sel;
+  QParams P;
+};
+
+struct BatchArgs {
+  uint32_t nseg;
+  uint32_t pad[3];
+  BatchSeg seg[kBatchSegs];
+};
+
+__global__ __launch_bounds__(kThreads) void quant_batch_kernel(BatchArgs A) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kBatchLds];
+  const uint32_t b = blockIdx.x;
+  uint32_t s = 0;
+  for (uint32_t i = 1; i < A.nseg; ++i) s = b >= A.seg[i].first_wg ? i : s;
+  const BatchSeg& S = A.seg[s];
+  const uint32_t bid = b - S.first_wg;
+  constexpr int AB = FP4_SCALE_ABSMAX;
+  switch (S.sel) {
+#define FP4_SEG_MXG(F, R)                                                                      \
+  case seg_sel(kSegMxGemm, F, R):                                                              \
+    quant_mx_gemm_body<F, R, AB, 0>(lds, bid, S.nwg, S.x, S.ldx_bytes, S.rows, S.nb, S.aux,    \
+                                    S.codes, S.scales, S.kchunks, S.P);                        \
+    break;
+#define FP4_SEG_ROWS(F, R)                                                                     \
+  case seg_sel(kSegRows, F, R):                                                                \
+    quant_rows_body<F, R, fmt_mx(F) ? 1 : 2, AB, 0>(lds, bid, S.nwg, S.x, S.ldx_bytes, S.rows, \
+                                                    S.nb, S.aux, S.codes, S.scales, S.kchunks, \
+                                                    0, S.gs, S.partials, S.npart, S.P);        \
+    break;
+    FP4_SEG_MXG(FP4_FMT_MXFP4, 0)
+    FP4_SEG_MXG(FP4_FMT_MXFP4, 1)
+    FP4_SEG_MXG(FP4_FMT_MXINT4, 0)
+    FP4_SEG_MXG(FP4_FMT_MXINT4, 1)
+    FP4_SEG_ROWS(FP4_FMT_MXFP4, 0)
+    FP4_SEG_ROWS(FP4_FMT_MXINT4, 0)
+    FP4_SEG_ROWS(FP4_FMT_MXFP4, 1)
+    FP4_SEG_ROWS(FP4_FMT_MXINT4, 1)
+    FP4_SEG_ROWS(FP4_FMT_NVFP4, 0)
+    FP4_SEG_ROWS(FP4_FMT_NVFP4, 1)
+    FP4_SEG_ROWS(FP4_FMT_NVINT4, 0)
+    FP4_SEG_ROWS(FP4_FMT_NVINT4, 1)
+#undef FP4_SEG_ROWS
+#undef FP4_SEG_MXG
+    case seg_sel(kSegAmax, 0, 0):
+      amax_chunk_body<false, kThreads / 64>(reinterpret_cast<float*>(lds), bid, S.nwg, S.x,
+                                            S.ldx_bytes, S.rows, S.aux, S.aux2, S.partials, 0u);
+      break;
+    case seg_sel(kSegAmax, 0, 1):
+      amax_chunk_body<true, kThreads / 64>(reinterpret_cast<float*>(lds), bid, S.nwg, S.x,
+                                           S.ldx_bytes, S.rows, S.aux, S.aux2, S.partials,
+                                           S.P.signs[0]);
+      break;
+    default:
+      break;
   }
 }
 
@@ -1529,6 +1657,90 @@ hipError_t launch_quantize_nv(int fmt, const void* x, int xdt, int rotate, int r
   if (rule == FP4_SCALE_FOUR_OVER_SIX)
     return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_FOUR_OVER_SIX, 0>(x, xdt, rb, rows, cols, ldx, codes, scales, 0, gs, partials, npart, P, st);
   return launch_q_rule<FP4_FMT_NVFP4, FP4_SCALE_ABSMAX, 0>(x, xdt, rb, rows, cols, ldx, codes, scales, 0, gs, partials, npart, P, st);
+}
+
+int batch_amax_partials(int64_t rows, int64_t cols) {
+  const int64_t tiles = rows * ((cols / 8 + 255) / 256);
+  int64_t g = (tiles + kThreads / 64 - 1) / (kThreads / 64);
+  if (g > kAmaxGrid) g = kAmaxGrid;
+  return (int)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_quantize_batch(const BatchItem* items, int n, hipStream_t st) {
+  BatchArgs A{};
+  uint32_t wgs = 0;
+  hipError_t err = hipSuccess;
+  auto flush = [&]() {
+    if (A.nseg > 0 && err == hipSuccess) {
+      quant_batch_kernel<<<wgs, kThreads, 0, st>>>(A);
+      err = hipGetLastError();
+    }
+    A.nseg = 0;
+    wgs = 0;
+  };
+  auto add = [&](const BatchSeg& seg) {
+    if (A.nseg == (uint32_t)kBatchSegs) flush();
+    A.seg[A.nseg] = seg;
+    A.seg[A.nseg].first_wg = wgs;
+    wgs += seg.nwg;
+    ++A.nseg;
+  };
+  auto base = [](const BatchItem& it) {
+    BatchSeg g{};
+    g.x = static_cast<const uint8_t*>(it.x);
+    g.codes = it.codes;
+    g.scales = it.scales;
+    g.gs = it.gs;
+    g.ldx_bytes = it.ldx * 2;
+    g.kchunks = mx_gemm_kchunks(it.cols);
+    g.rows = (uint32_t)it.rows;
+    g.nb = (uint32_t)(it.cols / fmt_block(it.fmt));
+    g.P = it.P;
+    return g;
+  };
+  auto encode_seg = [&](const BatchItem& it, int npart) {
+    BatchSeg g = base(it);
+    const int rot = it.rotate ? 1 : 0;
+    if (fmt_mx(it.fmt) && it.gemm_layout) {
+      const uint32_t kcs = (g.nb + 7) / 8;
+      int64_t wg = ((it.rows + 31) / 32) * (int64_t)kcs;
+      g.nwg = (uint32_t)(wg > 16384 ? 16384 : wg);
+      g.aux = kcs;
+      g.sel = seg_sel(kSegMxGemm, it.fmt, rot);
+    } else {
+      const int tpw = fmt_mx(it.fmt) ? 1 : 2;
+      const uint32_t wpr = (g.nb + 63) / 64;
+      const int64_t waves = (it.rows * (int64_t)wpr + tpw - 1) / tpw;
+      int64_t wg = (waves + kThreads / 64 - 1) / (kThreads / 64);
+      g.nwg = (uint32_t)(wg > 8192 ? 8192 : wg);
+      g.aux = wpr;
+      g.partials = it.partials;
+      g.npart = npart;
+      g.sel = seg_sel(kSegRows, it.fmt, rot);
+    }
+    add(g);
+  };
+  // launch 1: the maxima first (their workgroups run longest), then every
+  // encoding that needs nothing else
+  for (int i = 0; i < n; ++i) {
+    const BatchItem& it = items[i];
+    if (it.partials == nullptr) continue;
+    BatchSeg g = base(it);
+    g.nwg = (uint32_t)batch_amax_partials(it.rows, it.cols);
+    g.aux = (uint32_t)(it.cols / 8);
+    g.aux2 = (g.aux + 255) / 256;
+    g.partials = it.partials;
+    g.sel = seg_sel(kSegAmax, 0, it.rotate ? 1 : 0);
+    add(g);
+  }
+  for (int i = 0; i < n; ++i)
+    if (items[i].partials == nullptr) encode_seg(items[i], 0);
+  flush();
+  // launch 2: the encodings that read the maxima of launch 1
+  for (int i = 0; i < n; ++i)
+    if (items[i].partials != nullptr) encode_seg(items[i], batch_amax_partials(items[i].rows, items[i].cols));
+  flush();
+  return err;
 }
 
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t st) {

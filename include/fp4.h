@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP4_ABI_VERSION 3
+#define FP4_ABI_VERSION 4
 
 typedef enum {
     FP4_OK = 0,
@@ -235,6 +235,50 @@ int fp4_quantize_one_pass_fits(const fp4_qconfig* cfg, int32_t xdt, int64_t rows
 int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt,
                      int64_t rows, int64_t cols, int64_t ldx, float* global_scale,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* One quantization of a batch: the arguments of fp4_quantize. */
+typedef struct {
+    fp4_qconfig cfg;
+    const void* x;
+    int32_t xdt;
+    int64_t rows;
+    int64_t cols;
+    int64_t ldx;
+    uint8_t* codes;
+    uint8_t* scales;
+    float* global_scale;
+    int32_t gs_mode;
+} fp4_quant_job;
+
+/* Workspace bytes of fp4_quantize_batch for n jobs: 2048 per job.  Host
+ * function. */
+size_t fp4_quantize_batch_workspace_bytes(int32_t n);
+
+/* n independent quantizations, each exactly as fp4_quantize defines it (the
+ * same codes, scales and tensor scale as n fp4_quantize calls), in few
+ * launches.  Jobs with bf16 input, absmax block scales, nearest rounding,
+ * one-row blocks and no rotation or the block-sized one share two launches
+ * of one kernel: the first holds every MXFP4 / MXINT4 job, every NVFP4 /
+ * NVINT4 job with its tensor scale given and the tensor-maximum pass of the
+ * NVFP4 / NVINT4 jobs that compute it; the second encodes those jobs (16 jobs
+ * per launch; more make more launches).  Each tensor then pays one share of
+ * a launch's ramp-up and drain instead of a whole one.  Other jobs (other
+ * configurations, fp32 input, empty tensors) run first, as their own
+ * fp4_quantize launches, in job order.  An NVFP4 / NVINT4 job with
+ * FP4_GS_COMPUTE_ONE_PASS runs as FP4_GS_COMPUTE (same results; no exchange
+ * region involved).
+ * jobs: host array of n jobs, read during the call only; each job follows
+ *   fp4_quantize's argument rules.  No job's outputs may overlap another
+ *   job's input or outputs.
+ * ws/ws_bytes: device workspace of fp4_quantize_batch_workspace_bytes(n)
+ *   bytes, 4-byte aligned, any contents (job i uses bytes [2048 i,
+ *   2048 i + 2048) when it computes its tensor scale); may be NULL when no
+ *   job computes one.
+ * Every job is checked before anything is launched: the first failing job's
+ * status is returned and nothing runs.  n == 0 is a no-op; n < 0, or
+ * jobs == NULL with n > 0, is FP4_ERR_INVALID_ARG.  Asynchronous on stream. */
+int fp4_quantize_batch(int32_t n, const fp4_quant_job* jobs, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* ----------------------------------------------------------- dequantize */
 

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(fp4.EXPORTED)
-    assert L.fp4_abi_version() == 3
+    assert L.fp4_abi_version() == 4
     assert fp4.status_str(fp4.FP4_ERR_ALIGNMENT).startswith("misaligned")
 
 
@@ -141,6 +141,49 @@ def test_quantize_rejects_bad_arguments_on_host():
     # an empty MXFP4 tensor is a no-op that launches nothing
     assert _q(mx, rows=0, x=None, codes=None, scales=None) == E.FP4_OK
     assert _q(mx, cols=0, x=None, codes=None, scales=None) == E.FP4_OK
+
+
+def _job(cfg, rows=64, cols=256, ldx=256, x=FAKE, xdt=None, codes=FAKE, scales=FAKE, gs=FAKE,
+         gs_mode=fp4.GS_COMPUTE):
+    return fp4.quant_job(cfg, x, fp4.DT_BF16 if xdt is None else xdt, rows, cols, ldx, codes,
+                         scales, gs, gs_mode)
+
+
+def test_quantize_batch_rejects_bad_arguments_on_host():
+    """Every job is checked before anything is launched; the first failing
+    job's status comes back (fake pointers: a launch would fault, so reaching
+    one would crash this CPU test)."""
+    E = fp4
+    mx = fp4.qconfig(fp4.FMT_MXFP4, scale_layout=fp4.SCALES_GEMM)
+    nv = fp4.qconfig(fp4.FMT_NVFP4, True)
+    assert ctypes.sizeof(fp4.QuantJob) == 128
+    assert fp4.fp4_quantize_batch_workspace_bytes(0) == 0
+    assert fp4.fp4_quantize_batch_workspace_bytes(3) == 3 * 2048
+    assert fp4.fp4_quantize_batch_workspace_bytes(-1) == 0
+    good = [_job(mx), _job(nv)]
+
+    def run(jobs, ws=FAKE, ws_bytes=None, n=None):
+        n = len(jobs) if n is None else n
+        wsb = 2048 * len(jobs) if ws_bytes is None else ws_bytes
+        return fp4.fp4_quantize_batch(n, fp4.job_array(jobs) if jobs else None, ws, wsb, None)
+
+    assert run([]) == E.FP4_OK                                   # n == 0: nothing to do
+    assert fp4.fp4_quantize_batch(-1, None, None, 0, None) == E.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_quantize_batch(2, None, FAKE, 4096, None) == E.FP4_ERR_INVALID_ARG
+    # a bad job anywhere stops the whole batch, with that job's status
+    assert run(good + [_job(mx, cols=48)]) == E.FP4_ERR_INVALID_ARG
+    assert run(good + [_job(mx, x=MIS)]) == E.FP4_ERR_ALIGNMENT
+    assert run(good + [_job(mx, codes=MIS)]) == E.FP4_ERR_ALIGNMENT
+    assert run(good + [_job(nv, gs=None)]) == E.FP4_ERR_INVALID_ARG
+    assert run(good + [_job(nv, gs_mode=7)]) == E.FP4_ERR_INVALID_ARG
+    assert run(good + [_job(mx, xdt=9)]) == E.FP4_ERR_INVALID_ARG
+    assert run(good + [_job(fp4.qconfig(fp4.FMT_MXFP4, block_rows=16))]) == E.FP4_ERR_UNSUPPORTED
+    # workspace: 2048 bytes per job, 4-byte aligned, when a job computes a tensor scale
+    assert run(good, ws=None) == E.FP4_ERR_WORKSPACE
+    assert run(good, ws_bytes=2 * 2048 - 4) == E.FP4_ERR_WORKSPACE
+    assert run(good, ws=FAKE + 2) == E.FP4_ERR_ALIGNMENT
+    # all jobs empty: valid, and no workspace is needed for the MX formats
+    assert run([_job(mx, rows=0, x=None, codes=None, scales=None)], ws=None) == E.FP4_OK
 
 
 def test_dequantize_error_sums_and_relayout_reject_bad_arguments():
