@@ -7,8 +7,10 @@ Timed step (``value``): one pass of block-wise FP4 quantization over the
 NVFP4} x {no rotation, block Hadamard of the block size}, as one
 fp4_quantize_batch call: two launches of the grouped kernel (the four MXFP4
 encodings and the four NVFP4 tensor maxima, then the four NVFP4 encodings).
-Inputs are resident in HBM; the step cycles through several copies of every
-input and output so that the 256 MB last-level cache cannot serve a repeat.
+Inputs are resident in HBM; every variant reads its own input buffers, and the
+step cycles through several copies of every input and output, so that the
+256 MB last-level cache serves neither one variant's read to another nor a
+repeat.
 
 ``value`` = algorithmic bytes of the step (bf16 read once + codes + scales)
 divided by the step time, in GB/s, over K eagerly issued steps (after W
@@ -145,6 +147,9 @@ def main():
 
     variants = [(d, fmt, rot) for d in ("gauss", "laplace")
                 for fmt in (fp4.FMT_MXFP4, fp4.FMT_NVFP4) for rot in (False, True)]
+    # every variant reads its own buffers (the same values), so no variant's
+    # read is served from the cache lines another variant brought in
+    xv = {v: [x.clone() for x in xs[v[0]]] for v in variants}
     FN = {fp4.FMT_MXFP4: "mxfp4", fp4.FMT_NVFP4: "nvfp4", fp4.FMT_MXINT4: "mxint4",
           fp4.FMT_NVINT4: "nvint4"}
 
@@ -175,7 +180,7 @@ def main():
         jl = []
         for v in variants:
             q = outs[v][c]
-            jl.append(fp4.quant_job(q.cfg, xs[v[0]][c].data_ptr(), fp4.DT_BF16, rows, cols, cols,
+            jl.append(fp4.quant_job(q.cfg, xv[v][c].data_ptr(), fp4.DT_BF16, rows, cols, cols,
                                     q.codes.data_ptr(), q.scales.data_ptr(),
                                     q.global_scale.data_ptr(), fp4.GS_COMPUTE))
         batch_jobs.append(fp4.job_array(jl))
@@ -197,7 +202,7 @@ def main():
         'amax' runs only the NVFP4 tensor-scale pass; 'given' only the NVFP4
         quantize kernel with the tensor scale already in place."""
         d, fmt, rot = v
-        x = xs[d][c]
+        x = xv[v][c]
         q = outs[v][c]
         h = sh if sh is not None else sh_now()
         if fmt == fp4.FMT_MXFP4:

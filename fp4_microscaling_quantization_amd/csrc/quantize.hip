@@ -1168,14 +1168,36 @@ struct BatchArgs {
   BatchSeg seg[kBatchSegs];
 };
 
+// NV_ROWS: only NVFP4 / NVINT4 row-tile segments (the second launch), so the
+// kernel needs that body's registers and LDS alone.
+template <bool NV_ROWS>
 __global__ __launch_bounds__(kThreads) void quant_batch_kernel(BatchArgs A) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kBatchLds];
+  __shared__ __attribute__((aligned(16)))
+  uint8_t lds[NV_ROWS ? rows_lds_bytes<FP4_FMT_NVFP4>() : kBatchLds];
   const uint32_t b = blockIdx.x;
   uint32_t s = 0;
   for (uint32_t i = 1; i < A.nseg; ++i) s = b >= A.seg[i].first_wg ? i : s;
   const BatchSeg& S = A.seg[s];
   const uint32_t bid = b - S.first_wg;
   constexpr int AB = FP4_SCALE_ABSMAX;
+  if constexpr (NV_ROWS) {
+#define FP4_SEG_NV(F, R)                                                                       \
+  case seg_sel(kSegRows, F, R):                                                                \
+    quant_rows_body<F, R, 2, AB, 0>(lds, bid, S.nwg, S.x, S.ldx_bytes, S.rows, S.nb, S.aux,    \
+                                    S.codes, S.scales, S.kchunks, 0, S.gs, S.partials,         \
+                                    S.npart, S.P);                                             \
+    break;
+    switch (S.sel) {
+      FP4_SEG_NV(FP4_FMT_NVFP4, 0)
+      FP4_SEG_NV(FP4_FMT_NVFP4, 1)
+      FP4_SEG_NV(FP4_FMT_NVINT4, 0)
+      FP4_SEG_NV(FP4_FMT_NVINT4, 1)
+      default:
+        break;
+    }
+#undef FP4_SEG_NV
+    return;
+  }
   switch (S.sel) {
 #define FP4_SEG_MXG(F, R)                                                                      \
   case seg_sel(kSegMxGemm, F, R):                                                              \
@@ -1669,10 +1691,14 @@ int batch_amax_partials(int64_t rows, int64_t cols) {
 hipError_t launch_quantize_batch(const BatchItem* items, int n, hipStream_t st) {
   BatchArgs A{};
   uint32_t wgs = 0;
+  bool nv_rows_only = false;  // the second launch
   hipError_t err = hipSuccess;
   auto flush = [&]() {
     if (A.nseg > 0 && err == hipSuccess) {
-      quant_batch_kernel<<<wgs, kThreads, 0, st>>>(A);
+      if (nv_rows_only)
+        quant_batch_kernel<true><<<wgs, kThreads, 0, st>>>(A);
+      else
+        quant_batch_kernel<false><<<wgs, kThreads, 0, st>>>(A);
       err = hipGetLastError();
     }
     A.nseg = 0;
@@ -1737,6 +1763,7 @@ hipError_t launch_quantize_batch(const BatchItem* items, int n, hipStream_t st) 
     if (items[i].partials == nullptr) encode_seg(items[i], 0);
   flush();
   // launch 2: the encodings that read the maxima of launch 1
+  nv_rows_only = true;
   for (int i = 0; i < n; ++i)
     if (items[i].partials != nullptr) encode_seg(items[i], batch_amax_partials(items[i].rows, items[i].cols));
   flush();
