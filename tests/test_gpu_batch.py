@@ -15,7 +15,8 @@ torch = pytest.importorskip("torch")
 import fp4_microscaling_quantization_amd as fp4
 import oracle
 import workloads
-from gpu_common import codes_np, rowmajor_scales_np, say, to_dev_bf16
+from gpu_common import (assert_rotated_codes_close, codes_np, rowmajor_scales_np, say,
+                        to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -133,6 +134,11 @@ def test_batch_equals_separate_calls(shape):
                  not (kw.get("rotate") == 128 and cols % 128)]
         jobs.append(Job("nvfp4-fp32", fp4.FMT_NVFP4, dict(rotate=True), fp4.GS_COMPUTE,
                         _x("gauss", 33, rows, cols, f32=True)))
+        # strided views (leading dimension cols + 64) in the grouped launches
+        wide = _x("laplace", 34, rows, cols + 64)
+        view = wide[:, :cols]
+        jobs.append(Job("nvfp4-h16-strided", fp4.FMT_NVFP4, dict(rotate=True), fp4.GS_COMPUTE, view))
+        jobs.append(Job("mxfp4-gemm-strided", fp4.FMT_MXFP4, dict(scale_layout=MXG), None, view))
     say("batch vs separate", shape, len(jobs), "jobs")
     ws = _run_batch(jobs)
     for j in jobs:
@@ -182,6 +188,39 @@ def test_batch_against_oracle():
         assert np.array_equal(rowmajor_scales_np(j.out), rs), j.label
         if j.fmt not in fp4.MX_FORMATS:
             assert np.float32(j.out.global_scale.item()) == np.float32(rts), j.label
+
+
+def test_batch_full_size_step_against_oracle():
+    """The benchmark's step as it is timed: one batch of the eight 4096 x 4096
+    variants (two distributions x MXFP4 GEMM-layout / NVFP4 computing its
+    scale x plain / block Hadamard), every job on its own input buffer, against
+    the oracle on the whole tensors: bit-exact without rotation, within the
+    adjacent-mismatch budget with it (tensor scale within one ulp)."""
+    host = {d: workloads.cfg2_tensor(d, 0) for d in ("gauss", "laplace")}
+    jobs = []
+    for d in ("gauss", "laplace"):
+        for fmt, kw, m in ((fp4.FMT_MXFP4, dict(scale_layout=MXG), None),
+                           (fp4.FMT_NVFP4, {}, fp4.GS_COMPUTE)):
+            for rot in (False, True):
+                kw2 = dict(kw, rotate=rot)
+                jobs.append((d, rot, Job("%s/%d/%s" % (d, fmt, rot), fmt, kw2, m,
+                                         to_dev_bf16(host[d]))))
+    say("full-size batch step", len(jobs), "jobs")
+    ws = _run_batch([j for _, _, j in jobs])
+    torch.cuda.synchronize()
+    del ws
+    for d, rot, j in jobs:
+        rc, rs, rts = oracle.quantize(workloads.bf16_bits_to_f32(host[d]), j.fmt, rotate=rot)
+        gc, gsc = codes_np(j.out), rowmajor_scales_np(j.out)
+        if not rot:
+            assert np.array_equal(gc, rc) and np.array_equal(gsc, rs), j.label
+            if j.fmt == fp4.FMT_NVFP4:
+                assert np.float32(j.out.global_scale.item()) == np.float32(rts), j.label
+            continue
+        assert_rotated_codes_close(gc, rc, gsc, rs, what=j.label)
+        if j.fmt == fp4.FMT_NVFP4:
+            g = np.float32(j.out.global_scale.item())
+            assert abs(int(g.view(np.int32)) - int(np.float32(rts).view(np.int32))) <= 1, j.label
 
 
 def test_batch_graph_replays():
