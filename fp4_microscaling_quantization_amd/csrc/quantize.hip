@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_chunk_kernel(const uint8_t*
 
 // ---------------------------------------------------------- grouped launch
 // Several quantizations in one launch: segment s owns workgroups
-// [first_wg, first_wg + nwg) and runs one of the three bodies above (MXFP4 /
+// [first[s], first[s] + nwg) and runs one of the three bodies above (MXFP4 /
 // MXINT4 GEMM-layout tiles, row tiles, or the NVFP4 / NVINT4 tensor-maximum
 // pass with four waves per workgroup) on its own tensor, with the work split
 // of that body's own launch.  One ramp-up and one drain for the whole group
@@ -1153,7 +1153,7 @@ struct BatchSeg {
   float* partials;  // amax: written; rows (NVFP4 / NVINT4): read when npart > 0
   int64_t ldx_bytes;
   int64_t kchunks;
-  uint32_t first_wg, nwg;
+  uint32_t nwg;
   uint32_t rows, nb;
   uint32_t aux;     // kcs (GEMM-layout tiles), wpr (row tiles), cpr (amax)
   uint32_t aux2;    // wpr (amax)
@@ -1164,6 +1164,10 @@ struct BatchSeg {
 
 struct BatchArgs {
   uint32_t nseg;
+  // first workgroup of each segment, contiguous so that a workgroup finds its
+  // segment in one or two scalar cache lines instead of one line per segment
+  // (2.2 us less per call of eight 4096 x 4096 jobs)
+  uint32_t first[kBatchSegs];
   uint32_t pad[3];
   BatchSeg seg[kBatchSegs];
 };
@@ -1176,9 +1180,9 @@ __global__ __launch_bounds__(kThreads) void quant_batch_kernel(BatchArgs A) {
   uint8_t lds[NV_ROWS ? rows_lds_bytes<FP4_FMT_NVFP4>() : kBatchLds];
   const uint32_t b = blockIdx.x;
   uint32_t s = 0;
-  for (uint32_t i = 1; i < A.nseg; ++i) s = b >= A.seg[i].first_wg ? i : s;
+  for (uint32_t i = 1; i < A.nseg; ++i) s = b >= A.first[i] ? i : s;
   const BatchSeg& S = A.seg[s];
-  const uint32_t bid = b - S.first_wg;
+  const uint32_t bid = b - A.first[s];
   constexpr int AB = FP4_SCALE_ABSMAX;
   if constexpr (NV_ROWS) {
 #define FP4_SEG_NV(F, R)                                                                       \
@@ -1707,7 +1711,7 @@ hipError_t launch_quantize_batch(const BatchItem* items, int n, hipStream_t st) 
   auto add = [&](const BatchSeg& seg) {
     if (A.nseg == (uint32_t)kBatchSegs) flush();
     A.seg[A.nseg] = seg;
-    A.seg[A.nseg].first_wg = wgs;
+    A.first[A.nseg] = wgs;
     wgs += seg.nwg;
     ++A.nseg;
   };
