@@ -4,7 +4,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <vector>
 
 #include "fp4.h"
 #include "fp4_device.h"
@@ -240,8 +239,10 @@ int fp4_quantize_batch(int32_t n, const fp4_quant_job* jobs, void* ws, size_t ws
     if ((reinterpret_cast<uintptr_t>(ws) & 3u) != 0) return FP4_ERR_ALIGNMENT;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  std::vector<fp4lib::BatchItem> items;
-  items.reserve((size_t)n);
+  // grouped jobs are launched kBatchChunk at a time (no host allocation)
+  constexpr int kBatchChunk = 64;
+  fp4lib::BatchItem items[kBatchChunk];
+  int nitems = 0;
   for (int32_t i = 0; i < n; ++i) {
     const fp4_quant_job& j = jobs[i];
     const bool mx = fp4k::fmt_mx(j.cfg.fmt);
@@ -262,7 +263,12 @@ int fp4_quantize_batch(int32_t n, const fp4_quant_job* jobs, void* ws, size_t ws
       it.gs = mx ? nullptr : j.global_scale;
       it.partials = part;
       it.P = qparams(&j.cfg, j.cols);
-      items.push_back(it);
+      items[nitems++] = it;
+      if (nitems == kBatchChunk) {
+        const int rc = hip_status(fp4lib::launch_quantize_batch(items, nitems, st));
+        if (rc != FP4_OK) return rc;
+        nitems = 0;
+      }
       continue;
     }
     const int rc = mx ? quantize_mx(&j.cfg, j.x, j.xdt, j.rows, j.cols, j.ldx, j.codes, j.scales, st)
@@ -270,7 +276,7 @@ int fp4_quantize_batch(int32_t n, const fp4_quant_job* jobs, void* ws, size_t ws
                                            j.scales, j.global_scale, part, st);
     if (rc != FP4_OK) return rc;
   }
-  return hip_status(fp4lib::launch_quantize_batch(items.data(), (int)items.size(), st));
+  return hip_status(fp4lib::launch_quantize_batch(items, nitems, st));
 }
 
 int fp4_workspace_init(void* ws, size_t ws_bytes, void* stream) {

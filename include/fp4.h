@@ -260,11 +260,11 @@ size_t fp4_quantize_batch_workspace_bytes(int32_t n);
  * one-row blocks and no rotation or the block-sized one share two launches
  * of one kernel: the first holds every MXFP4 / MXINT4 job, every NVFP4 /
  * NVINT4 job with its tensor scale given and the tensor-maximum pass of the
- * NVFP4 / NVINT4 jobs that compute it; the second encodes those jobs (16 jobs
- * per launch; more make more launches).  Each tensor then pays one share of
- * a launch's ramp-up and drain instead of a whole one.  Other jobs (other
- * configurations, fp32 input, empty tensors) run first, as their own
- * fp4_quantize launches, in job order.  An NVFP4 / NVINT4 job with
+ * NVFP4 / NVINT4 jobs that compute it; the second encodes those jobs (up to 16
+ * jobs per launch and 64 per launch pair; more make more launches).  Each
+ * tensor then pays one share of a launch's ramp-up and drain instead of a
+ * whole one.  Other jobs (other configurations, fp32 input, empty tensors)
+ * run as their own fp4_quantize launches, in job order among themselves.  An NVFP4 / NVINT4 job with
  * FP4_GS_COMPUTE_ONE_PASS runs as FP4_GS_COMPUTE (same results; no exchange
  * region involved).
  * jobs: host array of n jobs, read during the call only; each job follows

@@ -170,6 +170,22 @@ def test_batch_many_jobs_and_empty_ones():
     assert jobs[4].label.startswith("empty") and jobs[4].out.global_scale.item() == 0.0
 
 
+def test_batch_more_than_one_chunk():
+    """70 grouped jobs: more than the 64 gathered per host-side chunk."""
+    jobs = []
+    for i in range(70):
+        label, fmt, kw, m = MERGED[i % len(MERGED)]
+        jobs.append(Job("%s/%d" % (label, i), fmt, kw, m, _x("gauss", 100 + i, 3 + (i % 5), 256)))
+    say("batch of", len(jobs), "small jobs")
+    ws = _run_batch(jobs)
+    for j in jobs:
+        j.run_separately()
+    torch.cuda.synchronize()
+    del ws
+    for j in jobs:
+        j.check()
+
+
 def test_batch_against_oracle():
     """Non-rotated grouped jobs against the oracle directly (ragged shape)."""
     b = workloads.cfg2_tensor("laplace", 9, rows=37, cols=4128)
