@@ -98,6 +98,11 @@ struct MxCfg {
   // (and count one DMA less per stage in their waits).
   static constexpr int LAST_W = (USED - (ROUNDS - 1) * RB + 1023) / 1024;
   static constexpr bool SKIP = LAST_W < NW;
+  // The last round holds only the scale tiles (and padding).  A scale tile
+  // covers 256 K, two stages, so odd stages skip that round and keep the
+  // even stage's scale registers; with NS - 2 even, every wait then counts
+  // the same number of DMAs.
+  static constexpr bool SC_ROUND = (BM + BN) * 64 == (ROUNDS - 1) * RB && (NS - 2) % 2 == 0;
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
 };
@@ -194,14 +199,17 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
     for (int r = 0; r < H; ++r)
       dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * C::RB + wave * 1024);
   };
-  // SHORT: this wave's part of the last round is slot padding, not loaded.
-  auto dma_tail = [&](int kt, auto short_tag) __attribute__((always_inline)) {
+  // SHORT: this wave's part of the last round is slot padding, not loaded;
+  // skip_last: an odd stage's scale round (SC_ROUND), not loaded either.
+  auto dma_tail = [&](int kt, auto short_tag, bool skip_last) __attribute__((always_inline)) {
     constexpr int RE = decltype(short_tag)::value ? ROUNDS - 1 : ROUNDS;
     const int ks = min(kt, kt1 - 1);
     uint8_t* slot = slot_of(kt);
 #pragma unroll
-    for (int r = H; r < RE; ++r)
+    for (int r = H; r < RE; ++r) {
+      if (r == ROUNDS - 1 && skip_last) continue;
       dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * C::RB + wave * 1024);
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -253,34 +261,41 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
   constexpr int NVA = ROUNDS - H;          // DMAs in the first half iteration
   constexpr int NVB = H;                   // DMAs in the second half
 
-  // The ring, for waves that load every round of a stage (PER = ROUNDS DMAs
-  // per stage) or all but the last (PER = ROUNDS - 1).
+  // The ring, for waves that load every round of a stage or all but the last
+  // (SHORT).  PAIR: DMAs of two consecutive stages.
   auto ring = [&](auto short_tag) __attribute__((always_inline)) {
-    constexpr int PER = decltype(short_tag)::value ? ROUNDS - 1 : ROUNDS;
+    constexpr bool SHORT = decltype(short_tag)::value;
+    constexpr bool SR = C::SC_ROUND;
+    constexpr int PAIR = SHORT ? 2 * (ROUNDS - 1) : (SR ? 2 * ROUNDS - 1 : 2 * ROUNDS);
+    constexpr int AFTER = (NS - 2) / 2 * PAIR + ((NS - 2) % 2) * (SHORT ? ROUNDS - 1 : ROUNDS);
     // In iteration kt the registers hold step 0 of stage kt (F0, S).  First
     // half: step 1's reads and the tail of stage kt+NS-1's DMA go out with
     // step 0's MFMAs.  Each wave then waits for its own DMA of stage kt+1 and
     // its LDS reads, and the workgroup syncs (stage kt+1 complete everywhere,
     // slot kt read by nobody).  Second half: the head of stage kt+NS's DMA
-    // into slot kt and stage kt+1's step-0 and scale reads go out with step
-    // 1's MFMAs.
+    // into slot kt and stage kt+1's step-0 (and, for an even stage, scale)
+    // reads go out with step 1's MFMAs.  Slices start at even stages.
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i) {
       dma_head(kt0 + i);
-      dma_tail(kt0 + i, short_tag);
+      dma_tail(kt0 + i, short_tag, SR && (i & 1));
     }
     dma_head(kt0 + NS - 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER + H, 15));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(AFTER + H, 15));
     __builtin_amdgcn_s_barrier();
     Frags F0, F1;
     Scales S, S1;
     read_frags(slot_of(kt0), 0, F0);
     read_scales(slot_of(kt0), S);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-    for (int kt = kt0; kt < kt1; ++kt) {
+    // ODD: parity of kt (used only with SR)
+    auto iter = [&](int kt, auto odd_tag) __attribute__((always_inline)) {
+      constexpr bool ODD = decltype(odd_tag)::value;
+      constexpr bool TAIL_SKIP = SR && (((ODD ? 1 : 0) + NS - 1) & 1);
+      constexpr bool READ_SC = !SR || ODD;  // stage kt+1 even: its scale tiles
       const int sel0 = (kt & 1) * 2;
       read_frags(slot_of(kt), 1, F1);
-      dma_tail(kt + NS - 1, short_tag);
+      dma_tail(kt + NS - 1, short_tag, TAIL_SKIP);
       mfmas(F0, S, sel0);
 #pragma unroll
       for (int k = 0; k < NMF; ++k) {
@@ -289,24 +304,36 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
         if (k < NVA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // DMA
       }
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * PER, 0));  // DMAs after stage kt+1
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(AFTER, 0));  // DMAs after stage kt+1
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       dma_head(kt + NS);
       read_frags(slot_of(kt + 1), 0, F0);
-      read_scales(slot_of(kt + 1), S1);
+      if constexpr (READ_SC) read_scales(slot_of(kt + 1), S1);
       mfmas(F1, S, sel0 + 1);
 #pragma unroll
       for (int k = 0; k < NMF; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-        if (k < NRD + NSC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (k < NRD + (READ_SC ? NSC : 0)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         if (k < NVB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (READ_SC) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) S.a[i] = S1.a[i];
+        for (int i = 0; i < TM; ++i) S.a[i] = S1.a[i];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) S.b[j] = S1.b[j];
+        for (int j = 0; j < TN; ++j) S.b[j] = S1.b[j];
+      }
+    };
+    if constexpr (SR) {
+      int kt = kt0;
+      for (; kt + 1 < kt1; kt += 2) {
+        iter(kt, std::false_type{});
+        iter(kt + 1, std::true_type{});
+      }
+      if (kt < kt1) iter(kt, std::false_type{});  // K % 256 == 128: a last, even stage
+    } else {
+      for (int kt = kt0; kt < kt1; ++kt) iter(kt, std::false_type{});
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   };
