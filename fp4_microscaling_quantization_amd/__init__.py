@@ -27,6 +27,7 @@ FP4_ERR_UNSUPPORTED = -2
 FP4_ERR_ALIGNMENT = -3
 FP4_ERR_WORKSPACE = -4
 FP4_ERR_HIP = -5
+FP4_ERR_EXCHANGE = -6
 FMT_MXFP4 = 0
 FMT_NVFP4 = 1
 FMT_MXINT4 = 2
@@ -281,13 +282,15 @@ def _dt(t) -> int:
 _ws_cache: dict = {}
 
 
-def _scratch_workspace(nbytes: int, device):
-    """Per-device scratch for the NVFP4 global-amax pass (partial maxima) and
-    the single-pass exchange region (zero when allocated, left ready by every
-    call).  One buffer per device and size is reused by every call, so calls
-    that use it must not overlap in time (they do not on one stream)."""
+def _scratch_workspace(nbytes: int, device, stream: int):
+    """Scratch of the NVFP4 global-amax pass (partial maxima) and of the
+    single-pass exchange region (zero when allocated, left ready by every
+    call), one per (device, stream, size).  Calls on one stream are ordered,
+    so they never overlap on their buffer; calls on two streams get two
+    buffers (a shared one would mix the partial maxima or the exchange slots
+    of concurrent calls)."""
     torch = _torch()
-    key = (str(device), nbytes)
+    key = (str(device), int(stream or 0), nbytes)
     t = _ws_cache.get(key)
     if t is None:
         t = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
@@ -295,16 +298,26 @@ def _scratch_workspace(nbytes: int, device):
     return t
 
 
+# Word 1 of the single-pass exchange region (byte 4096 + 4 of the NVFP4
+# workspace): non-zero after a call whose grid-wide wait gave up.
+EXCHANGE_FLAG_OFFSET = 4096 + 4
+
+
+def one_pass_gave_up(flag_word: int, global_scale: float) -> bool:
+    """True when a single-pass call's exchange wait gave up: the kernel sets
+    the exchange region's flag word and writes NaN as the tensor scale."""
+    return int(flag_word) != 0 or global_scale != global_scale
+
+
 _gemm_ws_cache = {}
 
 
-def _gemm_workspace(nbytes: int, device):
-    """Per-device GEMM split-K workspace (fp32 partial sums; any contents),
-    grown to the largest size asked for and reused by every call on the
-    device, so calls that use it must not overlap (they do not on one
-    stream)."""
+def _gemm_workspace(nbytes: int, device, stream: int):
+    """GEMM split-K workspace (fp32 partial sums; any contents) per (device,
+    stream), grown to the largest size asked for: calls on one stream never
+    overlap on it."""
     torch = _torch()
-    key = str(device)
+    key = (str(device), int(stream or 0))
     t = _gemm_ws_cache.get(key)
     if t is None or t.numel() < nbytes:
         t = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
@@ -317,6 +330,55 @@ def gemm_workspace(nbytes: int, device):
     one per stream or per captured graph)."""
     torch = _torch()
     return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def _workspace_arg(workspace, device, what: str):
+    """(pointer, size in bytes) of a caller's workspace tensor: the size passed
+    to the C ABI is the buffer's own, so that a buffer smaller than the call
+    needs makes the library run without it instead of writing past it."""
+    torch = _torch()
+    if workspace is None:
+        return None, 0
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("%s: workspace must be a contiguous uint8 tensor" % what)
+    if workspace.device != device:
+        raise ValueError("%s: workspace on %s, operands on %s" % (what, workspace.device, device))
+    return workspace.data_ptr(), workspace.numel()
+
+
+def _check_out(out, M: int, N: int, device, what: str):
+    """The output of a product: an [M, N] fp32 / bf16 tensor on the operands'
+    device with unit stride along N (its row stride becomes ldy)."""
+    torch = _torch()
+    if out.dim() != 2 or tuple(out.shape) != (M, N):
+        raise ValueError("%s: out must be [%d, %d], got %s" % (what, M, N, tuple(out.shape)))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("%s: out must be float32 or bfloat16, got %s" % (what, out.dtype))
+    if N > 1 and out.stride(1) != 1:
+        raise ValueError("%s: out needs unit stride along N" % what)
+    if M > 1 and out.stride(0) < N:
+        raise ValueError("%s: out rows overlap (stride %d < N)" % (what, out.stride(0)))
+    if out.device != device:
+        raise ValueError("%s: out on %s, operands on %s" % (what, out.device, device))
+
+
+def _same_rotation(a: QConfig, b: QConfig) -> bool:
+    return a.rotate == b.rotate and list(a.rot_signs) == list(b.rot_signs)
+
+
+def check_gemm_operands(a: "Quantized", b: "Quantized"):
+    """Operand checks of gemm(): same format and K, GEMM-layout scales for the
+    MX formats, and the same rotation (size and sign diagonal) on both sides:
+    the product of two differently rotated operands is not A B^T."""
+    fa, fb = a.cfg.fmt, b.cfg.fmt
+    if fa != fb:
+        raise ValueError("gemm: operand formats differ (%d, %d)" % (fa, fb))
+    if a.cols != b.cols:
+        raise ValueError("gemm: K differs (%d, %d)" % (a.cols, b.cols))
+    if fa in MX_FORMATS and (a.cfg.scale_layout != SCALES_GEMM or b.cfg.scale_layout != SCALES_GEMM):
+        raise ValueError("gemm: MX operands need FP4_SCALES_GEMM scales")
+    if not _same_rotation(a.cfg, b.cfg):
+        raise ValueError("gemm: operands quantized with different rotations")
 
 
 @dataclass
@@ -334,13 +396,21 @@ class Quantized:
 def quantize(x, fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
              global_scale=None, out: Quantized | None = None,
              rule: int = SCALE_ABSMAX, rounding: int = ROUND_NEAREST, block_rows: int = 1,
-             signs: int = 0, seed=(0, 0), one_pass: bool = False) -> Quantized:
+             signs: int = 0, seed=(0, 0), one_pass: bool = False,
+             check_one_pass: bool = False) -> Quantized:
     """Quantize a 2-D CUDA tensor (fp32 or bf16, unit stride along the last
     axis).  NVFP4: ``global_scale`` (a float32[1] CUDA tensor) is used as given
     when passed, otherwise computed from the tensor's amax (``one_pass``: the
     amax and the encoding in one launch when the tensor fits, the same
     results).  ``rule`` selects the block-scale rule (SCALE_ABSMAX, SCALE_MSE,
-    SCALE_FOUR_OVER_SIX)."""
+    SCALE_FOUR_OVER_SIX).
+
+    ``check_one_pass`` (with ``one_pass``): synchronise the stream and raise
+    FP4Error(FP4_ERR_EXCHANGE) when the single launch's grid-wide wait gave up
+    (its workgroups were not all resident, e.g. another grid-synchronising
+    kernel held CUs); the workspace's exchange region is re-zeroed first, so
+    the next call starts clean.  The workspace is per stream: single-pass
+    calls on different streams must still not run at the same time."""
     torch = _torch()
     assert x.dim() == 2 and x.stride(1) == 1
     rows, cols = x.shape
@@ -355,12 +425,21 @@ def quantize(x, fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
     if fmt not in MX_FORMATS and global_scale is not None:
         out.global_scale.copy_(global_scale.reshape(1))
         gs_mode = GS_GIVEN
+    stream = _stream()
     wsb = fp4_workspace_bytes(cfg, rows, cols)
-    ws = _scratch_workspace(wsb, x.device) if wsb else None
+    ws = _scratch_workspace(wsb, x.device, stream) if wsb else None
     rc = fp4_quantize(cfg, x.data_ptr(), _dt(x), rows, cols, x.stride(0), out.codes.data_ptr(),
                       out.scales.data_ptr(), out.global_scale.data_ptr(), gs_mode, _ptr(ws), wsb,
-                      _stream())
+                      stream)
     _check(rc, "fp4_quantize")
+    if check_one_pass and gs_mode == GS_COMPUTE_ONE_PASS and ws is not None:
+        torch.cuda.current_stream().synchronize()
+        off = EXCHANGE_FLAG_OFFSET
+        flag = int(ws[off:off + 4].view(torch.int32).item())
+        if one_pass_gave_up(flag, float(out.global_scale.item())):
+            _check(fp4_workspace_init(ws.data_ptr(), wsb, stream), "fp4_workspace_init")
+            torch.cuda.current_stream().synchronize()
+            raise FP4Error(FP4_ERR_EXCHANGE, "fp4_quantize (single pass)")
     return out
 
 
@@ -413,10 +492,11 @@ def global_scale(x, rotate=False, out=None, fmt: int = FMT_NVFP4, signs: int = 0
     cfg = qconfig(fmt, rotate, signs=signs)
     if out is None:
         out = torch.zeros(1, dtype=torch.float32, device=x.device)
+    stream = _stream()
     wsb = fp4_workspace_bytes(cfg, rows, cols)
-    ws = _scratch_workspace(wsb, x.device)
+    ws = _scratch_workspace(wsb, x.device, stream)
     rc = fp4_global_scale(cfg, x.data_ptr(), _dt(x), rows, cols, x.stride(0), out.data_ptr(),
-                          ws.data_ptr(), wsb, _stream())
+                          ws.data_ptr(), wsb, stream)
     _check(rc, "fp4_global_scale")
     return out
 
@@ -462,40 +542,56 @@ def scales_to_gemm_layout(rowmajor, rows: int, cols: int, fmt: int = FMT_MXFP4):
 
 def gemm_w4a16(a, b: Quantized, out_dtype=None, out=None, workspace=None):
     """Y = A * dequant(B)^T for bf16 activations A [M, K] (unit stride along K)
-    and quantized weights B (scales in GEMM layout)."""
+    and quantized weights B (scales in GEMM layout).  ``workspace``: a uint8
+    tensor on A's device (its whole size is offered; one smaller than
+    fp4_gemm_w4a16_workspace_bytes() makes the call run without split-K)."""
     torch = _torch()
-    assert a.dim() == 2 and a.stride(1) == 1 and a.dtype == torch.bfloat16
+    if a.dim() != 2 or a.stride(1) != 1 or a.dtype != torch.bfloat16:
+        raise ValueError("gemm_w4a16: A must be a 2-D bf16 tensor with unit stride along K")
     M, K = a.shape
     fmt, N = b.cfg.fmt, b.rows
-    assert b.cols == K
-    assert fmt not in MX_FORMATS or b.cfg.scale_layout == SCALES_GEMM, "weights need GEMM-layout scales"
+    if b.cols != K:
+        raise ValueError("gemm_w4a16: K differs (%d, %d)" % (K, b.cols))
+    if fmt in MX_FORMATS and b.cfg.scale_layout != SCALES_GEMM:
+        raise ValueError("gemm_w4a16: MX weights need FP4_SCALES_GEMM scales")
     if out is None:
         out = torch.empty(M, N, dtype=out_dtype or torch.bfloat16, device=a.device)
-    wsb = fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K)
-    if workspace is None and wsb:
-        workspace = _gemm_workspace(wsb, a.device)
+    _check_out(out, M, N, a.device, "gemm_w4a16")
+    stream = _stream()
+    if workspace is None:
+        wsb = fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K)
+        workspace = _gemm_workspace(wsb, a.device, stream) if wsb else None
+    ws_ptr, ws_bytes = _workspace_arg(workspace, a.device, "gemm_w4a16")
     rc = fp4_gemm_w4a16(fmt, M, N, K, a.data_ptr(), a.stride(0), b.codes.data_ptr(),
                         b.scales.data_ptr(), b.global_scale.data_ptr(), out.data_ptr(), _dt(out),
-                        out.stride(0), _ptr(workspace), wsb if workspace is not None else 0,
-                        _stream())
+                        out.stride(0), ws_ptr, ws_bytes, stream)
     _check(rc, "fp4_gemm_w4a16")
     return out
 
 
 def gemm(a: Quantized, b: Quantized, out_dtype=None, out=None, workspace=None):
-    """Y = A * B^T for two quantized operands sharing K (scales in GEMM layout)."""
+    """Y = A * B^T for two quantized operands sharing K, format and rotation
+    (MX scales in GEMM layout).  ``workspace``: a uint8 tensor on the operands'
+    device (its whole size is offered; one smaller than
+    fp4_gemm_workspace_bytes() makes the call run without split-K)."""
     torch = _torch()
+    check_gemm_operands(a, b)
     fmt = a.cfg.fmt
-    assert b.cfg.fmt == fmt and a.cols == b.cols
     M, N, K = a.rows, b.rows, a.cols
+    device = a.codes.device
+    if b.codes.device != device:
+        raise ValueError("gemm: operands on %s and %s" % (device, b.codes.device))
     if out is None:
-        out = torch.empty(M, N, dtype=out_dtype or torch.bfloat16, device=a.codes.device)
-    wsb = fp4_gemm_workspace_bytes(fmt, M, N, K)
-    if workspace is None and wsb:
-        workspace = _gemm_workspace(wsb, a.codes.device)
+        out = torch.empty(M, N, dtype=out_dtype or torch.bfloat16, device=device)
+    _check_out(out, M, N, device, "gemm")
+    stream = _stream()
+    if workspace is None:
+        wsb = fp4_gemm_workspace_bytes(fmt, M, N, K)
+        workspace = _gemm_workspace(wsb, device, stream) if wsb else None
+    ws_ptr, ws_bytes = _workspace_arg(workspace, device, "gemm")
     rc = fp4_gemm(fmt, M, N, K, a.codes.data_ptr(), a.scales.data_ptr(),
                   a.global_scale.data_ptr(), b.codes.data_ptr(), b.scales.data_ptr(),
                   b.global_scale.data_ptr(), out.data_ptr(), _dt(out), out.stride(0),
-                  _ptr(workspace), wsb if workspace is not None else 0, _stream())
+                  ws_ptr, ws_bytes, stream)
     _check(rc, "fp4_gemm")
     return out

@@ -165,6 +165,7 @@ const char* fp4_status_str(int status) {
     case FP4_ERR_ALIGNMENT: return "misaligned pointer or leading dimension";
     case FP4_ERR_WORKSPACE: return "workspace missing or too small";
     case FP4_ERR_HIP: return "HIP launch failed";
+    case FP4_ERR_EXCHANGE: return "single-pass exchange wait gave up";
     default: return "unknown status";
   }
 }

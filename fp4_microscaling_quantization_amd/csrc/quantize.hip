@@ -816,8 +816,9 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 // call left it).  The host caps the grid at one workgroup per CU, so the
 // whole grid is resident at once when no other grid-synchronising kernel
 // shares the device.  A wait that outlasts its bound (seconds) gives up: that
-// workgroup encodes with a NaN tensor scale (all-zero codes) and stores NaN
-// to *gs; the region then needs zeroing again.
+// workgroup encodes with a NaN tensor scale (all-zero codes), stores NaN
+// to *gs and sets xchg[1] (the give-up flag); the region then needs zeroing
+// again.
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / 64;
 constexpr int kMaxDevices = 64;
@@ -954,6 +955,9 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
     if (lane == 0) {
       ts_shared = ts;
       if (blockIdx.x == 0 || !ok) *gs = ts;
+      // the give-up flag (word 1 of the region): NaN in *gs alone could be
+      // overwritten by workgroup 0's finite scale
+      if (!ok) __hip_atomic_store(&xchg[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (blockIdx.x == 0) __hip_atomic_store(&xchg[0], E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

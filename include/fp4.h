@@ -60,7 +60,9 @@ typedef enum {
     FP4_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement */
     FP4_ERR_ALIGNMENT = -3,     /* a pointer or leading dimension is misaligned */
     FP4_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required */
-    FP4_ERR_HIP = -5            /* a HIP launch failed */
+    FP4_ERR_HIP = -5,           /* a HIP launch failed */
+    FP4_ERR_EXCHANGE = -6       /* FP4_GS_COMPUTE_ONE_PASS gave up its grid-wide wait
+                                   (reported by callers that read the give-up flag) */
 } fp4_status;
 
 /* MXINT4 / NVINT4 ("Bridging the Gap ...", MXINT4 and NVINT4): the MXFP4 /
@@ -156,7 +158,9 @@ typedef struct {
 
 /* ---------------------------------------------------------------- sizes */
 
-/* Bytes of packed codes for [rows, cols]: rows * cols / 2.  Host function. */
+/* Bytes of packed codes for [rows, cols]: rows * cols / 2, two 4-bit codes per
+ * byte ("NVFP4 vs MXFP4 ...", Figure 2: E2M1 values packed two per byte).
+ * 0 for negative sizes or odd cols.  Host function. */
 size_t fp4_codes_bytes(int64_t rows, int64_t cols);
 
 /* Bytes of the scale array, including the padding of the GEMM layout
@@ -179,7 +183,11 @@ size_t fp4_workspace_bytes(const fp4_qconfig* cfg, int64_t rows, int64_t cols);
 int fp4_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Byte index inside the scale array of the scale of (row r, block kb), for the
- * layout named in cfg; -1 if out of range.  Host function. */
+ * layout named in cfg; -1 if out of range.  The GEMM layout is this library's
+ * own scale reordering for the matrix-core loads ("Portable FP4 Quantization
+ * for Heterogeneous Accelerators", section 2.4: scales reordered to the
+ * layout the GEMM's loads want); this function is its definition for
+ * callers and tests.  Host function. */
 int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols,
                          int64_t r, int64_t kb);
 
@@ -199,10 +207,14 @@ int64_t fp4_scale_offset(const fp4_qconfig* cfg, int64_t rows, int64_t cols,
  *   otherwise it runs the two passes of FP4_GS_COMPUTE.  Its grid waits for
  *   all of its workgroups, so no other FP4_GS_COMPUTE_ONE_PASS call (nor any
  *   other kernel that waits for a whole grid) may run on the device at the
- *   same time; a wait that outlasts a few seconds gives up and writes NaN to
- *   *global_scale.  Bytes [4096, 8192) of ws must be zero before the first
+ *   same time; a wait that outlasts a few seconds gives up: the codes of the
+ *   workgroups that gave up are zero, NaN is written to *global_scale and the
+ *   32-bit word at byte 4100 of ws (the give-up flag) becomes non-zero.  The
+ *   call still returns FP4_OK (it cannot wait for the kernel); a caller that
+ *   needs to know synchronises and reads the flag, and reports
+ *   FP4_ERR_EXCHANGE.  Bytes [4096, 8192) of ws must be zero before the first
  *   call that uses this ws (every call leaves them ready for the next; after
- *   a NaN give-up they need zeroing again; fp4_workspace_init does it); ws
+ *   a give-up they need zeroing again; fp4_workspace_init does it); ws
  *   8-byte aligned.
  *   MXFP4 ignores global_scale and gs_mode (global_scale may be NULL).
  * ws/ws_bytes: device workspace of fp4_workspace_bytes() bytes, any contents
