@@ -76,6 +76,8 @@ def _load(path: str):
                                     ctypes.c_int]
     L.ora_quantize_spec.restype = ctypes.c_int
     L.ora_quantize_spec.argtypes = [ctypes.POINTER(QSpec), P, l, l, P, P, P, ctypes.c_int]
+    L.ora_tensor_scale.restype = ctypes.c_int
+    L.ora_tensor_scale.argtypes = [ctypes.c_int, ctypes.c_int, P, P, l, l, P]
     L.ora_dequantize_rot.restype = ctypes.c_int
     L.ora_dequantize_rot.argtypes = [ctypes.c_int, P, P, ctypes.c_float, l, l, ctypes.c_int, P, P]
     L.ora_rotate_signed.restype = ctypes.c_int
@@ -262,6 +264,21 @@ def quantize_spec(x, fmt: int, rot_n: int = 0, signs=None, rule: int = SCALE_ABS
     return codes, scales, np.float32(tsa[0])
 
 
+def tensor_scale(x, fmt: int, rotate: bool = False, signs=None) -> np.float32:
+    """NV per-tensor scale of x (rotated by the block size when rotate), the
+    same number quantize() computes: amax / 2688 (NVFP4) or / 3136 (NVINT4)."""
+    x = _f32(x)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    rows, cols = x.shape
+    sg = _signs_array(signs)
+    ts = np.zeros(1, dtype=np.float32)
+    rc = lib().ora_tensor_scale(fmt, BLOCK[fmt] if rotate else 0, _p(sg), _p(x), rows, cols, _p(ts))
+    if rc != 0:
+        raise ValueError("ora_tensor_scale: bad arguments")
+    return np.float32(ts[0])
+
+
 def dequantize_rot(codes, scales, fmt: int, ts: float = 0.0, rot_n: int = 0, signs=None):
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
@@ -330,6 +347,29 @@ def cosine(x, xhat) -> float:
     return float(s[2] / np.sqrt(s[1] * s[3]))
 
 
+def host_threads() -> int:
+    """Threads for the entry-wise products: the host's cores (at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _over_chunks(n: int, K: int, run):
+    """run(lo, hi) over contiguous chunks of n entries, on host threads when the
+    work is large (each entry is computed on its own, so the results do not
+    depend on the split; the C calls release the interpreter lock)."""
+    workers = host_threads()
+    if n * max(K, 1) < (1 << 24) or workers == 1 or n < 2 * workers:
+        return [run(0, n)]
+    from concurrent.futures import ThreadPoolExecutor
+    step = (n + 4 * workers - 1) // (4 * workers)
+    spans = [(lo, min(n, lo + step)) for lo in range(0, n, step)]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(lambda sp: run(*sp), spans))
+
+
 def gemm_entries(fmt: int, K: int, a_codes, a_scales, a_ts, b_codes, b_scales, b_ts,
                  rows, cols):
     """(y, |A||B|) at the listed (row, col) pairs of Y = A B^T, in double."""
@@ -342,10 +382,13 @@ def gemm_entries(fmt: int, K: int, a_codes, a_scales, a_ts, b_codes, b_scales, b
     assert rows.size == cols.size
     y = np.zeros(rows.size, dtype=np.float64)
     ab = np.zeros(rows.size, dtype=np.float64)
-    rc = lib().ora_gemm_entries(fmt, K, _p(a_codes), _p(a_scales), float(a_ts), _p(b_codes),
-                                _p(b_scales), float(b_ts), rows.size, _p(rows), _p(cols),
-                                _p(y), _p(ab))
-    if rc != 0:
+
+    def run(lo, hi):
+        return lib().ora_gemm_entries(fmt, K, _p(a_codes), _p(a_scales), float(a_ts), _p(b_codes),
+                                      _p(b_scales), float(b_ts), hi - lo, _p(rows[lo:hi]),
+                                      _p(cols[lo:hi]), _p(y[lo:hi]), _p(ab[lo:hi]))
+
+    if any(rc != 0 for rc in _over_chunks(rows.size, K, run)):
         raise ValueError("ora_gemm_entries: bad arguments")
     return y, ab
 
@@ -361,9 +404,13 @@ def gemm_w4a16_entries(fmt: int, K: int, a, b_codes, b_scales, b_ts, rows, cols)
     assert rows.size == cols.size and a.ndim == 2 and a.shape[1] == K
     y = np.zeros(rows.size, dtype=np.float64)
     ab = np.zeros(rows.size, dtype=np.float64)
-    rc = lib().ora_gemm_w4a16_entries(fmt, K, _p(a), K, _p(b_codes), _p(b_scales), float(b_ts),
-                                      rows.size, _p(rows), _p(cols), _p(y), _p(ab))
-    if rc != 0:
+
+    def run(lo, hi):
+        return lib().ora_gemm_w4a16_entries(fmt, K, _p(a), K, _p(b_codes), _p(b_scales),
+                                            float(b_ts), hi - lo, _p(rows[lo:hi]),
+                                            _p(cols[lo:hi]), _p(y[lo:hi]), _p(ab[lo:hi]))
+
+    if any(rc != 0 for rc in _over_chunks(rows.size, K, run)):
         raise ValueError("ora_gemm_w4a16_entries: bad arguments")
     return y, ab
 

@@ -436,6 +436,25 @@ static int nv_scale_code(float amax, float top, float tsv)
     return ora_e4m3_encode(t);
 }
 
+/* NV per-tensor scale of the n (rotated) values y ([VS] Figure 2: the global
+ * amax sets the fp32 tensor scale): amax / (6 * 448) for NVFP4, amax /
+ * (7 * 448) for NVINT4. */
+static float tensor_scale(int fmt, const float *y, long n)
+{
+    float gamax = 0.0f;
+    for (long i = 0; i < n; ++i) {
+        float a = fabsf(y[i]);
+        if (a > gamax)
+            gamax = a;
+    }
+    float tsv;
+    if (fmt == ORA_NVFP4)
+        tsv = gamax / 2688.0f;          /* 6 * 448 */
+    else
+        tsv = gamax / 3136.0f;          /* 7 * 448: the INT4 maximum */
+    return tsv;
+}
+
 /*
  * Quantize x [rows, cols] (fp32, row-major, blocks run along cols).
  *   fmt     ORA_MXFP4 (block 32, E8M0) or ORA_NVFP4 (block 16, E4M3 x fp32),
@@ -527,16 +546,7 @@ int ora_quantize_spec(const ora_qspec *q, const float *x, long rows, long cols,
         if (gs_given) {
             tsv = *ts;
         } else {
-            float gamax = 0.0f;
-            for (long i = 0; i < n; ++i) {
-                float a = fabsf(y[i]);
-                if (a > gamax)
-                    gamax = a;
-            }
-            if (fmt == ORA_NVFP4)
-                tsv = gamax / 2688.0f;          /* 6 * 448 */
-            else
-                tsv = gamax / 3136.0f;          /* 7 * 448: the INT4 maximum */
+            tsv = tensor_scale(fmt, y, n);
             *ts = tsv;
         }
     }
@@ -613,6 +623,32 @@ int ora_quantize_spec(const ora_qspec *q, const float *x, long rows, long cols,
         }
     }
     free(ybuf);
+    return ORA_OK;
+}
+
+/* The NV per-tensor scale alone, exactly as ora_quantize_spec computes it
+ * without a given scale: x rotated by rot_n (0 or the block size) with the
+ * sign mask `signs` (may be NULL), then tensor_scale.  Returns ORA_EINVAL
+ * for MX formats or bad sizes. */
+int ora_tensor_scale(int fmt, int rot_n, const uint32_t *signs, const float *x, long rows,
+                     long cols, float *ts)
+{
+    int G = fmt_block(fmt);
+    if (G == 0 || fmt_mx(fmt) || ts == NULL || rows < 0 || cols < 0 || cols % G != 0)
+        return ORA_EINVAL;
+    if (rot_n != 0 && rot_n != G)
+        return ORA_EINVAL;
+    long n = rows * cols;
+    if (!rot_n) {
+        *ts = tensor_scale(fmt, x, n);
+        return ORA_OK;
+    }
+    float *y = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+    if (!y)
+        return ORA_EINVAL;
+    ora_rotate_signed(x, y, rows, cols, rot_n, signs, 0);
+    *ts = tensor_scale(fmt, y, n);
+    free(y);
     return ORA_OK;
 }
 

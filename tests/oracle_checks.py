@@ -142,8 +142,13 @@ def check_e4m3_decode():
 
 
 def _binade_rne_e4m3(t: np.ndarray) -> np.ndarray:
-    """Generic float rounding for E4M3 (clip to [0, 448], binade exponent floored
-    at -6, spacing 2^(e-3), ties to even); returns the value."""
+    """E4M3 rounding binade by binade, the way "NVFP4 vs MXFP4: 4-Bit Floating
+    Point for LLM Training and Inference (2026)" emulates it in its section
+    "Emulating both formats yourself": clip to [0, 448], take the binade
+    exponent (floored at -6, the subnormal range), round onto that binade's
+    spacing 2^(e-3) with ties to even; returns the value.  A different
+    algorithm from the oracle's nearest-value scan, so it pins the oracle's
+    E4M3 encoder to the page's definition."""
     x = np.clip(t.astype(np.float64), 0, 448)
     out = np.zeros_like(x)
     m = x > 0
@@ -178,6 +183,30 @@ def check_e4m3_encode_exhaustive():
             c = oracle.e4m3_encode(mid)
             assert c in (i - 1, i) and c % 2 == 0, (i, c)
     assert oracle.e4m3_encode(0.0) == 0 and oracle.e4m3_encode(1e30) == 0x7E
+
+
+def check_tensor_scale_alone():
+    """The tensor scale on its own equals the one quantize() computes, the
+    worked example's 2.6 / 2688 ("NVFP4 vs MXFP4 ...", "A worked example, by
+    hand"), the closed form max|x| / 2688 (or / 3136 for NVINT4) in fp32,
+    and over row chunks its maximum is the whole tensor's (so a tensor can be
+    scaled chunk by chunk)."""
+    ex = np.array([0.1, -0.3, 0.7, 1.1, -0.2, 0.05, 0.9, 2.6] + [0.0] * 8, np.float32)
+    assert oracle.tensor_scale(ex, oracle.NVFP4) == np.float32(2.6) / np.float32(2688.0)
+    x = workloads.bf16_bits_to_f32(workloads.cfg2_tensor("laplace", 3, rows=96, cols=256))
+    for fmt, div in ((oracle.NVFP4, 2688.0), (oracle.NVINT4, 3136.0)):
+        assert oracle.tensor_scale(x, fmt) == np.float32(np.abs(x).max()) / np.float32(div)
+        for rot in (False, True):
+            _, _, ts = oracle.quantize(x, fmt, rotate=rot)
+            assert oracle.tensor_scale(x, fmt, rotate=rot) == ts
+            parts = [oracle.tensor_scale(x[i:i + 17], fmt, rotate=rot) for i in range(0, 96, 17)]
+            assert max(parts) == ts
+    for bad in ((x, oracle.MXFP4), (x[:, :250], oracle.NVFP4)):
+        try:
+            oracle.tensor_scale(*bad)
+        except ValueError:
+            continue
+        raise AssertionError("tensor_scale accepted a bad call")
 
 
 def check_e8m0():
