@@ -403,16 +403,36 @@ def _device_operand(codes, scales_rm, gs, fmt, rows, K):
     return fp4.Quantized(c, s, g, cfg, rows, K)
 
 
-def _check_gemm(fmt, M, N, K, seed, out_dtype, nrows=2, nent=256):
-    say("gemm", FNAME[fmt], M, N, K, out_dtype)
-    ac, asc, ags, bc, bsc, bgs = _rand_operands(fmt, M, N, K, seed)
+def _extreme_operands(fmt, M, N, K, seed):
+    """Random codes with scales at the ends of their formats' ranges: E8M0
+    codes 0/1 against 253/254 (paired so every product of scales is finite,
+    ordinary codes on every fourth block), or subnormal and zero E4M3 codes
+    on every other block."""
+    G = fp4.BLOCK[fmt]
+    ac = workloads.random_codes(M, K, seed, stream=31)
+    bc = workloads.random_codes(N, K, seed, stream=32)
+    mx = fmt in fp4.MX_FORMATS
+    # MXINT4 expands n * 2^e to bf16: codes above 252 (7 * 2^126) overflow it,
+    # and no finite input quantizes to them (the largest bf16 gives 252)
+    big = (251, 252) if fmt == fp4.FMT_MXINT4 else (253, 254)
+    asc = workloads.extreme_scales(M, K // G, "a", mx, seed, stream=33, big_codes=big)
+    bsc = workloads.extreme_scales(N, K // G, "b", mx, seed, stream=34, big_codes=big)
+    ags, bgs = (np.float32(0), np.float32(0)) if mx else (np.float32(3.5e3), np.float32(2.25e2))
+    return ac, asc, ags, bc, bsc, bgs
+
+
+def _check_gemm(fmt, M, N, K, seed, out_dtype, nrows=8, nent=256, operands=None):
+    """GEMM against the oracle on every column of `nrows` random rows (plus
+    the first and last row) and `nent` random entries."""
+    say("gemm", FNAME[fmt], M, N, K, out_dtype, "extreme scales" if operands else "")
+    ac, asc, ags, bc, bsc, bgs = (operands or _rand_operands)(fmt, M, N, K, seed)
     qa = _device_operand(ac, asc, ags, fmt, M, K)
     qb = _device_operand(bc, bsc, bgs, fmt, N, K)
     y = fp4.gemm(qa, qb, out_dtype=out_dtype)
     y2 = fp4.gemm(qa, qb, out_dtype=out_dtype)
     torch.cuda.synchronize()
     g = np.random.default_rng(seed)
-    rsel = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, nrows)]))[: max(2, nrows)]
+    rsel = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, nrows)]))
     rows = np.concatenate([np.repeat(rsel, N), g.integers(0, M, nent)])
     cols = np.concatenate([np.tile(np.arange(N), rsel.size), g.integers(0, N, nent)])
     ref, absref = oracle.gemm_entries(fmt, K, ac, asc, ags, bc, bsc, bgs, rows, cols)
@@ -437,18 +457,56 @@ def test_gemm_small_full_check(fmt, M, N, K):
 LLAMA8B = [(4096, 4096, 4096), (4096, 6144, 4096), (4096, 14336, 4096), (4096, 4096, 14336)]
 
 
+OUT_DT = [torch.float32, torch.bfloat16]
+OUT_IDS = ["f32out", "bf16out"]
+
+
+@pytest.mark.parametrize("out_dtype", OUT_DT, ids=OUT_IDS)
 @pytest.mark.parametrize("M,N,K", LLAMA8B, ids=["qkvo", "kv6144", "up", "down"])
-def test_gemm_mx_llama8b_shapes(M, N, K):
-    _check_gemm(fp4.FMT_MXFP4, M, N, K, seed=7, out_dtype=torch.bfloat16, nrows=1, nent=256)
+def test_gemm_mx_llama8b_shapes(M, N, K, out_dtype):
+    """Llama-3-8B linears at M = 4096 in the benchmark's launch configuration:
+    fp32 output against the bare 1e-5 (|A||B|) bound, bf16 output with its
+    half-ulp allowance; every column of 8 random rows plus 256 entries."""
+    _check_gemm(fp4.FMT_MXFP4, M, N, K, seed=7, out_dtype=out_dtype,
+                nrows=8 if out_dtype == torch.float32 else 2)
 
 
 LLAMA70B = [(m, n, k) for m in (1, 16, 128, 8192) for (k, n) in ((8192, 28672), (28672, 8192))]
 
 
+@pytest.mark.parametrize("out_dtype", OUT_DT, ids=OUT_IDS)
 @pytest.mark.parametrize("M,N,K", LLAMA70B, ids=["%dx%dx%d" % s for s in LLAMA70B])
 @pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
-def test_gemm_llama70b_mlp_shapes(fmt, M, N, K):
-    _check_gemm(fmt, M, N, K, seed=11, out_dtype=torch.bfloat16, nrows=1, nent=128)
+def test_gemm_llama70b_mlp_shapes(fmt, M, N, K, out_dtype):
+    """Every column of 8 random rows and 256 entries with fp32 output (the bare
+    bound); the bf16 output of the same call on 2 rows and 256 entries."""
+    _check_gemm(fmt, M, N, K, seed=11, out_dtype=out_dtype,
+                nrows=8 if out_dtype == torch.float32 else 2)
+
+
+# Shapes that take the 256 x 256 tile plan (at least 256 such tiles) with
+# ragged M and N, a K with a last 128-K stage (K % 256 == 128), and a split-K
+# slice with an odd number of stages.
+PLAN_EDGES = [(4000, 4100, 4096), (4000, 4100, 4224), (64, 1024, 1152), (4000, 4100, 1024)]
+
+
+@pytest.mark.parametrize("out_dtype", OUT_DT, ids=OUT_IDS)
+@pytest.mark.parametrize("M,N,K", PLAN_EDGES, ids=["%dx%dx%d" % s for s in PLAN_EDGES])
+@pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
+def test_gemm_tile_plan_edges(fmt, M, N, K, out_dtype):
+    _check_gemm(fmt, M, N, K, seed=M + K, out_dtype=out_dtype)
+
+
+EXTREME = [(256, 512, 1024), (16, 4096, 4096), (4000, 4100, 4096), (128, 4096, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", EXTREME, ids=["%dx%dx%d" % s for s in EXTREME])
+@pytest.mark.parametrize("fmt", FMTS + INT4, ids=["mxfp4", "nvfp4", "mxint4", "nvint4"])
+def test_gemm_extreme_scales(fmt, M, N, K):
+    """E8M0 codes 0, 1, 253, 254 (products of scales from 2^-1 to 2^1 and
+    ordinary ones) and E4M3 subnormal / zero block scales reach the MFMA
+    paths: fp32 output against the bare bound."""
+    _check_gemm(fmt, M, N, K, seed=K + N, out_dtype=torch.float32, operands=_extreme_operands)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
@@ -477,7 +535,7 @@ def test_quantize_then_gemm_end_to_end(fmt):
 # ---------------------------------------------------------------- W4A16
 
 
-def _check_w4a16(fmt, M, N, K, seed, out_dtype, lda_pad=0, nrows=2, nent=256, split=True):
+def _check_w4a16(fmt, M, N, K, seed, out_dtype, lda_pad=0, nrows=8, nent=256, split=True):
     say("w4a16", FNAME[fmt], M, N, K, out_dtype, "lda+%d" % lda_pad, "split" if split else "unsplit")
     _, _, _, bc, bsc, bgs = _rand_operands(fmt, M, N, K, seed)
     qb = _device_operand(bc, bsc, bgs, fmt, N, K)
@@ -495,7 +553,7 @@ def _check_w4a16(fmt, M, N, K, seed, out_dtype, lda_pad=0, nrows=2, nent=256, sp
         assert rc == fp4.FP4_OK
     torch.cuda.synchronize()
     g = np.random.default_rng(seed)
-    rsel = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, nrows)]))[: max(2, nrows)]
+    rsel = np.unique(np.concatenate([[0, M - 1], g.integers(0, M, nrows)]))
     rows = np.concatenate([np.repeat(rsel, N), g.integers(0, M, nent)])
     cols = np.concatenate([np.tile(np.arange(N), rsel.size), g.integers(0, N, nent)])
     av = workloads.bf16_bits_to_f32(abits)[:, :K]
@@ -531,10 +589,12 @@ def test_gemm_w4a16_strided_activations_and_unsplit(fmt):
 LLAMA70B_DECODE = [(m, n, k) for m in (1, 16, 128) for (k, n) in ((8192, 28672), (28672, 8192))]
 
 
+@pytest.mark.parametrize("out_dtype", OUT_DT, ids=OUT_IDS)
 @pytest.mark.parametrize("M,N,K", LLAMA70B_DECODE, ids=["%dx%dx%d" % s for s in LLAMA70B_DECODE])
 @pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
-def test_gemm_w4a16_llama70b_mlp_shapes(fmt, M, N, K):
-    _check_w4a16(fmt, M, N, K, seed=13, out_dtype=torch.bfloat16, nrows=1, nent=128)
+def test_gemm_w4a16_llama70b_mlp_shapes(fmt, M, N, K, out_dtype):
+    _check_w4a16(fmt, M, N, K, seed=13, out_dtype=out_dtype,
+                 nrows=8 if out_dtype == torch.float32 else 2)
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
@@ -584,7 +644,7 @@ def test_gemm_int4_small_full_check(fmt, M, N, K):
 @pytest.mark.parametrize("M,N,K", [(8192, 28672, 8192), (16, 8192, 28672)], ids=["8192x28672x8192", "16x8192x28672"])
 @pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
 def test_gemm_int4_llama70b_shapes(fmt, M, N, K):
-    _check_gemm(fmt, M, N, K, seed=17, out_dtype=torch.bfloat16, nrows=1, nent=128)
+    _check_gemm(fmt, M, N, K, seed=17, out_dtype=torch.float32)
 
 
 @pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])

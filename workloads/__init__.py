@@ -33,7 +33,7 @@ __all__ = [
     "rng", "uniform_open", "laplace", "normal", "choose_subset", "to_bf16_bits",
     "bf16_bits_to_f32", "scale_entries", "scale_columns", "CONFIGS",
     "cfg1_tensor", "cfg2_tensor", "cfg3_tensor", "gemm_activation", "gemm_weight",
-    "random_codes", "random_scales",
+    "random_codes", "random_scales", "edge_tensor", "extreme_scales",
 ]
 
 
@@ -169,3 +169,88 @@ def random_scales(rows: int, nblocks: int, lo: int, hi: int, seed: int = 0,
                   stream: int = 8) -> np.ndarray:
     """Uniformly random scale bytes in [lo, hi], [rows, nblocks]."""
     return rng(seed, stream).integers(lo, hi + 1, size=(rows, nblocks), dtype=np.uint8)
+
+
+# Kinds of 16-element groups in edge_tensor (one kind per group; an MX block
+# holds two groups, an NV block one).
+EDGE_KINDS_MX = ("laplace", "tiny", "subnormal", "signed_zeros", "huge", "one_nonzero",
+                 "laplace_one_huge")
+EDGE_KINDS_NV = ("laplace", "small", "smaller", "subnormal", "signed_zeros", "one_nonzero",
+                 "laplace_one_huge")
+
+
+def edge_tensor(rows: int, cols: int, seed: int = 0, family: str = "mx",
+                huge: float = 3.0e38) -> np.ndarray:
+    """bf16 bit patterns [rows, cols] whose 16-element groups are each drawn
+    from one kind of edge input.  family 'mx' (block scales set by each
+    block's own maximum): Laplace(0,1); tiny values 2^-134 .. 2^-126 (block
+    maxima below 2^-125, subnormals included); bf16 subnormals only; +0 and
+    -0 only; +-huge; a single non-zero element; Laplace with one +-huge
+    element.  family 'nv' (one tensor maximum sets the block scales' range):
+    Laplace(0,1); Laplace x 1e-5 and x 1e-7 (block maxima far below the tensor
+    maximum); bf16 subnormals; signed zeros; a single non-zero; Laplace with
+    one element of magnitude `huge`.  Exact bit patterns where the kind needs
+    them (subnormals, signed zeros), otherwise fp32 values rounded to bf16."""
+    if cols % 16:
+        raise ValueError("cols must be a multiple of 16")
+    kinds = EDGE_KINDS_MX if family == "mx" else EDGE_KINDS_NV
+    ng = rows * (cols // 16)
+    g = rng(seed, 7001)
+    kind = g.integers(0, len(kinds), size=ng)
+    vals = laplace(rng(seed, 7002), ng * 16, 1.0).reshape(ng, 16)
+    sign = np.where(g.random((ng, 16)) < 0.5, -1.0, 1.0)
+    pos = g.integers(0, 16, size=ng)
+    bits = to_bf16_bits(vals.astype(np.float32)).reshape(ng, 16)
+    for k, name in enumerate(kinds):
+        m = kind == k
+        n = int(m.sum())
+        if n == 0 or name == "laplace":
+            continue
+        if name == "tiny":
+            e = g.uniform(-134.0, -126.0, size=(n, 16))
+            v = sign[m] * np.exp2(e)
+            bits[m] = to_bf16_bits(v.astype(np.float32)).reshape(n, 16)
+        elif name == "subnormal":
+            mant = g.integers(1, 128, size=(n, 16)).astype(np.uint16)
+            bits[m] = np.where(sign[m] < 0, 0x8000, 0).astype(np.uint16) | mant
+        elif name == "signed_zeros":
+            bits[m] = np.where(sign[m] < 0, 0x8000, 0).astype(np.uint16)
+        elif name == "huge":
+            v = sign[m] * huge * g.uniform(0.25, 1.0, size=(n, 16))
+            bits[m] = to_bf16_bits(v.astype(np.float32)).reshape(n, 16)
+        elif name in ("small", "smaller"):
+            f = 1e-5 if name == "small" else 1e-7
+            bits[m] = to_bf16_bits((vals[m] * f).astype(np.float32)).reshape(n, 16)
+        elif name == "one_nonzero":
+            row = np.zeros((n, 16), dtype=np.float64)
+            row[np.arange(n), pos[m]] = vals[m][np.arange(n), pos[m]] * 7.0
+            bits[m] = to_bf16_bits(row.astype(np.float32)).reshape(n, 16)
+        elif name == "laplace_one_huge":
+            row = vals[m].copy()
+            row[np.arange(n), pos[m]] = sign[m][np.arange(n), pos[m]] * huge
+            bits[m] = to_bf16_bits(row.astype(np.float32)).reshape(n, 16)
+    return bits.reshape(rows, cols)
+
+
+def extreme_scales(rows: int, nblocks: int, side: str, fmt_mx: bool, seed: int = 0,
+                   stream: int = 9, big_codes=(253, 254)) -> np.ndarray:
+    """Scale bytes [rows, nblocks] at the ends of the scale formats' ranges,
+    paired across the two GEMM operands so that every product of scales stays
+    finite.  MX (E8M0): even blocks give side 'a' codes 253/254 and side 'b'
+    codes 0/1; odd blocks the reverse (big_codes replaces 253/254); every
+    fourth block ordinary codes 120..130 on both sides.  NV (E4M3): subnormal codes 0x01..0x07 and zero
+    (0x00) on every other block, ordinary codes 0x30..0x7E elsewhere."""
+    g = rng(seed, stream)
+    kb = np.arange(nblocks)[None, :]
+    if fmt_mx:
+        big = g.integers(big_codes[0], big_codes[1] + 1, size=(rows, nblocks))
+        small = g.integers(0, 2, size=(rows, nblocks))
+        mid = g.integers(120, 131, size=(rows, nblocks))
+        a_big = (kb % 2 == 0)
+        out = np.where(a_big == (side == "a"), big, small)
+        out = np.where(kb % 4 == 3, mid, out)
+    else:
+        sub = g.integers(0, 8, size=(rows, nblocks))
+        mid = g.integers(0x30, 0x7F, size=(rows, nblocks))
+        out = np.where(kb % 2 == 0, sub, mid)
+    return out.astype(np.uint8)
