@@ -390,6 +390,11 @@ def main():
                 "traffic": traffic, "traffic_note": traffic_note,
                 "alg_bytes_per_step": dk["alg_bytes"], "avg_step_us": round(dk["avg_us"], 3),
                 "launches_per_step": 2,
+                "alg_bytes_min": step_bytes,
+                "achieved_min": round(step_bytes / (dk["avg_us"] * 1e-6) / 1e9, 1),
+                "frac_min": round(step_bytes / (dk["avg_us"] * 1e-6) / PEAK_HBM, 4),
+                "alg_bytes_min_note": "the step's own bytes only (each input read once, codes, "
+                                      "scales), without the NVFP4 maximum pass's second read",
                 "alg_bytes_note": "the step's bytes (each input read once, codes, scales) plus the "
                                   "second read of the four NVFP4 inputs by their tensor-maximum "
                                   "pass"}
@@ -480,23 +485,12 @@ def main():
     # -------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
+        cpu = cpu_baseline(variants, host, alg_bytes, workloads, fp4)
+        log("cpu baseline %.4f GB/s on 1 core (%.1fs), %.4f GB/s on %d threads (%.1fs)"
+            % (cpu["value_1core"], cpu["seconds_1core"], cpu["value"], cpu["cores"],
+               cpu["seconds"]))
+    if not args.no_cpu_baseline:
         import oracle
-        # the oracle on the complete step (all rows of every variant), timed
-        t_or = 0.0
-        b_or = 0
-        for v in variants:
-            d, fmt, rot = v
-            xh = workloads.bf16_bits_to_f32(host[d])
-            t1 = time.perf_counter()
-            oracle.quantize(xh, fmt, rotate=rot)
-            t_or += time.perf_counter() - t1
-            b_or += alg_bytes(fmt)
-        cpu = {"value": round(b_or / t_or / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": "one complete step: all 4096 rows of each of the 8 variants, single-threaded "
-                         "plain-C oracle (NVFP4 includes its amax pass); same algorithmic bytes as "
-                         "the GPU line",
-               "seconds": round(t_or, 2)}
-        log("cpu baseline %.4f GB/s over %.1fs" % (cpu["value"], t_or))
         # NMSE of a 256-row sample, oracle vs GPU on the same rows (untimed)
         sample_rows = 256
         for v in variants:
@@ -509,6 +503,14 @@ def main():
             sg = fp4.error_sums(xd, qg).cpu().numpy()
             nmse[vname(v)].update({"oracle_sample": oracle.nmse(xh, ref),
                                    "gpu_sample": float(sg[0] / sg[1])})
+
+    # ------------------------------------------ cfg1 / cfg3 (parity configs)
+    cfg1 = bench_cfg1(torch, fp4, workloads, stream, sh_now, capture, args.no_cpu_baseline)
+    log("cfg1 quantize %.2f us, dequantize %.2f us, error sums %.2f us"
+        % (cfg1["quantize_us"], cfg1["dequantize_us"], cfg1["error_sums_us"]))
+    cfg3 = bench_cfg3(torch, fp4, workloads, dev, stream, sh_now, capture)
+    log("cfg3 " + ", ".join("%s %.2f us (%.3f of HBM)" % (k, v["avg_us"], v["frac"])
+                            for k, v in cfg3["kernels"].items()))
 
     # --------------------------------------------------------------- GEMM
     gemm = None
@@ -548,9 +550,178 @@ def main():
         "cpu_baseline": cpu,
         "nmse": nmse,
         "quantizer_variants": search,
+        "cfg1_mxfp4_131072_fp32": cfg1,
+        "cfg3_fused_activation_8192x4096": cfg3,
         "gemm": gemm,
     }
     print(json.dumps(line), flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(variants, host, alg_bytes, workloads, fp4):
+    """The plain-C oracle on one complete step: single-threaded, and split
+    over row chunks on every host core (a thread pool; the oracle's ctypes
+    calls release the interpreter lock).  NV variants that compute their
+    tensor scale do it as two parallel phases, the oracle's tensor scale of
+    each chunk (whose maximum is the tensor's) and then the chunks' encoding
+    with that scale; rotated NV variants therefore rotate twice."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    xs = {d: workloads.bf16_bits_to_f32(h) for d, h in host.items()}
+    t1 = 0.0
+    nbytes = 0
+    for (d, fmt, rot) in variants:
+        t = time.perf_counter()
+        oracle.quantize(xs[d], fmt, rotate=rot)
+        t1 += time.perf_counter() - t
+        nbytes += alg_bytes(fmt)
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    ncpu = max(1, min(ncpu, 16))
+    rows = next(iter(xs.values())).shape[0]
+    chunk = max(1, (rows + 4 * ncpu - 1) // (4 * ncpu))
+    spans = [(r, min(rows, r + chunk)) for r in range(0, rows, chunk)]
+    with ThreadPoolExecutor(max_workers=ncpu) as ex:
+        t = time.perf_counter()
+        for (d, fmt, rot) in variants:
+            x = xs[d]
+            ts = None
+            if fmt not in fp4.MX_FORMATS:
+                parts = ex.map(lambda sp: oracle.tensor_scale(x[sp[0]:sp[1]], fmt, rotate=rot), spans)
+                ts = max(parts)
+            list(ex.map(lambda sp: oracle.quantize(x[sp[0]:sp[1]], fmt, rotate=rot, ts=ts), spans))
+        tp = time.perf_counter() - t
+    return {"value": round(nbytes / tp / 1e9, 4), "unit": "GB/s", "cores": ncpu, "kind": "oracle",
+            "sample": "one complete step: all 4096 rows of each of the 8 variants (the same "
+                      "algorithmic bytes as the GPU line), the plain-C oracle split over %d row "
+                      "chunks on %d threads; value_1core: the same step single-threaded" % (
+                          len(spans), ncpu),
+            "seconds": round(tp, 2), "value_1core": round(nbytes / t1 / 1e9, 4),
+            "seconds_1core": round(t1, 2), "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def time_graph(torch, stream, capture, fn, reps):
+    """Average us per call of fn(i): reps calls recorded as one HIP graph and
+    replayed between two HIP events on the launching stream."""
+    fn(0)
+    torch.cuda.synchronize()
+    g = capture(lambda: [fn(i) for i in range(reps)])
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def bench_cfg1(torch, fp4, workloads, stream, sh_now, capture, no_oracle):
+    """MXFP4 quantize -> dequantize -> error sums of the fp32 [1, 131072]
+    tensor (Laplace(0,1), 1 % of entries x50): microseconds per launch and the
+    NMSE from the GPU's error sums beside the oracle's."""
+    x = workloads.cfg1_tensor(0)
+    xd = torch.from_numpy(x).to("cuda")
+    q = fp4.quantize(xd, fp4.FMT_MXFP4)
+    y = torch.empty_like(xd)
+    rows, cols = x.shape
+    ewsb = fp4.fp4_error_workspace_bytes(q.cfg, rows, cols)
+    ews = torch.empty(max(ewsb, 64), dtype=torch.uint8, device="cuda")
+    sums = torch.empty(4, dtype=torch.float64, device="cuda")
+
+    def qf(i=0):
+        rc = fp4.fp4_quantize(q.cfg, xd.data_ptr(), fp4.DT_F32, rows, cols, cols, q.codes.data_ptr(),
+                              q.scales.data_ptr(), None, fp4.GS_COMPUTE, None, 0, sh_now())
+        assert rc == 0
+
+    def df(i=0):
+        rc = fp4.fp4_dequantize(q.cfg, q.codes.data_ptr(), q.scales.data_ptr(), None, rows, cols,
+                                y.data_ptr(), fp4.DT_F32, cols, 0, sh_now())
+        assert rc == 0
+
+    def ef(i=0):
+        rc = fp4.fp4_error_sums(q.cfg, xd.data_ptr(), fp4.DT_F32, rows, cols, cols, q.codes.data_ptr(),
+                                q.scales.data_ptr(), None, sums.data_ptr(), ews.data_ptr(), ewsb,
+                                sh_now())
+        assert rc == 0
+
+    def allf(i=0):
+        qf(); df(); ef()
+
+    out = {"quantize_us": round(time_graph(torch, stream, capture, qf, 50), 3),
+           "dequantize_us": round(time_graph(torch, stream, capture, df, 50), 3),
+           "error_sums_us": round(time_graph(torch, stream, capture, ef, 50), 3),
+           "all_three_us": round(time_graph(torch, stream, capture, allf, 50), 3)}
+    allf()
+    torch.cuda.synchronize()
+    s = sums.cpu().numpy()
+    out["nmse_gpu"] = float(s[0] / s[1])
+    if not no_oracle:
+        import oracle
+        c, sc, _ = oracle.quantize(x, fp4.FMT_MXFP4)
+        out["nmse_oracle"] = oracle.nmse(x, oracle.dequantize(c, sc, fp4.FMT_MXFP4))
+        out["codes_equal_oracle"] = bool(np.array_equal(fp4.codes_view(q).cpu().numpy(), c))
+    out["bytes_note"] = ("alg bytes: read 4 B/elem fp32, codes 0.5 B/elem, scales 1/32 B/elem; "
+                         "launch-latency bound at this size (0.59 MB), reported in us")
+    return out
+
+
+def bench_cfg3(torch, fp4, workloads, dev, stream, sh_now, capture):
+    """The fused activation path on 8192x4096 bf16 (Laplace(0,1), 8 of 4096
+    channels x50): block-Hadamard(32) + MXFP4 with GEMM-layout scales, and
+    the NVFP4 + Hadamard(16) variant with its tensor scale computed (one
+    launch, and the two passes).  Six input copies rotate so that the
+    256 MB last-level cache serves no repeat."""
+    rows, cols = 8192, 4096
+    n = rows * cols
+    base = torch.from_numpy(workloads.cfg3_tensor(0).view(np.int16)).to(dev).view(torch.bfloat16)
+    ncopy = 6
+    xs = [base] + [base.clone() for _ in range(ncopy - 1)]
+    res = {}
+    wsb = 8192
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    for name, fmt, lay, mode in (("mxfp4_h32_gemm_layout", fp4.FMT_MXFP4, fp4.SCALES_GEMM, None),
+                                 ("nvfp4_h16_one_pass", fp4.FMT_NVFP4, fp4.SCALES_ROWMAJOR,
+                                  fp4.GS_COMPUTE_ONE_PASS),
+                                 ("nvfp4_h16_two_pass", fp4.FMT_NVFP4, fp4.SCALES_ROWMAJOR,
+                                  fp4.GS_COMPUTE)):
+        cfg = fp4.qconfig(fmt, True, lay)
+        outs = [fp4.quantize(xs[0], fmt, rotate=True, scale_layout=lay) for _ in range(ncopy)]
+
+        def f(i, outs=outs, cfg=cfg, fmt=fmt, mode=mode):
+            q = outs[i % ncopy]
+            rc = fp4.fp4_quantize(cfg, xs[i % ncopy].data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                  q.codes.data_ptr(), q.scales.data_ptr(),
+                                  q.global_scale.data_ptr(), mode if mode is not None else 0,
+                                  ws.data_ptr(), wsb, sh_now())
+            assert rc == 0
+
+        us = time_graph(torch, stream, capture, f, 4 * ncopy)
+        G = fp4.BLOCK[fmt]
+        nbytes = n * 2 + n // 2 + n // G
+        ent = {"avg_us": round(us, 3), "alg_bytes": nbytes,
+               "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+               "frac": round(nbytes / (us * 1e-6) / PEAK_HBM, 4)}
+        if mode == fp4.GS_COMPUTE:
+            ent["note"] = "two launches (maximum pass, encode); alg_bytes count the input once"
+        res[name] = ent
+        del outs
+    return {"kernels": res, "shape": [rows, cols],
+            "note": "per call: a HIP graph of back-to-back calls over 6 rotating input copies, "
+                    "between one HIP event pair; bytes = bf16 read once + codes + scales"}
 
 
 def bench_gemm(args, torch, fp4, workloads, dev, stream):

@@ -31,13 +31,29 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel, then link libfp4.so."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *srcs]
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="fp4build") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(s) + ".o") for s in srcs]
+
+        def run(cmd):
+            return subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+        with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+            results = list(ex.map(run, [[hipcc(), *compile_flags, *inc, "-c", "-o", o, s]
+                                        for s, o in zip(srcs, objs)]))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        results.append(run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+                       if all(r.returncode == 0 for r in results) else results[0])
+        out = "\n".join(l for r in results for l in r.stdout.splitlines()
+                        if "packed-fp32-ops" not in l)
+        if any(r.returncode != 0 for r in results):
+            raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
     os.replace(tmp, LIB)
