@@ -339,7 +339,10 @@ int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor,
  * ws/ws_bytes: device workspace of fp4_gemm_workspace_bytes() bytes (any
  * contents; used for split-K partial sums; 16-byte aligned).
  * MXINT4 / NVINT4 operands: the same call with fmt = FP4_FMT_MXINT4 (GEMM-
- * layout E8M0 scales; n * 2^e expanded exactly to bf16, bf16 MFMA) or
+ * layout E8M0 scales; n * 2^e expanded exactly to bf16, bf16 MFMA; exact for
+ * every operand fp4_quantize writes -- scale codes up to 252 with elements
+ * -7 .. 7 -- and for any element with codes up to 251: the element -8 at
+ * code 252, or any code above 252, leaves bf16's range) or
  * FP4_FMT_NVINT4 (n * e4m3 expanded exactly to fp16, fp16 MFMA, tensor scales
  * in the epilogue); K % 256 == 0 for them.
  * Requirements: M, N >= 0, K >= 0 with K % 128 == 0; codes and scales

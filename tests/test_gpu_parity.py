@@ -412,9 +412,11 @@ def _extreme_operands(fmt, M, N, K, seed):
     ac = workloads.random_codes(M, K, seed, stream=31)
     bc = workloads.random_codes(N, K, seed, stream=32)
     mx = fmt in fp4.MX_FORMATS
-    # MXINT4 expands n * 2^e to bf16: codes above 252 (7 * 2^126) overflow it,
-    # and no finite input quantizes to them (the largest bf16 gives 252)
-    big = (251, 252) if fmt == fp4.FMT_MXINT4 else (253, 254)
+    # MXINT4 expands n * 2^(c - 127) to bf16, whose largest finite value is
+    # just below 2^128: -8 * 2^125 (code 252) overflows it.  The quantizer
+    # writes neither the element -8 nor codes above 252 (the largest bf16 input
+    # gives 252 with elements in -7 .. 7), so the extreme codes here stop at 251.
+    big = (250, 251) if fmt == fp4.FMT_MXINT4 else (253, 254)
     asc = workloads.extreme_scales(M, K // G, "a", mx, seed, stream=33, big_codes=big)
     bsc = workloads.extreme_scales(N, K // G, "b", mx, seed, stream=34, big_codes=big)
     ags, bgs = (np.float32(0), np.float32(0)) if mx else (np.float32(3.5e3), np.float32(2.25e2))
