@@ -49,7 +49,8 @@ MX_FORMATS = (FMT_MXFP4, FMT_MXINT4)
 
 EXPORTED = [
     "fp4_codes_bytes", "fp4_scales_bytes", "fp4_workspace_bytes", "fp4_scale_offset",
-    "fp4_quantize", "fp4_quantize_one_pass_fits", "fp4_workspace_init", "fp4_global_scale",
+    "fp4_quantize", "fp4_quantize_noalloc", "fp4_quantize_one_pass_fits", "fp4_workspace_init",
+    "fp4_global_scale",
     "fp4_quantize_batch_workspace_bytes", "fp4_quantize_batch", "fp4_dequantize",
     "fp4_error_workspace_bytes", "fp4_error_sums",
     "fp4_scales_to_gemm_layout", "fp4_gemm_workspace_bytes", "fp4_gemm",
@@ -116,6 +117,8 @@ def lib():
         L.fp4_scale_offset.argtypes = [CP, I64, I64, I64, I64]
         L.fp4_quantize.restype = ctypes.c_int
         L.fp4_quantize.argtypes = [CP, P, I32, I64, I64, I64, P, P, P, I32, P, SZ, P]
+        L.fp4_quantize_noalloc.restype = ctypes.c_int
+        L.fp4_quantize_noalloc.argtypes = [CP, P, I32, I64, I64, I64, P, P, P, I32, P]
         L.fp4_workspace_init.restype = ctypes.c_int
         L.fp4_workspace_init.argtypes = [P, SZ, P]
         L.fp4_quantize_one_pass_fits.restype = ctypes.c_int
@@ -189,6 +192,14 @@ def fp4_quantize(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, gs_m
     """Raw call: pointers are ints (device addresses), stream an int handle."""
     return lib().fp4_quantize(ctypes.byref(cfg), x, xdt, rows, cols, ldx, codes, scales,
                               global_scale, gs_mode, ws, ws_bytes, stream)
+
+
+def fp4_quantize_noalloc(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, gs_mode,
+                         stream) -> int:
+    """Raw call: fp4_quantize with the library's static per-GPU scratch (no
+    workspace argument, nothing allocated)."""
+    return lib().fp4_quantize_noalloc(ctypes.byref(cfg), x, xdt, rows, cols, ldx, codes, scales,
+                                      global_scale, gs_mode, stream)
 
 
 def fp4_workspace_init(ws, ws_bytes, stream) -> int:

@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp4.so")
-SOURCES = ["api.cpp", "quantize.hip", "dequant.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "dequant.hip", "gemm.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

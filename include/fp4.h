@@ -248,6 +248,24 @@ int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt,
                      int64_t rows, int64_t cols, int64_t ldx, float* global_scale,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* fp4_quantize without the workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc.  The same computation and results as
+ * fp4_quantize with the same arguments; the NVFP4 / NVINT4 scratch (partial
+ * maxima, single-pass exchange region) is a static device array of 8192
+ * bytes inside the library, one per GPU, held until the process ends.  The
+ * call allocates nothing; its first call on a device also zeroes the exchange
+ * region (a fill kernel on `stream`).  Every call on a GPU uses that GPU's one
+ * array, which keeps the last call's contents: calls that may overlap in time
+ * on one GPU (other streams, other host threads) race on it and must be
+ * serialised by the caller (one stream is enough).  Returns
+ * FP4_ERR_WORKSPACE if a configuration would need more than the static
+ * scratch (none does today), otherwise exactly what fp4_quantize returns. */
+int fp4_quantize_noalloc(const fp4_qconfig* cfg, const void* x, int32_t xdt,
+                         int64_t rows, int64_t cols, int64_t ldx,
+                         uint8_t* codes, uint8_t* scales, float* global_scale, int32_t gs_mode,
+                         void* stream);
+
 /* One quantization of a batch: the arguments of fp4_quantize. */
 typedef struct {
     fp4_qconfig cfg;

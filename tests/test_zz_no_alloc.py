@@ -1,0 +1,83 @@
+"""fp4_quantize_noalloc: the quantize entry point whose NVFP4 scratch is a
+static per-GPU device array instead of a caller workspace.  Called through
+the C ABI and compared with fp4_quantize (the same configuration with a
+workspace) bit for bit: codes, scales and tensor scale, for NVFP4 with the
+tensor scale computed in two passes and in one, NVINT4, rotated and plain,
+and MXFP4 (which needs no scratch); two calls in a row, the second with a
+smaller input, so that the static scratch is reused."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import fp4_microscaling_quantization_amd as fp4
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+CASES = [(fp4.FMT_NVFP4, False, fp4.GS_COMPUTE), (fp4.FMT_NVFP4, True, fp4.GS_COMPUTE),
+         (fp4.FMT_NVFP4, False, fp4.GS_COMPUTE_ONE_PASS), (fp4.FMT_NVFP4, True, fp4.GS_COMPUTE_ONE_PASS),
+         (fp4.FMT_NVINT4, True, fp4.GS_COMPUTE_ONE_PASS), (fp4.FMT_MXFP4, True, fp4.GS_COMPUTE)]
+IDS = ["nvfp4-2pass", "nvfp4-h16-2pass", "nvfp4-1pass", "nvfp4-h16-1pass", "nvint4-h16-1pass",
+       "mxfp4-h32"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fp4.lib()
+
+
+def _outputs(cfg, rows, cols, fill):
+    """Output buffers: codes prefilled with `fill` (every byte is written);
+    scales prefilled with 0xAA on both sides, since the GEMM layout's padding
+    bytes are left as they are."""
+    codes = torch.full((max(fp4.fp4_codes_bytes(rows, cols), 16),), fill, dtype=torch.uint8, device="cuda")
+    scales = torch.full((max(fp4.fp4_scales_bytes(cfg, rows, cols), 16),), 0xAA, dtype=torch.uint8,
+                        device="cuda")
+    gs = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    return codes, scales, gs
+
+
+@pytest.mark.parametrize("fmt,rot,mode", CASES, ids=IDS)
+def test_noalloc_matches_workspace_entry_point(fmt, rot, mode):
+    stream = torch.cuda.current_stream().cuda_stream
+    lay = fp4.SCALES_GEMM if fmt in fp4.MX_FORMATS else fp4.SCALES_ROWMAJOR
+    cfg = fp4.qconfig(fmt, rot, lay)
+    for rows, cols, seed in ((2048, 4096, 31), (37, 4128, 32)):  # the second call smaller
+        print("noalloc", fmt, rot, mode, rows, cols, flush=True)
+        x = torch.from_numpy(workloads.cfg2_tensor("laplace", seed, rows=rows, cols=cols).view(np.int16))
+        x = x.to("cuda").view(torch.bfloat16)
+        ref = _outputs(cfg, rows, cols, 0xAA)
+        got = _outputs(cfg, rows, cols, 0x55)
+        wsb = fp4.fp4_workspace_bytes(cfg, rows, cols)
+        ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        rc = fp4.fp4_quantize(cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols, ref[0].data_ptr(),
+                              ref[1].data_ptr(), ref[2].data_ptr(), mode, ws.data_ptr(), wsb, stream)
+        assert rc == fp4.FP4_OK
+        rc = fp4.fp4_quantize_noalloc(cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                      got[0].data_ptr(), got[1].data_ptr(), got[2].data_ptr(), mode,
+                                      stream)
+        assert rc == fp4.FP4_OK
+        torch.cuda.synchronize()
+        n = fp4.fp4_codes_bytes(rows, cols)
+        ns = fp4.fp4_scales_bytes(cfg, rows, cols)
+        assert torch.equal(got[0][:n], ref[0][:n])
+        assert torch.equal(got[1][:ns], ref[1][:ns])
+        if fmt not in fp4.MX_FORMATS:
+            assert torch.equal(got[2], ref[2])
+
+
+def test_noalloc_rejects_what_fp4_quantize_rejects():
+    stream = torch.cuda.current_stream().cuda_stream
+    cfg = fp4.qconfig(fp4.FMT_NVFP4)
+    x = torch.zeros(4, 32, dtype=torch.bfloat16, device="cuda")
+    c, s, g = _outputs(cfg, 4, 32, 0)
+    assert fp4.fp4_quantize_noalloc(cfg, x.data_ptr(), fp4.DT_BF16, 4, 30, 32, c.data_ptr(),
+                                    s.data_ptr(), g.data_ptr(), fp4.GS_COMPUTE, stream) \
+        == fp4.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_quantize_noalloc(cfg, x.data_ptr(), fp4.DT_BF16, 4, 32, 32, c.data_ptr(),
+                                    s.data_ptr(), None, fp4.GS_COMPUTE, stream) \
+        == fp4.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_workspace_bytes(cfg, 4096, 4096) <= 8192  # the static scratch's size
