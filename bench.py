@@ -72,6 +72,10 @@ def parse():
     ap.add_argument("--gemm-iters", type=int, default=10)
     ap.add_argument("--no-copy-probe", action="store_true",
                     help="skip the untimed 64 MiB device copy used to calibrate HBM byte counters")
+    ap.add_argument("--only-gemm", default=None, metavar="SHAPES",
+                    help="run only these GEMMs a few times and print their timings (for profiler "
+                         "runs): comma-separated fmt:MxNxK with fmt mx, nv, mxint4, nvint4 or "
+                         "w4mx / w4nv (weight-only), e.g. mx:4096x4096x4096,mx:1x28672x8192")
     return ap.parse_args()
 
 
@@ -128,6 +132,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only_gemm:
+        only_gemm(args, torch, fp4, workloads, dev)
+        return
 
     # ------------------------------------------------------------ workload
     rows, cols = 4096, 4096
@@ -555,6 +562,51 @@ def main():
         "gemm": gemm,
     }
     print(json.dumps(line), flush=True)
+
+
+def only_gemm(args, torch, fp4, workloads, dev):
+    """A few calls of each listed GEMM (a short program for profiler runs):
+    seeded operands as in the GEMM section (Gaussian weights, Laplace
+    activations with outlier channels, the block Hadamard of the format,
+    GEMM-layout scales), bf16 output, `--gemm-iters` timed calls each."""
+    fmts = {"mx": fp4.FMT_MXFP4, "nv": fp4.FMT_NVFP4, "mxint4": fp4.FMT_MXINT4,
+            "nvint4": fp4.FMT_NVINT4, "w4mx": fp4.FMT_MXFP4, "w4nv": fp4.FMT_NVFP4}
+    res = {}
+    for item in args.only_gemm.split(","):
+        name, shape = item.split(":")
+        M, N, K = (int(v) for v in shape.split("x"))
+        fmt = fmts[name]
+        w = torch.from_numpy(workloads.gemm_weight(N, K, seed=1).view(np.int16)).to(dev).view(torch.bfloat16)
+        a = torch.from_numpy(workloads.gemm_activation(M, K, seed=1).view(np.int16)).to(dev).view(torch.bfloat16)
+        qw = fp4.quantize(w, fmt, rotate=True, scale_layout=fp4.SCALES_GEMM)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        if name.startswith("w4"):
+            wsb = fp4.fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K)
+            ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+
+            def call():
+                fp4.gemm_w4a16(a, qw, out=y, workspace=ws if wsb else None)
+        else:
+            qa = fp4.quantize(a, fmt, rotate=True, scale_layout=fp4.SCALES_GEMM)
+            wsb = fp4.fp4_gemm_workspace_bytes(fmt, M, N, K)
+            ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+
+            def call():
+                fp4.gemm(qa, qw, out=y, workspace=ws if wsb else None)
+        call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(max(1, args.gemm_iters)):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / max(1, args.gemm_iters)
+        res[item] = {"us_per_call": round(us, 2), "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
+        log("%s %.2f us" % (item, us))
+        del w, a, qw, y
+    print(json.dumps({"only_gemm": res}), flush=True)
 
 
 def cpu_model() -> str:

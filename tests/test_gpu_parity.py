@@ -511,6 +511,28 @@ def test_gemm_extreme_scales(fmt, M, N, K):
     _check_gemm(fmt, M, N, K, seed=K + N, out_dtype=torch.float32, operands=_extreme_operands)
 
 
+@pytest.mark.parametrize("fmt", FMTS + INT4, ids=["mxfp4", "nvfp4", "mxint4", "nvint4"])
+def test_gemm_split_k_workspace_reuse(fmt):
+    """One workspace serves split-K calls of different shapes in turn (any
+    contents on entry), and the results are repeatable bit for bit and within
+    the bound."""
+    ws = fp4.gemm_workspace(1 << 26, "cuda")
+    for (M, N, K) in ((16, 4096, 8192), (1, 2048, 28672), (128, 1024, 4096), (16, 4096, 8192)):
+        assert fp4.fp4_gemm_workspace_bytes(fmt, M, N, K) > 0
+        ac, asc, ags, bc, bsc, bgs = _rand_operands(fmt, M, N, K, seed=M + K)
+        qa = _device_operand(ac, asc, ags, fmt, M, K)
+        qb = _device_operand(bc, bsc, bgs, fmt, N, K)
+        y1 = fp4.gemm(qa, qb, out_dtype=torch.float32, workspace=ws)
+        y2 = fp4.gemm(qa, qb, out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+        rows = np.repeat(np.arange(M), 64)
+        cols = np.tile(np.arange(0, N, N // 64), M)
+        ref, absref = oracle.gemm_entries(fmt, K, ac, asc, ags, bc, bsc, bgs, rows, cols)
+        got = y1.cpu().numpy()[rows, cols].astype(np.float64)
+        assert np.all(gemm_tolerance_ok(got, ref, absref, False)), (M, N, K)
+
+
 @pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
 def test_quantize_then_gemm_end_to_end(fmt):
     """bf16 activations and weights quantized on the GPU (non-rotated, hence
