@@ -942,31 +942,45 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT>::NW * 64)) void gem
 // ------------------------------------------------------------------ W4A16
 // Weight-only FP4: Y[M, N] = A[M, K] (bf16) * dequant(B)[N, K]^T with fp32
 // accumulation on v_mfma_f32_32x32x16_bf16 ("Bridging the Gap ...": the
-// W4A16 control of the FP4 weight formats; decode streams the weights).  The
-// weights' codes and scales go through the same DMA ring as above; each wave
-// expands its own B fragments to bf16 in registers (MXFP4: the hardware
-// decode applies the E8M0 scale exactly; NVFP4: e2m1 * e4m3 in fp32, exact in
-// bf16).  Row tiles are 32 activations high (M is small in decode); the 32
-// rows' bf16 activations come straight from global memory into registers,
-// one stage ahead.  B's K order within a 64-K step is the FP4 kernels' (lane
-// half h, dword t of its 32 codes); A's lane reads the same K positions.
-template <int FMT, int BN, int NS>
+// W4A16 control of the FP4 weight formats; decode streams the weights).
+//
+// One ring carries both operands: per K-stage of 128, the BM activation rows
+// (256 bytes of bf16 each), the BN weight rows' codes (64 bytes each) and
+// their scales stream into an NS-slot LDS ring by DMA, as in the FP4 kernels.
+// Eight waves: wave w takes 64-K step w / 4 of every stage, and the four
+// waves of a step share the BM x 128 output tile.  With WMS = 1 each owns all
+// BM rows and 32 weight columns, so every weight fragment is expanded to bf16
+// once per workgroup (MXFP4: the hardware decode applies the E8M0 scale
+// exactly; NVFP4: e2m1 * e4m3 in fp32, exact in bf16) and feeds BM / 32
+// MFMAs.  With WMS = 2 each owns BM / 2 rows and 64 columns: the weights are
+// expanded twice, but each activation fragment read from LDS feeds two MFMAs
+// instead of one (the cheaper trade where expansion is cheap, MXFP4).  Two
+// waves per SIMD hide each other's LDS reads and expansion; the two step
+// groups' accumulators are summed through LDS at the end.  B's K order within a 64-K step is the FP4
+// kernels' (lane half h, dword t of its 32 codes); A's lane reads the same K
+// positions, chunk 8s + 4h + t of its row.  A rows rotate their sixteen
+// 16-byte chunks by row % 16, so the sixteen rows a fragment read serves at
+// once hit sixteen different bank groups; NVFP4 scales are read as one
+// 16-byte piece per row (sixteen consecutive rows: one bank line) rather
+// than as 16-bit loads at a 16-byte stride.
+template <int FMT, int BM, int NS, int WMS>
 struct W4Cfg {
-  static constexpr int WN = BN / 4, TN = WN / 32;
-  static constexpr int SC_BYTES = fmt_mx(FMT) ? (BN / 32) * 256 : BN * 16;
-  static constexpr int USED = BN * 64 + SC_BYTES;
-  static constexpr int RB = 4096;  // four waves, 1 KB each per round
+  static constexpr int BN = 128, NW = 8, WM = BM / WMS, WN = 32 * WMS;
+  static constexpr int TM = WM / 32, TN = WN / 32, NWN = BN / WN;
+  static_assert(TM >= 1 && NWN * WMS == 4, "four waves per step cover the tile");
+  static constexpr int B_CODES = BM * 256;  // A: BM rows x 128 bf16
+  static constexpr int B_SC = B_CODES + BN * 64;
+  static constexpr int USED = B_SC + (fmt_mx(FMT) ? (BN / 32) * 256 : BN * 16);
+  static constexpr int SC_ADV = fmt_mx(FMT) ? 256 : 16;  // scale bytes per 256-K chunk and source
+  static constexpr int RB = NW * 1024;
   static constexpr int ROUNDS = (USED + RB - 1) / RB;
   static constexpr int STAGE = ROUNDS * RB;
   static constexpr int LDS = NS * STAGE;
-  static constexpr int A_LOADS = 8;  // 16-byte activation loads per lane per stage
-  // vector-memory operations a wave may leave pending once stage kt + 1 has
-  // landed: the later stages' DMA (NS - 2 stages) and the next stage's
-  // activation loads (the activations run only one stage ahead)
-  static constexpr int IN_FLIGHT = (NS - 2) * ROUNDS + A_LOADS;
-  static_assert(NS >= 3 && IN_FLIGHT <= 63, "vmcnt range");
+  static constexpr int IN_FLIGHT = (NS - 2) * ROUNDS;
+  static_assert(B_CODES % RB == 0 && (BN * 64) % RB == 0, "rounds hold one kind of data");
+  static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS");
 };
-
 
 // Eight E2M1 codes -> eight bf16 times 2^E (E8M0 scale as the operand's exponent).
 __device__ __forceinline__ u32x4 expand8_bf16_mx(uint32_t w, float scale) {
@@ -991,154 +1005,229 @@ __device__ __forceinline__ u32x4 expand8_bf16_nv(uint32_t w, float s) {
                pack_bf16(v2[0] * s, v2[1] * s), pack_bf16(v3[0] * s, v3[1] * s)};
 }
 
-template <int FMT, int BN, int NS, int YDT, bool PARTIAL>
-__global__ __launch_bounds__(256) void gemm_w4a16_kernel(
+template <int TM, int TN, bool MX>
+struct W4Frags {
+  u32x4 a[TM][4];  // A: four chunks (one per MFMA of the step) per 32-row fragment
+  u32x4 b[TN];     // 32 weight columns each: 32 codes per lane
+  // raw scale words, decoded in the MFMA phase (decoding them on arrival
+  // would wait for every LDS read issued before them): MX the lane's scale
+  // dword of the tile (one byte per 64-K step), NV the row's 16 E4M3 bytes
+  std::conditional_t<MX, uint32_t, u32x4> sc[TN];
+};
+
+template <int FMT, int BM, int NS, int WMS, int YDT, bool PARTIAL>
+__global__ __launch_bounds__(512) void gemm_w4a16_kernel(
     const uint8_t* __restrict__ A, int64_t lda_bytes, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, const float* __restrict__ bgs, void* __restrict__ Y,
     int64_t ldy, int M, int N, int K, int kchunks, int tiles_n, int kt_per_split,
     float* __restrict__ part) {
-  using C = W4Cfg<FMT, BN, NS>;
-  constexpr int TN = C::TN, WN = C::WN, ROUNDS = C::ROUNDS;
+  using C = W4Cfg<FMT, BM, NS, WMS>;
+  constexpr int TM = C::TM, TN = C::TN, BN = C::BN, ROUNDS = C::ROUNDS;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave >> 2;  // the 64-K step of each stage this wave takes
+  const int wn = (wave & 3) % C::NWN, wm = (wave & 3) / C::NWN;
   int tm, tn;
-  tile_of((M + 31) / 32, tiles_n, tm, tn);
-  const int m0 = tm * 32, n0 = tn * BN;
+  tile_of((M + BM - 1) / BM, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int64_t rowbytes = K / 2;
   const int KT_total = K / 128;
   const int kt0 = PARTIAL ? blockIdx.y * kt_per_split : 0;
   const int kt1 = PARTIAL ? min(KT_total, kt0 + kt_per_split) : KT_total;
 
-  // DMA sources: B code rows, then the scale pieces of the stage.
+  // DMA sources of this thread, one per round: A rows, B code rows, then the
+  // scale pieces of the stage (and slot padding, which re-reads scales).
   const uint8_t* src[ROUNDS];
-  int kind[ROUNDS];  // 0 codes, 1 MX scale tile, 2 NV scale chunk
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int p = r * C::RB + tid * 16;
-    if (p < BN * 64) {
-      const int row = p >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
+    if (r * C::RB < C::B_CODES) {
+      const int row = p >> 8, chunk = ((p >> 4) & 15) ^ (row & 15);
+      src[r] = A + (int64_t)min(m0 + row, M - 1) * lda_bytes + chunk * 16;
+    } else if (r * C::RB < C::B_SC) {
+      const int row = (p - C::B_CODES) >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
       src[r] = B + (int64_t)min(n0 + row, N - 1) * rowbytes + chunk * 16;
-      kind[r] = 0;
     } else if (p < C::USED) {
-      const int q = p - BN * 64;
+      const int q = p - C::B_SC;
       if constexpr (fmt_mx(FMT))
         src[r] = Bs + (int64_t)min((n0 >> 5) + (q >> 8), (N - 1) >> 5) * kchunks * 256 + (q & 255);
       else
         src[r] = Bs + (int64_t)min(n0 + (q >> 4), N - 1) * (K / 16);
-      kind[r] = fmt_mx(FMT) ? 1 : 2;
     } else {
       src[r] = Bs;
-      kind[r] = 2;
     }
   }
   auto slot_of = [&](int kt) __attribute__((always_inline)) {
     return dyn_lds + (kt % NS) * C::STAGE;
   };
   constexpr int H = ROUNDS / 2;
-  auto dma_part = [&](int kt, int r) __attribute__((always_inline)) {
+  auto dma = [&](int kt, int r) __attribute__((always_inline)) {
     const int ks = min(kt, kt1 - 1);
-    const int64_t adv = kind[r] == 0 ? ks * 64 : (kind[r] == 1 ? (ks >> 1) * 256 : (ks >> 1) * 16);
+    const int64_t adv = r * C::RB < C::B_CODES ? (int64_t)ks * 256
+                        : r * C::RB < C::B_SC  ? (int64_t)ks * 64
+                                               : (int64_t)(ks >> 1) * C::SC_ADV;
     dma16(src[r] + adv, slot_of(kt) + r * C::RB + wave * 1024);
   };
-
-  // activations: lane row m0 + lane % 32 (clamped), K half h = lane / 32
-  const uint8_t* arow = A + (int64_t)min(m0 + (lane & 31), M - 1) * lda_bytes + (lane >> 5) * 64;
-  u32x4 a_cur[8], a_nxt[8];
-  auto load_a = [&](int kt, u32x4* dst) __attribute__((always_inline)) {
-    const int ks = min(kt, kt1 - 1);
+  auto dma_head = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int r = 0; r < H; ++r) dma(kt, r);
+  };
+  auto dma_tail = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        dst[s * 4 + t] = *reinterpret_cast<const u32x4*>(arow + (int64_t)ks * 256 + s * 128 + t * 16);
+    for (int r = H; r < ROUNDS; ++r) dma(kt, r);
   };
 
-  f32x16 acc[TN];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // one 64-K step: B fragments of the step from LDS, expanded per MFMA
-  auto step = [&](int kt, int s, const u32x4* a) __attribute__((always_inline)) {
+  using Frags = W4Frags<TM, TN, fmt_mx(FMT)>;
+  // the weights' pieces first: the expansion that opens the MFMA phase needs
+  // them before any activation fragment
+  auto read_step = [&](int kt, int s, Frags& f) __attribute__((always_inline)) {
     const uint8_t* slot = slot_of(kt);
-    const int q = s * 2 + (lane >> 5);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int row = wave * WN + j * 32 + (lane & 31);
-      const u32x4 codes = *reinterpret_cast<const u32x4*>(slot + row * 64 + ((q ^ swz4(row)) * 16));
+      const int brow = wn * C::WN + j * 32 + (lane & 31);  // the lane's weight row in the tile
+      f.b[j] = *reinterpret_cast<const u32x4*>(slot + C::B_CODES + brow * 64 +
+                                               (((2 * s + h) ^ swz4(brow)) * 16));
+      if constexpr (fmt_mx(FMT))
+        f.sc[j] = *reinterpret_cast<const uint32_t*>(slot + C::B_SC + (brow >> 5) * 256 +
+                                                     (lane & 31) * 4 + h * 128);
+      else
+        f.sc[j] = *reinterpret_cast<const u32x4*>(slot + C::B_SC + brow * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const uint8_t* ar = slot + (wm * C::WM + i * 32 + (lane & 31)) * 256;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        f.a[i][t] = *reinterpret_cast<const u32x4*>(ar + (((8 * s + 4 * h + t) ^ (lane & 15)) * 16));
+    }
+  };
+  // MFMAs t0 .. t1-1 of the step s of stage kt (one per 16-K piece of the
+  // lane's codes)
+  auto mfmas = [&](int kt, int s, const Frags& f, int t0, int t1) __attribute__((always_inline)) {
+    float s0[TN], s1[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
       if constexpr (fmt_mx(FMT)) {
-        const uint32_t sc = *reinterpret_cast<const uint32_t*>(slot + BN * 64 + (row >> 5) * 256 + (lane & 31) * 4 +
-                                                                (lane >> 5) * 128);
-        const uint32_t code = (sc >> (8 * (2 * (kt & 1) + s))) & 0xFFu;
-        if constexpr (fmt_int(FMT)) {
-          const float p = e8m0_value(code);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[j] = mfma_bf16(a[s * 4 + t], expand8_i4_bf16(codes[t], p), acc[j]);
-        } else {
-          const float scale = e8m0_as_cvt_scale(code);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[j] = mfma_bf16(a[s * 4 + t], expand8_bf16_mx(codes[t], scale), acc[j]);
-        }
+        const uint32_t code = (f.sc[j] >> (8 * (2 * (kt & 1) + s))) & 0xFFu;
+        s0[j] = s1[j] = fmt_int(FMT) ? e8m0_value(code) : e8m0_as_cvt_scale(code);
       } else {
-        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(
-            slot + BN * 64 + row * 16 + 8 * (kt & 1) + 4 * s + 2 * (lane >> 5));
-        const float s0 = e4m3_value(sc2 & 0xFFu), s1 = e4m3_value(sc2 >> 8);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc[j] = mfma_bf16(a[s * 4 + t],
-                             fmt_int(FMT) ? expand8_i4_bf16(codes[t], t < 2 ? s0 : s1)
-                                          : expand8_bf16_nv(codes[t], t < 2 ? s0 : s1),
-                             acc[j]);
+        const uint32_t lo = (kt & 1) ? f.sc[j][2] : f.sc[j][0], hi = (kt & 1) ? f.sc[j][3] : f.sc[j][1];
+        const uint32_t w = (s ? hi : lo) >> (16 * h);
+        s0[j] = e4m3_value(w & 0xFFu);
+        s1[j] = e4m3_value((w >> 8) & 0xFFu);
       }
+    }
+#pragma unroll
+    for (int t = t0; t < t1; ++t) {
+      u32x4 bv[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const float sc = t < 2 ? s0[j] : s1[j];
+        if constexpr (fmt_int(FMT))
+          bv[j] = expand8_i4_bf16(f.b[j][t], sc);
+        else if constexpr (fmt_mx(FMT))
+          bv[j] = expand8_bf16_mx(f.b[j][t], sc);
+        else
+          bv[j] = expand8_bf16_nv(f.b[j][t], sc);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_bf16(f.a[i][t], bv[j], acc[i][j]);
     }
   };
 
   if (kt0 < kt1) {
-    load_a(kt0, a_cur);
+    // Per stage (this wave's step of it, fragments already in registers):
+    // the tail of stage kt+NS-1's DMA with the first two MFMAs; wait for
+    // stage kt+1 and sync; the head of stage kt+NS's DMA (into slot kt, which
+    // nobody reads after the sync) and the reads of stage kt+1 with the last
+    // two MFMAs, so the reads' latency falls under MFMA work although all
+    // waves leave the barrier together.
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i)
-#pragma unroll
-      for (int r = 0; r < ROUNDS; ++r) dma_part(kt0 + i, r);
-#pragma unroll
-    for (int r = 0; r < H; ++r) dma_part(kt0 + NS - 1, r);
+    for (int i = 0; i < NS - 1; ++i) {
+      dma_head(kt0 + i);
+      dma_tail(kt0 + i);
+    }
+    dma_head(kt0 + NS - 1);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * ROUNDS + H, 15));
     __builtin_amdgcn_s_barrier();
-    for (int kt = kt0; kt < kt1; ++kt) {
-      // first half: next stage's activations, the tail of stage kt+NS-1's
-      // DMA, step 0; then wait for stage kt+1 and sync; second half: the
-      // head of stage kt+NS's DMA (into slot kt, read by nobody after the
-      // sync of the next iteration) and step 1.
-      load_a(kt + 1, a_nxt);
-#pragma unroll
-      for (int r = H; r < ROUNDS; ++r) dma_part(kt + NS - 1, r);
-      step(kt, 0, a_cur);
-      step(kt, 1, a_cur);
+    Frags F0, F1;
+    read_step(kt0, kg, F0);
+    auto stage = [&](int kt, const Frags& f, Frags& g) __attribute__((always_inline)) {
+      dma_tail(kt + NS - 1);
+      mfmas(kt, kg, f, 0, 2);
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::IN_FLIGHT, 0));
       __builtin_amdgcn_s_barrier();
-#pragma unroll
-      for (int r = 0; r < H; ++r) dma_part(kt + NS, r);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a_cur[i] = a_nxt[i];
+      __builtin_amdgcn_sched_barrier(0);
+      dma_head(kt + NS);
+      read_step(kt + 1, kg, g);
+      __builtin_amdgcn_sched_barrier(0);  // the reads go out before the MFMAs
+      mfmas(kt, kg, f, 2, 4);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = kt0;
+    for (; kt + 1 < kt1; kt += 2) {
+      stage(kt, F0, F1);
+      stage(kt + 1, F1, F0);
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+    if (kt < kt1) stage(kt, F0, F1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   }
 
+  // Sum of the two step groups: the second group's accumulators go through
+  // LDS (the ring is idle: every wave has passed its last read and waited for
+  // its DMAs), lane-contiguous dwords.
+  static_assert(4 * TM * TN * 4096 <= C::LDS, "reduction fits the ring");
+  float* red = reinterpret_cast<float*>(dyn_lds) + (wave & 3) * TM * TN * 1024;
+  __builtin_amdgcn_s_barrier();
+  if (kg == 1) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[((i * TN + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  __builtin_amdgcn_s_barrier();
+  if (kg == 1) return;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] += red[((i * TN + j) * 16 + e) * 64 + lane];
+
   const float g = (!fmt_mx(FMT) && !PARTIAL) ? *bgs : 1.0f;
+  const bool full = m0 + BM <= M && n0 + BN <= N;
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = m0 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-      const int col = n0 + wave * WN + j * 32 + (lane & 31);
-      if (row < M && col < N) {
-        if constexpr (PARTIAL)
-          part[((int64_t)blockIdx.y * M + row) * N + col] = acc[j][e];
-        else
-          store_out<YDT>(Y, ldy, row, col, acc[j][e] * g);
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm * C::WM + i * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+        const int col = n0 + wn * C::WN + j * 32 + (lane & 31);
+        if (full || (row < M && col < N)) {
+          if constexpr (PARTIAL)
+            part[((int64_t)blockIdx.y * M + row) * N + col] = acc[i][j][e];
+          else
+            store_out<YDT>(Y, ldy, row, col, acc[i][j][e] * g);
+        }
+        if (e == 15) __builtin_amdgcn_sched_barrier(0);
       }
-    }
 }
 
 // The ring needs more than the default 64 KB of LDS; raise the limit once.
@@ -1242,53 +1331,69 @@ hipError_t launch_nv_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, cons
   return hipGetLastError();
 }
 
-template <int FMT, int YDT, bool PARTIAL>
+template <int FMT, int BM, int NS, int WMS, int YDT, bool PARTIAL>
 hipError_t w4_lds_attr() {
   static hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_w4a16_kernel<FMT, 256, 3, YDT, PARTIAL>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, W4Cfg<FMT, 256, 3>::LDS);
+      reinterpret_cast<const void*>(&gemm_w4a16_kernel<FMT, BM, NS, WMS, YDT, PARTIAL>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, W4Cfg<FMT, BM, NS, WMS>::LDS);
   return status;
 }
 
-template <int FMT>
-hipError_t launch_w4_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda_bytes,
+template <int FMT, int BM, int NS, int WMS>
+hipError_t launch_w4_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda_bytes,
                          const uint8_t* b, const uint8_t* bs, const float* bgs, void* y, int ydt,
                          int64_t ldy, int splits, int kt_per, float* part, hipStream_t st) {
-  using C = W4Cfg<FMT, 256, 3>;
-  const int tiles_n = (int)((N + 255) / 256);
-  const dim3 grid((unsigned)(((M + 31) / 32) * tiles_n), (unsigned)splits);
+  using C = W4Cfg<FMT, BM, NS, WMS>;
+  const int tiles_n = (int)((N + C::BN - 1) / C::BN);
+  const dim3 grid((unsigned)(((M + BM - 1) / BM) * tiles_n), (unsigned)splits);
   const int kchunks = (int)mx_gemm_kchunks(K);
   hipError_t e;
   if (splits > 1) {
-    if ((e = w4_lds_attr<FMT, FP4_DT_F32, true>()) != hipSuccess) return e;
-    gemm_w4a16_kernel<FMT, 256, 3, FP4_DT_F32, true><<<grid, 256, C::LDS, st>>>(
+    if ((e = w4_lds_attr<FMT, BM, NS, WMS, FP4_DT_F32, true>()) != hipSuccess) return e;
+    gemm_w4a16_kernel<FMT, BM, NS, WMS, FP4_DT_F32, true><<<grid, C::NW * 64, C::LDS, st>>>(
         a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
   } else if (ydt == FP4_DT_F32) {
-    if ((e = w4_lds_attr<FMT, FP4_DT_F32, false>()) != hipSuccess) return e;
-    gemm_w4a16_kernel<FMT, 256, 3, FP4_DT_F32, false><<<grid, 256, C::LDS, st>>>(
+    if ((e = w4_lds_attr<FMT, BM, NS, WMS, FP4_DT_F32, false>()) != hipSuccess) return e;
+    gemm_w4a16_kernel<FMT, BM, NS, WMS, FP4_DT_F32, false><<<grid, C::NW * 64, C::LDS, st>>>(
         a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
   } else {
-    if ((e = w4_lds_attr<FMT, FP4_DT_BF16, false>()) != hipSuccess) return e;
-    gemm_w4a16_kernel<FMT, 256, 3, FP4_DT_BF16, false><<<grid, 256, C::LDS, st>>>(
+    if ((e = w4_lds_attr<FMT, BM, NS, WMS, FP4_DT_BF16, false>()) != hipSuccess) return e;
+    gemm_w4a16_kernel<FMT, BM, NS, WMS, FP4_DT_BF16, false><<<grid, C::NW * 64, C::LDS, st>>>(
         a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
   }
   return hipGetLastError();
 }
 
-// Split factor of the weight-only GEMM: 32-row tiles, split K while fewer than
-// 512 workgroups would run (at least 4 stages per slice, slices of whole
-// 256-K scale chunks).
+// Row tile of the weight-only GEMM: the rows of M up to 128 in one tile (32,
+// 64 or 128; shallower tiles get deeper rings), 128 weight columns.  Split K
+// while fewer than 256 workgroups would run (at least 4 stages per slice,
+// slices of whole 256-K scale chunks).
 struct W4Plan {
-  int splits, kt_per;
+  int bm, splits, kt_per;
 };
 W4Plan plan_w4(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + 31) / 32) * ((N + 255) / 256);
+  const int bm = M <= 32 ? 32 : (M <= 64 ? 64 : 128);
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + 127) / 128);
   const int KT = (int)(K / 128);
   int splits = 1;
-  while (tiles * splits * 2 <= 512 && splits < 16 && KT / (splits * 2) >= 4) splits *= 2;
+  while (tiles * splits * 2 <= 256 && splits < 16 && KT / (splits * 2) >= 4) splits *= 2;
   int kt_per = (KT + splits - 1) / splits;
   kt_per += kt_per & 1;
-  return W4Plan{splits, kt_per};
+  return W4Plan{bm, splits, kt_per};
+}
+
+template <int FMT>
+hipError_t launch_w4_fmt(int bm, int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda_bytes,
+                         const uint8_t* b, const uint8_t* bs, const float* bgs, void* y, int ydt,
+                         int64_t ldy, int splits, int kt_per, float* part, hipStream_t st) {
+  // MXFP4 expands cheaply: split the rows over two waves to halve the
+  // activation reads; the other formats expand each weight fragment once.
+  constexpr int WMS = FMT == FP4_FMT_MXFP4 ? 2 : 1;
+  if (bm == 32)
+    return launch_w4_cfg<FMT, 32, 6, 1>(M, N, K, a, lda_bytes, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  if (bm == 64)
+    return launch_w4_cfg<FMT, 64, 4, WMS>(M, N, K, a, lda_bytes, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  return launch_w4_cfg<FMT, 128, 3, WMS>(M, N, K, a, lda_bytes, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
 }
 
 // Y = 0 (a product over an empty K range).
@@ -1617,13 +1722,13 @@ hipError_t launch_gemm_w4a16(int fmt, int64_t M, int64_t N, int64_t K, const voi
   const uint8_t* ab = static_cast<const uint8_t*>(a);
   hipError_t e;
   if (fmt == FP4_FMT_MXFP4)
-    e = launch_w4_fmt<FP4_FMT_MXFP4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_w4_fmt<FP4_FMT_MXFP4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else if (fmt == FP4_FMT_NVFP4)
-    e = launch_w4_fmt<FP4_FMT_NVFP4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_w4_fmt<FP4_FMT_NVFP4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else if (fmt == FP4_FMT_MXINT4)
-    e = launch_w4_fmt<FP4_FMT_MXINT4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_w4_fmt<FP4_FMT_MXINT4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else
-    e = launch_w4_fmt<FP4_FMT_NVINT4>(M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_w4_fmt<FP4_FMT_NVINT4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy,
                               fmt_mx(fmt) ? nullptr : bgs, nullptr, st);

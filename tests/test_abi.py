@@ -261,7 +261,9 @@ def test_gemm_w4a16_rejects_bad_arguments_on_host():
     assert _w(M=0, y=None) == E.FP4_OK                       # empty output: nothing to do
     assert _w(N=0, y=None) == E.FP4_OK
     assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXFP4, 1, 8192, 28672) > 0
-    assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_NVFP4, 16, 28672, 8192) > 0
+    assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_NVFP4, 16, 4096, 8192) > 0
+    # 224 column tiles of 128 already fill the GPU: no split
+    assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_NVFP4, 16, 28672, 8192) == 0
     assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXFP4, 1, 8192, 1000) == 0
     assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXFP4, 4096, 4096, 4096) == 0
     assert fp4.fp4_gemm_w4a16_workspace_bytes(fp4.FMT_MXINT4, 1, 8192, 28672) > 0

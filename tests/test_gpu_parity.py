@@ -589,8 +589,8 @@ def _check_w4a16(fmt, M, N, K, seed, out_dtype, lda_pad=0, nrows=8, nent=256, sp
     return y
 
 
-W4_SMALL = [(1, 64, 256), (7, 96, 512), (16, 300, 768), (33, 520, 1024), (100, 256, 256),
-            (257, 130, 512), (1, 4096, 4096), (16, 1024, 2048)]
+W4_SMALL = [(1, 64, 256), (7, 96, 512), (16, 300, 768), (33, 520, 1024), (64, 200, 512),
+            (100, 256, 256), (128, 384, 1024), (257, 130, 512), (1, 4096, 4096), (16, 1024, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", W4_SMALL, ids=["%dx%dx%d" % s for s in W4_SMALL])
@@ -691,8 +691,11 @@ def test_int4_quantize_then_gemm_end_to_end(fmt):
     assert np.all(gemm_tolerance_ok(got, ref, absref, False))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (16, 300, 768), (33, 520, 1024), (1, 8192, 28672)],
-                         ids=["1x64x256", "16x300x768", "33x520x1024", "1x8192x28672"])
+W4_INT4 = [(1, 64, 256), (16, 300, 768), (33, 520, 1024), (65, 384, 768), (128, 1024, 2048),
+           (1, 8192, 28672)]
+
+
+@pytest.mark.parametrize("M,N,K", W4_INT4, ids=["%dx%dx%d" % s for s in W4_INT4])
 @pytest.mark.parametrize("fmt", INT4, ids=["mxint4", "nvint4"])
 def test_gemm_w4a16_int4_weights(fmt, M, N, K):
     _check_w4a16(fmt, M, N, K, seed=M + N + K, out_dtype=torch.float32, nrows=min(M, 8), nent=256)
