@@ -677,6 +677,15 @@ struct NvCfg {
   static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
 };
 
+// Two E4M3 codes (bits 0-7 and 8-15 of w) as fp16 / fp32 by the hardware FP8
+// conversion: every finite E4M3 value, subnormals included, is exactly an
+// fp16 and an fp32 value (checked against the bit construction for all 127
+// finite codes), and one instruction replaces a subnormal test per code.
+__device__ __forceinline__ f16x2 e4m3x2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+__device__ __forceinline__ f32x2 e4m3x2_f32(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, false); }
+
 __device__ __forceinline__ f32x16 mfma_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -860,17 +869,11 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT>::NW * 64)) void gem
       }
       return;
     }
-    _Float16 sa[TM][2], sbv[TN][2];
+    f16x2 sa[TM], sbv[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      sa[i][0] = (_Float16)e4m3_value(f.sa[i] & 0xFFu);
-      sa[i][1] = (_Float16)e4m3_value((f.sa[i] >> 8) & 0xFFu);
-    }
+    for (int i = 0; i < TM; ++i) sa[i] = e4m3x2_f16(f.sa[i]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      sbv[j][0] = (_Float16)e4m3_value(f.sb[j] & 0xFFu);
-      sbv[j][1] = (_Float16)e4m3_value((f.sb[j] >> 8) & 0xFFu);
-    }
+    for (int j = 0; j < TN; ++j) sbv[j] = e4m3x2_f16(f.sb[j]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f16x8 av[TM], bv[TN];
@@ -1123,8 +1126,9 @@ __global__ __launch_bounds__(512) void gemm_w4a16_kernel(
       } else {
         const uint32_t lo = (kt & 1) ? f.sc[j][2] : f.sc[j][0], hi = (kt & 1) ? f.sc[j][3] : f.sc[j][1];
         const uint32_t w = (s ? hi : lo) >> (16 * h);
-        s0[j] = e4m3_value(w & 0xFFu);
-        s1[j] = e4m3_value((w >> 8) & 0xFFu);
+        const f32x2 sv = e4m3x2_f32(w);
+        s0[j] = sv[0];
+        s1[j] = sv[1];
       }
     }
 #pragma unroll
@@ -1477,7 +1481,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nv_kernel(
   auto expand = [&](u32x4 codes, uint32_t sc2, uint8_t* dst_row) __attribute__((always_inline)) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const _Float16 s = (_Float16)e4m3_value((sc2 >> (8 * blk)) & 0xFFu);
+      const _Float16 s = e4m3x2_f16(sc2)[blk];
       const f16x2 s2 = {s, s};
 #pragma unroll
       for (int dwi = 0; dwi < 2; ++dwi) {
