@@ -655,7 +655,7 @@ __global__ __launch_bounds__((Mx2Cfg<BM, BN, WM, WN>::NW * 64)) void gemm_mx2_ke
 // 32) as in the MXFP4 kernel and feeds dword t of them to MFMA t of the step,
 // for A rows and B columns alike.  The fp32 tensor scales multiply the
 // accumulators in the epilogue.
-template <int BM, int BN, int WM, int WN, int NS, int FMT = FP4_FMT_NVFP4>
+template <int BM, int BN, int WM, int WN, int NS, int FMT = FP4_FMT_NVFP4, int KG = 1>
 struct NvCfg {
   // MX: E8M0 scales in the GEMM layout (one 256-byte tile per 32 rows per
   // 256 K, re-loaded with each stage of the pair); NV: each row's 16 E4M3
@@ -667,14 +667,19 @@ struct NvCfg {
   static constexpr int B_SC = A_SC + (MX ? BM * 8 : BM * 16);
   static constexpr int USED = B_SC + (MX ? BN * 8 : BN * 16);
   static constexpr int SC_ADV = MX ? 256 : 16;  // scale bytes per 256-K chunk and source
-  static constexpr int NW = (BM / WM) * (BN / WN);
+  // KG = 2: two groups of waves, each taking one 64-K step of every stage
+  // (two waves per SIMD for the small decode tiles), summed at the end
+  static constexpr int WPG = (BM / WM) * (BN / WN);  // waves per group
+  static constexpr int NW = KG * WPG;
   static constexpr int RB = NW * 1024;
   static constexpr int ROUNDS = (USED + RB - 1) / RB;
   static constexpr int STAGE = ROUNDS * RB;
   static constexpr int LDS = NS * STAGE;
   static constexpr int IN_FLIGHT = (NS - 2) * ROUNDS;
   static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(KG == 1 || KG == 2, "one or two K-step groups");
   static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
+  static_assert(KG == 1 || WPG * TM * TN * 4096 <= LDS, "the group sum fits the ring");
 };
 
 // Two E4M3 codes (bits 0-7 and 8-15 of w) as fp16 / fp32 by the hardware FP8
@@ -740,18 +745,19 @@ struct NvFrags {
   uint32_t sa[TM], sb[TN];  // two E4M3 scale bytes per fragment (blocks of the lane's 32 codes)
 };
 
-template <int FMT, int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
-__global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT>::NW * 64)) void gemm_nv_ring_kernel(
+template <int FMT, int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL, int KG>
+__global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void gemm_nv_ring_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ ags,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ bgs,
     void* __restrict__ Y, int64_t ldy, int M, int N, int K, int tiles_n, int kt_per_split,
     float* __restrict__ part) {
-  using C = NvCfg<BM, BN, WM, WN, NS, FMT>;
+  using C = NvCfg<BM, BN, WM, WN, NS, FMT, KG>;
   constexpr int TM = C::TM, TN = C::TN, ROUNDS = C::ROUNDS;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / (BN / WN), wn = wave % (BN / WN);
+  const int kg = wave / C::WPG, wg = wave % C::WPG;  // K-step group, wave in the group
+  const int wm = wg / (BN / WN), wn = wg % (BN / WN);
   const int64_t kchunks = K / 256;
   int tm, tn;
   tile_of((M + BM - 1) / BM, tiles_n, tm, tn);
@@ -847,7 +853,8 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT>::NW * 64)) void gem
         f.sb[j] = *reinterpret_cast<const uint16_t*>(slot + C::B_SC + row * 16 + sb);
     }
   };
-  auto mfmas = [&](const Frags& f) __attribute__((always_inline)) {
+  // MFMAs t0 .. t1-1 of a step (one per 16-K piece of the lane's codes)
+  auto mfmas = [&](const Frags& f, int t0 = 0, int t1 = 4) __attribute__((always_inline)) {
     if constexpr (C::MX) {
       // MXINT4: q * 2^e exact in bf16, bf16 MFMA
       float pa[TM], pb[TN];
@@ -856,7 +863,7 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT>::NW * 64)) void gem
 #pragma unroll
       for (int j = 0; j < TN; ++j) pb[j] = e8m0_value(f.sb[j]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = t0; t < t1; ++t) {
         u32x4 av[TM], bv[TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i) av[i] = expand8_i4_bf16(f.a[i][t], pa[i]);
@@ -875,7 +882,7 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT>::NW * 64)) void gem
 #pragma unroll
     for (int j = 0; j < TN; ++j) sbv[j] = e4m3x2_f16(f.sb[j]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = t0; t < t1; ++t) {
       f16x8 av[TM], bv[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -890,36 +897,97 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT>::NW * 64)) void gem
     }
   };
 
-  if (kt0 < kt1) {
-    // Same schedule as the MXFP4 kernel: step 1's reads and the tail of
-    // stage kt+NS-1's DMA with step 0's MFMAs; wait for stage kt+1 and sync;
-    // the head of stage kt+NS's DMA and stage kt+1's step-0 reads with step
-    // 1's MFMAs.
+  if constexpr (KG == 1) {
+    if (kt0 < kt1) {
+      // Same schedule as the MXFP4 kernel: step 1's reads and the tail of
+      // stage kt+NS-1's DMA with step 0's MFMAs; wait for stage kt+1 and
+      // sync; the head of stage kt+NS's DMA and stage kt+1's step-0 reads
+      // with step 1's MFMAs.
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i) {
-      dma_head(kt0 + i);
-      dma_tail(kt0 + i);
-    }
-    dma_head(kt0 + NS - 1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * ROUNDS + H, 15));
-    __builtin_amdgcn_s_barrier();
-    Frags F0, F1;
-    read_step(kt0, 0, F0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-    for (int kt = kt0; kt < kt1; ++kt) {
-      read_step(kt, 1, F1);
-      dma_tail(kt + NS - 1);
-      mfmas(F0);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::IN_FLIGHT, 0));
+      for (int i = 0; i < NS - 1; ++i) {
+        dma_head(kt0 + i);
+        dma_tail(kt0 + i);
+      }
+      dma_head(kt0 + NS - 1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * ROUNDS + H, 15));
       __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      dma_head(kt + NS);
-      read_step(kt + 1, 0, F0);
-      mfmas(F1);
-      __builtin_amdgcn_sched_barrier(0);
+      Frags F0, F1;
+      read_step(kt0, 0, F0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      for (int kt = kt0; kt < kt1; ++kt) {
+        read_step(kt, 1, F1);
+        dma_tail(kt + NS - 1);
+        mfmas(F0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::IN_FLIGHT, 0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        dma_head(kt + NS);
+        read_step(kt + 1, 0, F0);
+        mfmas(F1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+  } else {
+    if (kt0 < kt1) {
+      // Each group takes its own step of every stage: the tail of stage
+      // kt+NS-1's DMA with the first two MFMAs; wait for stage kt+1 and sync;
+      // the head of stage kt+NS's DMA and the reads of stage kt+1 with the
+      // last two.
+#pragma unroll
+      for (int i = 0; i < NS - 1; ++i) {
+        dma_head(kt0 + i);
+        dma_tail(kt0 + i);
+      }
+      dma_head(kt0 + NS - 1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * ROUNDS + H, 15));
+      __builtin_amdgcn_s_barrier();
+      Frags F0, F1;
+      read_step(kt0, kg, F0);
+      auto stage = [&](int kt, const Frags& f, Frags& g) __attribute__((always_inline)) {
+        dma_tail(kt + NS - 1);
+        mfmas(f, 0, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::IN_FLIGHT, 0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        dma_head(kt + NS);
+        read_step(kt + 1, kg, g);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(f, 2, 4);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      int kt = kt0;
+      for (; kt + 1 < kt1; kt += 2) {
+        stage(kt, F0, F1);
+        stage(kt + 1, F1, F0);
+      }
+      if (kt < kt1) stage(kt, F0, F1);
+    }
+    // Sum of the two groups through LDS (every wave has passed its last
+    // read; the DMAs still in flight land in ring slots, so wait for them),
+    // lane-contiguous dwords.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    float* red = reinterpret_cast<float*>(dyn_lds) + wg * TM * TN * 1024;
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) red[((i * TN + j) * 16 + e) * 64 + lane] = acc[i][j][e];
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    __builtin_amdgcn_s_barrier();
+    if (kg == 1) return;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] += red[((i * TN + j) * 16 + e) * 64 + lane];
   }
 
   const float g = (PARTIAL || C::MX) ? 1.0f : (*ags) * (*bgs);
@@ -1302,34 +1370,34 @@ hipError_t launch_mx2_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   return hipGetLastError();
 }
 
-template <int FMT, int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
+template <int FMT, int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL, int KG>
 hipError_t nv_lds_attr() {
   static hipError_t status = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, YDT, PARTIAL>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, NvCfg<BM, BN, WM, WN, NS, FMT>::LDS);
+      reinterpret_cast<const void*>(&gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, YDT, PARTIAL, KG>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, NvCfg<BM, BN, WM, WN, NS, FMT, KG>::LDS);
   return status;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int FMT = FP4_FMT_NVFP4>
+template <int BM, int BN, int WM, int WN, int NS, int FMT = FP4_FMT_NVFP4, int KG = 1>
 hipError_t launch_nv_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                          const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
                          void* y, int ydt, int64_t ldy, int splits, int kt_per, float* part,
                          hipStream_t st) {
-  using C = NvCfg<BM, BN, WM, WN, NS, FMT>;
+  using C = NvCfg<BM, BN, WM, WN, NS, FMT, KG>;
   const int tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(((M + BM - 1) / BM) * tiles_n), (unsigned)splits);
   hipError_t e;
   if (splits > 1) {
-    if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, true>()) != hipSuccess) return e;
-    gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, true><<<grid, C::NW * 64, C::LDS, st>>>(
+    if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, true, KG>()) != hipSuccess) return e;
+    gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, true, KG><<<grid, C::NW * 64, C::LDS, st>>>(
         a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
   } else if (ydt == FP4_DT_F32) {
-    if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, false>()) != hipSuccess) return e;
-    gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, false><<<grid, C::NW * 64, C::LDS, st>>>(
+    if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, false, KG>()) != hipSuccess) return e;
+    gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, false, KG><<<grid, C::NW * 64, C::LDS, st>>>(
         a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
   } else {
-    if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_BF16, false>()) != hipSuccess) return e;
-    gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_BF16, false><<<grid, C::NW * 64, C::LDS, st>>>(
+    if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_BF16, false, KG>()) != hipSuccess) return e;
+    gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_BF16, false, KG><<<grid, C::NW * 64, C::LDS, st>>>(
         a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
   }
   return hipGetLastError();
@@ -1652,7 +1720,7 @@ hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, c
   else if (p.cfg == 1)
     e = launch_nv_cfg<128, 128, 64, 64, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else
-    e = launch_nv_cfg<32, 256, 32, 64, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_nv_cfg<32, 256, 32, 64, 3, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, fmt_mx(FMT) ? nullptr : ags,
                               fmt_mx(FMT) ? nullptr : bgs, st);
@@ -1688,8 +1756,8 @@ hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
       e = launch_nv_cfg<256, 256, 128, 128, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
     else if (p.cfg == 1)
       e = launch_nv_cfg<128, 128, 64, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
-    else
-      e = launch_nv_cfg<32, 256, 32, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    else  // M <= 32: two K-step groups of four waves (two waves per SIMD)
+      e = launch_nv_cfg<32, 256, 32, 64, 3, FP4_FMT_NVFP4, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
     if (e != hipSuccess || !split) return e;
     return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, ags, bgs, st);
   }
