@@ -674,8 +674,14 @@ struct NvCfg {
   static constexpr int RB = NW * 1024;
   static constexpr int ROUNDS = (USED + RB - 1) / RB;
   static constexpr int STAGE = ROUNDS * RB;
-  static constexpr int LDS = NS * STAGE;
-  static constexpr int IN_FLIGHT = (NS - 2) * ROUNDS;
+  // With two groups the A tile of each stage is expanded once per workgroup
+  // (one 8-code piece per thread) into one of two 16-bit LDS buffers, two
+  // stages ahead of its use, instead of by every wave that reads it.
+  static constexpr bool AEXP = KG == 2;
+  static constexpr int ABUF = AEXP ? BM * 256 : 0;  // BM rows x 128 K x 2 bytes
+  static constexpr int LDS = NS * STAGE + 2 * ABUF;
+  static constexpr int IN_FLIGHT = (NS - (AEXP ? 3 : 2)) * ROUNDS;
+  static_assert(!AEXP || (NS >= 4 && BM * 16 == NW * 64), "A expansion: lookahead and one piece per thread");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(KG == 1 || KG == 2, "one or two K-step groups");
   static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
@@ -743,6 +749,7 @@ template <int TM, int TN>
 struct NvFrags {
   u32x4 a[TM], b[TN];
   uint32_t sa[TM], sb[TN];  // two E4M3 scale bytes per fragment (blocks of the lane's 32 codes)
+  u32x4 a16[TM][4];         // A already expanded (one 16-bit chunk per MFMA of the step)
 };
 
 template <int FMT, int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL, int KG>
@@ -827,6 +834,32 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   using Frags = NvFrags<TM, TN>;
+  auto abuf_of = [&](int kt) __attribute__((always_inline)) {
+    return dyn_lds + NS * C::STAGE + (kt & 1) * C::ABUF;
+  };
+  // A expansion of stage kt: thread p takes row p / 16, codes 8 (p % 16) ..
+  // +7 of the stage, and writes them as 16-bit values to chunk p % 16 of the
+  // row rotated by row % 16 (the fragment reads below: conflict-free)
+  auto expand_a = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (C::AEXP) {
+      const uint8_t* slot = slot_of(kt);
+      const int row = tid >> 4, g = tid & 15;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(
+          slot + row * 64 + (((g >> 2) ^ swz4(row)) * 16) + (g & 3) * 4);
+      u32x4 v;
+      if constexpr (C::MX) {
+        const int s = g >> 3, hh = (g >> 2) & 1;
+        const uint32_t code = (*reinterpret_cast<const uint32_t*>(slot + C::A_SC + (row >> 5) * 256 +
+                                                                  (row & 31) * 4 + hh * 128) >>
+                               (8 * (2 * (kt & 1) + s))) & 0xFFu;
+        v = expand8_i4_bf16(w, e8m0_value(code));
+      } else {
+        const _Float16 sc = e4m3x2_f16(slot[C::A_SC + row * 16 + 8 * (kt & 1) + (g >> 1)])[0];
+        v = __builtin_bit_cast(u32x4, FMT == FP4_FMT_NVINT4 ? expand8_i4_f16(w, sc) : expand8(w, sc));
+      }
+      *reinterpret_cast<u32x4*>(abuf_of(kt) + row * 256 + ((g ^ (row & 15)) * 16)) = v;
+    }
+  };
   // fragments and scale bytes of step s (0, 1) of stage kt
   auto read_step = [&](int kt, int s, Frags& f) __attribute__((always_inline)) {
     const uint8_t* slot = slot_of(kt);
@@ -837,6 +870,13 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int row = wm * WM + i * 32 + (lane & 31);
+      if constexpr (C::AEXP) {
+        const uint8_t* ar = abuf_of(kt) + row * 256;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          f.a16[i][t] = *reinterpret_cast<const u32x4*>(ar + (((8 * s + 4 * (lane >> 5) + t) ^ (lane & 15)) * 16));
+        continue;
+      }
       f.a[i] = *reinterpret_cast<const u32x4*>(slot + row * 64 + ((q ^ swz4(row)) * 16));
       if constexpr (C::MX)
         f.sa[i] = (*reinterpret_cast<const uint32_t*>(slot + C::A_SC + (row >> 5) * 256 + mxo) >> mxb) & 0xFFu;
@@ -866,7 +906,8 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
       for (int t = t0; t < t1; ++t) {
         u32x4 av[TM], bv[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) av[i] = expand8_i4_bf16(f.a[i][t], pa[i]);
+        for (int i = 0; i < TM; ++i)
+          av[i] = C::AEXP ? f.a16[i][t] : expand8_i4_bf16(f.a[i][t], pa[i]);
 #pragma unroll
         for (int j = 0; j < TN; ++j) bv[j] = expand8_i4_bf16(f.b[j][t], pb[j]);
 #pragma unroll
@@ -886,7 +927,9 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
       f16x8 av[TM], bv[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        av[i] = FMT == FP4_FMT_NVINT4 ? expand8_i4_f16(f.a[i][t], sa[i][t >> 1]) : expand8(f.a[i][t], sa[i][t >> 1]);
+        av[i] = C::AEXP ? __builtin_bit_cast(f16x8, f.a16[i][t])
+                : FMT == FP4_FMT_NVINT4 ? expand8_i4_f16(f.a[i][t], sa[i][t >> 1])
+                                        : expand8(f.a[i][t], sa[i][t >> 1]);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         bv[j] = FMT == FP4_FMT_NVINT4 ? expand8_i4_f16(f.b[j][t], sbv[j][t >> 1]) : expand8(f.b[j][t], sbv[j][t >> 1]);
@@ -932,16 +975,22 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
   } else {
     if (kt0 < kt1) {
       // Each group takes its own step of every stage: the tail of stage
-      // kt+NS-1's DMA with the first two MFMAs; wait for stage kt+1 and sync;
-      // the head of stage kt+NS's DMA and the reads of stage kt+1 with the
-      // last two.
+      // kt+NS-1's DMA with the first two MFMAs; wait for stage kt+2 (the A
+      // expansion's lookahead) and sync; the head of stage kt+NS's DMA, the
+      // expansion of stage kt+2's A and the reads of stage kt+1 with the
+      // last two.  A buffer kt % 2 is free then: its reads (of stage kt)
+      // were done before the sync.
 #pragma unroll
       for (int i = 0; i < NS - 1; ++i) {
         dma_head(kt0 + i);
         dma_tail(kt0 + i);
       }
       dma_head(kt0 + NS - 1);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * ROUNDS + H, 15));
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 3) * ROUNDS + H, 15));
+      __builtin_amdgcn_s_barrier();
+      expand_a(kt0);
+      expand_a(kt0 + 1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
       __builtin_amdgcn_s_barrier();
       Frags F0, F1;
       read_step(kt0, kg, F0);
@@ -953,6 +1002,7 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         dma_head(kt + NS);
+        expand_a(kt + 2);
         read_step(kt + 1, kg, g);
         __builtin_amdgcn_sched_barrier(0);
         mfmas(f, 2, 4);
@@ -1720,7 +1770,7 @@ hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, c
   else if (p.cfg == 1)
     e = launch_nv_cfg<128, 128, 64, 64, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else
-    e = launch_nv_cfg<32, 256, 32, 64, 3, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_nv_cfg<32, 256, 32, 64, 4, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, fmt_mx(FMT) ? nullptr : ags,
                               fmt_mx(FMT) ? nullptr : bgs, st);
@@ -1757,7 +1807,7 @@ hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
     else if (p.cfg == 1)
       e = launch_nv_cfg<128, 128, 64, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
     else  // M <= 32: two K-step groups of four waves (two waves per SIMD)
-      e = launch_nv_cfg<32, 256, 32, 64, 3, FP4_FMT_NVFP4, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+      e = launch_nv_cfg<32, 256, 32, 64, 4, FP4_FMT_NVFP4, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
     if (e != hipSuccess || !split) return e;
     return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, ags, bgs, st);
   }
