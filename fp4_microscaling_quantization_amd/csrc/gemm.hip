@@ -677,11 +677,11 @@ struct NvCfg {
   // With two groups the A tile of each stage is expanded once per workgroup
   // (one 8-code piece per thread) into one of two 16-bit LDS buffers, two
   // stages ahead of its use, instead of by every wave that reads it.
-  static constexpr bool AEXP = KG == 2;
+  static constexpr bool AEXP = KG == 2 && BM * 16 == NW * 64;
   static constexpr int ABUF = AEXP ? BM * 256 : 0;  // BM rows x 128 K x 2 bytes
   static constexpr int LDS = NS * STAGE + 2 * ABUF;
   static constexpr int IN_FLIGHT = (NS - (AEXP ? 3 : 2)) * ROUNDS;
-  static_assert(!AEXP || (NS >= 4 && BM * 16 == NW * 64), "A expansion: lookahead and one piece per thread");
+  static_assert(!AEXP || NS >= 4, "A expansion: lookahead");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(KG == 1 || KG == 2, "one or two K-step groups");
   static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
@@ -975,23 +975,25 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
   } else {
     if (kt0 < kt1) {
       // Each group takes its own step of every stage: the tail of stage
-      // kt+NS-1's DMA with the first two MFMAs; wait for stage kt+2 (the A
-      // expansion's lookahead) and sync; the head of stage kt+NS's DMA, the
-      // expansion of stage kt+2's A and the reads of stage kt+1 with the
-      // last two.  A buffer kt % 2 is free then: its reads (of stage kt)
-      // were done before the sync.
+      // kt+NS-1's DMA with the first two MFMAs; wait for stage kt+1 (kt+2
+      // with the A expansion's lookahead) and sync; the head of stage
+      // kt+NS's DMA, the expansion of stage kt+2's A and the reads of stage
+      // kt+1 with the last two.  A buffer kt % 2 is free then: its reads (of
+      // stage kt) were done before the sync.
 #pragma unroll
       for (int i = 0; i < NS - 1; ++i) {
         dma_head(kt0 + i);
         dma_tail(kt0 + i);
       }
       dma_head(kt0 + NS - 1);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 3) * ROUNDS + H, 15));
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - (C::AEXP ? 3 : 2)) * ROUNDS + H, 15));
       __builtin_amdgcn_s_barrier();
-      expand_a(kt0);
-      expand_a(kt0 + 1);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-      __builtin_amdgcn_s_barrier();
+      if constexpr (C::AEXP) {
+        expand_a(kt0);
+        expand_a(kt0 + 1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        __builtin_amdgcn_s_barrier();
+      }
       Frags F0, F1;
       read_step(kt0, kg, F0);
       auto stage = [&](int kt, const Frags& f, Frags& g) __attribute__((always_inline)) {
@@ -1746,9 +1748,15 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, nullptr, nullptr, st);
 }
 
+// The NVFP4 / INT4 ring plans: as MXFP4's, and at M <= 128 the 128x128
+// tiles run two K-step groups of waves and stop at 256 workgroups (K8192
+// N28672, M = 128: 95 -> 83 us against one group with split-K 2; at M >= 256
+// one group stays faster).
+MxPlan plan_nv(int64_t M, int64_t N, int64_t K) { return plan_mx(M, N, K, 256, true); }
+
 size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K) {
   if (K % 256 != 0 || K == 0) return 0;
-  MxPlan p = plan_mx(M, N, K);
+  MxPlan p = plan_nv(M, N, K);
   return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -1759,7 +1767,7 @@ hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, c
                             const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
                             void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
                             hipStream_t st) {
-  MxPlan p = plan_mx(M, N, K);
+  MxPlan p = plan_nv(M, N, K);
   const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_nv_workspace(M, N, K);
   const int splits = split ? p.splits : 1;
   const int kt_per = split ? p.kt_per : (int)(K / 128);
@@ -1767,6 +1775,8 @@ hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, c
   hipError_t e;
   if (p.cfg == 0)
     e = launch_nv_cfg<256, 256, 128, 128, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+  else if (p.cfg == 1 && M <= 128)
+    e = launch_nv_cfg<128, 128, 64, 64, 3, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else if (p.cfg == 1)
     e = launch_nv_cfg<128, 128, 64, 64, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else
@@ -1796,7 +1806,7 @@ hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   if (M == 0 || N == 0) return hipSuccess;
   if (K % 256 == 0 && K > 0) {
     // LDS ring with in-register fp16 expansion; tiles and split-K as for MXFP4
-    MxPlan p = plan_mx(M, N, K);
+    MxPlan p = plan_nv(M, N, K);
     const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_nv_workspace(M, N, K);
     const int splits = split ? p.splits : 1;
     const int kt_per = split ? p.kt_per : (int)(K / 128);
@@ -1804,6 +1814,8 @@ hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
     hipError_t e;
     if (p.cfg == 0)
       e = launch_nv_cfg<256, 256, 128, 128, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    else if (p.cfg == 1 && M <= 128)
+      e = launch_nv_cfg<128, 128, 64, 64, 3, FP4_FMT_NVFP4, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
     else if (p.cfg == 1)
       e = launch_nv_cfg<128, 128, 64, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
     else  // M <= 32: two K-step groups of four waves (two waves per SIMD)
