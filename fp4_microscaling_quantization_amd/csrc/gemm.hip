@@ -677,11 +677,13 @@ struct NvCfg {
   // With two groups the A tile of each stage is expanded once per workgroup
   // (one 8-code piece per thread) into one of two 16-bit LDS buffers, two
   // stages ahead of its use, instead of by every wave that reads it.
-  static constexpr bool AEXP = KG == 2 && BM * 16 == NW * 64;
+  static constexpr bool AEXP = KG == 2 && WM == BM;  // every wave reads all BM rows
   static constexpr int ABUF = AEXP ? BM * 256 : 0;  // BM rows x 128 K x 2 bytes
+  static constexpr int APIECES = AEXP ? BM * 16 / (NW * 64) : 0;  // 8-code pieces per thread
   static constexpr int LDS = NS * STAGE + 2 * ABUF;
   static constexpr int IN_FLIGHT = (NS - (AEXP ? 3 : 2)) * ROUNDS;
-  static_assert(!AEXP || NS >= 4, "A expansion: lookahead");
+  static_assert(!AEXP || (NS >= 4 && APIECES * NW * 64 == BM * 16), "A expansion: lookahead, whole pieces");
+  static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(KG == 1 || KG == 2, "one or two K-step groups");
   static_assert(NS >= 3 && (NS - 1) * ROUNDS <= 63, "vmcnt range");
@@ -837,13 +839,16 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
   auto abuf_of = [&](int kt) __attribute__((always_inline)) {
     return dyn_lds + NS * C::STAGE + (kt & 1) * C::ABUF;
   };
-  // A expansion of stage kt: thread p takes row p / 16, codes 8 (p % 16) ..
-  // +7 of the stage, and writes them as 16-bit values to chunk p % 16 of the
-  // row rotated by row % 16 (the fragment reads below: conflict-free)
+  // A expansion of stage kt: piece p (thread p, p + 64 NW, ...) is row p / 16,
+  // codes 8 (p % 16) .. +7 of the stage, written as 16-bit values to chunk
+  // p % 16 of the row rotated by row % 16 (the fragment reads below:
+  // conflict-free)
   auto expand_a = [&](int kt) __attribute__((always_inline)) {
-    if constexpr (C::AEXP) {
+#pragma unroll
+    for (int pc = 0; pc < C::APIECES; ++pc) {
       const uint8_t* slot = slot_of(kt);
-      const int row = tid >> 4, g = tid & 15;
+      const int p = pc * C::NW * 64 + tid;
+      const int row = p >> 4, g = p & 15;
       const uint32_t w = *reinterpret_cast<const uint32_t*>(
           slot + row * 64 + (((g >> 2) ^ swz4(row)) * 16) + (g & 3) * 4);
       u32x4 v;
@@ -1751,7 +1756,10 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
 // The NVFP4 / INT4 ring plans: as MXFP4's, and at M <= 128 the 128x128
 // tiles run two K-step groups of waves and stop at 256 workgroups (K8192
 // N28672, M = 128: 95 -> 83 us against one group with split-K 2; at M >= 256
-// one group stays faster).
+// one group stays faster).  NVFP4 waves there own 64x64 sub-tiles; the INT4
+// formats, whose expansion costs more, own all 128 rows x 32 columns with
+// the A tile expanded once per workgroup into LDS (NVINT4 128 -> 109 us,
+// MXINT4 155 -> 127 us; NVFP4 80 -> 95 us that way, so it keeps 64x64).
 MxPlan plan_nv(int64_t M, int64_t N, int64_t K) { return plan_mx(M, N, K, 256, true); }
 
 size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K) {
@@ -1776,7 +1784,7 @@ hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, c
   if (p.cfg == 0)
     e = launch_nv_cfg<256, 256, 128, 128, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else if (p.cfg == 1 && M <= 128)
-    e = launch_nv_cfg<128, 128, 64, 64, 3, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_nv_cfg<128, 128, 128, 32, 4, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else if (p.cfg == 1)
     e = launch_nv_cfg<128, 128, 64, 64, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
   else
