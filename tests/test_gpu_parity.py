@@ -599,11 +599,13 @@ def test_gemm_w4a16_small_full_check(fmt, M, N, K):
     _check_w4a16(fmt, M, N, K, seed=M + N + K, out_dtype=torch.float32, nrows=min(M, 16), nent=512)
 
 
+@pytest.mark.parametrize("M", [16, 48, 100], ids=["rows32", "rows64", "rows128"])
 @pytest.mark.parametrize("fmt", FMTS, ids=["mxfp4", "nvfp4"])
-def test_gemm_w4a16_strided_activations_and_unsplit(fmt):
-    """A row-strided activation view (lda > K), and the call without a
-    workspace (one pass over K) against the oracle and the split result."""
-    M, N, K = 16, 768, 4096
+def test_gemm_w4a16_strided_activations_and_unsplit(fmt, M):
+    """A row-strided activation view (lda > K) through each row tile (32, 64
+    and 128 rows), and the call without a workspace (one pass over K)
+    against the oracle and the split result."""
+    N, K = 768, 4096
     y1 = _check_w4a16(fmt, M, N, K, seed=5, out_dtype=torch.float32, lda_pad=64, nrows=16)
     y2 = _check_w4a16(fmt, M, N, K, seed=5, out_dtype=torch.float32, lda_pad=64, nrows=16, split=False)
     assert fp4.fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K) > 0
