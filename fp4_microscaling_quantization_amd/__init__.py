@@ -36,6 +36,9 @@ DT_F32 = 0
 DT_BF16 = 1
 SCALES_ROWMAJOR = 0
 SCALES_GEMM = 1
+CODES_ROWMAJOR = 0
+CODES_TILED = 1
+GEMM_B_TILED = 0x100
 GS_COMPUTE = 0
 GS_GIVEN = 1
 GS_COMPUTE_ONE_PASS = 2
@@ -68,7 +71,8 @@ class QConfig(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("block", ctypes.c_int32), ("rotate", ctypes.c_int32),
                 ("rule", ctypes.c_int32), ("scale_layout", ctypes.c_int32),
                 ("rounding", ctypes.c_int32), ("block_rows", ctypes.c_int32),
-                ("rot_signs", ctypes.c_uint32 * 4), ("seed", ctypes.c_uint32 * 2)]
+                ("rot_signs", ctypes.c_uint32 * 4), ("seed", ctypes.c_uint32 * 2),
+                ("code_layout", ctypes.c_int32)]
 
 
 class QuantJob(ctypes.Structure):
@@ -81,16 +85,19 @@ class QuantJob(ctypes.Structure):
 
 def qconfig(fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
             rule: int = SCALE_ABSMAX, rounding: int = ROUND_NEAREST, block_rows: int = 1,
-            signs: int = 0, seed=(0, 0)) -> QConfig:
+            signs: int = 0, seed=(0, 0), code_layout: int = CODES_ROWMAJOR) -> QConfig:
     """rotate: False / True (a rotation of the block size) or the rotation size
     (MX formats: 32, 64, 128).  signs: the rotation's sign mask as an integer
-    (bit i negates element i of each group).  seed: stochastic-rounding key."""
+    (bit i negates element i of each group).  seed: stochastic-rounding key.
+    code_layout: CODES_ROWMAJOR or CODES_TILED (8 KB tiles of 128 rows x 128
+    elements, for weights the GEMM streams; rows and cols multiples of 128)."""
     G = BLOCK[fmt]
     rot = 0 if rotate is False or rotate is None else (G if rotate is True else int(rotate))
     q = QConfig(fmt, G, rot, rule, scale_layout, rounding, block_rows)
     for k in range(4):
         q.rot_signs[k] = (int(signs) >> (32 * k)) & 0xFFFFFFFF
     q.seed[0], q.seed[1] = int(seed[0]) & 0xFFFFFFFF, int(seed[1]) & 0xFFFFFFFF
+    q.code_layout = code_layout
     return q
 
 
@@ -388,6 +395,8 @@ def check_gemm_operands(a: "Quantized", b: "Quantized"):
         raise ValueError("gemm: K differs (%d, %d)" % (a.cols, b.cols))
     if fa in MX_FORMATS and (a.cfg.scale_layout != SCALES_GEMM or b.cfg.scale_layout != SCALES_GEMM):
         raise ValueError("gemm: MX operands need FP4_SCALES_GEMM scales")
+    if a.cfg.code_layout != CODES_ROWMAJOR:
+        raise ValueError("gemm: A codes must be row-major (only B may be tiled)")
     if not _same_rotation(a.cfg, b.cfg):
         raise ValueError("gemm: operands quantized with different rotations")
 
@@ -408,13 +417,15 @@ def quantize(x, fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
              global_scale=None, out: Quantized | None = None,
              rule: int = SCALE_ABSMAX, rounding: int = ROUND_NEAREST, block_rows: int = 1,
              signs: int = 0, seed=(0, 0), one_pass: bool = False,
-             check_one_pass: bool = False) -> Quantized:
+             check_one_pass: bool = False, code_layout: int = CODES_ROWMAJOR) -> Quantized:
     """Quantize a 2-D CUDA tensor (fp32 or bf16, unit stride along the last
     axis).  NVFP4: ``global_scale`` (a float32[1] CUDA tensor) is used as given
     when passed, otherwise computed from the tensor's amax (``one_pass``: the
     amax and the encoding in one launch when the tensor fits, the same
     results).  ``rule`` selects the block-scale rule (SCALE_ABSMAX, SCALE_MSE,
-    SCALE_FOUR_OVER_SIX).
+    SCALE_FOUR_OVER_SIX).  ``code_layout``: CODES_TILED writes the codes in
+    8 KB tiles of 128 rows x 128 elements (weights for gemm / gemm_w4a16 as
+    their B operand; rows and cols multiples of 128).
 
     ``check_one_pass`` (with ``one_pass``): synchronise the stream and raise
     FP4Error(FP4_ERR_EXCHANGE) when the single launch's grid-wide wait gave up
@@ -425,7 +436,7 @@ def quantize(x, fmt: int, rotate=False, scale_layout: int = SCALES_ROWMAJOR,
     torch = _torch()
     assert x.dim() == 2 and x.stride(1) == 1
     rows, cols = x.shape
-    cfg = qconfig(fmt, rotate, scale_layout, rule, rounding, block_rows, signs, seed)
+    cfg = qconfig(fmt, rotate, scale_layout, rule, rounding, block_rows, signs, seed, code_layout)
     if out is None:
         codes = torch.empty(max(fp4_codes_bytes(rows, cols), 16), dtype=torch.uint8, device=x.device)
         scales = torch.empty(max(fp4_scales_bytes(cfg, rows, cols), 16), dtype=torch.uint8,
@@ -458,7 +469,7 @@ def quantize_batch(items: list) -> list:
     """Several quantizations in one fp4_quantize_batch call.  items: dicts
     with the arguments of quantize() ("x" and "fmt", optionally "rotate",
     "scale_layout", "global_scale", "rule", "rounding", "block_rows",
-    "signs", "seed", "out").  Returns one Quantized per item, the same as
+    "signs", "seed", "code_layout", "out").  Returns one Quantized per item, the same as
     quantize() would give."""
     torch = _torch()
     outs, jobs = [], []
@@ -470,7 +481,8 @@ def quantize_batch(items: list) -> list:
         rows, cols = x.shape
         cfg = qconfig(fmt, it.get("rotate", False), it.get("scale_layout", SCALES_ROWMAJOR),
                       it.get("rule", SCALE_ABSMAX), it.get("rounding", ROUND_NEAREST),
-                      it.get("block_rows", 1), it.get("signs", 0), it.get("seed", (0, 0)))
+                      it.get("block_rows", 1), it.get("signs", 0), it.get("seed", (0, 0)),
+                      it.get("code_layout", CODES_ROWMAJOR))
         out = it.get("out")
         if out is None:
             codes = torch.empty(max(fp4_codes_bytes(rows, cols), 16), dtype=torch.uint8, device=dev)
@@ -513,6 +525,9 @@ def global_scale(x, rotate=False, out=None, fmt: int = FMT_NVFP4, signs: int = 0
 
 
 def codes_view(q: Quantized):
+    """The codes as [rows, cols/2] bytes (row-major codes only)."""
+    if q.cfg.code_layout != CODES_ROWMAJOR:
+        raise ValueError("codes_view: the codes are tiled")
     return q.codes[: q.rows * q.cols // 2].view(q.rows, q.cols // 2)
 
 
@@ -565,6 +580,8 @@ def gemm_w4a16(a, b: Quantized, out_dtype=None, out=None, workspace=None):
         raise ValueError("gemm_w4a16: K differs (%d, %d)" % (K, b.cols))
     if fmt in MX_FORMATS and b.cfg.scale_layout != SCALES_GEMM:
         raise ValueError("gemm_w4a16: MX weights need FP4_SCALES_GEMM scales")
+    if b.cfg.code_layout == CODES_TILED:
+        fmt |= GEMM_B_TILED
     if out is None:
         out = torch.empty(M, N, dtype=out_dtype or torch.bfloat16, device=a.device)
     _check_out(out, M, N, a.device, "gemm_w4a16")
@@ -587,7 +604,7 @@ def gemm(a: Quantized, b: Quantized, out_dtype=None, out=None, workspace=None):
     fp4_gemm_workspace_bytes() makes the call run without split-K)."""
     torch = _torch()
     check_gemm_operands(a, b)
-    fmt = a.cfg.fmt
+    fmt = a.cfg.fmt | (GEMM_B_TILED if b.cfg.code_layout == CODES_TILED else 0)
     M, N, K = a.rows, b.rows, a.cols
     device = a.codes.device
     if b.codes.device != device:

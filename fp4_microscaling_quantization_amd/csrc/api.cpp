@@ -31,6 +31,10 @@ int check_cfg(const fp4_qconfig* cfg, int64_t rows, int64_t cols) {
   if (cfg->scale_layout != FP4_SCALES_ROWMAJOR && cfg->scale_layout != FP4_SCALES_GEMM)
     return FP4_ERR_INVALID_ARG;
   if (rows < 0 || cols < 0 || cols % G != 0) return FP4_ERR_INVALID_ARG;
+  if (cfg->code_layout != FP4_CODES_ROWMAJOR && cfg->code_layout != FP4_CODES_TILED)
+    return FP4_ERR_INVALID_ARG;
+  if (cfg->code_layout == FP4_CODES_TILED && (rows % 128 != 0 || cols % 128 != 0))
+    return FP4_ERR_INVALID_ARG;
   if (cfg->rotate != 0 && cols % cfg->rotate != 0) return FP4_ERR_INVALID_ARG;
   if (cfg->rounding != FP4_ROUND_NEAREST && cfg->rounding != FP4_ROUND_STOCHASTIC)
     return FP4_ERR_INVALID_ARG;
@@ -75,6 +79,7 @@ fp4k::QParams qparams(const fp4_qconfig* cfg, int64_t cols) {
   if (cfg->rotate == 64) P.any_sign = (P.signs[0] | P.signs[1]) != 0u;
   P.seed0 = cfg->seed[0];
   P.seed1 = cfg->seed[1];
+  P.tiled = cfg->code_layout == FP4_CODES_TILED ? 1u : 0u;
   P.cols = cols;
   return P;
 }
@@ -371,7 +376,17 @@ int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor, i
                                                   static_cast<hipStream_t>(stream)));
 }
 
+// fmt of the GEMM calls: the format, possibly with FP4_GEMM_B_TILED.  Returns
+// the format, -1 for unknown bits; *bt the B layout flag.
+int32_t gemm_fmt(int32_t fmt, int* bt) {
+  *bt = (fmt & FP4_GEMM_B_TILED) != 0 ? 1 : 0;
+  const int32_t f = fmt & ~(int32_t)FP4_GEMM_B_TILED;
+  return (f < FP4_FMT_MXFP4 || f > FP4_FMT_NVINT4) ? -1 : f;
+}
+
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
+  int bt;
+  fmt = gemm_fmt(fmt, &bt);
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return 0;
   if (fmt == FP4_FMT_MXFP4) return fp4lib::gemm_mx_workspace(M, N, K);
   if (fmt == FP4_FMT_NVFP4 || fmt == FP4_FMT_MXINT4 || fmt == FP4_FMT_NVINT4)
@@ -383,8 +398,11 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_code
              const uint8_t* a_scales, const float* a_gs, const uint8_t* b_codes,
              const uint8_t* b_scales, const float* b_gs, void* y, int32_t ydt, int64_t ldy,
              void* ws, size_t ws_bytes, void* stream) {
-  if (fmt < FP4_FMT_MXFP4 || fmt > FP4_FMT_NVINT4) return FP4_ERR_INVALID_ARG;
+  int bt;
+  fmt = gemm_fmt(fmt, &bt);
+  if (fmt < 0) return FP4_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID_ARG;
+  if (bt && N % 128 != 0) return FP4_ERR_INVALID_ARG;
   if (K % 128 != 0) return FP4_ERR_UNSUPPORTED;
   if (fp4k::fmt_int(fmt) && K % 256 != 0) return FP4_ERR_UNSUPPORTED;
   if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
@@ -401,21 +419,23 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_code
   if (ws && !aligned16(ws)) return FP4_ERR_ALIGNMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (fmt == FP4_FMT_MXFP4)
-    return hip_status(fp4lib::launch_gemm_mx(M, N, K, a_codes, a_scales, b_codes, b_scales, y, ydt,
-                                             ldy, ws, ws_bytes, st));
+    return hip_status(fp4lib::launch_gemm_mx(M, N, K, a_codes, a_scales, b_codes, b_scales, bt, y,
+                                             ydt, ldy, ws, ws_bytes, st));
   if (fmt == FP4_FMT_MXINT4)
     return hip_status(fp4lib::launch_gemm_int4(fmt, M, N, K, a_codes, a_scales, nullptr, b_codes,
-                                               b_scales, nullptr, y, ydt, ldy, ws, ws_bytes, st));
+                                               b_scales, nullptr, bt, y, ydt, ldy, ws, ws_bytes, st));
   if (!a_gs || !b_gs) return FP4_ERR_INVALID_ARG;
   if (fmt == FP4_FMT_NVINT4)
     return hip_status(fp4lib::launch_gemm_int4(fmt, M, N, K, a_codes, a_scales, a_gs, b_codes,
-                                               b_scales, b_gs, y, ydt, ldy, ws, ws_bytes, st));
+                                               b_scales, b_gs, bt, y, ydt, ldy, ws, ws_bytes, st));
   return hip_status(fp4lib::launch_gemm_nv(M, N, K, a_codes, a_scales, a_gs, b_codes, b_scales,
-                                           b_gs, y, ydt, ldy, ws, ws_bytes, st));
+                                           b_gs, bt, y, ydt, ldy, ws, ws_bytes, st));
 }
 
 size_t fp4_gemm_w4a16_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
-  if (fmt < FP4_FMT_MXFP4 || fmt > FP4_FMT_NVINT4) return 0;
+  int bt;
+  fmt = gemm_fmt(fmt, &bt);
+  if (fmt < 0) return 0;
   if (M < 0 || N < 0 || K < 0 || K % 256 != 0) return 0;
   return fp4lib::gemm_w4a16_workspace(M, N, K);
 }
@@ -423,8 +443,11 @@ size_t fp4_gemm_w4a16_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t
 int fp4_gemm_w4a16(int32_t fmt, int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
                    const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gs, void* y,
                    int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
-  if (fmt < FP4_FMT_MXFP4 || fmt > FP4_FMT_NVINT4) return FP4_ERR_INVALID_ARG;
+  int bt;
+  fmt = gemm_fmt(fmt, &bt);
+  if (fmt < 0) return FP4_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return FP4_ERR_INVALID_ARG;
+  if (bt && N % 128 != 0) return FP4_ERR_INVALID_ARG;
   if (K % 256 != 0) return FP4_ERR_UNSUPPORTED;
   if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31))
     return FP4_ERR_UNSUPPORTED;
@@ -441,8 +464,8 @@ int fp4_gemm_w4a16(int32_t fmt, int64_t M, int64_t N, int64_t K, const void* a, 
   }
   if (ws && !aligned16(ws)) return FP4_ERR_ALIGNMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return hip_status(fp4lib::launch_gemm_w4a16(fmt, M, N, K, a, lda, b_codes, b_scales, b_gs, y,
-                                              ydt, ldy, ws, ws_bytes, st));
+  return hip_status(fp4lib::launch_gemm_w4a16(fmt, M, N, K, a, lda, b_codes, b_scales, b_gs, bt,
+                                              y, ydt, ldy, ws, ws_bytes, st));
 }
 
 }  // extern "C"

@@ -35,7 +35,7 @@ __device__ __forceinline__ void decode_block(const uint8_t* __restrict__ codes,
   constexpr int NDW = G / 8;
   uint32_t w[NDW];
   if constexpr (fmt_mx(FMT)) {
-    const u32x4 t = *reinterpret_cast<const u32x4*>(codes + (int64_t)r * (nb * 16) + (int64_t)kb * 16);
+    const u32x4 t = *reinterpret_cast<const u32x4*>(codes + code_offset(r, (int64_t)kb * 16, (int64_t)nb * 16, P.tiled != 0));
     w[0] = t[0];
     w[1] = t[1];
     w[2] = t[2];
@@ -59,7 +59,7 @@ __device__ __forceinline__ void decode_block(const uint8_t* __restrict__ codes,
         }
     }
   } else {
-    const u32x2 t = *reinterpret_cast<const u32x2*>(codes + (int64_t)r * (nb * 8) + (int64_t)kb * 8);
+    const u32x2 t = *reinterpret_cast<const u32x2*>(codes + code_offset(r, (int64_t)kb * 8, (int64_t)nb * 8, P.tiled != 0));
     w[0] = t[0];
     w[1] = t[1];
     const float e4 = e4m3_value(scales[(int64_t)r * nb + kb]);

@@ -207,7 +207,7 @@ struct QParams {
   uint32_t signs[4];
   uint32_t any_sign;  // nonzero when some sign bit is set
   uint32_t seed0, seed1;
-  uint32_t pad;
+  uint32_t tiled;     // nonzero: codes in the tiled layout (code_offset)
   int64_t cols;       // row length, for the element index of stochastic rounding
 };
 
@@ -354,6 +354,18 @@ __host__ __device__ __forceinline__ int64_t mx_gemm_scale_offset(int64_t r, int6
 
 __host__ __device__ __forceinline__ int64_t mx_gemm_kchunks(int64_t cols) {
   return (cols + 255) / 256;
+}
+
+// Byte b of row r of a packed-code matrix with row_bytes bytes per row.
+// Row-major: r * row_bytes + b.  Tiled (rows and row_bytes multiples of 128
+// and 64): 8 KB tiles of 128 rows x 64 bytes (128 elements), row-major inside
+// the tile; the tiles of one 128-row panel follow each other along the row,
+// and the panels follow each other.  A GEMM stage of 128 rows x 128 K of the
+// weights is then one contiguous 8 KB block.
+__host__ __device__ __forceinline__ int64_t code_offset(int64_t r, int64_t b, int64_t row_bytes,
+                                                        bool tiled) {
+  return tiled ? ((((r >> 7) * (row_bytes >> 6) + (b >> 6)) << 13) + ((r & 127) << 6) + (b & 63))
+               : r * row_bytes + b;
 }
 
 }  // namespace fp4k

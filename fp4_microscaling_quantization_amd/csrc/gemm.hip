@@ -172,7 +172,7 @@ template <int BM, int BN, int WM, int WN, int NS, int YDT, bool PARTIAL>
 __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, void* __restrict__ Y, int64_t ldy, int M, int N, int K,
-    int kchunks, int tiles_n, int kt_per_split, float* __restrict__ part) {
+    int kchunks, int tiles_n, int kt_per_split, float* __restrict__ part, int bt) {
   using C = MxCfg<BM, BN, WM, WN, NS>;
   constexpr int TM = C::TM, TN = C::TN, ROUNDS = C::ROUNDS;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
@@ -187,31 +187,34 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
   const int kt0 = PARTIAL ? blockIdx.y * kt_per_split : 0;
   const int kt1 = PARTIAL ? min(KT_total, kt0 + kt_per_split) : KT_total;
 
-  // DMA sources of this thread, one per round: slot byte p = r*RB + tid*16.
+  // DMA sources of this thread, one per round: slot byte p = r*RB + tid*16,
+  // and the bytes a stage advances them (0: a scale round, which advances one
+  // 256-byte tile every two stages).  Tiled B codes (bt): a stage is the next
+  // 8 KB tile of the row panel.
   const uint8_t* src[ROUNDS];
-  bool code_src[ROUNDS];
+  uint32_t cadv[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int p = r * C::RB + tid * 16;
     if (p < C::B_CODES) {
       const int row = p >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
       src[r] = A + (int64_t)min(m0 + row, M - 1) * rowbytes + chunk * 16;
-      code_src[r] = true;
+      cadv[r] = 64;
     } else if (p < C::A_SC) {
       const int row = (p - C::B_CODES) >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
-      src[r] = B + (int64_t)min(n0 + row, N - 1) * rowbytes + chunk * 16;
-      code_src[r] = true;
+      src[r] = B + code_offset(min(n0 + row, N - 1), chunk * 16, rowbytes, bt != 0);
+      cadv[r] = bt ? 8192 : 64;
     } else if (p < C::B_SC) {
       const int t = (p - C::A_SC) >> 8;
       src[r] = As + (int64_t)min((m0 >> 5) + t, (M - 1) >> 5) * kchunks * 256 + (p & 255);
-      code_src[r] = false;
+      cadv[r] = 0;
     } else if (p < C::USED) {
       const int t = (p - C::B_SC) >> 8;
       src[r] = Bs + (int64_t)min((n0 >> 5) + t, (N - 1) >> 5) * kchunks * 256 + (p & 255);
-      code_src[r] = false;
+      cadv[r] = 0;
     } else {  // slot padding: any valid address
       src[r] = As + (p & 255);
-      code_src[r] = false;
+      cadv[r] = 0;
     }
   }
   auto slot_of = [&](int kt) __attribute__((always_inline)) {
@@ -226,7 +229,7 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
     uint8_t* slot = slot_of(kt);
 #pragma unroll
     for (int r = 0; r < H; ++r)
-      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * C::RB + wave * 1024);
+      dma16(src[r] + (cadv[r] ? (int64_t)ks * cadv[r] : (int64_t)(ks >> 1) * 256), slot + r * C::RB + wave * 1024);
   };
   // SHORT: this wave's part of the last round is slot padding, not loaded;
   // skip_last: an odd stage's scale round (SC_ROUND), not loaded either.
@@ -237,7 +240,7 @@ __global__ __launch_bounds__((MxCfg<BM, BN, WM, WN, NS>::NW * 64)) void gemm_mx_
 #pragma unroll
     for (int r = H; r < RE; ++r) {
       if (r == ROUNDS - 1 && skip_last) continue;
-      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * 256), slot + r * C::RB + wave * 1024);
+      dma16(src[r] + (cadv[r] ? (int64_t)ks * cadv[r] : (int64_t)(ks >> 1) * 256), slot + r * C::RB + wave * 1024);
     }
   };
 
@@ -425,7 +428,7 @@ template <int BM, int BN, int WM, int WN, int YDT, bool PARTIAL>
 __global__ __launch_bounds__((Mx2Cfg<BM, BN, WM, WN>::NW * 64)) void gemm_mx2_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, void* __restrict__ Y, int64_t ldy, int M, int N, int K,
-    int kchunks, int tiles_n, int ks_per_split, float* __restrict__ part, int vec_out) {
+    int kchunks, int tiles_n, int ks_per_split, float* __restrict__ part, int vec_out, int bt) {
   using C = Mx2Cfg<BM, BN, WM, WN>;
   constexpr int TM = C::TM, TN = C::TN, ROUNDS = C::ROUNDS;
   constexpr int CR = C::A_SC / C::RB;  // rounds of codes (A, then B)
@@ -443,16 +446,19 @@ __global__ __launch_bounds__((Mx2Cfg<BM, BN, WM, WN>::NW * 64)) void gemm_mx2_ke
   const int ks1 = PARTIAL ? min(KS_total, ks0 + ks_per_split) : KS_total;
 
   // DMA sources: 32-bit offsets from A or B for the code rounds (a stage
-  // advances them by 128 bytes), full pointers for the scale rounds (a stage
-  // advances them by one 256-byte tile).
+  // advances them by 128 bytes, or by two 8 KB tiles for tiled B codes), full
+  // pointers for the scale rounds (a stage advances them by one 256-byte tile).
+  static_assert(C::B_CODES % C::RB == 0, "a code round is all A or all B");
   uint32_t coff[CR];
 #pragma unroll
   for (int r = 0; r < CR; ++r) {
     const int p = r * C::RB + tid * 16;
     const bool isa = p < C::B_CODES;
     const int row = (isa ? p : p - C::B_CODES) >> 7, chunk = ((p >> 4) & 7) ^ swz32(row);
-    coff[r] = (uint32_t)min((isa ? m0 : n0) + row, (isa ? M : N) - 1) * rowbytes + chunk * 16;
+    const int64_t grow = min((isa ? m0 : n0) + row, (isa ? M : N) - 1);
+    coff[r] = (uint32_t)code_offset(grow, chunk * 16, rowbytes, !isa && bt != 0);
   }
+  const uint32_t badv = bt ? 16384u : 128u;
   const uint8_t* ssrc[ROUNDS - CR];
 #pragma unroll
   for (int r = CR; r < ROUNDS; ++r) {
@@ -476,7 +482,9 @@ __global__ __launch_bounds__((Mx2Cfg<BM, BN, WM, WN>::NW * 64)) void gemm_mx2_ke
     for (int r = r0; r < r1; ++r) {
       if (!FULL && r == ROUNDS - 1) continue;
       if (r < CR)
-        dma16((r * C::RB < C::B_CODES ? A : B) + (coff[r] + (uint32_t)ks * 128u), slot + r * C::RB);
+        dma16((r * C::RB < C::B_CODES ? A : B) +
+                  (coff[r] + (uint32_t)ks * (r * C::RB < C::B_CODES ? 128u : badv)),
+              slot + r * C::RB);
       else
         dma16(ssrc[r - CR] + ks * 256, slot + r * C::RB);
     }
@@ -759,7 +767,7 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ ags,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ bgs,
     void* __restrict__ Y, int64_t ldy, int M, int N, int K, int tiles_n, int kt_per_split,
-    float* __restrict__ part) {
+    float* __restrict__ part, int bt) {
   using C = NvCfg<BM, BN, WM, WN, NS, FMT, KG>;
   constexpr int TM = C::TM, TN = C::TN, ROUNDS = C::ROUNDS;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
@@ -776,36 +784,37 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
   const int kt0 = PARTIAL ? blockIdx.y * kt_per_split : 0;
   const int kt1 = PARTIAL ? min(KT_total, kt0 + kt_per_split) : KT_total;
 
+  // DMA sources and per-stage advances as in gemm_mx_kernel (cadv 0: scales).
   const uint8_t* src[ROUNDS];
-  bool code_src[ROUNDS];
+  uint32_t cadv[ROUNDS];
 #pragma unroll
   for (int r = 0; r < ROUNDS; ++r) {
     const int p = r * C::RB + tid * 16;
     if (p < C::B_CODES) {
       const int row = p >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
       src[r] = A + (int64_t)min(m0 + row, M - 1) * rowbytes + chunk * 16;
-      code_src[r] = true;
+      cadv[r] = 64;
     } else if (p < C::A_SC) {
       const int row = (p - C::B_CODES) >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
-      src[r] = B + (int64_t)min(n0 + row, N - 1) * rowbytes + chunk * 16;
-      code_src[r] = true;
+      src[r] = B + code_offset(min(n0 + row, N - 1), chunk * 16, rowbytes, bt != 0);
+      cadv[r] = bt ? 8192 : 64;
     } else if (p < C::B_SC) {
       const int q = p - C::A_SC;
       if constexpr (C::MX)
         src[r] = As + (int64_t)min((m0 >> 5) + (q >> 8), (M - 1) >> 5) * kchunks * 256 + (q & 255);
       else
         src[r] = As + (int64_t)min(m0 + (q >> 4), M - 1) * srow;
-      code_src[r] = false;
+      cadv[r] = 0;
     } else if (p < C::USED) {
       const int q = p - C::B_SC;
       if constexpr (C::MX)
         src[r] = Bs + (int64_t)min((n0 >> 5) + (q >> 8), (N - 1) >> 5) * kchunks * 256 + (q & 255);
       else
         src[r] = Bs + (int64_t)min(n0 + (q >> 4), N - 1) * srow;
-      code_src[r] = false;
+      cadv[r] = 0;
     } else {
       src[r] = As;
-      code_src[r] = false;
+      cadv[r] = 0;
     }
   }
   auto slot_of = [&](int kt) __attribute__((always_inline)) {
@@ -817,14 +826,14 @@ __global__ __launch_bounds__((NvCfg<BM, BN, WM, WN, NS, FMT, KG>::NW * 64)) void
     uint8_t* slot = slot_of(kt);
 #pragma unroll
     for (int r = 0; r < H; ++r)
-      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * C::SC_ADV), slot + r * C::RB + wave * 1024);
+      dma16(src[r] + (cadv[r] ? (int64_t)ks * cadv[r] : (int64_t)(ks >> 1) * C::SC_ADV), slot + r * C::RB + wave * 1024);
   };
   auto dma_tail = [&](int kt) __attribute__((always_inline)) {
     const int ks = min(kt, kt1 - 1);
     uint8_t* slot = slot_of(kt);
 #pragma unroll
     for (int r = H; r < ROUNDS; ++r)
-      dma16(src[r] + (code_src[r] ? ks * 64 : (ks >> 1) * C::SC_ADV), slot + r * C::RB + wave * 1024);
+      dma16(src[r] + (cadv[r] ? (int64_t)ks * cadv[r] : (int64_t)(ks >> 1) * C::SC_ADV), slot + r * C::RB + wave * 1024);
   };
 
   f32x16 acc[TM][TN];
@@ -1148,7 +1157,7 @@ __global__ __launch_bounds__(512) void gemm_w4a16_kernel(
     const uint8_t* __restrict__ A, int64_t lda_bytes, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, const float* __restrict__ bgs, void* __restrict__ Y,
     int64_t ldy, int M, int N, int K, int kchunks, int tiles_n, int kt_per_split,
-    float* __restrict__ part) {
+    float* __restrict__ part, int bt) {
   using C = W4Cfg<FMT, BM, NS, WMS>;
   constexpr int TM = C::TM, TN = C::TN, BN = C::BN, ROUNDS = C::ROUNDS;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
@@ -1176,7 +1185,7 @@ __global__ __launch_bounds__(512) void gemm_w4a16_kernel(
       src[r] = A + (int64_t)min(m0 + row, M - 1) * lda_bytes + chunk * 16;
     } else if (r * C::RB < C::B_SC) {
       const int row = (p - C::B_CODES) >> 6, chunk = ((p >> 4) & 3) ^ swz4(row);
-      src[r] = B + (int64_t)min(n0 + row, N - 1) * rowbytes + chunk * 16;
+      src[r] = B + code_offset(min(n0 + row, N - 1), chunk * 16, rowbytes, bt != 0);
     } else if (p < C::USED) {
       const int q = p - C::B_SC;
       if constexpr (fmt_mx(FMT))
@@ -1191,10 +1200,11 @@ __global__ __launch_bounds__(512) void gemm_w4a16_kernel(
     return dyn_lds + (kt % NS) * C::STAGE;
   };
   constexpr int H = ROUNDS / 2;
+  const int64_t badv = bt ? 8192 : 64;  // tiled B codes: the next 8 KB tile
   auto dma = [&](int kt, int r) __attribute__((always_inline)) {
     const int ks = min(kt, kt1 - 1);
     const int64_t adv = r * C::RB < C::B_CODES ? (int64_t)ks * 256
-                        : r * C::RB < C::B_SC  ? (int64_t)ks * 64
+                        : r * C::RB < C::B_SC  ? (int64_t)ks * badv
                                                : (int64_t)(ks >> 1) * C::SC_ADV;
     dma16(src[r] + adv, slot_of(kt) + r * C::RB + wave * 1024);
   };
@@ -1370,7 +1380,7 @@ hipError_t mx_lds_attr() {
 
 template <int BM, int BN, int WM, int WN, int NS>
 hipError_t launch_mx_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
-                         const uint8_t* b, const uint8_t* bs, void* y, int ydt, int64_t ldy,
+                         const uint8_t* b, const uint8_t* bs, int bt, void* y, int ydt, int64_t ldy,
                          int splits, int kt_per, float* part, hipStream_t st) {
   const int tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(((M + BM - 1) / BM) * tiles_n), (unsigned)splits);
@@ -1380,15 +1390,15 @@ hipError_t launch_mx_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, cons
   if (splits > 1) {
     if ((e = mx_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, true>()) != hipSuccess) return e;
     gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, true><<<grid, (MxCfg<BM, BN, WM, WN, NS>::NW * 64), lds, st>>>(
-        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part, bt);
   } else if (ydt == FP4_DT_F32) {
     if ((e = mx_lds_attr<BM, BN, WM, WN, NS, FP4_DT_F32, false>()) != hipSuccess) return e;
     gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_F32, false><<<grid, (MxCfg<BM, BN, WM, WN, NS>::NW * 64), lds, st>>>(
-        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part, bt);
   } else {
     if ((e = mx_lds_attr<BM, BN, WM, WN, NS, FP4_DT_BF16, false>()) != hipSuccess) return e;
     gemm_mx_kernel<BM, BN, WM, WN, NS, FP4_DT_BF16, false><<<grid, (MxCfg<BM, BN, WM, WN, NS>::NW * 64), lds, st>>>(
-        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part, bt);
   }
   return hipGetLastError();
 }
@@ -1403,7 +1413,7 @@ hipError_t mx2_lds_attr() {
 
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_mx2_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
-                          const uint8_t* b, const uint8_t* bs, void* y, int ydt, int64_t ldy,
+                          const uint8_t* b, const uint8_t* bs, int bt, void* y, int ydt, int64_t ldy,
                           int splits, int ks_per, float* part, hipStream_t st) {
   using C = Mx2Cfg<BM, BN, WM, WN>;
   const int tiles_n = (int)((N + BN - 1) / BN);
@@ -1413,16 +1423,16 @@ hipError_t launch_mx2_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   if (splits > 1) {
     if ((e = mx2_lds_attr<BM, BN, WM, WN, FP4_DT_F32, true>()) != hipSuccess) return e;
     gemm_mx2_kernel<BM, BN, WM, WN, FP4_DT_F32, true><<<grid, C::NW * 64, C::LDS, st>>>(
-        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, ks_per, part, 0);
+        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, ks_per, part, 0, bt);
   } else if (ydt == FP4_DT_F32) {
     if ((e = mx2_lds_attr<BM, BN, WM, WN, FP4_DT_F32, false>()) != hipSuccess) return e;
     gemm_mx2_kernel<BM, BN, WM, WN, FP4_DT_F32, false><<<grid, C::NW * 64, C::LDS, st>>>(
-        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, ks_per, part, 0);
+        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, ks_per, part, 0, bt);
   } else {
     if ((e = mx2_lds_attr<BM, BN, WM, WN, FP4_DT_BF16, false>()) != hipSuccess) return e;
     const int vec_out = (ldy % 8 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15u) == 0);
     gemm_mx2_kernel<BM, BN, WM, WN, FP4_DT_BF16, false><<<grid, C::NW * 64, C::LDS, st>>>(
-        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, ks_per, part, vec_out);
+        a, as, b, bs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, ks_per, part, vec_out, bt);
   }
   return hipGetLastError();
 }
@@ -1438,7 +1448,7 @@ hipError_t nv_lds_attr() {
 template <int BM, int BN, int WM, int WN, int NS, int FMT = FP4_FMT_NVFP4, int KG = 1>
 hipError_t launch_nv_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                          const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
-                         void* y, int ydt, int64_t ldy, int splits, int kt_per, float* part,
+                         int bt, void* y, int ydt, int64_t ldy, int splits, int kt_per, float* part,
                          hipStream_t st) {
   using C = NvCfg<BM, BN, WM, WN, NS, FMT, KG>;
   const int tiles_n = (int)((N + BN - 1) / BN);
@@ -1447,15 +1457,15 @@ hipError_t launch_nv_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, cons
   if (splits > 1) {
     if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, true, KG>()) != hipSuccess) return e;
     gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, true, KG><<<grid, C::NW * 64, C::LDS, st>>>(
-        a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
+        a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part, bt);
   } else if (ydt == FP4_DT_F32) {
     if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, false, KG>()) != hipSuccess) return e;
     gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_F32, false, KG><<<grid, C::NW * 64, C::LDS, st>>>(
-        a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
+        a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part, bt);
   } else {
     if ((e = nv_lds_attr<FMT, BM, BN, WM, WN, NS, FP4_DT_BF16, false, KG>()) != hipSuccess) return e;
     gemm_nv_ring_kernel<FMT, BM, BN, WM, WN, NS, FP4_DT_BF16, false, KG><<<grid, C::NW * 64, C::LDS, st>>>(
-        a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part);
+        a, as, ags, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, tiles_n, kt_per, part, bt);
   }
   return hipGetLastError();
 }
@@ -1470,7 +1480,7 @@ hipError_t w4_lds_attr() {
 
 template <int FMT, int BM, int NS, int WMS>
 hipError_t launch_w4_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda_bytes,
-                         const uint8_t* b, const uint8_t* bs, const float* bgs, void* y, int ydt,
+                         const uint8_t* b, const uint8_t* bs, const float* bgs, int bt, void* y, int ydt,
                          int64_t ldy, int splits, int kt_per, float* part, hipStream_t st) {
   using C = W4Cfg<FMT, BM, NS, WMS>;
   const int tiles_n = (int)((N + C::BN - 1) / C::BN);
@@ -1480,15 +1490,15 @@ hipError_t launch_w4_cfg(int64_t M, int64_t N, int64_t K, const uint8_t* a, int6
   if (splits > 1) {
     if ((e = w4_lds_attr<FMT, BM, NS, WMS, FP4_DT_F32, true>()) != hipSuccess) return e;
     gemm_w4a16_kernel<FMT, BM, NS, WMS, FP4_DT_F32, true><<<grid, C::NW * 64, C::LDS, st>>>(
-        a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+        a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part, bt);
   } else if (ydt == FP4_DT_F32) {
     if ((e = w4_lds_attr<FMT, BM, NS, WMS, FP4_DT_F32, false>()) != hipSuccess) return e;
     gemm_w4a16_kernel<FMT, BM, NS, WMS, FP4_DT_F32, false><<<grid, C::NW * 64, C::LDS, st>>>(
-        a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+        a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part, bt);
   } else {
     if ((e = w4_lds_attr<FMT, BM, NS, WMS, FP4_DT_BF16, false>()) != hipSuccess) return e;
     gemm_w4a16_kernel<FMT, BM, NS, WMS, FP4_DT_BF16, false><<<grid, C::NW * 64, C::LDS, st>>>(
-        a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part);
+        a, lda_bytes, b, bs, bgs, y, ldy, (int)M, (int)N, (int)K, kchunks, tiles_n, kt_per, part, bt);
   }
   return hipGetLastError();
 }
@@ -1513,16 +1523,16 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K) {
 
 template <int FMT>
 hipError_t launch_w4_fmt(int bm, int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda_bytes,
-                         const uint8_t* b, const uint8_t* bs, const float* bgs, void* y, int ydt,
+                         const uint8_t* b, const uint8_t* bs, const float* bgs, int bt, void* y, int ydt,
                          int64_t ldy, int splits, int kt_per, float* part, hipStream_t st) {
   // MXFP4 expands cheaply: split the rows over two waves to halve the
   // activation reads; the other formats expand each weight fragment once.
   constexpr int WMS = FMT == FP4_FMT_MXFP4 ? 2 : 1;
   if (bm == 32)
-    return launch_w4_cfg<FMT, 32, 6, 1>(M, N, K, a, lda_bytes, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    return launch_w4_cfg<FMT, 32, 6, 1>(M, N, K, a, lda_bytes, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
   if (bm == 64)
-    return launch_w4_cfg<FMT, 64, 4, WMS>(M, N, K, a, lda_bytes, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
-  return launch_w4_cfg<FMT, 128, 3, WMS>(M, N, K, a, lda_bytes, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    return launch_w4_cfg<FMT, 64, 4, WMS>(M, N, K, a, lda_bytes, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
+  return launch_w4_cfg<FMT, 128, 3, WMS>(M, N, K, a, lda_bytes, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
 }
 
 // Y = 0 (a product over an empty K range).
@@ -1578,7 +1588,7 @@ template <int YDT>
 __global__ __launch_bounds__(kThreads) void gemm_nv_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ ags,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ bgs,
-    void* __restrict__ Y, int64_t ldy, int M, int N, int K, int tiles_n) {
+    void* __restrict__ Y, int64_t ldy, int M, int N, int K, int tiles_n, int bt) {
   constexpr int BM = 128, BN = 128, WM = 64, WN = 64, TM = WM / 16, TN = WN / 16;
   constexpr int ROWB = 128;  // bytes per LDS row: 64 fp16
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][(BM + BN) * ROWB];
@@ -1598,7 +1608,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nv_kernel(
   uint32_t sca, scb;
   auto gload = [&](int kt) __attribute__((always_inline)) {
     ra = *reinterpret_cast<const u32x4*>(A + (int64_t)a_row * rowbytes + kt * 32 + c_half * 16);
-    rb = *reinterpret_cast<const u32x4*>(B + (int64_t)b_row * rowbytes + kt * 32 + c_half * 16);
+    rb = *reinterpret_cast<const u32x4*>(B + code_offset(b_row, (int64_t)kt * 32 + c_half * 16, rowbytes, bt != 0));
     sca = *reinterpret_cast<const uint16_t*>(As + (int64_t)a_row * srow + kt * 4 + c_half * 2);
     scb = *reinterpret_cast<const uint16_t*>(Bs + (int64_t)b_row * srow + kt * 4 + c_half * 2);
   };
@@ -1725,7 +1735,7 @@ size_t gemm_mx_workspace(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
-                          const uint8_t* b, const uint8_t* bs, void* y, int ydt, int64_t ldy,
+                          const uint8_t* b, const uint8_t* bs, int bt, void* y, int ydt, int64_t ldy,
                           void* ws, size_t ws_bytes, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (K == 0) {  // empty sum
@@ -1741,14 +1751,15 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   // 256 x 256 tiles: K-stages of 256 (whole 128-byte lines per row and DMA,
   // measured 2-13 % faster on the Llama shapes than the 128-K ring) when K
   // allows them
-  if (p.cfg == 0 && K % 256 == 0 && splits == 1)
-    e = launch_mx2_cfg<256, 256, 128, 64>(M, N, K, a, as, b, bs, y, ydt, ldy, 1, (int)(K / 256), part, st);
+  // (its DMA offsets are 32-bit: operands under 4 GB)
+  if (p.cfg == 0 && K % 256 == 0 && splits == 1 && (uint64_t)max(M, N) * (uint64_t)(K / 2) < (1ull << 32))
+    e = launch_mx2_cfg<256, 256, 128, 64>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, 1, (int)(K / 256), part, st);
   else if (p.cfg == 0)
-    e = launch_mx_cfg<256, 256, 128, 64, 4>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_mx_cfg<256, 256, 128, 64, 4>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, splits, kt_per, part, st);
   else if (p.cfg == 1)
-    e = launch_mx_cfg<128, 128, 64, 64, 4>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_mx_cfg<128, 128, 64, 64, 4>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, splits, kt_per, part, st);
   else
-    e = launch_mx_cfg<32, 128, 32, 32, 6>(M, N, K, a, as, b, bs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_mx_cfg<32, 128, 32, 32, 6>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, nullptr, nullptr, st);
 }
@@ -1773,7 +1784,7 @@ size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K) {
 template <int FMT>
 hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                             const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
-                            void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                            int bt, void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
                             hipStream_t st) {
   MxPlan p = plan_nv(M, N, K);
   const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_nv_workspace(M, N, K);
@@ -1782,13 +1793,13 @@ hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, c
   float* part = static_cast<float*>(ws);
   hipError_t e;
   if (p.cfg == 0)
-    e = launch_nv_cfg<256, 256, 128, 128, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_nv_cfg<256, 256, 128, 128, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
   else if (p.cfg == 1 && M <= 128)
-    e = launch_nv_cfg<128, 128, 128, 32, 4, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_nv_cfg<128, 128, 128, 32, 4, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
   else if (p.cfg == 1)
-    e = launch_nv_cfg<128, 128, 64, 64, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_nv_cfg<128, 128, 64, 64, 3, FMT>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
   else
-    e = launch_nv_cfg<32, 256, 32, 64, 4, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_nv_cfg<32, 256, 32, 64, 4, FMT, 2>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, fmt_mx(FMT) ? nullptr : ags,
                               fmt_mx(FMT) ? nullptr : bgs, st);
@@ -1796,7 +1807,7 @@ hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, c
 
 hipError_t launch_gemm_int4(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a,
                             const uint8_t* as, const float* ags, const uint8_t* b, const uint8_t* bs,
-                            const float* bgs, void* y, int ydt, int64_t ldy, void* ws,
+                            const float* bgs, int bt, void* y, int ydt, int64_t ldy, void* ws,
                             size_t ws_bytes, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (K == 0) {
@@ -1804,13 +1815,14 @@ hipError_t launch_gemm_int4(int fmt, int64_t M, int64_t N, int64_t K, const uint
     return hipGetLastError();
   }
   if (fmt == FP4_FMT_MXINT4)
-    return launch_ring_int4<FP4_FMT_MXINT4>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, ws, ws_bytes, st);
-  return launch_ring_int4<FP4_FMT_NVINT4>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, ws, ws_bytes, st);
+    return launch_ring_int4<FP4_FMT_MXINT4>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, ws, ws_bytes, st);
+  return launch_ring_int4<FP4_FMT_NVINT4>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, ws, ws_bytes, st);
 }
 
 hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                           const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
-                          void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t st) {
+                          int bt, void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                          hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (K % 256 == 0 && K > 0) {
     // LDS ring with in-register fp16 expansion; tiles and split-K as for MXFP4
@@ -1821,13 +1833,13 @@ hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
     float* part = static_cast<float*>(ws);
     hipError_t e;
     if (p.cfg == 0)  // eight waves of 128x64 (two per SIMD): 4096^3 133 -> 126 us, 70B shapes level
-      e = launch_nv_cfg<256, 256, 128, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+      e = launch_nv_cfg<256, 256, 128, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
     else if (p.cfg == 1 && M <= 128)
-      e = launch_nv_cfg<128, 128, 64, 64, 3, FP4_FMT_NVFP4, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+      e = launch_nv_cfg<128, 128, 64, 64, 3, FP4_FMT_NVFP4, 2>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
     else if (p.cfg == 1)
-      e = launch_nv_cfg<128, 128, 64, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+      e = launch_nv_cfg<128, 128, 64, 64, 3>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
     else  // M <= 32: two K-step groups of four waves (two waves per SIMD)
-      e = launch_nv_cfg<32, 256, 32, 64, 4, FP4_FMT_NVFP4, 2>(M, N, K, a, as, ags, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+      e = launch_nv_cfg<32, 256, 32, 64, 4, FP4_FMT_NVFP4, 2>(M, N, K, a, as, ags, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
     if (e != hipSuccess || !split) return e;
     return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy, ags, bgs, st);
   }
@@ -1835,10 +1847,10 @@ hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   const unsigned grid = (unsigned)(((M + 127) / 128) * tiles_n);
   if (ydt == FP4_DT_F32)
     gemm_nv_kernel<FP4_DT_F32><<<grid, kThreads, 0, st>>>(a, as, ags, b, bs, bgs, y, ldy, (int)M,
-                                                          (int)N, (int)K, tiles_n);
+                                                          (int)N, (int)K, tiles_n, bt);
   else
     gemm_nv_kernel<FP4_DT_BF16><<<grid, kThreads, 0, st>>>(a, as, ags, b, bs, bgs, y, ldy, (int)M,
-                                                           (int)N, (int)K, tiles_n);
+                                                           (int)N, (int)K, tiles_n, bt);
   return hipGetLastError();
 }
 
@@ -1849,8 +1861,8 @@ size_t gemm_w4a16_workspace(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_w4a16(int fmt, int64_t M, int64_t N, int64_t K, const void* a, int64_t lda,
-                             const uint8_t* b, const uint8_t* bs, const float* bgs, void* y, int ydt,
-                             int64_t ldy, void* ws, size_t ws_bytes, hipStream_t st) {
+                             const uint8_t* b, const uint8_t* bs, const float* bgs, int bt, void* y,
+                             int ydt, int64_t ldy, void* ws, size_t ws_bytes, hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
   if (K == 0) {
     zero_out_kernel<<<256, kThreads, 0, st>>>(y, ydt, (int)M, (int)N, ldy);
@@ -1864,13 +1876,13 @@ hipError_t launch_gemm_w4a16(int fmt, int64_t M, int64_t N, int64_t K, const voi
   const uint8_t* ab = static_cast<const uint8_t*>(a);
   hipError_t e;
   if (fmt == FP4_FMT_MXFP4)
-    e = launch_w4_fmt<FP4_FMT_MXFP4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_w4_fmt<FP4_FMT_MXFP4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
   else if (fmt == FP4_FMT_NVFP4)
-    e = launch_w4_fmt<FP4_FMT_NVFP4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_w4_fmt<FP4_FMT_NVFP4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
   else if (fmt == FP4_FMT_MXINT4)
-    e = launch_w4_fmt<FP4_FMT_MXINT4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_w4_fmt<FP4_FMT_MXINT4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
   else
-    e = launch_w4_fmt<FP4_FMT_NVINT4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, y, ydt, ldy, splits, kt_per, part, st);
+    e = launch_w4_fmt<FP4_FMT_NVINT4>(p.bm, M, N, K, ab, lda * 2, b, bs, bgs, bt, y, ydt, ldy, splits, kt_per, part, st);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(part, splits, M, N, y, ydt, ldy,
                               fmt_mx(fmt) ? nullptr : bgs, nullptr, st);

@@ -537,12 +537,12 @@ template <int FMT>
 __device__ __forceinline__ void store_block(const u32x4& out, uint32_t code, int64_t r, int64_t kb,
                                             int64_t nb, uint8_t* __restrict__ codes,
                                             uint8_t* __restrict__ scales, int64_t kchunks,
-                                            int gemm_layout) {
+                                            int gemm_layout, uint32_t tiled) {
   if constexpr (fmt_mx(FMT)) {
-    *reinterpret_cast<u32x4*>(codes + r * (nb * 16) + kb * 16) = out;
+    *reinterpret_cast<u32x4*>(codes + code_offset(r, kb * 16, nb * 16, tiled != 0)) = out;
     store_mx_scale(scales, r, kb, nb, kchunks, gemm_layout, code);
   } else {
-    *reinterpret_cast<u32x2*>(codes + r * (nb * 8) + kb * 8) = u32x2{out[0], out[1]};
+    *reinterpret_cast<u32x2*>(codes + code_offset(r, kb * 8, nb * 8, tiled != 0)) = u32x2{out[0], out[1]};
     scales[r * nb + kb] = (uint8_t)code;
   }
 }
@@ -554,7 +554,7 @@ __device__ __forceinline__ void quantize_block(const u32x4* c, const NvTs& T, in
                                                int gemm_layout, const QParams& P) {
   u32x4 out;
   const uint32_t code = compute_block<FMT, XDT, ROT, RULE, RND>(c, T, out, (uint32_t)r, (uint32_t)kb, P);
-  store_block<FMT>(out, code, r, kb, nb, codes, scales, kchunks, gemm_layout);
+  store_block<FMT>(out, code, r, kb, nb, codes, scales, kchunks, gemm_layout, P.tiled);
 }
 
 // Max of a workgroup (all threads must call); valid in every thread.
@@ -779,7 +779,7 @@ __device__ __forceinline__ void quant_rows_body(
       const uint32_t r = tile / wpr, w = tile - r * wpr;
       const uint32_t kb = w * 64 + lane;
       if (tile < tiles && kb < nb)
-        store_block<FMT>(out[u], code[u], r, kb, nb, codes, scales, kchunks, gemm_layout);
+        store_block<FMT>(out[u], code[u], r, kb, nb, codes, scales, kchunks, gemm_layout, P.tiled);
     }
     t0 += step;
     if (t0 >= tiles) break;
@@ -978,7 +978,7 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
         const uint32_t r = tile / wpr, w = tile - r * wpr;
         const uint32_t kb = w * 64 + lane;
         if (tile < tiles && kb < nb)
-          store_block<FMT>(u32x4{fo[u][0], fo[u][1], 0u, 0u}, fc[u], r, kb, nb, codes, scales, 0, 0);
+          store_block<FMT>(u32x4{fo[u][0], fo[u][1], 0u, 0u}, fc[u], r, kb, nb, codes, scales, 0, 0, P.tiled);
       }
       return;
     }
@@ -1001,7 +1001,7 @@ __global__ __launch_bounds__(kFusedThreads) void quant_nv_fused_kernel(
     } else {
       code = compute_block<FMT, FP4_DT_BF16, ROT, RULE, RND>(c[u], T, out, r, kb, P);
     }
-    if (kb < nb) store_block<FMT>(out, code, r, kb, nb, codes, scales, 0, 0);
+    if (kb < nb) store_block<FMT>(out, code, r, kb, nb, codes, scales, 0, 0, P.tiled);
   }
 }
 
@@ -1493,7 +1493,7 @@ __global__ __launch_bounds__(kThreads) void quant_nv2d_kernel(
       } else {
         o = u32x2{nv_enc8(&v[0], s), nv_enc8(&v[8], s)};
       }
-      *reinterpret_cast<u32x2*>(codes + (int64_t)r * (nb * 8) + (int64_t)kb * 8) = o;
+      *reinterpret_cast<u32x2*>(codes + code_offset(r, (int64_t)kb * 8, (int64_t)nb * 8, P.tiled != 0)) = o;
       scales[(int64_t)r * nb + kb] = (uint8_t)code;
     }
   }

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP4_ABI_VERSION 4
+#define FP4_ABI_VERSION 5
 
 typedef enum {
     FP4_OK = 0,
@@ -84,6 +84,21 @@ typedef enum {
 } fp4_scale_rule;
 typedef enum { FP4_DT_F32 = 0, FP4_DT_BF16 = 1 } fp4_dtype;
 typedef enum { FP4_SCALES_ROWMAJOR = 0, FP4_SCALES_GEMM = 1 } fp4_scale_layout;
+/* Layout of the packed codes (the same bytes, placed differently).  No page
+ * fixes a storage order for the codes; the tiled one is this library's, for
+ * weights that the GEMM streams from HBM.
+ *   FP4_CODES_ROWMAJOR: byte b of row r (elements 2b, 2b + 1) at
+ *     r * (cols / 2) + b.
+ *   FP4_CODES_TILED: 8 KB tiles of 128 rows x 64 bytes (128 elements),
+ *     row-major inside a tile; tile (r / 128, b / 64) starts at
+ *     ((r / 128) * (cols / 128) + b / 64) * 8192, so byte b of row r is at
+ *     that start + (r % 128) * 64 + b % 64.  rows and cols must be multiples
+ *     of 128.  The GEMM's weight (B) operand then streams in whole 8 KB
+ *     blocks instead of 64-byte pieces of rows far apart. */
+typedef enum { FP4_CODES_ROWMAJOR = 0, FP4_CODES_TILED = 1 } fp4_code_layout;
+/* OR'ed into the fmt of fp4_gemm / fp4_gemm_w4a16 (and their workspace
+ * queries): b_codes are in the FP4_CODES_TILED layout (N % 128 == 0). */
+#define FP4_GEMM_B_TILED 0x100
 typedef enum {
     FP4_GS_COMPUTE = 0,          /* tensor scale from the tensor: maximum pass, then encode */
     FP4_GS_GIVEN = 1,            /* tensor scale read from *global_scale */
@@ -140,6 +155,8 @@ typedef enum {
  *                 rotations); all zero is the plain transform.  The inverse
  *                 (fp4_dequantize, fp4_error_sums) applies it after.
  *   seed          stochastic-rounding key.
+ *   code_layout   fp4_code_layout of the codes that fp4_quantize writes and
+ *                 fp4_dequantize / fp4_error_sums read.
  * rotate may also be 64 or 128 for MXFP4 / MXINT4 ("Bridging the Gap ...":
  * larger rotations help MXFP4): rotation groups of 2 or 4 blocks, cols a
  * multiple of rotate; scales stay per 32-element block. */
@@ -154,13 +171,14 @@ typedef struct {
     int32_t block_rows;
     uint32_t rot_signs[4];
     uint32_t seed[2];
+    int32_t code_layout;
 } fp4_qconfig;
 
 /* ---------------------------------------------------------------- sizes */
 
 /* Bytes of packed codes for [rows, cols]: rows * cols / 2, two 4-bit codes per
- * byte ("NVFP4 vs MXFP4 ...", Figure 2: E2M1 values packed two per byte).
- * 0 for negative sizes or odd cols.  Host function. */
+ * byte ("NVFP4 vs MXFP4 ...", Figure 2: E2M1 values packed two per byte), in
+ * either code layout.  0 for negative sizes or odd cols.  Host function. */
 size_t fp4_codes_bytes(int64_t rows, int64_t cols);
 
 /* Bytes of the scale array, including the padding of the GEMM layout
@@ -316,7 +334,7 @@ int fp4_quantize_batch(int32_t n, const fp4_quant_job* jobs, void* ws, size_t ws
  *   MXFP4: e2m1 * 2^(c - 127);  NVFP4: fl32(fl32(e2m1 * e4m3) * ts),
  * then, if inverse_rotate != 0 and cfg->rotate != 0, the block Hadamard again
  * (it is its own inverse), giving values in the original domain.  bf16 output
- * rounds to nearest-even.  Scales are read in cfg's layout. */
+ * rounds to nearest-even.  Scales and codes are read in cfg's layouts. */
 int fp4_dequantize(const fp4_qconfig* cfg, const uint8_t* codes, const uint8_t* scales,
                    const float* global_scale, int64_t rows, int64_t cols,
                    void* y, int32_t ydt, int64_t ldy, int32_t inverse_rotate, void* stream);
@@ -349,6 +367,9 @@ int fp4_scales_to_gemm_layout(const fp4_qconfig* cfg, const uint8_t* rowmajor,
  * scales applied inside the product, higher-precision accumulation).
  *   A: a_codes [M, K/2] dense, a_scales in FP4_SCALES_GEMM layout for (M, K).
  *   B: b_codes [N, K/2] dense, b_scales in FP4_SCALES_GEMM layout for (N, K).
+ *   fmt | FP4_GEMM_B_TILED: b_codes in the FP4_CODES_TILED layout (N % 128
+ *   == 0, else FP4_ERR_INVALID_ARG); the result is bit-identical to the
+ *   row-major call.
  *   NVFP4: a_gs / b_gs point to the fp32 per-tensor scales (device); the
  *   product is multiplied by (*a_gs) * (*b_gs).  MXFP4 ignores them.
  *   Accumulation is fp32.  y has leading dimension ldy >= N and type ydt
@@ -376,7 +397,8 @@ int fp4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K,
  * weights; decode, where the weights stream from HBM once per token, is the
  * serving case the pages emphasise).
  *   A: bf16 activations [M, K], row stride lda (elements), unquantized.
- *   B: b_codes [N, K/2] dense, b_scales in FP4_SCALES_GEMM layout for (N, K)
+ *   B: b_codes [N, K/2] dense (fmt | FP4_GEMM_B_TILED: the FP4_CODES_TILED
+ *      layout, N % 128 == 0), b_scales in FP4_SCALES_GEMM layout for (N, K)
  *      (NVFP4: row-major), b_gs the NVFP4 tensor scale (device fp32; MXFP4
  *      ignores it).  MXINT4 / NVINT4 weights take the same call (the integer
  *      element times its scale is exact in bf16).  B is dequantized exactly (e2m1 * scale is exact in bf16)

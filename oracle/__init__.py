@@ -106,6 +106,8 @@ def _load(path: str):
     L.ora_int4_encode_array.argtypes = [P, l, P]
     L.ora_e4m3_encode_array.restype = None
     L.ora_e4m3_encode_array.argtypes = [P, l, P]
+    L.ora_tile_codes.restype = ctypes.c_int
+    L.ora_tile_codes.argtypes = [P, l, l, P]
     return L
 
 
@@ -325,6 +327,18 @@ def dequantize(codes, scales, fmt: int, ts: float = 0.0, inverse_rotate: bool = 
     if rc != 0:
         raise ValueError("ora_dequantize: bad arguments")
     return y
+
+
+def tile_codes(codes) -> np.ndarray:
+    """Row-major packed codes [rows, row_bytes] (rows % 128 == 0, row_bytes %
+    64 == 0) in the library's tiled code layout (8 KB tiles of 128 rows x 64
+    bytes; see ora_tile_codes), as a flat byte array."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    rows, row_bytes = codes.shape
+    out = np.zeros(rows * row_bytes, dtype=np.uint8)
+    if lib().ora_tile_codes(_p(codes), rows, row_bytes, _p(out)) != 0:
+        raise ValueError("ora_tile_codes: rows must be a multiple of 128, row bytes of 64")
+    return out
 
 
 def error_sums(x, xhat) -> np.ndarray:

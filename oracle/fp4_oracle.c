@@ -870,3 +870,25 @@ void ora_e4m3_encode_array(const float *t, long n, uint8_t *out)
     for (long i = 0; i < n; ++i)
         out[i] = (uint8_t)ora_e4m3_encode(t[i]);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Tiled code layout.  No page fixes a storage order for packed codes; this is
+ * the library's own FP4_CODES_TILED layout, written here from its definition:
+ * the code bytes of a [rows, row_bytes] row-major matrix (rows a multiple of
+ * 128, row_bytes of 64) go into 8192-byte tiles of 128 rows x 64 bytes,
+ * row-major inside a tile; the tiles of one 128-row panel follow each other
+ * along the row, and the panels follow each other.  A pure permutation. */
+int ora_tile_codes(const uint8_t *src, long rows, long row_bytes, uint8_t *dst)
+{
+    if (rows < 0 || row_bytes < 0 || rows % 128 != 0 || row_bytes % 64 != 0)
+        return ORA_EINVAL;
+    const long tiles_per_panel = row_bytes / 64;
+    for (long r = 0; r < rows; ++r) {
+        for (long b = 0; b < row_bytes; ++b) {
+            long panel = r / 128, tile = b / 64;
+            long start = (panel * tiles_per_panel + tile) * 8192;
+            dst[start + (r % 128) * 64 + (b % 64)] = src[r * row_bytes + b];
+        }
+    }
+    return ORA_OK;
+}

@@ -1030,4 +1030,35 @@ def check_sizes():
         assert 8 * (c.nbytes + s.nbytes) / (x.size / FMT[key]["block"]) == FMT[key]["bits_per_block"]
 
 
+
+def check_tiled_code_layout():
+    """The tiled code layout at positions worked out by hand from its
+    definition (8 KB tiles of 128 rows x 64 bytes; a panel's tiles along the
+    row, then the next panel), for a 256 x 512 matrix (256 bytes per row, four
+    tiles per panel), and that it only moves bytes."""
+    rows, row_bytes = 256, 256
+    expected = {(0, 0): 0, (1, 0): 64, (0, 63): 63, (0, 64): 8192, (127, 63): 8191,
+                (0, 255): 3 * 8192 + 63, (128, 0): 4 * 8192, (130, 100): 5 * 8192 + 2 * 64 + 36,
+                (255, 255): 65535}
+    for (r, b), pos in expected.items():
+        src = np.zeros((rows, row_bytes), np.uint8)
+        src[r, b] = 0xA5
+        t = oracle.tile_codes(src)
+        assert t.size == rows * row_bytes
+        assert np.flatnonzero(t).tolist() == [pos], ((r, b), np.flatnonzero(t)[:4], pos)
+    g = np.random.default_rng(3)
+    src = g.integers(0, 256, (384, 192), dtype=np.uint8)
+    t = oracle.tile_codes(src)
+    assert np.array_equal(np.sort(t), np.sort(src.ravel()))
+    # a one-panel, one-tile matrix is unchanged
+    one = g.integers(0, 256, (128, 64), dtype=np.uint8)
+    assert np.array_equal(oracle.tile_codes(one), one.ravel())
+    for bad in ((64, 64), (128, 32)):
+        try:
+            oracle.tile_codes(np.zeros(bad, np.uint8))
+        except ValueError:
+            continue
+        raise AssertionError("tile_codes accepted %r" % (bad,))
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(fp4.EXPORTED)
-    assert L.fp4_abi_version() == 4
+    assert L.fp4_abi_version() == 5
     assert fp4.status_str(fp4.FP4_ERR_ALIGNMENT).startswith("misaligned")
 
 
@@ -123,7 +123,7 @@ def test_quantize_rejects_bad_arguments_on_host():
     assert _q(fp4.qconfig(fp4.FMT_NVFP4, True, block_rows=16)) == E.FP4_ERR_UNSUPPORTED
     assert fp4.fp4_scales_bytes(fp4.qconfig(fp4.FMT_NVFP4, block_rows=16), 64, 256) == 64 * 16
     assert fp4.fp4_scales_bytes(fp4.qconfig(fp4.FMT_MXFP4, 128, fp4.SCALES_GEMM, signs=5), 64, 256) == 512
-    assert ctypes.sizeof(fp4.QConfig) == 52
+    assert ctypes.sizeof(fp4.QConfig) == 56
     # INT4-element formats: the MX / NV layouts, absmax scales only
     mxi = fp4.qconfig(fp4.FMT_MXINT4, scale_layout=fp4.SCALES_GEMM)
     nvi = fp4.qconfig(fp4.FMT_NVINT4)
@@ -232,6 +232,32 @@ def test_gemm_rejects_bad_arguments_on_host():
     assert fp4.fp4_gemm_workspace_bytes(fp4.FMT_MXFP4, 1, 8192, 28672) > 0
     assert fp4.fp4_gemm_workspace_bytes(fp4.FMT_MXFP4, 4096, 4096, 4096) == 0
     assert _g(ws=FAKE + 8, wsb=1 << 20) == E.FP4_ERR_ALIGNMENT  # split-K partials: 16-byte aligned
+
+
+def test_tiled_code_layout_is_checked_on_host():
+    """FP4_CODES_TILED needs rows and cols that are multiples of 128, tiled B
+    operands N % 128 == 0; unknown layout values and fmt bits are rejected."""
+    E = fp4
+    for fmt in (fp4.FMT_MXFP4, fp4.FMT_NVFP4, fp4.FMT_MXINT4, fp4.FMT_NVINT4):
+        t = fp4.qconfig(fmt, code_layout=fp4.CODES_TILED)
+        assert fp4.fp4_scales_bytes(t, 128, 256) == fp4.fp4_scales_bytes(fp4.qconfig(fmt), 128, 256)
+        assert fp4.fp4_scales_bytes(t, 64, 256) == 0
+        assert fp4.fp4_scales_bytes(t, 128, 192) == 0
+        assert _q(t, rows=64) == E.FP4_ERR_INVALID_ARG
+        assert _q(t, rows=128, cols=192, ldx=192) == E.FP4_ERR_INVALID_ARG
+        assert fp4.fp4_dequantize(t, FAKE, FAKE, FAKE, 64, 256, FAKE, fp4.DT_F32, 256, 0, None) == E.FP4_ERR_INVALID_ARG
+    assert fp4.fp4_scales_bytes(fp4.qconfig(fp4.FMT_MXFP4, code_layout=2), 128, 256) == 0
+    bt = fp4.GEMM_B_TILED
+    assert _g(fmt=fp4.FMT_MXFP4 | bt, N=64) == E.FP4_ERR_INVALID_ARG      # N % 128
+    assert _g(fmt=fp4.FMT_NVFP4 | bt, N=192, ldy=192) == E.FP4_ERR_INVALID_ARG
+    assert _g(fmt=fp4.FMT_MXFP4 | 0x200) == E.FP4_ERR_INVALID_ARG         # unknown flag bits
+    assert _g(fmt=fp4.FMT_MXFP4 | bt, N=128, ldy=128, M=0, y=None) == E.FP4_OK
+    assert _w(fmt=fp4.FMT_MXFP4 | bt, N=64) == E.FP4_ERR_INVALID_ARG
+    for fmt in (fp4.FMT_MXFP4, fp4.FMT_NVFP4, fp4.FMT_MXINT4, fp4.FMT_NVINT4):
+        for M, N, K in ((1, 28672, 8192), (16, 8192, 28672), (4096, 4096, 4096)):
+            assert fp4.fp4_gemm_workspace_bytes(fmt | bt, M, N, K) == fp4.fp4_gemm_workspace_bytes(fmt, M, N, K)
+            assert (fp4.fp4_gemm_w4a16_workspace_bytes(fmt | bt, M, N, K)
+                    == fp4.fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K))
 
 
 def _w(**kw):

@@ -73,6 +73,9 @@ MUTANTS = [
     ("two-dimensional tile of 8 rows", "long r0 = r - r % q->block_rows;", "long r0 = r - r % 8;"),
     ("int4 formats decode as E2M1", "return fmt_int(fmt) ? ora_int4_decode(code) : ora_e2m1_decode(code);",
      "return ora_e2m1_decode(code);"),
+    ("tiles ordered down the panels first", "long start = (panel * tiles_per_panel + tile) * 8192;",
+     "long start = (tile * (rows / 128) + panel) * 8192;"),
+    ("tile stored column-major", "dst[start + (r % 128) * 64 + (b % 64)]", "dst[start + (b % 64) * 128 + (r % 128)]"),
 ]
 
 
