@@ -568,7 +568,10 @@ def only_gemm(args, torch, fp4, workloads, dev):
     """A few calls of each listed GEMM (a short program for profiler runs):
     seeded operands as in the GEMM section (Gaussian weights, Laplace
     activations with outlier channels, the block Hadamard of the format,
-    GEMM-layout scales), bf16 output, `--gemm-iters` timed calls each."""
+    GEMM-layout scales, weights in the tiled code layout, four weight copies
+    used in turn as in the GEMM section, so that decode streams its weights
+    from HBM rather than the last-level cache), bf16 output, `--gemm-iters`
+    timed calls each."""
     fmts = {"mx": fp4.FMT_MXFP4, "nv": fp4.FMT_NVFP4, "mxint4": fp4.FMT_MXINT4,
             "nvint4": fp4.FMT_NVINT4, "w4mx": fp4.FMT_MXFP4, "w4nv": fp4.FMT_NVFP4}
     res = {}
@@ -578,34 +581,36 @@ def only_gemm(args, torch, fp4, workloads, dev):
         fmt = fmts[name]
         w = torch.from_numpy(workloads.gemm_weight(N, K, seed=1).view(np.int16)).to(dev).view(torch.bfloat16)
         a = torch.from_numpy(workloads.gemm_activation(M, K, seed=1).view(np.int16)).to(dev).view(torch.bfloat16)
-        qw = fp4.quantize(w, fmt, rotate=True, scale_layout=fp4.SCALES_GEMM)
+        q0 = fp4.quantize(w, fmt, rotate=True, scale_layout=fp4.SCALES_GEMM, code_layout=fp4.CODES_TILED)
+        qw = [q0] + [fp4.Quantized(q0.codes.clone(), q0.scales.clone(), q0.global_scale.clone(),
+                                   q0.cfg, q0.rows, q0.cols) for _ in range(3)]
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         if name.startswith("w4"):
             wsb = fp4.fp4_gemm_w4a16_workspace_bytes(fmt, M, N, K)
             ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
 
-            def call():
-                fp4.gemm_w4a16(a, qw, out=y, workspace=ws if wsb else None)
+            def call(i):
+                fp4.gemm_w4a16(a, qw[i % 4], out=y, workspace=ws if wsb else None)
         else:
             qa = fp4.quantize(a, fmt, rotate=True, scale_layout=fp4.SCALES_GEMM)
             wsb = fp4.fp4_gemm_workspace_bytes(fmt, M, N, K)
             ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
 
-            def call():
-                fp4.gemm(qa, qw, out=y, workspace=ws if wsb else None)
-        call()
+            def call(i):
+                fp4.gemm(qa, qw[i % 4], out=y, workspace=ws if wsb else None)
+        call(3)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(max(1, args.gemm_iters)):
-            call()
+        for i in range(max(1, args.gemm_iters)):
+            call(i)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / max(1, args.gemm_iters)
         res[item] = {"us_per_call": round(us, 2), "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
         log("%s %.2f us" % (item, us))
-        del w, a, qw, y
+        del w, a, q0, qw, y
     print(json.dumps({"only_gemm": res}), flush=True)
 
 
@@ -777,7 +782,7 @@ def bench_cfg3(torch, fp4, workloads, dev, stream, sh_now, capture):
 
 
 def bench_gemm(args, torch, fp4, workloads, dev, stream):
-    res = {}
+    res = {"weight_code_layout": "tiled: 8 KB tiles of 128 rows x 128 elements"}
     iters = max(1, args.gemm_iters)
 
     def to_dev(bits):
@@ -809,7 +814,9 @@ def bench_gemm(args, torch, fp4, workloads, dev, stream):
         return e0.elapsed_time(e1) * 1e3 / reps  # us
 
     def quant_copies(x_bf16, fmt, rot, ncopy):
-        q0 = fp4.quantize(x_bf16, fmt, rotate=rot, scale_layout=fp4.SCALES_GEMM)
+        # weights: tiled codes (whole 8 KB blocks per GEMM stage)
+        q0 = fp4.quantize(x_bf16, fmt, rotate=rot, scale_layout=fp4.SCALES_GEMM,
+                          code_layout=fp4.CODES_TILED)
         out = [q0]
         for _ in range(ncopy - 1):
             out.append(fp4.Quantized(q0.codes.clone(), q0.scales.clone(), q0.global_scale.clone(),

@@ -28,6 +28,8 @@ using namespace fp4k;
 namespace {
 
 constexpr int kThreads = 256;
+// Most K-slices a split-K plan uses.
+constexpr int kMaxSplits = 16;
 
 // XOR swizzle of 16-byte chunks within a 64-byte LDS row (4 chunks): four
 // consecutive rows share a 256-byte bank line, so rows 4i .. 4i+3 keep their
@@ -1515,7 +1517,7 @@ W4Plan plan_w4(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + 127) / 128);
   const int KT = (int)(K / 128);
   int splits = 1;
-  while (tiles * splits * 2 <= 256 && splits < 16 && KT / (splits * 2) >= 4) splits *= 2;
+  while (tiles * splits * 2 <= 256 && splits < kMaxSplits && KT / (splits * 2) >= 4) splits *= 2;
   int kt_per = (KT + splits - 1) / splits;
   kt_per += kt_per & 1;
   return W4Plan{bm, splits, kt_per};
@@ -1549,7 +1551,7 @@ __global__ __launch_bounds__(kThreads) void zero_out_kernel(void* __restrict__ Y
 
 // Y = sum over splits of the fp32 partials (fixed order), times the tensor
 // scales that are given (NVFP4: (*ga) * (*gb); weight-only NVFP4: *ga).
-template <int YDT>
+template <int YDT, bool VEC>
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __restrict__ part,
                                                                  int splits, int M, int N,
                                                                  void* __restrict__ Y,
@@ -1559,24 +1561,49 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __
   const int64_t total = (int64_t)M * N;
   const bool scaled = ga != nullptr || gb != nullptr;
   const float g = (ga ? *ga : 1.0f) * (gb ? *gb : 1.0f);
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * kThreads) {
-    float s = 0.0f;
-    for (int k = 0; k < splits; ++k) s += part[(int64_t)k * total + i];
-    const int row = (int)(i / N), col = (int)(i - (int64_t)row * N);
-    store_out<YDT>(Y, ldy, row, col, scaled ? s * g : s);
+  if constexpr (VEC) {
+    // four consecutive outputs (one row, N % 4 == 0) per thread; all of its
+    // 16-byte partial loads go out before the sums, which keep slice order
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < total / 4;
+         v += (int64_t)gridDim.x * kThreads) {
+      f32x4 p[kMaxSplits];
+#pragma unroll
+      for (int k = 0; k < kMaxSplits; ++k)
+        if (k < splits) p[k] = *reinterpret_cast<const f32x4*>(part + (int64_t)k * total + 4 * v);
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < kMaxSplits; ++k)
+        if (k < splits) acc += p[k];
+      const int row = (int)((4 * v) / N), col = (int)(4 * v - (int64_t)row * N);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out<YDT>(Y, ldy, row, col + e, scaled ? acc[e] * g : acc[e]);
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * kThreads) {
+      float acc = 0.0f;
+      for (int k = 0; k < splits; ++k) acc += part[(int64_t)k * total + i];
+      const int row = (int)(i / N), col = (int)(i - (int64_t)row * N);
+      store_out<YDT>(Y, ldy, row, col, scaled ? acc * g : acc);
+    }
   }
 }
 
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t N, void* y,
                                 int ydt, int64_t ldy, const float* ga, const float* gb,
                                 hipStream_t st) {
-  int64_t g = (M * N + kThreads - 1) / kThreads;
+  const bool vec = N % 4 == 0 && splits <= kMaxSplits;
+  int64_t g = (M * N / (vec ? 4 : 1) + kThreads - 1) / kThreads;
   if (g > 8192) g = 8192;
-  if (ydt == FP4_DT_F32)
-    splitk_reduce_kernel<FP4_DT_F32><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy, ga, gb);
+  if (g < 1) g = 1;
+  if (ydt == FP4_DT_F32 && vec)
+    splitk_reduce_kernel<FP4_DT_F32, true><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy, ga, gb);
+  else if (ydt == FP4_DT_F32)
+    splitk_reduce_kernel<FP4_DT_F32, false><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy, ga, gb);
+  else if (vec)
+    splitk_reduce_kernel<FP4_DT_BF16, true><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy, ga, gb);
   else
-    splitk_reduce_kernel<FP4_DT_BF16><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy, ga, gb);
+    splitk_reduce_kernel<FP4_DT_BF16, false><<<(int)g, kThreads, 0, st>>>(part, splits, (int)M, (int)N, y, ldy, ga, gb);
   return hipGetLastError();
 }
 
@@ -1718,7 +1745,7 @@ MxPlan plan_mx(int64_t M, int64_t N, int64_t K, int bn2 = 256, bool small_m_cap 
   int splits = 1;
   const int64_t cap = (p.cfg == 2 || (small_m_cap && p.cfg == 1 && M <= 128)) ? 256 : 512;
   if (p.cfg != 0)
-    while (tiles * splits * 2 <= cap && splits < 16 && KT / (splits * 2) >= 4) splits *= 2;
+    while (tiles * splits * 2 <= cap && splits < kMaxSplits && KT / (splits * 2) >= 4) splits *= 2;
   p.splits = splits;
   p.kt_per = (KT + splits - 1) / splits;
   p.kt_per += p.kt_per & 1;
