@@ -538,11 +538,18 @@ __device__ __forceinline__ void store_block(const u32x4& out, uint32_t code, int
                                             int64_t nb, uint8_t* __restrict__ codes,
                                             uint8_t* __restrict__ scales, int64_t kchunks,
                                             int gemm_layout, uint32_t tiled) {
+  // tiled is uniform: a branch, so the row-major path costs no extra VALU
   if constexpr (fmt_mx(FMT)) {
-    *reinterpret_cast<u32x4*>(codes + code_offset(r, kb * 16, nb * 16, tiled != 0)) = out;
+    if (tiled)
+      *reinterpret_cast<u32x4*>(codes + code_offset(r, kb * 16, nb * 16, true)) = out;
+    else
+      *reinterpret_cast<u32x4*>(codes + r * (nb * 16) + kb * 16) = out;
     store_mx_scale(scales, r, kb, nb, kchunks, gemm_layout, code);
   } else {
-    *reinterpret_cast<u32x2*>(codes + code_offset(r, kb * 8, nb * 8, tiled != 0)) = u32x2{out[0], out[1]};
+    if (tiled)
+      *reinterpret_cast<u32x2*>(codes + code_offset(r, kb * 8, nb * 8, true)) = u32x2{out[0], out[1]};
+    else
+      *reinterpret_cast<u32x2*>(codes + r * (nb * 8) + kb * 8) = u32x2{out[0], out[1]};
     scales[r * nb + kb] = (uint8_t)code;
   }
 }
