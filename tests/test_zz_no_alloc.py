@@ -3,8 +3,9 @@ static per-GPU device array instead of a caller workspace.  Called through
 the C ABI and compared with fp4_quantize (the same configuration with a
 workspace) bit for bit: codes, scales and tensor scale, for NVFP4 with the
 tensor scale computed in two passes and in one, NVINT4, rotated and plain,
-and MXFP4 (which needs no scratch); two calls in a row, the second with a
-smaller input, so that the static scratch is reused."""
+and MXFP4 (which needs no scratch), with row-major and tiled codes; two
+calls in a row, the second with a smaller input, so that the static scratch
+is reused."""
 import numpy as np
 import pytest
 
@@ -40,13 +41,16 @@ def _outputs(cfg, rows, cols, fill):
     return codes, scales, gs
 
 
+@pytest.mark.parametrize("tiled", [False, True], ids=["rowmajor", "tiled"])
 @pytest.mark.parametrize("fmt,rot,mode", CASES, ids=IDS)
-def test_noalloc_matches_workspace_entry_point(fmt, rot, mode):
+def test_noalloc_matches_workspace_entry_point(fmt, rot, mode, tiled):
     stream = torch.cuda.current_stream().cuda_stream
     lay = fp4.SCALES_GEMM if fmt in fp4.MX_FORMATS else fp4.SCALES_ROWMAJOR
-    cfg = fp4.qconfig(fmt, rot, lay)
-    for rows, cols, seed in ((2048, 4096, 31), (37, 4128, 32)):  # the second call smaller
-        print("noalloc", fmt, rot, mode, rows, cols, flush=True)
+    cfg = fp4.qconfig(fmt, rot, lay, code_layout=fp4.CODES_TILED if tiled else fp4.CODES_ROWMAJOR)
+    # the second call smaller (tiled codes: multiples of 128 rows and columns)
+    shapes = ((2048, 4096, 31), (256, 1024, 32)) if tiled else ((2048, 4096, 31), (37, 4128, 32))
+    for rows, cols, seed in shapes:
+        print("noalloc", fmt, rot, mode, tiled, rows, cols, flush=True)
         x = torch.from_numpy(workloads.cfg2_tensor("laplace", seed, rows=rows, cols=cols).view(np.int16))
         x = x.to("cuda").view(torch.bfloat16)
         ref = _outputs(cfg, rows, cols, 0xAA)
