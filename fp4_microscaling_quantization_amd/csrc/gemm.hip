@@ -538,23 +538,28 @@ __global__ __launch_bounds__((Mx2Cfg<BM, BN, WM, WN>::NW * 64)) void gemm_mx2_ke
   };
   constexpr int NMF = TM * TN;
   constexpr int NRD = TM + TN;
-  // A stage's DMA goes out in three parts: rounds [0, D0) right after the
-  // barrier that frees its slot, [D0, D1) and [D1, ROUNDS) with the MFMAs of
-  // steps 0 and 1 of the stage being multiplied meanwhile.
-  constexpr int D0 = (ROUNDS + 2) / 3, D1 = (2 * ROUNDS + 2) / 3;
+  // The stage barrier sits after step 2: by then every wave holds step 3's
+  // fragments in registers, so the stage's slot is free, and (each wave
+  // having waited for its own DMAs) the next stage has landed.  Step 3's MFMAs
+  // then cover the next stage's first fragment reads, its scale reads (issued
+  // after them) and the first E3 rounds of the stage after next, into the
+  // freed slot; that stage's remaining rounds go out in two parts with steps
+  // 0 and 1 of the next stage, four to five steps before the barrier that
+  // waits for them.  Measured against a barrier after step 3 (and three DMA
+  // parts within the stage): 4-8 % less time on every 256x256 shape.
+  constexpr int E3 = 4;
+  constexpr int H = (E3 + ROUNDS + 1) / 2;
+  static_assert(E3 < ROUNDS, "step 3's rounds are full rounds for every wave");
 
   auto ring = [&](auto full_tag) __attribute__((always_inline)) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    constexpr int PER = FULL ? ROUNDS : ROUNDS - 1;  // DMAs per stage of this wave
     dma_stage(ks0, 0, ROUNDS, full_tag);
     if (ks0 + 1 < ks1) {
-      dma_stage(ks0 + 1, 0, D0, full_tag);
-      // stage ks0 landed for this wave: only ks0 + 1's first part in flight
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(D0, 15));
+      dma_stage(ks0 + 1, 0, E3, full_tag);
+      // stage ks0 landed for this wave: only ks0 + 1's first E3 rounds in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(E3, 15));
     } else {
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     }
-    (void)PER;
     __builtin_amdgcn_s_barrier();
     Frags F0, F1;
     Scales S;
@@ -562,35 +567,43 @@ __global__ __launch_bounds__((Mx2Cfg<BM, BN, WM, WN>::NW * 64)) void gemm_mx2_ke
     read_scales(dyn_lds, S);
     for (int ks = ks0; ks < ks1; ++ks) {
       const uint8_t* slot = dyn_lds + (ks & 1) * C::STAGE;
+      const uint8_t* nslot = dyn_lds + ((ks + 1) & 1) * C::STAGE;
       const bool next = ks + 1 < ks1;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         Frags& cur = (s & 1) ? F1 : F0;
         Frags& nxt = (s & 1) ? F0 : F1;
         if (s < 3) read_frags(slot, s + 1, nxt);
-        if (s == 0 && next) dma_stage(ks + 1, D0, D1, full_tag);
-        if (s == 1 && next) dma_stage(ks + 1, D1, ROUNDS, full_tag);
+        if (s == 3) {
+          // past the last stage these reads fetch a stale slot (unused) and
+          // the DMA re-loads the last stage (its data, or a slot nobody reads
+          // again); unconditional, which keeps the register allocation spill-free
+          read_frags(nslot, 0, F0);
+          dma_stage(min(ks + 2, ks1 - 1), 0, E3, full_tag);
+        }
+        if (s == 0 && next) dma_stage(ks + 1, E3, H, full_tag);
+        if (s == 1 && next) dma_stage(ks + 1, H, ROUNDS, full_tag);
         mfmas(cur, S, s);
 #pragma unroll
         for (int k = 0; k < NMF; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (s < 3 && k < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          if (s < 2 && k < D1 - D0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          if (s < 2 && k < 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (s == 2) {
+          // stage ks + 1 complete (this wave's DMAs, then everyone's) and
+          // slot ks read by nobody any more
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      // stage ks + 1 complete (this wave's DMAs, then everyone's) and slot ks
-      // read by nobody
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      if (next) {
-        const uint8_t* nslot = dyn_lds + ((ks + 1) & 1) * C::STAGE;
-        read_frags(nslot, 0, F0);
-        read_scales(nslot, S);
-        if (ks + 2 < ks1) dma_stage(ks + 2, 0, D0, full_tag);
-      }
+      // after step 3's MFMAs have taken the current scales
+      read_scales(nslot, S);
     }
+    // the last stages' re-load DMAs land before the ring is reused
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   };
   if (ks0 < ks1) {
     if (wave < C::LAST_W)
