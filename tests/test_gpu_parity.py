@@ -488,8 +488,11 @@ def test_gemm_llama70b_mlp_shapes(fmt, M, N, K, out_dtype):
 
 # Shapes that take the 256 x 256 tile plan (at least 256 such tiles) with
 # ragged M and N, a K with a last 128-K stage (K % 256 == 128), and a split-K
-# slice with an odd number of stages.
-PLAN_EDGES = [(4000, 4100, 4096), (4000, 4100, 4224), (64, 1024, 1152), (4000, 4100, 1024)]
+# slice with an odd number of stages; the 256-K ring with 1, 2, 3 and 5 stages
+# (its first and last stages differ: stale reads and a re-load of the last
+# stage past the end).
+PLAN_EDGES = [(4000, 4100, 4096), (4000, 4100, 4224), (64, 1024, 1152), (4000, 4100, 1024),
+              (4096, 4096, 256), (4000, 4100, 512), (4000, 4100, 768), (4096, 4096, 1280)]
 
 
 @pytest.mark.parametrize("out_dtype", OUT_DT, ids=OUT_IDS)
