@@ -544,9 +544,10 @@ __global__ __launch_bounds__((Mx2Cfg<BM, BN, WM, WN>::NW * 64)) void gemm_mx2_ke
   // then cover the next stage's first fragment reads, its scale reads (issued
   // after them) and the first E3 rounds of the stage after next, into the
   // freed slot; that stage's remaining rounds go out in two parts with steps
-  // 0 and 1 of the next stage, four to five steps before the barrier that
-  // waits for them.  Measured against a barrier after step 3 (and three DMA
-  // parts within the stage): 4-8 % less time on every 256x256 shape.
+  // 0 and 1 of the next stage.  The barrier after the next stage's step 2
+  // waits for all of them: four, three and two steps after their issue.
+  // Measured against a barrier after step 3 (and three DMA parts within the
+  // stage): 4-8 % less time on every 256x256 shape.
   constexpr int E3 = 4;
   constexpr int H = (E3 + ROUNDS + 1) / 2;
   static_assert(E3 < ROUNDS, "step 3's rounds are full rounds for every wave");
