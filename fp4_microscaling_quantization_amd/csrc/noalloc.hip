@@ -30,6 +30,22 @@ static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
+// Zeroes the single-pass exchange region when its give-up flag (word 1) is
+// set.  A launch whose grid-wide wait gave up can leave a slot tagged with the
+// next call's number (a workgroup that started after workgroup 0 advanced the
+// call number), which the next single-pass call would otherwise read as one of
+// its own maxima; a caller workspace is re-zeroed with fp4_workspace_init, the
+// static scratch by this kernel, queued before every single-pass call.  One
+// workgroup: every thread reads the flag before any thread clears it.
+__global__ __launch_bounds__(256) void exchange_repair_kernel(uint32_t* __restrict__ region,
+                                                              uint32_t nwords) {
+  __shared__ uint32_t flag;
+  if (threadIdx.x == 0) flag = region[1];
+  __syncthreads();
+  if (flag == 0) return;
+  for (uint32_t i = threadIdx.x; i < nwords; i += blockDim.x) region[i] = 0u;
+}
+
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxScratchDevices];
 
@@ -68,6 +84,12 @@ extern "C" int fp4_quantize_noalloc(const fp4_qconfig* cfg, const void* x, int32
   void* ws = nullptr;
   const int rc = scratch_of_current_device(static_cast<hipStream_t>(stream), &ws);
   if (rc != FP4_OK) return rc;
+  if (gs_mode == FP4_GS_COMPUTE_ONE_PASS) {
+    uint32_t* xchg = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kExchangeOffset);
+    exchange_repair_kernel<<<1, 256, 0, static_cast<hipStream_t>(stream)>>>(
+        xchg, (uint32_t)((kScratchBytes - kExchangeOffset) / 4));
+    if (hipGetLastError() != hipSuccess) return FP4_ERR_HIP;
+  }
   return fp4_quantize(cfg, x, xdt, rows, cols, ldx, codes, scales, global_scale, gs_mode, ws,
                       kScratchBytes, stream);
 }

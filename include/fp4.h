@@ -276,7 +276,11 @@ int fp4_global_scale(const fp4_qconfig* cfg, const void* x, int32_t xdt,
  * region (a fill kernel on `stream`).  Every call on a GPU uses that GPU's one
  * array, which keeps the last call's contents: calls that may overlap in time
  * on one GPU (other streams, other host threads) race on it and must be
- * serialised by the caller (one stream is enough).  Returns
+ * serialised by the caller (one stream is enough).  With
+ * FP4_GS_COMPUTE_ONE_PASS a one-workgroup kernel is queued before the
+ * quantization that zeroes the exchange region if an earlier call gave up
+ * its grid-wide wait (NaN tensor scale; the region then needs zeroing, which
+ * a caller cannot do for the static array).  Returns
  * FP4_ERR_WORKSPACE if a configuration would need more than the static
  * scratch (none does today), otherwise exactly what fp4_quantize returns. */
 int fp4_quantize_noalloc(const fp4_qconfig* cfg, const void* x, int32_t xdt,

@@ -85,3 +85,51 @@ def test_noalloc_rejects_what_fp4_quantize_rejects():
                                     s.data_ptr(), None, fp4.GS_COMPUTE, stream) \
         == fp4.FP4_ERR_INVALID_ARG
     assert fp4.fp4_workspace_bytes(cfg, 4096, 4096) <= 8192  # the static scratch's size
+
+
+@pytest.mark.parametrize("rot", [False, True], ids=["plain", "h16"])
+def test_noalloc_one_pass_replayed_as_a_graph(rot):
+    """The single-pass call (the exchange-repair kernel, then the quantize
+    kernel) recorded in a HIP graph and replayed three times on changing
+    inputs, with eager work between the replays: every replay equals the
+    workspace entry point's result on the same input."""
+    rows, cols = 1024, 2048
+    cfg = fp4.qconfig(fp4.FMT_NVFP4, rot, fp4.SCALES_ROWMAJOR)
+    xs = [torch.from_numpy(workloads.cfg2_tensor("laplace", 40 + i, rows=rows, cols=cols).view(np.int16))
+          .to("cuda").view(torch.bfloat16) for i in range(3)]
+    x = torch.empty_like(xs[0])
+    got = _outputs(cfg, rows, cols, 0x55)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        h = torch.cuda.current_stream().cuda_stream
+        assert fp4.fp4_quantize_noalloc(cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                        got[0].data_ptr(), got[1].data_ptr(), got[2].data_ptr(),
+                                        fp4.GS_COMPUTE_ONE_PASS, h) == fp4.FP4_OK
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h = torch.cuda.current_stream().cuda_stream
+        rc = fp4.fp4_quantize_noalloc(cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols,
+                                      got[0].data_ptr(), got[1].data_ptr(), got[2].data_ptr(),
+                                      fp4.GS_COMPUTE_ONE_PASS, h)
+    assert rc == fp4.FP4_OK
+    stream = torch.cuda.current_stream().cuda_stream
+    wsb = fp4.fp4_workspace_bytes(cfg, rows, cols)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    n = fp4.fp4_codes_bytes(rows, cols)
+    ns = fp4.fp4_scales_bytes(cfg, rows, cols)
+    for i in range(3):
+        print("noalloc graph replay", rot, i, flush=True)
+        x.copy_(xs[i])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = _outputs(cfg, rows, cols, 0xAA)
+        assert fp4.fp4_quantize(cfg, x.data_ptr(), fp4.DT_BF16, rows, cols, cols, ref[0].data_ptr(),
+                                ref[1].data_ptr(), ref[2].data_ptr(), fp4.GS_COMPUTE_ONE_PASS,
+                                ws.data_ptr(), wsb, stream) == fp4.FP4_OK
+        torch.cuda.synchronize()
+        assert torch.equal(got[0][:n], ref[0][:n])
+        assert torch.equal(got[1][:ns], ref[1][:ns])
+        assert torch.equal(got[2], ref[2])
+        assert bool(torch.isfinite(got[2]).all())
