@@ -502,6 +502,16 @@ def test_gemm_tile_plan_edges(fmt, M, N, K, out_dtype):
     _check_gemm(fmt, M, N, K, seed=M + K, out_dtype=out_dtype)
 
 
+# Wide decode shapes (M <= 32) with ragged last column tiles, every row checked.
+WIDE_DECODE = [(1, 28672, 1024), (7, 26000, 1024), (32, 25088, 512), (16, 32000, 768)]
+
+
+@pytest.mark.parametrize("out_dtype", OUT_DT, ids=OUT_IDS)
+@pytest.mark.parametrize("M,N,K", WIDE_DECODE, ids=["%dx%dx%d" % s for s in WIDE_DECODE])
+def test_gemm_wide_decode_ragged(M, N, K, out_dtype):
+    _check_gemm(fp4.FMT_MXFP4, M, N, K, seed=N + K, out_dtype=out_dtype, nrows=M)
+
+
 EXTREME = [(256, 512, 1024), (16, 4096, 4096), (4000, 4100, 4096), (128, 4096, 8192)]
 
 
