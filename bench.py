@@ -76,6 +76,9 @@ def parse():
                     help="run only these GEMMs a few times and print their timings (for profiler "
                          "runs): comma-separated fmt:MxNxK with fmt mx, nv, mxint4, nvint4 or "
                          "w4mx / w4nv (weight-only), e.g. mx:4096x4096x4096,mx:1x28672x8192")
+    ap.add_argument("--vendor-mxfp4", action="store_true",
+                    help="run only a side-by-side of this library's MXFP4 GEMM and hipBLASLt's "
+                         "(torch._scaled_mm) on the large Llama shapes, as context")
     return ap.parse_args()
 
 
@@ -134,6 +137,9 @@ def main():
         del src, dst
     if args.only_gemm:
         only_gemm(args, torch, fp4, workloads, dev)
+        return
+    if args.vendor_mxfp4:
+        vendor_mxfp4(torch, fp4, dev)
         return
 
     # ------------------------------------------------------------ workload
@@ -612,6 +618,72 @@ def only_gemm(args, torch, fp4, workloads, dev):
         log("%s %.2f us" % (item, us))
         del w, a, q0, qw, y
     print(json.dumps({"only_gemm": res}), flush=True)
+
+
+def vendor_mxfp4(torch, fp4, dev):
+    """This library's MXFP4 GEMM beside hipBLASLt's (torch._scaled_mm with
+    float4_e2m1fn_x2 operands and float8_e8m0fnu scales), bf16 output, on the
+    same random E2M1 codes with every E8M0 scale 2^0, alternating three times
+    (ten calls each, best run).  Context for the MFMA fraction, not a bench
+    value; the two outputs are compared entry by entry (within bf16
+    rounding of each other)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    cfg = fp4.qconfig(fp4.FMT_MXFP4, False, fp4.SCALES_GEMM)
+
+    def operand(rows, K):
+        c = torch.randint(0, 256, (rows, K // 2), dtype=torch.uint8, device=dev, generator=gen)
+        sc = torch.full((fp4.fp4_scales_bytes(cfg, rows, K),), 127, dtype=torch.uint8, device=dev)
+        return c, fp4.Quantized(c.reshape(-1), sc, torch.ones(1, device=dev), cfg, rows, K)
+
+    def best_us(f, n=10):
+        f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    res = {}
+    for (M, N, K) in ((4096, 4096, 4096), (4096, 14336, 4096), (4096, 4096, 14336),
+                      (8192, 28672, 8192), (8192, 8192, 28672)):
+        key = "%dx%dx%d" % (M, N, K)
+        ca, qa = operand(M, K)
+        cb, qb = operand(N, K)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+        sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device=dev).view(torch.float8_e8m0fnu)
+        a4, b4 = ca.view(torch.float4_e2m1fn_x2), cb.view(torch.float4_e2m1fn_x2)
+
+        def ours():
+            fp4.gemm(qa, qb, out=y)
+
+        def vendor():
+            return torch._scaled_mm(a4, b4.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        flops = 2.0 * M * N * K
+        try:
+            yv = vendor()
+            ours()
+            torch.cuda.synchronize()
+            agree = bool(((yv.float() - y.float()).abs() <= 2.0 ** -7 * y.float().abs() + 1e-6).all())
+            to, tv = [], []
+            for _ in range(3):
+                to.append(best_us(ours))
+                tv.append(best_us(vendor))
+            res[key] = {"ours_us": round(min(to), 1), "ours_frac_fp4_peak": round(flops / min(to) / 1e9 / 10.1, 3),
+                        "hipblaslt_us": round(min(tv), 1),
+                        "hipblaslt_frac_fp4_peak": round(flops / min(tv) / 1e9 / 10.1, 3),
+                        "outputs_agree": agree}
+        except RuntimeError as e:  # the library call rejected the shape
+            res[key] = {"hipblaslt": "not available: " + str(e)[:160]}
+        log("%s %s" % (key, res[key]))
+        del ca, qa, cb, qb, y, sa, sb, a4, b4
+        torch.cuda.empty_cache()
+    print(json.dumps({"vendor_mxfp4": res}), flush=True)
 
 
 def cpu_model() -> str:
