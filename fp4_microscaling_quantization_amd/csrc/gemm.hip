@@ -1797,6 +1797,12 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
     e = launch_mx2_cfg<256, 256, 128, 64>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, 1, (int)(K / 256), part, st);
   else if (p.cfg == 0)
     e = launch_mx_cfg<256, 256, 128, 64, 4>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, splits, kt_per, part, st);
+  // unsplit 128 x 128 tiles above 128 rows: the 256-K kernel with eight waves
+  // of 64 x 32 (2048x4096x4096 32.6 -> 26.6 us, 512x14336x4096 30.5 -> 24.8 us
+  // against the 128-K ring; slower at 64-96 rows, level at 128)
+  else if (p.cfg == 1 && M > 128 && K % 256 == 0 && splits == 1 &&
+           (uint64_t)max(M, N) * (uint64_t)(K / 2) < (1ull << 32))
+    e = launch_mx2_cfg<128, 128, 64, 32>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, 1, (int)(K / 256), part, st);
   else if (p.cfg == 1)
     e = launch_mx_cfg<128, 128, 64, 64, 4>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, splits, kt_per, part, st);
   else

@@ -492,7 +492,10 @@ def test_gemm_llama70b_mlp_shapes(fmt, M, N, K, out_dtype):
 # (its first and last stages differ: stale reads and a re-load of the last
 # stage past the end).
 PLAN_EDGES = [(4000, 4100, 4096), (4000, 4100, 4224), (64, 1024, 1152), (4000, 4100, 1024),
-              (4096, 4096, 256), (4000, 4100, 512), (4000, 4100, 768), (4096, 4096, 1280)]
+              (4096, 4096, 256), (4000, 4100, 512), (4000, 4100, 768), (4096, 4096, 1280),
+              # unsplit 128 x 128 tiles above 128 rows (the 256-K kernel, eight waves
+              # of 64 x 32): ragged, three stages, and full-size medium shapes
+              (300, 1000, 768), (2048, 4096, 4096), (520, 14336, 4096), (129, 2000, 256)]
 
 
 @pytest.mark.parametrize("out_dtype", OUT_DT, ids=OUT_IDS)

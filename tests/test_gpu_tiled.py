@@ -151,7 +151,7 @@ def _operands(fmt, M, N, K, seed):
 # NVFP4 path for K % 256 == 128.
 GEMM_CASES = [
     (fp4.FMT_MXFP4, 1, 1024, 2048), (fp4.FMT_MXFP4, 16, 1024, 2048), (fp4.FMT_MXFP4, 200, 512, 1024),
-    (fp4.FMT_MXFP4, 16, 25088, 1024),
+    (fp4.FMT_MXFP4, 16, 25088, 1024), (fp4.FMT_MXFP4, 384, 4096, 768),
     (fp4.FMT_MXFP4, 4096, 4096, 512), (fp4.FMT_MXFP4, 4096, 4096, 384), (fp4.FMT_MXFP4, 4000, 4224, 768),
     (fp4.FMT_NVFP4, 16, 1024, 2048), (fp4.FMT_NVFP4, 128, 1024, 2048), (fp4.FMT_NVFP4, 256, 1024, 2048),
     (fp4.FMT_NVFP4, 4096, 4096, 512), (fp4.FMT_NVFP4, 64, 256, 384),
