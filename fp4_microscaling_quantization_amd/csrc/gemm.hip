@@ -1770,8 +1770,28 @@ MxPlan plan_mx(int64_t M, int64_t N, int64_t K, int bn2 = 256, bool small_m_cap 
 
 namespace fp4lib {
 
-size_t gemm_mx_workspace(int64_t M, int64_t N, int64_t K) {
+// The MXFP4 plan: plan_mx, except that 128 x 128 tiles above 128 rows with
+// K % 256 == 0 (and 32-bit DMA offsets) run unsplit on the 256-K kernel with
+// eight waves of 64 x 32.  Measured against the split plan on the 128-K ring
+// with its fp32 partials and reduction (side by side, bf16 output):
+// 1024x4096x4096 31.9 -> 17.7 us, 384x4096x4096 24.5 -> 13.8,
+// 2048x1024x2048 26.9 -> 8.7, and faster at every tile count down to 16
+// (256x1024x8192 19.3 -> 18.6 us).
+bool mx_unsplit_128(int64_t M, int64_t N, int64_t K) {
+  return M > 128 && K % 256 == 0 && (uint64_t)max(M, N) * (uint64_t)(K / 2) < (1ull << 32);
+}
+
+MxPlan plan_mx_fp4(int64_t M, int64_t N, int64_t K) {
   MxPlan p = plan_mx(M, N, K, 128, true);
+  if (p.cfg == 1 && mx_unsplit_128(M, N, K)) {
+    p.splits = 1;
+    p.kt_per = (int)(K / 128);
+  }
+  return p;
+}
+
+size_t gemm_mx_workspace(int64_t M, int64_t N, int64_t K) {
+  MxPlan p = plan_mx_fp4(M, N, K);
   return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -1783,7 +1803,7 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
     zero_out_kernel<<<256, kThreads, 0, st>>>(y, ydt, (int)M, (int)N, ldy);
     return hipGetLastError();
   }
-  MxPlan p = plan_mx(M, N, K, 128, true);
+  MxPlan p = plan_mx_fp4(M, N, K);
   const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_mx_workspace(M, N, K);
   const int splits = split ? p.splits : 1;
   const int kt_per = split ? p.kt_per : (int)(K / 128);
@@ -1797,11 +1817,11 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
     e = launch_mx2_cfg<256, 256, 128, 64>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, 1, (int)(K / 256), part, st);
   else if (p.cfg == 0)
     e = launch_mx_cfg<256, 256, 128, 64, 4>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, splits, kt_per, part, st);
-  // unsplit 128 x 128 tiles above 128 rows: the 256-K kernel with eight waves
-  // of 64 x 32 (2048x4096x4096 32.6 -> 26.6 us, 512x14336x4096 30.5 -> 24.8 us
-  // against the 128-K ring; slower at 64-96 rows, level at 128)
-  else if (p.cfg == 1 && M > 128 && K % 256 == 0 && splits == 1 &&
-           (uint64_t)max(M, N) * (uint64_t)(K / 2) < (1ull << 32))
+  // 128 x 128 tiles above 128 rows (plan_mx_fp4: unsplit): the 256-K kernel
+  // with eight waves of 64 x 32 (2048x4096x4096 32.6 -> 26.6 us,
+  // 512x14336x4096 30.5 -> 24.8 us against the 128-K ring; slower at 64-96
+  // rows, level at 128)
+  else if (p.cfg == 1 && mx_unsplit_128(M, N, K))
     e = launch_mx2_cfg<128, 128, 64, 32>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, 1, (int)(K / 256), part, st);
   else if (p.cfg == 1)
     e = launch_mx_cfg<128, 128, 64, 64, 4>(M, N, K, a, as, b, bs, bt, y, ydt, ldy, splits, kt_per, part, st);

@@ -495,7 +495,9 @@ PLAN_EDGES = [(4000, 4100, 4096), (4000, 4100, 4224), (64, 1024, 1152), (4000, 4
               (4096, 4096, 256), (4000, 4100, 512), (4000, 4100, 768), (4096, 4096, 1280),
               # unsplit 128 x 128 tiles above 128 rows (the 256-K kernel, eight waves
               # of 64 x 32): ragged, three stages, and full-size medium shapes
-              (300, 1000, 768), (2048, 4096, 4096), (520, 14336, 4096), (129, 2000, 256)]
+              (300, 1000, 768), (2048, 4096, 4096), (520, 14336, 4096), (129, 2000, 256),
+              # shapes the split-K plan used to take (few tiles, long K)
+              (256, 1024, 8192), (2048, 1000, 2048)]
 
 
 @pytest.mark.parametrize("out_dtype", OUT_DT, ids=OUT_IDS)
