@@ -390,7 +390,7 @@ size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return 0;
   if (fmt == FP4_FMT_MXFP4) return fp4lib::gemm_mx_workspace(M, N, K);
   if (fmt == FP4_FMT_NVFP4 || fmt == FP4_FMT_MXINT4 || fmt == FP4_FMT_NVINT4)
-    return fp4lib::gemm_nv_workspace(M, N, K);
+    return fp4lib::gemm_nv_workspace(fmt, M, N, K);
   return 0;
 }
 

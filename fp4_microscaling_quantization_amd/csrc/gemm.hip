@@ -1838,11 +1838,25 @@ hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
 // formats, whose expansion costs more, own all 128 rows x 32 columns with
 // the A tile expanded once per workgroup into LDS (NVINT4 128 -> 109 us,
 // MXINT4 155 -> 127 us; NVFP4 80 -> 95 us that way, so it keeps 64x64).
-MxPlan plan_nv(int64_t M, int64_t N, int64_t K) { return plan_mx(M, N, K, 256, true); }
+// The ring GEMMs' plan for format fmt (NVFP4, MXINT4, NVINT4): plan_mx,
+// except that NVFP4 above 128 rows with at least 128 tiles of 128 x 128 runs
+// unsplit.  Measured against split-K plus the reduction kernel (side by
+// side, bf16 output): 1024x4096x4096 55.1 -> 48.3 us, 2048x1024x2048 32.1 ->
+// 23.4 us; with fewer tiles the split plan is faster (256x1024x8192, 16
+// tiles: 22.6 against 67.4 us unsplit).  (MXINT4 lost 9 % on 2048x1024x2048
+// unsplit, NVINT4 gained 3-5 %: both keep the split plan.)
+MxPlan plan_nv(int fmt, int64_t M, int64_t N, int64_t K) {
+  MxPlan p = plan_mx(M, N, K, 256, true);
+  if (fmt == FP4_FMT_NVFP4 && p.cfg == 1 && M > 128 && ((M + 127) / 128) * ((N + 127) / 128) >= 128) {
+    p.splits = 1;
+    p.kt_per = (int)(K / 128);
+  }
+  return p;
+}
 
-size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K) {
+size_t gemm_nv_workspace(int fmt, int64_t M, int64_t N, int64_t K) {
   if (K % 256 != 0 || K == 0) return 0;
-  MxPlan p = plan_nv(M, N, K);
+  MxPlan p = plan_nv(fmt, M, N, K);
   return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -1853,8 +1867,8 @@ hipError_t launch_ring_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a, c
                             const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
                             int bt, void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
                             hipStream_t st) {
-  MxPlan p = plan_nv(M, N, K);
-  const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_nv_workspace(M, N, K);
+  MxPlan p = plan_nv(FMT, M, N, K);
+  const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_nv_workspace(FMT, M, N, K);
   const int splits = split ? p.splits : 1;
   const int kt_per = split ? p.kt_per : (int)(K / 128);
   float* part = static_cast<float*>(ws);
@@ -1893,8 +1907,8 @@ hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, con
   if (M == 0 || N == 0) return hipSuccess;
   if (K % 256 == 0 && K > 0) {
     // LDS ring with in-register fp16 expansion; tiles and split-K as for MXFP4
-    MxPlan p = plan_nv(M, N, K);
-    const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_nv_workspace(M, N, K);
+    MxPlan p = plan_nv(FP4_FMT_NVFP4, M, N, K);
+    const bool split = p.splits > 1 && ws != nullptr && ws_bytes >= gemm_nv_workspace(FP4_FMT_NVFP4, M, N, K);
     const int splits = split ? p.splits : 1;
     const int kt_per = split ? p.kt_per : (int)(K / 128);
     float* part = static_cast<float*>(ws);

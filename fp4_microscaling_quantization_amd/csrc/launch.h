@@ -69,7 +69,7 @@ size_t gemm_mx_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mx(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                           const uint8_t* b, const uint8_t* bs, int bt, void* y, int ydt, int64_t ldy,
                           void* ws, size_t ws_bytes, hipStream_t st);
-size_t gemm_nv_workspace(int64_t M, int64_t N, int64_t K);
+size_t gemm_nv_workspace(int fmt, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_nv(int64_t M, int64_t N, int64_t K, const uint8_t* a, const uint8_t* as,
                           const float* ags, const uint8_t* b, const uint8_t* bs, const float* bgs,
                           int bt, void* y, int ydt, int64_t ldy, void* ws, size_t ws_bytes,
